@@ -1,0 +1,145 @@
+"""Reference tile planner for jagged GDPA, in plain Python integers.
+
+TEST INFRASTRUCTURE (see the header of gdpa_ref.py for who may import it).  The
+C++ planner of the library must reproduce this plan bit for bit; it shares no
+code with it.
+
+Source: GDPA page (aitrends.kr/articles/26275, "Generalized Dot-Product Attention
+(GDPA): kernel optimisation for real recommendation-system training loads"),
+"Section details", paragraph and diagram on jagged inputs: the CPU enumerates the
+valid tiles in advance, sorts them, and assigns them to processors in a zigzag
+instead of round robin (max:min load 12:1 -> 5:4 in the diagram).
+
+Readings (the page gives no cost model or tie-break):
+  * a work item is (sample b, head h, stationary tile t) with a contiguous range
+    [s0, s1] of streaming tiles that hold at least one valid pair; items whose
+    other side is empty (Lk == 0 for Q-stationary lists, Lq == 0 for the
+    KV-stationary list) have no steps (s0 = 0, s1 = -1) and only write zeros;
+  * cost = (valid stationary rows) + sum over steps of (valid streaming rows + 32),
+    i.e. rows moved through memory plus a fixed per-step charge;
+  * stable order: cost descending, then (b, h, t) ascending;
+  * zigzag (snake) deal over P bins: the r-th item goes to bin r mod P in even
+    rounds and to P - 1 - (r mod P) in odd rounds (round = r // P);
+  * per-bin CSR keeps each bin's items in deal order.
+
+Three lists are planned: "fwd" and "dq" (Q-stationary: t is a q tile of BM rows,
+steps are kv tiles of BN rows) and "dkdv" (KV-stationary: t is a kv tile of BK
+rows, steps are q tiles of BQ rows).  Tile sizes come from the wave layout:
+BM = 32 WQ, BN = (4 / WQ) BNW; BK = 32 WK, BQ = 32 (4 / WK).
+"""
+from __future__ import annotations
+
+STEP_CHARGE = 32
+
+LISTS = ("fwd", "dkdv", "dq")
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def auto_layout(lq, lk, window: int = 0):
+    """Wave layouts chosen from the length statistics (integer rules)."""
+    nq = sum(1 for x in lq if x > 0)
+    nk = sum(1 for x in lk if x > 0)
+    sq, sk = sum(lq), sum(lk)
+    max_lk = max(lk) if len(lk) else 0
+
+    def waves(total, count):
+        if count == 0:
+            return 4
+        if total <= 40 * count:
+            return 1
+        if total <= 96 * count:
+            return 2
+        return 4
+
+    wq = waves(sq, nq)
+    bnw = 32 if (wq < 4 or max_lk <= 32) else 64
+    wk = waves(sk, nk)
+    return {"fwd": (wq, bnw), "dq": (wq, 32), "dkdv": (wk, 32)}
+
+
+def tile_sizes(kind: str, waves: int, bnw: int):
+    """(stationary tile rows, streaming tile rows) of a list."""
+    if kind in ("fwd", "dq"):
+        return 32 * waves, (4 // waves) * bnw
+    if kind == "dkdv":
+        return 32 * waves, 32 * (4 // waves)
+    raise ValueError(kind)
+
+
+def enumerate_items(kind: str, lq, lk, H: int, window: int, t_stat: int, t_strm: int):
+    """[(cost, b, h, t, s0, s1)] in (b, h, t) order."""
+    items = []
+    for b in range(len(lq)):
+        if kind == "dkdv":
+            ls, lo_other = int(lk[b]), int(lq[b])
+        else:
+            ls, lo_other = int(lq[b]), int(lk[b])
+        for h in range(H):
+            for t in range(_ceil_div(ls, t_stat)):
+                a0 = t * t_stat
+                a1 = min(ls, a0 + t_stat) - 1
+                n_stat = a1 - a0 + 1
+                if lo_other == 0:
+                    s0, s1 = 0, -1
+                elif window == 0:
+                    s0, s1 = 0, _ceil_div(lo_other, t_strm) - 1
+                else:
+                    lo = max(0, a0 - window + 1)
+                    hi = min(lo_other - 1, a1 + window - 1)
+                    s0, s1 = lo // t_strm, hi // t_strm
+                cost = n_stat
+                for s in range(s0, s1 + 1):
+                    cost += min(lo_other, (s + 1) * t_strm) - s * t_strm + STEP_CHARGE
+                items.append((cost, b, h, t, s0, s1))
+    return items
+
+
+def deal(items, P: int, zigzag: bool = True):
+    """Sort and deal items to P bins.  Returns (bin_ptr, ordered items, bin_cost)."""
+    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[3]))
+    bins = [[] for _ in range(P)]
+    for r, it in enumerate(order):
+        rnd, pos = divmod(r, P)
+        p = pos if (not zigzag or rnd % 2 == 0) else P - 1 - pos
+        bins[p].append(it)
+    bin_ptr = [0]
+    flat = []
+    for p in range(P):
+        flat.extend(bins[p])
+        bin_ptr.append(len(flat))
+    cost = [sum(it[0] for it in bins[p]) for p in range(P)]
+    return bin_ptr, flat, cost
+
+
+def plan_list(kind: str, lq, lk, H: int, window: int, P: int, waves: int, bnw: int,
+              zigzag: bool = True):
+    t_stat, t_strm = tile_sizes(kind, waves, bnw)
+    items = enumerate_items(kind, lq, lk, H, window, t_stat, t_strm)
+    bin_ptr, flat, cost = deal(items, P, zigzag)
+    return dict(kind=kind, P=P, t_stat=t_stat, t_strm=t_strm, waves=waves, bnw=bnw,
+                bin_ptr=bin_ptr, items=[it[1:] for it in flat], bin_cost=cost)
+
+
+def export(pl) -> list:
+    """The int32 serialisation the library's plan export produces:
+    [P, n_items, t_stat, t_strm, waves, bnw, bin_ptr[0..P], then (b, h, t, s0, s1) per item]."""
+    out = [pl["P"], len(pl["items"]), pl["t_stat"], pl["t_strm"], pl["waves"], pl["bnw"]]
+    out += list(pl["bin_ptr"])
+    for it in pl["items"]:
+        out += list(it)
+    return out
+
+
+def plan(lq, lk, H: int, window: int, P: int, layout=None):
+    """All three lists with the automatic (or given) wave layouts."""
+    layout = layout or auto_layout(lq, lk, window)
+    return {kind: plan_list(kind, lq, lk, H, window, P, *layout[kind]) for kind in LISTS}
+
+
+def imbalance(cost) -> float:
+    """max / min per-bin cost over bins with work (inf if some bin is idle)."""
+    lo, hi = min(cost), max(cost)
+    return float("inf") if lo == 0 else hi / lo
