@@ -1,0 +1,200 @@
+/*
+ * gdpa.h - C ABI of a jagged Generalized Dot-Product Attention (GDPA) library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (GDPA page: aitrends.kr/articles/26275, "Generalized
+ * Dot-Product Attention (GDPA): kernel optimisation for real recommendation-system
+ * training loads"; "Key summary" and "Section details", diagram "Self-attention,
+ * PMA and pFFN unified as GDPA", and the paragraph on removing the softmax
+ * correction step):  for every sample b and head h, over the valid pairs
+ * (i, j) with 0 <= i < Lq_b, 0 <= j < Lk_b and, if window > 0, |i - j| < window,
+ *
+ *     S_ij = <Q_i, K_j> / sqrt(d),   P_ij = act(S_ij),   O_i = sum_j P_ij V_j
+ *
+ * with no softmax and no row normalisation.  The backward pass returns dQ, dK,
+ * dV of the loss sum(O * dO), recomputing S inside the kernels (no O and no
+ * row statistics are kept).  The three shapes of the GEM page (techlist.io,
+ * "GEM training: ...", section on why high GPU utilisation is hard): jagged
+ * self-attention with an optional short window, user-ad cross-attention (long
+ * Q, short K/V) and PMA (short Q, long K/V) are all served by the same calls.
+ *
+ * Data layout.  Q, dO, O, dQ are [Tq, H, d] and K, V, dK, dV are [Tk, H, d],
+ * dense, row-major (d fastest, then heads, then tokens).  Offsets are int32
+ * [B + 1], non-decreasing, off[0] = 0, off[B] = T; sample b owns rows
+ * off[b] .. off[b+1]-1.  bf16 is IEEE bfloat16.
+ *
+ * Ownership.  The caller owns every tensor and offset buffer and keeps them
+ * alive until the stream work that uses them has finished.  A plan owns its
+ * host and device work lists; gdpa_plan_destroy frees them.  A plan is
+ * immutable after creation and may be used from several streams at once.
+ *
+ * Asynchrony.  gdpa_fwd / gdpa_bwd validate their arguments on the host, then
+ * only enqueue kernels on `stream` (NULL = the null stream); they never
+ * synchronise.  A fault during execution shows up at the caller's next
+ * synchronisation.
+ *
+ * Errors.  Every call returns a gdpa_status; no call throws.  Arguments are
+ * validated before anything is enqueued.  gdpa_last_error() returns a
+ * thread-local message describing the most recent failure on this thread.
+ *
+ * Determinism.  No atomics: every output row is written by exactly one work
+ * item, so results are bitwise identical from run to run.
+ */
+#ifndef GDPA_H
+#define GDPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDPA_OK = 0,
+    GDPA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, B/H/d/window out of range */
+    GDPA_ERR_BAD_OFFSETS = 2,   /* offsets not [0, .., T] non-decreasing, or a window with Lq != Lk */
+    GDPA_ERR_UNSUPPORTED = 3,   /* d not in {32, 64, 128}, activation/dtype combination not built */
+    GDPA_ERR_PLAN_MISMATCH = 4, /* B/H/d/window differ from the plan's, or a host-only plan */
+    GDPA_ERR_HIP = 5,           /* a HIP runtime call failed (message in gdpa_last_error) */
+    GDPA_ERR_NOMEM = 6          /* host or device allocation failed */
+} gdpa_status;
+
+/* Activations.  GELU is the exact erf form x * Phi(x).  GELU_POLY is an
+ * ALU-only clamped polynomial fit of it (FMA only; its absolute error bound is
+ * gdpa_gelu_poly_bound()).  GELU_TAYLOR6 is the GDPA page's series (code figure
+ * "ALU-only 6th-order Taylor GELU"), accurate only near 0.  IDENTITY and ONE
+ * (P = 1 on valid pairs) are test probes; ONE has no backward. */
+typedef enum {
+    GDPA_ACT_GELU = 0,
+    GDPA_ACT_SILU = 1,
+    GDPA_ACT_GELU_POLY = 2,
+    GDPA_ACT_GELU_TAYLOR6 = 3,
+    GDPA_ACT_IDENTITY = 4,
+    GDPA_ACT_ONE = 5
+} gdpa_act;
+
+/* Storage types.  BF16: bf16 inputs and outputs, fp32 accumulation (MFMA).
+ * BF16_F32OUT: bf16 inputs, fp32 outputs (O, dQ, dK, dV).  F32: fp32 in and
+ * out, plain fp32 arithmetic (no MFMA; a correctness path for small inputs). */
+typedef enum { GDPA_F32 = 0, GDPA_BF16 = 1, GDPA_BF16_F32OUT = 2 } gdpa_dtype;
+
+/* Work lists of a plan, for gdpa_plan_export / gdpa_plan_stats. */
+typedef enum { GDPA_LIST_FWD = 0, GDPA_LIST_DKDV = 1, GDPA_LIST_DQ = 2 } gdpa_list;
+
+/* Planning options.  All-zero (or a NULL pointer) selects the defaults. */
+typedef struct {
+    int host_only;   /* 1: plan on the host only (export / stats); no device memory is
+                        allocated and gdpa_fwd / gdpa_bwd reject the plan */
+    int bins[3];     /* persistent workgroups per list (GDPA_LIST_*); 0 = one per
+                        workgroup the device can hold resident (host_only: 256) */
+    int waves[3];    /* wave layout per list: 0 = automatic, else 1, 2 or 4 waves
+                        along the stationary side (fwd/dq: q blocks of 32 rows per
+                        work item; dkdv: kv blocks of 32 rows per work item) */
+    int bnw_fwd;     /* kv rows per wave per forward step: 0 = automatic, 32 or 64
+                        (64 only with 4 q waves) */
+    int round_robin; /* 1: deal sorted items round robin instead of zigzag (ablation) */
+} gdpa_plan_opts;
+
+/* Summary numbers of a plan. */
+typedef struct {
+    int64_t Tq, Tk;          /* total query / key rows */
+    int64_t valid_pairs;     /* sum over samples of the valid (i, j) pairs */
+    int32_t n_items[3];      /* work items per list */
+    int32_t n_steps[3];      /* streaming steps per list (a step-less item counts 0) */
+    int32_t bins[3];         /* persistent workgroups per list */
+    int32_t tile_stat[3];    /* stationary tile rows per list */
+    int32_t tile_strm[3];    /* streaming tile rows per list */
+    int64_t bin_cost_max[3]; /* per-bin cost extremes (planner cost units) */
+    int64_t bin_cost_min[3];
+} gdpa_plan_stats_t;
+
+typedef struct gdpa_plan_s* gdpa_plan;
+
+/*
+ * gdpa_plan_create - enumerate the non-empty tiles on the host and deal them to
+ * persistent workgroups (GDPA page, "Section details": the CPU precomputes the
+ * valid tiles, sorts them and assigns them to processors in a zigzag order).
+ *
+ *   q_off_host, kv_off_host : host int32 [B + 1] offsets (read during the call only)
+ *   B >= 0 samples, H >= 1 heads, d in {32, 64, 128}
+ *   window >= 0             : 0 = every in-range pair; w > 0 keeps |i - j| < w and
+ *                             requires Lq_b == Lk_b for every b
+ *   dtype                   : storage type the plan will be used with
+ *   opts                    : NULL or planning options
+ *   out                     : receives the plan (NULL on failure)
+ *
+ * Unless opts->host_only, uploads the work lists with hipMalloc / hipMemcpy on
+ * the current device (synchronous).  Errors: INVALID_ARG, BAD_OFFSETS,
+ * UNSUPPORTED, HIP, NOMEM.
+ */
+gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_host, int B, int H,
+                             int d, int window, gdpa_dtype dtype, const gdpa_plan_opts* opts,
+                             gdpa_plan* out);
+
+/*
+ * gdpa_fwd - O = act(Q K^T / sqrt(d)) V over the valid pairs (see top).
+ *
+ *   q [Tq,H,d], k [Tk,H,d], v [Tk,H,d] : device inputs of the plan's dtype
+ *   q_off_dev, kv_off_dev              : device int32 [B + 1], equal to the plan's
+ *                                        host offsets (precondition; GDPA_DEBUG=1 in
+ *                                        the environment re-checks it with a copy)
+ *   B, H, d, window                    : must equal the plan's
+ *   act                                : activation
+ *   o [Tq,H,d]                         : device output (bf16, or fp32 for F32 /
+ *                                        BF16_F32OUT); every row is written, rows
+ *                                        with no valid key as 0
+ *   stream                             : a hipStream_t (NULL = null stream)
+ *
+ * Errors: INVALID_ARG, PLAN_MISMATCH, UNSUPPORTED, HIP (launch failure).
+ */
+gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v,
+                     const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                     gdpa_act act, int window, void* o, void* stream);
+
+/*
+ * gdpa_bwd - gradients of sum(O * dO): dQ [Tq,H,d], dK and dV [Tk,H,d].
+ *
+ * dS = (dO V^T) * act'(S) on valid pairs; dV = P^T dO, dK = dS^T Q / sqrt(d),
+ * dQ = dS K / sqrt(d).  S is recomputed; O is not needed.  Arguments as for
+ * gdpa_fwd plus dout [Tq,H,d] (input) and dq, dk, dv (outputs, fully written;
+ * rows with no valid partner are 0).  act = GDPA_ACT_ONE is rejected
+ * (UNSUPPORTED).  Enqueues up to two kernels on `stream`.
+ */
+gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                     const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                     gdpa_act act, int window, void* dq, void* dk, void* dv, void* stream);
+
+/*
+ * gdpa_plan_export - serialise one work list as int32 values:
+ *   [P, n_items, tile_stat, tile_strm, waves, bnw, bin_ptr[0..P], then per item in
+ *    bin order (b, h, t, s0, s1)]
+ * where t is the stationary tile and [s0, s1] the streaming tiles (s1 < s0: no
+ * steps, the item writes zeros).  With buf == NULL, *n receives the length;
+ * otherwise *n is the capacity of buf on entry and the length on return.
+ * Errors: INVALID_ARG (bad list or capacity too small).
+ */
+gdpa_status gdpa_plan_export(gdpa_plan plan, int list, int32_t* buf, size_t* n);
+
+/* gdpa_plan_stats - summary numbers of a plan.  Errors: INVALID_ARG. */
+gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out);
+
+/* gdpa_plan_destroy - free a plan (NULL is ignored).  The caller must make sure
+ * no enqueued work still uses it. */
+void gdpa_plan_destroy(gdpa_plan plan);
+
+/* gdpa_status_string - static name of a status code. */
+const char* gdpa_status_string(gdpa_status s);
+
+/* gdpa_last_error - thread-local description of the last failure ("" if none). */
+const char* gdpa_last_error(void);
+
+/* gdpa_gelu_poly_bound - max |GELU_POLY(x) - x Phi(x)| over all real x, as
+ * derived when the polynomial was fitted (fp64 evaluation). */
+double gdpa_gelu_poly_bound(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDPA_H */

@@ -1,0 +1,240 @@
+"""Python binding of libgdpa, the MI355X jagged GDPA library (argument marshalling only).
+
+Every function mirrors the C entry point of the same name in include/gdpa.h;
+tensors may be passed as torch tensors (their data pointers are used) or as
+raw integer addresses.  All GDPA arithmetic runs in the library's HIP kernels;
+PyTorch is used here only to hand over device memory and streams.  If the
+library has not been built, loading it raises: there is no fallback.
+
+Build it with ``python -m recsys_attention_jagged_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdpa.so")
+
+GDPA_OK = 0
+STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARG", 2: "GDPA_ERR_BAD_OFFSETS", 3: "GDPA_ERR_UNSUPPORTED",
+          4: "GDPA_ERR_PLAN_MISMATCH", 5: "GDPA_ERR_HIP", 6: "GDPA_ERR_NOMEM"}
+ACT = {"gelu": 0, "silu": 1, "gelu_poly": 2, "gelu_taylor6": 3, "identity": 4, "one": 5}
+DTYPE = {"f32": 0, "bf16": 1, "bf16_f32out": 2}
+LIST = {"fwd": 0, "dkdv": 1, "dq": 2}
+
+
+class GdpaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class gdpa_plan_opts(ctypes.Structure):
+    _fields_ = [("host_only", ctypes.c_int), ("bins", ctypes.c_int * 3), ("waves", ctypes.c_int * 3),
+                ("bnw_fwd", ctypes.c_int), ("round_robin", ctypes.c_int)]
+
+
+class gdpa_plan_stats_t(ctypes.Structure):
+    _fields_ = [("Tq", ctypes.c_int64), ("Tk", ctypes.c_int64), ("valid_pairs", ctypes.c_int64),
+                ("n_items", ctypes.c_int32 * 3), ("n_steps", ctypes.c_int32 * 3),
+                ("bins", ctypes.c_int32 * 3), ("tile_stat", ctypes.c_int32 * 3),
+                ("tile_strm", ctypes.c_int32 * 3), ("bin_cost_max", ctypes.c_int64 * 3),
+                ("bin_cost_min", ctypes.c_int64 * 3)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libgdpa.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run: python -m recsys_attention_jagged_amd.build")
+    lib = ctypes.CDLL(path)
+    lib.gdpa_plan_create.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts),
+                                     ctypes.POINTER(_vp)]
+    lib.gdpa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
+    lib.gdpa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
+    lib.gdpa_plan_export.argtypes = [_vp, _i, _vp, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdpa_plan_stats.argtypes = [_vp, ctypes.POINTER(gdpa_plan_stats_t)]
+    lib.gdpa_plan_destroy.argtypes = [_vp]
+    lib.gdpa_plan_destroy.restype = None
+    lib.gdpa_status_string.argtypes = [_i]
+    lib.gdpa_status_string.restype = ctypes.c_char_p
+    lib.gdpa_last_error.argtypes = []
+    lib.gdpa_last_error.restype = ctypes.c_char_p
+    lib.gdpa_gelu_poly_bound.argtypes = []
+    lib.gdpa_gelu_poly_bound.restype = ctypes.c_double
+    for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_plan_export", "gdpa_plan_stats"):
+        getattr(lib, name).restype = _i
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != GDPA_OK:
+        raise GdpaError(status, load_library().gdpa_last_error().decode())
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr() or None
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(f"cannot pass {type(x)} as a pointer")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _enum(v, table):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: int, dtype,
+                     host_only: bool = False, bins=(0, 0, 0), waves=(0, 0, 0), bnw_fwd: int = 0,
+                     round_robin: bool = False) -> int:
+    """Returns an opaque plan handle (int).  Offsets: host int32 [B + 1]."""
+    qo = np.ascontiguousarray(q_off_host, dtype=np.int32)
+    ko = np.ascontiguousarray(kv_off_host, dtype=np.int32)
+    if qo.shape != (B + 1,) or ko.shape != (B + 1,):
+        raise ValueError("offsets must have B + 1 entries")
+    opts = gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*waves),
+                          int(bnw_fwd), int(round_robin))
+    out = _vp()
+    _check(load_library().gdpa_plan_create(qo.ctypes.data, ko.ctypes.data, B, H, d, window,
+                                           _enum(dtype, DTYPE), ctypes.byref(opts), ctypes.byref(out)))
+    return out.value
+
+
+def gdpa_fwd(plan, q, k, v, q_off_dev, kv_off_dev, B, H, d, act, window, o, stream=None):
+    _check(load_library().gdpa_fwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(q_off_dev), _ptr(kv_off_dev),
+                                   B, H, d, _enum(act, ACT), window, _ptr(o), _stream(stream)))
+
+
+def gdpa_bwd(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, dq, dk, dv,
+             stream=None):
+    _check(load_library().gdpa_bwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
+                                   _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def gdpa_plan_export(plan, list_) -> np.ndarray:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.gdpa_plan_export(plan, _enum(list_, LIST), None, ctypes.byref(n)))
+    buf = np.zeros(n.value, dtype=np.int32)
+    _check(lib.gdpa_plan_export(plan, _enum(list_, LIST), buf.ctypes.data, ctypes.byref(n)))
+    return buf
+
+
+def gdpa_plan_stats(plan) -> dict:
+    st = gdpa_plan_stats_t()
+    _check(load_library().gdpa_plan_stats(plan, ctypes.byref(st)))
+    out = {}
+    for name, _ in gdpa_plan_stats_t._fields_:
+        val = getattr(st, name)
+        out[name] = list(val) if hasattr(val, "__len__") else int(val)
+    return out
+
+
+def gdpa_plan_destroy(plan):
+    if plan:
+        load_library().gdpa_plan_destroy(plan)
+
+
+def gdpa_status_string(status: int) -> str:
+    return load_library().gdpa_status_string(status).decode()
+
+
+def gdpa_last_error() -> str:
+    return load_library().gdpa_last_error().decode()
+
+
+def gdpa_gelu_poly_bound() -> float:
+    return float(load_library().gdpa_gelu_poly_bound())
+
+
+# ---------------------------------------------------------------------------
+# convenience: a plan object that allocates outputs with torch
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """Owns a plan; ``fwd`` / ``bwd`` allocate outputs (torch) and call the library."""
+
+    def __init__(self, q_off_host, kv_off_host, H: int, d: int, window: int = 0, dtype="bf16", **opts):
+        self.q_off = np.asarray(q_off_host, dtype=np.int32)
+        self.kv_off = np.asarray(kv_off_host, dtype=np.int32)
+        self.B = len(self.q_off) - 1
+        self.H, self.d, self.window, self.dtype = H, d, window, dtype
+        self.handle = gdpa_plan_create(self.q_off, self.kv_off, self.B, H, d, window, dtype, **opts)
+
+    def close(self):
+        if self.handle:
+            gdpa_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def stats(self) -> dict:
+        return gdpa_plan_stats(self.handle)
+
+    def export(self, list_) -> np.ndarray:
+        return gdpa_plan_export(self.handle, list_)
+
+    def _out_dtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def fwd(self, q, k, v, q_off_dev, kv_off_dev, act, o=None, stream=None):
+        import torch
+        if o is None:
+            o = torch.empty(q.shape, dtype=self._out_dtype(), device=q.device)
+        gdpa_fwd(self.handle, q, k, v, q_off_dev, kv_off_dev, self.B, self.H, self.d, act, self.window, o,
+                 stream)
+        return o
+
+    def bwd(self, q, k, v, dout, q_off_dev, kv_off_dev, act, dq=None, dk=None, dv=None, stream=None):
+        import torch
+        dt = self._out_dtype()
+        dq = torch.empty(q.shape, dtype=dt, device=q.device) if dq is None else dq
+        dk = torch.empty(k.shape, dtype=dt, device=k.device) if dk is None else dk
+        dv = torch.empty(v.shape, dtype=dt, device=v.device) if dv is None else dv
+        gdpa_bwd(self.handle, q, k, v, dout, q_off_dev, kv_off_dev, self.B, self.H, self.d, act,
+                 self.window, dq, dk, dv, stream)
+        return dq, dk, dv

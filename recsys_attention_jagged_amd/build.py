@@ -1,0 +1,87 @@
+"""Build libgdpa.so (gfx950) in-tree with hipcc.
+
+    python -m recsys_attention_jagged_amd.build [--jobs N] [--verbose]
+
+Every HIP translation unit is compiled for gfx950 only.  Packed-fp32 VALU
+instructions are disabled for all device code.  Objects go to
+recsys_attention_jagged_amd/_build/, the library to recsys_attention_jagged_amd/libgdpa.so.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libgdpa.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+          "-Wno-unused-command-line-argument"]
+
+# (output object, source, extra flags)
+UNITS = [("plan.o", "plan.cpp", []),
+         ("api.o", "api.cpp", []),
+         ("fp32.o", "fp32.hip", [])]
+for _d in (32, 64, 128):
+    UNITS.append((f"fwd_d{_d}.o", "fwd_bf16.hip", [f"-DGDPA_D={_d}"]))
+    UNITS.append((f"bwd_d{_d}.o", "bwd_bf16.hip", [f"-DGDPA_D={_d}"]))
+
+
+def _compile(unit, verbose):
+    obj, src, extra = unit
+    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", os.path.join(BUILD, obj)]
+    t0 = time.time()
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 target feature; that warning is harmless
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(l for l in (p.stderr or "").splitlines() if noise not in l)
+    if p.returncode != 0:
+        raise RuntimeError(f"compiling {src} {' '.join(extra)} failed:\n{err}")
+    if verbose:
+        print(f"  {obj}: {time.time() - t0:.1f}s", flush=True)
+        if err.strip():
+            print(err)
+    return obj
+
+
+def build(jobs: int = 0, verbose: bool = False) -> str:
+    """Compile every unit and link the library; returns its path."""
+    if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or min(len(UNITS), os.cpu_count() or 4, 16)
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda u: _compile(u, verbose), UNITS))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + [os.path.join(BUILD, o) for o in objs]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"link failed:\n{p.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB} in {time.time() - t0:.1f}s", flush=True)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--jobs", type=int, default=0)
+    ap.add_argument("--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    build(args.jobs, args.verbose)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

@@ -1,0 +1,387 @@
+// C ABI of the GDPA library: argument validation, planning, upload and kernel
+// dispatch.  See include/gdpa.h for the contract of every entry point.
+#include "gdpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "gelu_poly.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+using namespace gdpa;
+
+namespace {
+
+thread_local std::string g_err;
+
+gdpa_status fail(gdpa_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+gdpa_status fail_hip(hipError_t e, const char* what) {
+    g_err = std::string(what) + ": " + hipGetErrorString(e);
+    return GDPA_ERR_HIP;
+}
+
+bool debug_enabled() {
+    const char* v = std::getenv("GDPA_DEBUG");
+    return v && *v && std::strcmp(v, "0") != 0;
+}
+
+const void* fwd_kernel_ptr(int d, int waves, int bnw, int act) {
+    switch (d) {
+        case 32: return fwd_bf16_kernel_ptr_d32(waves, bnw, act);
+        case 64: return fwd_bf16_kernel_ptr_d64(waves, bnw, act);
+        case 128: return fwd_bf16_kernel_ptr_d128(waves, bnw, act);
+    }
+    return nullptr;
+}
+const void* dq_kernel_ptr(int d, int waves, int act) {
+    switch (d) {
+        case 32: return dq_bf16_kernel_ptr_d32(waves, act);
+        case 64: return dq_bf16_kernel_ptr_d64(waves, act);
+        case 128: return dq_bf16_kernel_ptr_d128(waves, act);
+    }
+    return nullptr;
+}
+const void* dkdv_kernel_ptr(int d, int waves, int act) {
+    switch (d) {
+        case 32: return dkdv_bf16_kernel_ptr_d32(waves, act);
+        case 64: return dkdv_bf16_kernel_ptr_d64(waves, act);
+        case 128: return dkdv_bf16_kernel_ptr_d128(waves, act);
+    }
+    return nullptr;
+}
+
+int64_t pairs_of(int64_t lq, int64_t lk, int64_t w) {
+    if (w == 0) return lq * lk;
+    int64_t n = 0;
+    for (int64_t i = 0; i < lq; ++i) n += std::min(lk, i + w) - std::max<int64_t>(0, i - w + 1);
+    return n;
+}
+
+}  // namespace
+
+struct gdpa_plan_s {
+    int B = 0, H = 0, d = 0, window = 0;
+    gdpa_dtype dtype = GDPA_BF16;
+    bool host_only = true;
+    std::vector<int32_t> q_off, kv_off;
+    std::vector<int64_t> lq, lk;
+    int64_t Tq = 0, Tk = 0, valid_pairs = 0;
+    WorkList lists[3];
+    Item* d_items[3] = {nullptr, nullptr, nullptr};
+    int32_t* d_bin_ptr[3] = {nullptr, nullptr, nullptr};
+
+    ~gdpa_plan_s() {
+        for (int l = 0; l < 3; ++l) {
+            if (d_items[l]) (void)hipFree(d_items[l]);
+            if (d_bin_ptr[l]) (void)hipFree(d_bin_ptr[l]);
+        }
+    }
+};
+
+extern "C" {
+
+const char* gdpa_status_string(gdpa_status s) {
+    switch (s) {
+        case GDPA_OK: return "GDPA_OK";
+        case GDPA_ERR_INVALID_ARG: return "GDPA_ERR_INVALID_ARG";
+        case GDPA_ERR_BAD_OFFSETS: return "GDPA_ERR_BAD_OFFSETS";
+        case GDPA_ERR_UNSUPPORTED: return "GDPA_ERR_UNSUPPORTED";
+        case GDPA_ERR_PLAN_MISMATCH: return "GDPA_ERR_PLAN_MISMATCH";
+        case GDPA_ERR_HIP: return "GDPA_ERR_HIP";
+        case GDPA_ERR_NOMEM: return "GDPA_ERR_NOMEM";
+    }
+    return "GDPA_ERR_UNKNOWN";
+}
+
+const char* gdpa_last_error(void) { return g_err.c_str(); }
+
+double gdpa_gelu_poly_bound(void) { return GDPA_GELU_POLY_BOUND; }
+
+gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_host, int B, int H,
+                             int d, int window, gdpa_dtype dtype, const gdpa_plan_opts* opts,
+                             gdpa_plan* out) {
+    g_err.clear();
+    if (!out) return fail(GDPA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!q_off_host || !kv_off_host) return fail(GDPA_ERR_INVALID_ARG, "offsets are NULL");
+    if (B < 0) return fail(GDPA_ERR_INVALID_ARG, "B < 0");
+    if (H < 1 || H > 65535) return fail(GDPA_ERR_INVALID_ARG, "H out of range [1, 65535]");
+    if (window < 0) return fail(GDPA_ERR_INVALID_ARG, "window < 0");
+    if (dtype != GDPA_F32 && dtype != GDPA_BF16 && dtype != GDPA_BF16_F32OUT)
+        return fail(GDPA_ERR_INVALID_ARG, "unknown dtype");
+    if (d != 32 && d != 64 && d != 128) return fail(GDPA_ERR_UNSUPPORTED, "d must be 32, 64 or 128");
+    gdpa_plan_opts o{};
+    if (opts) o = *opts;
+    for (int l = 0; l < 3; ++l) {
+        if (o.bins[l] < 0) return fail(GDPA_ERR_INVALID_ARG, "bins < 0");
+        if (o.waves[l] != 0 && o.waves[l] != 1 && o.waves[l] != 2 && o.waves[l] != 4)
+            return fail(GDPA_ERR_INVALID_ARG, "waves must be 0, 1, 2 or 4");
+    }
+    if (o.bnw_fwd != 0 && o.bnw_fwd != 32 && o.bnw_fwd != 64)
+        return fail(GDPA_ERR_INVALID_ARG, "bnw_fwd must be 0, 32 or 64");
+
+    if (q_off_host[0] != 0 || kv_off_host[0] != 0)
+        return fail(GDPA_ERR_BAD_OFFSETS, "offsets must start at 0");
+    std::vector<int64_t> lq(B), lk(B);
+    const int64_t elem_out = (dtype == GDPA_BF16) ? 2 : 4;
+    for (int b = 0; b < B; ++b) {
+        lq[b] = (int64_t)q_off_host[b + 1] - q_off_host[b];
+        lk[b] = (int64_t)kv_off_host[b + 1] - kv_off_host[b];
+        if (lq[b] < 0 || lk[b] < 0)
+            return fail(GDPA_ERR_BAD_OFFSETS, "offsets decrease at sample " + std::to_string(b));
+        if (window > 0 && lq[b] != lk[b])
+            return fail(GDPA_ERR_BAD_OFFSETS, "a window needs Lq == Lk; sample " + std::to_string(b) + " differs");
+        // every (sample, head) slice is addressed with 32-bit byte offsets
+        if (std::max(lq[b], lk[b]) * (int64_t)H * d * elem_out >= (int64_t)1 << 31)
+            return fail(GDPA_ERR_UNSUPPORTED, "sample " + std::to_string(b) + " exceeds 2 GiB per head slice");
+    }
+
+    gdpa_plan_s* p = new (std::nothrow) gdpa_plan_s;
+    if (!p) return fail(GDPA_ERR_NOMEM, "plan allocation");
+    p->B = B;
+    p->H = H;
+    p->d = d;
+    p->window = window;
+    p->dtype = dtype;
+    p->host_only = o.host_only != 0;
+    p->q_off.assign(q_off_host, q_off_host + B + 1);
+    p->kv_off.assign(kv_off_host, kv_off_host + B + 1);
+    p->lq = lq;
+    p->lk = lk;
+    p->Tq = q_off_host[B];
+    p->Tk = kv_off_host[B];
+    for (int b = 0; b < B; ++b) p->valid_pairs += pairs_of(lq[b], lk[b], window);
+
+    Layout L = auto_layout(lq, lk);
+    for (int l = 0; l < 3; ++l)
+        if (o.waves[l]) L.waves[l] = o.waves[l];
+    if (o.waves[LIST_FWD] && !o.bnw_fwd) L.bnw[LIST_FWD] = 32;
+    if (o.bnw_fwd) L.bnw[LIST_FWD] = o.bnw_fwd;
+    if (L.bnw[LIST_FWD] == 64 && L.waves[LIST_FWD] != 4) {
+        delete p;
+        return fail(GDPA_ERR_INVALID_ARG, "bnw_fwd = 64 needs 4 q waves");
+    }
+
+    int cus = 256;
+    if (!p->host_only) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) {
+            delete p;
+            return fail_hip(e, "device query");
+        }
+    }
+    for (int l = 0; l < 3; ++l) {
+        int P = o.bins[l];
+        if (P == 0) {
+            P = cus;
+            if (!p->host_only && dtype != GDPA_F32) {
+                const void* f = l == LIST_FWD ? fwd_kernel_ptr(d, L.waves[l], L.bnw[l], GDPA_ACT_GELU)
+                              : l == LIST_DQ  ? dq_kernel_ptr(d, L.waves[l], GDPA_ACT_GELU)
+                                              : dkdv_kernel_ptr(d, L.waves[l], GDPA_ACT_GELU);
+                int per_cu = 0;
+                if (f && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 256, 0) == hipSuccess &&
+                    per_cu > 0)
+                    P = cus * per_cu;
+            }
+        }
+        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.waves[l], L.bnw[l], o.round_robin == 0);
+    }
+
+    if (!p->host_only) {
+        for (int l = 0; l < 3; ++l) {
+            const WorkList& wl = p->lists[l];
+            const size_t ni = std::max<size_t>(1, wl.items.size());
+            hipError_t e = hipMalloc((void**)&p->d_items[l], ni * sizeof(Item));
+            if (e == hipSuccess) e = hipMalloc((void**)&p->d_bin_ptr[l], wl.bin_ptr.size() * sizeof(int32_t));
+            if (e == hipSuccess && !wl.items.empty())
+                e = hipMemcpy(p->d_items[l], wl.items.data(), wl.items.size() * sizeof(Item), hipMemcpyHostToDevice);
+            if (e == hipSuccess)
+                e = hipMemcpy(p->d_bin_ptr[l], wl.bin_ptr.data(), wl.bin_ptr.size() * sizeof(int32_t),
+                              hipMemcpyHostToDevice);
+            if (e != hipSuccess) {
+                delete p;
+                return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "work list upload")
+                                                : fail_hip(e, "work list upload");
+            }
+        }
+    }
+    *out = p;
+    return GDPA_OK;
+}
+
+void gdpa_plan_destroy(gdpa_plan plan) { delete plan; }
+
+gdpa_status gdpa_plan_export(gdpa_plan plan, int list, int32_t* buf, size_t* n) {
+    g_err.clear();
+    if (!plan || !n) return fail(GDPA_ERR_INVALID_ARG, "plan or n is NULL");
+    if (list < 0 || list > 2) return fail(GDPA_ERR_INVALID_ARG, "list must be 0, 1 or 2");
+    const std::vector<int32_t> v = export_list(plan->lists[list]);
+    if (!buf) {
+        *n = v.size();
+        return GDPA_OK;
+    }
+    if (*n < v.size()) {
+        *n = v.size();
+        return fail(GDPA_ERR_INVALID_ARG, "buffer too small");
+    }
+    std::memcpy(buf, v.data(), v.size() * sizeof(int32_t));
+    *n = v.size();
+    return GDPA_OK;
+}
+
+gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
+    g_err.clear();
+    if (!plan || !out) return fail(GDPA_ERR_INVALID_ARG, "plan or out is NULL");
+    std::memset(out, 0, sizeof(*out));
+    out->Tq = plan->Tq;
+    out->Tk = plan->Tk;
+    out->valid_pairs = plan->valid_pairs;
+    for (int l = 0; l < 3; ++l) {
+        const WorkList& wl = plan->lists[l];
+        out->n_items[l] = (int32_t)wl.items.size();
+        out->n_steps[l] = (int32_t)wl.n_steps;
+        out->bins[l] = wl.P;
+        out->tile_stat[l] = wl.t_stat;
+        out->tile_strm[l] = wl.t_strm;
+        if (!wl.bin_cost.empty()) {
+            out->bin_cost_max[l] = *std::max_element(wl.bin_cost.begin(), wl.bin_cost.end());
+            out->bin_cost_min[l] = *std::min_element(wl.bin_cost.begin(), wl.bin_cost.end());
+        }
+    }
+    return GDPA_OK;
+}
+
+static gdpa_status check_call(gdpa_plan plan, const int32_t* q_off_dev, const int32_t* kv_off_dev, int B,
+                              int H, int d, gdpa_act act, int window) {
+    if (!plan) return fail(GDPA_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->host_only) return fail(GDPA_ERR_PLAN_MISMATCH, "host-only plan cannot run kernels");
+    if (B != plan->B || H != plan->H || d != plan->d || window != plan->window)
+        return fail(GDPA_ERR_PLAN_MISMATCH, "B, H, d or window differ from the plan");
+    if ((int)act < 0 || (int)act > GDPA_ACT_ONE) return fail(GDPA_ERR_INVALID_ARG, "unknown activation");
+    if (!q_off_dev || !kv_off_dev) return fail(GDPA_ERR_INVALID_ARG, "device offsets are NULL");
+    if (debug_enabled()) {
+        std::vector<int32_t> hq(B + 1), hk(B + 1);
+        hipError_t e = hipMemcpy(hq.data(), q_off_dev, (B + 1) * sizeof(int32_t), hipMemcpyDeviceToHost);
+        if (e == hipSuccess)
+            e = hipMemcpy(hk.data(), kv_off_dev, (B + 1) * sizeof(int32_t), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail_hip(e, "GDPA_DEBUG offset check");
+        if (hq != plan->q_off || hk != plan->kv_off)
+            return fail(GDPA_ERR_PLAN_MISMATCH, "device offsets differ from the plan's");
+    }
+    return GDPA_OK;
+}
+
+static KernelArgs base_args(gdpa_plan plan, const int32_t* q_off_dev, const int32_t* kv_off_dev) {
+    KernelArgs a{};
+    a.q_off = q_off_dev;
+    a.kv_off = kv_off_dev;
+    a.B = plan->B;
+    a.H = plan->H;
+    a.window = plan->window;
+    a.scale = 1.0f / std::sqrt((float)plan->d);
+    a.out_f32 = plan->dtype != GDPA_BF16;
+    return a;
+}
+
+gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v,
+                     const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                     gdpa_act act, int window, void* o, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
+    if (st != GDPA_OK) return st;
+    if (plan->Tq > 0 && (!q || !o)) return fail(GDPA_ERR_INVALID_ARG, "q or o is NULL");
+    if (plan->Tk > 0 && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
+    if (plan->Tq == 0) return GDPA_OK;
+    hipStream_t s = (hipStream_t)stream;
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    hipError_t e;
+    if (plan->dtype == GDPA_F32) {
+        e = launch_fwd_f32(a, (int)plan->Tq, d, act, s);
+    } else {
+        const WorkList& wl = plan->lists[LIST_FWD];
+        a.items = plan->d_items[LIST_FWD];
+        a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+        a.P = wl.P;
+        switch (d) {
+            case 32: e = launch_fwd_bf16_d32(a, wl.waves, wl.bnw, act, s); break;
+            case 64: e = launch_fwd_bf16_d64(a, wl.waves, wl.bnw, act, s); break;
+            default: e = launch_fwd_bf16_d128(a, wl.waves, wl.bnw, act, s); break;
+        }
+    }
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no forward kernel for this configuration");
+    if (e != hipSuccess) return fail_hip(e, "forward launch");
+    return GDPA_OK;
+}
+
+gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                     const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                     gdpa_act act, int window, void* dq, void* dk, void* dv, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
+    if (st != GDPA_OK) return st;
+    if (act == GDPA_ACT_ONE) return fail(GDPA_ERR_UNSUPPORTED, "GDPA_ACT_ONE has no backward");
+    if (plan->Tq > 0 && (!q || !dout || !dq)) return fail(GDPA_ERR_INVALID_ARG, "q, dout or dq is NULL");
+    if (plan->Tk > 0 && (!k || !v || !dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "k, v, dk or dv is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    hipError_t e = hipSuccess;
+    if (plan->dtype == GDPA_F32) {
+        e = launch_bwd_f32(a, (int)plan->Tq, (int)plan->Tk, d, act, s);
+    } else {
+        // dK/dV (KV-stationary) then dQ (Q-stationary), stream-ordered
+        if (plan->Tk > 0) {
+            const WorkList& wl = plan->lists[LIST_DKDV];
+            KernelArgs b = a;
+            b.items = plan->d_items[LIST_DKDV];
+            b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+            b.P = wl.P;
+            switch (d) {
+                case 32: e = launch_dkdv_bf16_d32(b, wl.waves, act, s); break;
+                case 64: e = launch_dkdv_bf16_d64(b, wl.waves, act, s); break;
+                default: e = launch_dkdv_bf16_d128(b, wl.waves, act, s); break;
+            }
+        }
+        if (e == hipSuccess && plan->Tq > 0) {
+            const WorkList& wl = plan->lists[LIST_DQ];
+            KernelArgs b = a;
+            b.items = plan->d_items[LIST_DQ];
+            b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+            b.P = wl.P;
+            switch (d) {
+                case 32: e = launch_dq_bf16_d32(b, wl.waves, act, s); break;
+                case 64: e = launch_dq_bf16_d64(b, wl.waves, act, s); break;
+                default: e = launch_dq_bf16_d128(b, wl.waves, act, s); break;
+            }
+        }
+    }
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no backward kernel for this configuration");
+    if (e != hipSuccess) return fail_hip(e, "backward launch");
+    return GDPA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Kernel arguments and launchers shared between the HIP kernels and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.hpp"
+
+namespace gdpa {
+
+// Arguments common to every kernel.  Tensors are [T, H, d] row-major; a work
+// list is (items, bin_ptr) over P persistent workgroups.
+struct KernelArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    void* o;    // forward output
+    void* dq;
+    void* dk;
+    void* dv;
+    const int32_t* q_off;
+    const int32_t* kv_off;
+    const Item* items;
+    const int32_t* bin_ptr;
+    int P;          // persistent workgroups = bins
+    int B;          // samples
+    int H;
+    int window;     // 0 = none
+    float scale;    // 1 / sqrt(d)
+    int out_f32;    // outputs stored as fp32 instead of bf16
+};
+
+// bf16 MFMA kernels, one translation unit per head dimension
+#define GDPA_DECLARE_LAUNCHERS(D)                                                                   \
+    hipError_t launch_fwd_bf16_d##D(const KernelArgs& a, int waves, int bnw, int act, hipStream_t s); \
+    hipError_t launch_dq_bf16_d##D(const KernelArgs& a, int waves, int act, hipStream_t s);           \
+    hipError_t launch_dkdv_bf16_d##D(const KernelArgs& a, int waves, int act, hipStream_t s);         \
+    const void* fwd_bf16_kernel_ptr_d##D(int waves, int bnw, int act);                                \
+    const void* dq_bf16_kernel_ptr_d##D(int waves, int act);                                          \
+    const void* dkdv_bf16_kernel_ptr_d##D(int waves, int act);
+GDPA_DECLARE_LAUNCHERS(32)
+GDPA_DECLARE_LAUNCHERS(64)
+GDPA_DECLARE_LAUNCHERS(128)
+#undef GDPA_DECLARE_LAUNCHERS
+
+// plain fp32 kernels (no MFMA): forward, dQ, dK/dV over the offsets directly
+hipError_t launch_fwd_f32(const KernelArgs& a, int Tq, int d, int act, hipStream_t s);
+hipError_t launch_bwd_f32(const KernelArgs& a, int Tq, int Tk, int d, int act, hipStream_t s);
+
+}  // namespace gdpa

@@ -1,0 +1,136 @@
+// Host tile planner (see plan.hpp for the rules and the source they follow).
+#include "plan.hpp"
+
+#include <algorithm>
+#include <numeric>
+
+namespace gdpa {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk) {
+    int64_t nq = 0, nk = 0, sq = 0, sk = 0, max_lk = 0;
+    for (size_t b = 0; b < lq.size(); ++b) {
+        nq += lq[b] > 0;
+        nk += lk[b] > 0;
+        sq += lq[b];
+        sk += lk[b];
+        max_lk = std::max(max_lk, lk[b]);
+    }
+    // waves along the stationary side from the mean non-empty length
+    auto waves = [](int64_t total, int64_t count) {
+        if (count == 0) return 4;
+        if (total <= 40 * count) return 1;
+        if (total <= 96 * count) return 2;
+        return 4;
+    };
+    Layout L;
+    const int wq = waves(sq, nq);
+    L.waves[LIST_FWD] = wq;
+    L.bnw[LIST_FWD] = (wq < 4 || max_lk <= 32) ? 32 : 64;
+    L.waves[LIST_DQ] = wq;
+    L.bnw[LIST_DQ] = 32;
+    L.waves[LIST_DKDV] = waves(sk, nk);
+    L.bnw[LIST_DKDV] = 32;
+    return L;
+}
+
+void tile_sizes(int kind, int waves, int bnw, int* t_stat, int* t_strm) {
+    *t_stat = 32 * waves;
+    *t_strm = (kind == LIST_DKDV) ? 32 * (4 / waves) : (4 / waves) * bnw;
+}
+
+namespace {
+struct Cand {
+    int64_t cost;
+    Item it;
+};
+}  // namespace
+
+WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
+                   int H, int window, int P, int waves, int bnw, bool zigzag) {
+    WorkList wl;
+    wl.kind = kind;
+    wl.P = P;
+    wl.waves = waves;
+    wl.bnw = bnw;
+    tile_sizes(kind, waves, bnw, &wl.t_stat, &wl.t_strm);
+    const int64_t TS = wl.t_stat, TR = wl.t_strm;
+
+    std::vector<Cand> cands;
+    for (size_t b = 0; b < lq.size(); ++b) {
+        const int64_t ls = (kind == LIST_DKDV) ? lk[b] : lq[b];
+        const int64_t lo = (kind == LIST_DKDV) ? lq[b] : lk[b];
+        const int64_t ntiles = ceil_div(ls, TS);
+        for (int h = 0; h < H; ++h) {
+            for (int64_t t = 0; t < ntiles; ++t) {
+                const int64_t a0 = t * TS;
+                const int64_t a1 = std::min(ls, a0 + TS) - 1;
+                int64_t s0, s1;
+                if (lo == 0) {
+                    s0 = 0;
+                    s1 = -1;
+                } else if (window == 0) {
+                    s0 = 0;
+                    s1 = ceil_div(lo, TR) - 1;
+                } else {
+                    const int64_t lo_row = std::max<int64_t>(0, a0 - window + 1);
+                    const int64_t hi_row = std::min<int64_t>(lo - 1, a1 + window - 1);
+                    s0 = lo_row / TR;
+                    s1 = hi_row / TR;
+                }
+                int64_t cost = a1 - a0 + 1;
+                for (int64_t s = s0; s <= s1; ++s)
+                    cost += std::min(lo, (s + 1) * TR) - s * TR + kStepCharge;
+                Cand c;
+                c.cost = cost;
+                c.it = Item{(int32_t)b, h, (int32_t)t, (int32_t)s0, (int32_t)s1, 0, 0, 0};
+                cands.push_back(c);
+            }
+        }
+    }
+    std::sort(cands.begin(), cands.end(), [](const Cand& x, const Cand& y) {
+        if (x.cost != y.cost) return x.cost > y.cost;
+        if (x.it.b != y.it.b) return x.it.b < y.it.b;
+        if (x.it.h != y.it.h) return x.it.h < y.it.h;
+        return x.it.t < y.it.t;
+    });
+
+    // zigzag (or round-robin) deal, then a bin-major CSR keeping deal order
+    std::vector<int32_t> bin_of(cands.size());
+    std::vector<int32_t> count(P, 0);
+    wl.bin_cost.assign(P, 0);
+    for (size_t r = 0; r < cands.size(); ++r) {
+        const int64_t rnd = (int64_t)r / P, pos = (int64_t)r % P;
+        const int p = (int)((!zigzag || rnd % 2 == 0) ? pos : P - 1 - pos);
+        bin_of[r] = p;
+        count[p]++;
+        wl.bin_cost[p] += cands[r].cost;
+    }
+    wl.bin_ptr.assign(P + 1, 0);
+    for (int p = 0; p < P; ++p) wl.bin_ptr[p + 1] = wl.bin_ptr[p] + count[p];
+    std::vector<int32_t> fill(wl.bin_ptr.begin(), wl.bin_ptr.end() - 1);
+    wl.items.resize(cands.size());
+    for (size_t r = 0; r < cands.size(); ++r) {
+        wl.items[fill[bin_of[r]]++] = cands[r].it;
+        const Item& it = cands[r].it;
+        if (it.s1 >= it.s0) wl.n_steps += it.s1 - it.s0 + 1;
+    }
+    return wl;
+}
+
+std::vector<int32_t> export_list(const WorkList& wl) {
+    std::vector<int32_t> out = {wl.P, (int32_t)wl.items.size(), wl.t_stat, wl.t_strm, wl.waves,
+                                wl.bnw};
+    out.insert(out.end(), wl.bin_ptr.begin(), wl.bin_ptr.end());
+    for (const Item& it : wl.items) {
+        out.push_back(it.b);
+        out.push_back(it.h);
+        out.push_back(it.t);
+        out.push_back(it.s0);
+        out.push_back(it.s1);
+    }
+    return out;
+}
+
+}  // namespace gdpa

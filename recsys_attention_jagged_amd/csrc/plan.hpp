@@ -1,0 +1,54 @@
+// Host tile planner for jagged GDPA.
+//
+// GDPA page (aitrends.kr/articles/26275, "Generalized Dot-Product Attention
+// (GDPA): kernel optimisation for real recommendation-system training loads"),
+// "Section details", jagged-input paragraph and zigzag scheduling diagram: the
+// host enumerates only the tiles that hold valid (query, key) pairs, sorts them
+// and deals them to the compute units in a zigzag so the per-unit load is even.
+//
+// A work item is (sample b, head h, stationary tile t) plus the contiguous range
+// [s0, s1] of streaming tiles it visits.  Q-stationary lists ("fwd", "dq") have
+// q tiles of 32*WQ rows and kv steps of (4/WQ)*BNW rows; the KV-stationary list
+// ("dkdv") has kv tiles of 32*WK rows and q steps of 32*(4/WK) rows.  Items whose
+// other side is empty get no steps and write zeros.
+//
+// Cost of an item: valid stationary rows + sum over steps of (valid streaming
+// rows + 32).  Order: cost descending, then (b, h, t).  Deal: the r-th item goes
+// to bin r mod P in even rounds and P-1 - (r mod P) in odd rounds.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+namespace gdpa {
+
+enum ListKind { LIST_FWD = 0, LIST_DKDV = 1, LIST_DQ = 2 };
+
+// One work item as the kernels read it (32 bytes, one scalar load).
+struct Item {
+    int32_t b, h, t, s0, s1, pad0, pad1, pad2;
+};
+static_assert(sizeof(Item) == 32, "Item must be 32 bytes");
+
+struct WorkList {
+    int kind = 0, P = 0, t_stat = 0, t_strm = 0, waves = 0, bnw = 0;
+    std::vector<int32_t> bin_ptr;   // P + 1
+    std::vector<Item> items;        // bin-major, deal order inside a bin
+    std::vector<int64_t> bin_cost;  // P
+    int64_t n_steps = 0;
+};
+
+struct Layout {
+    int waves[3];
+    int bnw[3];
+};
+
+constexpr int kStepCharge = 32;
+
+Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk);
+void tile_sizes(int kind, int waves, int bnw, int* t_stat, int* t_strm);
+WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
+                   int H, int window, int P, int waves, int bnw, bool zigzag);
+std::vector<int32_t> export_list(const WorkList& wl);
+
+}  // namespace gdpa

@@ -1,0 +1,168 @@
+"""CPU tests of the C ABI: the library loads and exports every declared symbol,
+host-only plans match the reference planner bit for bit, and argument errors are
+reported before anything touches a device.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import recsys_attention_jagged_amd as G
+from gdpa_workloads import WORKLOADS, offsets, workload_lengths
+from oracle import plan_ref as PR
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdpa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdpa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = G.load_library()
+    names = declared_functions()
+    assert "gdpa_fwd" in names and "gdpa_bwd" in names and "gdpa_plan_create" in names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings_and_poly_bound():
+    for code, name in G.STATUS.items():
+        assert G.gdpa_status_string(code) == name
+    assert 0 < G.gdpa_gelu_poly_bound() < 1e-4
+
+
+def _host_plan(lq, lk, H, d, window, P=256, waves=(0, 0, 0), bnw=0, rr=False):
+    qo, ko = offsets(lq), offsets(lk)
+    return G.gdpa_plan_create(qo, ko, len(lq), H, d, window, "bf16", host_only=True,
+                              bins=(P, P, P), waves=waves, bnw_fwd=bnw, round_robin=rr)
+
+
+def _ref_exports(lq, lk, H, window, P, layout=None, zigzag=True):
+    layout = layout or PR.auto_layout(list(lq), list(lk), window)
+    return {kind: PR.export(PR.plan_list(kind, list(lq), list(lk), H, window, P, *layout[kind], zigzag=zigzag))
+            for kind in PR.LISTS}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_plan_bit_exact_vs_reference_on_workloads(cfg):
+    w = WORKLOADS[cfg]
+    lq, lk = workload_lengths(cfg)
+    lq, lk = [int(x) for x in lq], [int(x) for x in lk]
+    plan = _host_plan(lq, lk, w["H"], w["d"], w["window"])
+    try:
+        ref = _ref_exports(lq, lk, w["H"], w["window"], 256)
+        for kind in PR.LISTS:
+            got = G.gdpa_plan_export(plan, kind)
+            np.testing.assert_array_equal(got, np.asarray(ref[kind], dtype=np.int32), err_msg=kind)
+        st = G.gdpa_plan_stats(plan)
+        assert st["Tq"] == sum(lq) and st["Tk"] == sum(lk)
+    finally:
+        G.gdpa_plan_destroy(plan)
+
+
+EDGE = [
+    ([0, 0, 0], [0, 0, 0], 0),
+    ([1], [1], 0),
+    ([5, 0, 70, 1, 33, 200], [64, 3, 0, 2, 129, 31], 0),
+    ([70, 1, 33, 200, 0, 513], [70, 1, 33, 200, 0, 513], 9),
+    ([31, 32, 33, 63, 64, 65, 127, 128, 129], [129, 128, 127, 65, 64, 63, 33, 32, 31], 0),
+]
+
+
+@pytest.mark.parametrize("lq,lk,window", EDGE)
+@pytest.mark.parametrize("waves,bnw", [((1, 1, 1), 32), ((2, 2, 2), 32), ((4, 4, 4), 32), ((4, 4, 4), 64)])
+@pytest.mark.parametrize("P,rr", [(1, False), (7, False), (256, False), (16, True)])
+def test_plan_bit_exact_vs_reference_edge_cases(lq, lk, window, waves, bnw, P, rr):
+    plan = _host_plan(lq, lk, 3, 64, window, P=P, waves=waves, bnw=bnw, rr=rr)
+    try:
+        layout = {"fwd": (waves[0], bnw), "dkdv": (waves[1], 32), "dq": (waves[2], 32)}
+        ref = _ref_exports(lq, lk, 3, window, P, layout, zigzag=not rr)
+        for kind in PR.LISTS:
+            np.testing.assert_array_equal(G.gdpa_plan_export(plan, kind), np.asarray(ref[kind], np.int32))
+    finally:
+        G.gdpa_plan_destroy(plan)
+
+
+def test_plan_stats_valid_pairs_and_balance():
+    lq, lk = workload_lengths(5, B=16)
+    plan = _host_plan(lq, lk, 4, 128, 128)
+    try:
+        st = G.gdpa_plan_stats(plan)
+        from oracle.gdpa_ref import useful_pairs
+        assert st["valid_pairs"] == useful_pairs(lq, lk, 128)
+        assert all(b == 256 for b in st["bins"])
+    finally:
+        G.gdpa_plan_destroy(plan)
+
+
+# ---------------------------------------------------------------------------
+# error paths (forced from the host)
+# ---------------------------------------------------------------------------
+
+def _status_of(fn, *args, **kw):
+    with pytest.raises(G.GdpaError) as e:
+        fn(*args, **kw)
+    return e.value.status
+
+
+def test_create_rejects_bad_arguments():
+    qo = offsets([3, 4])
+    bad = lambda **kw: _status_of(G.gdpa_plan_create, kw.pop("qo", qo), kw.pop("ko", qo), kw.pop("B", 2),
+                                  kw.pop("H", 2), kw.pop("d", 64), kw.pop("window", 0),
+                                  kw.pop("dtype", "bf16"), host_only=True, **kw)
+    assert bad(d=48) == 3                      # UNSUPPORTED
+    assert bad(d=256) == 3
+    assert bad(H=0) == 1                       # INVALID_ARG
+    assert bad(window=-1) == 1
+    assert bad(dtype=7) == 1
+    assert bad(waves=(3, 0, 0)) == 1
+    assert bad(bnw_fwd=48) == 1
+    assert bad(waves=(2, 0, 0), bnw_fwd=64) == 1
+    assert bad(qo=np.array([1, 3, 7], np.int32)) == 2           # BAD_OFFSETS: not starting at 0
+    assert bad(qo=np.array([0, 5, 3], np.int32)) == 2           # decreasing
+    assert bad(ko=offsets([3, 5]), window=4) == 2               # window with Lq != Lk
+    lib = G.load_library()
+    out = ctypes.c_void_p()
+    assert lib.gdpa_plan_create(None, None, 1, 1, 64, 0, 1, None, ctypes.byref(out)) == 1
+    assert lib.gdpa_plan_create(qo.ctypes.data, qo.ctypes.data, 2, 1, 64, 0, 1, None, None) == 1
+    assert "NULL" in G.gdpa_last_error()
+
+
+def test_calls_reject_host_only_and_mismatched_plans():
+    qo = offsets([3, 4])
+    plan = G.gdpa_plan_create(qo, qo, 2, 2, 64, 0, "bf16", host_only=True)
+    try:
+        fake = 1 << 20   # never dereferenced: validation fails first
+        assert _status_of(G.gdpa_fwd, plan, fake, fake, fake, fake, fake, 2, 2, 64, "gelu", 0, fake, 0) == 4
+        assert _status_of(G.gdpa_bwd, plan, fake, fake, fake, fake, fake, fake, 2, 2, 64, "gelu", 0,
+                          fake, fake, fake, 0) == 4
+        assert _status_of(G.gdpa_fwd, None, fake, fake, fake, fake, fake, 2, 2, 64, "gelu", 0, fake, 0) == 1
+        assert _status_of(G.gdpa_plan_export, plan, 5) == 1
+    finally:
+        G.gdpa_plan_destroy(plan)
+    G.gdpa_plan_destroy(None)
+
+
+def test_oversized_sample_is_unsupported():
+    qo = np.array([0, 1 << 22], np.int32)     # 4M rows x 8 heads x 128 x 2 B > 2 GiB per slice
+    assert _status_of(G.gdpa_plan_create, qo, qo, 1, 8, 128, 0, "bf16", host_only=True) == 3
+
+
+def test_export_capacity_check():
+    qo = offsets([300])
+    plan = G.gdpa_plan_create(qo, qo, 1, 1, 64, 0, "bf16", host_only=True)
+    try:
+        lib = G.load_library()
+        n = ctypes.c_size_t(0)
+        assert lib.gdpa_plan_export(plan, 0, None, ctypes.byref(n)) == 0 and n.value > 0
+        small = np.zeros(2, np.int32)
+        m = ctypes.c_size_t(2)
+        assert lib.gdpa_plan_export(plan, 0, small.ctypes.data, ctypes.byref(m)) == 1
+        assert m.value == n.value
+    finally:
+        G.gdpa_plan_destroy(plan)

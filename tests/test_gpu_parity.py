@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Tolerances (stated with the task's definition of the path):
+  * fp32 path: max |err| <= 1e-4 * max |ref|
+  * bf16 in / fp32 accumulate: relative L2 <= 1e-2 and max |err| <= 2e-2 * max |ref|,
+    for O and separately for each of dQ, dK, dV.
+  * the polynomial GELU against the exact-erf oracle: the bf16 bounds plus the
+    fit's bound propagated through the second product (eps * sum_j |V_j| per
+    element for O; eps' * sum |dP| |K| style terms for the gradients).
+Offset indexing is checked bit-exactly with count probes (act = one, fp32 outputs).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import recsys_attention_jagged_amd as G
+from gdpa_workloads import WORKLOADS, make_from_lengths, make_workload, offsets
+from oracle import gdpa_ref as R
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def dev_offsets(inp):
+    return (torch.tensor(inp.q_off, dtype=torch.int32, device=DEV),
+            torch.tensor(inp.kv_off, dtype=torch.int32, device=DEV))
+
+
+def check_close(got, ref, what, f32=False, extra=None):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, what
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    mx = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = np.abs(got - ref)
+    if extra is not None:
+        err = np.maximum(err - extra, 0.0)
+    if f32:
+        assert float(err.max(initial=0.0)) <= 1e-4 * mx + 1e-30, f"{what}: max err {err.max():.3e} vs max|ref| {mx:.3e}"
+        return
+    nrm = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(err)) / nrm if nrm > 0 else float(np.linalg.norm(err))
+    assert rel <= 1e-2, f"{what}: rel L2 {rel:.3e}"
+    assert float(err.max(initial=0.0)) <= 2e-2 * mx + 1e-30, f"{what}: max err {err.max():.3e} vs 2e-2*{mx:.3e}"
+
+
+def run_fwd(inp, act=None, dtype=None, **opts):
+    act = act or inp.act
+    dtype = dtype or inp.dtype
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, dtype, **opts) as plan:
+        o = plan.fwd(inp.q, inp.k, inp.v, qo, ko, act)
+        torch.cuda.synchronize()
+    return o.float().cpu().numpy()
+
+
+def run_bwd(inp, act=None, dtype=None, **opts):
+    act = act or inp.act
+    dtype = dtype or inp.dtype
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, dtype, **opts) as plan:
+        dq, dk, dv = plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, act)
+        torch.cuda.synchronize()
+    return tuple(t.float().cpu().numpy() for t in (dq, dk, dv))
+
+
+def oracle_fwd(inp, act=None):
+    return R.gdpa_fwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_off, inp.kv_off, act or inp.act,
+                      inp.window)
+
+
+def oracle_bwd(inp, act=None):
+    return R.gdpa_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do"), inp.q_off, inp.kv_off,
+                      act or inp.act, inp.window)
+
+
+# ---------------------------------------------------------------------------
+# workloads at reduced batch (several tiles and ragged tails each)
+# ---------------------------------------------------------------------------
+
+SMALL_B = {2: 48, 3: 24, 4: 12, 5: 3}
+
+
+def test_cfg1_fp32_forward():
+    say("cfg1 fp32 forward, full size")
+    inp = make_workload(1, device=DEV)
+    check_close(run_fwd(inp), oracle_fwd(inp), "cfg1 O", f32=True)
+
+
+def test_fp32_backward():
+    say("fp32 backward on cfg1 shapes")
+    inp = make_workload(1, device=DEV)
+    g = run_bwd(inp)
+    r = oracle_bwd(inp)
+    for name, a, b in zip(("dQ", "dK", "dV"), g, r):
+        check_close(a, b, f"fp32 {name}", f32=True)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_workload_forward_small(cfg):
+    say(f"cfg{cfg} forward, B={SMALL_B[cfg]}")
+    inp = make_workload(cfg, device=DEV, B=SMALL_B[cfg])
+    check_close(run_fwd(inp), oracle_fwd(inp), f"cfg{cfg} O")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_workload_backward_small(cfg):
+    say(f"cfg{cfg} backward, B={SMALL_B[cfg]}")
+    inp = make_workload(cfg, device=DEV, B=SMALL_B[cfg])
+    g = run_bwd(inp)
+    r = oracle_bwd(inp)
+    for name, a, b in zip(("dQ", "dK", "dV"), g, r):
+        check_close(a, b, f"cfg{cfg} {name}")
+
+
+# ---------------------------------------------------------------------------
+# every wave layout, head dimension and activation
+# ---------------------------------------------------------------------------
+
+RAGGED = [0, 1, 5, 31, 32, 33, 64, 65, 100, 127, 128, 129, 200, 300]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("waves,bnw", [(1, 32), (2, 32), (4, 32), (4, 64)])
+def test_layouts_forward(d, waves, bnw):
+    say(f"forward layout d={d} waves={waves} bnw={bnw}")
+    rng = np.random.default_rng(d + waves)
+    lq = rng.permutation(RAGGED)
+    lk = rng.permutation(RAGGED)
+    inp = make_from_lengths(lq, lk, 2, d, act="gelu", seed=3, device=DEV)
+    check_close(run_fwd(inp, waves=(waves, 0, 0), bnw_fwd=bnw), oracle_fwd(inp), f"O d={d} w={waves}/{bnw}")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("waves", [1, 2, 4])
+def test_layouts_backward(d, waves):
+    say(f"backward layout d={d} waves={waves}")
+    rng = np.random.default_rng(10 * d + waves)
+    lq = rng.permutation(RAGGED)
+    lk = rng.permutation(RAGGED)
+    inp = make_from_lengths(lq, lk, 2, d, act="silu", seed=4, device=DEV)
+    g = run_bwd(inp, waves=(0, waves, waves))
+    r = oracle_bwd(inp)
+    for name, a, b in zip(("dQ", "dK", "dV"), g, r):
+        check_close(a, b, f"{name} d={d} w={waves}")
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu", "gelu_taylor6", "identity"])
+def test_activations_forward_backward(act):
+    say(f"activation {act}")
+    inp = make_from_lengths([40, 130, 7, 260], [77, 20, 300, 129], 2, 64, act=act, seed=5, device=DEV)
+    check_close(run_fwd(inp), oracle_fwd(inp), f"O {act}")
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp), oracle_bwd(inp)):
+        check_close(a, b, f"{name} {act}")
+
+
+@pytest.mark.parametrize("window", [1, 2, 17, 128, 1000])
+@pytest.mark.parametrize("waves", [1, 4])
+def test_windows(window, waves):
+    say(f"window {window} waves {waves}")
+    L = [1, 33, 128, 129, 700, 0, 300]
+    inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, seed=6, device=DEV)
+    check_close(run_fwd(inp, waves=(waves, waves, waves)), oracle_fwd(inp), f"O w={window}")
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, waves=(waves, waves, waves)), oracle_bwd(inp)):
+        check_close(a, b, f"{name} w={window}")
+
+
+def test_empty_and_degenerate():
+    say("empty samples, Lk=0, Lq=0, empty batch")
+    lq = [0, 5, 0, 40, 3]
+    lk = [7, 0, 0, 90, 1]
+    inp = make_from_lengths(lq, lk, 3, 64, act="gelu", seed=7, device=DEV)
+    o = run_fwd(inp)
+    check_close(o, oracle_fwd(inp), "O degenerate")
+    assert np.all(o[0:5] == 0.0)                         # sample 1 has no keys
+    dq, dk, dv = run_bwd(inp)
+    rq, rk, rv = oracle_bwd(inp)
+    assert np.all(dk[0:7] == 0.0) and np.all(dv[0:7] == 0.0)   # sample 0 has no queries
+    assert np.all(dq[0:5] == 0.0)
+    for name, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), (rq, rk, rv)):
+        check_close(a, b, f"{name} degenerate")
+    # a batch with no rows at all
+    z = make_from_lengths([0, 0], [0, 0], 2, 64, seed=1, device=DEV)
+    assert run_fwd(z).shape == (0, 2, 64)
+
+
+def test_outputs_fully_written():
+    say("every output row is written (buffers pre-filled with NaN)")
+    inp = make_from_lengths([0, 3, 70, 1], [5, 0, 33, 2], 2, 64, act="silu", seed=8, device=DEV)
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, 2, 64, 0, "bf16") as plan:
+        o = torch.full_like(inp.q, float("nan"))
+        dq = torch.full_like(inp.q, float("nan"))
+        dk = torch.full_like(inp.k, float("nan"))
+        dv = torch.full_like(inp.v, float("nan"))
+        plan.fwd(inp.q, inp.k, inp.v, qo, ko, "silu", o=o)
+        plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "silu", dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+
+
+# ---------------------------------------------------------------------------
+# bit-exact offset indexing: count and bit probes
+# ---------------------------------------------------------------------------
+
+def _probe_expect(lq, lk, window, bit=None):
+    """Per query row: number of valid keys (bit=None) or of valid keys whose local
+    index has bit `bit` set.  Brute force over the valid set."""
+    out = []
+    for a, c in zip(lq, lk):
+        m = R.valid_mask(np.arange(a), np.arange(c), a, c, window)
+        if bit is not None:
+            m = m & (((np.arange(c) >> bit) & 1) == 1)[None, :]
+        out.append(m.sum(axis=1))
+    return np.concatenate(out) if out else np.zeros(0)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+@pytest.mark.parametrize("waves", [1, 2, 4])
+def test_index_probe_bit_exact(window, waves):
+    say(f"count/bit probe window={window} waves={waves}")
+    L = [1, 31, 32, 33, 127, 128, 129, 600, 0, 1100] if window else None
+    lq = L or [3, 31, 32, 33, 0, 128, 129, 257, 40, 1]
+    lk = L or [129, 1, 64, 0, 5, 300, 33, 257, 511, 2]
+    d = 32
+    inp = make_from_lengths(lq, lk, 2, d, act="one", window=window, seed=9, device=DEV)
+    # V[j, h, e] = bit e of the key's local index j (e < 16); V[j, h, 16:] = 1
+    vals = []
+    for c in lk:
+        j = np.arange(c)[:, None]
+        bits = ((j >> np.arange(16)[None, :]) & 1).astype(np.float32)
+        vals.append(np.concatenate([bits, np.ones((c, d - 16), np.float32)], axis=1))
+    V = np.concatenate(vals) if vals else np.zeros((0, d), np.float32)
+    inp.v = torch.tensor(np.repeat(V[:, None, :], 2, axis=1), dtype=torch.bfloat16, device=DEV)
+    o = run_fwd(inp, act="one", dtype="bf16_f32out", waves=(waves, 0, 0))
+    cnt = _probe_expect(lq, lk, window)
+    for h in range(2):
+        np.testing.assert_array_equal(o[:, h, 16], cnt)
+        for e in range(16):
+            np.testing.assert_array_equal(o[:, h, e], _probe_expect(lq, lk, window, bit=e))
+
+
+# ---------------------------------------------------------------------------
+# the polynomial GELU against the exact-erf oracle
+# ---------------------------------------------------------------------------
+
+def test_gelu_poly_within_stated_bound():
+    say("poly GELU vs exact-erf oracle, windowed shapes")
+    L = [700, 1300, 129]
+    inp = make_from_lengths(L, L, 2, 128, act="gelu", window=128, seed=11, device=DEV)
+    eps = G.gdpa_gelu_poly_bound()
+    o = run_fwd(inp, act="gelu_poly")
+    ref = oracle_fwd(inp, "gelu")
+    # |sum_j (P'_ij - P_ij) V_j| <= eps sum_j |V_j| over the valid keys of row i
+    absv = np.abs(inp.f64("v"))
+    bound = R.gdpa_fwd(inp.f64("q"), inp.f64("k"), absv, inp.q_off, inp.kv_off, "one", inp.window) * eps
+    check_close(o, ref, "O poly", extra=bound)
+    # taylor6 is the pages' series; against its own definition it must meet the bf16 bound
+    check_close(run_fwd(inp, act="gelu_taylor6"), oracle_fwd(inp, "gelu_taylor6"), "O taylor6")
+
+
+# ---------------------------------------------------------------------------
+# full sizes, in the launch configuration the benchmark times: sampled rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled(cfg):
+    w = WORKLOADS[cfg]
+    say(f"cfg{cfg} full size (B={w['B']}), fwd + bwd, sampled samples")
+    inp = make_workload(cfg, device=DEV)
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16") as plan:
+        o = plan.fwd(inp.q, inp.k, inp.v, qo, ko, inp.act)
+        dq, dk, dv = plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, inp.act)
+        torch.cuda.synchronize()
+    rng = np.random.default_rng(cfg)
+    B = len(inp.lq)
+    picks = sorted(set(rng.choice(B, size=min(4, B), replace=False).tolist()
+                       + [int(np.argmax(inp.lq)), int(np.argmax(inp.lk))]))
+    for b in picks:
+        qs, qe = int(inp.q_off[b]), int(inp.q_off[b + 1])
+        ks, ke = int(inp.kv_off[b]), int(inp.kv_off[b + 1])
+        f = lambda t, a, e: t[a:e].to("cpu", torch.float64).numpy()
+        one_q = np.array([0, qe - qs])
+        one_k = np.array([0, ke - ks])
+        q64, k64, v64, do64 = f(inp.q, qs, qe), f(inp.k, ks, ke), f(inp.v, ks, ke), f(inp.do, qs, qe)
+        ro = R.gdpa_fwd(q64, k64, v64, one_q, one_k, inp.act, inp.window)
+        rq, rk, rv = R.gdpa_bwd(q64, k64, v64, do64, one_q, one_k, inp.act, inp.window)
+        check_close(f(o, qs, qe), ro, f"cfg{cfg} O sample {b}")
+        check_close(f(dq, qs, qe), rq, f"cfg{cfg} dQ sample {b}")
+        check_close(f(dk, ks, ke), rk, f"cfg{cfg} dK sample {b}")
+        check_close(f(dv, ks, ke), rv, f"cfg{cfg} dV sample {b}")
+    # properties at any size: finite everywhere, zero rows where no partner exists
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+
+
+def test_determinism():
+    say("bitwise determinism run to run")
+    inp = make_workload(2, device=DEV, B=64)
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, 0, "bf16") as plan:
+        a = plan.fwd(inp.q, inp.k, inp.v, qo, ko, "silu")
+        b = plan.fwd(inp.q, inp.k, inp.v, qo, ko, "silu")
+        g1 = plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "silu")
+        g2 = plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "silu")
+        torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
