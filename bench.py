@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of jagged GDPA forward + backward (bf16 in, fp32 accumulate) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--act NAME]
+
+A step is one forward pass plus one backward pass (dK/dV kernel, then dQ kernel)
+over the whole batch of the chosen workload, with inputs resident in HBM.  The
+default workload is the jagged self-attention batch (B = 1024 samples, lognormal
+lengths with median 64 and max 512, H = 4, d = 128, SiLU, no window).
+
+Prints one JSON line: `value` is useful TFLOP/s over fwd + bwd, counting only
+valid (query, key) pairs: 4 H d |V| for the forward and 10 H d |V| for the
+backward.  `roofline` describes the slowest kernel against HBM bandwidth (every
+workload here sits below the bf16 MFMA ridge point), using its algorithmic bytes
+(each input read once, each output written once) and its average duration from
+HIP events recorded on the launch stream around each launch.  `cpu_baseline`
+times the fp64 oracle on the host cores over a bounded prefix of the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "useful TFLOP/s, jagged GDPA fwd+bwd bf16, % of MFMA peak, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_bytes(H, d, Tq, Tk):
+    """Algorithmic bytes per launch (bf16): every input read once, every output written once."""
+    e = 2 * H * d
+    return {"fwd": e * (2 * Tq + 2 * Tk),          # Q, K, V -> O
+            "dkdv": e * (2 * Tq + 4 * Tk),         # Q, dO, K, V -> dK, dV
+            "dq": e * (3 * Tq + 2 * Tk)}           # Q, dO, K, V -> dQ
+
+
+def cpu_baseline(inp, budget_s=15.0):
+    """Time the fp64 oracle (forward + backward) on a prefix of the batch."""
+    import numpy as np
+    import torch
+    from oracle import gdpa_ref as R
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    spent, flops, n = 0.0, 0, 0
+    for b in range(len(inp.lq)):
+        qs, qe = int(inp.q_off[b]), int(inp.q_off[b + 1])
+        ks, ke = int(inp.kv_off[b]), int(inp.kv_off[b + 1])
+        f = lambda t, a, e: t[a:e].to("cpu", torch.float64).numpy()
+        q, k, v, do = f(inp.q, qs, qe), f(inp.k, ks, ke), f(inp.v, ks, ke), f(inp.do, qs, qe)
+        qo, ko = np.array([0, qe - qs]), np.array([0, ke - ks])
+        t0 = time.perf_counter()
+        R.gdpa_fwd(q, k, v, qo, ko, inp.act, inp.window)
+        R.gdpa_bwd(q, k, v, do, qo, ko, inp.act, inp.window)
+        spent += time.perf_counter() - t0
+        flops += 14 * inp.H * inp.d * R.useful_pairs([qe - qs], [ke - ks], inp.window)
+        n += 1
+        if spent >= budget_s:
+            break
+    return {"value": flops / spent / 1e12 if spent > 0 else None, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {n} of {len(inp.lq)} samples, fp64 numpy/scipy forward+backward, "
+                      f"{spent:.1f} s, same seeded inputs"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--act", default=None, help="override the workload's activation (e.g. gelu_poly)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(GDPA shards by sample with no exchange; see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import recsys_attention_jagged_amd as G
+    from gdpa_workloads import WORKLOADS, make_workload
+
+    G.load_library()
+    w = WORKLOADS[args.config]
+    log(f"generating workload {args.config} ({w['name']}) on cuda:0 ...")
+    inp = make_workload(args.config, seed=args.seed, device="cuda", act=args.act)
+    torch.cuda.synchronize()
+    qo = torch.tensor(inp.q_off, dtype=torch.int32, device="cuda")
+    ko = torch.tensor(inp.kv_off, dtype=torch.int32, device="cuda")
+    B, H, d, win, act = len(inp.lq), inp.H, inp.d, inp.window, inp.act
+
+    t0 = time.perf_counter()
+    plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16")
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    st = plan.stats()
+    Tq, Tk, pairs = st["Tq"], st["Tk"], st["valid_pairs"]
+
+    o = torch.empty_like(inp.q)
+    dq = torch.empty_like(inp.q)
+    dk = torch.empty_like(inp.k)
+    dv = torch.empty_like(inp.v)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    h = plan.handle
+
+    def fwd():
+        G.gdpa_fwd(h, inp.q, inp.k, inp.v, qo, ko, B, H, d, act, win, o, sh)
+
+    def dkdv():
+        G.gdpa_bwd_dkdv(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, dk, dv, sh)
+
+    def dqk():
+        G.gdpa_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, dq, sh)
+
+    calls = [("fwd", fwd), ("dkdv", dkdv), ("dq", dqk)]
+    for _ in range(args.warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        for j, (_, c) in enumerate(calls):
+            c()
+            ev[i][j + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / K
+    kms = {name: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
+           for j, (name, _) in enumerate(calls)}
+
+    useful = 14.0 * H * d * pairs
+    value = useful / (ms_step * 1e-3) / 1e12
+    kb = kernel_bytes(H, d, Tq, Tk)
+    dom = max(kms, key=kms.get)
+    achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
+    kernels = {n: {"ms": round(kms[n], 4), "alg_GBps": round(kb[n] / (kms[n] * 1e-3) / 1e9, 1)}
+               for n in kms}
+    kernels["fwd"]["useful_TFLOPs"] = round(4.0 * H * d * pairs / (kms["fwd"] * 1e-3) / 1e12, 2)
+    bwd_ms = kms["dkdv"] + kms["dq"]
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
+        "config": {"workload": f"{w['name']} (configs[{args.config - 1}])", "B": B, "H": H, "d": d,
+                   "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs},
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_useful_TFLOPs": kernels["fwd"]["useful_TFLOPs"],
+        "bwd_useful_TFLOPs": round(10.0 * H * d * pairs / (bwd_ms * 1e-3) / 1e12, 2),
+        "kernels": kernels,
+        "plan_ms": round(plan_ms, 1),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    plan.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

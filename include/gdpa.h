@@ -166,6 +166,23 @@ gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v
                      gdpa_act act, int window, void* dq, void* dk, void* dv, void* stream);
 
 /*
+ * gdpa_bwd_dkdv - only dK and dV (one KV-stationary kernel); same arguments and
+ * errors as gdpa_bwd without dq.  For callers whose queries are frozen or who
+ * schedule the two halves of the backward pass separately.
+ */
+gdpa_status gdpa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                          const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                          gdpa_act act, int window, void* dk, void* dv, void* stream);
+
+/*
+ * gdpa_bwd_dq - only dQ (one Q-stationary kernel); same arguments and errors as
+ * gdpa_bwd without dk and dv.  gdpa_bwd == gdpa_bwd_dkdv followed by gdpa_bwd_dq.
+ */
+gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                        const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                        gdpa_act act, int window, void* dq, void* stream);
+
+/*
  * gdpa_plan_export - serialise one work list as int32 values:
  *   [P, n_items, tile_stat, tile_strm, waves, bnw, bin_ptr[0..P], then per item in
  *    bin order (b, h, t, s0, s1)]

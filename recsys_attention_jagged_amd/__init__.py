@@ -65,6 +65,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                      ctypes.POINTER(_vp)]
     lib.gdpa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
     lib.gdpa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
+    lib.gdpa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]
+    lib.gdpa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
     lib.gdpa_plan_export.argtypes = [_vp, _i, _vp, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdpa_plan_stats.argtypes = [_vp, ctypes.POINTER(gdpa_plan_stats_t)]
     lib.gdpa_plan_destroy.argtypes = [_vp]
@@ -75,7 +77,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_last_error.restype = ctypes.c_char_p
     lib.gdpa_gelu_poly_bound.argtypes = []
     lib.gdpa_gelu_poly_bound.restype = ctypes.c_double
-    for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_plan_export", "gdpa_plan_stats"):
+    for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
+                 "gdpa_plan_export", "gdpa_plan_stats"):
         getattr(lib, name).restype = _i
     if path == LIB_PATH:
         _lib = lib
@@ -142,6 +145,18 @@ def gdpa_bwd(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, d
     _check(load_library().gdpa_bwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
                                    _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, _ptr(dq),
                                    _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def gdpa_bwd_dkdv(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, dk, dv, stream=None):
+    _check(load_library().gdpa_bwd_dkdv(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
+                                        _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, _ptr(dk),
+                                        _ptr(dv), _stream(stream)))
+
+
+def gdpa_bwd_dq(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, dq, stream=None):
+    _check(load_library().gdpa_bwd_dq(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
+                                      _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, _ptr(dq),
+                                      _stream(stream)))
 
 
 def gdpa_plan_export(plan, list_) -> np.ndarray:

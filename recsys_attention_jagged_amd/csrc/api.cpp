@@ -331,15 +331,19 @@ gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v
     return GDPA_OK;
 }
 
-gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
-                     const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
-                     gdpa_act act, int window, void* dq, void* dk, void* dv, void* stream) {
+static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                             const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                             gdpa_act act, int window, void* dq, void* dk, void* dv, void* stream,
+                             bool want_dkdv, bool want_dq) {
     g_err.clear();
     gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
     if (st != GDPA_OK) return st;
     if (act == GDPA_ACT_ONE) return fail(GDPA_ERR_UNSUPPORTED, "GDPA_ACT_ONE has no backward");
-    if (plan->Tq > 0 && (!q || !dout || !dq)) return fail(GDPA_ERR_INVALID_ARG, "q, dout or dq is NULL");
-    if (plan->Tk > 0 && (!k || !v || !dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "k, v, dk or dv is NULL");
+    const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
+    if (any_q && (!q || !dout)) return fail(GDPA_ERR_INVALID_ARG, "q or dout is NULL");
+    if (any_k && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
+    if (want_dq && any_q && !dq) return fail(GDPA_ERR_INVALID_ARG, "dq is NULL");
+    if (want_dkdv && any_k && (!dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "dk or dv is NULL");
     hipStream_t s = (hipStream_t)stream;
     KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
     a.q = q;
@@ -351,10 +355,9 @@ gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v
     a.dv = dv;
     hipError_t e = hipSuccess;
     if (plan->dtype == GDPA_F32) {
-        e = launch_bwd_f32(a, (int)plan->Tq, (int)plan->Tk, d, act, s);
+        e = launch_bwd_f32(a, want_dq ? (int)plan->Tq : 0, want_dkdv ? (int)plan->Tk : 0, d, act, s);
     } else {
-        // dK/dV (KV-stationary) then dQ (Q-stationary), stream-ordered
-        if (plan->Tk > 0) {
+        if (want_dkdv && any_k) {
             const WorkList& wl = plan->lists[LIST_DKDV];
             KernelArgs b = a;
             b.items = plan->d_items[LIST_DKDV];
@@ -366,7 +369,7 @@ gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v
                 default: e = launch_dkdv_bf16_d128(b, wl.waves, act, s); break;
             }
         }
-        if (e == hipSuccess && plan->Tq > 0) {
+        if (e == hipSuccess && want_dq && any_q) {
             const WorkList& wl = plan->lists[LIST_DQ];
             KernelArgs b = a;
             b.items = plan->d_items[LIST_DQ];
@@ -382,6 +385,27 @@ gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no backward kernel for this configuration");
     if (e != hipSuccess) return fail_hip(e, "backward launch");
     return GDPA_OK;
+}
+
+gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                     const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                     gdpa_act act, int window, void* dq, void* dk, void* dv, void* stream) {
+    return bwd_parts(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, dq, dk, dv, stream,
+                     true, true);
+}
+
+gdpa_status gdpa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                          const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                          gdpa_act act, int window, void* dk, void* dv, void* stream) {
+    return bwd_parts(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, nullptr, dk, dv, stream,
+                     true, false);
+}
+
+gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                        const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                        gdpa_act act, int window, void* dq, void* stream) {
+    return bwd_parts(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, dq, nullptr, nullptr,
+                     stream, false, true);
 }
 
 }  // extern "C"
