@@ -79,7 +79,7 @@ struct gdpa_plan_s {
     std::vector<int64_t> lq, lk;
     int64_t Tq = 0, Tk = 0, valid_pairs = 0;
     WorkList lists[3];
-    Item* d_items[3] = {nullptr, nullptr, nullptr};
+    DevRec* d_items[3] = {nullptr, nullptr, nullptr};
     int32_t* d_bin_ptr[3] = {nullptr, nullptr, nullptr};
 
     ~gdpa_plan_s() {
@@ -204,11 +204,12 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
     if (!p->host_only) {
         for (int l = 0; l < 3; ++l) {
             const WorkList& wl = p->lists[l];
-            const size_t ni = std::max<size_t>(1, wl.items.size());
-            hipError_t e = hipMalloc((void**)&p->d_items[l], ni * sizeof(Item));
+            const std::vector<DevRec> recs = device_records(wl, p->q_off, p->kv_off);
+            const size_t ni = std::max<size_t>(1, recs.size());
+            hipError_t e = hipMalloc((void**)&p->d_items[l], ni * sizeof(DevRec));
             if (e == hipSuccess) e = hipMalloc((void**)&p->d_bin_ptr[l], wl.bin_ptr.size() * sizeof(int32_t));
-            if (e == hipSuccess && !wl.items.empty())
-                e = hipMemcpy(p->d_items[l], wl.items.data(), wl.items.size() * sizeof(Item), hipMemcpyHostToDevice);
+            if (e == hipSuccess && !recs.empty())
+                e = hipMemcpy(p->d_items[l], recs.data(), recs.size() * sizeof(DevRec), hipMemcpyHostToDevice);
             if (e == hipSuccess)
                 e = hipMemcpy(p->d_bin_ptr[l], wl.bin_ptr.data(), wl.bin_ptr.size() * sizeof(int32_t),
                               hipMemcpyHostToDevice);

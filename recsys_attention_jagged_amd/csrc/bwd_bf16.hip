@@ -9,18 +9,17 @@
 //     dV = P^T dO,   dK = dS^T Q / sqrt(d),   dQ = dS K / sqrt(d).
 //
 // Two persistent kernels, no atomics (every output row has one owner):
-//   * dq_kernel   - Q-stationary: an item is a q tile, steps stream K/V tiles.
-//                   S^T = K Q^T and dP^T = V dO^T (Q, dO in registers), then
-//                   dQ^T += K^T dS^T with the dS^T accumulator lanes as the
-//                   B operand (K^T from a transposed LDS copy).
-//   * dkdv_kernel - KV-stationary: an item is a kv tile, steps stream Q/dO
-//                   tiles.  S = Q K^T and dP = dO V^T (K, V in registers), then
-//                   dV^T += dO^T P and dK^T += Q^T dS with P, dS accumulator
-//                   lanes as B operands (Q^T, dO^T from transposed LDS copies).
-// Both walk their bin's (item, step) pairs as one flattened, prefetched loop,
-// as the forward kernel does.
-#include "device.hpp"
+//   * dq   - Q-stationary: an item is a q tile, steps stream K/V tiles.
+//            S^T = K Q^T and dP^T = V dO^T (Q, dO in registers), then
+//            dQ^T += K^T dS^T with the dS^T accumulator lanes as B operand and
+//            K^T read from the row-major K tile with transposing LDS reads.
+//   * dkdv - KV-stationary: an item is a kv tile, steps stream Q/dO tiles.
+//            S = Q K^T and dP = dO V^T (K, V in registers), then
+//            dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read from
+//            the row-major tiles with transposing LDS reads.
+// Both run on the multi-stage DMA pipeline shared with the forward kernel.
 #include "kernels.hpp"
+#include "pipe.hpp"
 
 #ifndef GDPA_D
 #error "compile with -DGDPA_D=<32|64|128>"
@@ -29,468 +28,354 @@
 namespace gdpa {
 namespace {
 
-// =========================================================================
-// dQ kernel (Q-stationary)
-// =========================================================================
-template <int D, int WQ>
-struct DqCfg {
-    static constexpr int WK = 4 / WQ, BNW = 32, BM = 32 * WQ, BN = WK * BNW;
-    static constexpr int NDB = D / 32, NKS = D / 16;
-    static constexpr int KST = D + 8, VST = BN + 8;
-    static constexpr int SZ_K = BN * KST, SZ_KT = D * VST, SZ_V = BN * KST, SZ_Q = BM * KST;
-    static constexpr int STEP_BYTES = (SZ_K + SZ_KT + SZ_V) * 2;
-    static constexpr int NBUF = (2 * STEP_BYTES + 2 * SZ_Q * 2) <= 160 * 1024 ? 2 : 1;
-    static constexpr int MAIN = NBUF * STEP_BYTES + 2 * SZ_Q * 2;
-    static constexpr int PART_BYTES = (WK - 1) * WQ * NDB * 64 * 16 * 4;
-    static constexpr int EPI_BYTES = PART_BYTES + BM * KST * 2;
-    static constexpr int LDS = MAIN > EPI_BYTES ? MAIN : EPI_BYTES;
-    static_assert(LDS <= 160 * 1024, "LDS budget exceeded");
-};
-
-template <int D, int WQ, int ACT>
-__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(const KernelArgs a) {
-    using C = DqCfg<D, WQ>;
-    constexpr int WK = C::WK, BNW = C::BNW, BM = C::BM, BN = C::BN, NDB = C::NDB, NKS = C::NKS;
-    constexpr int KST = C::KST, VST = C::VST;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wq = wave / WK, wk = wave % WK;
-    const int r = lane & 31, hh = lane >> 5;
-
-    const int bin = logical_bin(a.P);
-    const ItemRec* items = reinterpret_cast<const ItemRec*>(a.items);
-    StepIt cur;
-    cur.end = a.bin_ptr[bin + 1];
-    const int first_item = a.bin_ptr[bin];
-    if (first_item >= cur.end) return;
-    cur.load(items, a.q_off, a.kv_off, first_item);
-
-    const int H = a.H;
-    const uint32_t rs = (uint32_t)H * D * 2;
-    const uint32_t rso = (uint32_t)H * D * (a.out_f32 ? 4 : 2);
-    const int win = a.window > 0 ? a.window : (1 << 30);
-    const float scale = a.scale;
-    const __bf16* gq = (const __bf16*)a.q;
-    const __bf16* gk = (const __bf16*)a.k;
-    const __bf16* gv = (const __bf16*)a.v;
-    const __bf16* gdo = (const __bf16*)a.dout;
-
-    __bf16* sQ = (__bf16*)(smem + C::NBUF * C::STEP_BYTES);
-    __bf16* sdO = sQ + C::SZ_Q;
-    auto sK = [&](int buf) { return (__bf16*)(smem + buf * C::STEP_BYTES); };
-    auto sKT = [&](int buf) { return (__bf16*)(smem + buf * C::STEP_BYTES) + C::SZ_K; };
-    auto sV = [&](int buf) { return (__bf16*)(smem + buf * C::STEP_BYTES) + C::SZ_K + C::SZ_KT; };
-
-    TileStage<BN, D> stK, stV;
-    TileStage<BM, D> stQ, stO;
-
-    auto issue_loads = [&](const StepIt& st, bool with_q) {
-        if (st.has_steps()) {
-            const size_t kvb = ((size_t)st.ks * H + st.h) * D;
-            stK.load(slice_rsrc(gk + kvb, st.lk, rs, D * 2), st.s * BN, rs, tid);
-            stV.load(slice_rsrc(gv + kvb, st.lk, rs, D * 2), st.s * BN, rs, tid);
-        }
-        if (with_q) {
-            const size_t qb = ((size_t)st.qs * H + st.h) * D;
-            stQ.load(slice_rsrc(gq + qb, st.lq, rs, D * 2), st.t * BM, rs, tid);
-            stO.load(slice_rsrc(gdo + qb, st.lq, rs, D * 2), st.t * BM, rs, tid);
-        }
-    };
-    auto commit = [&](const StepIt& st, int buf, bool with_q) {
-        if (st.has_steps()) {
-            stK.template store_rows<KST>(sK(buf), tid);
-            stK.template store_cols<VST>(sKT(buf), tid);
-            stV.template store_rows<KST>(sV(buf), tid);
-        }
-        if (with_q) {
-            stQ.template store_rows<KST>(sQ, tid);
-            stO.template store_rows<KST>(sdO, tid);
-        }
-    };
-
-    issue_loads(cur, true);
-    commit(cur, 0, true);
-    __syncthreads();
-
-    f32x16 acc[NDB];
-    bf16x8 qf[NKS], of[NKS];
-    int buf = 0;
-    for (;;) {
-        const bool first = cur.first(), last = cur.last();
-        if (first) {
+// Sum the per-wave partial accumulators of NG waves that share an output block
+// (group member `mem` of group `grp`; member 0 keeps the sum), through LDS.
+template <int NDB, int NG, int NGRP>
+__device__ __forceinline__ void reduce_groups(f32x16 (&acc)[NDB], char* lds, int grp, int mem, int lane) {
+    f32x4* part = (f32x4*)lds;
+    if (mem > 0) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                qf[ks] = *(const bf16x8*)(sQ + (wq * 32 + r) * KST + 16 * ks + 8 * hh);
-                of[ks] = *(const bf16x8*)(sdO + (wq * 32 + r) * KST + 16 * ks + 8 * hh);
-            }
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-        }
-
-        StepIt nx = cur;
-        const bool has_next = nx.advance(items, a.q_off, a.kv_off);
-        const bool nx_first = has_next && nx.first();
-        if (has_next) issue_loads(nx, nx_first);
-
-        const int q0 = cur.t * BM + wq * 32;
-        const int j0 = cur.s * BN + wk * BNW;
-        if (cur.has_steps() && block_any(q0, j0, cur.lq, cur.lk, win)) {
-            const __bf16* k_t = sK(buf);
-            const __bf16* kt_t = sKT(buf);
-            const __bf16* v_t = sV(buf);
-            f32x16 st = {}, dpt = {};
+            for (int c4 = 0; c4 < 4; ++c4)
+                part[((((mem - 1) * NGRP + grp) * NDB + db) * 4 + c4) * 64 + lane] =
+                    f32x4{acc[db][4 * c4], acc[db][4 * c4 + 1], acc[db][4 * c4 + 2], acc[db][4 * c4 + 3]};
+    }
+    lds_barrier();
+    if (mem == 0) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 ka = *(const bf16x8*)(k_t + (wk * BNW + r) * KST + 16 * ks + 8 * hh);
-                const bf16x8 va = *(const bf16x8*)(v_t + (wk * BNW + r) * KST + 16 * ks + 8 * hh);
-                st = mfma32(ka, qf[ks], st);
-                dpt = mfma32(va, of[ks], dpt);
-            }
-            f32x16 ds;
-            const bool full = block_all(q0, j0, cur.lq, cur.lk, win);
-            const int qi = q0 + r;
+        for (int m2 = 1; m2 < NG; ++m2)
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                float f, g;
-                act_fwd_grad<ACT>(st[c] * scale, f, g);
-                const int kj = j0 + 8 * (c >> 2) + 4 * hh + (c & 3);
-                const int dd = qi - kj;
-                const bool ok = full || (kj < cur.lk && qi < cur.lq && dd < win && -dd < win);
-                ds[c] = ok ? dpt[c] * g : 0.0f;
-            }
-            const bf16x8 d0 = acc_to_bf16x8(ds, 0), d1 = acc_to_bf16x8(ds, 1);
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16x8 a0 = *(const bf16x8*)(kt_t + (db * 32 + r) * VST + wk * BNW + 8 * hh);
-                acc[db] = mfma32(a0, d0, acc[db]);
-            }
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                const bf16x8 a1 = *(const bf16x8*)(kt_t + (db * 32 + r) * VST + wk * BNW + 16 + 8 * hh);
-                acc[db] = mfma32(a1, d1, acc[db]);
-            }
-        }
-
-        if (last) {
-            __syncthreads();
-            if constexpr (WK > 1) {
-                float* part = (float*)smem;
-                if (wk > 0) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        float* dst = part + ((((wk - 1) * WQ + wq) * NDB + db) * 64 + lane) * 16;
-#pragma unroll
-                        for (int c4 = 0; c4 < 4; ++c4)
-                            *(f32x4*)(dst + 4 * c4) = f32x4{acc[db][4 * c4], acc[db][4 * c4 + 1], acc[db][4 * c4 + 2], acc[db][4 * c4 + 3]};
-                    }
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const f32x4 v = part[((((m2 - 1) * NGRP + grp) * NDB + db) * 4 + c4) * 64 + lane];
+                    for (int i = 0; i < 4; ++i) acc[db][4 * c4 + i] += v[i];
                 }
-                __syncthreads();
-                if (wk == 0) {
-#pragma unroll
-                    for (int w2 = 1; w2 < WK; ++w2)
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            const float* src = part + ((((w2 - 1) * WQ + wq) * NDB + db) * 64 + lane) * 16;
-#pragma unroll
-                            for (int c = 0; c < 16; ++c) acc[db][c] += src[c];
-                        }
-                }
-            }
-            const size_t ob = ((size_t)cur.qs * H + cur.h) * D;
-            if (a.out_f32) {
-                const rsrc_t ro = slice_rsrc((const float*)a.dq + ob, cur.lq, rso, D * 4);
-                if (wk == 0) {
-                    const int row = cur.t * BM + wq * 32 + r;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x4 v;
-                            for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[db][4 * j + i] * scale);
-                            buf_store16(ro, (uint32_t)row * rso + (db * 32 + 8 * j + 4 * hh) * 4, v);
-                        }
-                }
-            } else {
-                __bf16* sO = (__bf16*)(smem + C::PART_BYTES);
-                if (wk == 0) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x2 w;
-                            w[0] = pack_bf16x2(acc[db][4 * j] * scale, acc[db][4 * j + 1] * scale);
-                            w[1] = pack_bf16x2(acc[db][4 * j + 2] * scale, acc[db][4 * j + 3] * scale);
-                            *(u32x2*)(sO + (wq * 32 + r) * KST + db * 32 + 8 * j + 4 * hh) = w;
-                        }
-                }
-                __syncthreads();
-                const rsrc_t ro = slice_rsrc((const __bf16*)a.dq + ob, cur.lq, rso, D * 2);
-                constexpr int CPR = D / 8;
-                for (int ci = tid; ci < BM * CPR; ci += 256) {
-                    const int row = ci / CPR, c = ci % CPR;
-                    buf_store16(ro, (uint32_t)(cur.t * BM + row) * rso + c * 16, *(const u32x4*)(sO + row * KST + 8 * c));
-                }
-            }
-        }
+    }
+    lds_barrier();
+}
 
-        if (!has_next) break;
-        if constexpr (C::NBUF == 1) {
-            __syncthreads();
-            commit(nx, 0, nx_first);
-        } else {
-            if (last) __syncthreads();
-            commit(nx, buf ^ 1, nx_first);
-            buf ^= 1;
+// Store an accumulator tile whose lanes hold column `rowbase + r` (an output
+// row) and rows d = 32 db + 8 j + 4 hh + i: staged through LDS as bf16 rows,
+// then written with coalesced 16-byte stores; rows beyond the slice are dropped.
+template <int D, int NDB>
+__device__ __forceinline__ void stage_rows(const f32x16 (&acc)[NDB], float mul, __bf16* sO, int row, int hh) {
+    constexpr int SOST = D + 8;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[db][4 * j] * mul, acc[db][4 * j + 1] * mul);
+            w[1] = pack_bf16x2(acc[db][4 * j + 2] * mul, acc[db][4 * j + 3] * mul);
+            *(u32x2*)(sO + row * SOST + db * 32 + 8 * j + 4 * hh) = w;
         }
-        __syncthreads();
-        cur = nx;
+}
+
+template <int D, int ROWS>
+__device__ __forceinline__ void store_rows(const __bf16* sO, rsrc_t ro, int row0, uint32_t rso, int tid) {
+    constexpr int SOST = D + 8, CPR = D / 8;
+    for (int ci = tid; ci < ROWS * CPR; ci += 256) {
+        const int row = ci / CPR, c = ci % CPR;
+        buf_store16(ro, (uint32_t)(row0 + row) * rso + c * 16, *(const u32x4*)(sO + row * SOST + 8 * c));
     }
 }
 
-// =========================================================================
-// dK/dV kernel (KV-stationary)
-// =========================================================================
-template <int D, int WK>
-struct DkdvCfg {
-    static constexpr int WQ = 4 / WK, BK = 32 * WK, BQ = 32 * WQ;
-    static constexpr int NDB = D / 32, NKS = D / 16;
-    static constexpr int KST = D + 8, QTST = BQ + 8;
-    static constexpr int SZ_Q = BQ * KST, SZ_QT = D * QTST, SZ_K = BK * KST;
-    static constexpr int STEP_BYTES = 2 * (SZ_Q + SZ_QT) * 2;   // Q, Q^T, dO, dO^T
-    static constexpr int NBUF = (2 * STEP_BYTES + 2 * SZ_K * 2) <= 160 * 1024 ? 2 : 1;
-    static constexpr int MAIN = NBUF * STEP_BYTES + 2 * SZ_K * 2;
-    static constexpr int PART_BYTES = (WQ - 1) * WK * NDB * 2 * 64 * 16 * 4;
-    static constexpr int EPI_BYTES = PART_BYTES + 2 * BK * KST * 2;
-    static constexpr int LDS = MAIN > EPI_BYTES ? MAIN : EPI_BYTES;
-    static_assert(LDS <= 160 * 1024, "LDS budget exceeded");
+template <int NDB>
+__device__ __forceinline__ void store_f32(const f32x16 (&acc)[NDB], float mul, rsrc_t ro, int row, uint32_t rso, int hh) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x4 v;
+            for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[db][4 * j + i] * mul);
+            buf_store16(ro, (uint32_t)row * rso + (db * 32 + 8 * j + 4 * hh) * 4, v);
+        }
+}
+
+struct Lanes {
+    int tid, lane, wave, r, hh;
+    __device__ Lanes() {
+        tid = threadIdx.x;
+        lane = tid & 63;
+        wave = tid >> 6;
+        r = lane & 31;
+        hh = lane >> 5;
+    }
 };
 
-template <int D, int WK, int ACT>
-__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(const KernelArgs a) {
-    using C = DkdvCfg<D, WK>;
-    constexpr int WQ = C::WQ, BK = C::BK, BQ = C::BQ, NDB = C::NDB, NKS = C::NKS;
-    constexpr int KST = C::KST, QTST = C::QTST;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+// =========================================================================
+// dQ (Q-stationary)
+// =========================================================================
+template <int D, int WQ, int ACT>
+struct DqPol : Lanes {
+    static constexpr int WK = 4 / WQ, BM = 32 * WQ, BN = 32 * WK;
+    static constexpr int NDB = D / 32, NKS = D / 16;
+    using TQ = AsyncTile<BM, D>;
+    using TK = AsyncTile<BN, D>;
+    static constexpr int OFF_O = TQ::BYTES, OFF_K = 2 * TQ::BYTES, OFF_V = 2 * TQ::BYTES + TK::BYTES;
+    static constexpr int STAGE_BYTES = 2 * TQ::BYTES + 2 * TK::BYTES;
+    static constexpr int NS = Stages<STAGE_BYTES>::N;
+    static constexpr int LOADS = 2 * TQ::PER_WAVE + 2 * TK::PER_WAVE;
+    static_assert((WK - 1) * WQ * NDB * 4096 <= STAGE_BYTES && BM * (D + 8) * 2 <= STAGE_BYTES, "epilogue");
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wk = wave / WQ, wq = wave % WQ;
-    const int r = lane & 31, hh = lane >> 5;
+    const KernelArgs& a;
+    int wq, wk, H, win;
+    uint32_t rs, rso;
+    float scale;
+    rsrc_t empty, rq, ro, rk, rv;
+    TQ tq;
+    TK tk;
+    bf16x8 qf[NKS], of[NKS];
+    f32x16 acc[NDB];
 
-    const int bin = logical_bin(a.P);
-    const ItemRec* items = reinterpret_cast<const ItemRec*>(a.items);
-    StepIt cur;
-    cur.end = a.bin_ptr[bin + 1];
-    const int first_item = a.bin_ptr[bin];
-    if (first_item >= cur.end) return;
-    cur.load(items, a.q_off, a.kv_off, first_item);
-
-    const int H = a.H;
-    const uint32_t rs = (uint32_t)H * D * 2;
-    const uint32_t rso = (uint32_t)H * D * (a.out_f32 ? 4 : 2);
-    const int win = a.window > 0 ? a.window : (1 << 30);
-    const float scale = a.scale;
-    const __bf16* gq = (const __bf16*)a.q;
-    const __bf16* gk = (const __bf16*)a.k;
-    const __bf16* gv = (const __bf16*)a.v;
-    const __bf16* gdo = (const __bf16*)a.dout;
-
-    __bf16* sKs = (__bf16*)(smem + C::NBUF * C::STEP_BYTES);
-    __bf16* sVs = sKs + C::SZ_K;
-    auto sQ = [&](int buf) { return (__bf16*)(smem + buf * C::STEP_BYTES); };
-    auto sQT = [&](int buf) { return sQ(buf) + C::SZ_Q; };
-    auto sO = [&](int buf) { return sQ(buf) + C::SZ_Q + C::SZ_QT; };
-    auto sOT = [&](int buf) { return sQ(buf) + 2 * C::SZ_Q + C::SZ_QT; };
-
-    TileStage<BQ, D> stQ, stO;
-    TileStage<BK, D> stK, stV;
-
-    auto issue_loads = [&](const StepIt& st, bool with_kv) {
-        if (st.has_steps()) {
-            const size_t qb = ((size_t)st.qs * H + st.h) * D;
-            stQ.load(slice_rsrc(gq + qb, st.lq, rs, D * 2), st.s * BQ, rs, tid);
-            stO.load(slice_rsrc(gdo + qb, st.lq, rs, D * 2), st.s * BQ, rs, tid);
-        }
-        if (with_kv) {
-            const size_t kvb = ((size_t)st.ks * H + st.h) * D;
-            stK.load(slice_rsrc(gk + kvb, st.lk, rs, D * 2), st.t * BK, rs, tid);
-            stV.load(slice_rsrc(gv + kvb, st.lk, rs, D * 2), st.t * BK, rs, tid);
-        }
-    };
-    auto commit = [&](const StepIt& st, int buf, bool with_kv) {
-        if (st.has_steps()) {
-            stQ.template store_rows<KST>(sQ(buf), tid);
-            stQ.template store_cols<QTST>(sQT(buf), tid);
-            stO.template store_rows<KST>(sO(buf), tid);
-            stO.template store_cols<QTST>(sOT(buf), tid);
-        }
-        if (with_kv) {
-            stK.template store_rows<KST>(sKs, tid);
-            stV.template store_rows<KST>(sVs, tid);
-        }
-    };
-
-    issue_loads(cur, true);
-    commit(cur, 0, true);
-    __syncthreads();
-
-    f32x16 accK[NDB], accV[NDB];
-    bf16x8 kf[NKS], vf[NKS];
-    int buf = 0;
-    for (;;) {
-        const bool first = cur.first(), last = cur.last();
-        if (first) {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                kf[ks] = *(const bf16x8*)(sKs + (wk * 32 + r) * KST + 16 * ks + 8 * hh);
-                vf[ks] = *(const bf16x8*)(sVs + (wk * 32 + r) * KST + 16 * ks + 8 * hh);
-            }
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) accK[db] = accV[db] = f32x16{};
-        }
-
-        StepIt nx = cur;
-        const bool has_next = nx.advance(items, a.q_off, a.kv_off);
-        const bool nx_first = has_next && nx.first();
-        if (has_next) issue_loads(nx, nx_first);
-
-        const int i0 = cur.s * BQ + wq * 32;   // q rows of this wave
-        const int j0 = cur.t * BK + wk * 32;   // kv rows of this wave
-        if (cur.has_steps() && block_any(i0, j0, cur.lq, cur.lk, win)) {
-            const __bf16* q_t = sQ(buf);
-            const __bf16* qt_t = sQT(buf);
-            const __bf16* o_t = sO(buf);
-            const __bf16* ot_t = sOT(buf);
-            f32x16 s = {}, dp = {};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 qa = *(const bf16x8*)(q_t + (wq * 32 + r) * KST + 16 * ks + 8 * hh);
-                const bf16x8 oa = *(const bf16x8*)(o_t + (wq * 32 + r) * KST + 16 * ks + 8 * hh);
-                s = mfma32(qa, kf[ks], s);
-                dp = mfma32(oa, vf[ks], dp);
-            }
-            // accumulator lane: column = kv row j0 + r, rows = q rows i0 + 8 j + 4 hh + i
-            f32x16 p, ds;
-            const bool full = block_all(i0, j0, cur.lq, cur.lk, win);
-            const int kj = j0 + r;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                float f, g;
-                act_fwd_grad<ACT>(s[c] * scale, f, g);
-                const int qi = i0 + 8 * (c >> 2) + 4 * hh + (c & 3);
-                const int dd = qi - kj;
-                const bool ok = full || (kj < cur.lk && qi < cur.lq && dd < win && -dd < win);
-                p[c] = ok ? f : 0.0f;
-                ds[c] = ok ? dp[c] * g : 0.0f;
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const bf16x8 pm = acc_to_bf16x8(p, m), dm = acc_to_bf16x8(ds, m);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 oa = *(const bf16x8*)(ot_t + (db * 32 + r) * QTST + wq * 32 + 16 * m + 8 * hh);
-                    accV[db] = mfma32(oa, pm, accV[db]);
-                    const bf16x8 qa = *(const bf16x8*)(qt_t + (db * 32 + r) * QTST + wq * 32 + 16 * m + 8 * hh);
-                    accK[db] = mfma32(qa, dm, accK[db]);
-                }
-            }
-        }
-
-        if (last) {
-            __syncthreads();
-            if constexpr (WQ > 1) {
-                float* part = (float*)smem;
-                if (wq > 0) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        float* dk_dst = part + (((((wq - 1) * WK + wk) * NDB + db) * 2 + 0) * 64 + lane) * 16;
-                        float* dv_dst = part + (((((wq - 1) * WK + wk) * NDB + db) * 2 + 1) * 64 + lane) * 16;
-#pragma unroll
-                        for (int c4 = 0; c4 < 4; ++c4) {
-                            *(f32x4*)(dk_dst + 4 * c4) = f32x4{accK[db][4 * c4], accK[db][4 * c4 + 1], accK[db][4 * c4 + 2], accK[db][4 * c4 + 3]};
-                            *(f32x4*)(dv_dst + 4 * c4) = f32x4{accV[db][4 * c4], accV[db][4 * c4 + 1], accV[db][4 * c4 + 2], accV[db][4 * c4 + 3]};
-                        }
-                    }
-                }
-                __syncthreads();
-                if (wq == 0) {
-#pragma unroll
-                    for (int w2 = 1; w2 < WQ; ++w2)
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            const float* ks_ = part + (((((w2 - 1) * WK + wk) * NDB + db) * 2 + 0) * 64 + lane) * 16;
-                            const float* vs_ = part + (((((w2 - 1) * WK + wk) * NDB + db) * 2 + 1) * 64 + lane) * 16;
-#pragma unroll
-                            for (int c = 0; c < 16; ++c) {
-                                accK[db][c] += ks_[c];
-                                accV[db][c] += vs_[c];
-                            }
-                        }
-                }
-            }
-            const size_t ob = ((size_t)cur.ks * H + cur.h) * D;
-            if (a.out_f32) {
-                const rsrc_t rk = slice_rsrc((const float*)a.dk + ob, cur.lk, rso, D * 4);
-                const rsrc_t rv = slice_rsrc((const float*)a.dv + ob, cur.lk, rso, D * 4);
-                if (wq == 0) {
-                    const int row = cur.t * BK + wk * 32 + r;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x4 vk, vv;
-                            for (int i = 0; i < 4; ++i) {
-                                vk[i] = __float_as_uint(accK[db][4 * j + i] * scale);
-                                vv[i] = __float_as_uint(accV[db][4 * j + i]);
-                            }
-                            const uint32_t off = (uint32_t)row * rso + (db * 32 + 8 * j + 4 * hh) * 4;
-                            buf_store16(rk, off, vk);
-                            buf_store16(rv, off, vv);
-                        }
-                }
-            } else {
-                __bf16* oK = (__bf16*)(smem + C::PART_BYTES);
-                __bf16* oV = oK + BK * KST;
-                if (wq == 0) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x2 wkk, wvv;
-                            wkk[0] = pack_bf16x2(accK[db][4 * j] * scale, accK[db][4 * j + 1] * scale);
-                            wkk[1] = pack_bf16x2(accK[db][4 * j + 2] * scale, accK[db][4 * j + 3] * scale);
-                            wvv[0] = pack_bf16x2(accV[db][4 * j], accV[db][4 * j + 1]);
-                            wvv[1] = pack_bf16x2(accV[db][4 * j + 2], accV[db][4 * j + 3]);
-                            const int off = (wk * 32 + r) * KST + db * 32 + 8 * j + 4 * hh;
-                            *(u32x2*)(oK + off) = wkk;
-                            *(u32x2*)(oV + off) = wvv;
-                        }
-                }
-                __syncthreads();
-                const rsrc_t rk = slice_rsrc((const __bf16*)a.dk + ob, cur.lk, rso, D * 2);
-                const rsrc_t rv = slice_rsrc((const __bf16*)a.dv + ob, cur.lk, rso, D * 2);
-                constexpr int CPR = D / 8;
-                for (int ci = tid; ci < BK * CPR; ci += 256) {
-                    const int row = ci / CPR, c = ci % CPR;
-                    const uint32_t off = (uint32_t)(cur.t * BK + row) * rso + c * 16;
-                    buf_store16(rk, off, *(const u32x4*)(oK + row * KST + 8 * c));
-                    buf_store16(rv, off, *(const u32x4*)(oV + row * KST + 8 * c));
-                }
-            }
-        }
-
-        if (!has_next) break;
-        if constexpr (C::NBUF == 1) {
-            __syncthreads();
-            commit(nx, 0, nx_first);
-        } else {
-            if (last) __syncthreads();
-            commit(nx, buf ^ 1, nx_first);
-            buf ^= 1;
-        }
-        __syncthreads();
-        cur = nx;
+    __device__ DqPol(const KernelArgs& args) : a(args) {
+        wq = wave / WK;
+        wk = wave % WK;
+        H = a.H;
+        win = a.window > 0 ? a.window : (1 << 30);
+        rs = (uint32_t)H * D * 2;
+        rso = (uint32_t)H * D * (a.out_f32 ? 4 : 2);
+        scale = a.scale;
+        empty = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.q), 0, 0, 0x00020000);
+        rq = ro = rk = rv = empty;
+        tq.init(rs, wave, lane);
+        tk.init(rs, wave, lane);
     }
+
+    __device__ __forceinline__ void new_item(const Step& st) {
+        const size_t kvb = ((size_t)st.r.ks * H + st.r.h) * D;
+        rk = slice_rsrc((const __bf16*)a.k + kvb, st.r.lk, rs, D * 2);
+        rv = slice_rsrc((const __bf16*)a.v + kvb, st.r.lk, rs, D * 2);
+        const size_t qb = ((size_t)st.r.qs * H + st.r.h) * D;
+        rq = slice_rsrc((const __bf16*)a.q + qb, st.r.lq, rs, D * 2);
+        ro = slice_rsrc((const __bf16*)a.dout + qb, st.r.lq, rs, D * 2);
+    }
+
+    __device__ __forceinline__ void issue(const Step& st, char* stage) {
+        const bool kv = st.valid && st.has_steps();
+        const bool q = kv && st.first();
+        const uint32_t sq = (uint32_t)(st.r.t * BM) * rs, sk = (uint32_t)(st.s * BN) * rs;
+        tq.issue(rq, empty, sq, stage, wave, q);
+        tq.issue(ro, empty, sq, stage + OFF_O, wave, q);
+        tk.issue(rk, empty, sk, stage + OFF_K, wave, kv);
+        tk.issue(rv, empty, sk, stage + OFF_V, wave, kv);
+    }
+
+    __device__ __forceinline__ void item_start(const Step& st, const char* stage) {
+        if (st.has_steps()) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                qf[ks] = lds_row8<D>(stage, wq * 32 + r, 2 * ks + hh);
+                of[ks] = lds_row8<D>(stage + OFF_O, wq * 32 + r, 2 * ks + hh);
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    }
+
+    __device__ __forceinline__ void compute(const Step& st, const char* stage) {
+        const int q0 = st.r.t * BM + wq * 32;
+        const int jl = wk * 32;
+        const int j0 = st.s * BN + jl;
+        const int lq = st.r.lq, lk = st.r.lk;
+        if (!st.has_steps() || !block_any(q0, j0, lq, lk, win)) return;
+        const char* kt = stage + OFF_K;
+        const char* vt = stage + OFF_V;
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            s = mfma32(lds_row8<D>(kt, jl + r, 2 * ks + hh), qf[ks], s);
+            dp = mfma32(lds_row8<D>(vt, jl + r, 2 * ks + hh), of[ks], dp);
+        }
+        f32x16 ds;
+        const bool full = block_all(q0, j0, lq, lk, win);
+        const int qi = q0 + r;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            float f, g;
+            act_fwd_grad<ACT>(s[c] * scale, f, g);
+            const int kj = j0 + 8 * (c >> 2) + 4 * hh + (c & 3);
+            const int dd = qi - kj;
+            const bool ok = full || (kj < lk && qi < lq && dd < win && -dd < win);
+            ds[c] = ok ? dp[c] * g : 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const bf16x8 db8 = acc_to_bf16x8(ds, m);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = mfma32(lds_col8<D>(kt, jl + 16 * m, db * 32, lane), db8, acc[db]);
+        }
+    }
+
+    __device__ __forceinline__ void epilogue(const Step& st, char* stage) {
+        if constexpr (WK > 1) reduce_groups<NDB, WK, WQ>(acc, stage, wq, wk, lane);
+        const size_t ob = ((size_t)st.r.qs * H + st.r.h) * D;
+        if (a.out_f32) {
+            if (wk == 0)
+                store_f32<NDB>(acc, scale, slice_rsrc((const float*)a.dq + ob, st.r.lq, rso, D * 4),
+                               st.r.t * BM + wq * 32 + r, rso, hh);
+            return;
+        }
+        __bf16* sO = (__bf16*)stage;
+        if (wk == 0) stage_rows<D, NDB>(acc, scale, sO, wq * 32 + r, hh);
+        lds_barrier();
+        store_rows<D, BM>(sO, slice_rsrc((const __bf16*)a.dq + ob, st.r.lq, rso, D * 2), st.r.t * BM, rso, tid);
+    }
+};
+
+// =========================================================================
+// dK / dV (KV-stationary)
+// =========================================================================
+template <int D, int WK, int ACT>
+struct DkdvPol : Lanes {
+    static constexpr int WQ = 4 / WK, BK = 32 * WK, BQ = 32 * WQ;
+    static constexpr int NDB = D / 32, NKS = D / 16;
+    using TK = AsyncTile<BK, D>;
+    using TQ = AsyncTile<BQ, D>;
+    static constexpr int OFF_V = TK::BYTES, OFF_Q = 2 * TK::BYTES, OFF_O = 2 * TK::BYTES + TQ::BYTES;
+    static constexpr int STAGE_BYTES = 2 * TK::BYTES + 2 * TQ::BYTES;
+    static constexpr int NS = Stages<STAGE_BYTES>::N;
+    static constexpr int LOADS = 2 * TK::PER_WAVE + 2 * TQ::PER_WAVE;
+    static_assert((WQ - 1) * WK * NDB * 4096 <= STAGE_BYTES && 2 * BK * (D + 8) * 2 <= STAGE_BYTES, "epilogue");
+
+    const KernelArgs& a;
+    int wq, wk, H, win;
+    uint32_t rs, rso;
+    float scale;
+    rsrc_t empty, rk, rv, rq, ro;
+    TK tk;
+    TQ tq;
+    bf16x8 kf[NKS], vf[NKS];
+    f32x16 accK[NDB], accV[NDB];
+
+    __device__ DkdvPol(const KernelArgs& args) : a(args) {
+        wk = wave / WQ;
+        wq = wave % WQ;
+        H = a.H;
+        win = a.window > 0 ? a.window : (1 << 30);
+        rs = (uint32_t)H * D * 2;
+        rso = (uint32_t)H * D * (a.out_f32 ? 4 : 2);
+        scale = a.scale;
+        empty = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.k), 0, 0, 0x00020000);
+        rk = rv = rq = ro = empty;
+        tk.init(rs, wave, lane);
+        tq.init(rs, wave, lane);
+    }
+
+    __device__ __forceinline__ void new_item(const Step& st) {
+        const size_t kvb = ((size_t)st.r.ks * H + st.r.h) * D;
+        rk = slice_rsrc((const __bf16*)a.k + kvb, st.r.lk, rs, D * 2);
+        rv = slice_rsrc((const __bf16*)a.v + kvb, st.r.lk, rs, D * 2);
+        const size_t qb = ((size_t)st.r.qs * H + st.r.h) * D;
+        rq = slice_rsrc((const __bf16*)a.q + qb, st.r.lq, rs, D * 2);
+        ro = slice_rsrc((const __bf16*)a.dout + qb, st.r.lq, rs, D * 2);
+    }
+
+    __device__ __forceinline__ void issue(const Step& st, char* stage) {
+        const bool qs = st.valid && st.has_steps();
+        const bool kv = qs && st.first();
+        const uint32_t sk = (uint32_t)(st.r.t * BK) * rs, sq = (uint32_t)(st.s * BQ) * rs;
+        tk.issue(rk, empty, sk, stage, wave, kv);
+        tk.issue(rv, empty, sk, stage + OFF_V, wave, kv);
+        tq.issue(rq, empty, sq, stage + OFF_Q, wave, qs);
+        tq.issue(ro, empty, sq, stage + OFF_O, wave, qs);
+    }
+
+    __device__ __forceinline__ void item_start(const Step& st, const char* stage) {
+        if (st.has_steps()) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                kf[ks] = lds_row8<D>(stage, wk * 32 + r, 2 * ks + hh);
+                vf[ks] = lds_row8<D>(stage + OFF_V, wk * 32 + r, 2 * ks + hh);
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) accK[db] = accV[db] = f32x16{};
+    }
+
+    __device__ __forceinline__ void compute(const Step& st, const char* stage) {
+        const int il = wq * 32;
+        const int i0 = st.s * BQ + il;          // q rows of this wave
+        const int j0 = st.r.t * BK + wk * 32;   // kv rows of this wave
+        const int lq = st.r.lq, lk = st.r.lk;
+        if (!st.has_steps() || !block_any(i0, j0, lq, lk, win)) return;
+        const char* qt = stage + OFF_Q;
+        const char* ot = stage + OFF_O;
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            s = mfma32(lds_row8<D>(qt, il + r, 2 * ks + hh), kf[ks], s);
+            dp = mfma32(lds_row8<D>(ot, il + r, 2 * ks + hh), vf[ks], dp);
+        }
+        // accumulator lane: column = kv row j0 + r, rows = q rows i0 + 8 j + 4 hh + i
+        f32x16 p, ds;
+        const bool full = block_all(i0, j0, lq, lk, win);
+        const int kj = j0 + r;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            float f, g;
+            act_fwd_grad<ACT>(s[c] * scale, f, g);
+            const int qi = i0 + 8 * (c >> 2) + 4 * hh + (c & 3);
+            const int dd = qi - kj;
+            const bool ok = full || (kj < lk && qi < lq && dd < win && -dd < win);
+            p[c] = ok ? f : 0.0f;
+            ds[c] = ok ? dp[c] * g : 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const bf16x8 pm = acc_to_bf16x8(p, m), dm = acc_to_bf16x8(ds, m);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                accV[db] = mfma32(lds_col8<D>(ot, il + 16 * m, db * 32, lane), pm, accV[db]);
+                accK[db] = mfma32(lds_col8<D>(qt, il + 16 * m, db * 32, lane), dm, accK[db]);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void epilogue(const Step& st, char* stage) {
+        if constexpr (WQ > 1) {
+            reduce_groups<NDB, WQ, WK>(accK, stage, wk, wq, lane);
+            reduce_groups<NDB, WQ, WK>(accV, stage, wk, wq, lane);
+        }
+        const size_t ob = ((size_t)st.r.ks * H + st.r.h) * D;
+        const int row = st.r.t * BK + wk * 32 + r;
+        if (a.out_f32) {
+            if (wq == 0) {
+                store_f32<NDB>(accK, scale, slice_rsrc((const float*)a.dk + ob, st.r.lk, rso, D * 4), row, rso, hh);
+                store_f32<NDB>(accV, 1.0f, slice_rsrc((const float*)a.dv + ob, st.r.lk, rso, D * 4), row, rso, hh);
+            }
+            return;
+        }
+        __bf16* sK = (__bf16*)stage;
+        __bf16* sV = sK + BK * (D + 8);
+        if (wq == 0) {
+            stage_rows<D, NDB>(accK, scale, sK, wk * 32 + r, hh);
+            stage_rows<D, NDB>(accV, 1.0f, sV, wk * 32 + r, hh);
+        }
+        lds_barrier();
+        store_rows<D, BK>(sK, slice_rsrc((const __bf16*)a.dk + ob, st.r.lk, rso, D * 2), st.r.t * BK, rso, tid);
+        store_rows<D, BK>(sV, slice_rsrc((const __bf16*)a.dv + ob, st.r.lk, rso, D * 2), st.r.t * BK, rso, tid);
+    }
+};
+
+template <int D, int WQ, int ACT>
+__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(const KernelArgs a, const Rec* __restrict__ recs,
+                                                         const int32_t* __restrict__ bin_ptr) {
+    using Pol = DqPol<D, WQ, ACT>;
+    __shared__ __attribute__((aligned(1024))) char smem[Pol::NS * Pol::STAGE_BYTES];
+    Pol pol(a);
+    run_pipeline(pol, a.P, recs, bin_ptr, smem);
+}
+
+template <int D, int WK, int ACT>
+__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(const KernelArgs a, const Rec* __restrict__ recs,
+                                                           const int32_t* __restrict__ bin_ptr) {
+    using Pol = DkdvPol<D, WK, ACT>;
+    __shared__ __attribute__((aligned(1024))) char smem[Pol::NS * Pol::STAGE_BYTES];
+    Pol pol(a);
+    run_pipeline(pol, a.P, recs, bin_ptr, smem);
 }
 
 template <int WQ, int ACT>
@@ -544,7 +429,9 @@ static hipError_t launch(const void* f, const KernelArgs& a, hipStream_t s) {
     if (!f) return hipErrorInvalidValue;
     if (a.P <= 0) return hipSuccess;
     KernelArgs args = a;
-    void* params[] = {&args};
+    const void* recs = a.items;
+    const int32_t* bin_ptr = a.bin_ptr;
+    void* params[] = {&args, &recs, &bin_ptr};
     return hipLaunchKernel(f, dim3(a.P), dim3(256), params, 0, s);
 }
 

@@ -10,11 +10,10 @@
 //    4 j + i.  A and B operands give each lane 8 bf16 of one row (A) / column
 //    (B); which 8 contraction indices a lane group supplies is our choice, as
 //    long as A and B agree.
-//  * Transposed tiles: an operand that must be contracted over rows (V, K^T,
-//    Q^T, dO^T) is stored in LDS as [d][row'] where row' swaps bits 2 and 3 of
-//    the row index inside each 16-row block.  With that permutation the 8
-//    contraction rows a lane needs for a chained MFMA (the rows an accumulator
-//    lane holds) are contiguous, so every operand read is one 16-byte LDS read.
+//  * Chained products: the accumulator of S (or S^T) is converted to bf16 in
+//    registers and used directly as the B operand of the second product; the
+//    8 contraction rows a lane then supplies are rows {0..3, 8..11} + 4 (l/32)
+//    of a 16-row block, which the A operand reads with transposing LDS loads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,9 +73,6 @@ __device__ __forceinline__ bf16x8 acc_to_bf16x8(const f32x16& c, int m) {
     return r;
 }
 
-// row permutation of transposed tiles: swap bits 2 and 3
-__device__ __forceinline__ int tpos(int row) { return (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1); }
-
 // Logical bin of this workgroup.  Workgroups are dispatched round-robin over the
 // 8 XCDs, so consecutive logical bins (which the planner fills with neighbouring
 // items of equal cost, e.g. adjacent q tiles of one sample) are placed on the
@@ -90,12 +86,34 @@ __device__ __forceinline__ int logical_bin(int P) {
 // -------------------------------------------------------------------------
 // activations
 // -------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Phi(x) (standard normal CDF) and exp(-x^2 / 2) with the erf approximation of
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), t = 1/(1 + p z),
+// z >= 0, |error| <= 1.5e-7.  One reciprocal and one exponential, no branches.
+__device__ __forceinline__ void normal_cdf(float x, float& cdf, float& e) {
+    constexpr float p = 0.3275911f;
+    // a_k / 2, so that q = erfc(z) / 2 / exp(-z^2)
+    constexpr float h1 = 0.5f * 0.254829592f, h2 = 0.5f * -0.284496736f, h3 = 0.5f * 1.421413741f;
+    constexpr float h4 = 0.5f * -1.453152027f, h5 = 0.5f * 1.061405429f;
+    const float z = __builtin_fabsf(x) * 0.70710678118654752f;
+    const float t = fast_rcp(__builtin_fmaf(p, z, 1.0f));
+    const float q = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, h5, h4), h3), h2), h1);
+    e = fast_exp2(x * x * -0.72134752044448170f);   // exp(-x^2/2) = 2^(-x^2 log2(e) / 2)
+    const float c = q * e;                           // Phi(-|x|) = erfc(|x|/sqrt 2) / 2
+    cdf = x >= 0.0f ? 1.0f - c : c;
+}
+
 template <int ACT>
 __device__ __forceinline__ float act_fwd(float x) {
     if constexpr (ACT == ACT_GELU) {
-        return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+        float cdf, e;
+        normal_cdf(x, cdf, e);
+        return x * cdf;
     } else if constexpr (ACT == ACT_SILU) {
-        return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+        return x * fast_rcp(1.0f + fast_exp2(x * -1.4426950408889634f));
     } else if constexpr (ACT == ACT_GELU_POLY) {
         const float u = x * x;
         float p = kGeluPolyCoef[GDPA_GELU_POLY_DEGREE];
@@ -119,12 +137,12 @@ __device__ __forceinline__ float act_fwd(float x) {
 template <int ACT>
 __device__ __forceinline__ void act_fwd_grad(float x, float& f, float& g) {
     if constexpr (ACT == ACT_GELU) {
-        const float cdf = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
-        const float pdf = 0.39894228040143268f * __expf(-0.5f * x * x);
+        float cdf, e;
+        normal_cdf(x, cdf, e);
         f = x * cdf;
-        g = __builtin_fmaf(x, pdf, cdf);
+        g = __builtin_fmaf(x * 0.39894228040143268f, e, cdf);   // Phi(x) + x phi(x)
     } else if constexpr (ACT == ACT_SILU) {
-        const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+        const float s = fast_rcp(1.0f + fast_exp2(x * -1.4426950408889634f));
         f = x * s;
         g = s * __builtin_fmaf(x, 1.0f - s, 1.0f);
     } else if constexpr (ACT == ACT_GELU_POLY) {
@@ -154,119 +172,12 @@ __device__ __forceinline__ void act_fwd_grad(float x, float& f, float& g) {
 }
 
 // -------------------------------------------------------------------------
-// tile staging: global (one sample/head slice) -> registers -> LDS
+// work-list records (written by the host planner)
 // -------------------------------------------------------------------------
-// A tile of ROWS rows x D bf16 columns is read with coalesced 16-byte loads
-// (consecutive threads read consecutive 16-byte chunks of a row); each thread
-// owns row pairs (2p, 2p + 1) at one chunk so that a transposed store can write
-// the two rows' elements as one 32-bit word.
-template <int ROWS, int D>
-struct TileStage {
-    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    static constexpr int PAIRS_PER_PASS = 256 / CPR;
-    static constexpr int PASSES = (ROWS / 2 + PAIRS_PER_PASS - 1) / PAIRS_PER_PASS;
-    u32x4 r[PASSES][2];
-
-    // rows [row0, row0 + ROWS) of the slice; rows outside the slice read 0
-    __device__ __forceinline__ void load(rsrc_t rs, int row0, uint32_t row_stride_bytes, int tid) {
-        const int c = tid % CPR;
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int row = 2 * (p * PAIRS_PER_PASS + tid / CPR);
-            if (row < ROWS) {
-                const uint32_t off = (uint32_t)(row0 + row) * row_stride_bytes + (uint32_t)c * 16u;
-                r[p][0] = buf_load16(rs, off);
-                r[p][1] = buf_load16(rs, off + row_stride_bytes);
-            }
-        }
-    }
-
-    __device__ __forceinline__ void zero() {
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) r[p][0] = r[p][1] = u32x4{0u, 0u, 0u, 0u};
-    }
-
-    // row-major: lds[row * LDST + col]
-    template <int LDST>
-    __device__ __forceinline__ void store_rows(__bf16* lds, int tid) const {
-        const int c = tid % CPR;
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int row = 2 * (p * PAIRS_PER_PASS + tid / CPR);
-            if (row < ROWS) {
-                *(u32x4*)(lds + row * LDST + 8 * c) = r[p][0];
-                *(u32x4*)(lds + (row + 1) * LDST + 8 * c) = r[p][1];
-            }
-        }
-    }
-
-    // transposed: lds[col * LDST + tpos(row)]
-    template <int LDST>
-    __device__ __forceinline__ void store_cols(__bf16* lds, int tid) const {
-        const int c = tid % CPR;
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int row = 2 * (p * PAIRS_PER_PASS + tid / CPR);
-            if (row < ROWS) {
-                const int pos = tpos(row);   // even; row + 1 lands at pos + 1
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t a = r[p][0][w], b = r[p][1][w];
-                    const uint32_t lo = (a & 0xffffu) | (b << 16);       // column 8c + 2w
-                    const uint32_t hi = (a >> 16) | (b & 0xffff0000u);   // column 8c + 2w + 1
-                    *(uint32_t*)(lds + (8 * c + 2 * w) * LDST + pos) = lo;
-                    *(uint32_t*)(lds + (8 * c + 2 * w + 1) * LDST + pos) = hi;
-                }
-            }
-        }
-    }
-};
-
-// -------------------------------------------------------------------------
-// flattened walk over a bin's (item, step) pairs
-// -------------------------------------------------------------------------
-struct ItemRec {
-    int32_t b, h, t, s0, s1, pad0, pad1, pad2;
-};
-
-// All fields are uniform across the workgroup.  An item without steps
-// (s1 < s0) is visited once, as a step that only writes its (zero) output.
-struct StepIt {
-    int idx, end;
-    int b, h, t, s0, s1, s;
-    int qs, lq, ks, lk;
-
-    __device__ __forceinline__ void load(const ItemRec* items, const int32_t* q_off,
-                                         const int32_t* kv_off, int i) {
-        const ItemRec it = items[i];
-        idx = i;
-        b = it.b;
-        h = it.h;
-        t = it.t;
-        s0 = it.s0;
-        s1 = it.s1;
-        s = it.s0;
-        qs = q_off[b];
-        lq = q_off[b + 1] - qs;
-        ks = kv_off[b];
-        lk = kv_off[b + 1] - ks;
-    }
-    __device__ __forceinline__ bool has_steps() const { return s1 >= s0; }
-    __device__ __forceinline__ bool first() const { return s == s0; }
-    __device__ __forceinline__ bool last() const { return s >= s1; }
-    // move to the next step of this bin; false at the end
-    __device__ __forceinline__ bool advance(const ItemRec* items, const int32_t* q_off,
-                                            const int32_t* kv_off) {
-        if (s < s1) {
-            ++s;
-            return true;
-        }
-        if (idx + 1 < end) {
-            load(items, q_off, kv_off, idx + 1);
-            return true;
-        }
-        return false;
-    }
+// One work item: sample rows start at qs (queries) / ks (keys) with lengths lq /
+// lk, head h, stationary tile t and streaming tiles s0..s1 (none if s1 < s0).
+struct Rec {
+    int32_t qs, lq, ks, lk, h, t, s0, s1;
 };
 
 // Does the 32 x 32 block (rows i0.., columns j0..) of a sample with lengths

@@ -9,19 +9,20 @@
 //
 // Work decomposition.  A persistent workgroup (256 threads = 4 waves) walks the
 // items of its bin (host planner, zigzag deal) as one flattened sequence of
-// (item, kv step) pairs, prefetching the next step's K/V (and the next item's Q)
-// into registers while the current step computes, so short-KV items do not
-// drain the pipeline (GDPA page, "Section details": software pipelining moved
+// (item, kv step) pairs.  Each step's tiles (K, V, and Q when the step starts an
+// item) are copied global -> LDS by DMA several steps ahead, so short-KV items do
+// not drain the pipeline (GDPA page, "Section details": software pipelining moved
 // from the inner kv loop to the outer loop; loop flattening).
 //
 // Waves are WQ x WK: each wave owns 32 query rows of the item's q tile
 // (BM = 32 WQ rows) and BNW kv rows of each step (BN = WK BNW).  Per 32-row kv
 // block a wave computes S^T = K Q^T with MFMA (K from LDS, Q held in registers),
 // masks, applies the activation in registers, and feeds the accumulator lanes
-// straight back as the B operand of O^T += V^T P^T (V^T from LDS).  When WK > 1
-// the waves' partial O are summed through LDS at the item's end.
-#include "device.hpp"
+// straight back as the B operand of O^T += V^T P^T (V^T read from the row-major
+// V tile with transposing LDS reads).  When WK > 1 the waves' partial O are
+// summed through LDS at the item's end.
 #include "kernels.hpp"
+#include "pipe.hpp"
 
 #ifndef GDPA_D
 #error "compile with -DGDPA_D=<32|64|128>"
@@ -30,233 +31,183 @@
 namespace gdpa {
 namespace {
 
-template <int D, int WQ, int BNW>
-struct FwdCfg {
+template <int D, int WQ, int BNW, int ACT>
+struct FwdPol {
     static constexpr int WK = 4 / WQ, BM = 32 * WQ, BN = WK * BNW;
     static constexpr int NKB = BNW / 32, NDB = D / 32, NKS = D / 16;
-    static constexpr int KST = D + 8;         // row-major tile stride (elements)
-    static constexpr int VST = BN + 8;        // transposed V tile stride
-    static constexpr int SZ_K = BN * KST, SZ_VT = D * VST, SZ_Q = BM * KST;
-    static constexpr int STEP_BYTES = (SZ_K + SZ_VT) * 2;
+    using TQ = AsyncTile<BM, D>;
+    using TK = AsyncTile<BN, D>;
+    static constexpr int OFF_K = TQ::BYTES, OFF_V = TQ::BYTES + TK::BYTES;
+    static constexpr int STAGE_BYTES = TQ::BYTES + 2 * TK::BYTES;
+    static constexpr int NS = Stages<STAGE_BYTES>::N;
+    static constexpr int LOADS = TQ::PER_WAVE + 2 * TK::PER_WAVE;
+    static constexpr int SOST = D + 8;   // output staging row stride (bf16)
     static constexpr int PART_BYTES = (WK - 1) * WQ * NDB * 64 * 16 * 4;
-    static constexpr int SO_BYTES = BM * KST * 2;
-    static constexpr int EPI_BYTES = PART_BYTES + SO_BYTES;
-    // double-buffer the step tiles when it fits
-    static constexpr int NBUF = (2 * STEP_BYTES + SZ_Q * 2) <= 160 * 1024 ? 2 : 1;
-    // At an item's end every region is free (Q is in registers, the next step's
-    // tiles are still in staging registers), so the epilogue reuses LDS from 0.
-    static constexpr int MAIN = NBUF * STEP_BYTES + SZ_Q * 2;
-    static constexpr int LDS = MAIN > EPI_BYTES ? MAIN : EPI_BYTES;
-    static_assert(LDS <= 160 * 1024, "LDS budget exceeded");
+    static constexpr int SO_BYTES = BM * SOST * 2;
+    static_assert(PART_BYTES <= STAGE_BYTES && SO_BYTES <= STAGE_BYTES, "epilogue must fit in a stage");
+
+    const KernelArgs& a;
+    int tid, lane, wave, wq, wk, r, hh, H, win;
+    uint32_t rs, rso;
+    float scale;
+    rsrc_t empty, rq, rk, rv;   // issuing side: descriptors of the current item's slices
+    TQ tq;
+    TK tk;
+    bf16x8 qf[NKS];
+    f32x16 acc[NDB];
+
+    __device__ FwdPol(const KernelArgs& args) : a(args) {
+        tid = threadIdx.x;
+        lane = tid & 63;
+        wave = tid >> 6;
+        wq = wave / WK;
+        wk = wave % WK;
+        r = lane & 31;
+        hh = lane >> 5;
+        H = a.H;
+        win = a.window > 0 ? a.window : (1 << 30);
+        rs = (uint32_t)H * D * 2;
+        rso = (uint32_t)H * D * (a.out_f32 ? 4 : 2);
+        scale = a.scale;
+        empty = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.q), 0, 0, 0x00020000);
+        rq = rk = rv = empty;
+        tq.init(rs, wave, lane);
+        tk.init(rs, wave, lane);
+    }
+
+    __device__ __forceinline__ void new_item(const Step& st) {
+        const size_t kvb = ((size_t)st.r.ks * H + st.r.h) * D;
+        rk = slice_rsrc((const __bf16*)a.k + kvb, st.r.lk, rs, D * 2);
+        rv = slice_rsrc((const __bf16*)a.v + kvb, st.r.lk, rs, D * 2);
+        rq = slice_rsrc((const __bf16*)a.q + ((size_t)st.r.qs * H + st.r.h) * D, st.r.lq, rs, D * 2);
+    }
+
+    __device__ __forceinline__ void issue(const Step& st, char* stage) {
+        const bool kv = st.valid && st.has_steps();
+        const bool q = kv && st.first();
+        tq.issue(rq, empty, (uint32_t)(st.r.t * BM) * rs, stage, wave, q);
+        const uint32_t so = (uint32_t)(st.s * BN) * rs;
+        tk.issue(rk, empty, so, stage + OFF_K, wave, kv);
+        tk.issue(rv, empty, so, stage + OFF_V, wave, kv);
+    }
+
+    __device__ __forceinline__ void item_start(const Step& st, const char* stage) {
+        if (st.has_steps()) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) qf[ks] = lds_row8<D>(stage, wq * 32 + r, 2 * ks + hh);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    }
+
+    __device__ __forceinline__ void compute(const Step& st, const char* stage) {
+        const int q0 = st.r.t * BM + wq * 32;
+        const int lq = st.r.lq, lk = st.r.lk;
+        if (!st.has_steps() || q0 >= lq) return;
+        const char* kt = stage + OFF_K;
+        const char* vt = stage + OFF_V;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const int jl = wk * BNW + kb * 32;   // kv row inside the step tile
+            const int j0 = st.s * BN + jl;
+            if (!block_any(q0, j0, lq, lk, win)) continue;
+            f32x16 s = {};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) s = mfma32(lds_row8<D>(kt, jl + r, 2 * ks + hh), qf[ks], s);
+            f32x16 p;
+            if (block_all(q0, j0, lq, lk, win)) {
+#pragma unroll
+                for (int c = 0; c < 16; ++c) p[c] = act_fwd<ACT>(s[c] * scale);
+            } else {
+                const int qi = q0 + r;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    const int kj = j0 + 8 * (c >> 2) + 4 * hh + (c & 3);
+                    const int dd = qi - kj;
+                    const bool ok = kj < lk && qi < lq && dd < win && -dd < win;
+                    p[c] = ok ? act_fwd<ACT>(s[c] * scale) : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const bf16x8 pb = acc_to_bf16x8(p, m);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    acc[db] = mfma32(lds_col8<D>(vt, jl + 16 * m, db * 32, lane), pb, acc[db]);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void epilogue(const Step& st, char* stage) {
+        if constexpr (WK > 1) {
+            f32x4* part = (f32x4*)stage;
+            if (wk > 0) {
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int c4 = 0; c4 < 4; ++c4)
+                        part[((((wk - 1) * WQ + wq) * NDB + db) * 4 + c4) * 64 + lane] =
+                            f32x4{acc[db][4 * c4], acc[db][4 * c4 + 1], acc[db][4 * c4 + 2], acc[db][4 * c4 + 3]};
+            }
+            lds_barrier();
+            if (wk == 0) {
+#pragma unroll
+                for (int w2 = 1; w2 < WK; ++w2)
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int c4 = 0; c4 < 4; ++c4) {
+                            const f32x4 v = part[((((w2 - 1) * WQ + wq) * NDB + db) * 4 + c4) * 64 + lane];
+                            for (int i = 0; i < 4; ++i) acc[db][4 * c4 + i] += v[i];
+                        }
+            }
+            lds_barrier();
+        }
+        const size_t ob = ((size_t)st.r.qs * H + st.r.h) * D;
+        if (a.out_f32) {
+            const rsrc_t ro = slice_rsrc((const float*)a.o + ob, st.r.lq, rso, D * 4);
+            if (wk == 0) {
+                const int row = st.r.t * BM + wq * 32 + r;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        u32x4 v;
+                        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[db][4 * j + i]);
+                        buf_store16(ro, (uint32_t)row * rso + (db * 32 + 8 * j + 4 * hh) * 4, v);
+                    }
+            }
+            return;
+        }
+        __bf16* sO = (__bf16*)stage;
+        if (wk == 0) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x2 w;
+                    w[0] = pack_bf16x2(acc[db][4 * j], acc[db][4 * j + 1]);
+                    w[1] = pack_bf16x2(acc[db][4 * j + 2], acc[db][4 * j + 3]);
+                    *(u32x2*)(sO + (wq * 32 + r) * SOST + db * 32 + 8 * j + 4 * hh) = w;
+                }
+        }
+        lds_barrier();
+        const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, st.r.lq, rso, D * 2);
+        constexpr int CPR = D / 8;
+        for (int ci = tid; ci < BM * CPR; ci += 256) {
+            const int row = ci / CPR, c = ci % CPR;
+            buf_store16(ro, (uint32_t)(st.r.t * BM + row) * rso + c * 16, *(const u32x4*)(sO + row * SOST + 8 * c));
+        }
+    }
 };
 
 template <int D, int WQ, int BNW, int ACT>
-__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const KernelArgs a) {
-    using C = FwdCfg<D, WQ, BNW>;
-    constexpr int WK = C::WK, BM = C::BM, BN = C::BN, NKB = C::NKB, NDB = C::NDB, NKS = C::NKS;
-    constexpr int KST = C::KST, VST = C::VST;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wq = wave / WK, wk = wave % WK;
-    const int r = lane & 31, hh = lane >> 5;
-
-    const int bin = logical_bin(a.P);
-    const ItemRec* items = reinterpret_cast<const ItemRec*>(a.items);
-    StepIt cur;
-    cur.end = a.bin_ptr[bin + 1];
-    const int first_item = a.bin_ptr[bin];
-    if (first_item >= cur.end) return;
-    cur.load(items, a.q_off, a.kv_off, first_item);
-
-    const int H = a.H;
-    const uint32_t rs = (uint32_t)H * D * 2;                       // bf16 row stride
-    const uint32_t rso = (uint32_t)H * D * (a.out_f32 ? 4 : 2);    // output row stride
-    const int win = a.window > 0 ? a.window : (1 << 30);
-    const float scale = a.scale;
-    const __bf16* gq = (const __bf16*)a.q;
-    const __bf16* gk = (const __bf16*)a.k;
-    const __bf16* gv = (const __bf16*)a.v;
-
-    __bf16* sQ = (__bf16*)(smem + C::NBUF * C::STEP_BYTES);
-    auto sK = [&](int buf) { return (__bf16*)(smem + buf * C::STEP_BYTES); };
-    auto sVT = [&](int buf) { return (__bf16*)(smem + buf * C::STEP_BYTES) + C::SZ_K; };
-
-    TileStage<BN, D> stK, stV;
-    TileStage<BM, D> stQ;
-
-    auto issue_loads = [&](const StepIt& st, bool with_q) {
-        if (st.has_steps()) {
-            const size_t kvb = ((size_t)st.ks * H + st.h) * D;
-            const rsrc_t rk = slice_rsrc(gk + kvb, st.lk, rs, D * 2);
-            const rsrc_t rv = slice_rsrc(gv + kvb, st.lk, rs, D * 2);
-            stK.load(rk, st.s * BN, rs, tid);
-            stV.load(rv, st.s * BN, rs, tid);
-        }
-        if (with_q) {
-            const rsrc_t rq = slice_rsrc(gq + ((size_t)st.qs * H + st.h) * D, st.lq, rs, D * 2);
-            stQ.load(rq, st.t * BM, rs, tid);
-        }
-    };
-    auto commit = [&](const StepIt& st, int buf, bool with_q) {
-        if (st.has_steps()) {
-            stK.template store_rows<KST>(sK(buf), tid);
-            stV.template store_cols<VST>(sVT(buf), tid);
-        }
-        if (with_q) stQ.template store_rows<KST>(sQ, tid);
-    };
-
-    // prologue: the first step's tiles
-    issue_loads(cur, true);
-    commit(cur, 0, true);
-    __syncthreads();
-
-    f32x16 acc[NDB];
-    bf16x8 qf[NKS];
-    int buf = 0;
-    for (;;) {
-        const bool first = cur.first(), last = cur.last();
-        if (first) {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                qf[ks] = *(const bf16x8*)(sQ + (wq * 32 + r) * KST + 16 * ks + 8 * hh);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-        }
-
-        StepIt nx = cur;
-        const bool has_next = nx.advance(items, a.q_off, a.kv_off);
-        const bool nx_first = has_next && nx.first();
-        if (has_next) issue_loads(nx, nx_first);
-
-        // ---- compute this step ----
-        const int q0 = cur.t * BM + wq * 32;
-        if (cur.has_steps() && q0 < cur.lq) {
-            const __bf16* k_t = sK(buf);
-            const __bf16* vt_t = sVT(buf);
-            bf16x8 pf[NKB][2];
-            bool act_blk[NKB];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                const int j0 = cur.s * BN + wk * BNW + kb * 32;
-                act_blk[kb] = block_any(q0, j0, cur.lq, cur.lk, win);
-                if (!act_blk[kb]) continue;
-                f32x16 s = {};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8 ka = *(const bf16x8*)(k_t + (wk * BNW + kb * 32 + r) * KST + 16 * ks + 8 * hh);
-                    s = mfma32(ka, qf[ks], s);
-                }
-                f32x16 p;
-                if (block_all(q0, j0, cur.lq, cur.lk, win)) {
-#pragma unroll
-                    for (int c = 0; c < 16; ++c) p[c] = act_fwd<ACT>(s[c] * scale);
-                } else {
-                    const int qi = q0 + r;
-#pragma unroll
-                    for (int c = 0; c < 16; ++c) {
-                        const int kj = j0 + 8 * (c >> 2) + 4 * hh + (c & 3);
-                        const int dd = qi - kj;
-                        const bool ok = kj < cur.lk && qi < cur.lq && dd < win && -dd < win;
-                        p[c] = ok ? act_fwd<ACT>(s[c] * scale) : 0.0f;
-                    }
-                }
-                pf[kb][0] = acc_to_bf16x8(p, 0);
-                pf[kb][1] = acc_to_bf16x8(p, 1);
-            }
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                if (!act_blk[kb]) continue;
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const bf16x8 va = *(const bf16x8*)(vt_t + (db * 32 + r) * VST + wk * BNW + kb * 32 + 16 * m + 8 * hh);
-                        acc[db] = mfma32(va, pf[kb][m], acc[db]);
-                    }
-                }
-            }
-        }
-
-        // ---- epilogue: the item's output tile ----
-        if (last) {
-            __syncthreads();   // every wave is done with this step's tiles
-            char* epi = smem;
-            if constexpr (WK > 1) {
-                float* part = (float*)epi;
-                if (wk > 0) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        float* dst = part + ((((wk - 1) * WQ + wq) * NDB + db) * 64 + lane) * 16;
-#pragma unroll
-                        for (int c4 = 0; c4 < 4; ++c4)
-                            *(f32x4*)(dst + 4 * c4) = f32x4{acc[db][4 * c4], acc[db][4 * c4 + 1], acc[db][4 * c4 + 2], acc[db][4 * c4 + 3]};
-                    }
-                }
-                __syncthreads();
-                if (wk == 0) {
-#pragma unroll
-                    for (int w2 = 1; w2 < WK; ++w2) {
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            const float* src = part + ((((w2 - 1) * WQ + wq) * NDB + db) * 64 + lane) * 16;
-#pragma unroll
-                            for (int c = 0; c < 16; ++c) acc[db][c] += src[c];
-                        }
-                    }
-                }
-            }
-            const size_t ob = ((size_t)cur.qs * H + cur.h) * D;
-            if (a.out_f32) {
-                const rsrc_t ro = slice_rsrc((const float*)a.o + ob, cur.lq, rso, D * 4);
-                if (wk == 0) {
-                    const int row = cur.t * BM + wq * 32 + r;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int col = db * 32 + 8 * j + 4 * hh;
-                            u32x4 v;
-                            for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[db][4 * j + i]);
-                            buf_store16(ro, (uint32_t)row * rso + col * 4, v);
-                        }
-                }
-            } else {
-                __bf16* sO = (__bf16*)(epi + C::PART_BYTES);
-                if (wk == 0) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            u32x2 w;
-                            w[0] = pack_bf16x2(acc[db][4 * j], acc[db][4 * j + 1]);
-                            w[1] = pack_bf16x2(acc[db][4 * j + 2], acc[db][4 * j + 3]);
-                            *(u32x2*)(sO + (wq * 32 + r) * KST + db * 32 + 8 * j + 4 * hh) = w;
-                        }
-                }
-                __syncthreads();
-                const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, cur.lq, rso, D * 2);
-                constexpr int CPR = D / 8;
-                for (int ci = tid; ci < BM * CPR; ci += 256) {
-                    const int row = ci / CPR, c = ci % CPR;
-                    const u32x4 v = *(const u32x4*)(sO + row * KST + 8 * c);
-                    buf_store16(ro, (uint32_t)(cur.t * BM + row) * rso + c * 16, v);
-                }
-            }
-        }
-
-        if (!has_next) break;
-        if constexpr (C::NBUF == 1) {
-            __syncthreads();   // single buffer: all waves done before it is overwritten
-            commit(nx, 0, nx_first);
-        } else {
-            if (last) __syncthreads();   // the epilogue's LDS reads are done
-            commit(nx, buf ^ 1, nx_first);
-            buf ^= 1;
-        }
-        __syncthreads();
-        cur = nx;
-    }
+__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const KernelArgs a, const Rec* __restrict__ recs,
+                                                          const int32_t* __restrict__ bin_ptr) {
+    using Pol = FwdPol<D, WQ, BNW, ACT>;
+    __shared__ __attribute__((aligned(1024))) char smem[Pol::NS * Pol::STAGE_BYTES];
+    Pol pol(a);
+    run_pipeline(pol, a.P, recs, bin_ptr, smem);
 }
 
 template <int WQ, int BNW, int ACT>
@@ -295,7 +246,9 @@ hipError_t GDPA_CAT(launch_fwd_bf16_d, GDPA_D)(const KernelArgs& a, int waves, i
     if (!f) return hipErrorInvalidValue;
     if (a.P <= 0) return hipSuccess;
     KernelArgs args = a;
-    void* params[] = {&args};
+    const void* recs = a.items;
+    const int32_t* bin_ptr = a.bin_ptr;
+    void* params[] = {&args, &recs, &bin_ptr};
     return hipLaunchKernel(f, dim3(a.P), dim3(256), params, 0, s);
 }
 

@@ -21,7 +21,7 @@ struct KernelArgs {
     void* dv;
     const int32_t* q_off;
     const int32_t* kv_off;
-    const Item* items;
+    const void* items;          // device work-list records (Rec), bin-major
     const int32_t* bin_ptr;
     int P;          // persistent workgroups = bins
     int B;          // samples

@@ -133,4 +133,22 @@ std::vector<int32_t> export_list(const WorkList& wl) {
     return out;
 }
 
+std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
+                                   const std::vector<int32_t>& kv_off) {
+    std::vector<DevRec> out(wl.items.size());
+    for (size_t i = 0; i < wl.items.size(); ++i) {
+        const Item& it = wl.items[i];
+        DevRec& d = out[i];
+        d.qs = q_off[it.b];
+        d.lq = q_off[it.b + 1] - q_off[it.b];
+        d.ks = kv_off[it.b];
+        d.lk = kv_off[it.b + 1] - kv_off[it.b];
+        d.h = it.h;
+        d.t = it.t;
+        d.s0 = it.s0;
+        d.s1 = it.s1;
+    }
+    return out;
+}
+
 }  // namespace gdpa

@@ -30,6 +30,14 @@ struct Item {
 };
 static_assert(sizeof(Item) == 32, "Item must be 32 bytes");
 
+// The record a kernel reads per work item: the sample's row ranges are
+// resolved on the host, so a kernel needs one load per item and no dependent
+// loads of the offset arrays.
+struct DevRec {
+    int32_t qs, lq, ks, lk, h, t, s0, s1;
+};
+static_assert(sizeof(DevRec) == 32, "DevRec must be 32 bytes");
+
 struct WorkList {
     int kind = 0, P = 0, t_stat = 0, t_strm = 0, waves = 0, bnw = 0;
     std::vector<int32_t> bin_ptr;   // P + 1
@@ -50,5 +58,7 @@ void tile_sizes(int kind, int waves, int bnw, int* t_stat, int* t_strm);
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
                    int H, int window, int P, int waves, int bnw, bool zigzag);
 std::vector<int32_t> export_list(const WorkList& wl);
+std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
+                                   const std::vector<int32_t>& kv_off);
 
 }  // namespace gdpa
