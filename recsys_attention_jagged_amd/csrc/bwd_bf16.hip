@@ -120,7 +120,7 @@ struct DqPol : Lanes {
     static constexpr int LOADS = 2 * TQ::PER_WAVE + 2 * TK::PER_WAVE;
     static_assert((WK - 1) * WQ * NDB * 4096 <= STAGE_BYTES && BM * (D + 8) * 2 <= STAGE_BYTES, "epilogue");
 
-    const KernelArgs& a;
+    const KernelArgs a;   // by value: kept in SGPRs, not re-read from the argument segment
     int wq, wk, H, win;
     uint32_t rs, rso;
     float scale;
@@ -153,7 +153,7 @@ struct DqPol : Lanes {
         ro = slice_rsrc((const __bf16*)a.dout + qb, st.r.lq, rs, D * 2);
     }
 
-    __device__ __forceinline__ void issue(const Step& st, char* stage) {
+    __device__ __forceinline__ void issue(const Step& st, uint32_t stage) {
         const bool kv = st.valid && st.has_steps();
         const bool q = kv && st.first();
         const uint32_t sq = (uint32_t)(st.r.t * BM) * rs, sk = (uint32_t)(st.s * BN) * rs;
@@ -240,7 +240,7 @@ struct DkdvPol : Lanes {
     static constexpr int LOADS = 2 * TK::PER_WAVE + 2 * TQ::PER_WAVE;
     static_assert((WQ - 1) * WK * NDB * 4096 <= STAGE_BYTES && 2 * BK * (D + 8) * 2 <= STAGE_BYTES, "epilogue");
 
-    const KernelArgs& a;
+    const KernelArgs a;   // by value: kept in SGPRs, not re-read from the argument segment
     int wq, wk, H, win;
     uint32_t rs, rso;
     float scale;
@@ -273,7 +273,7 @@ struct DkdvPol : Lanes {
         ro = slice_rsrc((const __bf16*)a.dout + qb, st.r.lq, rs, D * 2);
     }
 
-    __device__ __forceinline__ void issue(const Step& st, char* stage) {
+    __device__ __forceinline__ void issue(const Step& st, uint32_t stage) {
         const bool qs = st.valid && st.has_steps();
         const bool kv = qs && st.first();
         const uint32_t sk = (uint32_t)(st.r.t * BK) * rs, sq = (uint32_t)(st.s * BQ) * rs;

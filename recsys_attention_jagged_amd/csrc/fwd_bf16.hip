@@ -46,7 +46,7 @@ struct FwdPol {
     static constexpr int SO_BYTES = BM * SOST * 2;
     static_assert(PART_BYTES <= STAGE_BYTES && SO_BYTES <= STAGE_BYTES, "epilogue must fit in a stage");
 
-    const KernelArgs& a;
+    const KernelArgs a;   // by value: kept in SGPRs, not re-read from the argument segment
     int tid, lane, wave, wq, wk, r, hh, H, win;
     uint32_t rs, rso;
     float scale;
@@ -82,7 +82,7 @@ struct FwdPol {
         rq = slice_rsrc((const __bf16*)a.q + ((size_t)st.r.qs * H + st.r.h) * D, st.r.lq, rs, D * 2);
     }
 
-    __device__ __forceinline__ void issue(const Step& st, char* stage) {
+    __device__ __forceinline__ void issue(const Step& st, uint32_t stage) {
         const bool kv = st.valid && st.has_steps();
         const bool q = kv && st.first();
         tq.issue(rq, empty, (uint32_t)(st.r.t * BM) * rs, stage, wave, q);

@@ -76,15 +76,18 @@ __device__ __forceinline__ bf16x8 lds_col8(const char* tile, int row0, int col0,
 // -------------------------------------------------------------------------
 // async tiles
 // -------------------------------------------------------------------------
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // One wave instruction: lane l's 16 bytes at byte offset `voff` of the buffer
-// land at lds + 16 l.  The whole offset is in the VGPR: the hardware range check
-// covers the VGPR offset, not the scalar one.
-__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, char* lds) {
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(size_t)(__attribute__((address_space(3))) char*)lds);
+// land at LDS address lds + 16 l (lds uniform).  The whole offset is in the
+// VGPR: the hardware range check covers the VGPR offset, not the scalar one.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(m0v), "v"(voff), "s"(rs)
+                 : "s"(lds), "v"(voff), "s"(rs)
                  : "memory", "m0");
 }
 
@@ -108,13 +111,14 @@ struct AsyncTile {
         }
     }
 
-    // rows [row0, row0 + ROWS) of the slice described by `rs`; row_off = row0 * stride
-    __device__ __forceinline__ void issue(rsrc_t rs, rsrc_t empty, uint32_t row_off, char* tile, int wave,
+    // rows [row0, row0 + ROWS) of the slice described by `rs`; row_off = row0 * stride;
+    // tile = LDS address of the tile; wave and real are uniform
+    __device__ __forceinline__ void issue(rsrc_t rs, rsrc_t empty, uint32_t row_off, uint32_t tile, int wave,
                                           bool real) const {
 #pragma unroll
         for (int j = 0; j < PER_WAVE; ++j) {
-            const int ins = wave + 4 * j;
-            char* dst = tile + ins * 1024;
+            const int ins = __builtin_amdgcn_readfirstlane(wave) + 4 * j;   // uniform
+            const uint32_t dst = tile + (uint32_t)ins * 1024u;
             if (real && ins < WINSTR) dma16(rs, off[j] + row_off, dst);
             else dma16(empty, 0u, dst);
         }
@@ -147,7 +151,8 @@ struct Step {
 };
 
 // Pol provides: NS (stages), STAGE_BYTES, LOADS (DMA instructions per wave per
-// stage), new_item(step) (per-item descriptors for issuing), issue(step, stage),
+// stage), new_item(step) (per-item descriptors for issuing), issue(step, stage
+// LDS address),
 // item_start(step, stage), compute(step, stage), epilogue(step, stage) (may use
 // the whole stage).  The issuing walk runs NS steps ahead of the computing one;
 // the computing side receives each step's record through a shift register, so
@@ -167,20 +172,23 @@ __device__ __forceinline__ void run_pipeline(Pol& pol, int P, const Rec* __restr
     is.s = is.r.s0;
     is.valid = true;
     pol.new_item(is);
+    Rec next = recs[idx + 1 < end ? idx + 1 : idx];   // prefetched one item ahead
 
+    const uint32_t base = lds_addr(smem);
     Step pipe[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         pipe[j] = is;
-        pol.issue(is, smem + j * Pol::STAGE_BYTES);
+        pol.issue(is, base + j * Pol::STAGE_BYTES);
         // advance the issuing walk
         if (is.valid) {
             if (is.s < is.r.s1) {
                 ++is.s;
             } else if (++idx < end) {
-                is.r = recs[idx];
+                is.r = next;
                 is.s = is.r.s0;
                 pol.new_item(is);
+                next = recs[idx + 1 < end ? idx + 1 : idx];
             } else {
                 is.valid = false;
             }
@@ -198,7 +206,7 @@ __device__ __forceinline__ void run_pipeline(Pol& pol, int P, const Rec* __restr
             pol.epilogue(cur, st);
             lds_barrier();
         }
-        pol.issue(is, st);
+        pol.issue(is, base + stage * Pol::STAGE_BYTES);
 #pragma unroll
         for (int j = 0; j + 1 < NS; ++j) pipe[j] = pipe[j + 1];
         pipe[NS - 1] = is;
@@ -206,9 +214,10 @@ __device__ __forceinline__ void run_pipeline(Pol& pol, int P, const Rec* __restr
             if (is.s < is.r.s1) {
                 ++is.s;
             } else if (++idx < end) {
-                is.r = recs[idx];
+                is.r = next;
                 is.s = is.r.s0;
                 pol.new_item(is);
+                next = recs[idx + 1 < end ? idx + 1 : idx];
             } else {
                 is.valid = false;
             }
