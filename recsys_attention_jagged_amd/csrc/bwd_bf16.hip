@@ -117,7 +117,6 @@ struct DqPol : Lanes {
     static constexpr int OFF_O = TQ::BYTES, OFF_K = 2 * TQ::BYTES, OFF_V = 2 * TQ::BYTES + TK::BYTES;
     static constexpr int STAGE_BYTES = 2 * TQ::BYTES + 2 * TK::BYTES;
     static constexpr int NS = Stages<STAGE_BYTES>::N;
-    static constexpr int LOADS = 2 * TQ::PER_WAVE + 2 * TK::PER_WAVE;
     static_assert((WK - 1) * WQ * NDB * 4096 <= STAGE_BYTES && BM * (D + 8) * 2 <= STAGE_BYTES, "epilogue");
 
     const KernelArgs a;   // by value: kept in SGPRs, not re-read from the argument segment
@@ -153,14 +152,18 @@ struct DqPol : Lanes {
         ro = slice_rsrc((const __bf16*)a.dout + qb, st.r.lq, rs, D * 2);
     }
 
-    __device__ __forceinline__ void issue(const Step& st, uint32_t stage) {
-        const bool kv = st.valid && st.has_steps();
-        const bool q = kv && st.first();
-        const uint32_t sq = (uint32_t)(st.r.t * BM) * rs, sk = (uint32_t)(st.s * BN) * rs;
-        tq.issue(rq, empty, sq, stage, wave, q);
-        tq.issue(ro, empty, sq, stage + OFF_O, wave, q);
-        tk.issue(rk, empty, sk, stage + OFF_K, wave, kv);
-        tk.issue(rv, empty, sk, stage + OFF_V, wave, kv);
+    __device__ __forceinline__ int issue(const Step& st, uint32_t stage) {
+        if (!st.valid || !st.has_steps()) return 0;
+        int n = 0;
+        if (st.first()) {
+            const uint32_t sq = (uint32_t)(st.r.t * BM) * rs;
+            n += tq.issue(rq, sq, stage, wave);
+            n += tq.issue(ro, sq, stage + OFF_O, wave);
+        }
+        const uint32_t sk = (uint32_t)(st.s * BN) * rs;
+        n += tk.issue(rk, sk, stage + OFF_K, wave);
+        n += tk.issue(rv, sk, stage + OFF_V, wave);
+        return n;
     }
 
     __device__ __forceinline__ void item_start(const Step& st, const char* stage) {
@@ -237,7 +240,6 @@ struct DkdvPol : Lanes {
     static constexpr int OFF_V = TK::BYTES, OFF_Q = 2 * TK::BYTES, OFF_O = 2 * TK::BYTES + TQ::BYTES;
     static constexpr int STAGE_BYTES = 2 * TK::BYTES + 2 * TQ::BYTES;
     static constexpr int NS = Stages<STAGE_BYTES>::N;
-    static constexpr int LOADS = 2 * TK::PER_WAVE + 2 * TQ::PER_WAVE;
     static_assert((WQ - 1) * WK * NDB * 4096 <= STAGE_BYTES && 2 * BK * (D + 8) * 2 <= STAGE_BYTES, "epilogue");
 
     const KernelArgs a;   // by value: kept in SGPRs, not re-read from the argument segment
@@ -273,14 +275,18 @@ struct DkdvPol : Lanes {
         ro = slice_rsrc((const __bf16*)a.dout + qb, st.r.lq, rs, D * 2);
     }
 
-    __device__ __forceinline__ void issue(const Step& st, uint32_t stage) {
-        const bool qs = st.valid && st.has_steps();
-        const bool kv = qs && st.first();
-        const uint32_t sk = (uint32_t)(st.r.t * BK) * rs, sq = (uint32_t)(st.s * BQ) * rs;
-        tk.issue(rk, empty, sk, stage, wave, kv);
-        tk.issue(rv, empty, sk, stage + OFF_V, wave, kv);
-        tq.issue(rq, empty, sq, stage + OFF_Q, wave, qs);
-        tq.issue(ro, empty, sq, stage + OFF_O, wave, qs);
+    __device__ __forceinline__ int issue(const Step& st, uint32_t stage) {
+        if (!st.valid || !st.has_steps()) return 0;
+        int n = 0;
+        if (st.first()) {
+            const uint32_t sk = (uint32_t)(st.r.t * BK) * rs;
+            n += tk.issue(rk, sk, stage, wave);
+            n += tk.issue(rv, sk, stage + OFF_V, wave);
+        }
+        const uint32_t sq = (uint32_t)(st.s * BQ) * rs;
+        n += tq.issue(rq, sq, stage + OFF_Q, wave);
+        n += tq.issue(ro, sq, stage + OFF_O, wave);
+        return n;
     }
 
     __device__ __forceinline__ void item_start(const Step& st, const char* stage) {

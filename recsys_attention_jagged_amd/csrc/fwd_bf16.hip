@@ -40,7 +40,6 @@ struct FwdPol {
     static constexpr int OFF_K = TQ::BYTES, OFF_V = TQ::BYTES + TK::BYTES;
     static constexpr int STAGE_BYTES = TQ::BYTES + 2 * TK::BYTES;
     static constexpr int NS = Stages<STAGE_BYTES>::N;
-    static constexpr int LOADS = TQ::PER_WAVE + 2 * TK::PER_WAVE;
     static constexpr int SOST = D + 8;   // output staging row stride (bf16)
     static constexpr int PART_BYTES = (WK - 1) * WQ * NDB * 64 * 16 * 4;
     static constexpr int SO_BYTES = BM * SOST * 2;
@@ -82,13 +81,14 @@ struct FwdPol {
         rq = slice_rsrc((const __bf16*)a.q + ((size_t)st.r.qs * H + st.r.h) * D, st.r.lq, rs, D * 2);
     }
 
-    __device__ __forceinline__ void issue(const Step& st, uint32_t stage) {
-        const bool kv = st.valid && st.has_steps();
-        const bool q = kv && st.first();
-        tq.issue(rq, empty, (uint32_t)(st.r.t * BM) * rs, stage, wave, q);
+    __device__ __forceinline__ int issue(const Step& st, uint32_t stage) {
+        if (!st.valid || !st.has_steps()) return 0;
+        int n = 0;
+        if (st.first()) n += tq.issue(rq, (uint32_t)(st.r.t * BM) * rs, stage, wave);
         const uint32_t so = (uint32_t)(st.s * BN) * rs;
-        tk.issue(rk, empty, so, stage + OFF_K, wave, kv);
-        tk.issue(rv, empty, so, stage + OFF_V, wave, kv);
+        n += tk.issue(rk, so, stage + OFF_K, wave);
+        n += tk.issue(rv, so, stage + OFF_V, wave);
+        return n;
     }
 
     __device__ __forceinline__ void item_start(const Step& st, const char* stage) {

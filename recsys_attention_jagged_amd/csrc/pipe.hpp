@@ -12,9 +12,10 @@
 // Rows outside the (sample, head) slice are out of the buffer descriptor's
 // range and arrive as zeros.
 //
-// Every stage issues the same number of DMA instructions per wave (unused ones
-// are issued with an empty descriptor into the tile's own padding), so waiting
-// for the oldest stage is one compile-time `s_waitcnt vmcnt(N)`.  The DMA is
+// Each wave counts the DMA instructions it issued per stage; since loads
+// complete in issue order, waiting for the oldest stage is `s_waitcnt vmcnt(n)`
+// with n = the instructions of the later stages.  A stage only loads what its
+// step needs (the stationary tile only when the step starts an item).  The DMA is
 // issued from inline assembly: the compiler then neither sees the asynchronous
 // LDS writes nor inserts full `vmcnt(0)` waits before LDS reads; ordering is
 // kept by the explicit waits and barriers below (all with memory clobbers).
@@ -112,23 +113,93 @@ struct AsyncTile {
     }
 
     // rows [row0, row0 + ROWS) of the slice described by `rs`; row_off = row0 * stride;
-    // tile = LDS address of the tile; wave and real are uniform
-    __device__ __forceinline__ void issue(rsrc_t rs, rsrc_t empty, uint32_t row_off, uint32_t tile, int wave,
-                                          bool real) const {
+    // tile = LDS address of the tile.  Returns the number of DMA instructions
+    // this wave issued (uniform).
+    __device__ __forceinline__ int issue(rsrc_t rs, uint32_t row_off, uint32_t tile, int wave) const {
+        const int w = __builtin_amdgcn_readfirstlane(wave);
+        int n = 0;
 #pragma unroll
         for (int j = 0; j < PER_WAVE; ++j) {
-            const int ins = __builtin_amdgcn_readfirstlane(wave) + 4 * j;   // uniform
-            const uint32_t dst = tile + (uint32_t)ins * 1024u;
-            if (real && ins < WINSTR) dma16(rs, off[j] + row_off, dst);
-            else dma16(empty, 0u, dst);
+            const int ins = w + 4 * j;   // uniform
+            if (ins < WINSTR) {
+                dma16(rs, off[j] + row_off, tile + (uint32_t)ins * 1024u);
+                ++n;
+            }
         }
+        return n;
     }
 };
 
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+// Wait until at most n vector-memory instructions of this wave are in flight
+// (n uniform; the count needs an immediate, hence the switch), then barrier.
+__device__ __forceinline__ void wait_vm_barrier(int n) {
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+        case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+        case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
+        case 14: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+        case 15: asm volatile("s_waitcnt vmcnt(15)" ::: "memory"); break;
+        case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+        case 17: asm volatile("s_waitcnt vmcnt(17)" ::: "memory"); break;
+        case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+        case 19: asm volatile("s_waitcnt vmcnt(19)" ::: "memory"); break;
+        case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+        case 21: asm volatile("s_waitcnt vmcnt(21)" ::: "memory"); break;
+        case 22: asm volatile("s_waitcnt vmcnt(22)" ::: "memory"); break;
+        case 23: asm volatile("s_waitcnt vmcnt(23)" ::: "memory"); break;
+        case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+        case 25: asm volatile("s_waitcnt vmcnt(25)" ::: "memory"); break;
+        case 26: asm volatile("s_waitcnt vmcnt(26)" ::: "memory"); break;
+        case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+        case 28: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+        case 29: asm volatile("s_waitcnt vmcnt(29)" ::: "memory"); break;
+        case 30: asm volatile("s_waitcnt vmcnt(30)" ::: "memory"); break;
+        case 31: asm volatile("s_waitcnt vmcnt(31)" ::: "memory"); break;
+        case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+        case 33: asm volatile("s_waitcnt vmcnt(33)" ::: "memory"); break;
+        case 34: asm volatile("s_waitcnt vmcnt(34)" ::: "memory"); break;
+        case 35: asm volatile("s_waitcnt vmcnt(35)" ::: "memory"); break;
+        case 36: asm volatile("s_waitcnt vmcnt(36)" ::: "memory"); break;
+        case 37: asm volatile("s_waitcnt vmcnt(37)" ::: "memory"); break;
+        case 38: asm volatile("s_waitcnt vmcnt(38)" ::: "memory"); break;
+        case 39: asm volatile("s_waitcnt vmcnt(39)" ::: "memory"); break;
+        case 40: asm volatile("s_waitcnt vmcnt(40)" ::: "memory"); break;
+        case 41: asm volatile("s_waitcnt vmcnt(41)" ::: "memory"); break;
+        case 42: asm volatile("s_waitcnt vmcnt(42)" ::: "memory"); break;
+        case 43: asm volatile("s_waitcnt vmcnt(43)" ::: "memory"); break;
+        case 44: asm volatile("s_waitcnt vmcnt(44)" ::: "memory"); break;
+        case 45: asm volatile("s_waitcnt vmcnt(45)" ::: "memory"); break;
+        case 46: asm volatile("s_waitcnt vmcnt(46)" ::: "memory"); break;
+        case 47: asm volatile("s_waitcnt vmcnt(47)" ::: "memory"); break;
+        case 48: asm volatile("s_waitcnt vmcnt(48)" ::: "memory"); break;
+        case 49: asm volatile("s_waitcnt vmcnt(49)" ::: "memory"); break;
+        case 50: asm volatile("s_waitcnt vmcnt(50)" ::: "memory"); break;
+        case 51: asm volatile("s_waitcnt vmcnt(51)" ::: "memory"); break;
+        case 52: asm volatile("s_waitcnt vmcnt(52)" ::: "memory"); break;
+        case 53: asm volatile("s_waitcnt vmcnt(53)" ::: "memory"); break;
+        case 54: asm volatile("s_waitcnt vmcnt(54)" ::: "memory"); break;
+        case 55: asm volatile("s_waitcnt vmcnt(55)" ::: "memory"); break;
+        case 56: asm volatile("s_waitcnt vmcnt(56)" ::: "memory"); break;
+        case 57: asm volatile("s_waitcnt vmcnt(57)" ::: "memory"); break;
+        case 58: asm volatile("s_waitcnt vmcnt(58)" ::: "memory"); break;
+        case 59: asm volatile("s_waitcnt vmcnt(59)" ::: "memory"); break;
+        case 60: asm volatile("s_waitcnt vmcnt(60)" ::: "memory"); break;
+        case 61: asm volatile("s_waitcnt vmcnt(61)" ::: "memory"); break;
+        case 62: asm volatile("s_waitcnt vmcnt(62)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(63)" ::: "memory"); break;
+    }
+    asm volatile("s_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -150,9 +221,9 @@ struct Step {
     __device__ __forceinline__ bool last() const { return s >= r.s1; }
 };
 
-// Pol provides: NS (stages), STAGE_BYTES, LOADS (DMA instructions per wave per
-// stage), new_item(step) (per-item descriptors for issuing), issue(step, stage
-// LDS address),
+// Pol provides: NS (stages), STAGE_BYTES, new_item(step) (per-item descriptors
+// for issuing), issue(step, stage LDS address) -> DMA instructions this wave
+// issued,
 // item_start(step, stage), compute(step, stage), epilogue(step, stage) (may use
 // the whole stage).  The issuing walk runs NS steps ahead of the computing one;
 // the computing side receives each step's record through a shift register, so
@@ -176,10 +247,11 @@ __device__ __forceinline__ void run_pipeline(Pol& pol, int P, const Rec* __restr
 
     const uint32_t base = lds_addr(smem);
     Step pipe[NS];
+    int cnt[NS];   // DMA instructions this wave issued for each stage in flight
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         pipe[j] = is;
-        pol.issue(is, base + j * Pol::STAGE_BYTES);
+        cnt[j] = pol.issue(is, base + j * Pol::STAGE_BYTES);
         // advance the issuing walk
         if (is.valid) {
             if (is.s < is.r.s1) {
@@ -196,7 +268,12 @@ __device__ __forceinline__ void run_pipeline(Pol& pol, int P, const Rec* __restr
     }
     int stage = 0;
     for (;;) {
-        wait_vm_barrier<(NS - 1) * Pol::LOADS>();
+        // loads complete in issue order: the oldest stage has landed once no more
+        // than the later stages' instructions remain (stores only make this stricter)
+        int later = 0;
+#pragma unroll
+        for (int j = 1; j < NS; ++j) later += cnt[j];
+        wait_vm_barrier(later);
         const Step cur = pipe[0];
         char* st = smem + stage * Pol::STAGE_BYTES;
         if (cur.first()) pol.item_start(cur, st);
@@ -206,10 +283,14 @@ __device__ __forceinline__ void run_pipeline(Pol& pol, int P, const Rec* __restr
             pol.epilogue(cur, st);
             lds_barrier();
         }
-        pol.issue(is, base + stage * Pol::STAGE_BYTES);
+        const int issued = pol.issue(is, base + stage * Pol::STAGE_BYTES);
 #pragma unroll
-        for (int j = 0; j + 1 < NS; ++j) pipe[j] = pipe[j + 1];
+        for (int j = 0; j + 1 < NS; ++j) {
+            pipe[j] = pipe[j + 1];
+            cnt[j] = cnt[j + 1];
+        }
         pipe[NS - 1] = is;
+        cnt[NS - 1] = issued;
         if (is.valid) {
             if (is.s < is.r.s1) {
                 ++is.s;
