@@ -42,6 +42,36 @@ def kernel_bytes(H, d, Tq, Tk):
             "dq": e * (3 * Tq + 2 * Tk)}           # Q, dO, K, V -> dQ
 
 
+KERNEL_SOURCES = ("device.hpp", "pipe.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "kernels.hpp", "plan.cpp",
+                  "plan.hpp", "gelu_poly.h")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel and planner sources (identifies the build the counters came from)."""
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "recsys_attention_jagged_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(root, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary of `workload`,
+    or None if there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes")
+
+
 def cpu_baseline(inp, budget_s=15.0):
     """Time the fp64 oracle (forward + backward) on a prefix of the batch."""
     import numpy as np
@@ -83,6 +113,9 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 3 times (reference kernel for "
+                         "calibrating the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -94,6 +127,16 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return 0
     import recsys_attention_jagged_amd as G
     from gdpa_workloads import WORKLOADS, make_workload
 
@@ -185,7 +228,8 @@ def main(argv=None):
         "plan_ms": round(plan_ms, 1),
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": kb[dom], "traffic": measured_traffic(w["name"], dom)},
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
