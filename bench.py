@@ -42,7 +42,7 @@ def kernel_bytes(H, d, Tq, Tk):
             "dq": e * (3 * Tq + 2 * Tk)}           # Q, dO, K, V -> dQ
 
 
-KERNEL_SOURCES = ("device.hpp", "pipe.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "kernels.hpp", "plan.cpp",
+KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "kernels.hpp", "plan.cpp",
                   "plan.hpp", "gelu_poly.h")
 
 

@@ -22,10 +22,10 @@ Readings (the page gives no cost model or tie-break):
     rounds and to P - 1 - (r mod P) in odd rounds (round = r // P);
   * per-bin CSR keeps each bin's items in deal order.
 
-Three lists are planned: "fwd" and "dq" (Q-stationary: t is a q tile of BM rows,
-steps are kv tiles of BN rows) and "dkdv" (KV-stationary: t is a kv tile of BK
-rows, steps are q tiles of BQ rows).  Tile sizes come from the wave layout:
-BM = 32 WQ, BN = (4 / WQ) BNW; BK = 32 WK, BQ = 32 (4 / WK).
+Three lists are planned: "fwd" and "dq" (Q-stationary: t is a q tile of 32 NB
+rows, steps are kv tiles of 32 rows) and "dkdv" (KV-stationary: t is a kv tile of
+32 rows, steps are q tiles of 32 rows).  One wave processes one item; NB (the
+32-row stationary blocks per item) comes from the length statistics.
 """
 from __future__ import annotations
 
@@ -39,34 +39,18 @@ def _ceil_div(a: int, b: int) -> int:
 
 
 def auto_layout(lq, lk, window: int = 0):
-    """Wave layouts chosen from the length statistics (integer rules)."""
+    """Stationary 32-row blocks per item: 2 for the Q-stationary lists when the
+    mean non-empty query length is at least 64, else 1; 1 for the KV-stationary list."""
     nq = sum(1 for x in lq if x > 0)
-    nk = sum(1 for x in lk if x > 0)
-    sq, sk = sum(lq), sum(lk)
-    max_lk = max(lk) if len(lk) else 0
-
-    def waves(total, count):
-        if count == 0:
-            return 4
-        if total <= 40 * count:
-            return 1
-        if total <= 96 * count:
-            return 2
-        return 4
-
-    wq = waves(sq, nq)
-    bnw = 32 if (wq < 4 or max_lk <= 32) else 64
-    wk = waves(sk, nk)
-    return {"fwd": (wq, bnw), "dq": (wq, 32), "dkdv": (wk, 32)}
+    nb = 2 if nq > 0 and sum(lq) >= 64 * nq else 1
+    return {"fwd": nb, "dq": nb, "dkdv": 1}
 
 
-def tile_sizes(kind: str, waves: int, bnw: int):
+def tile_sizes(kind: str, nb: int):
     """(stationary tile rows, streaming tile rows) of a list."""
-    if kind in ("fwd", "dq"):
-        return 32 * waves, (4 // waves) * bnw
-    if kind == "dkdv":
-        return 32 * waves, 32 * (4 // waves)
-    raise ValueError(kind)
+    if kind not in LISTS:
+        raise ValueError(kind)
+    return 32 * nb, 32
 
 
 def enumerate_items(kind: str, lq, lk, H: int, window: int, t_stat: int, t_strm: int):
@@ -114,19 +98,18 @@ def deal(items, P: int, zigzag: bool = True):
     return bin_ptr, flat, cost
 
 
-def plan_list(kind: str, lq, lk, H: int, window: int, P: int, waves: int, bnw: int,
-              zigzag: bool = True):
-    t_stat, t_strm = tile_sizes(kind, waves, bnw)
+def plan_list(kind: str, lq, lk, H: int, window: int, P: int, nb: int, zigzag: bool = True):
+    t_stat, t_strm = tile_sizes(kind, nb)
     items = enumerate_items(kind, lq, lk, H, window, t_stat, t_strm)
     bin_ptr, flat, cost = deal(items, P, zigzag)
-    return dict(kind=kind, P=P, t_stat=t_stat, t_strm=t_strm, waves=waves, bnw=bnw,
+    return dict(kind=kind, P=P, t_stat=t_stat, t_strm=t_strm, nb=nb,
                 bin_ptr=bin_ptr, items=[it[1:] for it in flat], bin_cost=cost)
 
 
 def export(pl) -> list:
     """The int32 serialisation the library's plan export produces:
-    [P, n_items, t_stat, t_strm, waves, bnw, bin_ptr[0..P], then (b, h, t, s0, s1) per item]."""
-    out = [pl["P"], len(pl["items"]), pl["t_stat"], pl["t_strm"], pl["waves"], pl["bnw"]]
+    [P, n_items, t_stat, t_strm, nb, bin_ptr[0..P], then (b, h, t, s0, s1) per item]."""
+    out = [pl["P"], len(pl["items"]), pl["t_stat"], pl["t_strm"], pl["nb"]]
     out += list(pl["bin_ptr"])
     for it in pl["items"]:
         out += list(it)
@@ -134,9 +117,9 @@ def export(pl) -> list:
 
 
 def plan(lq, lk, H: int, window: int, P: int, layout=None):
-    """All three lists with the automatic (or given) wave layouts."""
+    """All three lists with the automatic (or given) blocks per item."""
     layout = layout or auto_layout(lq, lk, window)
-    return {kind: plan_list(kind, lq, lk, H, window, P, *layout[kind]) for kind in LISTS}
+    return {kind: plan_list(kind, lq, lk, H, window, P, layout[kind]) for kind in LISTS}
 
 
 def imbalance(cost) -> float:

@@ -3,7 +3,8 @@
     python -m recsys_attention_jagged_amd.build [--jobs N] [--verbose]
 
 Every HIP translation unit is compiled for gfx950 only.  Packed-fp32 VALU
-instructions are disabled for all device code.  Objects go to
+instructions are disabled for all device code; MFMA instructions use the VGPR
+form.  Objects go to
 recsys_attention_jagged_amd/_build/, the library to recsys_attention_jagged_amd/libgdpa.so.
 """
 from __future__ import annotations
@@ -26,6 +27,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA results in VGPRs (gfx950 has one register file): no AGPR copies
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
           "-Wno-unused-command-line-argument"]
 

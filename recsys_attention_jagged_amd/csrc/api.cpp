@@ -37,27 +37,27 @@ bool debug_enabled() {
     return v && *v && std::strcmp(v, "0") != 0;
 }
 
-const void* fwd_kernel_ptr(int d, int waves, int bnw, int act) {
+const void* fwd_kernel_ptr(int d, int nb, int act) {
     switch (d) {
-        case 32: return fwd_bf16_kernel_ptr_d32(waves, bnw, act);
-        case 64: return fwd_bf16_kernel_ptr_d64(waves, bnw, act);
-        case 128: return fwd_bf16_kernel_ptr_d128(waves, bnw, act);
+        case 32: return fwd_bf16_kernel_ptr_d32(nb, act);
+        case 64: return fwd_bf16_kernel_ptr_d64(nb, act);
+        case 128: return fwd_bf16_kernel_ptr_d128(nb, act);
     }
     return nullptr;
 }
-const void* dq_kernel_ptr(int d, int waves, int act) {
+const void* dq_kernel_ptr(int d, int nb, int act) {
     switch (d) {
-        case 32: return dq_bf16_kernel_ptr_d32(waves, act);
-        case 64: return dq_bf16_kernel_ptr_d64(waves, act);
-        case 128: return dq_bf16_kernel_ptr_d128(waves, act);
+        case 32: return dq_bf16_kernel_ptr_d32(nb, act);
+        case 64: return dq_bf16_kernel_ptr_d64(nb, act);
+        case 128: return dq_bf16_kernel_ptr_d128(nb, act);
     }
     return nullptr;
 }
-const void* dkdv_kernel_ptr(int d, int waves, int act) {
+const void* dkdv_kernel_ptr(int d, int nb, int act) {
     switch (d) {
-        case 32: return dkdv_bf16_kernel_ptr_d32(waves, act);
-        case 64: return dkdv_bf16_kernel_ptr_d64(waves, act);
-        case 128: return dkdv_bf16_kernel_ptr_d128(waves, act);
+        case 32: return dkdv_bf16_kernel_ptr_d32(nb, act);
+        case 64: return dkdv_bf16_kernel_ptr_d64(nb, act);
+        case 128: return dkdv_bf16_kernel_ptr_d128(nb, act);
     }
     return nullptr;
 }
@@ -126,11 +126,11 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
     if (opts) o = *opts;
     for (int l = 0; l < 3; ++l) {
         if (o.bins[l] < 0) return fail(GDPA_ERR_INVALID_ARG, "bins < 0");
-        if (o.waves[l] != 0 && o.waves[l] != 1 && o.waves[l] != 2 && o.waves[l] != 4)
-            return fail(GDPA_ERR_INVALID_ARG, "waves must be 0, 1, 2 or 4");
+        const int max_nb = l == LIST_DKDV ? 1 : 2;
+        if (o.blocks[l] < 0 || o.blocks[l] > max_nb)
+            return fail(GDPA_ERR_INVALID_ARG, l == LIST_DKDV ? "blocks[1] (dK/dV) must be 0 or 1"
+                                                             : "blocks[0] / blocks[2] must be 0, 1 or 2");
     }
-    if (o.bnw_fwd != 0 && o.bnw_fwd != 32 && o.bnw_fwd != 64)
-        return fail(GDPA_ERR_INVALID_ARG, "bnw_fwd must be 0, 32 or 64");
 
     if (q_off_host[0] != 0 || kv_off_host[0] != 0)
         return fail(GDPA_ERR_BAD_OFFSETS, "offsets must start at 0");
@@ -166,13 +166,7 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
 
     Layout L = auto_layout(lq, lk);
     for (int l = 0; l < 3; ++l)
-        if (o.waves[l]) L.waves[l] = o.waves[l];
-    if (o.waves[LIST_FWD] && !o.bnw_fwd) L.bnw[LIST_FWD] = 32;
-    if (o.bnw_fwd) L.bnw[LIST_FWD] = o.bnw_fwd;
-    if (L.bnw[LIST_FWD] == 64 && L.waves[LIST_FWD] != 4) {
-        delete p;
-        return fail(GDPA_ERR_INVALID_ARG, "bnw_fwd = 64 needs 4 q waves");
-    }
+        if (o.blocks[l]) L.nb[l] = o.blocks[l];
 
     int cus = 256;
     if (!p->host_only) {
@@ -185,20 +179,21 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
         }
     }
     for (int l = 0; l < 3; ++l) {
+        // one bin per persistent wave: 4 waves per workgroup, resident workgroups per CU
         int P = o.bins[l];
         if (P == 0) {
-            P = cus;
+            P = 4 * cus;
             if (!p->host_only && dtype != GDPA_F32) {
-                const void* f = l == LIST_FWD ? fwd_kernel_ptr(d, L.waves[l], L.bnw[l], GDPA_ACT_GELU)
-                              : l == LIST_DQ  ? dq_kernel_ptr(d, L.waves[l], GDPA_ACT_GELU)
-                                              : dkdv_kernel_ptr(d, L.waves[l], GDPA_ACT_GELU);
+                const void* f = l == LIST_FWD ? fwd_kernel_ptr(d, L.nb[l], GDPA_ACT_GELU)
+                              : l == LIST_DQ  ? dq_kernel_ptr(d, L.nb[l], GDPA_ACT_GELU)
+                                              : dkdv_kernel_ptr(d, L.nb[l], GDPA_ACT_GELU);
                 int per_cu = 0;
                 if (f && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 256, 0) == hipSuccess &&
                     per_cu > 0)
-                    P = cus * per_cu;
+                    P = 4 * cus * per_cu;
             }
         }
-        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.waves[l], L.bnw[l], o.round_robin == 0);
+        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.nb[l], o.round_robin == 0);
     }
 
     if (!p->host_only) {
@@ -322,9 +317,9 @@ gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v
         a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
         a.P = wl.P;
         switch (d) {
-            case 32: e = launch_fwd_bf16_d32(a, wl.waves, wl.bnw, act, s); break;
-            case 64: e = launch_fwd_bf16_d64(a, wl.waves, wl.bnw, act, s); break;
-            default: e = launch_fwd_bf16_d128(a, wl.waves, wl.bnw, act, s); break;
+            case 32: e = launch_fwd_bf16_d32(a, wl.nb, act, s); break;
+            case 64: e = launch_fwd_bf16_d64(a, wl.nb, act, s); break;
+            default: e = launch_fwd_bf16_d128(a, wl.nb, act, s); break;
         }
     }
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no forward kernel for this configuration");
@@ -365,9 +360,9 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
             b.P = wl.P;
             switch (d) {
-                case 32: e = launch_dkdv_bf16_d32(b, wl.waves, act, s); break;
-                case 64: e = launch_dkdv_bf16_d64(b, wl.waves, act, s); break;
-                default: e = launch_dkdv_bf16_d128(b, wl.waves, act, s); break;
+                case 32: e = launch_dkdv_bf16_d32(b, wl.nb, act, s); break;
+                case 64: e = launch_dkdv_bf16_d64(b, wl.nb, act, s); break;
+                default: e = launch_dkdv_bf16_d128(b, wl.nb, act, s); break;
             }
         }
         if (e == hipSuccess && want_dq && any_q) {
@@ -377,9 +372,9 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
             b.P = wl.P;
             switch (d) {
-                case 32: e = launch_dq_bf16_d32(b, wl.waves, act, s); break;
-                case 64: e = launch_dq_bf16_d64(b, wl.waves, act, s); break;
-                default: e = launch_dq_bf16_d128(b, wl.waves, act, s); break;
+                case 32: e = launch_dq_bf16_d32(b, wl.nb, act, s); break;
+                case 64: e = launch_dq_bf16_d64(b, wl.nb, act, s); break;
+                default: e = launch_dq_bf16_d128(b, wl.nb, act, s); break;
             }
         }
     }

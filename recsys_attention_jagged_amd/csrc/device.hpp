@@ -73,45 +73,40 @@ __device__ __forceinline__ bf16x8 acc_to_bf16x8(const f32x16& c, int m) {
     return r;
 }
 
-// Logical bin of this workgroup.  Workgroups are dispatched round-robin over the
-// 8 XCDs, so consecutive logical bins (which the planner fills with neighbouring
-// items of equal cost, e.g. adjacent q tiles of one sample) are placed on the
-// same XCD and share its L2.
-__device__ __forceinline__ int logical_bin(int P) {
-    const int w = blockIdx.x;
-    if (P % 8 != 0) return w;
-    return (w % 8) * (P / 8) + w / 8;
-}
-
 // -------------------------------------------------------------------------
 // activations
 // -------------------------------------------------------------------------
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// Phi(x) (standard normal CDF) and exp(-x^2 / 2) with the erf approximation of
-// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), t = 1/(1 + p z),
-// z >= 0, |error| <= 1.5e-7.  One reciprocal and one exponential, no branches.
-__device__ __forceinline__ void normal_cdf(float x, float& cdf, float& e) {
-    constexpr float p = 0.3275911f;
+// Phi(-|x|) (standard normal tail) and e = exp(-x^2 / 2), with the erf
+// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26: erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+// t = 1/(1 + p z), z >= 0, |error| <= 1.5e-7.  One reciprocal and one
+// exponential, no branches.
+__device__ __forceinline__ float normal_tail(float x, float& e) {
+    constexpr float p = 0.3275911f * 0.70710678118654752f;   // p / sqrt(2): z = |x| / sqrt(2)
     // a_k / 2, so that q = erfc(z) / 2 / exp(-z^2)
     constexpr float h1 = 0.5f * 0.254829592f, h2 = 0.5f * -0.284496736f, h3 = 0.5f * 1.421413741f;
     constexpr float h4 = 0.5f * -1.453152027f, h5 = 0.5f * 1.061405429f;
-    const float z = __builtin_fabsf(x) * 0.70710678118654752f;
-    const float t = fast_rcp(__builtin_fmaf(p, z, 1.0f));
+    const float t = fast_rcp(__builtin_fmaf(p, __builtin_fabsf(x), 1.0f));
     const float q = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, h5, h4), h3), h2), h1);
     e = fast_exp2(x * x * -0.72134752044448170f);   // exp(-x^2/2) = 2^(-x^2 log2(e) / 2)
-    const float c = q * e;                           // Phi(-|x|) = erfc(|x|/sqrt 2) / 2
+    return q * e;
+}
+
+// Phi(x) and exp(-x^2 / 2)
+__device__ __forceinline__ void normal_cdf(float x, float& cdf, float& e) {
+    const float c = normal_tail(x, e);
     cdf = x >= 0.0f ? 1.0f - c : c;
 }
 
 template <int ACT>
 __device__ __forceinline__ float act_fwd(float x) {
     if constexpr (ACT == ACT_GELU) {
-        float cdf, e;
-        normal_cdf(x, cdf, e);
-        return x * cdf;
+        // x Phi(x) = max(x, 0) - |x| Phi(-|x|)
+        float e;
+        return __builtin_fmaf(-__builtin_fabsf(x), normal_tail(x, e), __builtin_fmaxf(x, 0.0f));
     } else if constexpr (ACT == ACT_SILU) {
         return x * fast_rcp(1.0f + fast_exp2(x * -1.4426950408889634f));
     } else if constexpr (ACT == ACT_GELU_POLY) {
@@ -180,13 +175,45 @@ struct Rec {
     int32_t qs, lq, ks, lk, h, t, s0, s1;
 };
 
-// Does the 32 x 32 block (rows i0.., columns j0..) of a sample with lengths
-// (li, lj) hold a valid pair / only valid pairs?  win = window or a huge value.
-__device__ __forceinline__ bool block_any(int i0, int j0, int li, int lj, int win) {
-    return i0 < li && j0 < lj && (j0 - (i0 + 31)) < win && (i0 - (j0 + 31)) < win;
+// Does every pair of the 32 x 32 block (rows i0.., columns j0..) lie inside the
+// band |i - j| < win?  (Sample lengths need no test: rows beyond a length are
+// zero-filled tiles, whose products and stores vanish.)
+__device__ __forceinline__ bool band_all(int i0, int j0, int win) {
+    return (i0 + 31 - j0) < win && (j0 + 31 - i0) < win;
 }
-__device__ __forceinline__ bool block_all(int i0, int j0, int li, int lj, int win) {
-    return i0 + 31 < li && j0 + 31 < lj && (i0 + 31 - j0) < win && (j0 + 31 - i0) < win;
+
+// -------------------------------------------------------------------------
+// stores of a 32-row output block held as an MFMA accumulator: lane l holds
+// output row `row` (the accumulator column) and columns d = 32 db + 8 j + 4 (l/32) + i
+// in element 4 j + i of acc[db]; rows beyond the slice are dropped by the
+// descriptor's range check
+// -------------------------------------------------------------------------
+template <int NDB>
+__device__ __forceinline__ void store_block_bf16(const f32x16 (&acc)[NDB], float mul, rsrc_t ro, uint32_t row_off,
+                                                 int hh) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[db][4 * j] * mul, acc[db][4 * j + 1] * mul);
+            w[1] = pack_bf16x2(acc[db][4 * j + 2] * mul, acc[db][4 * j + 3] * mul);
+            __builtin_amdgcn_raw_buffer_store_b64(w, ro, (int)(row_off + (32 * db + 8 * j + 4 * hh) * 2), 0, 0);
+        }
+}
+
+template <int NDB>
+__device__ __forceinline__ void store_block_f32(const f32x16 (&acc)[NDB], float mul, rsrc_t ro, uint32_t row_off,
+                                                int hh) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[db][4 * j + i] * mul);
+            buf_store16(ro, row_off + (32 * db + 8 * j + 4 * hh) * 4, v);
+        }
 }
 
 }  // namespace gdpa

@@ -8,36 +8,24 @@ namespace gdpa {
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk) {
-    int64_t nq = 0, nk = 0, sq = 0, sk = 0, max_lk = 0;
+Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>&) {
+    int64_t nq = 0, sq = 0;
     for (size_t b = 0; b < lq.size(); ++b) {
         nq += lq[b] > 0;
-        nk += lk[b] > 0;
         sq += lq[b];
-        sk += lk[b];
-        max_lk = std::max(max_lk, lk[b]);
     }
-    // waves along the stationary side from the mean non-empty length
-    auto waves = [](int64_t total, int64_t count) {
-        if (count == 0) return 4;
-        if (total <= 40 * count) return 1;
-        if (total <= 96 * count) return 2;
-        return 4;
-    };
+    // two q blocks per item once the mean non-empty query length reaches 64
+    const int nb = (nq > 0 && sq >= 64 * nq) ? 2 : 1;
     Layout L;
-    const int wq = waves(sq, nq);
-    L.waves[LIST_FWD] = wq;
-    L.bnw[LIST_FWD] = (wq < 4 || max_lk <= 32) ? 32 : 64;
-    L.waves[LIST_DQ] = wq;
-    L.bnw[LIST_DQ] = 32;
-    L.waves[LIST_DKDV] = waves(sk, nk);
-    L.bnw[LIST_DKDV] = 32;
+    L.nb[LIST_FWD] = nb;
+    L.nb[LIST_DQ] = nb;
+    L.nb[LIST_DKDV] = 1;
     return L;
 }
 
-void tile_sizes(int kind, int waves, int bnw, int* t_stat, int* t_strm) {
-    *t_stat = 32 * waves;
-    *t_strm = (kind == LIST_DKDV) ? 32 * (4 / waves) : (4 / waves) * bnw;
+void tile_sizes(int, int nb, int* t_stat, int* t_strm) {
+    *t_stat = 32 * nb;
+    *t_strm = 32;
 }
 
 namespace {
@@ -48,13 +36,12 @@ struct Cand {
 }  // namespace
 
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
-                   int H, int window, int P, int waves, int bnw, bool zigzag) {
+                   int H, int window, int P, int nb, bool zigzag) {
     WorkList wl;
     wl.kind = kind;
     wl.P = P;
-    wl.waves = waves;
-    wl.bnw = bnw;
-    tile_sizes(kind, waves, bnw, &wl.t_stat, &wl.t_strm);
+    wl.nb = nb;
+    tile_sizes(kind, nb, &wl.t_stat, &wl.t_strm);
     const int64_t TS = wl.t_stat, TR = wl.t_strm;
 
     std::vector<Cand> cands;
@@ -120,8 +107,7 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
 }
 
 std::vector<int32_t> export_list(const WorkList& wl) {
-    std::vector<int32_t> out = {wl.P, (int32_t)wl.items.size(), wl.t_stat, wl.t_strm, wl.waves,
-                                wl.bnw};
+    std::vector<int32_t> out = {wl.P, (int32_t)wl.items.size(), wl.t_stat, wl.t_strm, wl.nb};
     out.insert(out.end(), wl.bin_ptr.begin(), wl.bin_ptr.end());
     for (const Item& it : wl.items) {
         out.push_back(it.b);

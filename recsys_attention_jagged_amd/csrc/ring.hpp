@@ -1,0 +1,261 @@
+// Per-wave tile ring and persistent walk shared by the bf16 GDPA kernels (gfx950).
+//
+// Every wave of a workgroup is an independent persistent worker: it owns one
+// planner bin, its own slice of LDS and its own loads, and never synchronises
+// with the other waves (no barriers).  A wave's LDS slice is a ring of R slots,
+// each holding one 32-row tile of one tensor (32 x D bf16).  The wave walks its
+// bin's items as one flattened sequence of tile loads ("jobs"): for each item its
+// stationary tiles, then for each step its streaming tiles.  The issuing side
+// runs up to R jobs ahead of the computing side, across item boundaries, so short
+// items do not drain the pipeline (GDPA page, aitrends.kr/articles/26275,
+// "Section details": pipelining moved to the outer loop; loop flattening).
+//
+// Loads are buffer_load_dwordx4 ... lds: the 64 lanes of one instruction write
+// 1 KiB of consecutive LDS, without VGPR staging.  A tile is stored row-major
+// without padding, the 16-byte chunk c of row r at chunk position c ^ swz<D>(r);
+// the swizzle is applied on the global side (each lane fetches the chunk that
+// belongs at its LDS position) and makes both read patterns bank-conflict free:
+//   * row operands: 16 rows at one chunk (ds_read_b128);
+//   * transposed operands: 4 consecutive rows x 4 consecutive chunks
+//     (ds_read_b64_tr_b16), where lane i of each 16-lane group receives column
+//     i of a 4-row block whose rows are addressed by lanes 4k .. 4k+3.
+// Rows outside the (sample, head) slice are outside the buffer descriptor's
+// range and arrive as zeros; a job of an empty slice writes a zero tile.
+//
+// Synchronisation is per wave: a job's J instructions complete in issue order,
+// so "job k has landed" is `s_waitcnt vmcnt(J * (jobs issued after k))`; a slot
+// is re-filled only after the wave's LDS reads of it have completed
+// (`s_waitcnt lgkmcnt(0)`).  The loads are issued from inline assembly, so the
+// compiler neither sees the asynchronous LDS writes nor inserts waits of its own
+// for them; stores are left to the compiler and are not counted (a wait then
+// only becomes stricter).
+#pragma once
+
+#include "device.hpp"
+
+namespace gdpa {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (D == 128) {
+        return (row & 15) ^ ((row & 3) << 2);
+    } else if constexpr (D == 64) {
+        const int u = row >> 1;
+        return (u & 7) ^ ((u & 1) << 2);
+    } else {
+        return (row >> 2) & 3;
+    }
+}
+
+// byte offset of (row, 16-byte chunk) inside a swizzled tile
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+    return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
+}
+
+// 8 bf16 of `row`, columns [8 chunk, 8 chunk + 8)
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row8(const char* tile, int row, int chunk) {
+    return *(const bf16x8*)(tile + tile_off<D>(row, chunk));
+}
+
+// Transposed operand: lane l receives the 4 values tile[row0 + 4 (l/32) + i][col0 + l % 32],
+// i = 0..3 (row0 a multiple of 4, col0 a multiple of 32).
+template <int D>
+__device__ __forceinline__ bf16x4 lds_col4(const char* tile, int row0, int col0, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int row = row0 + 4 * (g >> 1) + (i >> 2);
+    const int t = i & 3;
+    const int col = col0 + 16 * (g & 1) + 4 * t;
+    const int off = tile_off<D>(row, col >> 3) + ((t & 1) << 3);
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + off));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// A operand of 8 contraction rows for the chained MFMA: rows
+// row0 + {0..3} + 4 (l/32) and row0 + 8 + {0..3} + 4 (l/32), column col0 + l % 32.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col8(const char* tile, int row0, int col0, int lane) {
+    const bf16x4 a = lds_col4<D>(tile, row0, col0, lane);
+    const bf16x4 b = lds_col4<D>(tile, row0 + 8, col0, lane);
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// One wave instruction: lane l's 16 bytes at byte offset `voff` of the buffer
+// land at LDS address lds + 16 l (lds uniform).  The whole offset is in the
+// VGPR: the hardware range check covers the VGPR offset, not the scalar one.
+// No memory clobber: LDS reads of other slots may move across it; ordering
+// against the waits below is kept because volatile asm statements stay in order.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rs));
+}
+
+// s_waitcnt vmcnt(J m) for a uniform m in [0, 7] (the count is an immediate)
+template <int J>
+__device__ __forceinline__ void wait_jobs(int m) {
+    static_assert(7 * J <= 63, "vmcnt is 6 bits");
+#define GDPA_WJ(M) \
+    case M: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(J * M) : "memory"); break;
+    switch (m) {
+        GDPA_WJ(0) GDPA_WJ(1) GDPA_WJ(2) GDPA_WJ(3) GDPA_WJ(4) GDPA_WJ(5) GDPA_WJ(6)
+        default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(J * 7) : "memory"); break;
+    }
+#undef GDPA_WJ
+}
+
+// this wave's LDS reads (and scalar loads) have completed
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <int D>
+struct RingGeom {
+    static constexpr int TILE = 32 * D * 2;            // bytes of one 32-row tile
+    static constexpr int J = TILE / 1024;              // wave instructions per tile
+    static constexpr int WAVE_LDS = 40 * 1024;         // LDS per wave (4 waves share 160 KiB)
+    static constexpr int R = (WAVE_LDS / TILE) > 8 ? 8 : (WAVE_LDS / TILE);   // slots
+    static_assert(R >= 3, "the ring needs room for one step plus look-ahead");
+};
+
+template <int D>
+struct Ring : RingGeom<D> {
+    using G = RingGeom<D>;
+    static constexpr int CPR = D / 8;   // 16-byte chunks per row
+    uint32_t off[G::J];                 // lane offsets of each instruction inside a tile
+    uint32_t base;                      // LDS address of slot 0 (uniform)
+    const char* gbase;                  // the same slot 0 as a generic pointer
+    int issued;                         // jobs issued so far (uniform)
+
+    __device__ __forceinline__ void init(char* slice, uint32_t row_stride_bytes, int lane) {
+        gbase = slice;
+        base = lds_addr(slice);
+        issued = 0;
+#pragma unroll
+        for (int j = 0; j < G::J; ++j) {
+            const int slot = j * 64 + lane;
+            const int row = slot / CPR, pos = slot % CPR;
+            off[j] = (uint32_t)row * row_stride_bytes + (uint32_t)((pos ^ swz<D>(row)) << 4);
+        }
+    }
+
+    __device__ __forceinline__ int slot_of(int job) const { return job % G::R; }
+    __device__ __forceinline__ const char* tile(int job) const { return gbase + slot_of(job) * G::TILE; }
+
+    // load rows [row0, row0 + 32) of the slice `rs` (row_off = row0 * stride) into the next slot
+    __device__ __forceinline__ void issue(rsrc_t rs, uint32_t row_off) {
+        const uint32_t lds = base + (uint32_t)(slot_of(issued) * G::TILE);
+#pragma unroll
+        for (int j = 0; j < G::J; ++j) dma16(rs, off[j] + row_off, lds + (uint32_t)j * 1024u);
+        ++issued;
+    }
+
+    // wait until job k has landed
+    __device__ __forceinline__ void wait(int k) const { wait_jobs<G::J>(issued - 1 - k); }
+};
+
+// The issuing walk over a bin's items.  Pol provides NSTAT (stationary tiles per
+// item with steps), NSTRM (streaming tiles per step), walk_item(rec) (per-item
+// descriptors of the issuing side) and issue_job(ring, rec, i) for the i-th job
+// of the item (i < NSTAT: stationary tile i; else step s0 + (i - NSTAT) / NSTRM,
+// tile (i - NSTAT) % NSTRM).  Items without steps have no jobs.
+struct Walk {
+    Rec r;
+    int idx, end, pos, njobs;
+    bool valid;
+};
+
+template <class Pol, class RingT>
+__device__ __forceinline__ void walk_settle(Pol& pol, Walk& w, const Rec* __restrict__ recs) {
+    // skip items without jobs
+    while (w.valid && w.njobs == 0) {
+        if (++w.idx < w.end) {
+            w.r = recs[w.idx];
+            w.pos = 0;
+            w.njobs = w.r.s1 >= w.r.s0 ? Pol::NSTAT + Pol::NSTRM * (w.r.s1 - w.r.s0 + 1) : 0;
+        } else {
+            w.valid = false;
+        }
+    }
+    if (w.valid && w.pos == 0) pol.walk_item(w.r);
+}
+
+// Issue jobs until the ring is full (consumed = jobs the computing side has freed).
+template <class Pol, class RingT>
+__device__ __forceinline__ void pump(Pol& pol, Walk& w, RingT& ring, int consumed, const Rec* __restrict__ recs) {
+    while (w.valid && ring.issued < consumed + RingT::R) {
+        pol.issue_job(ring, w.r, w.pos);
+        if (++w.pos == w.njobs) {
+            w.njobs = 0;
+            walk_settle<Pol, RingT>(pol, w, recs);
+        }
+    }
+}
+
+// This wave's bin: workgroups are dispatched round-robin over the 8 XCDs, so the
+// workgroup index is remapped to make consecutive logical workgroups (whose bins
+// the planner fills with neighbouring items of equal cost, e.g. the q tiles of one
+// sample) share an XCD and its L2; the 4 waves of a workgroup take 4 consecutive bins.
+__device__ __forceinline__ int wave_bin(int wave) {
+    const int G = gridDim.x, w = blockIdx.x;
+    const int lw = (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
+    return lw * 4 + wave;
+}
+
+// The computing side.  Pol also provides:
+//   item_begin(rec)               zero the accumulators
+//   load_stat(rec, ring, job)     stationary tiles (jobs job .. job + NSTAT - 1) -> registers
+//   step(rec, s, ring, job)       one streaming step (jobs job .. job + NSTRM - 1)
+//   item_end(rec)                 store the item's outputs
+template <class Pol, int D>
+__device__ __forceinline__ void run_wave(Pol& pol, int P, const Rec* __restrict__ recs,
+                                         const int32_t* __restrict__ bin_ptr, char* slice, uint32_t row_stride,
+                                         int wave, int lane) {
+    using RingT = Ring<D>;
+    const int bin = wave_bin(wave);
+    if (bin >= P) return;
+    const int beg = bin_ptr[bin], end = bin_ptr[bin + 1];
+    if (beg >= end) return;
+
+    RingT ring;
+    ring.init(slice, row_stride, lane);
+    Walk w;
+    w.idx = beg;
+    w.end = end;
+    w.r = recs[beg];
+    w.pos = 0;
+    w.njobs = w.r.s1 >= w.r.s0 ? Pol::NSTAT + Pol::NSTRM * (w.r.s1 - w.r.s0 + 1) : 0;
+    w.valid = true;
+    walk_settle<Pol, RingT>(pol, w, recs);
+    int job = 0;   // next job the computing side consumes
+    pump<Pol, RingT>(pol, w, ring, job, recs);
+
+    for (int ci = beg; ci < end; ++ci) {
+        const Rec c = recs[ci];
+        pol.item_begin(c);
+        if (c.s1 >= c.s0) {
+            ring.wait(job + Pol::NSTAT - 1);
+            pol.load_stat(c, ring, job);
+            wait_lds();
+            job += Pol::NSTAT;
+            pump<Pol, RingT>(pol, w, ring, job, recs);
+            for (int s = c.s0; s <= c.s1; ++s) {
+                ring.wait(job + Pol::NSTRM - 1);
+                pol.step(c, s, ring, job);
+                wait_lds();
+                job += Pol::NSTRM;
+                pump<Pol, RingT>(pol, w, ring, job, recs);
+            }
+        }
+        pol.item_end(c);
+    }
+}
+
+}  // namespace gdpa

@@ -36,15 +36,15 @@ def test_status_strings_and_poly_bound():
     assert 0 < G.gdpa_gelu_poly_bound() < 1e-4
 
 
-def _host_plan(lq, lk, H, d, window, P=256, waves=(0, 0, 0), bnw=0, rr=False):
+def _host_plan(lq, lk, H, d, window, P=1024, blocks=(0, 0, 0), rr=False):
     qo, ko = offsets(lq), offsets(lk)
     return G.gdpa_plan_create(qo, ko, len(lq), H, d, window, "bf16", host_only=True,
-                              bins=(P, P, P), waves=waves, bnw_fwd=bnw, round_robin=rr)
+                              bins=(P, P, P), blocks=blocks, round_robin=rr)
 
 
 def _ref_exports(lq, lk, H, window, P, layout=None, zigzag=True):
     layout = layout or PR.auto_layout(list(lq), list(lk), window)
-    return {kind: PR.export(PR.plan_list(kind, list(lq), list(lk), H, window, P, *layout[kind], zigzag=zigzag))
+    return {kind: PR.export(PR.plan_list(kind, list(lq), list(lk), H, window, P, layout[kind], zigzag=zigzag))
             for kind in PR.LISTS}
 
 
@@ -55,7 +55,7 @@ def test_plan_bit_exact_vs_reference_on_workloads(cfg):
     lq, lk = [int(x) for x in lq], [int(x) for x in lk]
     plan = _host_plan(lq, lk, w["H"], w["d"], w["window"])
     try:
-        ref = _ref_exports(lq, lk, w["H"], w["window"], 256)
+        ref = _ref_exports(lq, lk, w["H"], w["window"], 1024)
         for kind in PR.LISTS:
             got = G.gdpa_plan_export(plan, kind)
             np.testing.assert_array_equal(got, np.asarray(ref[kind], dtype=np.int32), err_msg=kind)
@@ -75,12 +75,12 @@ EDGE = [
 
 
 @pytest.mark.parametrize("lq,lk,window", EDGE)
-@pytest.mark.parametrize("waves,bnw", [((1, 1, 1), 32), ((2, 2, 2), 32), ((4, 4, 4), 32), ((4, 4, 4), 64)])
-@pytest.mark.parametrize("P,rr", [(1, False), (7, False), (256, False), (16, True)])
-def test_plan_bit_exact_vs_reference_edge_cases(lq, lk, window, waves, bnw, P, rr):
-    plan = _host_plan(lq, lk, 3, 64, window, P=P, waves=waves, bnw=bnw, rr=rr)
+@pytest.mark.parametrize("blocks", [(1, 1, 1), (2, 1, 2), (1, 1, 2), (2, 1, 1)])
+@pytest.mark.parametrize("P,rr", [(1, False), (7, False), (1024, False), (16, True)])
+def test_plan_bit_exact_vs_reference_edge_cases(lq, lk, window, blocks, P, rr):
+    plan = _host_plan(lq, lk, 3, 64, window, P=P, blocks=blocks, rr=rr)
     try:
-        layout = {"fwd": (waves[0], bnw), "dkdv": (waves[1], 32), "dq": (waves[2], 32)}
+        layout = {"fwd": blocks[0], "dkdv": blocks[1], "dq": blocks[2]}
         ref = _ref_exports(lq, lk, 3, window, P, layout, zigzag=not rr)
         for kind in PR.LISTS:
             np.testing.assert_array_equal(G.gdpa_plan_export(plan, kind), np.asarray(ref[kind], np.int32))
@@ -95,7 +95,7 @@ def test_plan_stats_valid_pairs_and_balance():
         st = G.gdpa_plan_stats(plan)
         from oracle.gdpa_ref import useful_pairs
         assert st["valid_pairs"] == useful_pairs(lq, lk, 128)
-        assert all(b == 256 for b in st["bins"])
+        assert all(b == 1024 for b in st["bins"])
     finally:
         G.gdpa_plan_destroy(plan)
 
@@ -120,9 +120,9 @@ def test_create_rejects_bad_arguments():
     assert bad(H=0) == 1                       # INVALID_ARG
     assert bad(window=-1) == 1
     assert bad(dtype=7) == 1
-    assert bad(waves=(3, 0, 0)) == 1
-    assert bad(bnw_fwd=48) == 1
-    assert bad(waves=(2, 0, 0), bnw_fwd=64) == 1
+    assert bad(blocks=(3, 0, 0)) == 1
+    assert bad(blocks=(0, 2, 0)) == 1          # dK/dV items hold one kv block
+    assert bad(blocks=(0, 0, -1)) == 1
     assert bad(qo=np.array([1, 3, 7], np.int32)) == 2           # BAD_OFFSETS: not starting at 0
     assert bad(qo=np.array([0, 5, 3], np.int32)) == 2           # decreasing
     assert bad(ko=offsets([3, 5]), window=4) == 2               # window with Lq != Lk

@@ -122,35 +122,47 @@ def test_workload_backward_small(cfg):
 
 
 # ---------------------------------------------------------------------------
-# every wave layout, head dimension and activation
+# every item layout, head dimension and activation
 # ---------------------------------------------------------------------------
 
 RAGGED = [0, 1, 5, 31, 32, 33, 64, 65, 100, 127, 128, 129, 200, 300]
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
-@pytest.mark.parametrize("waves,bnw", [(1, 32), (2, 32), (4, 32), (4, 64)])
-def test_layouts_forward(d, waves, bnw):
-    say(f"forward layout d={d} waves={waves} bnw={bnw}")
-    rng = np.random.default_rng(d + waves)
+@pytest.mark.parametrize("nb", [1, 2])
+def test_layouts_forward(d, nb):
+    say(f"forward layout d={d} blocks={nb}")
+    rng = np.random.default_rng(d + nb)
     lq = rng.permutation(RAGGED)
     lk = rng.permutation(RAGGED)
     inp = make_from_lengths(lq, lk, 2, d, act="gelu", seed=3, device=DEV)
-    check_close(run_fwd(inp, waves=(waves, 0, 0), bnw_fwd=bnw), oracle_fwd(inp), f"O d={d} w={waves}/{bnw}")
+    check_close(run_fwd(inp, blocks=(nb, 0, 0)), oracle_fwd(inp), f"O d={d} nb={nb}")
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
-@pytest.mark.parametrize("waves", [1, 2, 4])
-def test_layouts_backward(d, waves):
-    say(f"backward layout d={d} waves={waves}")
-    rng = np.random.default_rng(10 * d + waves)
+@pytest.mark.parametrize("nb", [1, 2])
+def test_layouts_backward(d, nb):
+    say(f"backward layout d={d} dq blocks={nb}")
+    rng = np.random.default_rng(10 * d + nb)
     lq = rng.permutation(RAGGED)
     lk = rng.permutation(RAGGED)
     inp = make_from_lengths(lq, lk, 2, d, act="silu", seed=4, device=DEV)
-    g = run_bwd(inp, waves=(0, waves, waves))
+    g = run_bwd(inp, blocks=(0, 1, nb))
     r = oracle_bwd(inp)
     for name, a, b in zip(("dQ", "dK", "dV"), g, r):
-        check_close(a, b, f"{name} d={d} w={waves}")
+        check_close(a, b, f"{name} d={d} nb={nb}")
+
+
+@pytest.mark.parametrize("bins", [(1, 1, 1), (3, 5, 6), (13, 9, 7)])
+def test_few_bins_long_walks(bins):
+    say(f"few bins {bins}: long per-wave walks across many items")
+    rng = np.random.default_rng(sum(bins))
+    lq = rng.permutation(RAGGED)
+    lk = rng.permutation(RAGGED)
+    inp = make_from_lengths(lq, lk, 3, 64, act="silu", seed=12, device=DEV)
+    check_close(run_fwd(inp, bins=bins), oracle_fwd(inp), f"O bins={bins}")
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, bins=bins), oracle_bwd(inp)):
+        check_close(a, b, f"{name} bins={bins}")
 
 
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_taylor6", "identity"])
@@ -163,13 +175,13 @@ def test_activations_forward_backward(act):
 
 
 @pytest.mark.parametrize("window", [1, 2, 17, 128, 1000])
-@pytest.mark.parametrize("waves", [1, 4])
-def test_windows(window, waves):
-    say(f"window {window} waves {waves}")
+@pytest.mark.parametrize("nb", [1, 2])
+def test_windows(window, nb):
+    say(f"window {window} blocks {nb}")
     L = [1, 33, 128, 129, 700, 0, 300]
     inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, seed=6, device=DEV)
-    check_close(run_fwd(inp, waves=(waves, waves, waves)), oracle_fwd(inp), f"O w={window}")
-    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, waves=(waves, waves, waves)), oracle_bwd(inp)):
+    check_close(run_fwd(inp, blocks=(nb, 1, nb)), oracle_fwd(inp), f"O w={window}")
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, blocks=(nb, 1, nb)), oracle_bwd(inp)):
         check_close(a, b, f"{name} w={window}")
 
 
@@ -225,9 +237,9 @@ def _probe_expect(lq, lk, window, bit=None):
 
 
 @pytest.mark.parametrize("window", [0, 128])
-@pytest.mark.parametrize("waves", [1, 2, 4])
-def test_index_probe_bit_exact(window, waves):
-    say(f"count/bit probe window={window} waves={waves}")
+@pytest.mark.parametrize("nb", [1, 2])
+def test_index_probe_bit_exact(window, nb):
+    say(f"count/bit probe window={window} blocks={nb}")
     L = [1, 31, 32, 33, 127, 128, 129, 600, 0, 1100] if window else None
     lq = L or [3, 31, 32, 33, 0, 128, 129, 257, 40, 1]
     lk = L or [129, 1, 64, 0, 5, 300, 33, 257, 511, 2]
@@ -241,7 +253,7 @@ def test_index_probe_bit_exact(window, waves):
         vals.append(np.concatenate([bits, np.ones((c, d - 16), np.float32)], axis=1))
     V = np.concatenate(vals) if vals else np.zeros((0, d), np.float32)
     inp.v = torch.tensor(np.repeat(V[:, None, :], 2, axis=1), dtype=torch.bfloat16, device=DEV)
-    o = run_fwd(inp, act="one", dtype="bf16_f32out", waves=(waves, 0, 0))
+    o = run_fwd(inp, act="one", dtype="bf16_f32out", blocks=(nb, 0, 0))
     cnt = _probe_expect(lq, lk, window)
     for h in range(2):
         np.testing.assert_array_equal(o[:, h, 16], cnt)

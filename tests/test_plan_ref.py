@@ -36,10 +36,10 @@ def _tiles_with_valid_pair(kind, lq, lk, H, window, t_stat, t_strm):
 
 @pytest.mark.parametrize("lq,lk,window", CASES)
 @pytest.mark.parametrize("kind", PR.LISTS)
-@pytest.mark.parametrize("waves", [1, 2, 4])
-def test_items_are_exactly_the_tiles_with_valid_pairs(lq, lk, window, kind, waves):
+@pytest.mark.parametrize("tiles", [(32, 32), (64, 32), (32, 64), (128, 64)])
+def test_items_are_exactly_the_tiles_with_valid_pairs(lq, lk, window, kind, tiles):
     H = 2
-    t_stat, t_strm = PR.tile_sizes(kind, waves, 32)
+    t_stat, t_strm = tiles
     items = PR.enumerate_items(kind, lq, lk, H, window, t_stat, t_strm)
     got = set()
     owned = set()
@@ -79,16 +79,19 @@ def test_zigzag_beats_round_robin_on_skewed_costs():
 
 
 def test_auto_layout_rules():
-    assert PR.auto_layout([32] * 8, [1000] * 8) == {"fwd": (1, 32), "dq": (1, 32), "dkdv": (4, 32)}
-    assert PR.auto_layout([300] * 8, [32] * 8) == {"fwd": (4, 32), "dq": (4, 32), "dkdv": (1, 32)}
-    assert PR.auto_layout([70] * 8, [70] * 8) == {"fwd": (2, 32), "dq": (2, 32), "dkdv": (2, 32)}
-    assert PR.auto_layout([4000] * 8, [4000] * 8) == {"fwd": (4, 64), "dq": (4, 32), "dkdv": (4, 32)}
+    assert PR.auto_layout([32] * 8, [1000] * 8) == {"fwd": 1, "dq": 1, "dkdv": 1}
+    assert PR.auto_layout([300] * 8, [32] * 8) == {"fwd": 2, "dq": 2, "dkdv": 1}
+    assert PR.auto_layout([63, 65, 0], [70] * 3) == {"fwd": 2, "dq": 2, "dkdv": 1}
+    assert PR.auto_layout([63, 64, 0], [70] * 3) == {"fwd": 1, "dq": 1, "dkdv": 1}
+    assert PR.auto_layout([0, 0], [5, 5]) == {"fwd": 1, "dq": 1, "dkdv": 1}
+    assert PR.tile_sizes("fwd", 2) == (64, 32) and PR.tile_sizes("dkdv", 1) == (32, 32)
 
 
 def test_export_layout():
-    pl = PR.plan_list("fwd", [70, 0, 5], [3, 9, 0], 2, 0, 4, 2, 32)
+    pl = PR.plan_list("fwd", [70, 0, 5], [3, 9, 0], 2, 0, 4, 2)
     ex = PR.export(pl)
     P, n = ex[0], ex[1]
     assert P == 4 and n == len(pl["items"])
-    assert ex[6:6 + P + 1] == pl["bin_ptr"]
-    assert len(ex) == 6 + P + 1 + 5 * n
+    assert ex[2:5] == [64, 32, 2]
+    assert ex[5:5 + P + 1] == pl["bin_ptr"]
+    assert len(ex) == 5 + P + 1 + 5 * n
