@@ -48,15 +48,33 @@ struct Common {
         scale = a.scale;
     }
 
-    template <int NDB>
-    __device__ __forceinline__ void store(const f32x16 (&acc)[NDB], float mul, void* out, size_t base, int rows,
-                                          int row) const {
+    // store a 32-row output block: fp32 directly from the accumulator, bf16 staged
+    // through `tile` (a slot of the item's last step) and written as whole rows
+    template <int D>
+    __device__ __forceinline__ void store(const f32x16 (&acc)[D / 32], float mul, void* out, size_t base, int rows,
+                                          int row0, char* tile) const {
         if (a.out_f32) {
-            store_block_f32<NDB>(acc, mul, slice_rsrc((const float*)out + base, rows, rso, NDB * 32 * 4),
-                                 (uint32_t)row * rso, hh);
+            store_block_f32<D / 32>(acc, mul, slice_rsrc((const float*)out + base, rows, rso, D * 4),
+                                    (uint32_t)(row0 + r) * rso, hh);
         } else {
-            store_block_bf16<NDB>(acc, mul, slice_rsrc((const __bf16*)out + base, rows, rso, NDB * 32 * 2),
-                                  (uint32_t)row * rso, hh);
+            stage_block<D>(acc, mul, tile, r, hh);
+            store_tile<D>(tile, slice_rsrc((const __bf16*)out + base, rows, rso, D * 2), (uint32_t)row0 * rso, rso,
+                          lane);
+        }
+    }
+
+    // zero rows row0 .. row0 + 31 of an output slice
+    template <int D>
+    __device__ __forceinline__ void zero(void* out, size_t base, int rows, int row0) const {
+        if (a.out_f32) {
+            f32x16 z[D / 32];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) z[db] = f32x16{};
+            store_block_f32<D / 32>(z, 1.0f, slice_rsrc((const float*)out + base, rows, rso, D * 4),
+                                    (uint32_t)(row0 + r) * rso, hh);
+        } else {
+            store_zero_rows<D>(slice_rsrc((const __bf16*)out + base, rows, rso, D * 2), (uint32_t)row0 * rso, rso,
+                               lane);
         }
     }
 };
@@ -170,10 +188,18 @@ struct DqPol : Common {
             }
     }
 
-    __device__ __forceinline__ void item_end(const Rec& c) {
+    template <class RingT>
+    __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) store<NDB>(acc[b], scale, a.dq, ob, c.lq, c.t * 32 * NB + 32 * b + r);
+        for (int b = 0; b < NB; ++b)
+            store<D>(acc[b], scale, a.dq, ob, c.lq, c.t * 32 * NB + 32 * b, g.tile(job - NSTRM + b));
+    }
+
+    __device__ __forceinline__ void item_zero(const Rec& c) {
+        const size_t ob = ((size_t)c.qs * H + c.h) * D;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) zero<D>(a.dq, ob, c.lq, c.t * 32 * NB + 32 * b);
     }
 };
 
@@ -274,11 +300,17 @@ struct DkdvPol : Common {
         }
     }
 
-    __device__ __forceinline__ void item_end(const Rec& c) {
+    template <class RingT>
+    __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
         const size_t ob = ((size_t)c.ks * H + c.h) * D;
-        const int row = c.t * 32 + r;
-        store<NDB>(accK, scale, a.dk, ob, c.lk, row);
-        store<NDB>(accV, 1.0f, a.dv, ob, c.lk, row);
+        store<D>(accK, scale, a.dk, ob, c.lk, c.t * 32, g.tile(job - 2));
+        store<D>(accV, 1.0f, a.dv, ob, c.lk, c.t * 32, g.tile(job - 1));
+    }
+
+    __device__ __forceinline__ void item_zero(const Rec& c) {
+        const size_t ob = ((size_t)c.ks * H + c.h) * D;
+        zero<D>(a.dk, ob, c.lk, c.t * 32);
+        zero<D>(a.dv, ob, c.lk, c.t * 32);
     }
 };
 

@@ -130,19 +130,39 @@ struct FwdPol {
                 for (int b = 0; b < NB; ++b) acc[b][db] = mfma32(vop[m][db], pb[b][m], acc[b][db]);
     }
 
-    __device__ __forceinline__ void item_end(const Rec& c) {
+    template <class RingT>
+    __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
         if (a.out_f32) {
             const rsrc_t ro = slice_rsrc((const float*)a.o + ob, c.lq, rso, D * 4);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
                 store_block_f32<NDB>(acc[b], 1.0f, ro, (uint32_t)(c.t * 32 * NB + 32 * b + r) * rso, hh);
-        } else {
-            const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, c.lq, rso, D * 2);
+            return;
+        }
+        // stage each 32-row block in a slot of the last step, then store whole rows
+        const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, c.lq, rso, D * 2);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) stage_block<D>(acc[b], 1.0f, g.tile(job - NSTRM + b), r, hh);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            store_tile<D>(g.tile(job - NSTRM + b), ro, (uint32_t)(c.t * 32 * NB + 32 * b) * rso, rso, lane);
+    }
+
+    // an item without keys: its rows are zero
+    __device__ __forceinline__ void item_zero(const Rec& c) {
+        const size_t ob = ((size_t)c.qs * H + c.h) * D;
+        if (a.out_f32) {
+            item_begin(c);
+            const rsrc_t ro = slice_rsrc((const float*)a.o + ob, c.lq, rso, D * 4);
 #pragma unroll
             for (int b = 0; b < NB; ++b)
-                store_block_bf16<NDB>(acc[b], 1.0f, ro, (uint32_t)(c.t * 32 * NB + 32 * b + r) * rso, hh);
+                store_block_f32<NDB>(acc[b], 1.0f, ro, (uint32_t)(c.t * 32 * NB + 32 * b + r) * rso, hh);
+            return;
         }
+        const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, c.lq, rso, D * 2);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) store_zero_rows<D>(ro, (uint32_t)(c.t * 32 * NB + 32 * b) * rso, rso, lane);
     }
 };
 

@@ -131,7 +131,7 @@ struct Ring : RingGeom<D> {
     static constexpr int CPR = D / 8;   // 16-byte chunks per row
     uint32_t off[G::J];                 // lane offsets of each instruction inside a tile
     uint32_t base;                      // LDS address of slot 0 (uniform)
-    const char* gbase;                  // the same slot 0 as a generic pointer
+    char* gbase;                        // the same slot 0 as a generic pointer
     int issued;                         // jobs issued so far (uniform)
 
     __device__ __forceinline__ void init(char* slice, uint32_t row_stride_bytes, int lane) {
@@ -147,7 +147,7 @@ struct Ring : RingGeom<D> {
     }
 
     __device__ __forceinline__ int slot_of(int job) const { return job % G::R; }
-    __device__ __forceinline__ const char* tile(int job) const { return gbase + slot_of(job) * G::TILE; }
+    __device__ __forceinline__ char* tile(int job) const { return gbase + slot_of(job) * G::TILE; }
 
     // load rows [row0, row0 + 32) of the slice `rs` (row_off = row0 * stride) into the next slot
     __device__ __forceinline__ void issue(rsrc_t rs, uint32_t row_off) {
@@ -160,6 +160,49 @@ struct Ring : RingGeom<D> {
     // wait until job k has landed
     __device__ __forceinline__ void wait(int k) const { wait_jobs<G::J>(issued - 1 - k); }
 };
+
+// -------------------------------------------------------------------------
+// output blocks: staged through LDS, stored as whole rows
+// -------------------------------------------------------------------------
+// Stage a 32-row output block held as an MFMA accumulator (lane (r, hh) holds
+// output row r and columns 32 db + 8 j + 4 hh + i in element 4 j + i of acc[db])
+// as bf16 into a swizzled 32 x D tile.
+template <int D>
+__device__ __forceinline__ void stage_block(const f32x16 (&acc)[D / 32], float mul, char* tile, int r, int hh) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[db][4 * j] * mul, acc[db][4 * j + 1] * mul);
+            w[1] = pack_bf16x2(acc[db][4 * j + 2] * mul, acc[db][4 * j + 3] * mul);
+            *(u32x2*)(tile + tile_off<D>(r, 4 * db + j) + 8 * hh) = w;
+        }
+}
+
+// Store a staged 32 x D bf16 tile as rows row0 .. row0 + 31 of the slice `ro`
+// (row_off0 = row0 * rso): each instruction writes whole rows, 16 bytes per lane.
+template <int D>
+__device__ __forceinline__ void store_tile(const char* tile, rsrc_t ro, uint32_t row_off0, uint32_t rso, int lane) {
+    constexpr int CPR = D / 8, RPI = 64 / CPR;   // chunks per row, rows per instruction
+    const int rr = lane / CPR, c = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = i * RPI + rr;
+        buf_store16(ro, row_off0 + (uint32_t)row * rso + (uint32_t)c * 16u,
+                    *(const u32x4*)(tile + tile_off<D>(row, c)));
+    }
+}
+
+// Zero rows row0 .. row0 + 31 of the bf16 slice `ro` (whole rows per instruction).
+template <int D>
+__device__ __forceinline__ void store_zero_rows(rsrc_t ro, uint32_t row_off0, uint32_t rso, int lane) {
+    constexpr int CPR = D / 8, RPI = 64 / CPR;
+    const int rr = lane / CPR, c = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i)
+        buf_store16(ro, row_off0 + (uint32_t)(i * RPI + rr) * rso + (uint32_t)c * 16u, u32x4{0u, 0u, 0u, 0u});
+}
 
 // The issuing walk over a bin's items.  Pol provides NSTAT (stationary tiles per
 // item with steps), NSTRM (streaming tiles per step), walk_item(rec) (per-item
@@ -213,7 +256,10 @@ __device__ __forceinline__ int wave_bin(int wave) {
 //   item_begin(rec)               zero the accumulators
 //   load_stat(rec, ring, job)     stationary tiles (jobs job .. job + NSTAT - 1) -> registers
 //   step(rec, s, ring, job)       one streaming step (jobs job .. job + NSTRM - 1)
-//   item_end(rec)                 store the item's outputs
+//   item_end(rec, ring, job)      store the item's outputs, staged through the slots
+//                                 of its last step (jobs job - NSTRM .. job - 1), which
+//                                 are refilled only afterwards
+//   item_zero(rec)                store the outputs of an item without steps (zeros)
 template <class Pol, int D>
 __device__ __forceinline__ void run_wave(Pol& pol, int P, const Rec* __restrict__ recs,
                                          const int32_t* __restrict__ bin_ptr, char* slice, uint32_t row_stride,
@@ -239,22 +285,27 @@ __device__ __forceinline__ void run_wave(Pol& pol, int P, const Rec* __restrict_
 
     for (int ci = beg; ci < end; ++ci) {
         const Rec c = recs[ci];
-        pol.item_begin(c);
-        if (c.s1 >= c.s0) {
-            ring.wait(job + Pol::NSTAT - 1);
-            pol.load_stat(c, ring, job);
-            wait_lds();
-            job += Pol::NSTAT;
-            pump<Pol, RingT>(pol, w, ring, job, recs);
-            for (int s = c.s0; s <= c.s1; ++s) {
-                ring.wait(job + Pol::NSTRM - 1);
-                pol.step(c, s, ring, job);
-                wait_lds();
-                job += Pol::NSTRM;
-                pump<Pol, RingT>(pol, w, ring, job, recs);
-            }
+        if (c.s1 < c.s0) {
+            pol.item_zero(c);
+            continue;
         }
-        pol.item_end(c);
+        pol.item_begin(c);
+        ring.wait(job + Pol::NSTAT - 1);
+        pol.load_stat(c, ring, job);
+        wait_lds();
+        job += Pol::NSTAT;
+        pump<Pol, RingT>(pol, w, ring, job, recs);
+        for (int s = c.s0;; ++s) {
+            ring.wait(job + Pol::NSTRM - 1);
+            pol.step(c, s, ring, job);
+            wait_lds();
+            job += Pol::NSTRM;
+            if (s == c.s1) break;
+            pump<Pol, RingT>(pol, w, ring, job, recs);
+        }
+        pol.item_end(c, ring, job);
+        wait_lds();
+        pump<Pol, RingT>(pol, w, ring, job, recs);
     }
 }
 
