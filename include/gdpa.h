@@ -86,10 +86,13 @@ typedef enum { GDPA_LIST_FWD = 0, GDPA_LIST_DKDV = 1, GDPA_LIST_DQ = 2 } gdpa_li
 typedef struct {
     int host_only;   /* 1: plan on the host only (export / stats); no device memory is
                         allocated and gdpa_fwd / gdpa_bwd reject the plan */
-    int bins[3];     /* bins per list (GDPA_LIST_*), one per persistent wave; 0 = four
-                        per workgroup the device can hold resident (host_only: 1024) */
-    int blocks[3];   /* 32-row stationary blocks per work item: 0 = automatic; forward
-                        and dQ lists 1 or 2 (q rows per item), dK/dV list 1 */
+    int bins[3];     /* bins per list (GDPA_LIST_*), one per persistent workgroup; 0 = as
+                        many workgroups as the device holds resident (host_only: 1024) */
+    int team[3];     /* waves per workgroup sharing one tile ring: 0 = automatic, 1, or 2
+                        (d = 128 only) */
+    int blocks[3];   /* 32-row stationary blocks per wave: 0 = automatic, 1 or 2 (dK/dV
+                        and two-wave teams: 1).  An item holds 32 * team * blocks
+                        stationary rows */
     int round_robin; /* 1: deal sorted items round robin instead of zigzag (ablation) */
 } gdpa_plan_opts;
 
@@ -99,7 +102,7 @@ typedef struct {
     int64_t valid_pairs;     /* sum over samples of the valid (i, j) pairs */
     int32_t n_items[3];      /* work items per list */
     int32_t n_steps[3];      /* streaming steps per list (a step-less item counts 0) */
-    int32_t bins[3];         /* bins (persistent waves) per list */
+    int32_t bins[3];         /* bins (persistent workgroups) per list */
     int32_t tile_stat[3];    /* stationary tile rows per list */
     int32_t tile_strm[3];    /* streaming tile rows per list */
     int64_t bin_cost_max[3]; /* per-bin cost extremes (planner cost units) */
@@ -110,7 +113,7 @@ typedef struct gdpa_plan_s* gdpa_plan;
 
 /*
  * gdpa_plan_create - enumerate the non-empty tiles on the host and deal them to
- * persistent waves (GDPA page, "Section details": the CPU precomputes the
+ * persistent workgroups (GDPA page, "Section details": the CPU precomputes the
  * valid tiles, sorts them and assigns them to processors in a zigzag order).
  *
  *   q_off_host, kv_off_host : host int32 [B + 1] offsets (read during the call only)
@@ -181,7 +184,7 @@ gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void
 
 /*
  * gdpa_plan_export - serialise one work list as int32 values:
- *   [P, n_items, tile_stat, tile_strm, blocks, bin_ptr[0..P], then per item in
+ *   [P, n_items, tile_stat, tile_strm, team, blocks, bin_ptr[0..P], then per item in
  *    bin order (b, h, t, s0, s1)]
  * where t is the stationary tile and [s0, s1] the streaming tiles (s1 < s0: no
  * steps, the item writes zeros).  With buf == NULL, *n receives the length;

@@ -22,10 +22,11 @@ Readings (the page gives no cost model or tie-break):
     rounds and to P - 1 - (r mod P) in odd rounds (round = r // P);
   * per-bin CSR keeps each bin's items in deal order.
 
-Three lists are planned: "fwd" and "dq" (Q-stationary: t is a q tile of 32 NB
-rows, steps are kv tiles of 32 rows) and "dkdv" (KV-stationary: t is a kv tile of
-32 rows, steps are q tiles of 32 rows).  One wave processes one item; NB (the
-32-row stationary blocks per item) comes from the length statistics.
+Three lists are planned: "fwd" and "dq" (Q-stationary: t is a q tile, steps are
+kv tiles of 32 rows) and "dkdv" (KV-stationary: t is a kv tile, steps are q tiles
+of 32 rows).  One team of waves processes one item; stationary tiles hold
+32 * team * nb rows (team waves with nb 32-row blocks each), chosen from the head
+dimension and the length statistics.
 """
 from __future__ import annotations
 
@@ -38,19 +39,22 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def auto_layout(lq, lk, window: int = 0):
-    """Stationary 32-row blocks per item: 2 for the Q-stationary lists when the
-    mean non-empty query length is at least 64, else 1; 1 for the KV-stationary list."""
-    nq = sum(1 for x in lq if x > 0)
-    nb = 2 if nq > 0 and sum(lq) >= 64 * nq else 1
-    return {"fwd": nb, "dq": nb, "dkdv": 1}
+def auto_layout(lq, lk, window: int = 0, d: int = 128):
+    """(team, nb) per list.  Forward: d = 128, two-wave teams with one block per
+    wave when the mean non-empty query length is at least 48, else one wave and one
+    block; d <= 64, one wave with nb = 2 when that mean is at least 64, else 1.
+    dQ and dK/dV: one wave, one block."""
+    n = sum(1 for x in lq if x > 0)
+    mean_at_least = lambda m: n > 0 and sum(lq) >= m * n
+    fwd = ((2 if mean_at_least(48) else 1), 1) if d == 128 else (1, 2 if mean_at_least(64) else 1)
+    return {"fwd": fwd, "dq": (1, 1), "dkdv": (1, 1)}
 
 
-def tile_sizes(kind: str, nb: int):
+def tile_sizes(kind: str, team: int, nb: int):
     """(stationary tile rows, streaming tile rows) of a list."""
     if kind not in LISTS:
         raise ValueError(kind)
-    return 32 * nb, 32
+    return 32 * team * nb, 32
 
 
 def enumerate_items(kind: str, lq, lk, H: int, window: int, t_stat: int, t_strm: int):
@@ -98,28 +102,28 @@ def deal(items, P: int, zigzag: bool = True):
     return bin_ptr, flat, cost
 
 
-def plan_list(kind: str, lq, lk, H: int, window: int, P: int, nb: int, zigzag: bool = True):
-    t_stat, t_strm = tile_sizes(kind, nb)
+def plan_list(kind: str, lq, lk, H: int, window: int, P: int, team: int, nb: int, zigzag: bool = True):
+    t_stat, t_strm = tile_sizes(kind, team, nb)
     items = enumerate_items(kind, lq, lk, H, window, t_stat, t_strm)
     bin_ptr, flat, cost = deal(items, P, zigzag)
-    return dict(kind=kind, P=P, t_stat=t_stat, t_strm=t_strm, nb=nb,
+    return dict(kind=kind, P=P, t_stat=t_stat, t_strm=t_strm, team=team, nb=nb,
                 bin_ptr=bin_ptr, items=[it[1:] for it in flat], bin_cost=cost)
 
 
 def export(pl) -> list:
     """The int32 serialisation the library's plan export produces:
-    [P, n_items, t_stat, t_strm, nb, bin_ptr[0..P], then (b, h, t, s0, s1) per item]."""
-    out = [pl["P"], len(pl["items"]), pl["t_stat"], pl["t_strm"], pl["nb"]]
+    [P, n_items, t_stat, t_strm, team, nb, bin_ptr[0..P], then (b, h, t, s0, s1) per item]."""
+    out = [pl["P"], len(pl["items"]), pl["t_stat"], pl["t_strm"], pl["team"], pl["nb"]]
     out += list(pl["bin_ptr"])
     for it in pl["items"]:
         out += list(it)
     return out
 
 
-def plan(lq, lk, H: int, window: int, P: int, layout=None):
-    """All three lists with the automatic (or given) blocks per item."""
-    layout = layout or auto_layout(lq, lk, window)
-    return {kind: plan_list(kind, lq, lk, H, window, P, layout[kind]) for kind in LISTS}
+def plan(lq, lk, H: int, window: int, P: int, d: int = 128, layout=None):
+    """All three lists with the automatic (or given) layouts."""
+    layout = layout or auto_layout(lq, lk, window, d)
+    return {kind: plan_list(kind, lq, lk, H, window, P, *layout[kind]) for kind in LISTS}
 
 
 def imbalance(cost) -> float:

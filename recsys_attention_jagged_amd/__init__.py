@@ -35,8 +35,8 @@ class GdpaError(RuntimeError):
 
 
 class gdpa_plan_opts(ctypes.Structure):
-    _fields_ = [("host_only", ctypes.c_int), ("bins", ctypes.c_int * 3), ("blocks", ctypes.c_int * 3),
-                ("round_robin", ctypes.c_int)]
+    _fields_ = [("host_only", ctypes.c_int), ("bins", ctypes.c_int * 3), ("team", ctypes.c_int * 3),
+                ("blocks", ctypes.c_int * 3), ("round_robin", ctypes.c_int)]
 
 
 class gdpa_plan_stats_t(ctypes.Structure):
@@ -120,15 +120,15 @@ def _enum(v, table):
 # ---------------------------------------------------------------------------
 
 def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: int, dtype,
-                     host_only: bool = False, bins=(0, 0, 0), blocks=(0, 0, 0),
+                     host_only: bool = False, bins=(0, 0, 0), team=(0, 0, 0), blocks=(0, 0, 0),
                      round_robin: bool = False) -> int:
     """Returns an opaque plan handle (int).  Offsets: host int32 [B + 1]."""
     qo = np.ascontiguousarray(q_off_host, dtype=np.int32)
     ko = np.ascontiguousarray(kv_off_host, dtype=np.int32)
     if qo.shape != (B + 1,) or ko.shape != (B + 1,):
         raise ValueError("offsets must have B + 1 entries")
-    opts = gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*blocks),
-                          int(round_robin))
+    opts = gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*team),
+                          (ctypes.c_int * 3)(*blocks), int(round_robin))
     out = _vp()
     _check(load_library().gdpa_plan_create(qo.ctypes.data, ko.ctypes.data, B, H, d, window,
                                            _enum(dtype, DTYPE), ctypes.byref(opts), ctypes.byref(out)))

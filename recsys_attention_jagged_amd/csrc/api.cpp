@@ -37,27 +37,27 @@ bool debug_enabled() {
     return v && *v && std::strcmp(v, "0") != 0;
 }
 
-const void* fwd_kernel_ptr(int d, int nb, int act) {
+const void* fwd_kernel_ptr(int d, int team, int nb, int act) {
     switch (d) {
-        case 32: return fwd_bf16_kernel_ptr_d32(nb, act);
-        case 64: return fwd_bf16_kernel_ptr_d64(nb, act);
-        case 128: return fwd_bf16_kernel_ptr_d128(nb, act);
+        case 32: return fwd_bf16_kernel_ptr_d32(team, nb, act);
+        case 64: return fwd_bf16_kernel_ptr_d64(team, nb, act);
+        case 128: return fwd_bf16_kernel_ptr_d128(team, nb, act);
     }
     return nullptr;
 }
-const void* dq_kernel_ptr(int d, int nb, int act) {
+const void* dq_kernel_ptr(int d, int team, int nb, int act) {
     switch (d) {
-        case 32: return dq_bf16_kernel_ptr_d32(nb, act);
-        case 64: return dq_bf16_kernel_ptr_d64(nb, act);
-        case 128: return dq_bf16_kernel_ptr_d128(nb, act);
+        case 32: return dq_bf16_kernel_ptr_d32(team, nb, act);
+        case 64: return dq_bf16_kernel_ptr_d64(team, nb, act);
+        case 128: return dq_bf16_kernel_ptr_d128(team, nb, act);
     }
     return nullptr;
 }
-const void* dkdv_kernel_ptr(int d, int nb, int act) {
+const void* dkdv_kernel_ptr(int d, int team, int nb, int act) {
     switch (d) {
-        case 32: return dkdv_bf16_kernel_ptr_d32(nb, act);
-        case 64: return dkdv_bf16_kernel_ptr_d64(nb, act);
-        case 128: return dkdv_bf16_kernel_ptr_d128(nb, act);
+        case 32: return dkdv_bf16_kernel_ptr_d32(team, nb, act);
+        case 64: return dkdv_bf16_kernel_ptr_d64(team, nb, act);
+        case 128: return dkdv_bf16_kernel_ptr_d128(team, nb, act);
     }
     return nullptr;
 }
@@ -126,10 +126,8 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
     if (opts) o = *opts;
     for (int l = 0; l < 3; ++l) {
         if (o.bins[l] < 0) return fail(GDPA_ERR_INVALID_ARG, "bins < 0");
-        const int max_nb = l == LIST_DKDV ? 1 : 2;
-        if (o.blocks[l] < 0 || o.blocks[l] > max_nb)
-            return fail(GDPA_ERR_INVALID_ARG, l == LIST_DKDV ? "blocks[1] (dK/dV) must be 0 or 1"
-                                                             : "blocks[0] / blocks[2] must be 0, 1 or 2");
+        if (o.blocks[l] < 0 || o.blocks[l] > 2) return fail(GDPA_ERR_INVALID_ARG, "blocks must be 0, 1 or 2");
+        if (o.team[l] < 0 || o.team[l] > 2) return fail(GDPA_ERR_INVALID_ARG, "team must be 0, 1 or 2");
     }
 
     if (q_off_host[0] != 0 || kv_off_host[0] != 0)
@@ -164,9 +162,20 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
     p->Tk = kv_off_host[B];
     for (int b = 0; b < B; ++b) p->valid_pairs += pairs_of(lq[b], lk[b], window);
 
-    Layout L = auto_layout(lq, lk);
-    for (int l = 0; l < 3; ++l)
+    Layout L = auto_layout(lq, lk, d);
+    for (int l = 0; l < 3; ++l) {
+        if (o.team[l]) L.team[l] = o.team[l];
         if (o.blocks[l]) L.nb[l] = o.blocks[l];
+        // layouts with a kernel: teams of two only for d = 128 and with one block per
+        // wave; dK/dV one block per wave
+        const bool ok = (L.team[l] == 1 || (d == 128 && L.nb[l] == 1)) && (l != LIST_DKDV || L.nb[l] == 1);
+        if (!ok) {
+            delete p;
+            return fail(GDPA_ERR_INVALID_ARG, "no kernel for team " + std::to_string(L.team[l]) + " x blocks " +
+                                                  std::to_string(L.nb[l]) + " in list " + std::to_string(l) +
+                                                  " at d = " + std::to_string(d));
+        }
+    }
 
     int cus = 256;
     if (!p->host_only) {
@@ -179,21 +188,22 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
         }
     }
     for (int l = 0; l < 3; ++l) {
-        // one bin per persistent wave: 4 waves per workgroup, resident workgroups per CU
+        // one bin per persistent workgroup (a team of waves): as many as the device
+        // holds resident (host_only: 4 per CU)
         int P = o.bins[l];
         if (P == 0) {
             P = 4 * cus;
             if (!p->host_only && dtype != GDPA_F32) {
-                const void* f = l == LIST_FWD ? fwd_kernel_ptr(d, L.nb[l], GDPA_ACT_GELU)
-                              : l == LIST_DQ  ? dq_kernel_ptr(d, L.nb[l], GDPA_ACT_GELU)
-                                              : dkdv_kernel_ptr(d, L.nb[l], GDPA_ACT_GELU);
+                const void* f = l == LIST_FWD ? fwd_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU)
+                              : l == LIST_DQ  ? dq_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU)
+                                              : dkdv_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU);
                 int per_cu = 0;
-                if (f && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 256, 0) == hipSuccess &&
+                if (f && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 64 * L.team[l], 0) == hipSuccess &&
                     per_cu > 0)
-                    P = 4 * cus * per_cu;
+                    P = cus * per_cu;
             }
         }
-        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.nb[l], o.round_robin == 0);
+        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.round_robin == 0);
     }
 
     if (!p->host_only) {
@@ -317,9 +327,9 @@ gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v
         a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
         a.P = wl.P;
         switch (d) {
-            case 32: e = launch_fwd_bf16_d32(a, wl.nb, act, s); break;
-            case 64: e = launch_fwd_bf16_d64(a, wl.nb, act, s); break;
-            default: e = launch_fwd_bf16_d128(a, wl.nb, act, s); break;
+            case 32: e = launch_fwd_bf16_d32(a, wl.team, wl.nb, act, s); break;
+            case 64: e = launch_fwd_bf16_d64(a, wl.team, wl.nb, act, s); break;
+            default: e = launch_fwd_bf16_d128(a, wl.team, wl.nb, act, s); break;
         }
     }
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no forward kernel for this configuration");
@@ -360,9 +370,9 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
             b.P = wl.P;
             switch (d) {
-                case 32: e = launch_dkdv_bf16_d32(b, wl.nb, act, s); break;
-                case 64: e = launch_dkdv_bf16_d64(b, wl.nb, act, s); break;
-                default: e = launch_dkdv_bf16_d128(b, wl.nb, act, s); break;
+                case 32: e = launch_dkdv_bf16_d32(b, wl.team, wl.nb, act, s); break;
+                case 64: e = launch_dkdv_bf16_d64(b, wl.team, wl.nb, act, s); break;
+                default: e = launch_dkdv_bf16_d128(b, wl.team, wl.nb, act, s); break;
             }
         }
         if (e == hipSuccess && want_dq && any_q) {
@@ -372,9 +382,9 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
             b.P = wl.P;
             switch (d) {
-                case 32: e = launch_dq_bf16_d32(b, wl.nb, act, s); break;
-                case 64: e = launch_dq_bf16_d64(b, wl.nb, act, s); break;
-                default: e = launch_dq_bf16_d128(b, wl.nb, act, s); break;
+                case 32: e = launch_dq_bf16_d32(b, wl.team, wl.nb, act, s); break;
+                case 64: e = launch_dq_bf16_d64(b, wl.team, wl.nb, act, s); break;
+                default: e = launch_dq_bf16_d128(b, wl.team, wl.nb, act, s); break;
             }
         }
     }

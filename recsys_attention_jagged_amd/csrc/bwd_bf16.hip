@@ -8,17 +8,17 @@
 //     dP = dO V^T,   dS = dP * act'(S),
 //     dV = P^T dO,   dK = dS^T Q / sqrt(d),   dQ = dS K / sqrt(d).
 //
-// Two persistent kernels, no atomics (every output row has one owner); every
-// wave is an independent worker over its own bin (see ring.hpp):
-//   * dq   - Q-stationary: an item is NB 32-row q blocks of one (sample, head),
-//            steps stream 32-row K and V tiles.  S^T = K Q^T and dP^T = V dO^T
-//            (Q, dO in registers), then dQ^T += K^T dS^T with the dS^T
-//            accumulator lanes as B operand and K^T read from the row-major K
+// Two persistent kernels, no atomics (every output row has one owner); a team of
+// T waves works on one item at a time (see ring.hpp):
+//   * dq   - Q-stationary: an item is T x NB 32-row q blocks of one (sample, head),
+//            NB per wave; steps stream 32-row K and V tiles.  S^T = K Q^T and
+//            dP^T = V dO^T (Q, dO in registers), then dQ^T += K^T dS^T with the
+//            dS^T accumulator lanes as B operand and K^T read from the row-major K
 //            tile with transposing LDS reads.
-//   * dkdv - KV-stationary: an item is one 32-row kv block, steps stream 32-row
-//            Q and dO tiles.  S = Q K^T and dP = dO V^T (K, V in registers), then
-//            dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T read from the
-//            row-major tiles with transposing LDS reads.
+//   * dkdv - KV-stationary: an item is T 32-row kv blocks, one per wave; steps
+//            stream 32-row Q and dO tiles.  S = Q K^T and dP = dO V^T (K, V in
+//            registers), then dV^T += dO^T P and dK^T += Q^T dS, with dO^T and Q^T
+//            read from the row-major tiles with transposing LDS reads.
 // Rows beyond a sample's lengths are zero tiles (their P, dS and products
 // vanish), so only the local window needs a mask.
 #include "kernels.hpp"
@@ -33,14 +33,15 @@ namespace {
 
 struct Common {
     const KernelArgs a;   // by value: kept in SGPRs, not re-read from the argument segment
-    int lane, r, hh, H, win;
+    int lane, r, hh, wt, H, win;
     uint32_t rs, rso;
     float scale;
 
-    __device__ Common(const KernelArgs& args, int lane_, int D) : a(args) {
+    __device__ Common(const KernelArgs& args, int lane_, int wt_, int D) : a(args) {
         lane = lane_;
         r = lane & 31;
         hh = lane >> 5;
+        wt = wt_;
         H = a.H;
         win = a.window;
         rs = (uint32_t)H * D * 2;
@@ -82,15 +83,20 @@ struct Common {
 // =========================================================================
 // dQ (Q-stationary)
 // =========================================================================
-template <int D, int NB, int ACT>
+template <int D, int T, int NB, int ACT>
 struct DqPol : Common {
-    static constexpr int NSTAT = 2 * NB, NSTRM = 2;
+    // stationary tiles, wave-major: (Q, dO) of block 0, (Q, dO) of block 1, ...
+    static constexpr int NSTAT = 2 * T * NB, NSTRM = 2;
     static constexpr int NDB = D / 32, NKS = D / 16;
+    static constexpr int ROWS = 32 * T * NB;   // q rows per item
+    static constexpr bool HOIST = TeamShape<D, T, 2>::HOIST;
     rsrc_t wq, wo, wk, wv;   // issuing side
     bf16x8 qf[NB][NKS], of[NB][NKS];
     f32x16 acc[NB][NDB];
 
-    __device__ DqPol(const KernelArgs& args, int lane_) : Common(args, lane_, D) {}
+    __device__ DqPol(const KernelArgs& args, int lane_, int wt_) : Common(args, lane_, wt_, D) {}
+
+    __device__ __forceinline__ int qrow(const Rec& c, int b) const { return c.t * ROWS + 32 * (wt * NB + b); }
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
@@ -101,12 +107,10 @@ struct DqPol : Common {
         wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
     }
 
-    // jobs: Q blocks 0..NB-1, dO blocks 0..NB-1, then (K, V) per step
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            const int b = i < NB ? i : i - NB;
-            g.issue(i < NB ? wq : wo, (uint32_t)(w.t * 32 * NB + 32 * b) * rs);
+            g.issue((i & 1) ? wo : wq, (uint32_t)(w.t * ROWS + 32 * (i >> 1)) * rs);
         } else {
             const int rel = i - NSTAT;
             g.issue((rel & 1) ? wv : wk, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
@@ -120,15 +124,17 @@ struct DqPol : Common {
             for (int db = 0; db < NDB; ++db) acc[b][db] = f32x16{};
     }
 
+    // stationary tiles i (Q) and i + 1 (dO) of block i / 2, owned by wave i / (2 NB)
     template <class RingT>
-    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
+    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job, int i) {
+        const int blk = i >> 1;
+        if (blk / NB == wt) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                qf[b][ks] = lds_row8<D>(g.tile(job + b), r, 2 * ks + hh);
-                of[b][ks] = lds_row8<D>(g.tile(job + NB + b), r, 2 * ks + hh);
+                qf[blk % NB][ks] = lds_row8<D>(g.tile(job), r, 2 * ks + hh);
+                of[blk % NB][ks] = lds_row8<D>(g.tile(job + 1), r, 2 * ks + hh);
             }
+        }
     }
 
     template <class RingT>
@@ -136,26 +142,31 @@ struct DqPol : Common {
         const char* kt = g.tile(job);
         const char* vt = g.tile(job + 1);
         bf16x8 kop[NKS], vop[NKS];
+        if constexpr (HOIST) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
-            vop[ks] = lds_row8<D>(vt, r, 2 * ks + hh);
+            for (int ks = 0; ks < NKS; ++ks) {
+                kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
+                vop[ks] = lds_row8<D>(vt, r, 2 * ks + hh);
+            }
         }
         f32x16 sc[NB], dp[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) sc[b] = dp[b] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 ko = HOIST ? kop[ks] : lds_row8<D>(kt, r, 2 * ks + hh);
+            const bf16x8 vo = HOIST ? vop[ks] : lds_row8<D>(vt, r, 2 * ks + hh);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                sc[b] = mfma32(kop[ks], qf[b][ks], sc[b]);
-                dp[b] = mfma32(vop[ks], of[b][ks], dp[b]);
+                sc[b] = mfma32(ko, qf[b][ks], sc[b]);
+                dp[b] = mfma32(vo, of[b][ks], dp[b]);
             }
+        }
         const int j0 = s * 32;
         bf16x8 dsb[NB][2];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const int q0 = c.t * 32 * NB + 32 * b;
+            const int q0 = qrow(c, b);
             f32x16 ds;
             if (win > 0 && !band_all(q0, j0, win)) {
                 // lane column: query q0 + r; element e: key j0 + 8 (e/4) + 4 hh + e % 4
@@ -193,28 +204,33 @@ struct DqPol : Common {
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-            store<D>(acc[b], scale, a.dq, ob, c.lq, c.t * 32 * NB + 32 * b, g.tile(job - NSTRM + b));
+            store<D>(acc[b], scale, a.dq, ob, c.lq, qrow(c, b), g.tile(job - 2 + (T > 1 ? wt : (b & 1))));
     }
 
     __device__ __forceinline__ void item_zero(const Rec& c) {
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) zero<D>(a.dq, ob, c.lq, c.t * 32 * NB + 32 * b);
+        for (int b = 0; b < NB; ++b) zero<D>(a.dq, ob, c.lq, qrow(c, b));
     }
 };
 
 // =========================================================================
 // dK / dV (KV-stationary)
 // =========================================================================
-template <int D, int ACT>
+template <int D, int T, int ACT>
 struct DkdvPol : Common {
-    static constexpr int NSTAT = 2, NSTRM = 2;
+    // stationary tiles, wave-major: (K, V) of wave 0's block, then wave 1's
+    static constexpr int NSTAT = 2 * T, NSTRM = 2;
     static constexpr int NDB = D / 32, NKS = D / 16;
+    static constexpr int ROWS = 32 * T;   // kv rows per item
+    static constexpr bool HOIST = TeamShape<D, T, 1>::HOIST;
     rsrc_t wk, wv, wq, wo;   // issuing side
     bf16x8 kf[NKS], vf[NKS];
     f32x16 accK[NDB], accV[NDB];
 
-    __device__ DkdvPol(const KernelArgs& args, int lane_) : Common(args, lane_, D) {}
+    __device__ DkdvPol(const KernelArgs& args, int lane_, int wt_) : Common(args, lane_, wt_, D) {}
+
+    __device__ __forceinline__ int krow(const Rec& c) const { return c.t * ROWS + 32 * wt; }
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
@@ -225,11 +241,10 @@ struct DkdvPol : Common {
         wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
     }
 
-    // jobs: K block, V block, then (Q, dO) per step
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            g.issue(i == 0 ? wk : wv, (uint32_t)(w.t * 32) * rs);
+            g.issue((i & 1) ? wv : wk, (uint32_t)(w.t * ROWS + 32 * (i >> 1)) * rs);
         } else {
             const int rel = i - NSTAT;
             g.issue((rel & 1) ? wo : wq, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
@@ -241,12 +256,15 @@ struct DkdvPol : Common {
         for (int db = 0; db < NDB; ++db) accK[db] = accV[db] = f32x16{};
     }
 
+    // stationary tiles i (K) and i + 1 (V), owned by wave i / 2
     template <class RingT>
-    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job) {
+    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job, int i) {
+        if ((i >> 1) == wt) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            kf[ks] = lds_row8<D>(g.tile(job), r, 2 * ks + hh);
-            vf[ks] = lds_row8<D>(g.tile(job + 1), r, 2 * ks + hh);
+            for (int ks = 0; ks < NKS; ++ks) {
+                kf[ks] = lds_row8<D>(g.tile(job), r, 2 * ks + hh);
+                vf[ks] = lds_row8<D>(g.tile(job + 1), r, 2 * ks + hh);
+            }
         }
     }
 
@@ -255,19 +273,21 @@ struct DkdvPol : Common {
         const char* qt = g.tile(job);
         const char* ot = g.tile(job + 1);
         bf16x8 qop[NKS], oop[NKS];
+        if constexpr (HOIST) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            qop[ks] = lds_row8<D>(qt, r, 2 * ks + hh);
-            oop[ks] = lds_row8<D>(ot, r, 2 * ks + hh);
+            for (int ks = 0; ks < NKS; ++ks) {
+                qop[ks] = lds_row8<D>(qt, r, 2 * ks + hh);
+                oop[ks] = lds_row8<D>(ot, r, 2 * ks + hh);
+            }
         }
         f32x16 sc = {}, dp = {};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            sc = mfma32(qop[ks], kf[ks], sc);
-            dp = mfma32(oop[ks], vf[ks], dp);
+            sc = mfma32(HOIST ? qop[ks] : lds_row8<D>(qt, r, 2 * ks + hh), kf[ks], sc);
+            dp = mfma32(HOIST ? oop[ks] : lds_row8<D>(ot, r, 2 * ks + hh), vf[ks], dp);
         }
         // accumulator lane: column = kv row j0 + r, element e: q row i0 + 8 (e/4) + 4 hh + e % 4
-        const int i0 = s * 32, j0 = c.t * 32;
+        const int i0 = s * 32, j0 = krow(c);
         f32x16 p, ds;
         if (win > 0 && !band_all(i0, j0, win)) {
             const int base = i0 + 4 * hh - j0 - r;
@@ -303,95 +323,102 @@ struct DkdvPol : Common {
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
         const size_t ob = ((size_t)c.ks * H + c.h) * D;
-        store<D>(accK, scale, a.dk, ob, c.lk, c.t * 32, g.tile(job - 2));
-        store<D>(accV, 1.0f, a.dv, ob, c.lk, c.t * 32, g.tile(job - 1));
+        store<D>(accK, scale, a.dk, ob, c.lk, krow(c), g.tile(job - 2 + (T > 1 ? wt : 0)));
+        store<D>(accV, 1.0f, a.dv, ob, c.lk, krow(c), g.tile(job - 2 + (T > 1 ? wt : 1)));
     }
 
     __device__ __forceinline__ void item_zero(const Rec& c) {
         const size_t ob = ((size_t)c.ks * H + c.h) * D;
-        zero<D>(a.dk, ob, c.lk, c.t * 32);
-        zero<D>(a.dv, ob, c.lk, c.t * 32);
+        zero<D>(a.dk, ob, c.lk, krow(c));
+        zero<D>(a.dv, ob, c.lk, krow(c));
     }
 };
 
-template <int D, int NB, int ACT>
-__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(const KernelArgs a, const Rec* __restrict__ recs,
-                                                         const int32_t* __restrict__ bin_ptr) {
-    using G = RingGeom<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[4 * G::R * G::TILE];
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+template <int D, int T, int NB, int ACT>
+__global__ __launch_bounds__((TeamShape<D, T, 2>::THREADS), (TeamShape<D, T, 2>::WPE)) void dq_bf16_kernel(
+    const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
+    using RingT = Ring<D, T, TeamShape<D, T, 2>::LDS>;
+    __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
+    const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
-    DqPol<D, NB, ACT> pol(a, lane);
-    run_wave<DqPol<D, NB, ACT>, D>(pol, a.P, recs, bin_ptr, smem + wave * (G::R * G::TILE),
-                                   (uint32_t)a.H * D * 2, wave, lane);
+    DqPol<D, T, NB, ACT> pol(a, lane, wt);
+    run_team<DqPol<D, T, NB, ACT>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt, lane);
 }
 
-template <int D, int ACT>
-__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(const KernelArgs a, const Rec* __restrict__ recs,
-                                                           const int32_t* __restrict__ bin_ptr) {
-    using G = RingGeom<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[4 * G::R * G::TILE];
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+template <int D, int T, int ACT>
+__global__ __launch_bounds__((TeamShape<D, T, 1>::THREADS), (TeamShape<D, T, 1>::WPE)) void dkdv_bf16_kernel(
+    const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
+    using RingT = Ring<D, T, TeamShape<D, T, 1>::LDS>;
+    __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
+    const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
-    DkdvPol<D, ACT> pol(a, lane);
-    run_wave<DkdvPol<D, ACT>, D>(pol, a.P, recs, bin_ptr, smem + wave * (G::R * G::TILE),
-                                 (uint32_t)a.H * D * 2, wave, lane);
+    DkdvPol<D, T, ACT> pol(a, lane, wt);
+    run_team<DkdvPol<D, T, ACT>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt, lane);
 }
 
-template <int NB, int ACT>
+template <int T, int NB, int ACT>
 const void* dq_ptr() {
-    return (const void*)&dq_bf16_kernel<GDPA_D, NB, ACT>;
+    return (const void*)&dq_bf16_kernel<GDPA_D, T, NB, ACT>;
 }
-template <int NB, int ACT>
+template <int T, int NB, int ACT>
 const void* dkdv_ptr() {
-    return (const void*)&dkdv_bf16_kernel<GDPA_D, ACT>;
+    return (const void*)&dkdv_bf16_kernel<GDPA_D, T, ACT>;
 }
 
-#define GDPA_ACT_SWITCH(F, W)                                         \
-    switch (act) {                                                    \
-        case ACT_GELU: return F<W, ACT_GELU>();                       \
-        case ACT_SILU: return F<W, ACT_SILU>();                       \
-        case ACT_GELU_POLY: return F<W, ACT_GELU_POLY>();             \
-        case ACT_GELU_TAYLOR6: return F<W, ACT_GELU_TAYLOR6>();       \
-        case ACT_IDENTITY: return F<W, ACT_IDENTITY>();               \
-    }                                                                 \
+#define GDPA_ACT_SWITCH(F, T, NB)                                       \
+    switch (act) {                                                      \
+        case ACT_GELU: return F<T, NB, ACT_GELU>();                     \
+        case ACT_SILU: return F<T, NB, ACT_SILU>();                     \
+        case ACT_GELU_POLY: return F<T, NB, ACT_GELU_POLY>();           \
+        case ACT_GELU_TAYLOR6: return F<T, NB, ACT_GELU_TAYLOR6>();     \
+        case ACT_IDENTITY: return F<T, NB, ACT_IDENTITY>();             \
+    }                                                                   \
     return nullptr;
 
-template <int NB>
-const void* dq_act(int act) { GDPA_ACT_SWITCH(dq_ptr, NB) }
-const void* dkdv_act(int act) { GDPA_ACT_SWITCH(dkdv_ptr, 1) }
+template <int T, int NB>
+const void* dq_act(int act) { GDPA_ACT_SWITCH(dq_ptr, T, NB) }
+template <int T>
+const void* dkdv_act(int act) { GDPA_ACT_SWITCH(dkdv_ptr, T, 1) }
 
 }  // namespace
 
 #define GDPA_CAT2(a, b) a##b
 #define GDPA_CAT(a, b) GDPA_CAT2(a, b)
 
-const void* GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(int nb, int act) {
-    if (nb == 1) return dq_act<1>(act);
-    if (nb == 2) return dq_act<2>(act);
+const void* GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
+    if (team == 1 && nb == 1) return dq_act<1, 1>(act);
+    if (team == 1 && nb == 2) return dq_act<1, 2>(act);
+#if GDPA_D == 128
+    if (team == 2 && nb == 1) return dq_act<2, 1>(act);
+#endif
     return nullptr;
 }
 
-const void* GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(int nb, int act) {
-    return nb == 1 ? dkdv_act(act) : nullptr;
+const void* GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
+    if (nb != 1) return nullptr;
+    if (team == 1) return dkdv_act<1>(act);
+#if GDPA_D == 128
+    if (team == 2) return dkdv_act<2>(act);
+#endif
+    return nullptr;
 }
 
-static hipError_t launch(const void* f, const KernelArgs& a, hipStream_t s) {
+static hipError_t launch(const void* f, const KernelArgs& a, int team, hipStream_t s) {
     if (!f) return hipErrorInvalidValue;
     if (a.P <= 0) return hipSuccess;
     KernelArgs args = a;
     const void* recs = a.items;
     const int32_t* bin_ptr = a.bin_ptr;
     void* params[] = {&args, &recs, &bin_ptr};
-    return hipLaunchKernel(f, dim3((a.P + 3) / 4), dim3(256), params, 0, s);
+    return hipLaunchKernel(f, dim3(a.P), dim3(64 * team), params, 0, s);
 }
 
-hipError_t GDPA_CAT(launch_dq_bf16_d, GDPA_D)(const KernelArgs& a, int nb, int act, hipStream_t s) {
-    return launch(GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(nb, act), a, s);
+hipError_t GDPA_CAT(launch_dq_bf16_d, GDPA_D)(const KernelArgs& a, int team, int nb, int act, hipStream_t s) {
+    return launch(GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(team, nb, act), a, team, s);
 }
 
-hipError_t GDPA_CAT(launch_dkdv_bf16_d, GDPA_D)(const KernelArgs& a, int nb, int act, hipStream_t s) {
-    return launch(GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(nb, act), a, s);
+hipError_t GDPA_CAT(launch_dkdv_bf16_d, GDPA_D)(const KernelArgs& a, int team, int nb, int act, hipStream_t s) {
+    return launch(GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(team, nb, act), a, team, s);
 }
 
 }  // namespace gdpa

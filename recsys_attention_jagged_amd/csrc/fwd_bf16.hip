@@ -7,15 +7,15 @@
 // activation between them; the softmax correction step is gone, so partial
 // products over kv tiles simply add).
 //
-// Work decomposition.  Every wave is an independent persistent worker (see
-// ring.hpp).  An item is one (sample, head) and NB consecutive 32-row q blocks;
-// its steps stream the sample's K and V in 32-row tiles through the wave's LDS
-// ring.  Per step and q block the wave computes S^T = K Q^T with MFMA (K rows
-// from LDS, Q held in registers, the K operand shared by the NB blocks), applies
+// Work decomposition.  A team of T waves (see ring.hpp) works on one item at a
+// time: one (sample, head) and T x NB consecutive 32-row q blocks, NB per wave;
+// its steps stream the sample's K and V in 32-row tiles through the team's LDS
+// ring.  Per step and q block a wave computes S^T = K Q^T with MFMA (K rows from
+// LDS, Q held in registers, the K operand shared by the wave's NB blocks), applies
 // the activation in registers, and feeds the accumulator lanes straight back as
 // the B operand of O^T += V^T P^T (V^T read from the row-major V tile with
-// transposing LDS reads, shared by the NB blocks).  Rows beyond a sample's
-// lengths are zero tiles, so only the local window needs a mask.
+// transposing LDS reads).  Rows beyond a sample's lengths are zero tiles, so only
+// the local window needs a mask.
 #include "kernels.hpp"
 #include "ring.hpp"
 
@@ -26,29 +26,35 @@
 namespace gdpa {
 namespace {
 
-template <int D, int NB, int ACT>
+template <int D, int T, int NB, int ACT>
 struct FwdPol {
-    static constexpr int NSTAT = NB, NSTRM = 2;
+    static constexpr int NSTAT = T * NB, NSTRM = 2;   // stationary tiles: wave-major q blocks
     static constexpr int NDB = D / 32, NKS = D / 16;
+    static constexpr int ROWS = 32 * T * NB;          // q rows per item
+    static constexpr bool HOIST = TeamShape<D, T, 0>::HOIST;
 
     const KernelArgs a;   // by value: kept in SGPRs, not re-read from the argument segment
-    int lane, r, hh, H, win;
+    int lane, r, hh, wt, H, win;
     uint32_t rs, rso;
     float scale;
     rsrc_t wq, wk, wv;    // issuing side: slices of the walk's current item
     bf16x8 qf[NB][NKS];
     f32x16 acc[NB][NDB];
 
-    __device__ FwdPol(const KernelArgs& args, int lane_) : a(args) {
+    __device__ FwdPol(const KernelArgs& args, int lane_, int wt_) : a(args) {
         lane = lane_;
         r = lane & 31;
         hh = lane >> 5;
+        wt = wt_;
         H = a.H;
         win = a.window;
         rs = (uint32_t)H * D * 2;
         rso = (uint32_t)H * D * (a.out_f32 ? 4 : 2);
         scale = a.scale;
     }
+
+    // first q row of this wave's block b
+    __device__ __forceinline__ int qrow(const Rec& c, int b) const { return c.t * ROWS + 32 * (wt * NB + b); }
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
@@ -60,7 +66,7 @@ struct FwdPol {
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            g.issue(wq, (uint32_t)(w.t * 32 * NB + 32 * i) * rs);
+            g.issue(wq, (uint32_t)(w.t * ROWS + 32 * i) * rs);
         } else {
             const int rel = i - NSTAT;
             g.issue((rel & 1) ? wv : wk, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
@@ -74,38 +80,48 @@ struct FwdPol {
             for (int db = 0; db < NDB; ++db) acc[b][db] = f32x16{};
     }
 
+    // stationary tiles i, i + 1 (jobs job, job + 1): tile u belongs to wave u / NB, block u % NB
     template <class RingT>
-    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job) {
+    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job, int i) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int u = 0; u < 2; ++u) {
+            const int tile = i + u;
+            if (tile < NSTAT && tile / NB == wt) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) qf[b][ks] = lds_row8<D>(g.tile(job + b), r, 2 * ks + hh);
+                for (int ks = 0; ks < NKS; ++ks) qf[tile % NB][ks] = lds_row8<D>(g.tile(job + u), r, 2 * ks + hh);
+            }
+        }
     }
 
     template <class RingT>
     __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
         const char* kt = g.tile(job);
         const char* vt = g.tile(job + 1);
-        // all operand reads are issued up front so their latency overlaps the MFMAs
+        // with one wave per SIMD all operand reads are issued up front so their
+        // latency overlaps the MFMAs; with two, each is read just before use
         bf16x8 kop[NKS], vop[2][NDB];
+        if constexpr (HOIST) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
+            for (int ks = 0; ks < NKS; ++ks) kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+            for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) vop[m][db] = lds_col8<D>(vt, 16 * m, db * 32, lane);
+                for (int db = 0; db < NDB; ++db) vop[m][db] = lds_col8<D>(vt, 16 * m, db * 32, lane);
+        }
         f32x16 sc[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) sc[b] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
+        for (int ks = 0; ks < NKS; ++ks) {
+            const bf16x8 ko = HOIST ? kop[ks] : lds_row8<D>(kt, r, 2 * ks + hh);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) sc[b] = mfma32(kop[ks], qf[b][ks], sc[b]);
+            for (int b = 0; b < NB; ++b) sc[b] = mfma32(ko, qf[b][ks], sc[b]);
+        }
         const int j0 = s * 32;
         bf16x8 pb[NB][2];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const int q0 = c.t * 32 * NB + 32 * b;
+            const int q0 = qrow(c, b);
             f32x16 p;
             if (win > 0 && !band_all(q0, j0, win)) {
                 // lane column: query q0 + r; element c: key j0 + 8 (c/4) + 4 hh + c % 4
@@ -125,28 +141,31 @@ struct FwdPol {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db) {
+                const bf16x8 vo = HOIST ? vop[m][db] : lds_col8<D>(vt, 16 * m, db * 32, lane);
 #pragma unroll
-                for (int b = 0; b < NB; ++b) acc[b][db] = mfma32(vop[m][db], pb[b][m], acc[b][db]);
+                for (int b = 0; b < NB; ++b) acc[b][db] = mfma32(vo, pb[b][m], acc[b][db]);
+            }
     }
 
+    // this wave's blocks, staged through a slot of the last step (one slot per wave
+    // in a team; blocks sharing a slot are staged one after the other)
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
         if (a.out_f32) {
             const rsrc_t ro = slice_rsrc((const float*)a.o + ob, c.lq, rso, D * 4);
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                store_block_f32<NDB>(acc[b], 1.0f, ro, (uint32_t)(c.t * 32 * NB + 32 * b + r) * rso, hh);
+            for (int b = 0; b < NB; ++b) store_block_f32<NDB>(acc[b], 1.0f, ro, (uint32_t)(qrow(c, b) + r) * rso, hh);
             return;
         }
-        // stage each 32-row block in a slot of the last step, then store whole rows
         const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, c.lq, rso, D * 2);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) stage_block<D>(acc[b], 1.0f, g.tile(job - NSTRM + b), r, hh);
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-            store_tile<D>(g.tile(job - NSTRM + b), ro, (uint32_t)(c.t * 32 * NB + 32 * b) * rso, rso, lane);
+        for (int b = 0; b < NB; ++b) {
+            char* st = g.tile(job - 2 + (T > 1 ? wt : (b & 1)));
+            stage_block<D>(acc[b], 1.0f, st, r, hh);
+            store_tile<D>(st, ro, (uint32_t)qrow(c, b) * rso, rso, lane);
+        }
     }
 
     // an item without keys: its rows are zero
@@ -156,42 +175,40 @@ struct FwdPol {
             item_begin(c);
             const rsrc_t ro = slice_rsrc((const float*)a.o + ob, c.lq, rso, D * 4);
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
-                store_block_f32<NDB>(acc[b], 1.0f, ro, (uint32_t)(c.t * 32 * NB + 32 * b + r) * rso, hh);
+            for (int b = 0; b < NB; ++b) store_block_f32<NDB>(acc[b], 1.0f, ro, (uint32_t)(qrow(c, b) + r) * rso, hh);
             return;
         }
         const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, c.lq, rso, D * 2);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) store_zero_rows<D>(ro, (uint32_t)(c.t * 32 * NB + 32 * b) * rso, rso, lane);
+        for (int b = 0; b < NB; ++b) store_zero_rows<D>(ro, (uint32_t)qrow(c, b) * rso, rso, lane);
     }
 };
 
-template <int D, int NB, int ACT>
-__global__ __launch_bounds__(256, 1) void fwd_bf16_kernel(const KernelArgs a, const Rec* __restrict__ recs,
-                                                          const int32_t* __restrict__ bin_ptr) {
-    using G = RingGeom<D>;
-    __shared__ __attribute__((aligned(1024))) char smem[4 * G::R * G::TILE];
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+template <int D, int T, int NB, int ACT>
+__global__ __launch_bounds__((TeamShape<D, T, 0>::THREADS), (TeamShape<D, T, 0>::WPE)) void fwd_bf16_kernel(
+    const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
+    using RingT = Ring<D, T, TeamShape<D, T, 0>::LDS>;
+    __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
+    const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
-    FwdPol<D, NB, ACT> pol(a, lane);
-    run_wave<FwdPol<D, NB, ACT>, D>(pol, a.P, recs, bin_ptr, smem + wave * (G::R * G::TILE),
-                                    (uint32_t)a.H * D * 2, wave, lane);
+    FwdPol<D, T, NB, ACT> pol(a, lane, wt);
+    run_team<FwdPol<D, T, NB, ACT>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt, lane);
 }
 
-template <int NB, int ACT>
+template <int T, int NB, int ACT>
 const void* kptr() {
-    return (const void*)&fwd_bf16_kernel<GDPA_D, NB, ACT>;
+    return (const void*)&fwd_bf16_kernel<GDPA_D, T, NB, ACT>;
 }
 
-template <int NB>
+template <int T, int NB>
 const void* kptr_act(int act) {
     switch (act) {
-        case ACT_GELU: return kptr<NB, ACT_GELU>();
-        case ACT_SILU: return kptr<NB, ACT_SILU>();
-        case ACT_GELU_POLY: return kptr<NB, ACT_GELU_POLY>();
-        case ACT_GELU_TAYLOR6: return kptr<NB, ACT_GELU_TAYLOR6>();
-        case ACT_IDENTITY: return kptr<NB, ACT_IDENTITY>();
-        case ACT_ONE: return kptr<NB, ACT_ONE>();
+        case ACT_GELU: return kptr<T, NB, ACT_GELU>();
+        case ACT_SILU: return kptr<T, NB, ACT_SILU>();
+        case ACT_GELU_POLY: return kptr<T, NB, ACT_GELU_POLY>();
+        case ACT_GELU_TAYLOR6: return kptr<T, NB, ACT_GELU_TAYLOR6>();
+        case ACT_IDENTITY: return kptr<T, NB, ACT_IDENTITY>();
+        case ACT_ONE: return kptr<T, NB, ACT_ONE>();
     }
     return nullptr;
 }
@@ -201,21 +218,24 @@ const void* kptr_act(int act) {
 #define GDPA_CAT2(a, b) a##b
 #define GDPA_CAT(a, b) GDPA_CAT2(a, b)
 
-const void* GDPA_CAT(fwd_bf16_kernel_ptr_d, GDPA_D)(int nb, int act) {
-    if (nb == 1) return kptr_act<1>(act);
-    if (nb == 2) return kptr_act<2>(act);
+const void* GDPA_CAT(fwd_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
+    if (team == 1 && nb == 1) return kptr_act<1, 1>(act);
+    if (team == 1 && nb == 2) return kptr_act<1, 2>(act);
+#if GDPA_D == 128
+    if (team == 2 && nb == 1) return kptr_act<2, 1>(act);
+#endif
     return nullptr;
 }
 
-hipError_t GDPA_CAT(launch_fwd_bf16_d, GDPA_D)(const KernelArgs& a, int nb, int act, hipStream_t s) {
-    const void* f = GDPA_CAT(fwd_bf16_kernel_ptr_d, GDPA_D)(nb, act);
+hipError_t GDPA_CAT(launch_fwd_bf16_d, GDPA_D)(const KernelArgs& a, int team, int nb, int act, hipStream_t s) {
+    const void* f = GDPA_CAT(fwd_bf16_kernel_ptr_d, GDPA_D)(team, nb, act);
     if (!f) return hipErrorInvalidValue;
     if (a.P <= 0) return hipSuccess;
     KernelArgs args = a;
     const void* recs = a.items;
     const int32_t* bin_ptr = a.bin_ptr;
     void* params[] = {&args, &recs, &bin_ptr};
-    return hipLaunchKernel(f, dim3((a.P + 3) / 4), dim3(256), params, 0, s);
+    return hipLaunchKernel(f, dim3(a.P), dim3(64 * team), params, 0, s);
 }
 
 }  // namespace gdpa

@@ -9,7 +9,7 @@
 namespace gdpa {
 
 // Arguments common to every kernel.  Tensors are [T, H, d] row-major; a work
-// list is (items, bin_ptr) over P bins, one per persistent wave.
+// list is (items, bin_ptr) over P bins, one per persistent workgroup.
 struct KernelArgs {
     const void* q;
     const void* k;
@@ -23,7 +23,7 @@ struct KernelArgs {
     const int32_t* kv_off;
     const void* items;          // device work-list records (Rec), bin-major
     const int32_t* bin_ptr;
-    int P;          // bins = persistent waves
+    int P;          // bins = persistent workgroups
     int B;          // samples
     int H;
     int window;     // 0 = none
@@ -31,16 +31,17 @@ struct KernelArgs {
     int out_f32;    // outputs stored as fp32 instead of bf16
 };
 
-// bf16 MFMA kernels, one translation unit per head dimension.  Every wave is a
-// persistent worker over one bin (P bins, (P + 3) / 4 workgroups of 4 waves);
-// nb = 32-row stationary blocks per work item (forward and dQ: 1 or 2; dK/dV: 1).
-#define GDPA_DECLARE_LAUNCHERS(D)                                                              \
-    hipError_t launch_fwd_bf16_d##D(const KernelArgs& a, int nb, int act, hipStream_t s);      \
-    hipError_t launch_dq_bf16_d##D(const KernelArgs& a, int nb, int act, hipStream_t s);       \
-    hipError_t launch_dkdv_bf16_d##D(const KernelArgs& a, int nb, int act, hipStream_t s);     \
-    const void* fwd_bf16_kernel_ptr_d##D(int nb, int act);                                     \
-    const void* dq_bf16_kernel_ptr_d##D(int nb, int act);                                      \
-    const void* dkdv_bf16_kernel_ptr_d##D(int nb, int act);
+// bf16 MFMA kernels, one translation unit per head dimension.  A workgroup is a
+// team of `team` waves (1, or 2 for d = 128) working on one bin (P bins, P
+// workgroups); nb = 32-row stationary blocks per wave (forward and dQ: 1 or 2,
+// dK/dV: 1), so an item holds 32 * team * nb stationary rows.
+#define GDPA_DECLARE_LAUNCHERS(D)                                                                      \
+    hipError_t launch_fwd_bf16_d##D(const KernelArgs& a, int team, int nb, int act, hipStream_t s);    \
+    hipError_t launch_dq_bf16_d##D(const KernelArgs& a, int team, int nb, int act, hipStream_t s);     \
+    hipError_t launch_dkdv_bf16_d##D(const KernelArgs& a, int team, int nb, int act, hipStream_t s);   \
+    const void* fwd_bf16_kernel_ptr_d##D(int team, int nb, int act);                                   \
+    const void* dq_bf16_kernel_ptr_d##D(int team, int nb, int act);                                    \
+    const void* dkdv_bf16_kernel_ptr_d##D(int team, int nb, int act);
 GDPA_DECLARE_LAUNCHERS(32)
 GDPA_DECLARE_LAUNCHERS(64)
 GDPA_DECLARE_LAUNCHERS(128)

@@ -8,23 +8,32 @@ namespace gdpa {
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>&) {
+Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>&, int d) {
     int64_t nq = 0, sq = 0;
     for (size_t b = 0; b < lq.size(); ++b) {
         nq += lq[b] > 0;
         sq += lq[b];
     }
-    // two q blocks per item once the mean non-empty query length reaches 64
-    const int nb = (nq > 0 && sq >= 64 * nq) ? 2 : 1;
+    // mean non-empty length >= m  <=>  total >= m * count
+    auto mean_at_least = [](int64_t total, int64_t count, int64_t m) { return count > 0 && total >= m * count; };
     Layout L;
-    L.nb[LIST_FWD] = nb;
-    L.nb[LIST_DQ] = nb;
-    L.nb[LIST_DKDV] = 1;
+    if (d == 128) {
+        // two-wave teams once the stationary side is long enough to fill them
+        // two-wave forward teams once the queries are long enough to fill them
+        L.team[LIST_FWD] = mean_at_least(sq, nq, 48) ? 2 : 1;
+        L.nb[LIST_FWD] = 1;
+        L.team[LIST_DQ] = L.team[LIST_DKDV] = 1;
+        L.nb[LIST_DQ] = L.nb[LIST_DKDV] = 1;
+    } else {
+        L.team[LIST_FWD] = L.team[LIST_DQ] = L.team[LIST_DKDV] = 1;
+        L.nb[LIST_FWD] = mean_at_least(sq, nq, 64) ? 2 : 1;
+        L.nb[LIST_DQ] = L.nb[LIST_DKDV] = 1;
+    }
     return L;
 }
 
-void tile_sizes(int, int nb, int* t_stat, int* t_strm) {
-    *t_stat = 32 * nb;
+void tile_sizes(int, int team, int nb, int* t_stat, int* t_strm) {
+    *t_stat = 32 * team * nb;
     *t_strm = 32;
 }
 
@@ -36,12 +45,13 @@ struct Cand {
 }  // namespace
 
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
-                   int H, int window, int P, int nb, bool zigzag) {
+                   int H, int window, int P, int team, int nb, bool zigzag) {
     WorkList wl;
     wl.kind = kind;
     wl.P = P;
+    wl.team = team;
     wl.nb = nb;
-    tile_sizes(kind, nb, &wl.t_stat, &wl.t_strm);
+    tile_sizes(kind, team, nb, &wl.t_stat, &wl.t_strm);
     const int64_t TS = wl.t_stat, TR = wl.t_strm;
 
     std::vector<Cand> cands;
@@ -107,7 +117,7 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
 }
 
 std::vector<int32_t> export_list(const WorkList& wl) {
-    std::vector<int32_t> out = {wl.P, (int32_t)wl.items.size(), wl.t_stat, wl.t_strm, wl.nb};
+    std::vector<int32_t> out = {wl.P, (int32_t)wl.items.size(), wl.t_stat, wl.t_strm, wl.team, wl.nb};
     out.insert(out.end(), wl.bin_ptr.begin(), wl.bin_ptr.end());
     for (const Item& it : wl.items) {
         out.push_back(it.b);

@@ -7,10 +7,11 @@
 // and deals them to the compute units in a zigzag so the per-unit load is even.
 //
 // A work item is (sample b, head h, stationary tile t) plus the contiguous range
-// [s0, s1] of streaming tiles it visits; one wave processes one item.
-// Q-stationary lists ("fwd", "dq") have q tiles of 32 NB rows and kv steps of 32
-// rows; the KV-stationary list ("dkdv") has kv tiles of 32 rows and q steps of 32
-// rows.  Items whose other side is empty get no steps and write zeros.
+// [s0, s1] of streaming tiles it visits; one team of waves processes one item.
+// Stationary tiles have 32 * team * nb rows (team waves with nb 32-row blocks
+// each), streaming tiles 32 rows: q tiles / kv steps for the Q-stationary lists
+// ("fwd", "dq"), kv tiles / q steps for the KV-stationary list ("dkdv").  Items
+// whose other side is empty get no steps and write zeros.
 //
 // Cost of an item: valid stationary rows + sum over steps of (valid streaming
 // rows + 32).  Order: cost descending, then (b, h, t).  Deal: the r-th item goes
@@ -39,24 +40,25 @@ struct DevRec {
 static_assert(sizeof(DevRec) == 32, "DevRec must be 32 bytes");
 
 struct WorkList {
-    int kind = 0, P = 0, t_stat = 0, t_strm = 0, nb = 0;
+    int kind = 0, P = 0, t_stat = 0, t_strm = 0, team = 0, nb = 0;
     std::vector<int32_t> bin_ptr;   // P + 1
     std::vector<Item> items;        // bin-major, deal order inside a bin
     std::vector<int64_t> bin_cost;  // P
     int64_t n_steps = 0;
 };
 
-// 32-row stationary blocks per item, per list
+// waves per team and 32-row stationary blocks per wave, per list
 struct Layout {
+    int team[3];
     int nb[3];
 };
 
 constexpr int kStepCharge = 32;
 
-Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk);
-void tile_sizes(int kind, int nb, int* t_stat, int* t_strm);
+Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk, int d);
+void tile_sizes(int kind, int team, int nb, int* t_stat, int* t_strm);
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
-                   int H, int window, int P, int nb, bool zigzag);
+                   int H, int window, int P, int team, int nb, bool zigzag);
 std::vector<int32_t> export_list(const WorkList& wl);
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
                                    const std::vector<int32_t>& kv_off);

@@ -1,20 +1,22 @@
-// Per-wave tile ring and persistent walk shared by the bf16 GDPA kernels (gfx950).
+// Tile ring and persistent walk shared by the bf16 GDPA kernels (gfx950).
 //
-// Every wave of a workgroup is an independent persistent worker: it owns one
-// planner bin, its own slice of LDS and its own loads, and never synchronises
-// with the other waves (no barriers).  A wave's LDS slice is a ring of R slots,
-// each holding one 32-row tile of one tensor (32 x D bf16).  The wave walks its
-// bin's items as one flattened sequence of tile loads ("jobs"): for each item its
-// stationary tiles, then for each step its streaming tiles.  The issuing side
+// A workgroup is a team of T waves (T = 1 or 2) that owns one planner bin and
+// one slice of LDS, and synchronises only with itself.  The slice is a ring of R
+// slots, each holding one 32-row tile of one tensor (32 x D bf16).  The team walks
+// its bin's items as one flattened sequence of tile loads ("jobs"): for each item
+// its stationary tiles, then for each step its streaming tiles.  The issuing side
 // runs up to R jobs ahead of the computing side, across item boundaries, so short
 // items do not drain the pipeline (GDPA page, aitrends.kr/articles/26275,
-// "Section details": pipelining moved to the outer loop; loop flattening).
+// "Section details": pipelining moved to the outer loop; loop flattening).  With
+// two waves per SIMD (two teams, or two one-wave workgroups, per SIMD) one wave's
+// loads overlap the other's arithmetic.
 //
 // Loads are buffer_load_dwordx4 ... lds: the 64 lanes of one instruction write
-// 1 KiB of consecutive LDS, without VGPR staging.  A tile is stored row-major
-// without padding, the 16-byte chunk c of row r at chunk position c ^ swz<D>(r);
-// the swizzle is applied on the global side (each lane fetches the chunk that
-// belongs at its LDS position) and makes both read patterns bank-conflict free:
+// 1 KiB of consecutive LDS, without VGPR staging; each wave of a team issues its
+// share of a tile's instructions.  A tile is stored row-major without padding,
+// the 16-byte chunk c of row r at chunk position c ^ swz<D>(r); the swizzle is
+// applied on the global side (each lane fetches the chunk that belongs at its LDS
+// position) and makes both read patterns bank-conflict free:
 //   * row operands: 16 rows at one chunk (ds_read_b128);
 //   * transposed operands: 4 consecutive rows x 4 consecutive chunks
 //     (ds_read_b64_tr_b16), where lane i of each 16-lane group receives column
@@ -22,13 +24,14 @@
 // Rows outside the (sample, head) slice are outside the buffer descriptor's
 // range and arrive as zeros; a job of an empty slice writes a zero tile.
 //
-// Synchronisation is per wave: a job's J instructions complete in issue order,
-// so "job k has landed" is `s_waitcnt vmcnt(J * (jobs issued after k))`; a slot
-// is re-filled only after the wave's LDS reads of it have completed
-// (`s_waitcnt lgkmcnt(0)`).  The loads are issued from inline assembly, so the
-// compiler neither sees the asynchronous LDS writes nor inserts waits of its own
-// for them; stores are left to the compiler and are not counted (a wait then
-// only becomes stricter).
+// Synchronisation: a wave's load instructions complete in issue order, so "job k
+// has landed" is `s_waitcnt vmcnt(JW * (jobs issued after k))` per wave, followed
+// by a workgroup barrier when T > 1 so that every wave's share is visible.  Slots
+// are re-filled only after such a barrier (and this wave's `s_waitcnt
+// lgkmcnt(0)`), i.e. after every wave has finished reading them.  The loads are
+// issued from inline assembly, so the compiler neither sees the asynchronous LDS
+// writes nor inserts waits of its own for them; stores are left to the compiler
+// and are not counted (a wait then only becomes stricter).
 #pragma once
 
 #include "device.hpp"
@@ -100,15 +103,16 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
                  : "s"(lds), "v"(voff), "s"(rs));
 }
 
-// s_waitcnt vmcnt(J m) for a uniform m in [0, 7] (the count is an immediate)
+// s_waitcnt vmcnt(J m) for a uniform m in [0, MMAX] (the count is an immediate)
 template <int J>
 __device__ __forceinline__ void wait_jobs(int m) {
-    static_assert(7 * J <= 63, "vmcnt is 6 bits");
+    constexpr int MMAX = (63 / J) > 15 ? 15 : (63 / J);
 #define GDPA_WJ(M) \
-    case M: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(J * M) : "memory"); break;
+    case M: if constexpr (M <= MMAX) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(J * M) : "memory"); break;
     switch (m) {
-        GDPA_WJ(0) GDPA_WJ(1) GDPA_WJ(2) GDPA_WJ(3) GDPA_WJ(4) GDPA_WJ(5) GDPA_WJ(6)
-        default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(J * 7) : "memory"); break;
+        GDPA_WJ(0) GDPA_WJ(1) GDPA_WJ(2) GDPA_WJ(3) GDPA_WJ(4) GDPA_WJ(5) GDPA_WJ(6) GDPA_WJ(7)
+        GDPA_WJ(8) GDPA_WJ(9) GDPA_WJ(10) GDPA_WJ(11) GDPA_WJ(12) GDPA_WJ(13) GDPA_WJ(14) GDPA_WJ(15)
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
 #undef GDPA_WJ
 }
@@ -116,50 +120,87 @@ __device__ __forceinline__ void wait_jobs(int m) {
 // this wave's LDS reads (and scalar loads) have completed
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-template <int D>
+// Geometry of a team's ring: T waves share LDS_BYTES of LDS.
+template <int D, int T, int LDS_BYTES>
 struct RingGeom {
     static constexpr int TILE = 32 * D * 2;            // bytes of one 32-row tile
     static constexpr int J = TILE / 1024;              // wave instructions per tile
-    static constexpr int WAVE_LDS = 40 * 1024;         // LDS per wave (4 waves share 160 KiB)
-    static constexpr int R = (WAVE_LDS / TILE) > 8 ? 8 : (WAVE_LDS / TILE);   // slots
-    static_assert(R >= 3, "the ring needs room for one step plus look-ahead");
+    static constexpr int JW = J / T;                   // issued by each wave of the team
+    static constexpr int RMAX = (63 / JW) + 1 > 16 ? 16 : (63 / JW) + 1;   // vmcnt is 6 bits
+    static constexpr int R = (LDS_BYTES / TILE) > RMAX ? RMAX : (LDS_BYTES / TILE);   // slots
+    static constexpr int BYTES = R * TILE;
+    static_assert(J % T == 0, "a tile's instructions are split evenly over the team");
+    // a consume point takes at most 2 jobs and the ring runs R - 2 jobs past the
+    // previous one, so R >= 4 keeps every awaited job issued
+    static_assert(R >= 4, "the ring needs a step plus look-ahead");
 };
 
-template <int D>
-struct Ring : RingGeom<D> {
-    using G = RingGeom<D>;
+template <int D, int T, int LDS_BYTES>
+struct Ring : RingGeom<D, T, LDS_BYTES> {
+    using G = RingGeom<D, T, LDS_BYTES>;
     static constexpr int CPR = D / 8;   // 16-byte chunks per row
-    uint32_t off[G::J];                 // lane offsets of each instruction inside a tile
+    uint32_t off[G::JW];                // lane offsets of this wave's instructions inside a tile
     uint32_t base;                      // LDS address of slot 0 (uniform)
     char* gbase;                        // the same slot 0 as a generic pointer
+    int wt;                             // this wave's index in the team (uniform)
     int issued;                         // jobs issued so far (uniform)
 
-    __device__ __forceinline__ void init(char* slice, uint32_t row_stride_bytes, int lane) {
+    __device__ __forceinline__ void init(char* slice, uint32_t row_stride_bytes, int wt_, int lane) {
         gbase = slice;
         base = lds_addr(slice);
+        wt = wt_;
         issued = 0;
 #pragma unroll
-        for (int j = 0; j < G::J; ++j) {
-            const int slot = j * 64 + lane;
+        for (int jj = 0; jj < G::JW; ++jj) {
+            const int slot = (jj * T + wt) * 64 + lane;
             const int row = slot / CPR, pos = slot % CPR;
-            off[j] = (uint32_t)row * row_stride_bytes + (uint32_t)((pos ^ swz<D>(row)) << 4);
+            off[jj] = (uint32_t)row * row_stride_bytes + (uint32_t)((pos ^ swz<D>(row)) << 4);
         }
     }
 
     __device__ __forceinline__ int slot_of(int job) const { return job % G::R; }
     __device__ __forceinline__ char* tile(int job) const { return gbase + slot_of(job) * G::TILE; }
 
-    // load rows [row0, row0 + 32) of the slice `rs` (row_off = row0 * stride) into the next slot
+    // this wave's share of loading rows [row0, row0 + 32) of the slice `rs`
+    // (row_off = row0 * stride) into the next slot
     __device__ __forceinline__ void issue(rsrc_t rs, uint32_t row_off) {
         const uint32_t lds = base + (uint32_t)(slot_of(issued) * G::TILE);
 #pragma unroll
-        for (int j = 0; j < G::J; ++j) dma16(rs, off[j] + row_off, lds + (uint32_t)j * 1024u);
+        for (int jj = 0; jj < G::JW; ++jj) dma16(rs, off[jj] + row_off, lds + (uint32_t)(jj * T + wt) * 1024u);
         ++issued;
     }
 
-    // wait until job k has landed
-    __device__ __forceinline__ void wait(int k) const { wait_jobs<G::J>(issued - 1 - k); }
+    // wait until this wave's share of job k has landed
+    __device__ __forceinline__ void wait(int k) const { wait_jobs<G::JW>(issued - 1 - k); }
 };
+
+// Launch shape of a team (KIND: 0 forward, 1 dK/dV, 2 dQ): waves per SIMD the
+// register budget is sized for (WPE), and the team's LDS (160 KiB per CU shared
+// by the resident teams).  Two waves per SIMD (8 per CU) where the registers fit
+// and it measured faster: the forward kernel (d <= 64: one-wave teams with 20 KiB;
+// d = 128: two-wave teams with 40 KiB) and the d <= 64 dQ kernel.  Otherwise one
+// wave per SIMD with 40 KiB per wave (80 KiB for a two-wave d = 128 backward
+// team).  With two waves per SIMD, operands are read from LDS just before use
+// (the other wave hides the latency); with one, all of a step's operand reads are
+// issued up front.
+template <int D, int T, int KIND>
+struct TeamShape {
+    static_assert(T == 1 || T == 2, "teams of one or two waves");
+    static constexpr int THREADS = 64 * T;
+    static constexpr bool TWO = KIND == 0 ? (D < 128 || T == 2) : (KIND == 2 && D < 128);
+    static constexpr int WPE = TWO ? 2 : 1;
+    static constexpr int LDS = (TWO ? 20 * 1024 : 40 * 1024) * T;
+    static constexpr bool HOIST = WPE == 1;
+};
+
+// this wave's LDS reads have completed and, for a team, every wave has arrived
+template <int T>
+__device__ __forceinline__ void team_sync() {
+    if constexpr (T > 1)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+        wait_lds();
+}
 
 // -------------------------------------------------------------------------
 // output blocks: staged through LDS, stored as whole rows
@@ -204,7 +245,8 @@ __device__ __forceinline__ void store_zero_rows(rsrc_t ro, uint32_t row_off0, ui
         buf_store16(ro, row_off0 + (uint32_t)(i * RPI + rr) * rso + (uint32_t)c * 16u, u32x4{0u, 0u, 0u, 0u});
 }
 
-// The issuing walk over a bin's items.  Pol provides NSTAT (stationary tiles per
+// The issuing walk over a bin's items (every wave of a team runs the same walk
+// and issues its share of each job).  Pol provides NSTAT (stationary tiles per
 // item with steps), NSTRM (streaming tiles per step), walk_item(rec) (per-item
 // descriptors of the issuing side) and issue_job(ring, rec, i) for the i-th job
 // of the item (i < NSTAT: stationary tile i; else step s0 + (i - NSTAT) / NSTRM,
@@ -242,36 +284,38 @@ __device__ __forceinline__ void pump(Pol& pol, Walk& w, RingT& ring, int consume
     }
 }
 
-// This wave's bin: workgroups are dispatched round-robin over the 8 XCDs, so the
+// This team's bin: workgroups are dispatched round-robin over the 8 XCDs, so the
 // workgroup index is remapped to make consecutive logical workgroups (whose bins
 // the planner fills with neighbouring items of equal cost, e.g. the q tiles of one
-// sample) share an XCD and its L2; the 4 waves of a workgroup take 4 consecutive bins.
-__device__ __forceinline__ int wave_bin(int wave) {
+// sample) share an XCD and its L2.
+__device__ __forceinline__ int team_bin() {
     const int G = gridDim.x, w = blockIdx.x;
-    const int lw = (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
-    return lw * 4 + wave;
+    return (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
 }
 
 // The computing side.  Pol also provides:
-//   item_begin(rec)               zero the accumulators
-//   load_stat(rec, ring, job)     stationary tiles (jobs job .. job + NSTAT - 1) -> registers
-//   step(rec, s, ring, job)       one streaming step (jobs job .. job + NSTRM - 1)
-//   item_end(rec, ring, job)      store the item's outputs, staged through the slots
-//                                 of its last step (jobs job - NSTRM .. job - 1), which
-//                                 are refilled only afterwards
-//   item_zero(rec)                store the outputs of an item without steps (zeros)
-template <class Pol, int D>
-__device__ __forceinline__ void run_wave(Pol& pol, int P, const Rec* __restrict__ recs,
+//   item_begin(rec)                 zero the accumulators
+//   load_stat(rec, ring, job, i)    stationary tiles i, i + 1 (jobs job, job + 1; only
+//                                   tile i if i + 1 == NSTAT) -> the owning wave's registers
+//   step(rec, s, ring, job)         one streaming step (jobs job, job + 1)
+//   item_end(rec, ring, job)        store this wave's outputs, staged through a slot of
+//                                   the item's last step (jobs job - 2, job - 1), which
+//                                   is re-filled only after the next barrier
+//   item_zero(rec)                  store this wave's outputs of an item without steps
+// Every consume point waits for its jobs, synchronises the team and only then
+// re-fills the slots the team has finished with.
+template <class Pol, class RingT, int T>
+__device__ __forceinline__ void run_team(Pol& pol, int P, const Rec* __restrict__ recs,
                                          const int32_t* __restrict__ bin_ptr, char* slice, uint32_t row_stride,
-                                         int wave, int lane) {
-    using RingT = Ring<D>;
-    const int bin = wave_bin(wave);
+                                         int wt, int lane) {
+    static_assert(Pol::NSTRM == 2, "a step streams two tiles");
+    const int bin = team_bin();
     if (bin >= P) return;
     const int beg = bin_ptr[bin], end = bin_ptr[bin + 1];
     if (beg >= end) return;
 
     RingT ring;
-    ring.init(slice, row_stride, lane);
+    ring.init(slice, row_stride, wt, lane);
     Walk w;
     w.idx = beg;
     w.end = end;
@@ -290,22 +334,25 @@ __device__ __forceinline__ void run_wave(Pol& pol, int P, const Rec* __restrict_
             continue;
         }
         pol.item_begin(c);
-        ring.wait(job + Pol::NSTAT - 1);
-        pol.load_stat(c, ring, job);
-        wait_lds();
-        job += Pol::NSTAT;
-        pump<Pol, RingT>(pol, w, ring, job, recs);
-        for (int s = c.s0;; ++s) {
-            ring.wait(job + Pol::NSTRM - 1);
-            pol.step(c, s, ring, job);
-            wait_lds();
-            job += Pol::NSTRM;
-            if (s == c.s1) break;
+#pragma unroll
+        for (int i = 0; i < Pol::NSTAT; i += 2) {
+            const int n = (Pol::NSTAT - i) < 2 ? 1 : 2;
+            ring.wait(job + n - 1);
+            team_sync<T>();
             pump<Pol, RingT>(pol, w, ring, job, recs);
+            pol.load_stat(c, ring, job, i);
+            job += n;
         }
+        for (int s = c.s0;; ++s) {
+            ring.wait(job + 1);
+            team_sync<T>();
+            pump<Pol, RingT>(pol, w, ring, job, recs);
+            pol.step(c, s, ring, job);
+            job += 2;
+            if (s == c.s1) break;
+        }
+        team_sync<T>();   // every wave is done with the last step's slots
         pol.item_end(c, ring, job);
-        wait_lds();
-        pump<Pol, RingT>(pol, w, ring, job, recs);
     }
 }
 

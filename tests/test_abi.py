@@ -36,15 +36,15 @@ def test_status_strings_and_poly_bound():
     assert 0 < G.gdpa_gelu_poly_bound() < 1e-4
 
 
-def _host_plan(lq, lk, H, d, window, P=1024, blocks=(0, 0, 0), rr=False):
+def _host_plan(lq, lk, H, d, window, P=1024, team=(0, 0, 0), blocks=(0, 0, 0), rr=False):
     qo, ko = offsets(lq), offsets(lk)
     return G.gdpa_plan_create(qo, ko, len(lq), H, d, window, "bf16", host_only=True,
-                              bins=(P, P, P), blocks=blocks, round_robin=rr)
+                              bins=(P, P, P), team=team, blocks=blocks, round_robin=rr)
 
 
-def _ref_exports(lq, lk, H, window, P, layout=None, zigzag=True):
-    layout = layout or PR.auto_layout(list(lq), list(lk), window)
-    return {kind: PR.export(PR.plan_list(kind, list(lq), list(lk), H, window, P, layout[kind], zigzag=zigzag))
+def _ref_exports(lq, lk, H, window, P, d, layout=None, zigzag=True):
+    layout = layout or PR.auto_layout(list(lq), list(lk), window, d)
+    return {kind: PR.export(PR.plan_list(kind, list(lq), list(lk), H, window, P, *layout[kind], zigzag=zigzag))
             for kind in PR.LISTS}
 
 
@@ -55,7 +55,7 @@ def test_plan_bit_exact_vs_reference_on_workloads(cfg):
     lq, lk = [int(x) for x in lq], [int(x) for x in lk]
     plan = _host_plan(lq, lk, w["H"], w["d"], w["window"])
     try:
-        ref = _ref_exports(lq, lk, w["H"], w["window"], 1024)
+        ref = _ref_exports(lq, lk, w["H"], w["window"], 1024, w["d"])
         for kind in PR.LISTS:
             got = G.gdpa_plan_export(plan, kind)
             np.testing.assert_array_equal(got, np.asarray(ref[kind], dtype=np.int32), err_msg=kind)
@@ -75,13 +75,17 @@ EDGE = [
 
 
 @pytest.mark.parametrize("lq,lk,window", EDGE)
-@pytest.mark.parametrize("blocks", [(1, 1, 1), (2, 1, 2), (1, 1, 2), (2, 1, 1)])
+@pytest.mark.parametrize("d,team,blocks", [(64, (1, 1, 1), (1, 1, 1)), (64, (1, 1, 1), (2, 1, 2)),
+                                           (128, (2, 2, 2), (1, 1, 1)), (128, (1, 2, 1), (2, 1, 2)),
+                                           (128, (0, 0, 0), (0, 0, 0)), (32, (0, 0, 0), (0, 0, 0))])
 @pytest.mark.parametrize("P,rr", [(1, False), (7, False), (1024, False), (16, True)])
-def test_plan_bit_exact_vs_reference_edge_cases(lq, lk, window, blocks, P, rr):
-    plan = _host_plan(lq, lk, 3, 64, window, P=P, blocks=blocks, rr=rr)
+def test_plan_bit_exact_vs_reference_edge_cases(lq, lk, window, d, team, blocks, P, rr):
+    plan = _host_plan(lq, lk, 3, d, window, P=P, team=team, blocks=blocks, rr=rr)
     try:
-        layout = {"fwd": blocks[0], "dkdv": blocks[1], "dq": blocks[2]}
-        ref = _ref_exports(lq, lk, 3, window, P, layout, zigzag=not rr)
+        auto = PR.auto_layout(list(lq), list(lk), window, d)
+        layout = {kind: (team[i] or auto[kind][0], blocks[i] or auto[kind][1])
+                  for i, kind in enumerate(("fwd", "dkdv", "dq"))}
+        ref = _ref_exports(lq, lk, 3, window, P, d, layout, zigzag=not rr)
         for kind in PR.LISTS:
             np.testing.assert_array_equal(G.gdpa_plan_export(plan, kind), np.asarray(ref[kind], np.int32))
     finally:
@@ -121,8 +125,12 @@ def test_create_rejects_bad_arguments():
     assert bad(window=-1) == 1
     assert bad(dtype=7) == 1
     assert bad(blocks=(3, 0, 0)) == 1
-    assert bad(blocks=(0, 2, 0)) == 1          # dK/dV items hold one kv block
+    assert bad(blocks=(0, 2, 0)) == 1          # dK/dV: one kv block per wave
     assert bad(blocks=(0, 0, -1)) == 1
+    assert bad(team=(3, 0, 0)) == 1
+    assert bad(team=(2, 0, 0)) == 1            # two-wave teams only at d = 128
+    assert bad(d=128, team=(0, 0, 2), blocks=(0, 0, 2)) == 1   # two-wave teams: one block per wave
+    assert bad(d=128, team=(2, 0, 0), blocks=(2, 0, 0)) == 1
     assert bad(qo=np.array([1, 3, 7], np.int32)) == 2           # BAD_OFFSETS: not starting at 0
     assert bad(qo=np.array([0, 5, 3], np.int32)) == 2           # decreasing
     assert bad(ko=offsets([3, 5]), window=4) == 2               # window with Lq != Lk

@@ -128,29 +128,35 @@ def test_workload_backward_small(cfg):
 RAGGED = [0, 1, 5, 31, 32, 33, 64, 65, 100, 127, 128, 129, 200, 300]
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
-@pytest.mark.parametrize("nb", [1, 2])
-def test_layouts_forward(d, nb):
-    say(f"forward layout d={d} blocks={nb}")
-    rng = np.random.default_rng(d + nb)
+FWD_LAYOUTS = [(32, 1, 1), (32, 1, 2), (64, 1, 1), (64, 1, 2), (128, 1, 1), (128, 1, 2), (128, 2, 1)]
+
+
+@pytest.mark.parametrize("d,team,nb", FWD_LAYOUTS)
+def test_layouts_forward(d, team, nb):
+    say(f"forward layout d={d} team={team} blocks={nb}")
+    rng = np.random.default_rng(d + 3 * team + nb)
     lq = rng.permutation(RAGGED)
     lk = rng.permutation(RAGGED)
     inp = make_from_lengths(lq, lk, 2, d, act="gelu", seed=3, device=DEV)
-    check_close(run_fwd(inp, blocks=(nb, 0, 0)), oracle_fwd(inp), f"O d={d} nb={nb}")
+    check_close(run_fwd(inp, team=(team, 0, 0), blocks=(nb, 0, 0)), oracle_fwd(inp), f"O d={d} t={team} nb={nb}")
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
-@pytest.mark.parametrize("nb", [1, 2])
-def test_layouts_backward(d, nb):
-    say(f"backward layout d={d} dq blocks={nb}")
-    rng = np.random.default_rng(10 * d + nb)
+# (d, dQ team, dQ blocks, dK/dV team)
+BWD_LAYOUTS = [(32, 1, 1, 1), (32, 1, 2, 1), (64, 1, 1, 1), (64, 1, 2, 1), (128, 1, 1, 1), (128, 1, 2, 1),
+               (128, 2, 1, 2)]
+
+
+@pytest.mark.parametrize("d,tq,nb,tk", BWD_LAYOUTS)
+def test_layouts_backward(d, tq, nb, tk):
+    say(f"backward layout d={d} dq team={tq} blocks={nb} dkdv team={tk}")
+    rng = np.random.default_rng(10 * d + 3 * tq + nb + tk)
     lq = rng.permutation(RAGGED)
     lk = rng.permutation(RAGGED)
     inp = make_from_lengths(lq, lk, 2, d, act="silu", seed=4, device=DEV)
-    g = run_bwd(inp, blocks=(0, 1, nb))
+    g = run_bwd(inp, team=(0, tk, tq), blocks=(0, 1, nb))
     r = oracle_bwd(inp)
     for name, a, b in zip(("dQ", "dK", "dV"), g, r):
-        check_close(a, b, f"{name} d={d} nb={nb}")
+        check_close(a, b, f"{name} d={d} tq={tq} nb={nb} tk={tk}")
 
 
 @pytest.mark.parametrize("bins", [(1, 1, 1), (3, 5, 6), (13, 9, 7)])
@@ -174,14 +180,19 @@ def test_activations_forward_backward(act):
         check_close(a, b, f"{name} {act}")
 
 
+# (team, blocks) for the forward / dK/dV / dQ lists
+WIN_LAYOUTS = [((1, 1, 1), (1, 1, 1)), ((1, 1, 1), (2, 1, 2)), ((2, 2, 2), (1, 1, 1)), ((1, 2, 1), (2, 1, 2))]
+
+
 @pytest.mark.parametrize("window", [1, 2, 17, 128, 1000])
-@pytest.mark.parametrize("nb", [1, 2])
-def test_windows(window, nb):
-    say(f"window {window} blocks {nb}")
+@pytest.mark.parametrize("lay", range(len(WIN_LAYOUTS)))
+def test_windows(window, lay):
+    team, blocks = WIN_LAYOUTS[lay]
+    say(f"window {window} team {team} blocks {blocks}")
     L = [1, 33, 128, 129, 700, 0, 300]
     inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, seed=6, device=DEV)
-    check_close(run_fwd(inp, blocks=(nb, 1, nb)), oracle_fwd(inp), f"O w={window}")
-    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, blocks=(nb, 1, nb)), oracle_bwd(inp)):
+    check_close(run_fwd(inp, team=team, blocks=blocks), oracle_fwd(inp), f"O w={window}")
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, team=team, blocks=blocks), oracle_bwd(inp)):
         check_close(a, b, f"{name} w={window}")
 
 
@@ -237,13 +248,12 @@ def _probe_expect(lq, lk, window, bit=None):
 
 
 @pytest.mark.parametrize("window", [0, 128])
-@pytest.mark.parametrize("nb", [1, 2])
-def test_index_probe_bit_exact(window, nb):
-    say(f"count/bit probe window={window} blocks={nb}")
+@pytest.mark.parametrize("d,team,nb", [(32, 1, 1), (32, 1, 2), (128, 1, 2), (128, 2, 1)])
+def test_index_probe_bit_exact(window, d, team, nb):
+    say(f"count/bit probe window={window} d={d} team={team} blocks={nb}")
     L = [1, 31, 32, 33, 127, 128, 129, 600, 0, 1100] if window else None
     lq = L or [3, 31, 32, 33, 0, 128, 129, 257, 40, 1]
     lk = L or [129, 1, 64, 0, 5, 300, 33, 257, 511, 2]
-    d = 32
     inp = make_from_lengths(lq, lk, 2, d, act="one", window=window, seed=9, device=DEV)
     # V[j, h, e] = bit e of the key's local index j (e < 16); V[j, h, 16:] = 1
     vals = []
@@ -253,7 +263,7 @@ def test_index_probe_bit_exact(window, nb):
         vals.append(np.concatenate([bits, np.ones((c, d - 16), np.float32)], axis=1))
     V = np.concatenate(vals) if vals else np.zeros((0, d), np.float32)
     inp.v = torch.tensor(np.repeat(V[:, None, :], 2, axis=1), dtype=torch.bfloat16, device=DEV)
-    o = run_fwd(inp, act="one", dtype="bf16_f32out", blocks=(nb, 0, 0))
+    o = run_fwd(inp, act="one", dtype="bf16_f32out", team=(team, 0, 0), blocks=(nb, 0, 0))
     cnt = _probe_expect(lq, lk, window)
     for h in range(2):
         np.testing.assert_array_equal(o[:, h, 16], cnt)

@@ -79,19 +79,23 @@ def test_zigzag_beats_round_robin_on_skewed_costs():
 
 
 def test_auto_layout_rules():
-    assert PR.auto_layout([32] * 8, [1000] * 8) == {"fwd": 1, "dq": 1, "dkdv": 1}
-    assert PR.auto_layout([300] * 8, [32] * 8) == {"fwd": 2, "dq": 2, "dkdv": 1}
-    assert PR.auto_layout([63, 65, 0], [70] * 3) == {"fwd": 2, "dq": 2, "dkdv": 1}
-    assert PR.auto_layout([63, 64, 0], [70] * 3) == {"fwd": 1, "dq": 1, "dkdv": 1}
-    assert PR.auto_layout([0, 0], [5, 5]) == {"fwd": 1, "dq": 1, "dkdv": 1}
-    assert PR.tile_sizes("fwd", 2) == (64, 32) and PR.tile_sizes("dkdv", 1) == (32, 32)
+    # d = 128: two-wave forward teams from a mean query length of 48, one block per wave
+    assert PR.auto_layout([32] * 8, [1000] * 8, 0, 128) == {"fwd": (1, 1), "dq": (1, 1), "dkdv": (1, 1)}
+    assert PR.auto_layout([300] * 8, [32] * 8, 0, 128) == {"fwd": (2, 1), "dq": (1, 1), "dkdv": (1, 1)}
+    assert PR.auto_layout([47, 49, 0], [5] * 3, 0, 128)["fwd"] == (2, 1)
+    assert PR.auto_layout([47, 48, 0], [5] * 3, 0, 128)["fwd"] == (1, 1)
+    # d <= 64: one-wave teams, two forward blocks from a mean query length of 64
+    assert PR.auto_layout([63, 65, 0], [70] * 3, 0, 64) == {"fwd": (1, 2), "dq": (1, 1), "dkdv": (1, 1)}
+    assert PR.auto_layout([63, 64, 0], [70] * 3, 0, 32) == {"fwd": (1, 1), "dq": (1, 1), "dkdv": (1, 1)}
+    assert PR.auto_layout([0, 0], [5, 5], 0, 128) == {"fwd": (1, 1), "dq": (1, 1), "dkdv": (1, 1)}
+    assert PR.tile_sizes("fwd", 2, 1) == (64, 32) and PR.tile_sizes("dkdv", 1, 1) == (32, 32)
 
 
 def test_export_layout():
-    pl = PR.plan_list("fwd", [70, 0, 5], [3, 9, 0], 2, 0, 4, 2)
+    pl = PR.plan_list("fwd", [70, 0, 5], [3, 9, 0], 2, 0, 4, 1, 2)
     ex = PR.export(pl)
     P, n = ex[0], ex[1]
     assert P == 4 and n == len(pl["items"])
-    assert ex[2:5] == [64, 32, 2]
-    assert ex[5:5 + P + 1] == pl["bin_ptr"]
-    assert len(ex) == 5 + P + 1 + 5 * n
+    assert ex[2:6] == [64, 32, 1, 2]
+    assert ex[6:6 + P + 1] == pl["bin_ptr"]
+    assert len(ex) == 6 + P + 1 + 5 * n
