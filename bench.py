@@ -39,7 +39,8 @@ def kernel_bytes(H, d, Tq, Tk):
     e = 2 * H * d
     return {"fwd": e * (2 * Tq + 2 * Tk),          # Q, K, V -> O
             "dkdv": e * (2 * Tq + 4 * Tk),         # Q, dO, K, V -> dK, dV
-            "dq": e * (3 * Tq + 2 * Tk)}           # Q, dO, K, V -> dQ
+            "dq": e * (3 * Tq + 2 * Tk),           # Q, dO, K, V -> dQ
+            "bwd": e * (3 * Tq + 4 * Tk)}          # one-pass backward: Q, dO, K, V -> dQ, dK, dV
 
 
 KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "kernels.hpp", "plan.cpp",
@@ -172,7 +173,12 @@ def main(argv=None):
     def dqk():
         G.gdpa_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, dq, sh)
 
-    calls = [("fwd", fwd), ("dkdv", dkdv), ("dq", dqk)]
+    def bwd():
+        G.gdpa_bwd(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, dq, dk, dv, sh)
+
+    # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels
+    fused = st["bwd_fused"]
+    calls = [("fwd", fwd), ("bwd", bwd)] if fused else [("fwd", fwd), ("dkdv", dkdv), ("dq", dqk)]
     for _ in range(args.warmup):
         for _, c in calls:
             c()
@@ -204,7 +210,7 @@ def main(argv=None):
     kernels = {n: {"ms": round(kms[n], 4), "alg_GBps": round(kb[n] / (kms[n] * 1e-3) / 1e9, 1)}
                for n in kms}
     kernels["fwd"]["useful_TFLOPs"] = round(4.0 * H * d * pairs / (kms["fwd"] * 1e-3) / 1e12, 2)
-    bwd_ms = kms["dkdv"] + kms["dq"]
+    bwd_ms = kms["bwd"] if fused else kms["dkdv"] + kms["dq"]
 
     out = {
         "metric": METRIC,
@@ -219,8 +225,9 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
-        "config": {"workload": f"{w['name']} (configs[{args.config - 1}])", "B": B, "H": H, "d": d,
-                   "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs},
+        "config": {"workload": w["name"], "B": B, "H": H, "d": d,
+                   "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs,
+                   "backward": ["dK/dV + dQ kernels", "one KV-stationary pass", "one Q-stationary pass"][fused]},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_useful_TFLOPs": kernels["fwd"]["useful_TFLOPs"],
         "bwd_useful_TFLOPs": round(10.0 * H * d * pairs / (bwd_ms * 1e-3) / 1e12, 2),

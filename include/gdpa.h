@@ -94,6 +94,7 @@ typedef struct {
                         and two-wave teams: 1).  An item holds 32 * team * blocks
                         stationary rows */
     int round_robin; /* 1: deal sorted items round robin instead of zigzag (ablation) */
+    int unfused;     /* 1: gdpa_bwd always runs the two backward kernels (see gdpa_bwd) */
 } gdpa_plan_opts;
 
 /* Summary numbers of a plan. */
@@ -107,6 +108,8 @@ typedef struct {
     int32_t tile_strm[3];    /* streaming tile rows per list */
     int64_t bin_cost_max[3]; /* per-bin cost extremes (planner cost units) */
     int64_t bin_cost_min[3];
+    int32_t bwd_fused;       /* what gdpa_bwd runs: 0 the two kernels, 1 one KV-stationary
+                                pass (every Lk <= 32), 2 one Q-stationary pass (every Lq <= 32) */
 } gdpa_plan_stats_t;
 
 typedef struct gdpa_plan_s* gdpa_plan;
@@ -159,7 +162,11 @@ gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v
  * dQ = dS K / sqrt(d).  S is recomputed; O is not needed.  Arguments as for
  * gdpa_fwd plus dout [Tq,H,d] (input) and dq, dk, dv (outputs, fully written;
  * rows with no valid partner are 0).  act = GDPA_ACT_ONE is rejected
- * (UNSUPPORTED).  Enqueues up to two kernels on `stream`.
+ * (UNSUPPORTED).  Enqueues up to two kernels on `stream`: one KV-stationary pass
+ * when every sample has at most 32 keys (and no sample has queries but no keys),
+ * else one Q-stationary pass when every sample has at most 32 queries (and none
+ * has keys but no queries), else a KV-stationary dK/dV kernel and a
+ * Q-stationary dQ kernel (always, with opts->unfused).
  */
 gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
                      const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,

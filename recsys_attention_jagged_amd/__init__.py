@@ -36,7 +36,7 @@ class GdpaError(RuntimeError):
 
 class gdpa_plan_opts(ctypes.Structure):
     _fields_ = [("host_only", ctypes.c_int), ("bins", ctypes.c_int * 3), ("team", ctypes.c_int * 3),
-                ("blocks", ctypes.c_int * 3), ("round_robin", ctypes.c_int)]
+                ("blocks", ctypes.c_int * 3), ("round_robin", ctypes.c_int), ("unfused", ctypes.c_int)]
 
 
 class gdpa_plan_stats_t(ctypes.Structure):
@@ -44,7 +44,7 @@ class gdpa_plan_stats_t(ctypes.Structure):
                 ("n_items", ctypes.c_int32 * 3), ("n_steps", ctypes.c_int32 * 3),
                 ("bins", ctypes.c_int32 * 3), ("tile_stat", ctypes.c_int32 * 3),
                 ("tile_strm", ctypes.c_int32 * 3), ("bin_cost_max", ctypes.c_int64 * 3),
-                ("bin_cost_min", ctypes.c_int64 * 3)]
+                ("bin_cost_min", ctypes.c_int64 * 3), ("bwd_fused", ctypes.c_int32)]
 
 
 _lib = None
@@ -121,14 +121,14 @@ def _enum(v, table):
 
 def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: int, dtype,
                      host_only: bool = False, bins=(0, 0, 0), team=(0, 0, 0), blocks=(0, 0, 0),
-                     round_robin: bool = False) -> int:
+                     round_robin: bool = False, unfused: bool = False) -> int:
     """Returns an opaque plan handle (int).  Offsets: host int32 [B + 1]."""
     qo = np.ascontiguousarray(q_off_host, dtype=np.int32)
     ko = np.ascontiguousarray(kv_off_host, dtype=np.int32)
     if qo.shape != (B + 1,) or ko.shape != (B + 1,):
         raise ValueError("offsets must have B + 1 entries")
     opts = gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*team),
-                          (ctypes.c_int * 3)(*blocks), int(round_robin))
+                          (ctypes.c_int * 3)(*blocks), int(round_robin), int(unfused))
     out = _vp()
     _check(load_library().gdpa_plan_create(qo.ctypes.data, ko.ctypes.data, B, H, d, window,
                                            _enum(dtype, DTYPE), ctypes.byref(opts), ctypes.byref(out)))

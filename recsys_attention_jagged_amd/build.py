@@ -39,6 +39,7 @@ UNITS = [("plan.o", "plan.cpp", []),
 for _d in (32, 64, 128):
     UNITS.append((f"fwd_d{_d}.o", "fwd_bf16.hip", [f"-DGDPA_D={_d}"]))
     UNITS.append((f"bwd_d{_d}.o", "bwd_bf16.hip", [f"-DGDPA_D={_d}"]))
+    UNITS.append((f"fused_d{_d}.o", "bwd_fused.hip", [f"-DGDPA_D={_d}"]))
 
 
 def _compile(unit, verbose):

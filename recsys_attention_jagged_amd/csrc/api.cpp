@@ -78,6 +78,7 @@ struct gdpa_plan_s {
     std::vector<int32_t> q_off, kv_off;
     std::vector<int64_t> lq, lk;
     int64_t Tq = 0, Tk = 0, valid_pairs = 0;
+    int fused = 0;   // gdpa_bwd: 0 two kernels, 1 one KV-stationary pass, 2 one Q-stationary pass
     WorkList lists[3];
     DevRec* d_items[3] = {nullptr, nullptr, nullptr};
     int32_t* d_bin_ptr[3] = {nullptr, nullptr, nullptr};
@@ -206,6 +207,18 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
         p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.round_robin == 0);
     }
 
+    // one-pass backward: one side of every sample fits one 32-row tile, and no
+    // sample has rows on that side only (their outputs would have no item)
+    if (dtype != GDPA_F32 && o.unfused == 0) {
+        bool kv_ok = L.team[LIST_DKDV] == 1 && L.nb[LIST_DKDV] == 1;
+        bool q_ok = L.team[LIST_DQ] == 1 && L.nb[LIST_DQ] == 1;
+        for (int b = 0; b < B; ++b) {
+            kv_ok = kv_ok && lk[b] <= 32 && (lk[b] > 0 || lq[b] == 0);
+            q_ok = q_ok && lq[b] <= 32 && (lq[b] > 0 || lk[b] == 0);
+        }
+        p->fused = kv_ok ? 1 : q_ok ? 2 : 0;
+    }
+
     if (!p->host_only) {
         for (int l = 0; l < 3; ++l) {
             const WorkList& wl = p->lists[l];
@@ -268,6 +281,7 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
             out->bin_cost_min[l] = *std::min_element(wl.bin_cost.begin(), wl.bin_cost.end());
         }
     }
+    out->bwd_fused = plan->fused;
     return GDPA_OK;
 }
 
@@ -362,6 +376,18 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
     hipError_t e = hipSuccess;
     if (plan->dtype == GDPA_F32) {
         e = launch_bwd_f32(a, want_dq ? (int)plan->Tq : 0, want_dkdv ? (int)plan->Tk : 0, d, act, s);
+    } else if (plan->fused && want_dkdv && want_dq) {
+        const int l = plan->fused == 1 ? LIST_DKDV : LIST_DQ;
+        KernelArgs b = a;
+        b.items = plan->d_items[l];
+        b.bin_ptr = plan->d_bin_ptr[l];
+        b.P = plan->lists[l].P;
+        const int kv = plan->fused == 1;
+        switch (d) {
+            case 32: e = launch_bwd_fused_d32(b, kv, act, s); break;
+            case 64: e = launch_bwd_fused_d64(b, kv, act, s); break;
+            default: e = launch_bwd_fused_d128(b, kv, act, s); break;
+        }
     } else {
         if (want_dkdv && any_k) {
             const WorkList& wl = plan->lists[LIST_DKDV];

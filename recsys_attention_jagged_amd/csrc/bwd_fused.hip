@@ -1,0 +1,370 @@
+// GDPA backward in one pass for the two shapes where one side of every sample
+// fits one 32-row tile (compiled once per D with -DGDPA_D=32|64|128):
+//
+//   * user-ad cross-attention (every Lk <= 32): the KV-stationary pass already
+//     visits all keys of a query tile in one step, so dQ of that tile is complete
+//     there: dQ = dS K / sqrt(d) is formed and stored per step, next to the dK and
+//     dV accumulation;
+//   * PMA (every Lq <= 32): the Q-stationary pass visits all queries of a key tile
+//     in one step, so dK = dS^T Q / sqrt(d) and dV = P^T dO of that tile are
+//     formed and stored per step, next to the dQ accumulation.
+//
+// Either way the second kernel, and its full pass over the long side, goes away
+// (GDPA page, aitrends.kr/articles/26275, "Section details": backward without the
+// softmax row statistics; S is recomputed).  The products that need the other
+// orientation of P or dS take it through a 32 x 32 bf16 scratch tile in LDS
+// (stage_transpose32), in the slot of a streamed tile the step has finished with;
+// the stationary operands of those products (K^T, or Q^T and dO^T) are read into
+// registers once per item.  Rows beyond a sample's lengths are zero tiles, so only
+// the local window needs a mask.
+#include "bwd_common.hpp"
+
+#ifndef GDPA_D
+#error "compile with -DGDPA_D=<32|64|128>"
+#endif
+
+namespace gdpa {
+namespace {
+
+// =========================================================================
+// KV-stationary: dK, dV accumulated, dQ stored per step (every Lk <= 32)
+// =========================================================================
+template <int D, int ACT>
+struct KvFusedPol : Common {
+    static constexpr int NSTAT = 2, NSTRM = 2;   // (K, V), then (Q, dO) per step
+    static constexpr int NDB = D / 32, NKS = D / 16;
+    static constexpr bool HOIST = TeamShape<D, 1, 2>::HOIST;
+    rsrc_t wk, wv, wq, wo;   // issuing side
+    bf16x8 kf[NKS], vf[NKS], kt[2][NDB];
+    f32x16 accK[NDB], accV[NDB];
+
+    __device__ KvFusedPol(const KernelArgs& args, int lane_) : Common(args, lane_, 0, D) {}
+
+    __device__ __forceinline__ void walk_item(const Rec& w) {
+        const size_t kvb = ((size_t)w.ks * H + w.h) * D;
+        wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+        wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        const size_t qb = ((size_t)w.qs * H + w.h) * D;
+        wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
+        wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
+        if (i < NSTAT) {
+            g.issue(i == 0 ? wk : wv, (uint32_t)(w.t * 32) * rs);
+        } else {
+            const int rel = i - NSTAT;
+            g.issue((rel & 1) ? wo : wq, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
+        }
+    }
+
+    __device__ __forceinline__ void item_begin(const Rec&) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) accK[db] = accV[db] = f32x16{};
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job, int) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            kf[ks] = lds_row8<D>(g.tile(job), r, 2 * ks + hh);
+            vf[ks] = lds_row8<D>(g.tile(job + 1), r, 2 * ks + hh);
+        }
+        // K^T, the A operand of dQ^T = K^T dS^T
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) kt[m][db] = lds_col8<D>(g.tile(job), 16 * m, db * 32, lane);
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
+        char* qt = g.tile(job);
+        char* ot = g.tile(job + 1);
+        bf16x8 qop[NKS], oop[NKS];
+        if constexpr (HOIST) {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                qop[ks] = lds_row8<D>(qt, r, 2 * ks + hh);
+                oop[ks] = lds_row8<D>(ot, r, 2 * ks + hh);
+            }
+        }
+        f32x16 sc = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            sc = mfma32(HOIST ? qop[ks] : lds_row8<D>(qt, r, 2 * ks + hh), kf[ks], sc);
+            dp = mfma32(HOIST ? oop[ks] : lds_row8<D>(ot, r, 2 * ks + hh), vf[ks], dp);
+        }
+        // accumulator lane: column = key j0 + r, element e: query i0 + 8 (e/4) + 4 hh + e % 4
+        const int i0 = s * 32, j0 = c.t * 32;
+        const bool masked = win > 0 && !band_all(i0, j0, win);
+        const int base = i0 + 4 * hh - j0 - r;
+        bf16x8 pm[2], dm[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) {
+                const int e = 8 * m + e8;
+                float f, gr;
+                act_fwd_grad<ACT>(sc[e] * scale, f, gr);
+                float ds = dp[e] * gr;
+                if (masked) {
+                    const int dd = base + 8 * (e >> 2) + (e & 3);
+                    const bool ok = dd < win && -dd < win;
+                    f = ok ? f : 0.0f;
+                    ds = ok ? ds : 0.0f;
+                }
+                pm[m][e8] = (__bf16)f;
+                dm[m][e8] = (__bf16)ds;
+            }
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                accV[db] = mfma32(lds_col8<D>(ot, 16 * m, db * 32, lane), pm[m], accV[db]);
+                accK[db] = mfma32(lds_col8<D>(qt, 16 * m, db * 32, lane), dm[m], accK[db]);
+            }
+        // dQ^T = K^T dS^T for this query tile: dS^T through a scratch tile in the dO
+        // slot (the products above have read it), dQ staged in the Q slot
+        stage_transpose32(dm, ot, r, hh);
+        bf16x8 dst[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) dst[m] = lds_col8<32>(ot, 16 * m, 0, lane);
+        f32x16 dq[NDB];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            dq[db] = mfma32(kt[0][db], dst[0], f32x16{});
+            dq[db] = mfma32(kt[1][db], dst[1], dq[db]);
+        }
+        const size_t qb = ((size_t)c.qs * H + c.h) * D;
+        store<D>(dq, scale, a.dq, qb, c.lq, i0, qt);
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        const size_t ob = ((size_t)c.ks * H + c.h) * D;
+        store<D>(accK, scale, a.dk, ob, c.lk, c.t * 32, g.tile(job - 2));
+        store<D>(accV, 1.0f, a.dv, ob, c.lk, c.t * 32, g.tile(job - 1));
+    }
+
+    // no queries: dK and dV are zero (the sample has no dQ rows)
+    __device__ __forceinline__ void item_zero(const Rec& c) {
+        const size_t ob = ((size_t)c.ks * H + c.h) * D;
+        zero<D>(a.dk, ob, c.lk, c.t * 32);
+        zero<D>(a.dv, ob, c.lk, c.t * 32);
+    }
+};
+
+// =========================================================================
+// Q-stationary: dQ accumulated, dK and dV stored per step (every Lq <= 32)
+// =========================================================================
+template <int D, int ACT>
+struct QFusedPol : Common {
+    static constexpr int NSTAT = 2, NSTRM = 2;   // (Q, dO), then (K, V) per step
+    static constexpr int NDB = D / 32, NKS = D / 16;
+    static constexpr bool HOIST = TeamShape<D, 1, 2>::HOIST;
+    rsrc_t wq, wo, wk, wv;   // issuing side
+    bf16x8 qf[NKS], of[NKS], qt[2][NDB], ot[2][NDB];
+    f32x16 acc[NDB];
+
+    __device__ QFusedPol(const KernelArgs& args, int lane_) : Common(args, lane_, 0, D) {}
+
+    __device__ __forceinline__ void walk_item(const Rec& w) {
+        const size_t kvb = ((size_t)w.ks * H + w.h) * D;
+        wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+        wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        const size_t qb = ((size_t)w.qs * H + w.h) * D;
+        wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
+        wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
+        if (i < NSTAT) {
+            g.issue(i == 0 ? wq : wo, (uint32_t)(w.t * 32) * rs);
+        } else {
+            const int rel = i - NSTAT;
+            g.issue((rel & 1) ? wv : wk, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
+        }
+    }
+
+    __device__ __forceinline__ void item_begin(const Rec&) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job, int) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            qf[ks] = lds_row8<D>(g.tile(job), r, 2 * ks + hh);
+            of[ks] = lds_row8<D>(g.tile(job + 1), r, 2 * ks + hh);
+        }
+        // Q^T and dO^T, the A operands of dK^T = Q^T dS and dV^T = dO^T P
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                qt[m][db] = lds_col8<D>(g.tile(job), 16 * m, db * 32, lane);
+                ot[m][db] = lds_col8<D>(g.tile(job + 1), 16 * m, db * 32, lane);
+            }
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
+        char* kt = g.tile(job);
+        char* vt = g.tile(job + 1);
+        f32x16 sc = {}, dp = {};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            sc = mfma32(lds_row8<D>(kt, r, 2 * ks + hh), qf[ks], sc);
+            dp = mfma32(lds_row8<D>(vt, r, 2 * ks + hh), of[ks], dp);
+        }
+        // accumulator lane: column = query q0 + r, element e: key j0 + 8 (e/4) + 4 hh + e % 4
+        const int q0 = c.t * 32, j0 = s * 32;
+        const bool masked = win > 0 && !band_all(q0, j0, win);
+        const int base = q0 + r - j0 - 4 * hh;
+        bf16x8 pm[2], dm[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e8 = 0; e8 < 8; ++e8) {
+                const int e = 8 * m + e8;
+                float f, gr;
+                act_fwd_grad<ACT>(sc[e] * scale, f, gr);
+                float ds = dp[e] * gr;
+                if (masked) {
+                    const int dd = base - (8 * (e >> 2) + (e & 3));
+                    const bool ok = dd < win && -dd < win;
+                    f = ok ? f : 0.0f;
+                    ds = ok ? ds : 0.0f;
+                }
+                pm[m][e8] = (__bf16)f;
+                dm[m][e8] = (__bf16)ds;
+            }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = mfma32(lds_col8<D>(kt, 16 * m, db * 32, lane), dm[m], acc[db]);
+        // dK^T = Q^T dS and dV^T = dO^T P for this key tile: dS and P through
+        // 32 x 32 scratch tiles at the start of the V and K slots (every read of
+        // those tiles above is done; a d = 32 slot holds exactly one), then dK
+        // staged in the K slot and dV in the V slot once the scratch is read
+        char* sds = vt;
+        char* sp = kt;
+        stage_transpose32(dm, sds, r, hh);
+        stage_transpose32(pm, sp, r, hh);
+        bf16x8 dsk[2], pk[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            dsk[m] = lds_col8<32>(sds, 16 * m, 0, lane);
+            pk[m] = lds_col8<32>(sp, 16 * m, 0, lane);
+        }
+        const size_t kvb = ((size_t)c.ks * H + c.h) * D;
+        if (a.out_f32) {
+            f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                dk[db] = mfma32(qt[1][db], dsk[1], mfma32(qt[0][db], dsk[0], f32x16{}));
+                dv[db] = mfma32(ot[1][db], pk[1], mfma32(ot[0][db], pk[0], f32x16{}));
+            }
+            store<D>(dk, scale, a.dk, kvb, c.lk, j0, kt);
+            store<D>(dv, 1.0f, a.dv, kvb, c.lk, j0, vt);
+            return;
+        }
+        // one 32-column part at a time keeps the per-step accumulators small
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const f32x16 dk = mfma32(qt[1][db], dsk[1], mfma32(qt[0][db], dsk[0], f32x16{}));
+            stage_part<D>(dk, db, scale, kt, r, hh);
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const f32x16 dv = mfma32(ot[1][db], pk[1], mfma32(ot[0][db], pk[0], f32x16{}));
+            stage_part<D>(dv, db, 1.0f, vt, r, hh);
+        }
+        store_tile<D>(kt, slice_rsrc((const __bf16*)a.dk + kvb, c.lk, rso, D * 2), (uint32_t)j0 * rso, rso, lane);
+        store_tile<D>(vt, slice_rsrc((const __bf16*)a.dv + kvb, c.lk, rso, D * 2), (uint32_t)j0 * rso, rso, lane);
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        const size_t ob = ((size_t)c.qs * H + c.h) * D;
+        store<D>(acc, scale, a.dq, ob, c.lq, c.t * 32, g.tile(job - 2));
+    }
+
+    // no keys: dQ is zero (the sample has no dK, dV rows)
+    __device__ __forceinline__ void item_zero(const Rec& c) {
+        const size_t ob = ((size_t)c.qs * H + c.h) * D;
+        zero<D>(a.dq, ob, c.lq, c.t * 32);
+    }
+};
+
+template <class Pol>
+__device__ __forceinline__ void fused_body(const KernelArgs& a, const Rec* __restrict__ recs,
+                                           const int32_t* __restrict__ bin_ptr, char* smem, int D) {
+    using RingT = Ring<GDPA_D, 1, TeamShape<GDPA_D, 1, 2>::LDS>;
+    const int lane = threadIdx.x & 63;
+    Pol pol(a, lane);
+    run_team<Pol, RingT, 1>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, 0, lane);
+}
+
+template <int D, int ACT>
+__global__ __launch_bounds__((TeamShape<D, 1, 2>::THREADS), (TeamShape<D, 1, 2>::WPE)) void kv_fused_kernel(
+    const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
+    __shared__ __attribute__((aligned(1024))) char smem[Ring<D, 1, TeamShape<D, 1, 2>::LDS>::BYTES];
+    fused_body<KvFusedPol<D, ACT>>(a, recs, bin_ptr, smem, D);
+}
+
+template <int D, int ACT>
+__global__ __launch_bounds__((TeamShape<D, 1, 2>::THREADS), (TeamShape<D, 1, 2>::WPE)) void q_fused_kernel(
+    const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
+    __shared__ __attribute__((aligned(1024))) char smem[Ring<D, 1, TeamShape<D, 1, 2>::LDS>::BYTES];
+    fused_body<QFusedPol<D, ACT>>(a, recs, bin_ptr, smem, D);
+}
+
+template <int ACT>
+const void* kv_ptr() {
+    return (const void*)&kv_fused_kernel<GDPA_D, ACT>;
+}
+template <int ACT>
+const void* q_ptr() {
+    return (const void*)&q_fused_kernel<GDPA_D, ACT>;
+}
+
+#define GDPA_FUSED_SWITCH(F)                                  \
+    switch (act) {                                            \
+        case ACT_GELU: return F<ACT_GELU>();                  \
+        case ACT_SILU: return F<ACT_SILU>();                  \
+        case ACT_GELU_POLY: return F<ACT_GELU_POLY>();        \
+        case ACT_GELU_TAYLOR6: return F<ACT_GELU_TAYLOR6>();  \
+        case ACT_IDENTITY: return F<ACT_IDENTITY>();          \
+    }                                                         \
+    return nullptr;
+
+}  // namespace
+
+#define GDPA_CAT2(a, b) a##b
+#define GDPA_CAT(a, b) GDPA_CAT2(a, b)
+
+const void* GDPA_CAT(bwd_fused_kernel_ptr_d, GDPA_D)(int kv_stationary, int act) {
+    if (kv_stationary) {
+        GDPA_FUSED_SWITCH(kv_ptr)
+    }
+    GDPA_FUSED_SWITCH(q_ptr)
+}
+
+hipError_t GDPA_CAT(launch_bwd_fused_d, GDPA_D)(const KernelArgs& a, int kv_stationary, int act, hipStream_t s) {
+    const void* f = GDPA_CAT(bwd_fused_kernel_ptr_d, GDPA_D)(kv_stationary, act);
+    if (!f) return hipErrorInvalidValue;
+    if (a.P <= 0) return hipSuccess;
+    KernelArgs args = a;
+    const void* recs = a.items;
+    const int32_t* bin_ptr = a.bin_ptr;
+    void* params[] = {&args, &recs, &bin_ptr};
+    return hipLaunchKernel(f, dim3(a.P), dim3(64), params, 0, s);
+}
+
+}  // namespace gdpa

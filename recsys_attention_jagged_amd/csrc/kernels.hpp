@@ -47,6 +47,17 @@ GDPA_DECLARE_LAUNCHERS(64)
 GDPA_DECLARE_LAUNCHERS(128)
 #undef GDPA_DECLARE_LAUNCHERS
 
+// One-pass backward (one-wave teams, one block per wave): kv_stationary = 1 runs
+// over the dK/dV list when every Lk <= 32 (dQ stored per step), 0 over the dQ
+// list when every Lq <= 32 (dK, dV stored per step).
+#define GDPA_DECLARE_FUSED(D)                                                                         \
+    hipError_t launch_bwd_fused_d##D(const KernelArgs& a, int kv_stationary, int act, hipStream_t s);   \
+    const void* bwd_fused_kernel_ptr_d##D(int kv_stationary, int act);
+GDPA_DECLARE_FUSED(32)
+GDPA_DECLARE_FUSED(64)
+GDPA_DECLARE_FUSED(128)
+#undef GDPA_DECLARE_FUSED
+
 // plain fp32 kernels (no MFMA): forward, dQ, dK/dV over the offsets directly
 hipError_t launch_fwd_f32(const KernelArgs& a, int Tq, int d, int act, hipStream_t s);
 hipError_t launch_bwd_f32(const KernelArgs& a, int Tq, int Tk, int d, int act, hipStream_t s);

@@ -221,6 +221,34 @@ __device__ __forceinline__ void stage_block(const f32x16 (&acc)[D / 32], float m
         }
 }
 
+// One 32-column part (db) of stage_block.
+template <int D>
+__device__ __forceinline__ void stage_part(const f32x16& acc, int db, float mul, char* tile, int r, int hh) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[4 * j] * mul, acc[4 * j + 1] * mul);
+        w[1] = pack_bf16x2(acc[4 * j + 2] * mul, acc[4 * j + 3] * mul);
+        *(u32x2*)(tile + tile_off<D>(r, 4 * db + j) + 8 * hh) = w;
+    }
+}
+
+// Write a 32 x 32 block held as two bf16x8 halves of an accumulator (lane (r, hh)
+// holds column r and rows 8 j + 4 hh + i, element 8 m + 4 (j % 2) + i of half m
+// = j / 2) into a swizzled 32 x 32 scratch tile as rows r (row r, columns
+// 8 j + 4 hh + i): reading it back with lds_col8<32>(tile, 16 m, 0, lane) then
+// gives lane l the values of rows 16 m + {0..3, 8..11} + 4 (l / 32) of column
+// l % 32 of the block, i.e. the block's transpose in the chained operand layout.
+__device__ __forceinline__ void stage_transpose32(const bf16x8 (&half)[2], char* tile, int r, int hh) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bf16x8& h = half[j >> 1];
+        const int o = 4 * (j & 1);
+        const bf16x4 v = {h[o], h[o + 1], h[o + 2], h[o + 3]};
+        *(bf16x4*)(tile + tile_off<32>(r, j) + 8 * hh) = v;
+    }
+}
+
 // Store a staged 32 x D bf16 tile as rows row0 .. row0 + 31 of the slice `ro`
 // (row_off0 = row0 * rso): each instruction writes whole rows, 16 bytes per lane.
 template <int D>

@@ -104,6 +104,31 @@ def test_plan_stats_valid_pairs_and_balance():
         G.gdpa_plan_destroy(plan)
 
 
+def test_plan_picks_one_pass_backward():
+    """gdpa_bwd's kernel choice: one KV-stationary pass when every Lk <= 32, one
+    Q-stationary pass when every Lq <= 32, else two kernels (never with unfused)."""
+    def mode(lq, lk, window=0, **kw):
+        p = G.gdpa_plan_create(offsets(lq), offsets(lk), len(lq), 2, 64, window, "bf16", host_only=True, **kw)
+        try:
+            return G.gdpa_plan_stats(p)["bwd_fused"]
+        finally:
+            G.gdpa_plan_destroy(p)
+    assert mode([300, 5, 0], [32, 1, 0]) == 1
+    assert mode([300, 5, 7], [32, 1, 0]) == 0          # queries without keys: dQ rows would have no item
+    assert mode([32, 1, 0], [900, 5, 0]) == 2
+    assert mode([32, 0, 1], [900, 5, 3]) == 0          # keys without queries
+    assert mode([32, 33], [900, 5]) == 0
+    assert mode([20, 32], [20, 32], window=4) == 1
+    assert mode([300, 5], [32, 1], unfused=True) == 0
+    assert mode([300, 5], [32, 1], blocks=(0, 0, 0), team=(0, 0, 0)) == 1
+    lq, lk = workload_lengths(3)
+    assert mode(list(lq), list(lk)) == 1
+    lq, lk = workload_lengths(4)
+    assert mode(list(lq), list(lk)) == 2
+    lq, lk = workload_lengths(2)
+    assert mode(list(lq), list(lk)) == 0
+
+
 # ---------------------------------------------------------------------------
 # error paths (forced from the host)
 # ---------------------------------------------------------------------------

@@ -171,6 +171,39 @@ def test_few_bins_long_walks(bins):
         check_close(a, b, f"{name} bins={bins}")
 
 
+# one-pass backward shapes: every Lk <= 32 (KV-stationary) or every Lq <= 32 (Q-stationary)
+FUSED_CASES = [
+    ([300, 5, 0, 77, 1, 64, 129], [32, 1, 0, 17, 32, 31, 2], 0),
+    ([32, 1, 0, 17, 32, 31, 2], [300, 5, 0, 77, 1, 64, 129], 0),
+    ([32, 1, 20, 0, 31], [32, 1, 20, 0, 31], 5),
+]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("case", range(len(FUSED_CASES)))
+@pytest.mark.parametrize("unfused", [False, True])
+def test_one_pass_backward(d, case, unfused):
+    lq, lk, window = FUSED_CASES[case]
+    say(f"one-pass backward d={d} case={case} unfused={unfused}")
+    inp = make_from_lengths(lq, lk, 3, d, act="gelu", window=window, seed=13 + case, device=DEV)
+    with G.Plan(inp.q_off, inp.kv_off, 3, d, window, "bf16", unfused=unfused) as plan:
+        assert plan.stats()["bwd_fused"] == (0 if unfused else (1 if case != 1 else 2))
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, unfused=unfused), oracle_bwd(inp)):
+        check_close(a, b, f"{name} d={d} case={case} unfused={unfused}")
+    # fp32 outputs through the same kernels
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, dtype="bf16_f32out", unfused=unfused), oracle_bwd(inp)):
+        check_close(a, b, f"{name} f32out d={d} case={case}")
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu", "gelu_taylor6", "identity"])
+def test_one_pass_backward_activations(act):
+    say(f"one-pass backward activation {act}")
+    for lq, lk in (([130, 7, 64], [32, 9, 30]), ([32, 9, 30], [130, 7, 64])):
+        inp = make_from_lengths(lq, lk, 2, 64, act=act, seed=17, device=DEV)
+        for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp), oracle_bwd(inp)):
+            check_close(a, b, f"{name} {act}")
+
+
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_taylor6", "identity"])
 def test_activations_forward_backward(act):
     say(f"activation {act}")
