@@ -43,8 +43,8 @@ def kernel_bytes(H, d, Tq, Tk):
             "bwd": e * (3 * Tq + 4 * Tk)}          # one-pass backward: Q, dO, K, V -> dQ, dK, dV
 
 
-KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "kernels.hpp", "plan.cpp",
-                  "plan.hpp", "gelu_poly.h")
+KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd_common.hpp", "bwd_fused.hip",
+                  "kernels.hpp", "plan.cpp", "plan.hpp", "api.cpp", "gelu_poly.h")
 
 
 def kernel_source_digest() -> str:
