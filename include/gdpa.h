@@ -93,7 +93,9 @@ typedef struct {
     int blocks[3];   /* 32-row stationary blocks per wave: 0 = automatic, 1 or 2 (dK/dV
                         and two-wave teams: 1).  An item holds 32 * team * blocks
                         stationary rows */
-    int round_robin; /* 1: deal sorted items round robin instead of zigzag (ablation) */
+    int deal;        /* how sorted items go to bins: 0 greedy (each item to the bin of
+                        least cost so far), 1 zigzag (snake), 2 round robin */
+    int no_split;    /* 1: never cut an item into chunks (see gdpa_plan_create) */
     int unfused;     /* 1: gdpa_bwd always runs the two backward kernels (see gdpa_bwd) */
 } gdpa_plan_opts;
 
@@ -110,6 +112,8 @@ typedef struct {
     int64_t bin_cost_min[3];
     int32_t bwd_fused;       /* what gdpa_bwd runs: 0 the two kernels, 1 one KV-stationary
                                 pass (every Lk <= 32), 2 one Q-stationary pass (every Lq <= 32) */
+    int32_t n_parts[3];      /* partial-output slots per list (chunks of cut items; 0 for
+                                the dK/dV list) */
 } gdpa_plan_stats_t;
 
 typedef struct gdpa_plan_s* gdpa_plan;
@@ -117,7 +121,9 @@ typedef struct gdpa_plan_s* gdpa_plan;
 /*
  * gdpa_plan_create - enumerate the non-empty tiles on the host and deal them to
  * persistent workgroups (GDPA page, "Section details": the CPU precomputes the
- * valid tiles, sorts them and assigns them to processors in a zigzag order).
+ * valid tiles, sorts them and assigns them to processors in a zigzag order; here
+ * the sorted items go by default each to the least-loaded bin, which balances
+ * better than the fixed snake, and zigzag remains an option).
  *
  *   q_off_host, kv_off_host : host int32 [B + 1] offsets (read during the call only)
  *   B >= 0 samples, H >= 1 heads, d in {32, 64, 128}
@@ -127,7 +133,15 @@ typedef struct gdpa_plan_s* gdpa_plan;
  *   opts                    : NULL or planning options
  *   out                     : receives the plan (NULL on failure)
  *
- * Unless opts->host_only, uploads the work lists with hipMalloc / hipMemcpy on
+ * Items of the Q-stationary lists (forward, dQ) whose cost exceeds the mean
+ * per-bin cost are cut into chunks of consecutive streaming tiles (unless
+ * opts->no_split); each chunk stores an fp32 partial output block into the plan's
+ * slot buffer and a small reduction kernel, enqueued right after the main kernel,
+ * adds the chunks of each cut item in a fixed order (no atomics).  Calls that use
+ * one plan therefore must not overlap in time (e.g. on two streams).
+ *
+ * Unless opts->host_only, uploads the work lists and allocates the slot buffers
+ * (n_parts * tile_stat * d * 4 bytes per list) with hipMalloc / hipMemcpy on
  * the current device (synchronous).  Errors: INVALID_ARG, BAD_OFFSETS,
  * UNSUPPORTED, HIP, NOMEM.
  */
@@ -192,9 +206,10 @@ gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void
 /*
  * gdpa_plan_export - serialise one work list as int32 values:
  *   [P, n_items, tile_stat, tile_strm, team, blocks, bin_ptr[0..P], then per item in
- *    bin order (b, h, t, s0, s1)]
- * where t is the stationary tile and [s0, s1] the streaming tiles (s1 < s0: no
- * steps, the item writes zeros).  With buf == NULL, *n receives the length;
+ *    bin order (b, h, t, s0, s1, part)]
+ * where t is the stationary tile, [s0, s1] the streaming tiles (s1 < s0: no
+ * steps, the item writes zeros) and part the chunk's partial-output slot (-1 for
+ * an item that stores its outputs itself).  With buf == NULL, *n receives the length;
  * otherwise *n is the capacity of buf on entry and the length on return.
  * Errors: INVALID_ARG (bad list or capacity too small).
  */

@@ -17,9 +17,21 @@ Readings (the page gives no cost model or tie-break):
     KV-stationary list) have no steps (s0 = 0, s1 = -1) and only write zeros;
   * cost = (valid stationary rows) + sum over steps of (valid streaming rows + 32),
     i.e. rows moved through memory plus a fixed per-step charge;
-  * stable order: cost descending, then (b, h, t) ascending;
-  * zigzag (snake) deal over P bins: the r-th item goes to bin r mod P in even
-    rounds and to P - 1 - (r mod P) in odd rounds (round = r // P);
+  * chunks (Q-stationary lists only): with m = ceil(total cost / P), the mean bin
+    cost, an item with n >= 2 steps and cost > m is cut into
+    k = min(n, ceil(cost / ceil(m / 4))) chunks of consecutive steps (no bin could
+    hold it at the mean), chunk j holding steps s0 + floor(j n / k) ..
+    s0 + floor((j + 1) n / k) - 1 and costing its stationary rows plus its steps;
+    chunk j of the g-th cut item (in (b, h, t) order) writes partial-output slot
+    (chunks of earlier cut items) + j, and the item's output is the sum of its
+    slots.  The page deals tiles, not whole rows of tiles, so a long row of tiles
+    need not sit in one bin; the chunks keep that freedom without atomics;
+  * stable order: cost descending, then (b, h, t, s0) ascending;
+  * deal over P bins, by default greedy: each item, in sorted order, to the bin
+    of least cost so far (lowest index on ties) -- the sorted assignment the page
+    describes, taken to the least-loaded bin instead of a fixed snake; the page's
+    zigzag (the r-th item to bin r mod P in even rounds and P - 1 - (r mod P) in
+    odd rounds, round = r // P) and round robin are the alternatives;
   * per-bin CSR keeps each bin's items in deal order.
 
 Three lists are planned: "fwd" and "dq" (Q-stationary: t is a q tile, steps are
@@ -29,6 +41,8 @@ of 32 rows).  One team of waves processes one item; stationary tiles hold
 dimension and the length statistics.
 """
 from __future__ import annotations
+
+import heapq
 
 STEP_CHARGE = 32
 
@@ -85,34 +99,75 @@ def enumerate_items(kind: str, lq, lk, H: int, window: int, t_stat: int, t_strm:
     return items
 
 
-def deal(items, P: int, zigzag: bool = True):
+def split_items(kind: str, items, lq, lk, P: int, t_stat: int, t_strm: int):
+    """Cut the long items of a Q-stationary list into chunks.  Returns
+    ([(cost, b, h, t, s0, s1, part)], number of slots); part = -1 for whole items."""
+    out = []
+    if kind == "dkdv" or P <= 0:
+        return [it + (-1,) for it in items], 0
+    mean = max(1, _ceil_div(sum(it[0] for it in items), P))
+    piece = max(1, _ceil_div(mean, 4))
+    slot = 0
+    for cost, b, h, t, s0, s1 in items:
+        n = s1 - s0 + 1
+        if n < 2 or cost <= mean:
+            out.append((cost, b, h, t, s0, s1, -1))
+            continue
+        k = min(n, _ceil_div(cost, piece))
+        n_stat = min(int(lq[b]), (t + 1) * t_stat) - t * t_stat
+        lo_other = int(lk[b])
+        for j in range(k):
+            f, l = s0 + j * n // k, s0 + (j + 1) * n // k - 1
+            c = n_stat + sum(min(lo_other, (s + 1) * t_strm) - s * t_strm + STEP_CHARGE for s in range(f, l + 1))
+            out.append((c, b, h, t, f, l, slot + j))
+        slot += k
+    return out, slot
+
+
+DEALS = ("greedy", "zigzag", "round_robin")
+
+
+def deal(items, P: int, mode: str = "greedy"):
     """Sort and deal items to P bins.  Returns (bin_ptr, ordered items, bin_cost)."""
-    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[3]))
+    if mode not in DEALS:
+        raise ValueError(mode)
+    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[3], it[4]))
     bins = [[] for _ in range(P)]
+    cost = [0] * P
+    least = [(0, p) for p in range(P)]   # (cost so far, bin), a heap: least cost, then lowest bin
     for r, it in enumerate(order):
-        rnd, pos = divmod(r, P)
-        p = pos if (not zigzag or rnd % 2 == 0) else P - 1 - pos
+        if mode == "greedy":
+            _, p = heapq.heappop(least)
+            heapq.heappush(least, (cost[p] + it[0], p))
+        else:
+            rnd, pos = divmod(r, P)
+            p = pos if (mode == "round_robin" or rnd % 2 == 0) else P - 1 - pos
         bins[p].append(it)
+        cost[p] += it[0]
     bin_ptr = [0]
     flat = []
     for p in range(P):
         flat.extend(bins[p])
         bin_ptr.append(len(flat))
-    cost = [sum(it[0] for it in bins[p]) for p in range(P)]
     return bin_ptr, flat, cost
 
 
-def plan_list(kind: str, lq, lk, H: int, window: int, P: int, team: int, nb: int, zigzag: bool = True):
+def plan_list(kind: str, lq, lk, H: int, window: int, P: int, team: int, nb: int, mode: str = "greedy",
+              split: bool = True):
     t_stat, t_strm = tile_sizes(kind, team, nb)
     items = enumerate_items(kind, lq, lk, H, window, t_stat, t_strm)
-    bin_ptr, flat, cost = deal(items, P, zigzag)
+    if split:
+        items, n_parts = split_items(kind, items, lq, lk, P, t_stat, t_strm)
+    else:
+        items, n_parts = [it + (-1,) for it in items], 0
+    bin_ptr, flat, cost = deal(items, P, mode)
     return dict(kind=kind, P=P, t_stat=t_stat, t_strm=t_strm, team=team, nb=nb,
-                bin_ptr=bin_ptr, items=[it[1:] for it in flat], bin_cost=cost)
+                bin_ptr=bin_ptr, items=[it[1:] for it in flat], bin_cost=cost, n_parts=n_parts)
 
 
 def export(pl) -> list:
     """The int32 serialisation the library's plan export produces:
-    [P, n_items, t_stat, t_strm, team, nb, bin_ptr[0..P], then (b, h, t, s0, s1) per item]."""
+    [P, n_items, t_stat, t_strm, team, nb, bin_ptr[0..P], then (b, h, t, s0, s1, part) per item]."""
     out = [pl["P"], len(pl["items"]), pl["t_stat"], pl["t_strm"], pl["team"], pl["nb"]]
     out += list(pl["bin_ptr"])
     for it in pl["items"]:
@@ -120,10 +175,30 @@ def export(pl) -> list:
     return out
 
 
-def plan(lq, lk, H: int, window: int, P: int, d: int = 128, layout=None):
+def plan(lq, lk, H: int, window: int, P: int, d: int = 128, layout=None, mode: str = "greedy",
+         split: bool = True):
     """All three lists with the automatic (or given) layouts."""
     layout = layout or auto_layout(lq, lk, window, d)
-    return {kind: plan_list(kind, lq, lk, H, window, P, *layout[kind]) for kind in LISTS}
+    return {kind: plan_list(kind, lq, lk, H, window, P, *layout[kind], mode=mode, split=split) for kind in LISTS}
+
+
+def groups(pl, q_off):
+    """Cut items of a list in slot order: [(row0, rows, h, slot0, n)] where output
+    rows row0 .. row0 + rows - 1 (absolute) of head h are the sum of n slots."""
+    by_slot = {}
+    for b, h, t, s0, s1, part in pl["items"]:
+        if part >= 0:
+            by_slot[part] = (b, h, t)
+    out = []
+    for s in range(pl["n_parts"]):
+        b, h, t = by_slot[s]
+        if out and by_slot[s - 1] == (b, h, t):
+            out[-1][4] += 1
+            continue
+        lq = q_off[b + 1] - q_off[b]
+        ts = pl["t_stat"]
+        out.append([q_off[b] + t * ts, min(ts, lq - t * ts), h, s, 1])
+    return [tuple(g) for g in out]
 
 
 def imbalance(cost) -> float:

@@ -25,6 +25,7 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARG", 2: "GDPA_ERR_BAD_OFFSETS", 3:
 ACT = {"gelu": 0, "silu": 1, "gelu_poly": 2, "gelu_taylor6": 3, "identity": 4, "one": 5}
 DTYPE = {"f32": 0, "bf16": 1, "bf16_f32out": 2}
 LIST = {"fwd": 0, "dkdv": 1, "dq": 2}
+DEAL = {"greedy": 0, "zigzag": 1, "round_robin": 2}
 
 
 class GdpaError(RuntimeError):
@@ -36,7 +37,8 @@ class GdpaError(RuntimeError):
 
 class gdpa_plan_opts(ctypes.Structure):
     _fields_ = [("host_only", ctypes.c_int), ("bins", ctypes.c_int * 3), ("team", ctypes.c_int * 3),
-                ("blocks", ctypes.c_int * 3), ("round_robin", ctypes.c_int), ("unfused", ctypes.c_int)]
+                ("blocks", ctypes.c_int * 3), ("deal", ctypes.c_int), ("no_split", ctypes.c_int),
+                ("unfused", ctypes.c_int)]
 
 
 class gdpa_plan_stats_t(ctypes.Structure):
@@ -44,7 +46,8 @@ class gdpa_plan_stats_t(ctypes.Structure):
                 ("n_items", ctypes.c_int32 * 3), ("n_steps", ctypes.c_int32 * 3),
                 ("bins", ctypes.c_int32 * 3), ("tile_stat", ctypes.c_int32 * 3),
                 ("tile_strm", ctypes.c_int32 * 3), ("bin_cost_max", ctypes.c_int64 * 3),
-                ("bin_cost_min", ctypes.c_int64 * 3), ("bwd_fused", ctypes.c_int32)]
+                ("bin_cost_min", ctypes.c_int64 * 3), ("bwd_fused", ctypes.c_int32),
+                ("n_parts", ctypes.c_int32 * 3)]
 
 
 _lib = None
@@ -121,14 +124,14 @@ def _enum(v, table):
 
 def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: int, dtype,
                      host_only: bool = False, bins=(0, 0, 0), team=(0, 0, 0), blocks=(0, 0, 0),
-                     round_robin: bool = False, unfused: bool = False) -> int:
+                     deal="greedy", split: bool = True, unfused: bool = False) -> int:
     """Returns an opaque plan handle (int).  Offsets: host int32 [B + 1]."""
     qo = np.ascontiguousarray(q_off_host, dtype=np.int32)
     ko = np.ascontiguousarray(kv_off_host, dtype=np.int32)
     if qo.shape != (B + 1,) or ko.shape != (B + 1,):
         raise ValueError("offsets must have B + 1 entries")
     opts = gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*team),
-                          (ctypes.c_int * 3)(*blocks), int(round_robin), int(unfused))
+                          (ctypes.c_int * 3)(*blocks), _enum(deal, DEAL), int(not split), int(unfused))
     out = _vp()
     _check(load_library().gdpa_plan_create(qo.ctypes.data, ko.ctypes.data, B, H, d, window,
                                            _enum(dtype, DTYPE), ctypes.byref(opts), ctypes.byref(out)))

@@ -82,11 +82,17 @@ struct gdpa_plan_s {
     WorkList lists[3];
     DevRec* d_items[3] = {nullptr, nullptr, nullptr};
     int32_t* d_bin_ptr[3] = {nullptr, nullptr, nullptr};
+    // cut items of the Q-stationary lists: groups for the reduction, fp32 slots
+    int n_groups[3] = {0, 0, 0};
+    DevGroup* d_groups[3] = {nullptr, nullptr, nullptr};
+    float* d_part[3] = {nullptr, nullptr, nullptr};
 
     ~gdpa_plan_s() {
         for (int l = 0; l < 3; ++l) {
             if (d_items[l]) (void)hipFree(d_items[l]);
             if (d_bin_ptr[l]) (void)hipFree(d_bin_ptr[l]);
+            if (d_groups[l]) (void)hipFree(d_groups[l]);
+            if (d_part[l]) (void)hipFree(d_part[l]);
         }
     }
 };
@@ -130,6 +136,7 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
         if (o.blocks[l] < 0 || o.blocks[l] > 2) return fail(GDPA_ERR_INVALID_ARG, "blocks must be 0, 1 or 2");
         if (o.team[l] < 0 || o.team[l] > 2) return fail(GDPA_ERR_INVALID_ARG, "team must be 0, 1 or 2");
     }
+    if (o.deal < 0 || o.deal > 2) return fail(GDPA_ERR_INVALID_ARG, "deal must be 0, 1 or 2");
 
     if (q_off_host[0] != 0 || kv_off_host[0] != 0)
         return fail(GDPA_ERR_BAD_OFFSETS, "offsets must start at 0");
@@ -204,7 +211,9 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
                     P = cus * per_cu;
             }
         }
-        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.round_robin == 0);
+        // the fp32 path runs no work lists; its plan keeps items whole
+        const bool split = o.no_split == 0 && dtype != GDPA_F32;
+        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split);
     }
 
     // one-pass backward: one side of every sample fits one 32-row tile, and no
@@ -231,6 +240,15 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
             if (e == hipSuccess)
                 e = hipMemcpy(p->d_bin_ptr[l], wl.bin_ptr.data(), wl.bin_ptr.size() * sizeof(int32_t),
                               hipMemcpyHostToDevice);
+            if (e == hipSuccess && wl.n_parts > 0) {
+                const std::vector<DevGroup> g = device_groups(wl, p->q_off, p->kv_off);
+                p->n_groups[l] = (int)g.size();
+                e = hipMalloc((void**)&p->d_groups[l], g.size() * sizeof(DevGroup));
+                if (e == hipSuccess)
+                    e = hipMemcpy(p->d_groups[l], g.data(), g.size() * sizeof(DevGroup), hipMemcpyHostToDevice);
+                if (e == hipSuccess)
+                    e = hipMalloc((void**)&p->d_part[l], (size_t)wl.n_parts * wl.t_stat * d * sizeof(float));
+            }
             if (e != hipSuccess) {
                 delete p;
                 return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "work list upload")
@@ -282,6 +300,7 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
         }
     }
     out->bwd_fused = plan->fused;
+    for (int l = 0; l < 3; ++l) out->n_parts[l] = plan->lists[l].n_parts;
     return GDPA_OK;
 }
 
@@ -317,6 +336,13 @@ static KernelArgs base_args(gdpa_plan plan, const int32_t* q_off_dev, const int3
     return a;
 }
 
+// outputs of the cut items of list l: the sum of their chunks' slots, times mul
+static hipError_t reduce_parts(gdpa_plan plan, int l, float mul, void* out, hipStream_t s) {
+    if (plan->n_groups[l] == 0) return hipSuccess;
+    return launch_partial_sum(plan->d_groups[l], plan->n_groups[l], plan->d_part[l], plan->lists[l].t_stat,
+                              plan->d, plan->H, mul, out, plan->dtype != GDPA_BF16, s);
+}
+
 gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v,
                      const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
                      gdpa_act act, int window, void* o, void* stream) {
@@ -340,11 +366,13 @@ gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v
         a.items = plan->d_items[LIST_FWD];
         a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
         a.P = wl.P;
+        a.part = plan->d_part[LIST_FWD];
         switch (d) {
             case 32: e = launch_fwd_bf16_d32(a, wl.team, wl.nb, act, s); break;
             case 64: e = launch_fwd_bf16_d64(a, wl.team, wl.nb, act, s); break;
             default: e = launch_fwd_bf16_d128(a, wl.team, wl.nb, act, s); break;
         }
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_FWD, 1.0f, o, s);
     }
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no forward kernel for this configuration");
     if (e != hipSuccess) return fail_hip(e, "forward launch");
@@ -383,11 +411,13 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
         b.bin_ptr = plan->d_bin_ptr[l];
         b.P = plan->lists[l].P;
         const int kv = plan->fused == 1;
+        b.part = plan->d_part[l];
         switch (d) {
             case 32: e = launch_bwd_fused_d32(b, kv, act, s); break;
             case 64: e = launch_bwd_fused_d64(b, kv, act, s); break;
             default: e = launch_bwd_fused_d128(b, kv, act, s); break;
         }
+        if (e == hipSuccess && !kv) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
     } else {
         if (want_dkdv && any_k) {
             const WorkList& wl = plan->lists[LIST_DKDV];
@@ -407,11 +437,13 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.items = plan->d_items[LIST_DQ];
             b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
             b.P = wl.P;
+            b.part = plan->d_part[LIST_DQ];
             switch (d) {
                 case 32: e = launch_dq_bf16_d32(b, wl.team, wl.nb, act, s); break;
                 case 64: e = launch_dq_bf16_d64(b, wl.team, wl.nb, act, s); break;
                 default: e = launch_dq_bf16_d128(b, wl.team, wl.nb, act, s); break;
             }
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
         }
     }
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no backward kernel for this configuration");

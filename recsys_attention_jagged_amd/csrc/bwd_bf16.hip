@@ -114,45 +114,52 @@ struct DqPol : Common {
                 dp[b] = mfma32(vo, of[b][ks], dp[b]);
             }
         }
+        // dS^T in two halves of 16 keys (accumulator elements 8 m .. 8 m + 7), each
+        // consumed by its MFMAs right away: short live ranges for the activation
         const int j0 = s * 32;
-        bf16x8 dsb[NB][2];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int q0 = qrow(c, b);
-            f32x16 ds;
-            if (win > 0 && !band_all(q0, j0, win)) {
-                // lane column: query q0 + r; element e: key j0 + 8 (e/4) + 4 hh + e % 4
-                const int base = q0 + r - j0 - 4 * hh;
+        for (int m = 0; m < 2; ++m) {
+            bf16x8 dsb[NB];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float f, gr;
-                    act_fwd_grad<ACT>(sc[b][e] * scale, f, gr);
-                    const int dd = base - (8 * (e >> 2) + (e & 3));
-                    ds[e] = (dd < win && -dd < win) ? dp[b][e] * gr : 0.0f;
-                }
-            } else {
+            for (int b = 0; b < NB; ++b) {
+                const int q0 = qrow(c, b);
+                if (win > 0 && !band_all(q0, j0, win)) {
+                    // lane column: query q0 + r; element e: key j0 + 8 (e/4) + 4 hh + e % 4
+                    const int base = q0 + r - j0 - 4 * hh;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float f, gr;
-                    act_fwd_grad<ACT>(sc[b][e] * scale, f, gr);
-                    ds[e] = dp[b][e] * gr;
+                    for (int k = 0; k < 8; ++k) {
+                        const int e = 8 * m + k;
+                        float f, gr;
+                        act_fwd_grad<ACT>(sc[b][e] * scale, f, gr);
+                        const int dd = base - (8 * (e >> 2) + (e & 3));
+                        dsb[b][k] = (__bf16)((dd < win && -dd < win) ? dp[b][e] * gr : 0.0f);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int e = 8 * m + k;
+                        float f, gr;
+                        act_fwd_grad<ACT>(sc[b][e] * scale, f, gr);
+                        dsb[b][k] = (__bf16)(dp[b][e] * gr);
+                    }
                 }
             }
-            dsb[b][0] = acc_to_bf16x8(ds, 0);
-            dsb[b][1] = acc_to_bf16x8(ds, 1);
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
                 const bf16x8 kto = lds_col8<D>(kt, 16 * m, db * 32, lane);
 #pragma unroll
-                for (int b = 0; b < NB; ++b) acc[b][db] = mfma32(kto, dsb[b][m], acc[b][db]);
+                for (int b = 0; b < NB; ++b) acc[b][db] = mfma32(kto, dsb[b], acc[b][db]);
             }
+        }
     }
 
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        if (c.part >= 0) {   // one chunk of a cut item: fp32 partial block (scaled by the reduction)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) store_partial<NDB>(acc[b], a.part, c.part, ROWS, 32 * (wt * NB + b), r, hh);
+            return;
+        }
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
 #pragma unroll
         for (int b = 0; b < NB; ++b)

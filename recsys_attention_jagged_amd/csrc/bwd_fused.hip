@@ -291,6 +291,10 @@ struct QFusedPol : Common {
 
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        if (c.part >= 0) {   // one chunk of a cut item: fp32 partial dQ block (scaled by the reduction)
+            store_partial<D / 32>(acc, a.part, c.part, 32, 0, r, hh);
+            return;
+        }
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
         store<D>(acc, scale, a.dq, ob, c.lq, c.t * 32, g.tile(job - 2));
     }

@@ -170,9 +170,11 @@ __device__ __forceinline__ void act_fwd_grad(float x, float& f, float& g) {
 // work-list records (written by the host planner)
 // -------------------------------------------------------------------------
 // One work item: sample rows start at qs (queries) / ks (keys) with lengths lq /
-// lk, head h, stationary tile t and streaming tiles s0..s1 (none if s1 < s0).
+// lk, head h, stationary tile t and streaming tiles s0..s1 (none if s1 < s0);
+// part >= 0: the item is one chunk of a longer one and stores its fp32 output
+// block into partial slot `part` instead of the output.
 struct Rec {
-    int32_t qs, lq, ks, lk, h, t, s0, s1;
+    int32_t qs, lq, ks, lk, h, t, s0, s1, part, pad0, pad1, pad2;
 };
 
 // Does every pair of the 32 x 32 block (rows i0.., columns j0..) lie inside the
@@ -200,6 +202,20 @@ __device__ __forceinline__ void store_block_bf16(const f32x16 (&acc)[NDB], float
             w[1] = pack_bf16x2(acc[db][4 * j + 2] * mul, acc[db][4 * j + 3] * mul);
             __builtin_amdgcn_raw_buffer_store_b64(w, ro, (int)(row_off + (32 * db + 8 * j + 4 * hh) * 2), 0, 0);
         }
+}
+
+template <int NDB>
+__device__ __forceinline__ void store_block_f32(const f32x16 (&acc)[NDB], float mul, rsrc_t ro, uint32_t row_off,
+                                                int hh);
+
+// A chunk's 32-row block as fp32 into slot `slot` of a [slots][rows][32 NDB]
+// buffer, at item row row0 (the lane's accumulator column r is row row0 + r).
+template <int NDB>
+__device__ __forceinline__ void store_partial(const f32x16 (&acc)[NDB], float* part, int slot, int rows, int row0,
+                                              int r, int hh) {
+    constexpr uint32_t RB = 32 * NDB * 4;
+    const rsrc_t ro = slice_rsrc(part + (size_t)slot * rows * 32 * NDB, rows, RB, RB);
+    store_block_f32<NDB>(acc, 1.0f, ro, (uint32_t)(row0 + r) * RB, hh);
 }
 
 template <int NDB>

@@ -152,6 +152,11 @@ struct FwdPol {
     // in a team; blocks sharing a slot are staged one after the other)
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        if (c.part >= 0) {   // one chunk of a cut item: fp32 partial block
+#pragma unroll
+            for (int b = 0; b < NB; ++b) store_partial<NDB>(acc[b], a.part, c.part, ROWS, 32 * (wt * NB + b), r, hh);
+            return;
+        }
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
         if (a.out_f32) {
             const rsrc_t ro = slice_rsrc((const float*)a.o + ob, c.lq, rso, D * 4);

@@ -2,7 +2,9 @@
 #include "plan.hpp"
 
 #include <algorithm>
+#include <functional>
 #include <numeric>
+#include <queue>
 
 namespace gdpa {
 
@@ -18,7 +20,6 @@ Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>&, 
     auto mean_at_least = [](int64_t total, int64_t count, int64_t m) { return count > 0 && total >= m * count; };
     Layout L;
     if (d == 128) {
-        // two-wave teams once the stationary side is long enough to fill them
         // two-wave forward teams once the queries are long enough to fill them
         L.team[LIST_FWD] = mean_at_least(sq, nq, 48) ? 2 : 1;
         L.nb[LIST_FWD] = 1;
@@ -45,7 +46,7 @@ struct Cand {
 }  // namespace
 
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
-                   int H, int window, int P, int team, int nb, bool zigzag) {
+                   int H, int window, int P, int team, int nb, int deal, bool split) {
     WorkList wl;
     wl.kind = kind;
     wl.P = P;
@@ -54,7 +55,9 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
     tile_sizes(kind, team, nb, &wl.t_stat, &wl.t_strm);
     const int64_t TS = wl.t_stat, TR = wl.t_strm;
 
-    std::vector<Cand> cands;
+    // whole items in (b, h, t) order
+    std::vector<Cand> whole;
+    std::vector<int64_t> n_stat;
     for (size_t b = 0; b < lq.size(); ++b) {
         const int64_t ls = (kind == LIST_DKDV) ? lk[b] : lq[b];
         const int64_t lo = (kind == LIST_DKDV) ? lq[b] : lk[b];
@@ -77,29 +80,75 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
                     s1 = hi_row / TR;
                 }
                 int64_t cost = a1 - a0 + 1;
-                for (int64_t s = s0; s <= s1; ++s)
-                    cost += std::min(lo, (s + 1) * TR) - s * TR + kStepCharge;
+                for (int64_t s = s0; s <= s1; ++s) cost += std::min(lo, (s + 1) * TR) - s * TR + kStepCharge;
                 Cand c;
                 c.cost = cost;
-                c.it = Item{(int32_t)b, h, (int32_t)t, (int32_t)s0, (int32_t)s1, 0, 0, 0};
-                cands.push_back(c);
+                c.it = Item{(int32_t)b, h, (int32_t)t, (int32_t)s0, (int32_t)s1, -1, 0, 0};
+                whole.push_back(c);
+                n_stat.push_back(a1 - a0 + 1);
             }
         }
+    }
+
+    // chunks of the long items of a Q-stationary list
+    std::vector<Cand> cands;
+    if (split && kind != LIST_DKDV && P > 0) {
+        int64_t total = 0;
+        for (const Cand& c : whole) total += c.cost;
+        const int64_t mean = std::max<int64_t>(1, ceil_div(total, (int64_t)P));
+        const int64_t piece = std::max<int64_t>(1, ceil_div(mean, 4));
+        int32_t slot = 0;
+        for (size_t i = 0; i < whole.size(); ++i) {
+            const Cand& c = whole[i];
+            const int64_t n = (int64_t)c.it.s1 - c.it.s0 + 1;
+            if (n < 2 || c.cost <= mean) {
+                cands.push_back(c);
+                continue;
+            }
+            const int64_t k = std::min(n, ceil_div(c.cost, piece));
+            const int64_t lo = lk[c.it.b];
+            for (int64_t j = 0; j < k; ++j) {
+                const int64_t f = c.it.s0 + j * n / k, l = c.it.s0 + (j + 1) * n / k - 1;
+                Cand p = c;
+                p.cost = n_stat[i];
+                for (int64_t s = f; s <= l; ++s) p.cost += std::min(lo, (s + 1) * TR) - s * TR + kStepCharge;
+                p.it.s0 = (int32_t)f;
+                p.it.s1 = (int32_t)l;
+                p.it.part = slot + (int32_t)j;
+                cands.push_back(p);
+            }
+            slot += (int32_t)k;
+        }
+        wl.n_parts = slot;
+    } else {
+        cands = std::move(whole);
     }
     std::sort(cands.begin(), cands.end(), [](const Cand& x, const Cand& y) {
         if (x.cost != y.cost) return x.cost > y.cost;
         if (x.it.b != y.it.b) return x.it.b < y.it.b;
         if (x.it.h != y.it.h) return x.it.h < y.it.h;
-        return x.it.t < y.it.t;
+        if (x.it.t != y.it.t) return x.it.t < y.it.t;
+        return x.it.s0 < y.it.s0;
     });
 
-    // zigzag (or round-robin) deal, then a bin-major CSR keeping deal order
+    // deal, then a bin-major CSR keeping deal order
     std::vector<int32_t> bin_of(cands.size());
     std::vector<int32_t> count(P, 0);
     wl.bin_cost.assign(P, 0);
+    typedef std::pair<int64_t, int> Load;   // (cost so far, bin): least cost, then lowest bin
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> least;
+    if (deal == DEAL_GREEDY)
+        for (int p = 0; p < P; ++p) least.push(Load(0, p));
     for (size_t r = 0; r < cands.size(); ++r) {
-        const int64_t rnd = (int64_t)r / P, pos = (int64_t)r % P;
-        const int p = (int)((!zigzag || rnd % 2 == 0) ? pos : P - 1 - pos);
+        int p;
+        if (deal == DEAL_GREEDY) {
+            p = least.top().second;
+            least.pop();
+            least.push(Load(wl.bin_cost[p] + cands[r].cost, p));
+        } else {
+            const int64_t rnd = (int64_t)r / P, pos = (int64_t)r % P;
+            p = (int)((deal == DEAL_ROUND_ROBIN || rnd % 2 == 0) ? pos : P - 1 - pos);
+        }
         bin_of[r] = p;
         count[p]++;
         wl.bin_cost[p] += cands[r].cost;
@@ -125,6 +174,7 @@ std::vector<int32_t> export_list(const WorkList& wl) {
         out.push_back(it.t);
         out.push_back(it.s0);
         out.push_back(it.s1);
+        out.push_back(it.part);
     }
     return out;
 }
@@ -143,6 +193,36 @@ std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t
         d.t = it.t;
         d.s0 = it.s0;
         d.s1 = it.s1;
+        d.part = it.part;
+        d.pad0 = d.pad1 = d.pad2 = 0;
+    }
+    return out;
+}
+
+std::vector<DevGroup> device_groups(const WorkList& wl, const std::vector<int32_t>& q_off,
+                                    const std::vector<int32_t>&) {
+    // chunk j of a cut item holds slot slot0 + j; slots of one item are consecutive
+    std::vector<const Item*> by_slot(wl.n_parts, nullptr);
+    for (const Item& it : wl.items)
+        if (it.part >= 0) by_slot[it.part] = &it;
+    std::vector<DevGroup> out;
+    for (int s = 0; s < wl.n_parts; ++s) {
+        const Item* it = by_slot[s];
+        const bool same = !out.empty() && s > 0 && by_slot[s - 1]->b == it->b && by_slot[s - 1]->h == it->h &&
+                          by_slot[s - 1]->t == it->t;
+        if (same) {
+            out.back().n++;
+            continue;
+        }
+        const int32_t lq = q_off[it->b + 1] - q_off[it->b];
+        DevGroup g;
+        g.row0 = q_off[it->b] + it->t * wl.t_stat;
+        g.rows = std::min(wl.t_stat, lq - it->t * wl.t_stat);
+        g.h = it->h;
+        g.slot0 = s;
+        g.n = 1;
+        g.pad0 = g.pad1 = g.pad2 = 0;
+        out.push_back(g);
     }
     return out;
 }

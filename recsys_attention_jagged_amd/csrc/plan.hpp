@@ -14,8 +14,15 @@
 // whose other side is empty get no steps and write zeros.
 //
 // Cost of an item: valid stationary rows + sum over steps of (valid streaming
-// rows + 32).  Order: cost descending, then (b, h, t).  Deal: the r-th item goes
-// to bin r mod P in even rounds and P-1 - (r mod P) in odd rounds.
+// rows + 32).  Chunks: in a Q-stationary list, an item with at least two steps
+// whose cost exceeds the mean bin cost m = ceil(total / P) is cut into
+// k = min(steps, ceil(cost / ceil(m / 4))) chunks of consecutive steps (chunk i:
+// steps s0 + floor(i n / k) .. s0 + floor((i + 1) n / k) - 1); each chunk writes its
+// partial output block to its own slot (numbered in (b, h, t) order) and a
+// reduction adds the slots of one item in chunk order.  Order: cost descending,
+// then (b, h, t, s0).  Deal: greedy (default: each item, in order, to the bin of
+// least cost so far, the lowest index on ties), zigzag (the r-th item goes to bin
+// r mod P in even rounds and P-1 - (r mod P) in odd rounds) or round robin.
 #pragma once
 
 #include <cstdint>
@@ -26,8 +33,9 @@ namespace gdpa {
 enum ListKind { LIST_FWD = 0, LIST_DKDV = 1, LIST_DQ = 2 };
 
 // One work item as the kernels read it (32 bytes, one scalar load).
+// part: partial-output slot of a chunk, -1 for an item that stores its outputs.
 struct Item {
-    int32_t b, h, t, s0, s1, pad0, pad1, pad2;
+    int32_t b, h, t, s0, s1, part, pad0, pad1;
 };
 static_assert(sizeof(Item) == 32, "Item must be 32 bytes");
 
@@ -35,9 +43,18 @@ static_assert(sizeof(Item) == 32, "Item must be 32 bytes");
 // resolved on the host, so a kernel needs one load per item and no dependent
 // loads of the offset arrays.
 struct DevRec {
-    int32_t qs, lq, ks, lk, h, t, s0, s1;
+    int32_t qs, lq, ks, lk, h, t, s0, s1, part, pad0, pad1, pad2;
 };
-static_assert(sizeof(DevRec) == 32, "DevRec must be 32 bytes");
+static_assert(sizeof(DevRec) == 48, "DevRec must be 48 bytes");
+
+// One item cut into chunks, for the reduction: output rows row0 .. row0 + rows - 1
+// of head h (absolute row indices) are the sum of slots slot0 .. slot0 + n - 1.
+struct DevGroup {
+    int32_t row0, rows, h, slot0, n, pad0, pad1, pad2;
+};
+static_assert(sizeof(DevGroup) == 32, "DevGroup must be 32 bytes");
+
+enum Deal { DEAL_GREEDY = 0, DEAL_ZIGZAG = 1, DEAL_ROUND_ROBIN = 2 };
 
 struct WorkList {
     int kind = 0, P = 0, t_stat = 0, t_strm = 0, team = 0, nb = 0;
@@ -45,6 +62,7 @@ struct WorkList {
     std::vector<Item> items;        // bin-major, deal order inside a bin
     std::vector<int64_t> bin_cost;  // P
     int64_t n_steps = 0;
+    int n_parts = 0;                // partial-output slots (chunks of cut items)
 };
 
 // waves per team and 32-row stationary blocks per wave, per list
@@ -58,9 +76,12 @@ constexpr int kStepCharge = 32;
 Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk, int d);
 void tile_sizes(int kind, int team, int nb, int* t_stat, int* t_strm);
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
-                   int H, int window, int P, int team, int nb, bool zigzag);
+                   int H, int window, int P, int team, int nb, int deal, bool split);
 std::vector<int32_t> export_list(const WorkList& wl);
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
                                    const std::vector<int32_t>& kv_off);
+// the cut items of a Q-stationary list, in slot order
+std::vector<DevGroup> device_groups(const WorkList& wl, const std::vector<int32_t>& q_off,
+                                    const std::vector<int32_t>& kv_off);
 
 }  // namespace gdpa

@@ -36,31 +36,35 @@ def test_status_strings_and_poly_bound():
     assert 0 < G.gdpa_gelu_poly_bound() < 1e-4
 
 
-def _host_plan(lq, lk, H, d, window, P=1024, team=(0, 0, 0), blocks=(0, 0, 0), rr=False):
+def _host_plan(lq, lk, H, d, window, P=1024, team=(0, 0, 0), blocks=(0, 0, 0), deal="greedy", split=True):
     qo, ko = offsets(lq), offsets(lk)
     return G.gdpa_plan_create(qo, ko, len(lq), H, d, window, "bf16", host_only=True,
-                              bins=(P, P, P), team=team, blocks=blocks, round_robin=rr)
+                              bins=(P, P, P), team=team, blocks=blocks, deal=deal, split=split)
 
 
-def _ref_exports(lq, lk, H, window, P, d, layout=None, zigzag=True):
+def _ref_exports(lq, lk, H, window, P, d, layout=None, deal="greedy", split=True):
     layout = layout or PR.auto_layout(list(lq), list(lk), window, d)
-    return {kind: PR.export(PR.plan_list(kind, list(lq), list(lk), H, window, P, *layout[kind], zigzag=zigzag))
+    return {kind: PR.export(PR.plan_list(kind, list(lq), list(lk), H, window, P, *layout[kind], mode=deal,
+                                         split=split))
             for kind in PR.LISTS}
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_plan_bit_exact_vs_reference_on_workloads(cfg):
+@pytest.mark.parametrize("cfg,deal", [(1, "greedy"), (2, "greedy"), (3, "greedy"), (4, "greedy"), (5, "greedy"),
+                                      (2, "zigzag"), (4, "zigzag")])
+def test_plan_bit_exact_vs_reference_on_workloads(cfg, deal):
     w = WORKLOADS[cfg]
     lq, lk = workload_lengths(cfg)
     lq, lk = [int(x) for x in lq], [int(x) for x in lk]
-    plan = _host_plan(lq, lk, w["H"], w["d"], w["window"])
+    plan = _host_plan(lq, lk, w["H"], w["d"], w["window"], deal=deal)
     try:
-        ref = _ref_exports(lq, lk, w["H"], w["window"], 1024, w["d"])
+        ref = _ref_exports(lq, lk, w["H"], w["window"], 1024, w["d"], deal=deal)
         for kind in PR.LISTS:
             got = G.gdpa_plan_export(plan, kind)
             np.testing.assert_array_equal(got, np.asarray(ref[kind], dtype=np.int32), err_msg=kind)
         st = G.gdpa_plan_stats(plan)
         assert st["Tq"] == sum(lq) and st["Tk"] == sum(lk)
+        for i, kind in enumerate(("fwd", "dkdv", "dq")):
+            assert st["n_parts"][i] == max([-1] + [r[5] for r in np.asarray(ref[kind][6 + 1024 + 1:]).reshape(-1, 6)]) + 1
     finally:
         G.gdpa_plan_destroy(plan)
 
@@ -78,14 +82,15 @@ EDGE = [
 @pytest.mark.parametrize("d,team,blocks", [(64, (1, 1, 1), (1, 1, 1)), (64, (1, 1, 1), (2, 1, 2)),
                                            (128, (2, 2, 2), (1, 1, 1)), (128, (1, 2, 1), (2, 1, 2)),
                                            (128, (0, 0, 0), (0, 0, 0)), (32, (0, 0, 0), (0, 0, 0))])
-@pytest.mark.parametrize("P,rr", [(1, False), (7, False), (1024, False), (16, True)])
-def test_plan_bit_exact_vs_reference_edge_cases(lq, lk, window, d, team, blocks, P, rr):
-    plan = _host_plan(lq, lk, 3, d, window, P=P, team=team, blocks=blocks, rr=rr)
+@pytest.mark.parametrize("P,deal,split", [(1, "greedy", True), (7, "greedy", True), (1024, "greedy", True),
+                                          (16, "round_robin", True), (5, "zigzag", True), (3, "greedy", False)])
+def test_plan_bit_exact_vs_reference_edge_cases(lq, lk, window, d, team, blocks, P, deal, split):
+    plan = _host_plan(lq, lk, 3, d, window, P=P, team=team, blocks=blocks, deal=deal, split=split)
     try:
         auto = PR.auto_layout(list(lq), list(lk), window, d)
         layout = {kind: (team[i] or auto[kind][0], blocks[i] or auto[kind][1])
                   for i, kind in enumerate(("fwd", "dkdv", "dq"))}
-        ref = _ref_exports(lq, lk, 3, window, P, d, layout, zigzag=not rr)
+        ref = _ref_exports(lq, lk, 3, window, P, d, layout, deal=deal, split=split)
         for kind in PR.LISTS:
             np.testing.assert_array_equal(G.gdpa_plan_export(plan, kind), np.asarray(ref[kind], np.int32))
     finally:

@@ -195,6 +195,37 @@ def test_one_pass_backward(d, case, unfused):
         check_close(a, b, f"{name} f32out d={d} case={case}")
 
 
+# long Q-stationary items cut into chunks (fp32 partial slots + reduction kernel);
+# few bins make the long-key samples' items exceed the mean bin cost
+CHUNK_CASES = [
+    ([32, 1, 20, 32, 5, 0], [3000, 5, 700, 1, 0, 0]),   # every Lq <= 32: one-pass Q-stationary backward
+    ([300, 5, 70, 129, 1], [1500, 7, 64, 1000, 33]),    # two-kernel backward
+]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("case", range(len(CHUNK_CASES)))
+@pytest.mark.parametrize("deal", ["zigzag", "greedy"])
+def test_cut_items(d, case, deal):
+    lq, lk = CHUNK_CASES[case]
+    say(f"cut items d={d} case={case} deal={deal}")
+    inp = make_from_lengths(lq, lk, 2, d, act="gelu", seed=31 + case, device=DEV)
+    opts = dict(bins=(16, 16, 16) if case == 0 else (16, 16, 32), deal=deal)
+    with G.Plan(inp.q_off, inp.kv_off, 2, d, 0, "bf16", **opts) as plan:
+        st = plan.stats()
+    assert st["n_parts"][0] > 0 and st["n_parts"][2] > 0 and st["n_parts"][1] == 0
+    assert st["bwd_fused"] == (2 if case == 0 else 0)
+    ro = oracle_fwd(inp)
+    rg = oracle_bwd(inp)
+    check_close(run_fwd(inp, **opts), ro, f"O cut d={d} case={case}")
+    check_close(run_fwd(inp, dtype="bf16_f32out", **opts), ro, f"O f32out cut d={d} case={case}")
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, **opts), rg):
+        check_close(a, b, f"{name} cut d={d} case={case}")
+    # the dQ kernel alone (Q-stationary list with chunks) and the two-kernel path
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, unfused=True, **opts), rg):
+        check_close(a, b, f"{name} cut unfused d={d} case={case}")
+
+
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_taylor6", "identity"])
 def test_one_pass_backward_activations(act):
     say(f"one-pass backward activation {act}")
@@ -357,6 +388,22 @@ def test_full_size_sampled(cfg):
     # properties at any size: finite everywhere, zero rows where no partner exists
     for t in (o, dq, dk, dv):
         assert torch.isfinite(t.float()).all()
+
+
+def test_determinism_with_cut_items():
+    say("bitwise determinism run to run, with chunks and their reduction")
+    inp = make_from_lengths(*CHUNK_CASES[0], 2, 128, act="gelu", seed=5, device=DEV)
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, 2, 128, 0, "bf16", bins=(16, 16, 16)) as plan:
+        assert plan.stats()["n_parts"][0] > 0
+        a = plan.fwd(inp.q, inp.k, inp.v, qo, ko, "gelu")
+        b = plan.fwd(inp.q, inp.k, inp.v, qo, ko, "gelu")
+        g1 = plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "gelu")
+        g2 = plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "gelu")
+        torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    for x, y in zip(g1, g2):
+        assert torch.equal(x, y)
 
 
 def test_determinism():

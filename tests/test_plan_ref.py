@@ -59,8 +59,8 @@ def test_items_are_exactly_the_tiles_with_valid_pairs(lq, lk, window, kind, tile
 @pytest.mark.parametrize("P", [1, 3, 8, 256])
 def test_zigzag_deal(P):
     items = [(c, i, 0, 0, 0, 0) for i, c in enumerate([5, 9, 9, 1, 7, 3, 3, 8, 2, 2, 6] * 7)]
-    bin_ptr, flat, cost = PR.deal(items, P)
-    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[3]))
+    bin_ptr, flat, cost = PR.deal(items, P, "zigzag")
+    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[3], it[4]))
     assert sorted(flat) == sorted(items)
     for r, it in enumerate(order):
         rnd, pos = divmod(r, P)
@@ -73,9 +73,30 @@ def test_zigzag_deal(P):
 
 def test_zigzag_beats_round_robin_on_skewed_costs():
     items = [(c, i, 0, 0, 0, 0) for i, c in enumerate(range(1000, 0, -1))]
-    _, _, zz = PR.deal(items, 16, zigzag=True)
-    _, _, rr = PR.deal(items, 16, zigzag=False)
-    assert PR.imbalance(zz) < PR.imbalance(rr)
+    _, _, zz = PR.deal(items, 16, "zigzag")
+    _, _, rr = PR.deal(items, 16, "round_robin")
+    _, _, gr = PR.deal(items, 16, "greedy")
+    assert PR.imbalance(gr) <= PR.imbalance(zz) < PR.imbalance(rr)
+
+
+@pytest.mark.parametrize("P", [1, 3, 8, 64])
+def test_greedy_deal_is_least_loaded_first(P):
+    """Each item, in sorted order, goes to the bin of least cost so far (lowest
+    index on ties): checked with a plain scan over the bins."""
+    rng = np.random.default_rng(P)
+    items = [(int(c), i, 0, 0, 0, 0) for i, c in enumerate(rng.integers(1, 500, 300))]
+    bin_ptr, flat, cost = PR.deal(items, P, "greedy")
+    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[3], it[4]))
+    load = [0] * P
+    want = [[] for _ in range(P)]
+    for it in order:
+        p = min(range(P), key=lambda q: (load[q], q))
+        want[p].append(it)
+        load[p] += it[0]
+    assert [flat[bin_ptr[p]:bin_ptr[p + 1]] for p in range(P)] == want
+    assert cost == load
+    # the classic bound of longest-first greedy: max load <= mean + largest item
+    assert max(cost) <= sum(load) / P + max(it[0] for it in items)
 
 
 def test_auto_layout_rules():
@@ -98,4 +119,80 @@ def test_export_layout():
     assert P == 4 and n == len(pl["items"])
     assert ex[2:6] == [64, 32, 1, 2]
     assert ex[6:6 + P + 1] == pl["bin_ptr"]
-    assert len(ex) == 6 + P + 1 + 5 * n
+    assert len(ex) == 6 + P + 1 + 6 * n
+
+
+SPLIT_CASES = [
+    ([32] * 6, [1, 1000, 31, 32, 33, 0], 0, 2),
+    ([32, 64, 5], [4096, 100, 3000], 0, 3),
+    ([300, 129, 64, 2], [300, 129, 64, 2], 128, 2),
+    ([70, 1, 33, 200, 0], [64, 3, 0, 2, 129], 0, 1),
+]
+
+
+@pytest.mark.parametrize("lq,lk,window,P", SPLIT_CASES)
+@pytest.mark.parametrize("kind", PR.LISTS)
+@pytest.mark.parametrize("layout", [(1, 1), (2, 1), (1, 2)])
+def test_chunks_cover_each_tile_once(lq, lk, window, P, kind, layout):
+    """Cutting items keeps the plan exact: every tile pair with a valid (i, j) is
+    visited once, every output tile has one owner -- a whole item, or the chunks of
+    one cut item with consecutive slots numbered in (b, h, t) order."""
+    H = 2
+    if kind == "dkdv" and layout != (1, 1):
+        return
+    pl = PR.plan_list(kind, lq, lk, H, window, P, *layout)
+    t_stat, t_strm = pl["t_stat"], pl["t_strm"]
+    seen, whole, chunks = set(), set(), {}
+    for b, h, t, s0, s1, part in pl["items"]:
+        for s in range(s0, s1 + 1):
+            assert (b, h, t, s) not in seen
+            seen.add((b, h, t, s))
+        if part < 0:
+            assert (b, h, t) not in whole and (b, h, t) not in chunks
+            whole.add((b, h, t))
+        else:
+            assert kind != "dkdv" and (b, h, t) not in whole
+            assert s1 >= s0
+            chunks.setdefault((b, h, t), []).append((s0, s1, part))
+    assert seen == _tiles_with_valid_pair(kind, lq, lk, H, window, t_stat, t_strm)
+    slots = []
+    for key in sorted(chunks):
+        cs = sorted(chunks[key])
+        assert len(cs) >= 2
+        assert all(cs[i][1] + 1 == cs[i + 1][0] for i in range(len(cs) - 1))   # consecutive steps
+        assert [c[2] for c in cs] == list(range(cs[0][2], cs[0][2] + len(cs)))  # consecutive slots
+        slots += [c[2] for c in cs]
+    assert slots == list(range(pl["n_parts"]))   # numbered in (b, h, t) order
+    ls = lk if kind == "dkdv" else lq
+    assert whole | set(chunks) == {(b, h, t) for b in range(len(ls)) for h in range(H)
+                                   for t in range(-(-ls[b] // t_stat))}
+
+
+def test_chunk_rule_on_a_long_item():
+    """One sample of 32 queries and 4096 keys next to 63 one-step samples, 16 bins,
+    no window: the long item (128 steps) costs 32 + 128 * 64 = 8224, the total is
+    8224 + 63 * (1 + 33) = 10366, the mean bin cost m = ceil(10366 / 16) = 648, so the
+    item is cut into k = ceil(8224 / ceil(648 / 4)) = ceil(8224 / 162) = 51 chunks of
+    2 or 3 steps; the one-step items stay whole."""
+    lq, lk = [32] + [1] * 63, [4096] + [1] * 63
+    pl = PR.plan_list("fwd", lq, lk, 1, 0, 16, 1, 1)
+    parts = sorted((s0, s1, part) for b, h, t, s0, s1, part in pl["items"] if part >= 0)
+    assert pl["n_parts"] == 51 and len(parts) == 51
+    assert [s1 - s0 + 1 for s0, s1, _ in parts] == [(j + 1) * 128 // 51 - j * 128 // 51 for j in range(51)]
+    assert all(part == -1 for b, h, t, s0, s1, part in pl["items"] if b > 0)
+    # the chunked plan balances where the whole item could not
+    whole = PR.plan_list("fwd", lq, lk, 1, 0, 16, 1, 1, split=False)
+    assert max(whole["bin_cost"]) >= 8224
+    for mode in PR.DEALS:
+        cut = PR.plan_list("fwd", lq, lk, 1, 0, 16, 1, 1, mode=mode)
+        assert max(cut["bin_cost"]) < 0.15 * max(whole["bin_cost"])
+        assert sum(cut["bin_cost"]) == sum(whole["bin_cost"]) + 50 * 32   # each extra chunk reloads 32 rows
+    g = PR.groups(pl, [0] + list(np.cumsum(lq)))
+    assert g == [(0, 32, 0, 0, 51)]
+
+
+def test_short_items_are_never_cut():
+    # one step per item, or a KV-stationary list: nothing to cut
+    lq, lk = [32] * 40, [20] * 40
+    assert PR.plan_list("fwd", lq, lk, 2, 0, 4, 1, 1)["n_parts"] == 0
+    assert PR.plan_list("dkdv", [4000, 1], [32, 1], 2, 0, 4, 1, 1)["n_parts"] == 0
