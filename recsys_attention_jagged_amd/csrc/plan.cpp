@@ -20,11 +20,13 @@ Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>&, 
     auto mean_at_least = [](int64_t total, int64_t count, int64_t m) { return count > 0 && total >= m * count; };
     Layout L;
     if (d == 128) {
-        // two-wave forward teams once the queries are long enough to fill them
+        // two-wave forward teams once the queries are long enough to fill them;
+        // two dQ blocks per wave once they fill 64 rows
         L.team[LIST_FWD] = mean_at_least(sq, nq, 48) ? 2 : 1;
         L.nb[LIST_FWD] = 1;
         L.team[LIST_DQ] = L.team[LIST_DKDV] = 1;
-        L.nb[LIST_DQ] = L.nb[LIST_DKDV] = 1;
+        L.nb[LIST_DQ] = mean_at_least(sq, nq, 64) ? 2 : 1;
+        L.nb[LIST_DKDV] = 1;
     } else {
         L.team[LIST_FWD] = L.team[LIST_DQ] = L.team[LIST_DKDV] = 1;
         L.nb[LIST_FWD] = mean_at_least(sq, nq, 64) ? 2 : 1;
