@@ -17,14 +17,14 @@ Readings (the page gives no cost model or tie-break):
     KV-stationary list) have no steps (s0 = 0, s1 = -1) and only write zeros;
   * cost = (valid stationary rows) + sum over steps of (valid streaming rows + 32),
     i.e. rows moved through memory plus a fixed per-step charge;
-  * chunks (Q-stationary lists only): with m = ceil(total cost / P), the mean bin
-    cost, an item with n >= 2 steps and cost > m is cut into
+  * chunks: with m = ceil(total cost / P), the mean bin cost, an item with n >= 2
+    steps and cost > m is cut into
     k = min(n, ceil(cost / ceil(m / 4))) chunks of consecutive steps (no bin could
     hold it at the mean), chunk j holding steps s0 + floor(j n / k) ..
     s0 + floor((j + 1) n / k) - 1 and costing its stationary rows plus its steps;
     chunk j of the g-th cut item (in (b, h, t) order) writes partial-output slot
-    (chunks of earlier cut items) + j, and the item's output is the sum of its
-    slots.  The page deals tiles, not whole rows of tiles, so a long row of tiles
+    (chunks of earlier cut items) + j (O or dQ; dK and dV for the KV-stationary
+    list), and the item's output is the sum of its slots.  The page deals tiles, not whole rows of tiles, so a long row of tiles
     need not sit in one bin; the chunks keep that freedom without atomics;
   * stable order: cost descending, then (b, h, t, s0) ascending;
   * deal over P bins, by default greedy: each item, in sorted order, to the bin
@@ -102,11 +102,12 @@ def enumerate_items(kind: str, lq, lk, H: int, window: int, t_stat: int, t_strm:
 
 
 def split_items(kind: str, items, lq, lk, P: int, t_stat: int, t_strm: int):
-    """Cut the long items of a Q-stationary list into chunks.  Returns
+    """Cut the items longer than a mean bin into chunks.  Returns
     ([(cost, b, h, t, s0, s1, part)], number of slots); part = -1 for whole items."""
     out = []
-    if kind == "dkdv" or P <= 0:
+    if P <= 0:
         return [it + (-1,) for it in items], 0
+    ls, lo = (lk, lq) if kind == "dkdv" else (lq, lk)
     mean = max(1, _ceil_div(sum(it[0] for it in items), P))
     piece = max(1, _ceil_div(mean, 4))
     slot = 0
@@ -116,8 +117,8 @@ def split_items(kind: str, items, lq, lk, P: int, t_stat: int, t_strm: int):
             out.append((cost, b, h, t, s0, s1, -1))
             continue
         k = min(n, _ceil_div(cost, piece))
-        n_stat = min(int(lq[b]), (t + 1) * t_stat) - t * t_stat
-        lo_other = int(lk[b])
+        n_stat = min(int(ls[b]), (t + 1) * t_stat) - t * t_stat
+        lo_other = int(lo[b])
         for j in range(k):
             f, l = s0 + j * n // k, s0 + (j + 1) * n // k - 1
             c = n_stat + sum(min(lo_other, (s + 1) * t_strm) - s * t_strm + STEP_CHARGE for s in range(f, l + 1))
@@ -184,9 +185,10 @@ def plan(lq, lk, H: int, window: int, P: int, d: int = 128, layout=None, mode: s
     return {kind: plan_list(kind, lq, lk, H, window, P, *layout[kind], mode=mode, split=split) for kind in LISTS}
 
 
-def groups(pl, q_off):
+def groups(pl, off):
     """Cut items of a list in slot order: [(row0, rows, h, slot0, n)] where output
-    rows row0 .. row0 + rows - 1 (absolute) of head h are the sum of n slots."""
+    rows row0 .. row0 + rows - 1 (absolute; off = query offsets, or key offsets for
+    the dK/dV list) of head h are the sum of n slots."""
     by_slot = {}
     for b, h, t, s0, s1, part in pl["items"]:
         if part >= 0:
@@ -197,9 +199,9 @@ def groups(pl, q_off):
         if out and by_slot[s - 1] == (b, h, t):
             out[-1][4] += 1
             continue
-        lq = q_off[b + 1] - q_off[b]
+        ln = off[b + 1] - off[b]
         ts = pl["t_stat"]
-        out.append([q_off[b] + t * ts, min(ts, lq - t * ts), h, s, 1])
+        out.append([off[b] + t * ts, min(ts, ln - t * ts), h, s, 1])
     return [tuple(g) for g in out]
 
 

@@ -246,8 +246,9 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
                 e = hipMalloc((void**)&p->d_groups[l], g.size() * sizeof(DevGroup));
                 if (e == hipSuccess)
                     e = hipMemcpy(p->d_groups[l], g.data(), g.size() * sizeof(DevGroup), hipMemcpyHostToDevice);
+                const size_t blocks = l == LIST_DKDV ? 2 : 1;   // dK and dV
                 if (e == hipSuccess)
-                    e = hipMalloc((void**)&p->d_part[l], (size_t)wl.n_parts * wl.t_stat * d * sizeof(float));
+                    e = hipMalloc((void**)&p->d_part[l], blocks * wl.n_parts * wl.t_stat * d * sizeof(float));
             }
             if (e != hipSuccess) {
                 delete p;
@@ -337,10 +338,12 @@ static KernelArgs base_args(gdpa_plan plan, const int32_t* q_off_dev, const int3
 }
 
 // outputs of the cut items of list l: the sum of their chunks' slots, times mul
-static hipError_t reduce_parts(gdpa_plan plan, int l, float mul, void* out, hipStream_t s) {
+// (the dK/dV list keeps two blocks per slot: block 0 dK, block 1 dV)
+static hipError_t reduce_parts(gdpa_plan plan, int l, float mul, void* out, hipStream_t s, int block = 0) {
     if (plan->n_groups[l] == 0) return hipSuccess;
     return launch_partial_sum(plan->d_groups[l], plan->n_groups[l], plan->d_part[l], plan->lists[l].t_stat,
-                              plan->d, plan->H, mul, out, plan->dtype != GDPA_BF16, s);
+                              l == LIST_DKDV ? 2 : 1, block, plan->d, plan->H, mul, out,
+                              plan->dtype != GDPA_BF16, s);
 }
 
 gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v,
@@ -418,6 +421,8 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             default: e = launch_bwd_fused_d128(b, kv, act, s); break;
         }
         if (e == hipSuccess && !kv) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
+        if (e == hipSuccess && kv) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
+        if (e == hipSuccess && kv) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
     } else {
         if (want_dkdv && any_k) {
             const WorkList& wl = plan->lists[LIST_DKDV];
@@ -425,11 +430,14 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.items = plan->d_items[LIST_DKDV];
             b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
             b.P = wl.P;
+            b.part = plan->d_part[LIST_DKDV];
             switch (d) {
                 case 32: e = launch_dkdv_bf16_d32(b, wl.team, wl.nb, act, s); break;
                 case 64: e = launch_dkdv_bf16_d64(b, wl.team, wl.nb, act, s); break;
                 default: e = launch_dkdv_bf16_d128(b, wl.team, wl.nb, act, s); break;
             }
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
         }
         if (e == hipSuccess && want_dq && any_q) {
             const WorkList& wl = plan->lists[LIST_DQ];

@@ -281,6 +281,11 @@ struct DkdvPol : Common {
 
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        if (c.part >= 0) {   // one chunk of a cut item: fp32 partial dK, dV blocks (scaled by the reduction)
+            store_partial<NDB>(accK, a.part, 2 * c.part, ROWS, 32 * wt, r, hh);
+            store_partial<NDB>(accV, a.part, 2 * c.part + 1, ROWS, 32 * wt, r, hh);
+            return;
+        }
         const size_t ob = ((size_t)c.ks * H + c.h) * D;
         store<D>(accK, scale, a.dk, ob, c.lk, krow(c), g.tile(job - 2 + (T > 1 ? wt : 0)));
         store<D>(accV, 1.0f, a.dv, ob, c.lk, krow(c), g.tile(job - 2 + (T > 1 ? wt : 1)));

@@ -23,7 +23,8 @@ struct KernelArgs {
     const int32_t* kv_off;
     const void* items;          // device work-list records (Rec), bin-major
     const int32_t* bin_ptr;
-    float* part;                // fp32 partial-output slots of chunks, [slots][rows per item][d]
+    float* part;                // fp32 partial-output slots of chunks, [slots][blocks][rows per item][d]
+                                // (one block per slot; two, dK then dV, for the dK/dV list)
     int P;          // bins = persistent workgroups
     int B;          // samples
     int H;
@@ -59,10 +60,13 @@ GDPA_DECLARE_FUSED(64)
 GDPA_DECLARE_FUSED(128)
 #undef GDPA_DECLARE_FUSED
 
-// O (or dQ) rows of cut items: out = mul * (sum of the item's slots, in slot
-// order), stored as bf16 (out_f32 = 0) or fp32
-hipError_t launch_partial_sum(const DevGroup* groups, int n_groups, const float* part, int rows_per_slot, int d,
-                              int H, float mul, void* out, int out_f32, hipStream_t s);
+// Output rows of cut items: out = mul * (sum of the item's slots, in slot order),
+// stored as bf16 (out_f32 = 0) or fp32.  A slot holds `stride` blocks of
+// rows_per_slot x d floats; block `offset` of each slot is summed (O and dQ:
+// stride 1; dK, dV: stride 2, offsets 0 and 1).
+hipError_t launch_partial_sum(const DevGroup* groups, int n_groups, const float* part, int rows_per_slot,
+                              int stride, int offset, int d, int H, float mul, void* out, int out_f32,
+                              hipStream_t s);
 
 // plain fp32 kernels (no MFMA): forward, dQ, dK/dV over the offsets directly
 hipError_t launch_fwd_f32(const KernelArgs& a, int Tq, int d, int act, hipStream_t s);

@@ -13,19 +13,21 @@ namespace gdpa {
 namespace {
 
 // one workgroup per cut item; a thread handles 4 consecutive columns of a row
+// Block b of slot s is at part + (stride s + offset) * rows_per_slot * d: one output
+// per slot (stride 1) or dK, dV interleaved (stride 2, offset 0 or 1).
 __global__ __launch_bounds__(256) void partial_sum_kernel(const DevGroup* __restrict__ groups,
                                                           const float* __restrict__ part, int rows_per_slot,
-                                                          int d, int H, float mul, void* __restrict__ out,
-                                                          int out_f32) {
+                                                          int stride, int offset, int d, int H, float mul,
+                                                          void* __restrict__ out, int out_f32) {
     const DevGroup g = groups[blockIdx.x];
     const int quads = g.rows * d / 4;
     const size_t slot_elems = (size_t)rows_per_slot * d;
     for (int i = threadIdx.x; i < quads; i += blockDim.x) {
         const int row = 4 * i / d, col = 4 * i % d;
-        const float* src = part + (size_t)g.slot0 * slot_elems + (size_t)row * d + col;
+        const float* src = part + ((size_t)stride * g.slot0 + offset) * slot_elems + (size_t)row * d + col;
         float4 acc = *(const float4*)src;
         for (int j = 1; j < g.n; ++j) {
-            const float4 x = *(const float4*)(src + (size_t)j * slot_elems);
+            const float4 x = *(const float4*)(src + (size_t)j * stride * slot_elems);
             acc.x += x.x;
             acc.y += x.y;
             acc.z += x.z;
@@ -45,12 +47,15 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(const DevGroup* __rest
 
 }  // namespace
 
-hipError_t launch_partial_sum(const DevGroup* groups, int n_groups, const float* part, int rows_per_slot, int d,
-                              int H, float mul, void* out, int out_f32, hipStream_t s) {
+hipError_t launch_partial_sum(const DevGroup* groups, int n_groups, const float* part, int rows_per_slot,
+                              int stride, int offset, int d, int H, float mul, void* out, int out_f32,
+                              hipStream_t s) {
     if (n_groups <= 0) return hipSuccess;
-    if (!groups || !part || !out || rows_per_slot <= 0 || d % 4 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(partial_sum_kernel, dim3(n_groups), dim3(256), 0, s, groups, part, rows_per_slot, d, H,
-                       mul, out, out_f32);
+    if (!groups || !part || !out || rows_per_slot <= 0 || d % 4 != 0 || stride < 1 || offset < 0 ||
+        offset >= stride)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(partial_sum_kernel, dim3(n_groups), dim3(256), 0, s, groups, part, rows_per_slot, stride,
+                       offset, d, H, mul, out, out_f32);
     return hipGetLastError();
 }
 

@@ -92,9 +92,9 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
         }
     }
 
-    // chunks of the long items of a Q-stationary list
+    // chunks of the items longer than a mean bin
     std::vector<Cand> cands;
-    if (split && kind != LIST_DKDV && P > 0) {
+    if (split && P > 0) {
         int64_t total = 0;
         for (const Cand& c : whole) total += c.cost;
         const int64_t mean = std::max<int64_t>(1, ceil_div(total, (int64_t)P));
@@ -108,7 +108,7 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
                 continue;
             }
             const int64_t k = std::min(n, ceil_div(c.cost, piece));
-            const int64_t lo = lk[c.it.b];
+            const int64_t lo = (kind == LIST_DKDV) ? lq[c.it.b] : lk[c.it.b];
             for (int64_t j = 0; j < k; ++j) {
                 const int64_t f = c.it.s0 + j * n / k, l = c.it.s0 + (j + 1) * n / k - 1;
                 Cand p = c;
@@ -202,7 +202,7 @@ std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t
 }
 
 std::vector<DevGroup> device_groups(const WorkList& wl, const std::vector<int32_t>& q_off,
-                                    const std::vector<int32_t>&) {
+                                    const std::vector<int32_t>& kv_off) {
     // chunk j of a cut item holds slot slot0 + j; slots of one item are consecutive
     std::vector<const Item*> by_slot(wl.n_parts, nullptr);
     for (const Item& it : wl.items)
@@ -216,10 +216,12 @@ std::vector<DevGroup> device_groups(const WorkList& wl, const std::vector<int32_
             out.back().n++;
             continue;
         }
-        const int32_t lq = q_off[it->b + 1] - q_off[it->b];
+        // output rows: queries of a Q-stationary list, keys of the KV-stationary one
+        const std::vector<int32_t>& off = wl.kind == LIST_DKDV ? kv_off : q_off;
+        const int32_t len = off[it->b + 1] - off[it->b];
         DevGroup g;
-        g.row0 = q_off[it->b] + it->t * wl.t_stat;
-        g.rows = std::min(wl.t_stat, lq - it->t * wl.t_stat);
+        g.row0 = off[it->b] + it->t * wl.t_stat;
+        g.rows = std::min(wl.t_stat, len - it->t * wl.t_stat);
         g.h = it->h;
         g.slot0 = s;
         g.n = 1;

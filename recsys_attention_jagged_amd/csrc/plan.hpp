@@ -14,12 +14,12 @@
 // whose other side is empty get no steps and write zeros.
 //
 // Cost of an item: valid stationary rows + sum over steps of (valid streaming
-// rows + 32).  Chunks: in a Q-stationary list, an item with at least two steps
-// whose cost exceeds the mean bin cost m = ceil(total / P) is cut into
-// k = min(steps, ceil(cost / ceil(m / 4))) chunks of consecutive steps (chunk i:
-// steps s0 + floor(i n / k) .. s0 + floor((i + 1) n / k) - 1); each chunk writes its
-// partial output block to its own slot (numbered in (b, h, t) order) and a
-// reduction adds the slots of one item in chunk order.  Order: cost descending,
+// rows + 32).  Chunks: an item with at least two steps whose cost exceeds the
+// mean bin cost m = ceil(total / P) is cut into k = min(steps, ceil(cost /
+// ceil(m / 4))) chunks of consecutive steps (chunk i: steps s0 + floor(i n / k) ..
+// s0 + floor((i + 1) n / k) - 1); each chunk writes its partial output block(s)
+// (O or dQ; dK and dV for the KV-stationary list) to its own slot (numbered in
+// (b, h, t) order) and a reduction adds the slots of one item in chunk order.  Order: cost descending,
 // then (b, h, t, s0).  Deal: greedy (default: each item, in order, to the bin of
 // least cost so far, the lowest index on ties), zigzag (the r-th item goes to bin
 // r mod P in even rounds and P-1 - (r mod P) in odd rounds) or round robin.
@@ -48,7 +48,8 @@ struct DevRec {
 static_assert(sizeof(DevRec) == 48, "DevRec must be 48 bytes");
 
 // One item cut into chunks, for the reduction: output rows row0 .. row0 + rows - 1
-// of head h (absolute row indices) are the sum of slots slot0 .. slot0 + n - 1.
+// of head h (absolute query rows, or key rows for dK/dV) are the sum of slots
+// slot0 .. slot0 + n - 1.
 struct DevGroup {
     int32_t row0, rows, h, slot0, n, pad0, pad1, pad2;
 };
@@ -80,7 +81,7 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
 std::vector<int32_t> export_list(const WorkList& wl);
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
                                    const std::vector<int32_t>& kv_off);
-// the cut items of a Q-stationary list, in slot order
+// the cut items of a list, in slot order (output rows: queries, or keys for dK/dV)
 std::vector<DevGroup> device_groups(const WorkList& wl, const std::vector<int32_t>& q_off,
                                     const std::vector<int32_t>& kv_off);
 

@@ -19,6 +19,7 @@ import torch
 import recsys_attention_jagged_amd as G
 from gdpa_workloads import WORKLOADS, make_from_lengths, make_workload, offsets
 from oracle import gdpa_ref as R
+from oracle import plan_ref as PR
 
 pytestmark = pytest.mark.gpu
 
@@ -195,11 +196,14 @@ def test_one_pass_backward(d, case, unfused):
         check_close(a, b, f"{name} f32out d={d} case={case}")
 
 
-# long Q-stationary items cut into chunks (fp32 partial slots + reduction kernel);
-# few bins make the long-key samples' items exceed the mean bin cost
+# items longer than a mean bin cut into chunks (fp32 partial slots + reduction
+# kernel); few bins make the long samples' items exceed the mean bin cost
 CHUNK_CASES = [
-    ([32, 1, 20, 32, 5, 0], [3000, 5, 700, 1, 0, 0]),   # every Lq <= 32: one-pass Q-stationary backward
-    ([300, 5, 70, 129, 1], [1500, 7, 64, 1000, 33]),    # two-kernel backward
+    # (lq, lk, bins, the list whose items must be cut, gdpa_bwd's kernels)
+    ([32, 1, 20, 32, 5, 0], [3000, 5, 700, 1, 0, 0], (16, 16, 16), "dq", 2),   # one Q-stationary pass
+    ([300, 5, 70, 129, 1], [1500, 7, 64, 1000, 33], (16, 16, 32), "fwd", 0),   # two kernels
+    ([3000, 5, 700, 1, 0, 0], [32, 1, 20, 32, 5, 0], (16, 16, 16), "dkdv", 1),  # one KV-stationary pass
+    ([4000, 7, 300], [64, 900, 33], (32, 32, 32), "dkdv", 0),                  # two kernels, every list cut
 ]
 
 
@@ -207,21 +211,26 @@ CHUNK_CASES = [
 @pytest.mark.parametrize("case", range(len(CHUNK_CASES)))
 @pytest.mark.parametrize("deal", ["zigzag", "greedy"])
 def test_cut_items(d, case, deal):
-    lq, lk = CHUNK_CASES[case]
+    lq, lk, bins, cut, fused = CHUNK_CASES[case]
     say(f"cut items d={d} case={case} deal={deal}")
     inp = make_from_lengths(lq, lk, 2, d, act="gelu", seed=31 + case, device=DEV)
-    opts = dict(bins=(16, 16, 16) if case == 0 else (16, 16, 32), deal=deal)
+    opts = dict(bins=bins, deal=deal)
     with G.Plan(inp.q_off, inp.kv_off, 2, d, 0, "bf16", **opts) as plan:
         st = plan.stats()
-    assert st["n_parts"][0] > 0 and st["n_parts"][2] > 0 and st["n_parts"][1] == 0
-    assert st["bwd_fused"] == (2 if case == 0 else 0)
+    layout = PR.auto_layout(lq, lk, 0, d)
+    want = [PR.plan_list(k, lq, lk, 2, 0, bins[i], *layout[k], mode=deal)["n_parts"]
+            for i, k in enumerate(("fwd", "dkdv", "dq"))]
+    assert list(st["n_parts"]) == want and want[("fwd", "dkdv", "dq").index(cut)] > 0
+    assert st["bwd_fused"] == fused
     ro = oracle_fwd(inp)
     rg = oracle_bwd(inp)
     check_close(run_fwd(inp, **opts), ro, f"O cut d={d} case={case}")
     check_close(run_fwd(inp, dtype="bf16_f32out", **opts), ro, f"O f32out cut d={d} case={case}")
     for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, **opts), rg):
         check_close(a, b, f"{name} cut d={d} case={case}")
-    # the dQ kernel alone (Q-stationary list with chunks) and the two-kernel path
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, dtype="bf16_f32out", **opts), rg):
+        check_close(a, b, f"{name} f32out cut d={d} case={case}")
+    # the two-kernel path over the same cut lists
     for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, unfused=True, **opts), rg):
         check_close(a, b, f"{name} cut unfused d={d} case={case}")
 
@@ -392,10 +401,10 @@ def test_full_size_sampled(cfg):
 
 def test_determinism_with_cut_items():
     say("bitwise determinism run to run, with chunks and their reduction")
-    inp = make_from_lengths(*CHUNK_CASES[0], 2, 128, act="gelu", seed=5, device=DEV)
+    inp = make_from_lengths(*CHUNK_CASES[3][:2], 2, 128, act="gelu", seed=5, device=DEV)
     qo, ko = dev_offsets(inp)
-    with G.Plan(inp.q_off, inp.kv_off, 2, 128, 0, "bf16", bins=(16, 16, 16)) as plan:
-        assert plan.stats()["n_parts"][0] > 0
+    with G.Plan(inp.q_off, inp.kv_off, 2, 128, 0, "bf16", bins=(32, 32, 32)) as plan:
+        assert min(plan.stats()["n_parts"]) > 0
         a = plan.fwd(inp.q, inp.k, inp.v, qo, ko, "gelu")
         b = plan.fwd(inp.q, inp.k, inp.v, qo, ko, "gelu")
         g1 = plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "gelu")

@@ -155,7 +155,7 @@ def test_chunks_cover_each_tile_once(lq, lk, window, P, kind, layout):
             assert (b, h, t) not in whole and (b, h, t) not in chunks
             whole.add((b, h, t))
         else:
-            assert kind != "dkdv" and (b, h, t) not in whole
+            assert (b, h, t) not in whole
             assert s1 >= s0
             chunks.setdefault((b, h, t), []).append((s0, s1, part))
     assert seen == _tiles_with_valid_pair(kind, lq, lk, H, window, t_stat, t_strm)
@@ -196,7 +196,19 @@ def test_chunk_rule_on_a_long_item():
 
 
 def test_short_items_are_never_cut():
-    # one step per item, or a KV-stationary list: nothing to cut
+    # one step per item: nothing to cut
     lq, lk = [32] * 40, [20] * 40
     assert PR.plan_list("fwd", lq, lk, 2, 0, 4, 1, 1)["n_parts"] == 0
-    assert PR.plan_list("dkdv", [4000, 1], [32, 1], 2, 0, 4, 1, 1)["n_parts"] == 0
+    assert PR.plan_list("dkdv", lk, lq, 2, 0, 4, 1, 1)["n_parts"] == 0
+
+
+def test_kv_stationary_chunks_group_key_rows():
+    """A 32-key sample with 4000 queries: its two dK/dV items (one per head) stream
+    125 q tiles each and are cut; the groups name key rows (the sample's keys start
+    after the 3 keys of sample 0)."""
+    lq, lk = [5, 4000], [3, 32]
+    pl = PR.plan_list("dkdv", lq, lk, 2, 0, 4, 1, 1)
+    assert pl["n_parts"] > 0
+    g = PR.groups(pl, [0, 3, 35])
+    assert [(r0, rows, h) for r0, rows, h, _, _ in g] == [(3, 32, 0), (3, 32, 1)]
+    assert sum(n for *_, n in g) == pl["n_parts"]
