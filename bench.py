@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of jagged GDPA forward + backward (bf16 in, fp32 accumulate) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--act NAME]
+    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5|pffn] [--act NAME]
 
 A step is one forward pass plus one backward pass (dK/dV kernel, then dQ kernel)
 over the whole batch of the chosen workload, with inputs resident in HBM.  The
@@ -10,11 +10,14 @@ lengths with median 64 and max 512, H = 4, d = 128, SiLU, no window).
 
 Prints one JSON line: `value` is useful TFLOP/s over fwd + bwd, counting only
 valid (query, key) pairs: 4 H d |V| for the forward and 10 H d |V| for the
-backward.  `roofline` describes the slowest kernel against HBM bandwidth (every
-workload here sits below the bf16 MFMA ridge point), using its algorithmic bytes
-(each input read once, each output written once) and its average duration from
-HIP events recorded on the launch stream around each launch.  `cpu_baseline`
-times the fp64 oracle on the host cores over a bounded prefix of the same batch.
+backward.  `roofline` describes the slowest kernel against the roof its
+arithmetic intensity puts it under: HBM bandwidth for the attention workloads
+(algorithmic bytes: each input read once, each output written once), the bf16
+MFMA peak for pFFN (algorithmic FLOPs: the products the kernel's algorithm
+performs, 4, 8, 6 and 10 H d |V| for the forward, dK/dV, dQ and one-pass
+kernels), with the kernel's average duration from HIP events recorded on the
+launch stream around each launch.  `cpu_baseline` times the fp64 oracle on the
+host cores over a bounded prefix of the same batch.
 """
 from __future__ import annotations
 
@@ -32,6 +35,12 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_flops(H, d, pairs):
+    """Algorithmic FLOPs per launch: the MFMA products each kernel's algorithm performs."""
+    u = 2.0 * H * d * pairs          # one product over the valid pairs
+    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd": 5 * u}
 
 
 def kernel_bytes(H, d, Tq, Tk):
@@ -83,25 +92,34 @@ def cpu_baseline(inp, budget_s=15.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    spent, flops, n = 0.0, 0, 0
+    spent, flops, n, rows = 0.0, 0, 0, 0
+    f = lambda t, a, e: t[a:e].to("cpu", torch.float64).numpy()
     for b in range(len(inp.lq)):
         qs, qe = int(inp.q_off[b]), int(inp.q_off[b + 1])
         ks, ke = int(inp.kv_off[b]), int(inp.kv_off[b + 1])
-        f = lambda t, a, e: t[a:e].to("cpu", torch.float64).numpy()
-        q, k, v, do = f(inp.q, qs, qe), f(inp.k, ks, ke), f(inp.v, ks, ke), f(inp.do, qs, qe)
-        qo, ko = np.array([0, qe - qs]), np.array([0, ke - ks])
-        t0 = time.perf_counter()
-        R.gdpa_fwd(q, k, v, qo, ko, inp.act, inp.window)
-        R.gdpa_bwd(q, k, v, do, qo, ko, inp.act, inp.window)
-        spent += time.perf_counter() - t0
-        flops += 14 * inp.H * inp.d * R.useful_pairs([qe - qs], [ke - ks], inp.window)
+        k, v = f(inp.k, ks, ke), f(inp.v, ks, ke)
+        # a long windowless sample is taken in blocks of 2048 query rows (each block
+        # against all the sample's keys), so the budget can stop inside it
+        step = 2048 if inp.window == 0 else qe - qs
+        for a in range(qs, max(qe, qs + 1), max(step, 1)):
+            e = min(qe, a + step)
+            q, do = f(inp.q, a, e), f(inp.do, a, e)
+            qo, ko = np.array([0, e - a]), np.array([0, ke - ks])
+            t0 = time.perf_counter()
+            R.gdpa_fwd(q, k, v, qo, ko, inp.act, inp.window)
+            R.gdpa_bwd(q, k, v, do, qo, ko, inp.act, inp.window)
+            spent += time.perf_counter() - t0
+            flops += 14 * inp.H * inp.d * R.useful_pairs([e - a], [ke - ks], inp.window)
+            rows += e - a
+            if spent >= budget_s:
+                break
         n += 1
         if spent >= budget_s:
             break
     return {"value": flops / spent / 1e12 if spent > 0 else None, "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"first {n} of {len(inp.lq)} samples, fp64 numpy/scipy forward+backward, "
-                      f"{spent:.1f} s, same seeded inputs"}
+            "sample": f"{rows} query rows of the first {n} of {len(inp.lq)} samples, fp64 numpy/scipy "
+                      f"forward+backward, {spent:.1f} s, same seeded inputs"}
 
 
 def main(argv=None):
@@ -109,7 +127,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", default="2", choices=["2", "3", "4", "5", "pffn"])
     ap.add_argument("--act", default=None, help="override the workload's activation (e.g. gelu_poly)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -139,12 +157,15 @@ def main(argv=None):
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
         return 0
     import recsys_attention_jagged_amd as G
-    from gdpa_workloads import WORKLOADS, make_workload
+    from gdpa_workloads import PFFN, WORKLOADS, make_pffn, make_workload
 
     G.load_library()
-    w = WORKLOADS[args.config]
+    w = PFFN if args.config == "pffn" else WORKLOADS[int(args.config)]
     log(f"generating workload {args.config} ({w['name']}) on cuda:0 ...")
-    inp = make_workload(args.config, seed=args.seed, device="cuda", act=args.act)
+    if args.config == "pffn":   # one sample: every query row against the shared weight rows
+        inp = make_pffn(seed=args.seed, device="cuda", act=args.act)
+    else:
+        inp = make_workload(int(args.config), seed=args.seed, device="cuda", act=args.act)
     torch.cuda.synchronize()
     qo = torch.tensor(inp.q_off, dtype=torch.int32, device="cuda")
     ko = torch.tensor(inp.kv_off, dtype=torch.int32, device="cuda")
@@ -205,8 +226,20 @@ def main(argv=None):
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
     kb = kernel_bytes(H, d, Tq, Tk)
+    kf = kernel_flops(H, d, pairs)
     dom = max(kms, key=kms.get)
-    achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
+    # the roof the kernel's arithmetic intensity puts it under (ridge: peak FLOP/s / peak B/s)
+    mfma_bound = kf[dom] / kb[dom] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved = kf[dom] / (kms[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "algorithmic_flops": kf[dom], "traffic": measured_traffic(w["name"], dom)}
+    else:
+        achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                    "algorithmic_bytes": kb[dom], "traffic": measured_traffic(w["name"], dom)}
     kernels = {n: {"ms": round(kms[n], 4), "alg_GBps": round(kb[n] / (kms[n] * 1e-3) / 1e9, 1)}
                for n in kms}
     kernels["fwd"]["useful_TFLOPs"] = round(4.0 * H * d * pairs / (kms["fwd"] * 1e-3) / 1e12, 2)
@@ -234,9 +267,7 @@ def main(argv=None):
         "kernels": kernels,
         "plan_ms": round(plan_ms, 1),
         "wall_s_timed": round(wall, 3),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "algorithmic_bytes": kb[dom], "traffic": measured_traffic(w["name"], dom)},
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")

@@ -174,6 +174,26 @@ def make_workload(cfg: int, seed: int = 0, device: str = "cpu", B: Optional[int]
                              pma_seeds=w.get("pma_seeds", False), cfg=cfg)
 
 
+# pFFN as GDPA (the third module of the GDPA page's unified-modules diagram; read as
+# shared weight rows W_K, W_V [M, H, d] for every query row of the batch): the query
+# rows of the jagged self-attention batch (workload 2's lengths, Tq = 79,265 at seed
+# 0) against M = 512 weight rows per head, H = 4, d = 128, SiLU.  The weights are
+# drawn like keys and values (N(0, 1), RMS-normalised); they stand in for trained
+# weights, which are not available.
+PFFN = dict(name="pffn_silu_bf16", queries_of=2, M=512, H=4, d=128, act="silu", dtype="bf16", rms="qkv")
+
+
+def make_pffn(seed: int = 0, device: str = "cpu", Tq: Optional[int] = None, M: Optional[int] = None,
+              act: Optional[str] = None) -> JaggedInputs:
+    """pFFN inputs as one sample: q [Tq, H, d], k = W_K and v = W_V [M, H, d], dO."""
+    w = PFFN
+    if Tq is None:
+        lq, _ = workload_lengths(w["queries_of"], seed)
+        Tq = int(np.sum(lq))
+    return make_from_lengths([Tq], [w["M"] if M is None else M], w["H"], w["d"], act=act or w["act"],
+                             window=0, dtype=w["dtype"], seed=seed, device=device, rms=w["rms"])
+
+
 def pad_waste(lengths, multiple: Optional[int] = None) -> float:
     """Fraction of token slots that are padding when samples are padded to the
     batch max (``multiple=None``) or up to a multiple of ``multiple``."""

@@ -204,6 +204,30 @@ gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void
                         gdpa_act act, int window, void* dq, void* stream);
 
 /*
+ * pFFN as GDPA (GDPA page, "Section details", diagram of self-attention, PMA and
+ * pFFN unified as GDPA).  The page gives no formula; read here as: per head,
+ * weight matrices W_K, W_V [M, H, d] shared by every query row of the batch,
+ *     O_i = sum_{j < M} act(Q_i . W_K,j / sqrt(d)) W_V,j,
+ * with the weight gradients dW_K, dW_V summed over all Tq query rows.  Samples do
+ * not interact, so this is GDPA on one sample of Tq queries and M keys; the
+ * planner's chunks spread the weight-gradient reduction over the device.
+ *
+ * gdpa_pffn_plan_create - a plan for Tq >= 0 query rows and M >= 0 weight rows
+ *   (H, d, dtype, opts as for gdpa_plan_create).  Also keeps device copies of the
+ *   offsets, so the pFFN calls take none.  Errors as gdpa_plan_create.
+ * gdpa_pffn_fwd - O [Tq, H, d] from q [Tq, H, d], wk, wv [M, H, d]; act as gdpa_fwd.
+ * gdpa_pffn_bwd - dQ [Tq, H, d], dW_K and dW_V [M, H, d] for the loss sum(O * dO).
+ *   Both: device pointers in the plan's dtype; errors as gdpa_fwd / gdpa_bwd, and
+ *   PLAN_MISMATCH for a plan not made by gdpa_pffn_plan_create.
+ */
+gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,
+                                  gdpa_plan* out);
+gdpa_status gdpa_pffn_fwd(gdpa_plan plan, const void* q, const void* wk, const void* wv, gdpa_act act, void* o,
+                          void* stream);
+gdpa_status gdpa_pffn_bwd(gdpa_plan plan, const void* q, const void* wk, const void* wv, const void* dout,
+                          gdpa_act act, void* dq, void* dwk, void* dwv, void* stream);
+
+/*
  * gdpa_plan_export - serialise one work list as int32 values:
  *   [P, n_items, tile_stat, tile_strm, team, blocks, bin_ptr[0..P], then per item in
  *    bin order (b, h, t, s0, s1, part)]

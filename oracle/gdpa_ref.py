@@ -249,3 +249,26 @@ def useful_pairs(lq, lk, window: int = 0) -> int:
             for i in range(a):
                 total += min(c, i + window) - max(0, i - window + 1)
     return total
+
+
+# ---------------------------------------------------------------------------
+# pFFN as GDPA
+# ---------------------------------------------------------------------------
+# GDPA page, "Section details", diagram "Self-attention, PMA and pFFN unified as
+# GDPA": pFFN is the third module with the two-products-and-an-activation shape.
+# The page defines nothing more; the reading used here: per head, learned weight
+# matrices W_K, W_V [M, H, d] play the keys and values of every query row of the
+# batch, so O_i = sum_j act(Q_i . W_K,j / sqrt(d)) W_V,j over all M weight rows,
+# and the weight gradients dW_K, dW_V are sums over every query row.  Samples do
+# not interact, so this is GDPA on one sample holding all Tq query rows.
+
+def pffn_fwd(q, wk, wv, act: str) -> np.ndarray:
+    """O [Tq, H, d] (fp64) of pFFN with shared weights wk, wv [M, H, d]."""
+    tq, m = q.shape[0], wk.shape[0]
+    return gdpa_fwd(q, wk, wv, np.array([0, tq]), np.array([0, m]), act, 0)
+
+
+def pffn_bwd(q, wk, wv, do, act: str):
+    """(dQ, dW_K, dW_V) in fp64 for the loss sum(O * dO)."""
+    tq, m = q.shape[0], wk.shape[0]
+    return gdpa_bwd(q, wk, wv, do, np.array([0, tq]), np.array([0, m]), act, 0)

@@ -18,7 +18,8 @@ Readings (the page gives no cost model or tie-break):
   * cost = (valid stationary rows) + sum over steps of (valid streaming rows + 32),
     i.e. rows moved through memory plus a fixed per-step charge;
   * chunks: with m = ceil(total cost / P), the mean bin cost, an item with n >= 2
-    steps and cost > m is cut into
+    steps and cost > m (> ceil(m / 4) when the list has fewer than 2 P items, which
+    no deal could balance) is cut into
     k = min(n, ceil(cost / ceil(m / 4))) chunks of consecutive steps (no bin could
     hold it at the mean), chunk j holding steps s0 + floor(j n / k) ..
     s0 + floor((j + 1) n / k) - 1 and costing its stationary rows plus its steps;
@@ -110,10 +111,11 @@ def split_items(kind: str, items, lq, lk, P: int, t_stat: int, t_strm: int):
     ls, lo = (lk, lq) if kind == "dkdv" else (lq, lk)
     mean = max(1, _ceil_div(sum(it[0] for it in items), P))
     piece = max(1, _ceil_div(mean, 4))
+    limit = piece if len(items) < 2 * P else mean
     slot = 0
     for cost, b, h, t, s0, s1 in items:
         n = s1 - s0 + 1
-        if n < 2 or cost <= mean:
+        if n < 2 or cost <= limit:
             out.append((cost, b, h, t, s0, s1, -1))
             continue
         k = min(n, _ceil_div(cost, piece))

@@ -80,8 +80,12 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_last_error.restype = ctypes.c_char_p
     lib.gdpa_gelu_poly_bound.argtypes = []
     lib.gdpa_gelu_poly_bound.restype = ctypes.c_double
+    lib.gdpa_pffn_plan_create.argtypes = [_i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts), ctypes.POINTER(_vp)]
+    lib.gdpa_pffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
+    lib.gdpa_pffn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp]
     for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
-                 "gdpa_plan_export", "gdpa_plan_stats"):
+                 "gdpa_plan_export", "gdpa_plan_stats", "gdpa_pffn_plan_create", "gdpa_pffn_fwd",
+                 "gdpa_pffn_bwd"):
         getattr(lib, name).restype = _i
     if path == LIB_PATH:
         _lib = lib
@@ -130,8 +134,7 @@ def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: in
     ko = np.ascontiguousarray(kv_off_host, dtype=np.int32)
     if qo.shape != (B + 1,) or ko.shape != (B + 1,):
         raise ValueError("offsets must have B + 1 entries")
-    opts = gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*team),
-                          (ctypes.c_int * 3)(*blocks), _enum(deal, DEAL), int(not split), int(unfused))
+    opts = _opts(host_only, bins, team, blocks, deal, split, unfused)
     out = _vp()
     _check(load_library().gdpa_plan_create(qo.ctypes.data, ko.ctypes.data, B, H, d, window,
                                            _enum(dtype, DTYPE), ctypes.byref(opts), ctypes.byref(out)))
@@ -160,6 +163,32 @@ def gdpa_bwd_dq(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window
     _check(load_library().gdpa_bwd_dq(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
                                       _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, _ptr(dq),
                                       _stream(stream)))
+
+
+def _opts(host_only, bins, team, blocks, deal, split, unfused):
+    return gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*team),
+                          (ctypes.c_int * 3)(*blocks), _enum(deal, DEAL), int(not split), int(unfused))
+
+
+def gdpa_pffn_plan_create(Tq: int, M: int, H: int, d: int, dtype, host_only: bool = False, bins=(0, 0, 0),
+                          team=(0, 0, 0), blocks=(0, 0, 0), deal="greedy", split: bool = True,
+                          unfused: bool = False) -> int:
+    """Plan of pFFN over Tq query rows and M shared weight rows (opaque handle)."""
+    opts = _opts(host_only, bins, team, blocks, deal, split, unfused)
+    out = _vp()
+    _check(load_library().gdpa_pffn_plan_create(Tq, M, H, d, _enum(dtype, DTYPE), ctypes.byref(opts),
+                                                ctypes.byref(out)))
+    return out.value
+
+
+def gdpa_pffn_fwd(plan, q, wk, wv, act, o, stream=None):
+    _check(load_library().gdpa_pffn_fwd(plan, _ptr(q), _ptr(wk), _ptr(wv), _enum(act, ACT), _ptr(o),
+                                        _stream(stream)))
+
+
+def gdpa_pffn_bwd(plan, q, wk, wv, dout, act, dq, dwk, dwv, stream=None):
+    _check(load_library().gdpa_pffn_bwd(plan, _ptr(q), _ptr(wk), _ptr(wv), _ptr(dout), _enum(act, ACT),
+                                        _ptr(dq), _ptr(dwk), _ptr(dwv), _stream(stream)))
 
 
 def gdpa_plan_export(plan, list_) -> np.ndarray:

@@ -86,6 +86,9 @@ struct gdpa_plan_s {
     int n_groups[3] = {0, 0, 0};
     DevGroup* d_groups[3] = {nullptr, nullptr, nullptr};
     float* d_part[3] = {nullptr, nullptr, nullptr};
+    // pFFN plans: device copies of the offsets {0, Tq} and {0, M}
+    int32_t* d_off = nullptr;
+    bool pffn = false;
 
     ~gdpa_plan_s() {
         for (int l = 0; l < 3; ++l) {
@@ -94,6 +97,7 @@ struct gdpa_plan_s {
             if (d_groups[l]) (void)hipFree(d_groups[l]);
             if (d_part[l]) (void)hipFree(d_part[l]);
         }
+        if (d_off) (void)hipFree(d_off);
     }
 };
 
@@ -478,6 +482,54 @@ gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void
                         gdpa_act act, int window, void* dq, void* stream) {
     return bwd_parts(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, dq, nullptr, nullptr,
                      stream, false, true);
+}
+
+gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,
+                                  gdpa_plan* out) {
+    g_err.clear();
+    if (!out) return fail(GDPA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (Tq < 0 || M < 0) return fail(GDPA_ERR_INVALID_ARG, "Tq and M must be >= 0");
+    const int32_t q_off[2] = {0, Tq}, kv_off[2] = {0, M};
+    gdpa_plan p = nullptr;
+    gdpa_status st = gdpa_plan_create(q_off, kv_off, 1, H, d, 0, dtype, opts, &p);
+    if (st != GDPA_OK) return st;
+    p->pffn = true;
+    if (!p->host_only) {
+        const int32_t off[4] = {0, Tq, 0, M};
+        hipError_t e = hipMalloc((void**)&p->d_off, sizeof(off));
+        if (e == hipSuccess) e = hipMemcpy(p->d_off, off, sizeof(off), hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            delete p;
+            return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "offset upload") : fail_hip(e, "offset upload");
+        }
+    }
+    *out = p;
+    return GDPA_OK;
+}
+
+static gdpa_status check_pffn(gdpa_plan plan) {
+    if (!plan) return fail(GDPA_ERR_INVALID_ARG, "plan is NULL");
+    if (!plan->pffn) return fail(GDPA_ERR_PLAN_MISMATCH, "not a pFFN plan (use gdpa_pffn_plan_create)");
+    if (plan->host_only) return fail(GDPA_ERR_PLAN_MISMATCH, "host-only plan cannot run kernels");
+    return GDPA_OK;
+}
+
+gdpa_status gdpa_pffn_fwd(gdpa_plan plan, const void* q, const void* wk, const void* wv, gdpa_act act, void* o,
+                          void* stream) {
+    g_err.clear();
+    gdpa_status st = check_pffn(plan);
+    if (st != GDPA_OK) return st;
+    return gdpa_fwd(plan, q, wk, wv, plan->d_off, plan->d_off + 2, 1, plan->H, plan->d, act, 0, o, stream);
+}
+
+gdpa_status gdpa_pffn_bwd(gdpa_plan plan, const void* q, const void* wk, const void* wv, const void* dout,
+                          gdpa_act act, void* dq, void* dwk, void* dwv, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_pffn(plan);
+    if (st != GDPA_OK) return st;
+    return gdpa_bwd(plan, q, wk, wv, dout, plan->d_off, plan->d_off + 2, 1, plan->H, plan->d, act, 0, dq, dwk,
+                    dwv, stream);
 }
 
 }  // extern "C"

@@ -99,11 +99,13 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
         for (const Cand& c : whole) total += c.cost;
         const int64_t mean = std::max<int64_t>(1, ceil_div(total, (int64_t)P));
         const int64_t piece = std::max<int64_t>(1, ceil_div(mean, 4));
+        // fewer than two items per bin: no deal can balance them, so cut at a quarter bin
+        const int64_t limit = (int64_t)whole.size() < 2 * (int64_t)P ? piece : mean;
         int32_t slot = 0;
         for (size_t i = 0; i < whole.size(); ++i) {
             const Cand& c = whole[i];
             const int64_t n = (int64_t)c.it.s1 - c.it.s0 + 1;
-            if (n < 2 || c.cost <= mean) {
+            if (n < 2 || c.cost <= limit) {
                 cands.push_back(c);
                 continue;
             }

@@ -15,8 +15,9 @@
 //
 // Cost of an item: valid stationary rows + sum over steps of (valid streaming
 // rows + 32).  Chunks: an item with at least two steps whose cost exceeds the
-// mean bin cost m = ceil(total / P) is cut into k = min(steps, ceil(cost /
-// ceil(m / 4))) chunks of consecutive steps (chunk i: steps s0 + floor(i n / k) ..
+// mean bin cost m = ceil(total / P) (a quarter of it, ceil(m / 4), when the list
+// has fewer than 2 P items) is cut into k = min(steps, ceil(cost / ceil(m / 4)))
+// chunks of consecutive steps (chunk i: steps s0 + floor(i n / k) ..
 // s0 + floor((i + 1) n / k) - 1); each chunk writes its partial output block(s)
 // (O or dQ; dK and dV for the KV-stationary list) to its own slot (numbered in
 // (b, h, t) order) and a reduction adds the slots of one item in chunk order.  Order: cost descending,

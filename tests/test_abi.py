@@ -204,3 +204,20 @@ def test_export_capacity_check():
         assert m.value == n.value
     finally:
         G.gdpa_plan_destroy(plan)
+
+
+def test_pffn_host_plan_is_one_sample():
+    """A pFFN plan is the plan of one sample holding every query row and the M
+    weight rows, bit for bit; only its own calls accept it."""
+    Tq, M = 1000, 300
+    h = G.gdpa_pffn_plan_create(Tq, M, 2, 64, "bf16", host_only=True, bins=(16, 16, 16))
+    try:
+        ref = _ref_exports([Tq], [M], 2, 0, 16, 64)
+        for kind in PR.LISTS:
+            np.testing.assert_array_equal(G.gdpa_plan_export(h, kind), np.asarray(ref[kind], np.int32))
+        st = G.gdpa_plan_stats(h)
+        assert st["Tq"] == Tq and st["Tk"] == M and st["valid_pairs"] == Tq * M
+        assert G.STATUS[_status_of(G.gdpa_pffn_fwd, h, None, None, None, "silu", None, 0)] == "GDPA_ERR_PLAN_MISMATCH"
+    finally:
+        G.gdpa_plan_destroy(h)
+    assert G.STATUS[_status_of(G.gdpa_pffn_plan_create, -1, 3, 2, 64, "bf16", host_only=True)] == "GDPA_ERR_INVALID_ARG"

@@ -235,6 +235,48 @@ def test_cut_items(d, case, deal):
         check_close(a, b, f"{name} cut unfused d={d} case={case}")
 
 
+# ---------------------------------------------------------------------------
+# pFFN as GDPA: every query row against the same M weight rows
+# ---------------------------------------------------------------------------
+
+def run_pffn(inp, act, **opts):
+    Tq, M = int(inp.q_off[-1]), int(inp.kv_off[-1])
+    h = G.gdpa_pffn_plan_create(Tq, M, inp.H, inp.d, "bf16", **opts)
+    try:
+        st = G.gdpa_plan_stats(h)
+        o = torch.empty_like(inp.q)
+        dq, dwk, dwv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+        G.gdpa_pffn_fwd(h, inp.q, inp.k, inp.v, act, o)
+        G.gdpa_pffn_bwd(h, inp.q, inp.k, inp.v, inp.do, act, dq, dwk, dwv)
+        torch.cuda.synchronize()
+    finally:
+        G.gdpa_plan_destroy(h)
+    return st, [t.float().cpu().numpy() for t in (o, dq, dwk, dwv)]
+
+
+@pytest.mark.parametrize("Tq,M,d,bins", [(300, 96, 64, 16), (1000, 200, 128, 32), (77, 32, 32, 8),
+                                         (2500, 65, 128, 0), (0, 64, 64, 8), (50, 0, 128, 8)])
+@pytest.mark.parametrize("act", ["silu", "gelu"])
+def test_pffn(Tq, M, d, bins, act):
+    say(f"pFFN Tq={Tq} M={M} d={d} bins={bins} act={act}")
+    inp = make_from_lengths([Tq], [M], 2, d, act=act, seed=41, device=DEV)
+    st, (o, dq, dwk, dwv) = run_pffn(inp, act, bins=(bins,) * 3)
+    if Tq and M and bins:
+        assert st["n_parts"][1] > 0   # the weight gradients are reduced over chunks
+    q, wk, wv, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    check_close(o, R.pffn_fwd(q, wk, wv, act), f"pFFN O d={d}")
+    for name, a, b in zip(("dQ", "dW_K", "dW_V"), (dq, dwk, dwv), R.pffn_bwd(q, wk, wv, do, act)):
+        check_close(a, b, f"pFFN {name} d={d}")
+
+
+def test_pffn_rejects_a_jagged_plan():
+    inp = make_from_lengths([5, 7], [3, 4], 2, 64, act="silu", seed=1, device=DEV)
+    with G.Plan(inp.q_off, inp.kv_off, 2, 64, 0, "bf16") as plan:
+        with pytest.raises(G.GdpaError) as e:
+            G.gdpa_pffn_fwd(plan.handle, inp.q, inp.k, inp.v, "silu", torch.empty_like(inp.q))
+        assert G.STATUS[e.value.status] == "GDPA_ERR_PLAN_MISMATCH"
+
+
 @pytest.mark.parametrize("act", ["gelu", "silu", "gelu_taylor6", "identity"])
 def test_one_pass_backward_activations(act):
     say(f"one-pass backward activation {act}")

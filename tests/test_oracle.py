@@ -293,3 +293,48 @@ def test_pins_catch_a_missing_scale(monkeypatch):
     monkeypatch.setattr(R.math, "sqrt", lambda x: 1.0 if x in (4, 16) else math.pow(x, 0.5))
     with pytest.raises(AssertionError):
         test_jagged_equals_padded_dense_library("gelu", 0)
+
+
+# ---------------------------------------------------------------------------
+# pFFN as GDPA (shared weight rows for every query row)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+def test_pffn_equals_per_sample_gdpa_with_replicated_weights(act):
+    """Reading of the unified-modules diagram: every query row of every sample uses
+    the same weight rows.  The one-sample form must equal jagged GDPA in which each
+    sample gets its own copy of the weights, and the weight gradients must be the
+    sums of the per-sample key/value gradients."""
+    rng = np.random.default_rng(7)
+    lq, M, H, d = [5, 0, 17, 9], 6, 2, 8
+    tq = sum(lq)
+    q = rng.standard_normal((tq, H, d))
+    wk = rng.standard_normal((M, H, d))
+    wv = rng.standard_normal((M, H, d))
+    do = rng.standard_normal((tq, H, d))
+    B = len(lq)
+    q_off = np.concatenate([[0], np.cumsum(lq)])
+    kv_off = np.arange(B + 1) * M
+    kr, vr = np.concatenate([wk] * B), np.concatenate([wv] * B)
+    o = R.pffn_fwd(q, wk, wv, act)
+    np.testing.assert_allclose(o, R.gdpa_fwd(q, kr, vr, q_off, kv_off, act), rtol=1e-12, atol=1e-12)
+    dq, dwk, dwv = R.pffn_bwd(q, wk, wv, do, act)
+    gq, gk, gv = R.gdpa_bwd(q, kr, vr, do, q_off, kv_off, act)
+    np.testing.assert_allclose(dq, gq, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dwk, gk.reshape(B, M, H, d).sum(0), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dwv, gv.reshape(B, M, H, d).sum(0), rtol=1e-12, atol=1e-12)
+
+
+def test_pffn_identity_is_two_matrix_products():
+    """With act = identity, pFFN is (Q W_K^T / sqrt(d)) W_V per head: two plain
+    matrix products by a library routine (numpy matmul), and its weight gradient
+    dW_V = P^T dO."""
+    rng = np.random.default_rng(8)
+    tq, M, H, d = 23, 7, 3, 16
+    q, wk, wv, do = (rng.standard_normal(s) for s in ((tq, H, d), (M, H, d), (M, H, d), (tq, H, d)))
+    o = R.pffn_fwd(q, wk, wv, "identity")
+    _, _, dwv = R.pffn_bwd(q, wk, wv, do, "identity")
+    for h in range(H):
+        p = q[:, h] @ wk[:, h].T / np.sqrt(d)
+        np.testing.assert_allclose(o[:, h], p @ wv[:, h], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dwv[:, h], p.T @ do[:, h], rtol=1e-12, atol=1e-12)

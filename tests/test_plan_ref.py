@@ -212,3 +212,16 @@ def test_kv_stationary_chunks_group_key_rows():
     g = PR.groups(pl, [0, 3, 35])
     assert [(r0, rows, h) for r0, rows, h, _, _ in g] == [(3, 32, 0), (3, 32, 1)]
     assert sum(n for *_, n in g) == pl["n_parts"]
+
+
+def test_few_items_are_cut_to_quarter_bins():
+    """Fewer items than 2 P: 20 KV-stationary items over 16 bins, each 32 key rows
+    streaming 1000 queries, cost 32 + 31 * (32 + 32) + (8 + 32) = 2056 (mean bin cost
+    ceil(41120 / 16) = 2570).  Whole, two land in one bin; so every item above a
+    quarter bin (643) is cut, into ceil(2056 / 643) = 4 chunks."""
+    lq, lk = [1000], [300]
+    pl = PR.plan_list("dkdv", lq, lk, 2, 0, 16, 1, 1)
+    assert len(pl["items"]) == 80 and pl["n_parts"] == 80
+    whole = PR.plan_list("dkdv", lq, lk, 2, 0, 16, 1, 1, split=False)
+    assert max(whole["bin_cost"]) == 2 * 2056
+    assert max(pl["bin_cost"]) <= 1.1 * sum(pl["bin_cost"]) / 16
