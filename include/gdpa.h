@@ -204,6 +204,22 @@ gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void
                         gdpa_act act, int window, void* dq, void* stream);
 
 /*
+ * gdpa_jfa_fwd - jagged softmax attention (JFA) on a GDPA plan: over the same valid
+ * pairs, P_ij = exp(S_ij - LSE_i) with LSE_i = log sum_j exp(S_ij) over row i's valid
+ * keys, O = P V (the softmax's row max, row sum and rescale that GDPA drops; GDPA
+ * page, "Section details"; GEM page on jagged attention kernels).  Arguments as
+ * gdpa_fwd without act, plus
+ *   lse : device fp32 [H, Tq] (head-major), written: LSE of each row, -inf for rows
+ *         with no valid key (their O rows are 0).
+ * The plan must be bf16 and its forward items whole (create it with
+ * opts->no_split = 1 when the planner would cut them; UNSUPPORTED otherwise).
+ * Errors as gdpa_fwd.
+ */
+gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v, const int32_t* q_off_dev,
+                         const int32_t* kv_off_dev, int B, int H, int d, int window, void* o, float* lse,
+                         void* stream);
+
+/*
  * pFFN as GDPA (GDPA page, "Section details", diagram of self-attention, PMA and
  * pFFN unified as GDPA).  The page gives no formula; read here as: per head,
  * weight matrices W_K, W_V [M, H, d] shared by every query row of the batch,

@@ -272,3 +272,77 @@ def pffn_bwd(q, wk, wv, do, act: str):
     """(dQ, dW_K, dW_V) in fp64 for the loss sum(O * dO)."""
     tq, m = q.shape[0], wk.shape[0]
     return gdpa_bwd(q, wk, wv, do, np.array([0, tq]), np.array([0, m]), act, 0)
+
+
+# ---------------------------------------------------------------------------
+# JFA: softmax attention on the same jagged pairs
+# ---------------------------------------------------------------------------
+# GEM page, section "why high GPU utilisation is hard" (jagged attention kernels)
+# and GDPA page, "Section details" (GDPA drops the softmax's row max, row sum and
+# correction; JFA is the variant that keeps them).  Per sample b, head h, over the
+# same valid set V_b: P_ij = exp(S_ij) / sum_{j' : (i, j') in V_b} exp(S_ij'), O = P V.
+# A row with no valid key has O = 0 and log-sum-exp -inf.  Backward for
+# l = sum(O * dO): dP = dO V^T, D_i = sum_e dO_ie O_ie, dS = P (dP - D), then dV, dQ,
+# dK as for GDPA.
+
+def jfa_fwd(q, k, v, q_off, kv_off, window: int = 0):
+    """(O [Tq, H, d], LSE [H, Tq]) in fp64; LSE_i = log sum_j exp(S_ij) over the valid keys."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, window)
+    d, H = q.shape[2], q.shape[1]
+    scale = 1.0 / math.sqrt(d)
+    o = np.zeros_like(q)
+    lse = np.full((H, q.shape[0]), -np.inf)
+    for b in range(len(q_off) - 1):
+        qs, lq = int(q_off[b]), int(q_off[b + 1] - q_off[b])
+        ks, lk = int(kv_off[b]), int(kv_off[b + 1] - kv_off[b])
+        if lq == 0 or lk == 0:
+            continue
+        for i0, i1, j0, j1 in _row_groups(lq, lk, window):
+            qh = q[qs + i0:qs + i1].transpose(1, 0, 2)
+            kh = k[ks + j0:ks + j1].transpose(1, 0, 2)
+            vh = v[ks + j0:ks + j1].transpose(1, 0, 2)
+            m = valid_mask(np.arange(i0, i1), np.arange(j0, j1), lq, lk, window)
+            s = np.where(m, np.matmul(qh, kh.transpose(0, 2, 1)) * scale, -np.inf)
+            mx = s.max(axis=2, keepdims=True)
+            e = np.exp(s - mx)                                  # exp(-inf) = 0 off the valid set
+            tot = e.sum(axis=2, keepdims=True)
+            o[qs + i0:qs + i1] = np.matmul(e / tot, vh).transpose(1, 0, 2)
+            lse[:, qs + i0:qs + i1] = (mx + np.log(tot))[:, :, 0]
+    return o, lse
+
+
+def jfa_bwd(q, k, v, do, q_off, kv_off, window: int = 0):
+    """(dQ, dK, dV) in fp64 for the loss sum(O * dO) of jfa_fwd."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    q_off, kv_off = _check(q, k, v, q_off, kv_off, window)
+    o, lse = jfa_fwd(q, k, v, q_off, kv_off, window)
+    d = q.shape[2]
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(q_off) - 1):
+        qs, lq = int(q_off[b]), int(q_off[b + 1] - q_off[b])
+        ks, lk = int(kv_off[b]), int(kv_off[b + 1] - kv_off[b])
+        if lq == 0 or lk == 0:
+            continue
+        for i0, i1, j0, j1 in _row_groups(lq, lk, window):
+            qh = q[qs + i0:qs + i1].transpose(1, 0, 2)
+            kh = k[ks + j0:ks + j1].transpose(1, 0, 2)
+            vh = v[ks + j0:ks + j1].transpose(1, 0, 2)
+            doh = do[qs + i0:qs + i1].transpose(1, 0, 2)
+            oh = o[qs + i0:qs + i1].transpose(1, 0, 2)
+            m = valid_mask(np.arange(i0, i1), np.arange(j0, j1), lq, lk, window)
+            s = np.matmul(qh, kh.transpose(0, 2, 1)) * scale
+            p = np.where(m, np.exp(s - lse[:, qs + i0:qs + i1, None]), 0.0)
+            dp = np.matmul(doh, vh.transpose(0, 2, 1))
+            dd = (doh * oh).sum(axis=2, keepdims=True)          # D_i
+            ds = p * (dp - dd)
+            dq[qs + i0:qs + i1] += (np.matmul(ds, kh) * scale).transpose(1, 0, 2)
+            dk[ks + j0:ks + j1] += (np.matmul(ds.transpose(0, 2, 1), qh) * scale).transpose(1, 0, 2)
+            dv[ks + j0:ks + j1] += np.matmul(p.transpose(0, 2, 1), doh).transpose(1, 0, 2)
+    return dq, dk, dv

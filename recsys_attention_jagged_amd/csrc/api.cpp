@@ -484,6 +484,41 @@ gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void
                      stream, false, true);
 }
 
+gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v, const int32_t* q_off_dev,
+                         const int32_t* kv_off_dev, int B, int H, int d, int window, void* o, float* lse,
+                         void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
+    if (st != GDPA_OK) return st;
+    if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "JFA runs on bf16 plans");
+    if (plan->lists[LIST_FWD].n_parts > 0)
+        return fail(GDPA_ERR_UNSUPPORTED, "JFA needs a plan whose forward items are whole (opts.no_split = 1)");
+    if (plan->Tq > 0 && (!q || !o || !lse)) return fail(GDPA_ERR_INVALID_ARG, "q, o or lse is NULL");
+    if (plan->Tk > 0 && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
+    if (plan->Tq == 0) return GDPA_OK;
+    hipStream_t s = (hipStream_t)stream;
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.Tq = (int)plan->Tq;
+    const WorkList& wl = plan->lists[LIST_FWD];
+    a.items = plan->d_items[LIST_FWD];
+    a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+    a.P = wl.P;
+    hipError_t e;
+    switch (d) {
+        case 32: e = launch_fwd_bf16_d32(a, wl.team, wl.nb, kActSoftmax, s); break;
+        case 64: e = launch_fwd_bf16_d64(a, wl.team, wl.nb, kActSoftmax, s); break;
+        default: e = launch_fwd_bf16_d128(a, wl.team, wl.nb, kActSoftmax, s); break;
+    }
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no forward kernel for this configuration");
+    if (e != hipSuccess) return fail_hip(e, "JFA forward launch");
+    return GDPA_OK;
+}
+
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,
                                   gdpa_plan* out) {
     g_err.clear();

@@ -30,7 +30,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-enum Act { ACT_GELU = 0, ACT_SILU = 1, ACT_GELU_POLY = 2, ACT_GELU_TAYLOR6 = 3, ACT_IDENTITY = 4, ACT_ONE = 5 };
+enum Act { ACT_GELU = 0, ACT_SILU = 1, ACT_GELU_POLY = 2, ACT_GELU_TAYLOR6 = 3, ACT_IDENTITY = 4, ACT_ONE = 5,
+           ACT_SOFTMAX = 6 };   // softmax: jagged softmax attention (JFA) through the same kernels
+
+// running-max sentinel of the softmax kernels: finite, so that differences of two
+// sentinels are 0, not NaN
+constexpr float kNegBig = -1.0e30f;
 
 // -------------------------------------------------------------------------
 // buffer resources

@@ -16,6 +16,12 @@
 // the B operand of O^T += V^T P^T (V^T read from the row-major V tile with
 // transposing LDS reads).  Rows beyond a sample's lengths are zero tiles, so only
 // the local window needs a mask.
+//
+// The same kernels run jagged softmax attention (JFA, act = softmax): the block's
+// scores go through an online softmax (running max and sum per q row, the O
+// accumulator rescaled when the max moves) instead of the activation; there the
+// keys beyond a sample's length are masked too, and the item's end divides by the
+// row sum and stores the row's log-sum-exp.
 #include "kernels.hpp"
 #include "ring.hpp"
 
@@ -40,6 +46,9 @@ struct FwdPol {
     rsrc_t wq, wk, wv;    // issuing side: slices of the walk's current item
     bf16x8 qf[NB][NKS];
     f32x16 acc[NB][NDB];
+    // softmax only: running max (log2 units) of this lane's q row and this lane's
+    // share of the running sum (the other share sits in lane ^ 32)
+    float mrow[NB], lrow[NB];
 
     __device__ FwdPol(const KernelArgs& args, int lane_, int wt_) : a(args) {
         lane = lane_;
@@ -75,9 +84,53 @@ struct FwdPol {
 
     __device__ __forceinline__ void item_begin(const Rec&) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[b][db] = f32x16{};
+            mrow[b] = kNegBig;
+            lrow[b] = 0.0f;
+        }
+    }
+
+    // Online softmax of one 32 x 32 block (JFA): lane column = query q0 + r, element
+    // e = key j0 + 8 (e/4) + 4 hh + e % 4.  Keys outside the sample or the window are
+    // masked (zero tiles give S = 0, and exp(0) is not 0).  The running max moves to
+    // the block's max; the accumulator and the running sum are rescaled when it does.
+    __device__ __forceinline__ void softmax_block(int b, const f32x16& sc, int q0, int j0, int lk, f32x16& p) {
+        constexpr float L2E = 1.4426950408889634f;
+        const bool tail = j0 + 32 > lk;
+        const bool band = win > 0 && !band_all(q0, j0, win);
+        float mt = kNegBig;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {   // p holds the scores in log2 units first
+            const int jr = 8 * (e >> 2) + 4 * hh + (e & 3);
+            bool ok = true;
+            if (tail) ok = j0 + jr < lk;
+            if (band) {
+                const int dd = q0 + r - j0 - jr;
+                ok = ok && dd < win && -dd < win;
+            }
+            p[e] = ok ? sc[e] * (scale * L2E) : kNegBig;
+            mt = __builtin_fmaxf(mt, p[e]);
+        }
+        mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = __builtin_fmaxf(mrow[b], mt);
+        const float alpha = fast_exp2(mrow[b] - mn);   // 1 while the max stays, 0 from the sentinel
+        mrow[b] = mn;
+        float ls = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            p[e] = p[e] > 0.5f * kNegBig ? fast_exp2(p[e] - mn) : 0.0f;
+            ls += p[e];
+        }
+        lrow[b] = __builtin_fmaf(lrow[b], alpha, ls);
+        // rescale only when some row's max moved (every lane of the wave agrees on the branch)
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[b][db][e] *= alpha;
+        }
     }
 
     // stationary tiles i, i + 1 (jobs job, job + 1): tile u belongs to wave u / NB, block u % NB
@@ -123,7 +176,9 @@ struct FwdPol {
         for (int b = 0; b < NB; ++b) {
             const int q0 = qrow(c, b);
             f32x16 p;
-            if (win > 0 && !band_all(q0, j0, win)) {
+            if constexpr (ACT == ACT_SOFTMAX) {
+                softmax_block(b, sc[b], q0, j0, c.lk, p);
+            } else if (win > 0 && !band_all(q0, j0, win)) {
                 // lane column: query q0 + r; element c: key j0 + 8 (c/4) + 4 hh + c % 4
                 const int base = q0 + r - j0 - 4 * hh;
 #pragma unroll
@@ -150,6 +205,18 @@ struct FwdPol {
 
     // this wave's blocks, staged through a slot of the last step (one slot per wave
     // in a team; blocks sharing a slot are staged one after the other)
+    // softmax: this lane's row sum (both halves), the output scale 1 / sum, and the
+    // row's log-sum-exp stored by the lanes of the first half (rows without keys:
+    // O = 0 and LSE = -inf)
+    __device__ __forceinline__ float softmax_finish(const Rec& c, int b) {
+        const float l = lrow[b] + __shfl_xor(lrow[b], 32);
+        const int row = qrow(c, b) + r;
+        if (hh == 0 && row < c.lq)
+            a.lse[(size_t)c.h * a.Tq + c.qs + row] =
+                l > 0.0f ? (mrow[b] + __builtin_amdgcn_logf(l)) * 0.69314718055994531f : -__builtin_inff();
+        return l > 0.0f ? 1.0f / l : 0.0f;
+    }
+
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
         if (c.part >= 0) {   // one chunk of a cut item: fp32 partial block
@@ -158,23 +225,34 @@ struct FwdPol {
             return;
         }
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
+        float mul[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) mul[b] = ACT == ACT_SOFTMAX ? softmax_finish(c, b) : 1.0f;
         if (a.out_f32) {
             const rsrc_t ro = slice_rsrc((const float*)a.o + ob, c.lq, rso, D * 4);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) store_block_f32<NDB>(acc[b], 1.0f, ro, (uint32_t)(qrow(c, b) + r) * rso, hh);
+            for (int b = 0; b < NB; ++b) store_block_f32<NDB>(acc[b], mul[b], ro, (uint32_t)(qrow(c, b) + r) * rso, hh);
             return;
         }
         const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, c.lq, rso, D * 2);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             char* st = g.tile(job - 2 + (T > 1 ? wt : (b & 1)));
-            stage_block<D>(acc[b], 1.0f, st, r, hh);
+            stage_block<D>(acc[b], mul[b], st, r, hh);
             store_tile<D>(st, ro, (uint32_t)qrow(c, b) * rso, rso, lane);
         }
     }
 
-    // an item without keys: its rows are zero
+    // an item without keys: its rows are zero (softmax: and their LSE -inf)
     __device__ __forceinline__ void item_zero(const Rec& c) {
+        if constexpr (ACT == ACT_SOFTMAX) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                lrow[b] = 0.0f;
+                mrow[b] = kNegBig;
+                (void)softmax_finish(c, b);
+            }
+        }
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
         if (a.out_f32) {
             item_begin(c);
@@ -214,6 +292,7 @@ const void* kptr_act(int act) {
         case ACT_GELU_TAYLOR6: return kptr<T, NB, ACT_GELU_TAYLOR6>();
         case ACT_IDENTITY: return kptr<T, NB, ACT_IDENTITY>();
         case ACT_ONE: return kptr<T, NB, ACT_ONE>();
+        case ACT_SOFTMAX: return kptr<T, NB, ACT_SOFTMAX>();
     }
     return nullptr;
 }

@@ -31,7 +31,14 @@ struct KernelArgs {
     int window;     // 0 = none
     float scale;    // 1 / sqrt(d)
     int out_f32;    // outputs stored as fp32 instead of bf16
+    // softmax attention (JFA) only: per-row log-sum-exp, fp32 [H, Tq] (head-major)
+    float* lse;
+    int Tq;
 };
+
+// the activation code of the softmax (JFA) variant of the bf16 kernels (device
+// enum Act::ACT_SOFTMAX); the public activations are gdpa_act
+constexpr int kActSoftmax = 6;
 
 // bf16 MFMA kernels, one translation unit per head dimension.  A workgroup is a
 // team of `team` waves (1, or 2 for d = 128) working on one bin (P bins, P

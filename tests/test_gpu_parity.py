@@ -236,6 +236,68 @@ def test_cut_items(d, case, deal):
 
 
 # ---------------------------------------------------------------------------
+# JFA: jagged softmax attention through the same kernels
+# ---------------------------------------------------------------------------
+
+def run_jfa_fwd(inp, dtype="bf16", **opts):
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, dtype, split=False, **opts) as plan:
+        o = torch.empty(inp.q.shape, dtype=torch.float32 if dtype == "bf16_f32out" else torch.bfloat16, device=DEV)
+        lse = torch.empty((inp.H, inp.q.shape[0]), dtype=torch.float32, device=DEV)
+        G.gdpa_jfa_fwd(plan.handle, inp.q, inp.k, inp.v, qo, ko, plan.B, inp.H, inp.d, inp.window, o, lse)
+        torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def check_lse(got, ref, what):
+    """Row log-sum-exp: -inf exactly where the oracle has no valid key, else within 1e-3."""
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{what}: -inf rows differ"
+    fin = np.isfinite(ref)
+    assert np.all(np.isfinite(got[fin])), f"{what}: non-finite LSE"
+    err = float(np.max(np.abs(got[fin] - ref[fin]), initial=0.0))
+    assert err <= 1e-3, f"{what}: max LSE error {err:.2e}"
+
+
+JFA_LQ = [5, 0, 70, 1, 33, 200, 31, 96, 7]
+JFA_LK = [64, 3, 0, 2, 129, 31, 300, 96, 1]
+
+
+@pytest.mark.parametrize("d,team,nb", FWD_LAYOUTS)
+def test_jfa_forward_layouts(d, team, nb):
+    say(f"JFA forward d={d} team={team} blocks={nb}")
+    inp = make_from_lengths(JFA_LQ, JFA_LK, 2, d, act="gelu", seed=51, device=DEV)
+    o, lse = run_jfa_fwd(inp, team=(team, 0, 0), blocks=(nb, 0, 0))
+    ro, rl = R.jfa_fwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_off, inp.kv_off, 0)
+    check_close(o, ro, f"JFA O d={d}")
+    check_lse(lse, rl, f"JFA LSE d={d}")
+    o32, lse32 = run_jfa_fwd(inp, dtype="bf16_f32out", team=(team, 0, 0), blocks=(nb, 0, 0))
+    check_close(o32, ro, f"JFA O f32out d={d}")
+
+
+@pytest.mark.parametrize("window", [1, 2, 17, 128])
+def test_jfa_forward_windows(window):
+    say(f"JFA forward window={window}")
+    L = [1, 31, 32, 33, 127, 300, 0, 65]
+    inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, seed=52, device=DEV)
+    o, lse = run_jfa_fwd(inp)
+    ro, rl = R.jfa_fwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_off, inp.kv_off, window)
+    check_close(o, ro, f"JFA O window={window}")
+    check_lse(lse, rl, f"JFA LSE window={window}")
+
+
+def test_jfa_rejects_cut_forward_items():
+    inp = make_from_lengths([32, 1], [3000, 5], 2, 64, act="gelu", seed=53, device=DEV)
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, 2, 64, 0, "bf16", bins=(16, 16, 16)) as plan:
+        assert plan.stats()["n_parts"][0] > 0
+        o = torch.empty_like(inp.q)
+        lse = torch.empty((2, 33), dtype=torch.float32, device=DEV)
+        with pytest.raises(G.GdpaError) as e:
+            G.gdpa_jfa_fwd(plan.handle, inp.q, inp.k, inp.v, qo, ko, 2, 2, 64, 0, o, lse)
+        assert G.STATUS[e.value.status] == "GDPA_ERR_UNSUPPORTED"
+
+
+# ---------------------------------------------------------------------------
 # pFFN as GDPA: every query row against the same M weight rows
 # ---------------------------------------------------------------------------
 

@@ -338,3 +338,70 @@ def test_pffn_identity_is_two_matrix_products():
         p = q[:, h] @ wk[:, h].T / np.sqrt(d)
         np.testing.assert_allclose(o[:, h], p @ wv[:, h], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(dwv[:, h], p.T @ do[:, h], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# JFA: softmax attention on the jagged pairs
+# ---------------------------------------------------------------------------
+
+JFA_CASES = [
+    ([5, 0, 17, 9, 33], [3, 4, 21, 0, 40], 0),
+    ([12, 1, 30], [12, 1, 30], 4),
+]
+
+
+@pytest.mark.parametrize("lq,lk,window", JFA_CASES)
+def test_jfa_equals_torch_sdpa_per_sample(lq, lk, window):
+    """The oracle's jagged softmax attention equals the library routine
+    (torch scaled_dot_product_attention, fp64, dense per sample with a boolean
+    mask of the valid pairs); rows without keys give O = 0 and LSE = -inf; LSE is
+    scipy's logsumexp of the masked scores."""
+    import torch
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(11)
+    H, d = 2, 8
+    q_off = np.concatenate([[0], np.cumsum(lq)])
+    kv_off = np.concatenate([[0], np.cumsum(lk)])
+    q, do = rng.standard_normal((q_off[-1], H, d)), rng.standard_normal((q_off[-1], H, d))
+    k, v = rng.standard_normal((kv_off[-1], H, d)), rng.standard_normal((kv_off[-1], H, d))
+    o, lse = R.jfa_fwd(q, k, v, q_off, kv_off, window)
+    for b in range(len(lq)):
+        qs, qe, ks, ke = q_off[b], q_off[b + 1], kv_off[b], kv_off[b + 1]
+        if lq[b] == 0:
+            continue
+        if lk[b] == 0:
+            assert np.all(o[qs:qe] == 0) and np.all(np.isneginf(lse[:, qs:qe]))
+            continue
+        m = R.valid_mask(np.arange(lq[b]), np.arange(lk[b]), lq[b], lk[b], window)
+        t = lambda x: torch.tensor(x.transpose(1, 0, 2))
+        ref = torch.nn.functional.scaled_dot_product_attention(t(q[qs:qe]), t(k[ks:ke]), t(v[ks:ke]),
+                                                               attn_mask=torch.tensor(m)[None])
+        np.testing.assert_allclose(o[qs:qe], ref.numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+        s = np.einsum("ihe,jhe->hij", q[qs:qe], k[ks:ke]) / np.sqrt(d)
+        np.testing.assert_allclose(lse[:, qs:qe], logsumexp(np.where(m, s, -np.inf), axis=2), rtol=1e-12)
+
+
+@pytest.mark.parametrize("lq,lk,window", JFA_CASES)
+def test_jfa_backward_equals_torch_autograd(lq, lk, window):
+    """Gradients of sum(O * dO) against torch autograd through fp64
+    scaled_dot_product_attention, sample by sample."""
+    import torch
+    rng = np.random.default_rng(12)
+    H, d = 2, 8
+    q_off = np.concatenate([[0], np.cumsum(lq)])
+    kv_off = np.concatenate([[0], np.cumsum(lk)])
+    q, do = rng.standard_normal((q_off[-1], H, d)), rng.standard_normal((q_off[-1], H, d))
+    k, v = rng.standard_normal((kv_off[-1], H, d)), rng.standard_normal((kv_off[-1], H, d))
+    dq, dk, dv = R.jfa_bwd(q, k, v, do, q_off, kv_off, window)
+    for b in range(len(lq)):
+        qs, qe, ks, ke = q_off[b], q_off[b + 1], kv_off[b], kv_off[b + 1]
+        if lq[b] == 0 or lk[b] == 0:
+            assert np.all(dq[qs:qe] == 0) and np.all(dk[ks:ke] == 0) and np.all(dv[ks:ke] == 0)
+            continue
+        m = R.valid_mask(np.arange(lq[b]), np.arange(lk[b]), lq[b], lk[b], window)
+        t = lambda x: torch.tensor(x.transpose(1, 0, 2), requires_grad=True)
+        tq, tk, tv = t(q[qs:qe]), t(k[ks:ke]), t(v[ks:ke])
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(m)[None])
+        (ref * torch.tensor(do[qs:qe].transpose(1, 0, 2))).sum().backward()
+        for got, want in ((dq[qs:qe], tq.grad), (dk[ks:ke], tk.grad), (dv[ks:ke], tv.grad)):
+            np.testing.assert_allclose(got, want.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
