@@ -220,6 +220,24 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
                          void* stream);
 
 /*
+ * gdpa_jfa_bwd - gradients of sum(O * dO) for gdpa_jfa_fwd: with the forward's
+ * O and LSE, P_ij = exp(S_ij - LSE_i) on the valid pairs, D_i = sum_c dO_ic O_ic,
+ * dS = P * (dO V^T - D_i) (the softmax Jacobian; GEM page on jagged attention
+ * kernels, backward of the fused attention), dV = P^T dO, dK = dS^T Q / sqrt(d),
+ * dQ = dS K / sqrt(d).  Arguments as gdpa_bwd without act, plus
+ *   o, lse : the forward's outputs (bf16 [Tq,H,d]; fp32 [H,Tq]), read;
+ *   stat   : device fp32 [H, Tq, 2], caller-owned scratch, written: per (head, q
+ *            row) the pair (LSE_i log2(e), D_i) that the gradient kernels read.
+ * Enqueues a row-statistics pre-pass, the KV-stationary dK/dV kernel and the
+ * Q-stationary dQ kernel (never the one-pass kernels), plus the chunk reductions
+ * of cut items.  The plan must be bf16 with one-wave dQ and dK/dV teams (the
+ * automatic layouts; UNSUPPORTED otherwise).  Errors as gdpa_bwd.
+ */
+gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
+                         int B, int H, int d, int window, float* stat, void* dq, void* dk, void* dv, void* stream);
+
+/*
  * pFFN as GDPA (GDPA page, "Section details", diagram of self-attention, PMA and
  * pFFN unified as GDPA).  The page gives no formula; read here as: per head,
  * weight matrices W_K, W_V [M, H, d] shared by every query row of the batch,

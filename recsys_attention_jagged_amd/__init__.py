@@ -81,12 +81,14 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_gelu_poly_bound.argtypes = []
     lib.gdpa_gelu_poly_bound.restype = ctypes.c_double
     lib.gdpa_jfa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
+    lib.gdpa_jfa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                 _vp]
     lib.gdpa_pffn_plan_create.argtypes = [_i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts), ctypes.POINTER(_vp)]
     lib.gdpa_pffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
     lib.gdpa_pffn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp]
     for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
                  "gdpa_plan_export", "gdpa_plan_stats", "gdpa_pffn_plan_create", "gdpa_pffn_fwd",
-                 "gdpa_pffn_bwd", "gdpa_jfa_fwd"):
+                 "gdpa_pffn_bwd", "gdpa_jfa_fwd", "gdpa_jfa_bwd"):
         getattr(lib, name).restype = _i
     if path == LIB_PATH:
         _lib = lib
@@ -170,6 +172,14 @@ def gdpa_jfa_fwd(plan, q, k, v, q_off_dev, kv_off_dev, B, H, d, window, o, lse, 
     """Jagged softmax attention: O [Tq, H, d] and LSE fp32 [H, Tq]."""
     _check(load_library().gdpa_jfa_fwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(q_off_dev), _ptr(kv_off_dev),
                                        B, H, d, window, _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def gdpa_jfa_bwd(plan, q, k, v, o, lse, dout, q_off_dev, kv_off_dev, B, H, d, window, stat, dq, dk, dv,
+                 stream=None):
+    """Gradients of jagged softmax attention from its O and LSE; stat is fp32 [H, Tq, 2] scratch."""
+    _check(load_library().gdpa_jfa_bwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                       _ptr(q_off_dev), _ptr(kv_off_dev), B, H, d, window, _ptr(stat), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def _opts(host_only, bins, team, blocks, deal, split, unfused):

@@ -36,7 +36,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 UNITS = [("plan.o", "plan.cpp", []),
          ("api.o", "api.cpp", []),
          ("fp32.o", "fp32.hip", []),
-         ("partials.o", "partials.hip", [])]
+         ("partials.o", "partials.hip", []),
+         ("jfa.o", "jfa.hip", [])]
 for _d in (32, 64, 128):
     UNITS.append((f"fwd_d{_d}.o", "fwd_bf16.hip", [f"-DGDPA_D={_d}"]))
     UNITS.append((f"bwd_d{_d}.o", "bwd_bf16.hip", [f"-DGDPA_D={_d}"]))

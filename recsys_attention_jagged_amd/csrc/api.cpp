@@ -519,6 +519,65 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
     return GDPA_OK;
 }
 
+gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
+                         int B, int H, int d, int window, float* stat, void* dq, void* dk, void* dv, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
+    if (st != GDPA_OK) return st;
+    if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "JFA runs on bf16 plans");
+    if (plan->lists[LIST_DQ].team != 1 || plan->lists[LIST_DKDV].team != 1)
+        return fail(GDPA_ERR_UNSUPPORTED, "the JFA backward runs one-wave dQ and dK/dV teams");
+    const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
+    if (any_q && (!q || !o || !lse || !dout || !stat || !dq))
+        return fail(GDPA_ERR_INVALID_ARG, "q, o, lse, dout, stat or dq is NULL");
+    if (any_k && (!k || !v || !dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "k, v, dk or dv is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.stat = stat;
+    a.Tq = (int)plan->Tq;
+    hipError_t e = launch_jfa_stat(o, dout, lse, (int)plan->Tq, H, d, stat, s);
+    if (e == hipSuccess && any_k) {
+        const WorkList& wl = plan->lists[LIST_DKDV];
+        KernelArgs b = a;
+        b.items = plan->d_items[LIST_DKDV];
+        b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+        b.P = wl.P;
+        b.part = plan->d_part[LIST_DKDV];
+        switch (d) {
+            case 32: e = launch_dkdv_bf16_d32(b, wl.team, wl.nb, kActSoftmax, s); break;
+            case 64: e = launch_dkdv_bf16_d64(b, wl.team, wl.nb, kActSoftmax, s); break;
+            default: e = launch_dkdv_bf16_d128(b, wl.team, wl.nb, kActSoftmax, s); break;
+        }
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
+    }
+    if (e == hipSuccess && any_q) {
+        const WorkList& wl = plan->lists[LIST_DQ];
+        KernelArgs b = a;
+        b.items = plan->d_items[LIST_DQ];
+        b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+        b.P = wl.P;
+        b.part = plan->d_part[LIST_DQ];
+        switch (d) {
+            case 32: e = launch_dq_bf16_d32(b, wl.team, wl.nb, kActSoftmax, s); break;
+            case 64: e = launch_dq_bf16_d64(b, wl.team, wl.nb, kActSoftmax, s); break;
+            default: e = launch_dq_bf16_d128(b, wl.team, wl.nb, kActSoftmax, s); break;
+        }
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
+    }
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no JFA backward kernel for this configuration");
+    if (e != hipSuccess) return fail_hip(e, "JFA backward launch");
+    return GDPA_OK;
+}
+
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,
                                   gdpa_plan* out) {
     g_err.clear();

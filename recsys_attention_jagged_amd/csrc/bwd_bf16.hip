@@ -21,6 +21,15 @@
 //            read from the row-major tiles with transposing LDS reads.
 // Rows beyond a sample's lengths are zero tiles (their P, dS and products
 // vanish), so only the local window needs a mask.
+//
+// With act = softmax the same kernels run the backward of jagged softmax attention
+// (JFA): P = exp(S / sqrt(d) - LSE_i) from the forward's row log-sum-exp, and
+// dS = P * (dP - D_i) with D_i = sum_c dO_ic O_ic (the softmax Jacobian applied to
+// dP); dQ, dK and dV are then the products above.  The two row statistics of the
+// 32 q rows of a tile travel with it: one more load instruction per job brings
+// them into a side buffer of the tile's ring slot (ring.hpp), and jobs without
+// statistics load a zero-range side so that every job counts the same.  Keys past
+// a sample's length are masked in dQ: exp(0 - LSE) is not 0 there.
 #include "bwd_common.hpp"
 #include "kernels.hpp"
 #include "ring.hpp"
@@ -42,9 +51,12 @@ struct DqPol : Common {
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr int ROWS = 32 * T * NB;   // q rows per item
     static constexpr bool HOIST = TeamShape<D, T, 2>::HOIST;
+    static constexpr bool SM = ACT == ACT_SOFTMAX;
     rsrc_t wq, wo, wk, wv;   // issuing side
+    rsrc_t wst, wnull;       // softmax: row statistics of the item's q rows; a zero-range side
     bf16x8 qf[NB][NKS], of[NB][NKS];
     f32x16 acc[NB][NDB];
+    float l2q[NB], dq_[NB];  // softmax: this lane's q row's LSE log2(e) and D
 
     __device__ DqPol(const KernelArgs& args, int lane_, int wt_) : Common(args, lane_, wt_, D) {}
 
@@ -57,15 +69,29 @@ struct DqPol : Common {
         const size_t qb = ((size_t)w.qs * H + w.h) * D;
         wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
         wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        if constexpr (SM) {
+            wst = slice_rsrc(a.stat + ((size_t)w.h * a.Tq + w.qs) * 2, w.lq, 8u, 8u);
+            wnull = slice_rsrc(a.stat, 0, 8u, 8u);
+        }
+    }
+
+    // tile rows at byte offset `off` of `t`; softmax: and the side at x_off of `xs`
+    template <class RingT>
+    __device__ __forceinline__ void put(RingT& g, rsrc_t t, uint32_t off, rsrc_t xs, uint32_t x_off) {
+        if constexpr (SM)
+            g.issue(t, off, xs, x_off);
+        else
+            g.issue(t, off);
     }
 
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            g.issue((i & 1) ? wo : wq, (uint32_t)(w.t * ROWS + 32 * (i >> 1)) * rs);
+            const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * (i >> 1));
+            put(g, (i & 1) ? wo : wq, row0 * rs, (i & 1) ? wnull : wst, row0 * 8u);
         } else {
             const int rel = i - NSTAT;
-            g.issue((rel & 1) ? wv : wk, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
+            put(g, (rel & 1) ? wv : wk, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs, wnull, 0u);
         }
     }
 
@@ -86,6 +112,38 @@ struct DqPol : Common {
                 qf[blk % NB][ks] = lds_row8<D>(g.tile(job), r, 2 * ks + hh);
                 of[blk % NB][ks] = lds_row8<D>(g.tile(job + 1), r, 2 * ks + hh);
             }
+            if constexpr (SM) {   // the Q job's side: (LSE log2 e, D) of this lane's q row
+                const float2 st = *(const float2*)(g.side(job) + 8 * r);
+                l2q[blk % NB] = st.x;
+                dq_[blk % NB] = st.y;
+            }
+        }
+    }
+
+    // softmax dS^T of half m (keys j0 + 16 m ..) of block b: lane column = query q0 + r,
+    // element e = key j0 + 8 (e/4) + 4 hh + e % 4; keys past lk or outside the window are 0
+    __device__ __forceinline__ void softmax_ds(int b, int m, int q0, int j0, int lk, const f32x16& sc,
+                                               const f32x16& dp, bf16x8& dsb) const {
+        constexpr float L2E = 1.4426950408889634f;
+        const float c2 = scale * L2E;
+        const bool tail = j0 + 32 > lk;
+        const bool band = win > 0 && !band_all(q0, j0, win);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = 8 * m + k;
+            const float pe = fast_exp2(__builtin_fmaf(sc[e], c2, -l2q[b]));
+            float v = pe * (dp[e] - dq_[b]);
+            if (tail || band) {
+                const int jr = 8 * (e >> 2) + 4 * hh + (e & 3);
+                bool ok = true;
+                if (tail) ok = j0 + jr < lk;
+                if (band) {
+                    const int dd = q0 + r - j0 - jr;
+                    ok = ok && dd < win && -dd < win;
+                }
+                v = ok ? v : 0.0f;
+            }
+            dsb[k] = (__bf16)v;
         }
     }
 
@@ -123,7 +181,9 @@ struct DqPol : Common {
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int q0 = qrow(c, b);
-                if (win > 0 && !band_all(q0, j0, win)) {
+                if constexpr (SM) {
+                    softmax_ds(b, m, q0, j0, c.lk, sc[b], dp[b], dsb[b]);
+                } else if (win > 0 && !band_all(q0, j0, win)) {
                     // lane column: query q0 + r; element e: key j0 + 8 (e/4) + 4 hh + e % 4
                     const int base = q0 + r - j0 - 4 * hh;
 #pragma unroll
@@ -183,7 +243,9 @@ struct DkdvPol : Common {
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr int ROWS = 32 * T;   // kv rows per item
     static constexpr bool HOIST = TeamShape<D, T, 1>::HOIST;
+    static constexpr bool SM = ACT == ACT_SOFTMAX;
     rsrc_t wk, wv, wq, wo;   // issuing side
+    rsrc_t wst, wnull;       // softmax: row statistics of the item's q rows; a zero-range side
     bf16x8 kf[NKS], vf[NKS];
     f32x16 accK[NDB], accV[NDB];
 
@@ -198,15 +260,29 @@ struct DkdvPol : Common {
         const size_t qb = ((size_t)w.qs * H + w.h) * D;
         wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
         wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        if constexpr (SM) {
+            wst = slice_rsrc(a.stat + ((size_t)w.h * a.Tq + w.qs) * 2, w.lq, 8u, 8u);
+            wnull = slice_rsrc(a.stat, 0, 8u, 8u);
+        }
+    }
+
+    // tile rows at byte offset `off` of `t`; softmax: and the side at x_off of `xs`
+    template <class RingT>
+    __device__ __forceinline__ void put(RingT& g, rsrc_t t, uint32_t off, rsrc_t xs, uint32_t x_off) {
+        if constexpr (SM)
+            g.issue(t, off, xs, x_off);
+        else
+            g.issue(t, off);
     }
 
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            g.issue((i & 1) ? wv : wk, (uint32_t)(w.t * ROWS + 32 * (i >> 1)) * rs);
+            put(g, (i & 1) ? wv : wk, (uint32_t)(w.t * ROWS + 32 * (i >> 1)) * rs, wnull, 0u);
         } else {
             const int rel = i - NSTAT;
-            g.issue((rel & 1) ? wo : wq, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
+            const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
+            put(g, (rel & 1) ? wo : wq, row0 * rs, (rel & 1) ? wnull : wst, row0 * 8u);
         }
     }
 
@@ -232,6 +308,15 @@ struct DkdvPol : Common {
         const char* qt = g.tile(job);
         const char* ot = g.tile(job + 1);
         bf16x8 qop[NKS], oop[NKS];
+        // softmax: (LSE log2 e, D) of q rows i0 + 8 j + 4 hh + {0, 1} and {2, 3}, from the Q job's side
+        float4 st[SM ? 4 : 1][2];
+        if constexpr (SM) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                st[j][0] = *(const float4*)(g.side(job) + 8 * (8 * j + 4 * hh));
+                st[j][1] = *(const float4*)(g.side(job) + 8 * (8 * j + 4 * hh) + 16);
+            }
+        }
         if constexpr (HOIST) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -248,7 +333,27 @@ struct DkdvPol : Common {
         // accumulator lane: column = kv row j0 + r, element e: q row i0 + 8 (e/4) + 4 hh + e % 4
         const int i0 = s * 32, j0 = krow(c);
         f32x16 p, ds;
-        if (win > 0 && !band_all(i0, j0, win)) {
+        if constexpr (SM) {
+            constexpr float L2E = 1.4426950408889634f;
+            const float c2 = scale * L2E;
+            const bool band = win > 0 && !band_all(i0, j0, win);
+            const int base = i0 + 4 * hh - j0 - r;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float4& sv = st[e >> 2][(e >> 1) & 1];
+                const float l2 = (e & 1) ? sv.z : sv.x, dd = (e & 1) ? sv.w : sv.y;
+                float pe = fast_exp2(__builtin_fmaf(sc[e], c2, -l2));
+                float de = pe * (dp[e] - dd);
+                if (band) {
+                    const int k = base + 8 * (e >> 2) + (e & 3);
+                    const bool ok = k < win && -k < win;
+                    pe = ok ? pe : 0.0f;
+                    de = ok ? de : 0.0f;
+                }
+                p[e] = pe;
+                ds[e] = de;
+            }
+        } else if (win > 0 && !band_all(i0, j0, win)) {
             const int base = i0 + 4 * hh - j0 - r;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -301,7 +406,7 @@ struct DkdvPol : Common {
 template <int D, int T, int NB, int ACT>
 __global__ __launch_bounds__((TeamShape<D, T, 2>::THREADS), (TeamShape<D, T, 2>::WPE)) void dq_bf16_kernel(
     const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
-    using RingT = Ring<D, T, TeamShape<D, T, 2>::LDS>;
+    using RingT = Ring<D, T, TeamShape<D, T, 2>::LDS, ACT == ACT_SOFTMAX ? 1 : 0>;
     __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
     const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
@@ -312,7 +417,7 @@ __global__ __launch_bounds__((TeamShape<D, T, 2>::THREADS), (TeamShape<D, T, 2>:
 template <int D, int T, int ACT>
 __global__ __launch_bounds__((TeamShape<D, T, 1>::THREADS), (TeamShape<D, T, 1>::WPE)) void dkdv_bf16_kernel(
     const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
-    using RingT = Ring<D, T, TeamShape<D, T, 1>::LDS>;
+    using RingT = Ring<D, T, TeamShape<D, T, 1>::LDS, ACT == ACT_SOFTMAX ? 1 : 0>;
     __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
     const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
@@ -350,6 +455,11 @@ const void* dkdv_act(int act) { GDPA_ACT_SWITCH(dkdv_ptr, T, 1) }
 #define GDPA_CAT(a, b) GDPA_CAT2(a, b)
 
 const void* GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
+    if (act == ACT_SOFTMAX) {   // one-wave teams (the side buffers of the ring)
+        if (team == 1 && nb == 1) return dq_ptr<1, 1, ACT_SOFTMAX>();
+        if (team == 1 && nb == 2) return dq_ptr<1, 2, ACT_SOFTMAX>();
+        return nullptr;
+    }
     if (team == 1 && nb == 1) return dq_act<1, 1>(act);
     if (team == 1 && nb == 2) return dq_act<1, 2>(act);
 #if GDPA_D == 128
@@ -360,6 +470,7 @@ const void* GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
 
 const void* GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
     if (nb != 1) return nullptr;
+    if (act == ACT_SOFTMAX) return team == 1 ? dkdv_ptr<1, 1, ACT_SOFTMAX>() : nullptr;
     if (team == 1) return dkdv_act<1>(act);
 #if GDPA_D == 128
     if (team == 2) return dkdv_act<2>(act);

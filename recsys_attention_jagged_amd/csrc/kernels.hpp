@@ -31,8 +31,11 @@ struct KernelArgs {
     int window;     // 0 = none
     float scale;    // 1 / sqrt(d)
     int out_f32;    // outputs stored as fp32 instead of bf16
-    // softmax attention (JFA) only: per-row log-sum-exp, fp32 [H, Tq] (head-major)
+    // softmax attention (JFA) only: per-row log-sum-exp, fp32 [H, Tq] (head-major),
+    // written by the forward; the backward reads per (head, q row) the pair
+    // (LSE log2(e), D = sum of dO * O over the row), fp32 [H, Tq, 2]
     float* lse;
+    const float* stat;
     int Tq;
 };
 
@@ -74,6 +77,11 @@ GDPA_DECLARE_FUSED(128)
 hipError_t launch_partial_sum(const DevGroup* groups, int n_groups, const float* part, int rows_per_slot,
                               int stride, int offset, int d, int H, float mul, void* out, int out_f32,
                               hipStream_t s);
+
+// JFA backward pre-pass: stat[h, i] = (lse[h, i] log2(e), sum_c dout[i, h, c] o[i, h, c])
+// for the Tq rows of o, dout ([Tq, H, d] bf16)
+hipError_t launch_jfa_stat(const void* o, const void* dout, const float* lse, int Tq, int H, int d, float* stat,
+                           hipStream_t s);
 
 // plain fp32 kernels (no MFMA): forward, dQ, dK/dV over the offsets directly
 hipError_t launch_fwd_f32(const KernelArgs& a, int Tq, int d, int act, hipStream_t s);

@@ -25,7 +25,8 @@
 // range and arrive as zeros; a job of an empty slice writes a zero tile.
 //
 // Synchronisation: a wave's load instructions complete in issue order, so "job k
-// has landed" is `s_waitcnt vmcnt(JW * (jobs issued after k))` per wave, followed
+// has landed" is `s_waitcnt vmcnt(JX * (jobs issued after k))` per wave (JX load
+// instructions per job and wave, the same for every job), followed
 // by a workgroup barrier when T > 1 so that every wave's share is visible.  Slots
 // are re-filled only after such a barrier (and this wave's `s_waitcnt
 // lgkmcnt(0)`), i.e. after every wave has finished reading them.  The loads are
@@ -103,6 +104,14 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
                  : "s"(lds), "v"(voff), "s"(rs));
 }
 
+// One wave instruction: lane l's 4 bytes at byte offset `voff` land at LDS
+// address lds + 4 l (256 bytes per instruction).
+__device__ __forceinline__ void dma4(rsrc_t rs, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rs));
+}
+
 // s_waitcnt vmcnt(J m) for a uniform m in [0, MMAX] (the count is an immediate)
 template <int J>
 __device__ __forceinline__ void wait_jobs(int m) {
@@ -120,36 +129,45 @@ __device__ __forceinline__ void wait_jobs(int m) {
 // this wave's LDS reads (and scalar loads) have completed
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// Geometry of a team's ring: T waves share LDS_BYTES of LDS.
-template <int D, int T, int LDS_BYTES>
+// Geometry of a team's ring: T waves share LDS_BYTES of LDS.  With XJ = 1 every
+// slot also has a 256-byte side buffer, filled by one more instruction per job
+// (per-row statistics that travel with a tile; one-wave teams only), so that every
+// job still counts the same number of instructions.
+template <int D, int T, int LDS_BYTES, int XJ = 0>
 struct RingGeom {
     static constexpr int TILE = 32 * D * 2;            // bytes of one 32-row tile
+    static constexpr int SIDE = 256 * XJ;              // side bytes per slot
     static constexpr int J = TILE / 1024;              // wave instructions per tile
     static constexpr int JW = J / T;                   // issued by each wave of the team
-    static constexpr int RMAX = (63 / JW) + 1 > 16 ? 16 : (63 / JW) + 1;   // vmcnt is 6 bits
-    static constexpr int R = (LDS_BYTES / TILE) > RMAX ? RMAX : (LDS_BYTES / TILE);   // slots
-    static constexpr int BYTES = R * TILE;
+    static constexpr int JX = JW + XJ;                 // instructions per job and wave
+    static constexpr int RMAX = (63 / JX) + 1 > 16 ? 16 : (63 / JX) + 1;   // vmcnt is 6 bits
+    static constexpr int RFIT = LDS_BYTES / (TILE + SIDE);
+    static constexpr int R = RFIT > RMAX ? RMAX : RFIT;   // slots
+    static constexpr int BYTES = R * (TILE + SIDE);
     static_assert(J % T == 0, "a tile's instructions are split evenly over the team");
+    static_assert(XJ == 0 || T == 1, "side buffers with one-wave teams");
     // a consume point takes at most 2 jobs and the ring runs R - 2 jobs past the
     // previous one, so R >= 4 keeps every awaited job issued
     static_assert(R >= 4, "the ring needs a step plus look-ahead");
 };
 
-template <int D, int T, int LDS_BYTES>
-struct Ring : RingGeom<D, T, LDS_BYTES> {
-    using G = RingGeom<D, T, LDS_BYTES>;
+template <int D, int T, int LDS_BYTES, int XJ = 0>
+struct Ring : RingGeom<D, T, LDS_BYTES, XJ> {
+    using G = RingGeom<D, T, LDS_BYTES, XJ>;
     static constexpr int CPR = D / 8;   // 16-byte chunks per row
     uint32_t off[G::JW];                // lane offsets of this wave's instructions inside a tile
     uint32_t base;                      // LDS address of slot 0 (uniform)
     char* gbase;                        // the same slot 0 as a generic pointer
     int wt;                             // this wave's index in the team (uniform)
     int issued;                         // jobs issued so far (uniform)
+    uint32_t xlane;                     // this lane's byte offset in a side load
 
     __device__ __forceinline__ void init(char* slice, uint32_t row_stride_bytes, int wt_, int lane) {
         gbase = slice;
         base = lds_addr(slice);
         wt = wt_;
         issued = 0;
+        xlane = 4u * (uint32_t)lane;
 #pragma unroll
         for (int jj = 0; jj < G::JW; ++jj) {
             const int slot = (jj * T + wt) * 64 + lane;
@@ -160,18 +178,35 @@ struct Ring : RingGeom<D, T, LDS_BYTES> {
 
     __device__ __forceinline__ int slot_of(int job) const { return job % G::R; }
     __device__ __forceinline__ char* tile(int job) const { return gbase + slot_of(job) * G::TILE; }
+    // side buffer of job's slot (XJ = 1)
+    __device__ __forceinline__ const char* side(int job) const {
+        return gbase + G::R * G::TILE + slot_of(job) * G::SIDE;
+    }
 
     // this wave's share of loading rows [row0, row0 + 32) of the slice `rs`
     // (row_off = row0 * stride) into the next slot
     __device__ __forceinline__ void issue(rsrc_t rs, uint32_t row_off) {
+        static_assert(XJ == 0, "jobs of a ring with side buffers carry a side load");
         const uint32_t lds = base + (uint32_t)(slot_of(issued) * G::TILE);
 #pragma unroll
         for (int jj = 0; jj < G::JW; ++jj) dma16(rs, off[jj] + row_off, lds + (uint32_t)(jj * T + wt) * 1024u);
         ++issued;
     }
 
+    // issue() plus 256 bytes at byte offset x_off of `xs` into the slot's side
+    // buffer (a zero-range `xs` fills it with zeros)
+    __device__ __forceinline__ void issue(rsrc_t rs, uint32_t row_off, rsrc_t xs, uint32_t x_off) {
+        static_assert(XJ == 1, "side loads need side buffers");
+        const int slot = slot_of(issued);
+        const uint32_t lds = base + (uint32_t)(slot * G::TILE);
+#pragma unroll
+        for (int jj = 0; jj < G::JW; ++jj) dma16(rs, off[jj] + row_off, lds + (uint32_t)(jj * T + wt) * 1024u);
+        dma4(xs, x_off + xlane, base + (uint32_t)(G::R * G::TILE + slot * G::SIDE));
+        ++issued;
+    }
+
     // wait until this wave's share of job k has landed
-    __device__ __forceinline__ void wait(int k) const { wait_jobs<G::JW>(issued - 1 - k); }
+    __device__ __forceinline__ void wait(int k) const { wait_jobs<G::JX>(issued - 1 - k); }
 };
 
 // Launch shape of a team (KIND: 0 forward, 1 dK/dV, 2 dQ): waves per SIMD the
