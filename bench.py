@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of jagged GDPA forward + backward (bf16 in, fp32 accumulate) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5|pffn] [--act NAME]
+    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5|pffn] [--act NAME] [--attn gdpa|softmax]
 
 A step is one forward pass plus one backward pass (dK/dV kernel, then dQ kernel)
 over the whole batch of the chosen workload, with inputs resident in HBM.  The
@@ -18,6 +18,11 @@ performs, 4, 8, 6 and 10 H d |V| for the forward, dK/dV, dQ and one-pass
 kernels), with the kernel's average duration from HIP events recorded on the
 launch stream around each launch.  `cpu_baseline` times the fp64 oracle on the
 host cores over a bounded prefix of the same batch.
+
+--attn softmax runs jagged softmax attention (JFA) through the same kernels on the
+same batch instead: the forward (also writing the row log-sum-exp), the backward's
+row-statistics pre-pass, then the dK/dV and dQ kernels; FLOPs are counted as for
+GDPA (the exponentials are not counted).
 """
 from __future__ import annotations
 
@@ -29,6 +34,7 @@ import sys
 import time
 
 METRIC = "useful TFLOP/s, jagged GDPA fwd+bwd bf16, % of MFMA peak, 1 MI355X"
+METRIC_JFA = "useful TFLOP/s, jagged softmax attention (JFA) fwd+bwd bf16, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
@@ -37,23 +43,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_flops(H, d, pairs):
-    """Algorithmic FLOPs per launch: the MFMA products each kernel's algorithm performs."""
+def kernel_flops(H, d, pairs, Tq=0):
+    """Algorithmic FLOPs per launch: the MFMA products each kernel's algorithm performs
+    (stat: the JFA pre-pass's dot products dO . O)."""
     u = 2.0 * H * d * pairs          # one product over the valid pairs
-    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd": 5 * u}
+    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd": 5 * u, "stat": 2.0 * H * d * Tq}
 
 
-def kernel_bytes(H, d, Tq, Tk):
-    """Algorithmic bytes per launch (bf16): every input read once, every output written once."""
+def kernel_bytes(H, d, Tq, Tk, softmax=False):
+    """Algorithmic bytes per launch (bf16): every input read once, every output written
+    once; softmax (JFA): plus the fp32 row LSE written by the forward, and the fp32
+    (LSE, D) row pair that the pre-pass writes and the gradient kernels read."""
     e = 2 * H * d
-    return {"fwd": e * (2 * Tq + 2 * Tk),          # Q, K, V -> O
-            "dkdv": e * (2 * Tq + 4 * Tk),         # Q, dO, K, V -> dK, dV
-            "dq": e * (3 * Tq + 2 * Tk),           # Q, dO, K, V -> dQ
-            "bwd": e * (3 * Tq + 4 * Tk)}          # one-pass backward: Q, dO, K, V -> dQ, dK, dV
+    lse, st = (4 * H * Tq, 8 * H * Tq) if softmax else (0, 0)
+    return {"fwd": e * (2 * Tq + 2 * Tk) + lse,         # Q, K, V -> O (, LSE)
+            "dkdv": e * (2 * Tq + 4 * Tk) + st,         # Q, dO, K, V (, stat) -> dK, dV
+            "dq": e * (3 * Tq + 2 * Tk) + st,           # Q, dO, K, V (, stat) -> dQ
+            "bwd": e * (3 * Tq + 4 * Tk),               # one-pass backward: Q, dO, K, V -> dQ, dK, dV
+            "stat": 2 * e * Tq + lse + st}              # O, dO, LSE -> stat
 
 
 KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd_common.hpp", "bwd_fused.hip",
-                  "kernels.hpp", "plan.cpp", "plan.hpp", "api.cpp", "gelu_poly.h")
+                  "jfa.hip", "partials.hip", "kernels.hpp", "plan.cpp", "plan.hpp", "api.cpp", "gelu_poly.h")
 
 
 def kernel_source_digest() -> str:
@@ -82,8 +93,9 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else k.get("hbm_bytes")
 
 
-def cpu_baseline(inp, budget_s=15.0):
-    """Time the fp64 oracle (forward + backward) on a prefix of the batch."""
+def cpu_baseline(inp, budget_s=15.0, softmax=False):
+    """Time the fp64 oracle (forward + backward; softmax: jfa_fwd + jfa_bwd) on a prefix
+    of the batch."""
     import numpy as np
     import torch
     from oracle import gdpa_ref as R
@@ -106,8 +118,12 @@ def cpu_baseline(inp, budget_s=15.0):
             q, do = f(inp.q, a, e), f(inp.do, a, e)
             qo, ko = np.array([0, e - a]), np.array([0, ke - ks])
             t0 = time.perf_counter()
-            R.gdpa_fwd(q, k, v, qo, ko, inp.act, inp.window)
-            R.gdpa_bwd(q, k, v, do, qo, ko, inp.act, inp.window)
+            if softmax:
+                R.jfa_fwd(q, k, v, qo, ko, inp.window)
+                R.jfa_bwd(q, k, v, do, qo, ko, inp.window)
+            else:
+                R.gdpa_fwd(q, k, v, qo, ko, inp.act, inp.window)
+                R.gdpa_bwd(q, k, v, do, qo, ko, inp.act, inp.window)
             spent += time.perf_counter() - t0
             flops += 14 * inp.H * inp.d * R.useful_pairs([e - a], [ke - ks], inp.window)
             rows += e - a
@@ -129,6 +145,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="2", choices=["2", "3", "4", "5", "pffn"])
     ap.add_argument("--act", default=None, help="override the workload's activation (e.g. gelu_poly)")
+    ap.add_argument("--attn", default="gdpa", choices=["gdpa", "softmax"],
+                    help="softmax: jagged softmax attention (JFA) on the same batch")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -171,9 +189,15 @@ def main(argv=None):
     ko = torch.tensor(inp.kv_off, dtype=torch.int32, device="cuda")
     B, H, d, win, act = len(inp.lq), inp.H, inp.d, inp.window, inp.act
 
+    sm = args.attn == "softmax"
+    if sm and args.config == "pffn":
+        print("--attn softmax runs the attention workloads", file=sys.stderr)
+        return 2
     t0 = time.perf_counter()
     plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16")
     plan_ms = (time.perf_counter() - t0) * 1e3
+    # the JFA forward needs whole items (a softmax row is not a sum of chunk partials)
+    plan_f = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", split=False) if sm else None
     st = plan.stats()
     Tq, Tk, pairs = st["Tq"], st["Tk"], st["valid_pairs"]
 
@@ -197,9 +221,30 @@ def main(argv=None):
     def bwd():
         G.gdpa_bwd(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, dq, dk, dv, sh)
 
-    # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels
-    fused = st["bwd_fused"]
-    calls = [("fwd", fwd), ("bwd", bwd)] if fused else [("fwd", fwd), ("dkdv", dkdv), ("dq", dqk)]
+    if sm:
+        act = "softmax"
+        lse = torch.empty((H, Tq), dtype=torch.float32, device="cuda")
+        stat = torch.empty((H, Tq, 2), dtype=torch.float32, device="cuda")
+
+        def jfwd():
+            G.gdpa_jfa_fwd(plan_f.handle, inp.q, inp.k, inp.v, qo, ko, B, H, d, win, o, lse, sh)
+
+        def jstat():
+            G.gdpa_jfa_bwd_stat(h, o, lse, inp.do, H, d, stat, sh)
+
+        def jdkdv():
+            G.gdpa_jfa_bwd_dkdv(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, win, stat, dk, dv, sh)
+
+        def jdq():
+            G.gdpa_jfa_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, win, stat, dq, sh)
+
+    # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels (JFA:
+    # always the pre-pass and the two kernels)
+    fused = 0 if sm else st["bwd_fused"]
+    if sm:
+        calls = [("fwd", jfwd), ("stat", jstat), ("dkdv", jdkdv), ("dq", jdq)]
+    else:
+        calls = [("fwd", fwd), ("bwd", bwd)] if fused else [("fwd", fwd), ("dkdv", dkdv), ("dq", dqk)]
     for _ in range(args.warmup):
         for _, c in calls:
             c()
@@ -225,28 +270,29 @@ def main(argv=None):
 
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
-    kb = kernel_bytes(H, d, Tq, Tk)
-    kf = kernel_flops(H, d, pairs)
+    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm)
+    kf = kernel_flops(H, d, pairs, Tq)
     dom = max(kms, key=kms.get)
+    trace_name = w["name"] + ("_jfa" if sm else "")   # the counter record of this workload's kernels
     # the roof the kernel's arithmetic intensity puts it under (ridge: peak FLOP/s / peak B/s)
     mfma_bound = kf[dom] / kb[dom] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
         achieved = kf[dom] / (kms[dom] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "algorithmic_flops": kf[dom], "traffic": measured_traffic(w["name"], dom)}
+                    "algorithmic_flops": kf[dom], "traffic": measured_traffic(trace_name, dom)}
     else:
         achieved = kb[dom] / (kms[dom] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                    "algorithmic_bytes": kb[dom], "traffic": measured_traffic(w["name"], dom)}
+                    "algorithmic_bytes": kb[dom], "traffic": measured_traffic(trace_name, dom)}
     kernels = {n: {"ms": round(kms[n], 4), "alg_GBps": round(kb[n] / (kms[n] * 1e-3) / 1e9, 1)}
                for n in kms}
     kernels["fwd"]["useful_TFLOPs"] = round(4.0 * H * d * pairs / (kms["fwd"] * 1e-3) / 1e12, 2)
-    bwd_ms = kms["bwd"] if fused else kms["dkdv"] + kms["dq"]
+    bwd_ms = kms["bwd"] if fused else kms["dkdv"] + kms["dq"] + kms.get("stat", 0.0)
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC_JFA if sm else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -260,7 +306,8 @@ def main(argv=None):
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs,
-                   "backward": ["dK/dV + dQ kernels", "one KV-stationary pass", "one Q-stationary pass"][fused]},
+                   "backward": ("row-statistics pre-pass + dK/dV + dQ kernels" if sm else
+                                ["dK/dV + dQ kernels", "one KV-stationary pass", "one Q-stationary pass"][fused])},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_useful_TFLOPs": kernels["fwd"]["useful_TFLOPs"],
         "bwd_useful_TFLOPs": round(10.0 * H * d * pairs / (bwd_ms * 1e-3) / 1e12, 2),
@@ -271,8 +318,10 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, softmax=sm)
     plan.close()
+    if plan_f is not None:
+        plan_f.close()
     print(json.dumps(out), flush=True)
     return 0
 

@@ -232,10 +232,28 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
  * Q-stationary dQ kernel (never the one-pass kernels), plus the chunk reductions
  * of cut items.  The plan must be bf16 with one-wave dQ and dK/dV teams (the
  * automatic layouts; UNSUPPORTED otherwise).  Errors as gdpa_bwd.
+ * gdpa_jfa_bwd == gdpa_jfa_bwd_stat, then gdpa_jfa_bwd_dkdv, then gdpa_jfa_bwd_dq.
  */
 gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
                          int B, int H, int d, int window, float* stat, void* dq, void* dk, void* dv, void* stream);
+
+/*
+ * The three parts of gdpa_jfa_bwd, for callers who schedule them separately:
+ *   gdpa_jfa_bwd_stat - only the pre-pass: fills stat [H, Tq, 2] from o, lse and
+ *                       dout (H and d must match the plan);
+ *   gdpa_jfa_bwd_dkdv - only dK, dV, reading a stat filled for the same o, lse, dout;
+ *   gdpa_jfa_bwd_dq   - only dQ, likewise.
+ * Arguments and errors as gdpa_jfa_bwd; stat is read-only in the last two.
+ */
+gdpa_status gdpa_jfa_bwd_stat(gdpa_plan plan, const void* o, const float* lse, const void* dout, int H, int d,
+                              float* stat, void* stream);
+gdpa_status gdpa_jfa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                              const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, int window,
+                              const float* stat, void* dk, void* dv, void* stream);
+gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                            const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, int window,
+                            const float* stat, void* dq, void* stream);
 
 /*
  * pFFN as GDPA (GDPA page, "Section details", diagram of self-attention, PMA and

@@ -83,12 +83,16 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_jfa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                  _vp]
+    lib.gdpa_jfa_bwd_stat.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]
+    lib.gdpa_jfa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
+    lib.gdpa_jfa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_pffn_plan_create.argtypes = [_i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts), ctypes.POINTER(_vp)]
     lib.gdpa_pffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
     lib.gdpa_pffn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp]
     for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
                  "gdpa_plan_export", "gdpa_plan_stats", "gdpa_pffn_plan_create", "gdpa_pffn_fwd",
-                 "gdpa_pffn_bwd", "gdpa_jfa_fwd", "gdpa_jfa_bwd"):
+                 "gdpa_pffn_bwd", "gdpa_jfa_fwd", "gdpa_jfa_bwd", "gdpa_jfa_bwd_stat", "gdpa_jfa_bwd_dkdv",
+                 "gdpa_jfa_bwd_dq"):
         getattr(lib, name).restype = _i
     if path == LIB_PATH:
         _lib = lib
@@ -180,6 +184,24 @@ def gdpa_jfa_bwd(plan, q, k, v, o, lse, dout, q_off_dev, kv_off_dev, B, H, d, wi
     _check(load_library().gdpa_jfa_bwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                                        _ptr(q_off_dev), _ptr(kv_off_dev), B, H, d, window, _ptr(stat), _ptr(dq),
                                        _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def gdpa_jfa_bwd_stat(plan, o, lse, dout, H, d, stat, stream=None):
+    """The JFA backward's pre-pass: stat [H, Tq, 2] = (LSE log2 e, sum dO * O)."""
+    _check(load_library().gdpa_jfa_bwd_stat(plan, _ptr(o), _ptr(lse), _ptr(dout), H, d, _ptr(stat),
+                                            _stream(stream)))
+
+
+def gdpa_jfa_bwd_dkdv(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, window, stat, dk, dv, stream=None):
+    _check(load_library().gdpa_jfa_bwd_dkdv(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
+                                            _ptr(kv_off_dev), B, H, d, window, _ptr(stat), _ptr(dk), _ptr(dv),
+                                            _stream(stream)))
+
+
+def gdpa_jfa_bwd_dq(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, window, stat, dq, stream=None):
+    _check(load_library().gdpa_jfa_bwd_dq(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
+                                          _ptr(kv_off_dev), B, H, d, window, _ptr(stat), _ptr(dq),
+                                          _stream(stream)))
 
 
 def _opts(host_only, bins, team, blocks, deal, split, unfused):

@@ -519,20 +519,32 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
     return GDPA_OK;
 }
 
-gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
-                         const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
-                         int B, int H, int d, int window, float* stat, void* dq, void* dk, void* dv, void* stream) {
-    g_err.clear();
-    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
-    if (st != GDPA_OK) return st;
+// the JFA backward's row statistics: stat[h, i] = (LSE log2 e, sum dO * O)
+static gdpa_status jfa_stat(gdpa_plan plan, const void* o, const float* lse, const void* dout, float* stat,
+                            hipStream_t s) {
+    if (plan->Tq == 0) return GDPA_OK;
+    if (!o || !lse || !dout || !stat) return fail(GDPA_ERR_INVALID_ARG, "o, lse, dout or stat is NULL");
+    const hipError_t e = launch_jfa_stat(o, dout, lse, (int)plan->Tq, plan->H, plan->d, stat, s);
+    if (e != hipSuccess) return fail_hip(e, "JFA row-statistics launch");
+    return GDPA_OK;
+}
+
+static gdpa_status jfa_check(gdpa_plan plan) {
     if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "JFA runs on bf16 plans");
     if (plan->lists[LIST_DQ].team != 1 || plan->lists[LIST_DKDV].team != 1)
         return fail(GDPA_ERR_UNSUPPORTED, "the JFA backward runs one-wave dQ and dK/dV teams");
+    return GDPA_OK;
+}
+
+// dK/dV and/or dQ of the JFA backward from filled row statistics
+static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                             const int32_t* q_off_dev, const int32_t* kv_off_dev, const float* stat, void* dq,
+                             void* dk, void* dv, hipStream_t s, bool want_dkdv, bool want_dq) {
     const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
-    if (any_q && (!q || !o || !lse || !dout || !stat || !dq))
-        return fail(GDPA_ERR_INVALID_ARG, "q, o, lse, dout, stat or dq is NULL");
-    if (any_k && (!k || !v || !dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "k, v, dk or dv is NULL");
-    hipStream_t s = (hipStream_t)stream;
+    if (any_q && (!q || !dout || !stat)) return fail(GDPA_ERR_INVALID_ARG, "q, dout or stat is NULL");
+    if (any_k && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
+    if (want_dq && any_q && !dq) return fail(GDPA_ERR_INVALID_ARG, "dq is NULL");
+    if (want_dkdv && any_k && (!dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "dk or dv is NULL");
     KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
     a.q = q;
     a.k = k;
@@ -543,8 +555,9 @@ gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const voi
     a.dv = dv;
     a.stat = stat;
     a.Tq = (int)plan->Tq;
-    hipError_t e = launch_jfa_stat(o, dout, lse, (int)plan->Tq, H, d, stat, s);
-    if (e == hipSuccess && any_k) {
+    const int d = plan->d;
+    hipError_t e = hipSuccess;
+    if (want_dkdv && any_k) {
         const WorkList& wl = plan->lists[LIST_DKDV];
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DKDV];
@@ -559,7 +572,7 @@ gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const voi
         if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
         if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
     }
-    if (e == hipSuccess && any_q) {
+    if (e == hipSuccess && want_dq && any_q) {
         const WorkList& wl = plan->lists[LIST_DQ];
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DQ];
@@ -576,6 +589,55 @@ gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const voi
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no JFA backward kernel for this configuration");
     if (e != hipSuccess) return fail_hip(e, "JFA backward launch");
     return GDPA_OK;
+}
+
+gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
+                         int B, int H, int d, int window, float* stat, void* dq, void* dk, void* dv, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
+    if (st == GDPA_OK) st = jfa_check(plan);
+    if (st != GDPA_OK) return st;
+    if (plan->Tq > 0 && !dq) return fail(GDPA_ERR_INVALID_ARG, "dq is NULL");
+    if (plan->Tk > 0 && (!k || !v || !dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "k, v, dk or dv is NULL");
+    if (plan->Tq > 0 && !q) return fail(GDPA_ERR_INVALID_ARG, "q is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    st = jfa_stat(plan, o, lse, dout, stat, s);
+    if (st != GDPA_OK) return st;
+    return jfa_grads(plan, q, k, v, dout, q_off_dev, kv_off_dev, stat, dq, dk, dv, s, true, true);
+}
+
+gdpa_status gdpa_jfa_bwd_stat(gdpa_plan plan, const void* o, const float* lse, const void* dout, int H, int d,
+                              float* stat, void* stream) {
+    g_err.clear();
+    if (!plan) return fail(GDPA_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->host_only) return fail(GDPA_ERR_PLAN_MISMATCH, "host-only plan cannot run kernels");
+    if (H != plan->H || d != plan->d) return fail(GDPA_ERR_PLAN_MISMATCH, "H or d differ from the plan");
+    const gdpa_status st = jfa_check(plan);
+    if (st != GDPA_OK) return st;
+    return jfa_stat(plan, o, lse, dout, stat, (hipStream_t)stream);
+}
+
+gdpa_status gdpa_jfa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                              const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, int window,
+                              const float* stat, void* dk, void* dv, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
+    if (st == GDPA_OK) st = jfa_check(plan);
+    if (st != GDPA_OK) return st;
+    return jfa_grads(plan, q, k, v, dout, q_off_dev, kv_off_dev, stat, nullptr, dk, dv, (hipStream_t)stream, true,
+                     false);
+}
+
+gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                            const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, int window,
+                            const float* stat, void* dq, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
+    if (st == GDPA_OK) st = jfa_check(plan);
+    if (st != GDPA_OK) return st;
+    return jfa_grads(plan, q, k, v, dout, q_off_dev, kv_off_dev, stat, dq, nullptr, nullptr, (hipStream_t)stream,
+                     false, true);
 }
 
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,

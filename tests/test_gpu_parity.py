@@ -379,6 +379,25 @@ def test_jfa_backward_cut_items():
     check_jfa_grads(got, inp, "cut")
 
 
+def test_jfa_backward_parts_match_whole():
+    """gdpa_jfa_bwd_stat, _dkdv and _dq in turn give gdpa_jfa_bwd's outputs bit for bit."""
+    say("JFA backward in three calls")
+    inp = make_from_lengths(JFA_LQ, JFA_LK, 2, 128, act="gelu", seed=58, device=DEV)
+    whole = run_jfa_bwd(inp)
+    qo, ko = dev_offsets(inp)
+    o = torch.tensor(whole[3], dtype=torch.bfloat16, device=DEV)
+    lse = torch.tensor(whole[4], device=DEV)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, 0, "bf16") as plan:
+        stat = torch.full((inp.H, inp.q.shape[0], 2), float("nan"), device=DEV)
+        dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+        G.gdpa_jfa_bwd_stat(plan.handle, o, lse, inp.do, inp.H, inp.d, stat)
+        G.gdpa_jfa_bwd_dkdv(plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, plan.B, inp.H, inp.d, 0, stat, dk, dv)
+        G.gdpa_jfa_bwd_dq(plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, plan.B, inp.H, inp.d, 0, stat, dq)
+        torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV", "stat"), (dq, dk, dv, stat), (whole[0], whole[1], whole[2], whole[5])):
+        assert np.array_equal(a.float().cpu().numpy(), b, equal_nan=True), name
+
+
 def test_jfa_backward_rejects():
     inp = make_from_lengths([40, 3], [50, 7], 2, 128, act="gelu", seed=57, device=DEV)
     qo, ko = dev_offsets(inp)
