@@ -196,8 +196,6 @@ def main(argv=None):
     t0 = time.perf_counter()
     plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16")
     plan_ms = (time.perf_counter() - t0) * 1e3
-    # the JFA forward needs whole items (a softmax row is not a sum of chunk partials)
-    plan_f = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", split=False) if sm else None
     st = plan.stats()
     Tq, Tk, pairs = st["Tq"], st["Tk"], st["valid_pairs"]
 
@@ -227,7 +225,7 @@ def main(argv=None):
         stat = torch.empty((H, Tq, 2), dtype=torch.float32, device="cuda")
 
         def jfwd():
-            G.gdpa_jfa_fwd(plan_f.handle, inp.q, inp.k, inp.v, qo, ko, B, H, d, win, o, lse, sh)
+            G.gdpa_jfa_fwd(h, inp.q, inp.k, inp.v, qo, ko, B, H, d, win, o, lse, sh)
 
         def jstat():
             G.gdpa_jfa_bwd_stat(h, o, lse, inp.do, H, d, stat, sh)
@@ -320,8 +318,6 @@ def main(argv=None):
         log("timing the fp64 oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, softmax=sm)
     plan.close()
-    if plan_f is not None:
-        plan_f.close()
     print(json.dumps(out), flush=True)
     return 0
 

@@ -141,7 +141,8 @@ typedef struct gdpa_plan_s* gdpa_plan;
  * one plan therefore must not overlap in time (e.g. on two streams).
  *
  * Unless opts->host_only, uploads the work lists and allocates the slot buffers
- * (n_parts * tile_stat * d * 4 bytes per list) with hipMalloc / hipMemcpy on
+ * (n_parts * tile_stat * w * 4 bytes per list, w = d + 2 for the forward list,
+ * 2 d for dK/dV, d for dQ) with hipMalloc / hipMemcpy on
  * the current device (synchronous).  Errors: INVALID_ARG, BAD_OFFSETS,
  * UNSUPPORTED, HIP, NOMEM.
  */
@@ -211,9 +212,10 @@ gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void
  * gdpa_fwd without act, plus
  *   lse : device fp32 [H, Tq] (head-major), written: LSE of each row, -inf for rows
  *         with no valid key (their O rows are 0).
- * The plan must be bf16 and its forward items whole (create it with
- * opts->no_split = 1 when the planner would cut them; UNSUPPORTED otherwise).
- * Errors as gdpa_fwd.
+ * The plan must be bf16 (UNSUPPORTED otherwise).  A cut forward item's chunks
+ * store unnormalised partial rows with their running max and sum; a combine
+ * kernel rescales them to the common max and divides by the total sum (in slot
+ * order, so the result does not depend on scheduling).  Errors as gdpa_fwd.
  */
 gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v, const int32_t* q_off_dev,
                          const int32_t* kv_off_dev, int B, int H, int d, int window, void* o, float* lse,

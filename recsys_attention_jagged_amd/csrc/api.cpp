@@ -250,9 +250,11 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
                 e = hipMalloc((void**)&p->d_groups[l], g.size() * sizeof(DevGroup));
                 if (e == hipSuccess)
                     e = hipMemcpy(p->d_groups[l], g.data(), g.size() * sizeof(DevGroup), hipMemcpyHostToDevice);
-                const size_t blocks = l == LIST_DKDV ? 2 : 1;   // dK and dV
+                // dK and dV blocks; the forward list also keeps two floats per slot row
+                // (softmax chunks' row max and sum) after its blocks
+                const size_t per_row = l == LIST_DKDV ? 2 * (size_t)d : l == LIST_FWD ? (size_t)d + 2 : (size_t)d;
                 if (e == hipSuccess)
-                    e = hipMalloc((void**)&p->d_part[l], blocks * wl.n_parts * wl.t_stat * d * sizeof(float));
+                    e = hipMalloc((void**)&p->d_part[l], per_row * wl.n_parts * wl.t_stat * sizeof(float));
             }
             if (e != hipSuccess) {
                 delete p;
@@ -491,8 +493,6 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
     gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
     if (st != GDPA_OK) return st;
     if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "JFA runs on bf16 plans");
-    if (plan->lists[LIST_FWD].n_parts > 0)
-        return fail(GDPA_ERR_UNSUPPORTED, "JFA needs a plan whose forward items are whole (opts.no_split = 1)");
     if (plan->Tq > 0 && (!q || !o || !lse)) return fail(GDPA_ERR_INVALID_ARG, "q, o or lse is NULL");
     if (plan->Tk > 0 && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
     if (plan->Tq == 0) return GDPA_OK;
@@ -508,12 +508,17 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
     a.items = plan->d_items[LIST_FWD];
     a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
     a.P = wl.P;
+    a.part = plan->d_part[LIST_FWD];
+    a.part_stat = a.part ? a.part + (size_t)wl.n_parts * wl.t_stat * d : nullptr;
     hipError_t e;
     switch (d) {
         case 32: e = launch_fwd_bf16_d32(a, wl.team, wl.nb, kActSoftmax, s); break;
         case 64: e = launch_fwd_bf16_d64(a, wl.team, wl.nb, kActSoftmax, s); break;
         default: e = launch_fwd_bf16_d128(a, wl.team, wl.nb, kActSoftmax, s); break;
     }
+    if (e == hipSuccess && plan->n_groups[LIST_FWD] > 0)
+        e = launch_jfa_combine(plan->d_groups[LIST_FWD], plan->n_groups[LIST_FWD], a.part, a.part_stat, wl.t_stat,
+                               d, H, (int)plan->Tq, o, plan->dtype != GDPA_BF16, lse, s);
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no forward kernel for this configuration");
     if (e != hipSuccess) return fail_hip(e, "JFA forward launch");
     return GDPA_OK;

@@ -222,6 +222,15 @@ struct FwdPol {
         if (c.part >= 0) {   // one chunk of a cut item: fp32 partial block
 #pragma unroll
             for (int b = 0; b < NB; ++b) store_partial<NDB>(acc[b], a.part, c.part, ROWS, 32 * (wt * NB + b), r, hh);
+            if constexpr (ACT == ACT_SOFTMAX) {   // softmax: the block is unnormalised; its rows' max and sum
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const float l = lrow[b] + __shfl_xor(lrow[b], 32);
+                    if (hh == 0)
+                        *(float2*)(a.part_stat + ((size_t)c.part * ROWS + 32 * (wt * NB + b) + r) * 2) =
+                            make_float2(mrow[b], l);
+                }
+            }
             return;
         }
         const size_t ob = ((size_t)c.qs * H + c.h) * D;

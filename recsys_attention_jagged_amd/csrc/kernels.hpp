@@ -25,6 +25,8 @@ struct KernelArgs {
     const int32_t* bin_ptr;
     float* part;                // fp32 partial-output slots of chunks, [slots][blocks][rows per item][d]
                                 // (one block per slot; two, dK then dV, for the dK/dV list)
+    float* part_stat;           // softmax forward chunks: per slot row (running max in log2 units, row sum),
+                                // [slots][rows per item][2]
     int P;          // bins = persistent workgroups
     int B;          // samples
     int H;
@@ -76,6 +78,13 @@ GDPA_DECLARE_FUSED(128)
 // stride 1; dK, dV: stride 2, offsets 0 and 1).
 hipError_t launch_partial_sum(const DevGroup* groups, int n_groups, const float* part, int rows_per_slot,
                               int stride, int offset, int d, int H, float mul, void* out, int out_f32,
+                              hipStream_t s);
+
+// JFA forward chunks: per row of each cut item, O = (sum_j 2^(m_j - m) O_j) / l and
+// LSE = (m + log2 l) ln 2, with m = max_j m_j and l = sum_j 2^(m_j - m) l_j over the
+// item's slots j in slot order (out bf16 or fp32 [Tq, H, d]; lse [H, Tq])
+hipError_t launch_jfa_combine(const DevGroup* groups, int n_groups, const float* part, const float* part_stat,
+                              int rows_per_slot, int d, int H, int Tq, void* out, int out_f32, float* lse,
                               hipStream_t s);
 
 // JFA backward pre-pass: stat[h, i] = (lse[h, i] log2(e), sum_c dout[i, h, c] o[i, h, c])

@@ -242,7 +242,7 @@ def test_cut_items(d, case, deal):
 
 def run_jfa_fwd(inp, dtype="bf16", **opts):
     qo, ko = dev_offsets(inp)
-    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, dtype, split=False, **opts) as plan:
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, dtype, **opts) as plan:
         o = torch.empty(inp.q.shape, dtype=torch.float32 if dtype == "bf16_f32out" else torch.bfloat16, device=DEV)
         lse = torch.empty((inp.H, inp.q.shape[0]), dtype=torch.float32, device=DEV)
         G.gdpa_jfa_fwd(plan.handle, inp.q, inp.k, inp.v, qo, ko, plan.B, inp.H, inp.d, inp.window, o, lse)
@@ -286,16 +286,33 @@ def test_jfa_forward_windows(window):
     check_lse(lse, rl, f"JFA LSE window={window}")
 
 
-def test_jfa_rejects_cut_forward_items():
-    inp = make_from_lengths([32, 1], [3000, 5], 2, 64, act="gelu", seed=53, device=DEV)
-    qo, ko = dev_offsets(inp)
-    with G.Plan(inp.q_off, inp.kv_off, 2, 64, 0, "bf16", bins=(16, 16, 16)) as plan:
+JFA_CUT_CASES = [   # (lq, lk, d, window, team, nb): long rows of kv tiles cut into chunks
+    ([32, 1], [3000, 5], 64, 0, 1, 1),
+    ([32, 40, 3, 64], [2500, 700, 0, 1800], 128, 0, 2, 1),
+    ([96, 17], [2000, 33], 32, 0, 1, 2),
+    ([300, 5], [300, 5], 128, 100, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(JFA_CUT_CASES)))
+def test_jfa_forward_cut_items(case):
+    """A cut item's chunks keep unnormalised rows with their max and sum; the combine
+    rescales them to the common max (also the LSE of those rows)."""
+    lq, lk, d, window, team, nb = JFA_CUT_CASES[case]
+    say(f"JFA forward cut items case={case}")
+    inp = make_from_lengths(lq, lk, 2, d, act="gelu", window=window, seed=53 + case, device=DEV)
+    opts = dict(bins=(16, 16, 16), team=(team, 0, 0), blocks=(nb, 0, 0))
+    with G.Plan(inp.q_off, inp.kv_off, 2, d, window, "bf16", **opts) as plan:
         assert plan.stats()["n_parts"][0] > 0
-        o = torch.empty_like(inp.q)
-        lse = torch.empty((2, 33), dtype=torch.float32, device=DEV)
-        with pytest.raises(G.GdpaError) as e:
-            G.gdpa_jfa_fwd(plan.handle, inp.q, inp.k, inp.v, qo, ko, 2, 2, 64, 0, o, lse)
-        assert G.STATUS[e.value.status] == "GDPA_ERR_UNSUPPORTED"
+    ro, rl = R.jfa_fwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_off, inp.kv_off, window)
+    o, lse = run_jfa_fwd(inp, **opts)
+    check_close(o, ro, f"JFA O cut case={case}")
+    check_lse(lse, rl, f"JFA LSE cut case={case}")
+    o32, lse32 = run_jfa_fwd(inp, dtype="bf16_f32out", **opts)
+    check_close(o32, ro, f"JFA O f32out cut case={case}")
+    check_lse(lse32, rl, f"JFA LSE f32out cut case={case}")
+    ow, lw = run_jfa_fwd(inp, split=False, team=(team, 0, 0), blocks=(nb, 0, 0))
+    check_close(ow, ro, f"JFA O whole items case={case}")
 
 
 def run_jfa_bwd(inp, dtype="bf16", **opts):
@@ -303,7 +320,7 @@ def run_jfa_bwd(inp, dtype="bf16", **opts):
     (dQ, dK, dV, O, LSE, stat) as numpy."""
     qo, ko = dev_offsets(inp)
     Tq = inp.q.shape[0]
-    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16", split=False) as pf:
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16") as pf:
         o = torch.empty_like(inp.q)
         lse = torch.empty((inp.H, Tq), dtype=torch.float32, device=DEV)
         G.gdpa_jfa_fwd(pf.handle, inp.q, inp.k, inp.v, qo, ko, pf.B, inp.H, inp.d, inp.window, o, lse)
