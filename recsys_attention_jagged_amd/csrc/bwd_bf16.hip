@@ -128,22 +128,23 @@ struct DqPol : Common {
         const float c2 = scale * L2E;
         const bool tail = j0 + 32 > lk;
         const bool band = win > 0 && !band_all(q0, j0, win);
+        if (tail || band) {   // one uniform branch per half, not per element
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = 8 * m + k;
-            const float pe = fast_exp2(__builtin_fmaf(sc[e], c2, -l2q[b]));
-            float v = pe * (dp[e] - dq_[b]);
-            if (tail || band) {
+            for (int k = 0; k < 8; ++k) {
+                const int e = 8 * m + k;
+                const float pe = fast_exp2(__builtin_fmaf(sc[e], c2, -l2q[b]));
                 const int jr = 8 * (e >> 2) + 4 * hh + (e & 3);
-                bool ok = true;
-                if (tail) ok = j0 + jr < lk;
-                if (band) {
-                    const int dd = q0 + r - j0 - jr;
-                    ok = ok && dd < win && -dd < win;
-                }
-                v = ok ? v : 0.0f;
+                const int dd = q0 + r - j0 - jr;
+                const bool ok = (j0 + jr < lk) & (!band | in_band(dd, win));
+                dsb[k] = (__bf16)(ok ? pe * (dp[e] - dq_[b]) : 0.0f);
             }
-            dsb[k] = (__bf16)v;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = 8 * m + k;
+                const float pe = fast_exp2(__builtin_fmaf(sc[e], c2, -l2q[b]));
+                dsb[k] = (__bf16)(pe * (dp[e] - dq_[b]));
+            }
         }
     }
 
@@ -192,7 +193,7 @@ struct DqPol : Common {
                         float f, gr;
                         act_fwd_grad<ACT>(sc[b][e] * scale, f, gr);
                         const int dd = base - (8 * (e >> 2) + (e & 3));
-                        dsb[b][k] = (__bf16)((dd < win && -dd < win) ? dp[b][e] * gr : 0.0f);
+                        dsb[b][k] = (__bf16)(in_band(dd, win) ? dp[b][e] * gr : 0.0f);
                     }
                 } else {
 #pragma unroll
@@ -342,16 +343,17 @@ struct DkdvPol : Common {
             for (int e = 0; e < 16; ++e) {
                 const float4& sv = st[e >> 2][(e >> 1) & 1];
                 const float l2 = (e & 1) ? sv.z : sv.x, dd = (e & 1) ? sv.w : sv.y;
-                float pe = fast_exp2(__builtin_fmaf(sc[e], c2, -l2));
-                float de = pe * (dp[e] - dd);
-                if (band) {
+                p[e] = fast_exp2(__builtin_fmaf(sc[e], c2, -l2));
+                ds[e] = p[e] * (dp[e] - dd);
+            }
+            if (band) {   // one uniform branch per block
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
                     const int k = base + 8 * (e >> 2) + (e & 3);
-                    const bool ok = k < win && -k < win;
-                    pe = ok ? pe : 0.0f;
-                    de = ok ? de : 0.0f;
+                    const bool ok = in_band(k, win);
+                    p[e] = ok ? p[e] : 0.0f;
+                    ds[e] = ok ? ds[e] : 0.0f;
                 }
-                p[e] = pe;
-                ds[e] = de;
             }
         } else if (win > 0 && !band_all(i0, j0, win)) {
             const int base = i0 + 4 * hh - j0 - r;
@@ -360,7 +362,7 @@ struct DkdvPol : Common {
                 float f, gr;
                 act_fwd_grad<ACT>(sc[e] * scale, f, gr);
                 const int dd = base + 8 * (e >> 2) + (e & 3);
-                const bool ok = dd < win && -dd < win;
+                const bool ok = in_band(dd, win);
                 p[e] = ok ? f : 0.0f;
                 ds[e] = ok ? dp[e] * gr : 0.0f;
             }

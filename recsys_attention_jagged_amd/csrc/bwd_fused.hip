@@ -111,7 +111,7 @@ struct KvFusedPol : Common {
                 float ds = dp[e] * gr;
                 if (masked) {
                     const int dd = base + 8 * (e >> 2) + (e & 3);
-                    const bool ok = dd < win && -dd < win;
+                    const bool ok = in_band(dd, win);
                     f = ok ? f : 0.0f;
                     ds = ok ? ds : 0.0f;
                 }
@@ -241,7 +241,7 @@ struct QFusedPol : Common {
                 float ds = dp[e] * gr;
                 if (masked) {
                     const int dd = base - (8 * (e >> 2) + (e & 3));
-                    const bool ok = dd < win && -dd < win;
+                    const bool ok = in_band(dd, win);
                     f = ok ? f : 0.0f;
                     ds = ok ? ds : 0.0f;
                 }

@@ -182,6 +182,12 @@ struct Rec {
     int32_t qs, lq, ks, lk, h, t, s0, s1, part, pad0, pad1, pad2;
 };
 
+// |dd| < win (win >= 1) as one unsigned compare, so that a mask is a select and
+// not a branch: dd + win - 1 lies in [0, 2 win - 2]
+__device__ __forceinline__ bool in_band(int dd, int win) {
+    return (uint32_t)(dd + win - 1) <= (uint32_t)(2 * win - 2);
+}
+
 // Does every pair of the 32 x 32 block (rows i0.., columns j0..) lie inside the
 // band |i - j| < win?  (Sample lengths need no test: rows beyond a length are
 // zero-filled tiles, whose products and stores vanish.)

@@ -94,28 +94,39 @@ struct FwdPol {
 
     // Online softmax of one 32 x 32 block (JFA): lane column = query q0 + r, element
     // e = key j0 + 8 (e/4) + 4 hh + e % 4.  Keys outside the sample or the window are
-    // masked (zero tiles give S = 0, and exp(0) is not 0).  The running max moves to
-    // the block's max; the accumulator and the running sum are rescaled when it does.
+    // masked (zero tiles give S = 0, and exp(0) is not 0).  The reference max of a row
+    // moves to the block's max only when that exceeds it by more than kLazy (log2
+    // units), so P stays below 2^kLazy (exact in fp32 and bf16 up to rounding) and the
+    // accumulator and running sum are rescaled only then, not whenever the max grows.
     __device__ __forceinline__ void softmax_block(int b, const f32x16& sc, int q0, int j0, int lk, f32x16& p) {
         constexpr float L2E = 1.4426950408889634f;
         const bool tail = j0 + 32 > lk;
         const bool band = win > 0 && !band_all(q0, j0, win);
+        const float c2 = scale * L2E;
         float mt = kNegBig;
+        // p holds the scores in log2 units first; the mask test is taken once per block
+        // (a uniform branch), not per element
+        if (tail || band) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {   // p holds the scores in log2 units first
-            const int jr = 8 * (e >> 2) + 4 * hh + (e & 3);
-            bool ok = true;
-            if (tail) ok = j0 + jr < lk;
-            if (band) {
+            for (int e = 0; e < 16; ++e) {
+                const int jr = 8 * (e >> 2) + 4 * hh + (e & 3);
                 const int dd = q0 + r - j0 - jr;
-                ok = ok && dd < win && -dd < win;
+                const bool ok = (j0 + jr < lk) & (!band | in_band(dd, win));
+                p[e] = ok ? sc[e] * c2 : kNegBig;
+                mt = __builtin_fmaxf(mt, p[e]);
             }
-            p[e] = ok ? sc[e] * (scale * L2E) : kNegBig;
-            mt = __builtin_fmaxf(mt, p[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[e] = sc[e] * c2;
+                mt = __builtin_fmaxf(mt, p[e]);
+            }
         }
         mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = __builtin_fmaxf(mrow[b], mt);
-        const float alpha = fast_exp2(mrow[b] - mn);   // 1 while the max stays, 0 from the sentinel
+        constexpr float kLazy = 8.0f;
+        const float mo = mrow[b];
+        const float mn = mt > mo + kLazy ? mt : mo;   // from the sentinel: the first block with a valid key
+        const float alpha = fast_exp2(mo - mn);       // 1 while the reference stays, 0 from the sentinel
         mrow[b] = mn;
         float ls = 0.0f;
 #pragma unroll
@@ -124,8 +135,9 @@ struct FwdPol {
             ls += p[e];
         }
         lrow[b] = __builtin_fmaf(lrow[b], alpha, ls);
-        // rescale only when some row's max moved (every lane of the wave agrees on the branch)
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+        // rescale only when some row's reference moved from a finite value (rows still at
+        // the sentinel have a zero accumulator; every lane of the wave takes the same branch)
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f && mo > 0.5f * kNegBig)) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -184,7 +196,8 @@ struct FwdPol {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int dd = base - (8 * (e >> 2) + (e & 3));
-                    p[e] = (dd < win && -dd < win) ? act_fwd<ACT>(sc[b][e] * scale) : 0.0f;
+                    const float f = act_fwd<ACT>(sc[b][e] * scale);
+                    p[e] = in_band(dd, win) ? f : 0.0f;
                 }
             } else {
 #pragma unroll
