@@ -22,6 +22,9 @@ Recipe (all seeds explicit):
     N(0, 0.02^2), shared by every sample.
   * RMS normalisation of an input (per token and head, over d, no gain):
     x / sqrt(mean(x^2) + 1e-6), in fp32, before rounding.
+  * raw inputs for the fused-norm path (rms = ""): with row_spread s > 0, each
+    (token, head) row of Q, K and V is multiplied by exp(s N(0, 1)), drawn after dO
+    in the order Q, K, V, so that rows differ in scale as un-normalised activations do.
   * rounding: fp32 -> storage dtype (bf16 round-to-nearest-even); the oracle is
     fed the rounded values widened to fp64.
 """
@@ -127,7 +130,7 @@ def _rms_normalise(x, eps: float = 1e-6):
 def make_from_lengths(lq, lk, H: int, d: int, *, act: str = "gelu", window: int = 0,
                       dtype: str = "bf16", seed: int = 0, device: str = "cpu",
                       rms: str = "qkv", pma_seeds: bool = False, cfg: Optional[int] = None,
-                      q_scale: float = 1.0) -> JaggedInputs:
+                      q_scale: float = 1.0, row_spread: float = 0.0) -> JaggedInputs:
     """Draw Q, K, V, dO for the given per-sample lengths (see the module recipe)."""
     import torch
     lq = np.asarray(lq, dtype=np.int64)
@@ -150,6 +153,9 @@ def make_from_lengths(lq, lk, H: int, d: int, *, act: str = "gelu", window: int 
     k = torch.randn((Tk, H, d), generator=g, device=device, dtype=f32)
     v = torch.randn((Tk, H, d), generator=g, device=device, dtype=f32)
     do = torch.randn((Tq, H, d), generator=g, device=device, dtype=f32)
+    if row_spread > 0.0:
+        q, k, v = (x * torch.exp(row_spread * torch.randn(x.shape[:2] + (1,), generator=g, device=device,
+                                                          dtype=f32)) for x in (q, k, v))
     if "q" in rms and not pma_seeds:
         q = _rms_normalise(q)
     if "k" in rms:

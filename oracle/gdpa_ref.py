@@ -275,6 +275,59 @@ def pffn_bwd(q, wk, wv, do, act: str):
 
 
 # ---------------------------------------------------------------------------
+# RMSNorm prologue: GDPA on normalised Q, K (and V)
+# ---------------------------------------------------------------------------
+# GDPA page, "Section details", the chart comparing tanh GELU with the 6th-order
+# series: in the models, RMSNorm keeps the activation's inputs in range.  The pages
+# say no more; the reading used here is the norm applied right before the
+# attention, per (token, head) over the d features, with no gain and eps = 1e-6:
+#     x^ = x r,   r = 1 / sqrt(mean_c x_c^2 + eps),
+# on the tensors named in `norm` (a subset of "qkv"), and GDPA on the normalised
+# tensors.  The gradient of the raw input follows from the chain rule through the
+# norm: dx = r (dx^ - x^ mean_c(dx^_c x^_c)).
+
+RMS_EPS = 1e-6
+
+
+def rms_norm(x, eps: float = RMS_EPS) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) over the last axis, in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def rms_norm_bwd(x, dy, eps: float = RMS_EPS) -> np.ndarray:
+    """Gradient of sum(rms_norm(x) * dy) with respect to x."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x * r
+    return r * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
+
+
+def _normed(q, k, v, norm: str):
+    if set(norm) - set("qkv"):
+        raise ValueError(f"norm must be a subset of 'qkv', got {norm!r}")
+    return (rms_norm(q) if "q" in norm else np.asarray(q, np.float64),
+            rms_norm(k) if "k" in norm else np.asarray(k, np.float64),
+            rms_norm(v) if "v" in norm else np.asarray(v, np.float64))
+
+
+def norm_gdpa_fwd(q, k, v, q_off, kv_off, act: str, window: int = 0, norm: str = "qkv") -> np.ndarray:
+    """O of GDPA on the RMS-normalised tensors named in `norm`."""
+    qn, kn, vn = _normed(q, k, v, norm)
+    return gdpa_fwd(qn, kn, vn, q_off, kv_off, act, window)
+
+
+def norm_gdpa_bwd(q, k, v, do, q_off, kv_off, act: str, window: int = 0, norm: str = "qkv"):
+    """(dQ, dK, dV) with respect to the raw tensors for the loss sum(O * dO)."""
+    qn, kn, vn = _normed(q, k, v, norm)
+    dqn, dkn, dvn = gdpa_bwd(qn, kn, vn, do, q_off, kv_off, act, window)
+    return (rms_norm_bwd(q, dqn) if "q" in norm else dqn,
+            rms_norm_bwd(k, dkn) if "k" in norm else dkn,
+            rms_norm_bwd(v, dvn) if "v" in norm else dvn)
+
+
+# ---------------------------------------------------------------------------
 # JFA: softmax attention on the same jagged pairs
 # ---------------------------------------------------------------------------
 # GEM page, section "why high GPU utilisation is hard" (jagged attention kernels)

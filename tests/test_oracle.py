@@ -405,3 +405,90 @@ def test_jfa_backward_equals_torch_autograd(lq, lk, window):
         (ref * torch.tensor(do[qs:qe].transpose(1, 0, 2))).sum().backward()
         for got, want in ((dq[qs:qe], tq.grad), (dk[ks:ke], tk.grad), (dv[ks:ke], tv.grad)):
             np.testing.assert_allclose(got, want.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm prologue (reading: per (token, head) RMSNorm over d, no gain, eps 1e-6,
+# on the tensors named, right before GDPA; GDPA page, chart of tanh GELU against
+# the 6th-order series)
+# ---------------------------------------------------------------------------
+
+def raw_case(lq, lk, H=2, d=8, seed=0):
+    """Raw (unnormalised) inputs whose rows differ in scale by up to ~30x."""
+    q, k, v, do, qo, ko = rand_case(lq, lk, H=H, d=d, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    q, k, v = (x * np.exp(rng.normal(0.0, 1.0, x.shape[:2] + (1,))) for x in (q, k, v))
+    return q, k, v, do, qo, ko
+
+
+def test_rms_norm_equals_torch_rms_norm():
+    x = raw_case([7], [5], H=3, d=16, seed=1)[0]
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (16,), eps=1e-6).numpy()
+    np.testing.assert_allclose(R.rms_norm(x), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_rms_norm_bwd_matches_central_finite_differences():
+    x = raw_case([3], [2], H=2, d=6, seed=2)[0]
+    dy = np.random.default_rng(3).standard_normal(x.shape)
+    g = R.rms_norm_bwd(x, dy)
+    fd = np.zeros_like(x)
+    h = 1e-6
+    for idx in np.ndindex(*x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        fd[idx] = ((R.rms_norm(xp) * dy).sum() - (R.rms_norm(xm) * dy).sum()) / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("norm", ["qkv", "kv", "qk", ""])
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+def test_norm_gdpa_equals_torch_autograd(norm, act):
+    """Forward and raw-input gradients against torch's rms_norm and autograd (fp64)."""
+    lq, lk = [6, 0, 9, 4], [5, 3, 7, 0]
+    q, k, v, do, qo, ko = raw_case(lq, lk, H=2, d=8, seed=4)
+    o = R.norm_gdpa_fwd(q, k, v, qo, ko, act, 0, norm)
+    dq, dk, dv = R.norm_gdpa_bwd(q, k, v, do, qo, ko, act, 0, norm)
+    f = {"gelu": torch.nn.functional.gelu, "silu": torch.nn.functional.silu}[act]
+    nrm = lambda t, c: torch.nn.functional.rms_norm(t, (8,), eps=1e-6) if c in norm else t
+    for b in range(len(lq)):
+        Q = torch.tensor(q[qo[b]:qo[b + 1]], requires_grad=True)
+        K = torch.tensor(k[ko[b]:ko[b + 1]], requires_grad=True)
+        V = torch.tensor(v[ko[b]:ko[b + 1]], requires_grad=True)
+        S = torch.einsum("ihe,jhe->hij", nrm(Q, "q"), nrm(K, "k")) / 8 ** 0.5
+        O = torch.einsum("hij,jhe->ihe", f(S), nrm(V, "v"))
+        (O * torch.tensor(do[qo[b]:qo[b + 1]])).sum().backward()
+        np.testing.assert_allclose(o[qo[b]:qo[b + 1]], O.detach().numpy(), rtol=1e-11, atol=1e-12)
+        for got, t in ((dq[qo[b]:qo[b + 1]], Q), (dk[ko[b]:ko[b + 1]], K), (dv[ko[b]:ko[b + 1]], V)):
+            ref = t.grad.numpy() if t.grad is not None else np.zeros(t.shape)
+            np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_norm_gdpa_is_scale_invariant_and_gradients_orthogonal():
+    """Rescaling a normalised input's rows leaves O unchanged, and its raw gradient is
+    orthogonal to the row (both exactly so as eps -> 0; here to eps's order)."""
+    lq, lk = [9, 4], [6, 11]
+    q, k, v, do, qo, ko = raw_case(lq, lk, H=2, d=8, seed=5)
+    o = R.norm_gdpa_fwd(q, k, v, qo, ko, "gelu", 0, "qkv")
+    c = np.exp(np.random.default_rng(6).normal(0.0, 1.0, q.shape[:2] + (1,)))
+    # eps shifts r by a relative eps / (2 mean(x^2)) at most, on either side
+    ms = min(np.mean(q * q, -1).min(), np.mean((q * c) ** 2, -1).min())
+    tol = 10 * R.RMS_EPS / ms * np.abs(o).max()
+    assert np.abs(R.norm_gdpa_fwd(q * c, k, v, qo, ko, "gelu", 0, "qkv") - o).max() <= tol
+    for x, g in zip((q, k, v), R.norm_gdpa_bwd(q, k, v, do, qo, ko, "gelu", 0, "qkv")):
+        dots = np.abs((x * g).sum(-1))
+        assert dots.max() <= 1e-4 * (np.abs(x) * np.abs(g)).sum(-1).max()
+
+
+def test_norm_gdpa_without_norm_is_gdpa():
+    q, k, v, do, qo, ko = raw_case([5, 3], [4, 6], H=2, d=8, seed=7)
+    np.testing.assert_array_equal(R.norm_gdpa_fwd(q, k, v, qo, ko, "silu", 0, ""),
+                                  R.gdpa_fwd(q, k, v, qo, ko, "silu", 0))
+
+
+def test_pins_catch_a_norm_gradient_without_the_projection(monkeypatch):
+    """A plausible mistake, dx = r dx^ (dropping the term through r), fails the autograd pin."""
+    monkeypatch.setattr(R, "rms_norm_bwd", lambda x, dy, eps=1e-6: dy / np.sqrt(
+        np.mean(np.asarray(x) ** 2, axis=-1, keepdims=True) + eps))
+    with pytest.raises(AssertionError):
+        test_norm_gdpa_equals_torch_autograd("qkv", "gelu")
