@@ -258,6 +258,33 @@ gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const 
                             const float* stat, void* dq, void* stream);
 
 /*
+ * gdpa_norm_fwd / gdpa_norm_bwd - GDPA with a fused RMSNorm prologue: the inputs
+ * named by `norm` (a combination of 1 = Q, 2 = K, 4 = V) are taken through a
+ * per-(token, head) RMSNorm over d, x^ = x / sqrt(mean(x^2) + 1e-6) with no gain,
+ * before the attention (GDPA page, "Section details", chart of tanh GELU against
+ * the 6th-order series: RMSNorm keeps the activation's inputs in range).  The
+ * kernels read the raw tensors and scale by each row's 1/rms, so no normalised
+ * copy is written; gdpa_norm_bwd returns the gradients of the RAW inputs,
+ * dx = r (dx^ - x^ mean(dx^ x^)) for a normalised input (dx^ otherwise).
+ * Arguments as gdpa_fwd / gdpa_bwd, plus
+ *   norm : 0..7 as above;
+ *   rstd : device fp32 scratch of H * (Tq + 2 Tk) floats: gdpa_norm_fwd writes the
+ *          factors there ([H, Tq] for Q, then [H, Tk, 2] pairs for K and V; 1 for a
+ *          tensor not normalised) and gdpa_norm_bwd reads them, so pass the
+ *          forward's buffer, unchanged, with the same q, k, v and norm.
+ * Enqueues a pre-pass and the forward kernel (gdpa_norm_fwd), or the dK/dV and dQ
+ * kernels (gdpa_norm_bwd; never the one-pass kernels), plus chunk reductions.
+ * bf16 plans only; act = GDPA_ACT_ONE is rejected (UNSUPPORTED).  Errors as
+ * gdpa_fwd / gdpa_bwd.
+ */
+gdpa_status gdpa_norm_fwd(gdpa_plan plan, const void* q, const void* k, const void* v, const int32_t* q_off_dev,
+                          const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act, int window, int norm,
+                          float* rstd, void* o, void* stream);
+gdpa_status gdpa_norm_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                          const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
+                          int window, int norm, const float* rstd, void* dq, void* dk, void* dv, void* stream);
+
+/*
  * pFFN as GDPA (GDPA page, "Section details", diagram of self-attention, PMA and
  * pFFN unified as GDPA).  The page gives no formula; read here as: per head,
  * weight matrices W_K, W_V [M, H, d] shared by every query row of the batch,

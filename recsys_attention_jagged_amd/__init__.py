@@ -83,6 +83,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_jfa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                  _vp]
+    lib.gdpa_norm_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
+    lib.gdpa_norm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                  _vp]
     lib.gdpa_jfa_bwd_stat.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]
     lib.gdpa_jfa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
@@ -92,7 +95,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
                  "gdpa_plan_export", "gdpa_plan_stats", "gdpa_pffn_plan_create", "gdpa_pffn_fwd",
                  "gdpa_pffn_bwd", "gdpa_jfa_fwd", "gdpa_jfa_bwd", "gdpa_jfa_bwd_stat", "gdpa_jfa_bwd_dkdv",
-                 "gdpa_jfa_bwd_dq"):
+                 "gdpa_jfa_bwd_dq", "gdpa_norm_fwd", "gdpa_norm_bwd"):
         getattr(lib, name).restype = _i
     if path == LIB_PATH:
         _lib = lib
@@ -202,6 +205,31 @@ def gdpa_jfa_bwd_dq(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, window,
     _check(load_library().gdpa_jfa_bwd_dq(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
                                           _ptr(kv_off_dev), B, H, d, window, _ptr(stat), _ptr(dq),
                                           _stream(stream)))
+
+
+NORM_BITS = {"q": 1, "k": 2, "v": 4}
+
+
+def norm_code(norm) -> int:
+    """"qkv"-style subset (or an int 0..7) -> the library's norm bits."""
+    if isinstance(norm, int):
+        return norm
+    return sum(NORM_BITS[c] for c in set(norm))
+
+
+def gdpa_norm_fwd(plan, q, k, v, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, o, stream=None):
+    """GDPA with a fused RMSNorm prologue on the tensors in `norm`; rstd: fp32 H (Tq + 2 Tk) scratch."""
+    _check(load_library().gdpa_norm_fwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(q_off_dev), _ptr(kv_off_dev), B, H,
+                                        d, _enum(act, ACT), window, norm_code(norm), _ptr(rstd), _ptr(o),
+                                        _stream(stream)))
+
+
+def gdpa_norm_bwd(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, dq, dk, dv,
+                  stream=None):
+    """Raw-input gradients of gdpa_norm_fwd, reading the forward's rstd."""
+    _check(load_library().gdpa_norm_bwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
+                                        _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, norm_code(norm),
+                                        _ptr(rstd), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def _opts(host_only, bins, team, blocks, deal, split, unfused):

@@ -37,7 +37,8 @@ UNITS = [("plan.o", "plan.cpp", []),
          ("api.o", "api.cpp", []),
          ("fp32.o", "fp32.hip", []),
          ("partials.o", "partials.hip", []),
-         ("jfa.o", "jfa.hip", [])]
+         ("jfa.o", "jfa.hip", []),
+         ("norm.o", "norm.hip", [])]
 for _d in (32, 64, 128):
     UNITS.append((f"fwd_d{_d}.o", "fwd_bf16.hip", [f"-DGDPA_D={_d}"]))
     UNITS.append((f"bwd_d{_d}.o", "bwd_bf16.hip", [f"-DGDPA_D={_d}"]))

@@ -311,6 +311,9 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
     return GDPA_OK;
 }
 
+// RMSNorm prologue: eps under the root
+constexpr float kRmsEps = 1e-6f;
+
 static gdpa_status check_call(gdpa_plan plan, const int32_t* q_off_dev, const int32_t* kv_off_dev, int B,
                               int H, int d, gdpa_act act, int window) {
     if (!plan) return fail(GDPA_ERR_INVALID_ARG, "plan is NULL");
@@ -643,6 +646,116 @@ gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const 
     if (st != GDPA_OK) return st;
     return jfa_grads(plan, q, k, v, dout, q_off_dev, kv_off_dev, stat, dq, nullptr, nullptr, (hipStream_t)stream,
                      false, true);
+}
+
+// the RMSNorm prologue's checks and its factor arrays inside `rstd`
+static gdpa_status norm_check(gdpa_plan plan, gdpa_act act, int norm, const float* rstd) {
+    if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "the RMSNorm prologue runs on bf16 plans");
+    if (act == GDPA_ACT_ONE) return fail(GDPA_ERR_UNSUPPORTED, "GDPA_ACT_ONE has no RMSNorm-prologue kernels");
+    if (norm < 0 || norm > 7) return fail(GDPA_ERR_INVALID_ARG, "norm must be a combination of 1 (Q), 2 (K), 4 (V)");
+    if ((plan->Tq > 0 || plan->Tk > 0) && !rstd) return fail(GDPA_ERR_INVALID_ARG, "rstd is NULL");
+    return GDPA_OK;
+}
+
+static void norm_args(gdpa_plan plan, int norm, const float* rstd, KernelArgs& a) {
+    a.rq = rstd;
+    a.rkv = rstd ? rstd + (size_t)plan->H * plan->Tq : nullptr;
+    a.Tq = (int)plan->Tq;
+    a.Tk = (int)plan->Tk;
+    a.norm = norm;
+}
+
+gdpa_status gdpa_norm_fwd(gdpa_plan plan, const void* q, const void* k, const void* v, const int32_t* q_off_dev,
+                          const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act, int window, int norm,
+                          float* rstd, void* o, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
+    if (st == GDPA_OK) st = norm_check(plan, act, norm, rstd);
+    if (st != GDPA_OK) return st;
+    if (plan->Tq > 0 && (!q || !o)) return fail(GDPA_ERR_INVALID_ARG, "q or o is NULL");
+    if (plan->Tk > 0 && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    norm_args(plan, norm, rstd, a);
+    hipError_t e = launch_norm_rstd(q, k, v, (int)plan->Tq, (int)plan->Tk, H, d, norm, kRmsEps, rstd,
+                                    rstd + (size_t)H * plan->Tq, s);
+    if (e != hipSuccess) return fail_hip(e, "RMSNorm pre-pass launch");
+    if (plan->Tq == 0) return GDPA_OK;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    const WorkList& wl = plan->lists[LIST_FWD];
+    a.items = plan->d_items[LIST_FWD];
+    a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+    a.P = wl.P;
+    a.part = plan->d_part[LIST_FWD];
+    const int code = (int)act | kActNorm;
+    switch (d) {
+        case 32: e = launch_fwd_bf16_d32(a, wl.team, wl.nb, code, s); break;
+        case 64: e = launch_fwd_bf16_d64(a, wl.team, wl.nb, code, s); break;
+        default: e = launch_fwd_bf16_d128(a, wl.team, wl.nb, code, s); break;
+    }
+    if (e == hipSuccess) e = reduce_parts(plan, LIST_FWD, 1.0f, o, s);
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no RMSNorm-prologue forward kernel here");
+    if (e != hipSuccess) return fail_hip(e, "forward launch");
+    return GDPA_OK;
+}
+
+gdpa_status gdpa_norm_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                          const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
+                          int window, int norm, const float* rstd, void* dq, void* dk, void* dv, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
+    if (st == GDPA_OK) st = norm_check(plan, act, norm, rstd);
+    if (st != GDPA_OK) return st;
+    const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
+    if (any_q && (!q || !dout || !dq)) return fail(GDPA_ERR_INVALID_ARG, "q, dout or dq is NULL");
+    if (any_k && (!k || !v || !dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "k, v, dk or dv is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    norm_args(plan, norm, rstd, a);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    const int code = (int)act | kActNorm;
+    hipError_t e = hipSuccess;
+    if (any_k) {
+        const WorkList& wl = plan->lists[LIST_DKDV];
+        KernelArgs b = a;
+        b.items = plan->d_items[LIST_DKDV];
+        b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+        b.P = wl.P;
+        b.part = plan->d_part[LIST_DKDV];
+        switch (d) {
+            case 32: e = launch_dkdv_bf16_d32(b, wl.team, wl.nb, code, s); break;
+            case 64: e = launch_dkdv_bf16_d64(b, wl.team, wl.nb, code, s); break;
+            default: e = launch_dkdv_bf16_d128(b, wl.team, wl.nb, code, s); break;
+        }
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
+    }
+    if (e == hipSuccess && any_q) {
+        const WorkList& wl = plan->lists[LIST_DQ];
+        KernelArgs b = a;
+        b.items = plan->d_items[LIST_DQ];
+        b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+        b.P = wl.P;
+        b.part = plan->d_part[LIST_DQ];
+        switch (d) {
+            case 32: e = launch_dq_bf16_d32(b, wl.team, wl.nb, code, s); break;
+            case 64: e = launch_dq_bf16_d64(b, wl.team, wl.nb, code, s); break;
+            default: e = launch_dq_bf16_d128(b, wl.team, wl.nb, code, s); break;
+        }
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
+    }
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no RMSNorm-prologue backward kernel here");
+    if (e != hipSuccess) return fail_hip(e, "backward launch");
+    return GDPA_OK;
 }
 
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,

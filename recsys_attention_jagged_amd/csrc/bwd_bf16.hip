@@ -30,6 +30,15 @@
 // them into a side buffer of the tile's ring slot (ring.hpp), and jobs without
 // statistics load a zero-range side so that every job counts the same.  Keys past
 // a sample's length are masked in dQ: exp(0 - LSE) is not 0 there.
+//
+// With the RMSNorm prologue (NORM) the inputs are raw and each row's 1/rms r (from a
+// pre-pass, carried in the side buffers like the JFA statistics) scales the
+// products: S_ij = r_q,i r_k,j (q_i . k_j) / sqrt(d), dP_ij = r_v,j (dO_i . v_j), and
+// the gradients of the normalised rows are dQ^_i = sum_j (dS_ij r_k,j) k_j / sqrt(d),
+// dK^_j = sum_i (dS_ij r_q,i) q_i / sqrt(d), dV^_j = sum_i P_ij dO_i.  The item's end
+// takes each normalised tensor's gradient through the norm,
+// dx = r (dx^ - x^ mean_c(dx^_c x^_c)) with x^ = r x, reading the stationary rows
+// once more from their tile in the accumulator's column layout.
 #include "bwd_common.hpp"
 #include "kernels.hpp"
 #include "ring.hpp"
@@ -44,7 +53,39 @@ namespace {
 // =========================================================================
 // dQ (Q-stationary)
 // =========================================================================
-template <int D, int T, int NB, int ACT>
+// gradient through the RMSNorm of one 32-row block: lane (r, hh) holds row r's
+// columns 32 db + 8 j + 4 hh + i of the normalised input's gradient in element
+// 4 j + i of acc[db] and the raw input's same columns in x[db][j]; rr = 1/rms.
+template <int NDB>
+__device__ __forceinline__ void norm_grad(f32x16 (&acc)[NDB], const bf16x4 (&x)[NDB][4], float rr) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dot = __builtin_fmaf(acc[db][4 * j + i], (float)x[db][j][i], dot);
+    dot += __shfl_xor(dot, 32);
+    const float m = dot * rr * rr * (1.0f / (32 * NDB));   // mean(dx^ x^) with x^ = rr x
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[db][4 * j + i] = rr * __builtin_fmaf(-(float)x[db][j][i], m, acc[db][4 * j + i]);
+}
+
+// a 32-row tile's row r in the accumulator's column layout (see norm_grad)
+template <int D>
+__device__ __forceinline__ void lds_acc_row(const char* tile, int r, int hh, bf16x4 (&x)[D / 32][4]) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[db][j] = *(const bf16x4*)(tile + tile_off<D>(r, 4 * db + j) + 8 * hh);
+}
+
+template <int D, int T, int NB, int ACT, int NORM>
 struct DqPol : Common {
     // stationary tiles, wave-major: (Q, dO) of block 0, (Q, dO) of block 1, ...
     static constexpr int NSTAT = 2 * T * NB, NSTRM = 2;
@@ -57,6 +98,9 @@ struct DqPol : Common {
     bf16x8 qf[NB][NKS], of[NB][NKS];
     f32x16 acc[NB][NDB];
     float l2q[NB], dq_[NB];  // softmax: this lane's q row's LSE log2(e) and D
+    rsrc_t wrq, wrkv;        // NORM: 1/rms of the item's q rows, (k, v) row pairs
+    float rqv[NB];           // NORM: 1/rms of this lane's q row
+    bf16x4 qa[NORM ? NB : 1][D / 32][4];   // NORM: this lane's q row in the accumulator's layout
 
     __device__ DqPol(const KernelArgs& args, int lane_, int wt_) : Common(args, lane_, wt_, D) {}
 
@@ -73,12 +117,17 @@ struct DqPol : Common {
             wst = slice_rsrc(a.stat + ((size_t)w.h * a.Tq + w.qs) * 2, w.lq, 8u, 8u);
             wnull = slice_rsrc(a.stat, 0, 8u, 8u);
         }
+        if constexpr (NORM) {
+            wrq = slice_rsrc(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wrkv = slice_rsrc(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
+            wnull = slice_rsrc(a.rkv, 0, 8u, 8u);
+        }
     }
 
-    // tile rows at byte offset `off` of `t`; softmax: and the side at x_off of `xs`
+    // tile rows at byte offset `off` of `t`; softmax, NORM: and the side at x_off of `xs`
     template <class RingT>
     __device__ __forceinline__ void put(RingT& g, rsrc_t t, uint32_t off, rsrc_t xs, uint32_t x_off) {
-        if constexpr (SM)
+        if constexpr (SM || NORM)
             g.issue(t, off, xs, x_off);
         else
             g.issue(t, off);
@@ -88,10 +137,17 @@ struct DqPol : Common {
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
             const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * (i >> 1));
-            put(g, (i & 1) ? wo : wq, row0 * rs, (i & 1) ? wnull : wst, row0 * 8u);
+            if constexpr (NORM)
+                put(g, (i & 1) ? wo : wq, row0 * rs, (i & 1) ? wnull : wrq, row0 * 4u);
+            else
+                put(g, (i & 1) ? wo : wq, row0 * rs, (i & 1) ? wnull : wst, row0 * 8u);
         } else {
             const int rel = i - NSTAT;
-            put(g, (rel & 1) ? wv : wk, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs, wnull, 0u);
+            const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
+            if constexpr (NORM)
+                put(g, (rel & 1) ? wv : wk, row0 * rs, (rel & 1) ? wnull : wrkv, row0 * 8u);
+            else
+                put(g, (rel & 1) ? wv : wk, row0 * rs, wnull, 0u);
         }
     }
 
@@ -116,6 +172,10 @@ struct DqPol : Common {
                 const float2 st = *(const float2*)(g.side(job) + 8 * r);
                 l2q[blk % NB] = st.x;
                 dq_[blk % NB] = st.y;
+            }
+            if constexpr (NORM) {   // the Q job's side: 1/rms of this lane's q row; the row for the norm's gradient
+                rqv[blk % NB] = *(const float*)(g.side(job) + 4 * r);
+                lds_acc_row<D>(g.tile(job), r, hh, qa[blk % NB]);
             }
         }
     }
@@ -153,6 +213,23 @@ struct DqPol : Common {
         const char* kt = g.tile(job);
         const char* vt = g.tile(job + 1);
         bf16x8 kop[NKS], vop[NKS];
+        // NORM: (1/rms of k, of v) of keys j0 + 8 j + 4 hh + {0, 1} and {2, 3}, from the K job's side
+        float4 rkv[NORM ? 4 : 1][2];
+        if constexpr (NORM) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                rkv[j][0] = *(const float4*)(g.side(job) + 8 * (8 * j + 4 * hh));
+                rkv[j][1] = *(const float4*)(g.side(job) + 8 * (8 * j + 4 * hh) + 16);
+            }
+        }
+        auto fk = [&](int e) -> float {
+            if constexpr (NORM) return (e & 1) ? rkv[e >> 2][(e >> 1) & 1].z : rkv[e >> 2][(e >> 1) & 1].x;
+            else return 1.0f;
+        };
+        auto fv = [&](int e) -> float {
+            if constexpr (NORM) return (e & 1) ? rkv[e >> 2][(e >> 1) & 1].w : rkv[e >> 2][(e >> 1) & 1].y;
+            else return 1.0f;
+        };
         if constexpr (HOIST) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -187,21 +264,23 @@ struct DqPol : Common {
                 } else if (win > 0 && !band_all(q0, j0, win)) {
                     // lane column: query q0 + r; element e: key j0 + 8 (e/4) + 4 hh + e % 4
                     const int base = q0 + r - j0 - 4 * hh;
+                    const float cq = NORM ? scale * rqv[b] : scale;
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
                         const int e = 8 * m + k;
                         float f, gr;
-                        act_fwd_grad<ACT>(sc[b][e] * scale, f, gr);
+                        act_fwd_grad<ACT>(sc[b][e] * cq * fk(e), f, gr);
                         const int dd = base - (8 * (e >> 2) + (e & 3));
-                        dsb[b][k] = (__bf16)(in_band(dd, win) ? dp[b][e] * gr : 0.0f);
+                        dsb[b][k] = (__bf16)(in_band(dd, win) ? dp[b][e] * fv(e) * gr * fk(e) : 0.0f);
                     }
                 } else {
+                    const float cq = NORM ? scale * rqv[b] : scale;
 #pragma unroll
                     for (int k = 0; k < 8; ++k) {
                         const int e = 8 * m + k;
                         float f, gr;
-                        act_fwd_grad<ACT>(sc[b][e] * scale, f, gr);
-                        dsb[b][k] = (__bf16)(dp[b][e] * gr);
+                        act_fwd_grad<ACT>(sc[b][e] * cq * fk(e), f, gr);
+                        dsb[b][k] = (__bf16)(dp[b][e] * fv(e) * gr * fk(e));
                     }
                 }
             }
@@ -216,6 +295,12 @@ struct DqPol : Common {
 
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        if constexpr (NORM) {   // through the norm (linear in dQ^, so chunks may take it separately)
+            if (a.norm & 1) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) norm_grad<NDB>(acc[b], qa[b], rqv[b]);
+            }
+        }
         if (c.part >= 0) {   // one chunk of a cut item: fp32 partial block (scaled by the reduction)
 #pragma unroll
             for (int b = 0; b < NB; ++b) store_partial<NDB>(acc[b], a.part, c.part, ROWS, 32 * (wt * NB + b), r, hh);
@@ -237,7 +322,7 @@ struct DqPol : Common {
 // =========================================================================
 // dK / dV (KV-stationary)
 // =========================================================================
-template <int D, int T, int ACT>
+template <int D, int T, int ACT, int NORM>
 struct DkdvPol : Common {
     // stationary tiles, wave-major: (K, V) of wave 0's block, then wave 1's
     static constexpr int NSTAT = 2 * T, NSTRM = 2;
@@ -247,6 +332,9 @@ struct DkdvPol : Common {
     static constexpr bool SM = ACT == ACT_SOFTMAX;
     rsrc_t wk, wv, wq, wo;   // issuing side
     rsrc_t wst, wnull;       // softmax: row statistics of the item's q rows; a zero-range side
+    rsrc_t wrq, wrkv;        // NORM: 1/rms of the item's q rows, (k, v) row pairs
+    float rkl, rvl;          // NORM: 1/rms of this lane's k and v rows
+    bf16x4 ka[NORM ? D / 32 : 1][4], va[NORM ? D / 32 : 1][4];   // NORM: those rows in the accumulator's layout
     bf16x8 kf[NKS], vf[NKS];
     f32x16 accK[NDB], accV[NDB];
 
@@ -265,12 +353,17 @@ struct DkdvPol : Common {
             wst = slice_rsrc(a.stat + ((size_t)w.h * a.Tq + w.qs) * 2, w.lq, 8u, 8u);
             wnull = slice_rsrc(a.stat, 0, 8u, 8u);
         }
+        if constexpr (NORM) {
+            wrq = slice_rsrc(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wrkv = slice_rsrc(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
+            wnull = slice_rsrc(a.rkv, 0, 8u, 8u);
+        }
     }
 
-    // tile rows at byte offset `off` of `t`; softmax: and the side at x_off of `xs`
+    // tile rows at byte offset `off` of `t`; softmax, NORM: and the side at x_off of `xs`
     template <class RingT>
     __device__ __forceinline__ void put(RingT& g, rsrc_t t, uint32_t off, rsrc_t xs, uint32_t x_off) {
-        if constexpr (SM)
+        if constexpr (SM || NORM)
             g.issue(t, off, xs, x_off);
         else
             g.issue(t, off);
@@ -279,11 +372,15 @@ struct DkdvPol : Common {
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            put(g, (i & 1) ? wv : wk, (uint32_t)(w.t * ROWS + 32 * (i >> 1)) * rs, wnull, 0u);
+            const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * (i >> 1));
+            put(g, (i & 1) ? wv : wk, row0 * rs, (NORM && !(i & 1)) ? wrkv : wnull, row0 * 8u);
         } else {
             const int rel = i - NSTAT;
             const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
-            put(g, (rel & 1) ? wo : wq, row0 * rs, (rel & 1) ? wnull : wst, row0 * 8u);
+            if constexpr (NORM)
+                put(g, (rel & 1) ? wo : wq, row0 * rs, (rel & 1) ? wnull : wrq, row0 * 4u);
+            else
+                put(g, (rel & 1) ? wo : wq, row0 * rs, (rel & 1) ? wnull : wst, row0 * 8u);
         }
     }
 
@@ -300,6 +397,13 @@ struct DkdvPol : Common {
             for (int ks = 0; ks < NKS; ++ks) {
                 kf[ks] = lds_row8<D>(g.tile(job), r, 2 * ks + hh);
                 vf[ks] = lds_row8<D>(g.tile(job + 1), r, 2 * ks + hh);
+            }
+            if constexpr (NORM) {   // the K job's side: (1/rms of k, of v) of this lane's row; the rows for the norm
+                const float2 f = *(const float2*)(g.side(job) + 8 * r);
+                rkl = f.x;
+                rvl = f.y;
+                lds_acc_row<D>(g.tile(job), r, hh, ka);
+                lds_acc_row<D>(g.tile(job + 1), r, hh, va);
             }
         }
     }
@@ -318,6 +422,16 @@ struct DkdvPol : Common {
                 st[j][1] = *(const float4*)(g.side(job) + 8 * (8 * j + 4 * hh) + 16);
             }
         }
+        // NORM: 1/rms of q rows i0 + 8 j + 4 hh + {0..3}, from the Q job's side
+        float4 rqs[NORM ? 4 : 1];
+        if constexpr (NORM) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) rqs[j] = *(const float4*)(g.side(job) + 4 * (8 * j + 4 * hh));
+        }
+        auto fq = [&](int e) -> float {
+            if constexpr (NORM) return rqs[e >> 2][e & 3];
+            else return 1.0f;
+        };
         if constexpr (HOIST) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
@@ -357,22 +471,24 @@ struct DkdvPol : Common {
             }
         } else if (win > 0 && !band_all(i0, j0, win)) {
             const int base = i0 + 4 * hh - j0 - r;
+            const float ck = NORM ? scale * rkl : scale, cv = NORM ? rvl : 1.0f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float f, gr;
-                act_fwd_grad<ACT>(sc[e] * scale, f, gr);
+                act_fwd_grad<ACT>(sc[e] * ck * fq(e), f, gr);
                 const int dd = base + 8 * (e >> 2) + (e & 3);
                 const bool ok = in_band(dd, win);
                 p[e] = ok ? f : 0.0f;
-                ds[e] = ok ? dp[e] * gr : 0.0f;
+                ds[e] = ok ? dp[e] * cv * gr * fq(e) : 0.0f;
             }
         } else {
+            const float ck = NORM ? scale * rkl : scale, cv = NORM ? rvl : 1.0f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 float f, gr;
-                act_fwd_grad<ACT>(sc[e] * scale, f, gr);
+                act_fwd_grad<ACT>(sc[e] * ck * fq(e), f, gr);
                 p[e] = f;
-                ds[e] = dp[e] * gr;
+                ds[e] = dp[e] * cv * gr * fq(e);
             }
         }
 #pragma unroll
@@ -388,6 +504,10 @@ struct DkdvPol : Common {
 
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        if constexpr (NORM) {   // through the norms (linear in dK^, dV^, so chunks may take them separately)
+            if (a.norm & 2) norm_grad<NDB>(accK, ka, rkl);
+            if (a.norm & 4) norm_grad<NDB>(accV, va, rvl);
+        }
         if (c.part >= 0) {   // one chunk of a cut item: fp32 partial dK, dV blocks (scaled by the reduction)
             store_partial<NDB>(accK, a.part, 2 * c.part, ROWS, 32 * wt, r, hh);
             store_partial<NDB>(accV, a.part, 2 * c.part + 1, ROWS, 32 * wt, r, hh);
@@ -405,45 +525,55 @@ struct DkdvPol : Common {
     }
 };
 
-template <int D, int T, int NB, int ACT>
+template <int D, int T, int NB, int ACT, int NORM>
 __global__ __launch_bounds__((TeamShape<D, T, 2>::THREADS), (TeamShape<D, T, 2>::WPE)) void dq_bf16_kernel(
     const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
-    using RingT = Ring<D, T, TeamShape<D, T, 2>::LDS, ACT == ACT_SOFTMAX ? 1 : 0>;
+    using RingT = Ring<D, T, TeamShape<D, T, 2>::LDS, (ACT == ACT_SOFTMAX || NORM) ? 1 : 0>;
     __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
     const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
-    DqPol<D, T, NB, ACT> pol(a, lane, wt);
-    run_team<DqPol<D, T, NB, ACT>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt, lane);
+    DqPol<D, T, NB, ACT, NORM> pol(a, lane, wt);
+    run_team<DqPol<D, T, NB, ACT, NORM>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt, lane);
 }
 
-template <int D, int T, int ACT>
+template <int D, int T, int ACT, int NORM>
 __global__ __launch_bounds__((TeamShape<D, T, 1>::THREADS), (TeamShape<D, T, 1>::WPE)) void dkdv_bf16_kernel(
     const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
-    using RingT = Ring<D, T, TeamShape<D, T, 1>::LDS, ACT == ACT_SOFTMAX ? 1 : 0>;
+    using RingT = Ring<D, T, TeamShape<D, T, 1>::LDS, (ACT == ACT_SOFTMAX || NORM) ? 1 : 0>;
     __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
     const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
-    DkdvPol<D, T, ACT> pol(a, lane, wt);
-    run_team<DkdvPol<D, T, ACT>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt, lane);
+    DkdvPol<D, T, ACT, NORM> pol(a, lane, wt);
+    run_team<DkdvPol<D, T, ACT, NORM>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt, lane);
 }
 
-template <int T, int NB, int ACT>
+template <int T, int NB, int ACT, int NORM = 0>
 const void* dq_ptr() {
-    return (const void*)&dq_bf16_kernel<GDPA_D, T, NB, ACT>;
+    return (const void*)&dq_bf16_kernel<GDPA_D, T, NB, ACT, NORM>;
 }
-template <int T, int NB, int ACT>
+template <int T, int NB, int ACT, int NORM = 0>
 const void* dkdv_ptr() {
-    return (const void*)&dkdv_bf16_kernel<GDPA_D, T, ACT>;
+    return (const void*)&dkdv_bf16_kernel<GDPA_D, T, ACT, NORM>;
 }
 
-#define GDPA_ACT_SWITCH(F, T, NB)                                       \
-    switch (act) {                                                      \
-        case ACT_GELU: return F<T, NB, ACT_GELU>();                     \
-        case ACT_SILU: return F<T, NB, ACT_SILU>();                     \
-        case ACT_GELU_POLY: return F<T, NB, ACT_GELU_POLY>();           \
-        case ACT_GELU_TAYLOR6: return F<T, NB, ACT_GELU_TAYLOR6>();     \
-        case ACT_IDENTITY: return F<T, NB, ACT_IDENTITY>();             \
-    }                                                                   \
+#define GDPA_ACT_SWITCH(F, T, NB)                                                           \
+    if (act & kActNorm) {   /* the RMSNorm-prologue variants */                             \
+        switch (act & ~kActNorm) {                                                          \
+            case ACT_GELU: return F<T, NB, ACT_GELU, 1>();                                  \
+            case ACT_SILU: return F<T, NB, ACT_SILU, 1>();                                  \
+            case ACT_GELU_POLY: return F<T, NB, ACT_GELU_POLY, 1>();                        \
+            case ACT_GELU_TAYLOR6: return F<T, NB, ACT_GELU_TAYLOR6, 1>();                  \
+            case ACT_IDENTITY: return F<T, NB, ACT_IDENTITY, 1>();                          \
+        }                                                                                   \
+        return nullptr;                                                                     \
+    }                                                                                       \
+    switch (act) {                                                                          \
+        case ACT_GELU: return F<T, NB, ACT_GELU>();                                         \
+        case ACT_SILU: return F<T, NB, ACT_SILU>();                                         \
+        case ACT_GELU_POLY: return F<T, NB, ACT_GELU_POLY>();                               \
+        case ACT_GELU_TAYLOR6: return F<T, NB, ACT_GELU_TAYLOR6>();                         \
+        case ACT_IDENTITY: return F<T, NB, ACT_IDENTITY>();                                 \
+    }                                                                                       \
     return nullptr;
 
 template <int T, int NB>

@@ -22,6 +22,12 @@
 // accumulator rescaled when the max moves) instead of the activation; there the
 // keys beyond a sample's length are masked too, and the item's end divides by the
 // row sum and stores the row's log-sum-exp.
+//
+// With the RMSNorm prologue (NORM) the kernels read the raw Q, K, V and scale by
+// each row's 1 / rms instead of normalising the tensors: S_ij = r_q,i r_k,j (q_i . k_j)
+// / sqrt(d), and P_ij r_v,j takes the place of P_ij (O = sum_j P_ij r_v,j v_j).  The
+// factors of a tile's 32 rows (a pre-pass writes them) travel with the tile in the
+// ring's side buffers: r_q with each Q tile, (r_k, r_v) pairs with each K tile.
 #include "kernels.hpp"
 #include "ring.hpp"
 
@@ -32,7 +38,7 @@
 namespace gdpa {
 namespace {
 
-template <int D, int T, int NB, int ACT>
+template <int D, int T, int NB, int ACT, int NORM>
 struct FwdPol {
     static constexpr int NSTAT = T * NB, NSTRM = 2;   // stationary tiles: wave-major q blocks
     static constexpr int NDB = D / 32, NKS = D / 16;
@@ -44,7 +50,9 @@ struct FwdPol {
     uint32_t rs, rso;
     float scale;
     rsrc_t wq, wk, wv;    // issuing side: slices of the walk's current item
+    rsrc_t wrq, wrkv, wnull;   // NORM: 1/rms of the item's q rows, (k, v) row pairs; a zero-range side
     bf16x8 qf[NB][NKS];
+    float rqv[NB];        // NORM: 1/rms of this lane's q row
     f32x16 acc[NB][NDB];
     // softmax only: running max (log2 units) of this lane's q row and this lane's
     // share of the running sum (the other share sits in lane ^ 32)
@@ -70,15 +78,28 @@ struct FwdPol {
         wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
         wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
         wq = slice_rsrc((const __bf16*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs, D * 2);
+        if constexpr (NORM) {
+            wrq = slice_rsrc(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wrkv = slice_rsrc(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
+            wnull = slice_rsrc(a.rkv, 0, 8u, 8u);
+        }
     }
 
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            g.issue(wq, (uint32_t)(w.t * ROWS + 32 * i) * rs);
+            const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * i);
+            if constexpr (NORM)
+                g.issue(wq, row0 * rs, wrq, row0 * 4u);
+            else
+                g.issue(wq, row0 * rs);
         } else {
             const int rel = i - NSTAT;
-            g.issue((rel & 1) ? wv : wk, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
+            const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
+            if constexpr (NORM)
+                g.issue((rel & 1) ? wv : wk, row0 * rs, (rel & 1) ? wnull : wrkv, row0 * 8u);
+            else
+                g.issue((rel & 1) ? wv : wk, row0 * rs);
         }
     }
 
@@ -154,6 +175,7 @@ struct FwdPol {
             if (tile < NSTAT && tile / NB == wt) {
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) qf[tile % NB][ks] = lds_row8<D>(g.tile(job + u), r, 2 * ks + hh);
+                if constexpr (NORM) rqv[tile % NB] = *(const float*)(g.side(job + u) + 4 * r);
             }
         }
     }
@@ -165,6 +187,24 @@ struct FwdPol {
         // with one wave per SIMD all operand reads are issued up front so their
         // latency overlaps the MFMAs; with two, each is read just before use
         bf16x8 kop[NKS], vop[2][NDB];
+        // NORM: (1/rms of k, of v) of keys j0 + 8 j + 4 hh + {0, 1} and {2, 3}, from the K job's side
+        float4 rkv[NORM ? 4 : 1][2];
+        if constexpr (NORM) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                rkv[j][0] = *(const float4*)(g.side(job) + 8 * (8 * j + 4 * hh));
+                rkv[j][1] = *(const float4*)(g.side(job) + 8 * (8 * j + 4 * hh) + 16);
+            }
+        }
+        // element e's key factors
+        auto fk = [&](int e) -> float {
+            if constexpr (NORM) return (e & 1) ? rkv[e >> 2][(e >> 1) & 1].z : rkv[e >> 2][(e >> 1) & 1].x;
+            else return 1.0f;
+        };
+        auto fv = [&](int e) -> float {
+            if constexpr (NORM) return (e & 1) ? rkv[e >> 2][(e >> 1) & 1].w : rkv[e >> 2][(e >> 1) & 1].y;
+            else return 1.0f;
+        };
         if constexpr (HOIST) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
@@ -193,15 +233,17 @@ struct FwdPol {
             } else if (win > 0 && !band_all(q0, j0, win)) {
                 // lane column: query q0 + r; element c: key j0 + 8 (c/4) + 4 hh + c % 4
                 const int base = q0 + r - j0 - 4 * hh;
+                const float cq = NORM ? scale * rqv[b] : scale;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int dd = base - (8 * (e >> 2) + (e & 3));
-                    const float f = act_fwd<ACT>(sc[b][e] * scale);
+                    const float f = act_fwd<ACT>(sc[b][e] * cq * fk(e)) * fv(e);
                     p[e] = in_band(dd, win) ? f : 0.0f;
                 }
             } else {
+                const float cq = NORM ? scale * rqv[b] : scale;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) p[e] = act_fwd<ACT>(sc[b][e] * scale);
+                for (int e = 0; e < 16; ++e) p[e] = act_fwd<ACT>(sc[b][e] * cq * fk(e)) * fv(e);
             }
             pb[b][0] = acc_to_bf16x8(p, 0);
             pb[b][1] = acc_to_bf16x8(p, 1);
@@ -289,24 +331,35 @@ struct FwdPol {
     }
 };
 
-template <int D, int T, int NB, int ACT>
+template <int D, int T, int NB, int ACT, int NORM>
 __global__ __launch_bounds__((TeamShape<D, T, 0>::THREADS), (TeamShape<D, T, 0>::WPE)) void fwd_bf16_kernel(
     const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
-    using RingT = Ring<D, T, TeamShape<D, T, 0>::LDS>;
+    using RingT = Ring<D, T, TeamShape<D, T, 0>::LDS, NORM ? 1 : 0>;
     __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
     const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
-    FwdPol<D, T, NB, ACT> pol(a, lane, wt);
-    run_team<FwdPol<D, T, NB, ACT>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt, lane);
+    FwdPol<D, T, NB, ACT, NORM> pol(a, lane, wt);
+    run_team<FwdPol<D, T, NB, ACT, NORM>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt,
+                                                    lane);
 }
 
-template <int T, int NB, int ACT>
+template <int T, int NB, int ACT, int NORM = 0>
 const void* kptr() {
-    return (const void*)&fwd_bf16_kernel<GDPA_D, T, NB, ACT>;
+    return (const void*)&fwd_bf16_kernel<GDPA_D, T, NB, ACT, NORM>;
 }
 
 template <int T, int NB>
 const void* kptr_act(int act) {
+    if (act & kActNorm) {   // the RMSNorm-prologue variants
+        switch (act & ~kActNorm) {
+            case ACT_GELU: return kptr<T, NB, ACT_GELU, 1>();
+            case ACT_SILU: return kptr<T, NB, ACT_SILU, 1>();
+            case ACT_GELU_POLY: return kptr<T, NB, ACT_GELU_POLY, 1>();
+            case ACT_GELU_TAYLOR6: return kptr<T, NB, ACT_GELU_TAYLOR6, 1>();
+            case ACT_IDENTITY: return kptr<T, NB, ACT_IDENTITY, 1>();
+        }
+        return nullptr;
+    }
     switch (act) {
         case ACT_GELU: return kptr<T, NB, ACT_GELU>();
         case ACT_SILU: return kptr<T, NB, ACT_SILU>();

@@ -39,11 +39,21 @@ struct KernelArgs {
     float* lse;
     const float* stat;
     int Tq;
+    // RMSNorm prologue only: 1/rms per (head, row) of Q, fp32 [H, Tq], and of K and V
+    // as pairs, fp32 [H, Tk, 2] (1 for a tensor left raw); `norm` says which of Q (1),
+    // K (2), V (4) are normalised (their gradients go through the norm)
+    const float* rq;
+    const float* rkv;
+    int Tk;
+    int norm;
 };
 
 // the activation code of the softmax (JFA) variant of the bf16 kernels (device
 // enum Act::ACT_SOFTMAX); the public activations are gdpa_act
 constexpr int kActSoftmax = 6;
+
+// flag on an activation code: the RMSNorm-prologue variant of a GDPA kernel
+constexpr int kActNorm = 16;
 
 // bf16 MFMA kernels, one translation unit per head dimension.  A workgroup is a
 // team of `team` waves (1, or 2 for d = 128) working on one bin (P bins, P
@@ -79,6 +89,12 @@ GDPA_DECLARE_FUSED(128)
 hipError_t launch_partial_sum(const DevGroup* groups, int n_groups, const float* part, int rows_per_slot,
                               int stride, int offset, int d, int H, float mul, void* out, int out_f32,
                               hipStream_t s);
+
+// RMSNorm prologue pre-pass: rq[h, i] = 1 / sqrt(mean_c q[i, h, c]^2 + eps) for
+// i < Tq when norm & 1 (else 1); rkv[h, j] = (the same of k, of v) for j < Tk when
+// norm & 2, norm & 4 (else 1); inputs bf16 [T, H, d]
+hipError_t launch_norm_rstd(const void* q, const void* k, const void* v, int Tq, int Tk, int H, int d, int norm,
+                            float eps, float* rq, float* rkv, hipStream_t s);
 
 // JFA forward chunks: per row of each cut item, O = (sum_j 2^(m_j - m) O_j) / l and
 // LSE = (m + log2 l) ln 2, with m = max_j m_j and l = sum_j 2^(m_j - m) l_j over the

@@ -130,9 +130,11 @@ __device__ __forceinline__ void wait_jobs(int m) {
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Geometry of a team's ring: T waves share LDS_BYTES of LDS.  With XJ = 1 every
-// slot also has a 256-byte side buffer, filled by one more instruction per job
-// (per-row statistics that travel with a tile; one-wave teams only), so that every
-// job still counts the same number of instructions.
+// slot also has a 256-byte side buffer, filled by one more instruction per job and
+// wave (per-row statistics that travel with a tile), so that every job still counts
+// the same number of instructions.  In a two-wave team both waves load the same 256
+// bytes into the same side buffer: the second write stores the values the first
+// did, and the buffer is read only after the team barrier that follows both.
 template <int D, int T, int LDS_BYTES, int XJ = 0>
 struct RingGeom {
     static constexpr int TILE = 32 * D * 2;            // bytes of one 32-row tile
@@ -145,7 +147,6 @@ struct RingGeom {
     static constexpr int R = RFIT > RMAX ? RMAX : RFIT;   // slots
     static constexpr int BYTES = R * (TILE + SIDE);
     static_assert(J % T == 0, "a tile's instructions are split evenly over the team");
-    static_assert(XJ == 0 || T == 1, "side buffers with one-wave teams");
     // a consume point takes at most 2 jobs and the ring runs R - 2 jobs past the
     // previous one, so R >= 4 keeps every awaited job issued
     static_assert(R >= 4, "the ring needs a step plus look-ahead");

@@ -237,6 +237,82 @@ def test_cut_items(d, case, deal):
 
 
 # ---------------------------------------------------------------------------
+# RMSNorm prologue: GDPA on normalised Q, K, V from the raw tensors
+# ---------------------------------------------------------------------------
+
+def run_norm(inp, norm, act=None, **opts):
+    """gdpa_norm_fwd then gdpa_norm_bwd on one plan: (O, dQ, dK, dV, rstd) as numpy."""
+    act = act or inp.act
+    qo, ko = dev_offsets(inp)
+    Tq, Tk = inp.q.shape[0], inp.k.shape[0]
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16", **opts) as plan:
+        rstd = torch.full((inp.H * (Tq + 2 * Tk),), float("nan"), device=DEV)
+        o = torch.empty_like(inp.q)
+        dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+        args = (plan.handle, inp.q, inp.k, inp.v)
+        G.gdpa_norm_fwd(*args, qo, ko, plan.B, inp.H, inp.d, act, inp.window, norm, rstd, o)
+        G.gdpa_norm_bwd(*args, inp.do, qo, ko, plan.B, inp.H, inp.d, act, inp.window, norm, rstd, dq, dk, dv)
+        torch.cuda.synchronize()
+        n_parts = plan.stats()["n_parts"]
+    return tuple(t.float().cpu().numpy() for t in (o, dq, dk, dv, rstd)) + (n_parts,)
+
+
+def check_norm(got, inp, norm, act, what):
+    o, dq, dk, dv, rstd = got[:5]
+    args = (inp.f64("q"), inp.f64("k"), inp.f64("v"))
+    check_close(o, R.norm_gdpa_fwd(*args, inp.q_off, inp.kv_off, act, inp.window, norm), f"norm O {what}")
+    ref = R.norm_gdpa_bwd(*args, inp.f64("do"), inp.q_off, inp.kv_off, act, inp.window, norm)
+    for name, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        check_close(a, b, f"norm {name} {what}")
+    # the pre-pass: 1/rms per (head, row), [H, Tq] then [H, Tk, 2]; 1 where not normalised
+    H, Tq, Tk = inp.H, inp.q.shape[0], inp.k.shape[0]
+    inv = lambda x, on: (1.0 / np.sqrt(np.mean(x * x, -1) + R.RMS_EPS)).T if on else np.ones((H, x.shape[0]))
+    want = np.concatenate([inv(args[0], "q" in norm).ravel(),
+                           np.stack([inv(args[1], "k" in norm), inv(args[2], "v" in norm)], -1).ravel()])
+    np.testing.assert_allclose(rstd, want, rtol=2e-6, err_msg=f"rstd {what}")
+
+
+NORM_LAYOUTS = [(32, 1, 1, 1, 1), (32, 1, 2, 1, 2), (64, 1, 1, 1, 1), (64, 1, 2, 1, 2),
+                (128, 1, 1, 1, 1), (128, 1, 2, 1, 2), (128, 2, 1, 2, 1)]
+
+
+@pytest.mark.parametrize("d,tf,nb,tb,nbq", NORM_LAYOUTS)
+def test_norm_prologue_layouts(d, tf, nb, tb, nbq):
+    """Every forward layout, and the dQ / dK-dV layouts, with Q, K, V normalised."""
+    say(f"norm prologue d={d} fwd {tf}x{nb} dq {tb}x{nbq} dkdv {tb}x1")
+    inp = make_from_lengths(JFA_LQ, JFA_LK, 2, d, act="silu", rms="", row_spread=1.0, seed=61, device=DEV)
+    got = run_norm(inp, "qkv", team=(tf, tb, tb if nbq == 1 else 1), blocks=(nb, 1, nbq))
+    check_norm(got, inp, "qkv", "silu", f"d={d}")
+
+
+@pytest.mark.parametrize("norm", ["q", "kv", "qk", ""])
+@pytest.mark.parametrize("act", ["gelu", "identity"])
+def test_norm_prologue_subsets(norm, act):
+    say(f"norm prologue norm={norm!r} act={act}")
+    inp = make_from_lengths(JFA_LQ, JFA_LK, 2, 64, act=act, rms="", row_spread=1.0, seed=62, device=DEV)
+    check_norm(run_norm(inp, norm), inp, norm, act, f"norm={norm!r} act={act}")
+
+
+@pytest.mark.parametrize("window", [1, 17, 128])
+def test_norm_prologue_windows(window):
+    say(f"norm prologue window={window}")
+    L = [1, 31, 32, 33, 127, 300, 0, 65]
+    inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, rms="", row_spread=1.0, seed=63, device=DEV)
+    check_norm(run_norm(inp, "qkv"), inp, "qkv", "gelu", f"window={window}")
+
+
+def test_norm_prologue_cut_items():
+    """Chunks take the norm's gradient separately: it is linear in the normalised
+    row's gradient, so the partial sums still add up."""
+    say("norm prologue with cut items")
+    inp = make_from_lengths([32, 3000, 1], [3000, 40, 5], 2, 64, act="silu", rms="", row_spread=1.0, seed=64,
+                            device=DEV)
+    got = run_norm(inp, "qkv", bins=(16, 16, 16))
+    assert got[5][0] > 0 and got[5][1] > 0 and got[5][2] > 0, got[5]
+    check_norm(got, inp, "qkv", "silu", "cut")
+
+
+# ---------------------------------------------------------------------------
 # JFA: jagged softmax attention through the same kernels
 # ---------------------------------------------------------------------------
 
