@@ -2,6 +2,7 @@
 """Benchmark of jagged GDPA forward + backward (bf16 in, fp32 accumulate) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 2|3|4|5|pffn] [--act NAME] [--attn gdpa|softmax]
+                    [--norm]
 
 A step is one forward pass plus one backward pass (dK/dV kernel, then dQ kernel)
 over the whole batch of the chosen workload, with inputs resident in HBM.  The
@@ -23,6 +24,12 @@ host cores over a bounded prefix of the same batch.
 same batch instead: the forward (also writing the row log-sum-exp), the backward's
 row-statistics pre-pass, then the dK/dV and dQ kernels; FLOPs are counted as for
 GDPA (the exponentials are not counted).
+
+--norm runs GDPA with the fused RMSNorm prologue on raw inputs (the tensors the
+workload normalises: Q, K, V, or K, V for PMA): the 1/rms pre-pass, then the
+forward, dK/dV and dQ kernels that read the raw tensors.  The line also carries the
+plain kernels' time on the same batch and the HBM floor of the unfused norm the
+prologue replaces (forward: read x, write x^; backward: read x and dx^, write dx).
 """
 from __future__ import annotations
 
@@ -35,6 +42,7 @@ import time
 
 METRIC = "useful TFLOP/s, jagged GDPA fwd+bwd bf16, % of MFMA peak, 1 MI355X"
 METRIC_JFA = "useful TFLOP/s, jagged softmax attention (JFA) fwd+bwd bf16, 1 MI355X"
+METRIC_NORM = "useful TFLOP/s, jagged GDPA fwd+bwd with fused RMSNorm prologue, bf16, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
@@ -50,17 +58,21 @@ def kernel_flops(H, d, pairs, Tq=0):
     return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd": 5 * u, "stat": 2.0 * H * d * Tq}
 
 
-def kernel_bytes(H, d, Tq, Tk, softmax=False):
+def kernel_bytes(H, d, Tq, Tk, softmax=False, norm=""):
     """Algorithmic bytes per launch (bf16): every input read once, every output written
     once; softmax (JFA): plus the fp32 row LSE written by the forward, and the fp32
-    (LSE, D) row pair that the pre-pass writes and the gradient kernels read."""
+    (LSE, D) row pair that the pre-pass writes and the gradient kernels read; norm
+    (RMSNorm prologue): plus the fp32 1/rms factors (H (Tq + 2 Tk)) that the rstd
+    pre-pass writes, after reading the tensors it normalises, and the kernels read."""
     e = 2 * H * d
     lse, st = (4 * H * Tq, 8 * H * Tq) if softmax else (0, 0)
-    return {"fwd": e * (2 * Tq + 2 * Tk) + lse,         # Q, K, V -> O (, LSE)
-            "dkdv": e * (2 * Tq + 4 * Tk) + st,         # Q, dO, K, V (, stat) -> dK, dV
-            "dq": e * (3 * Tq + 2 * Tk) + st,           # Q, dO, K, V (, stat) -> dQ
+    rs = 4 * H * (Tq + 2 * Tk) if norm else 0
+    return {"fwd": e * (2 * Tq + 2 * Tk) + lse + rs,    # Q, K, V (, rstd) -> O (, LSE)
+            "dkdv": e * (2 * Tq + 4 * Tk) + st + rs,    # Q, dO, K, V (, stat or rstd) -> dK, dV
+            "dq": e * (3 * Tq + 2 * Tk) + st + rs,      # Q, dO, K, V (, stat or rstd) -> dQ
             "bwd": e * (3 * Tq + 4 * Tk),               # one-pass backward: Q, dO, K, V -> dQ, dK, dV
-            "stat": 2 * e * Tq + lse + st}              # O, dO, LSE -> stat
+            "stat": 2 * e * Tq + lse + st,              # O, dO, LSE -> stat
+            "rstd": e * (Tq * ("q" in norm) + Tk * ("k" in norm) + Tk * ("v" in norm)) + rs}
 
 
 KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd_common.hpp", "bwd_fused.hip",
@@ -93,9 +105,9 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else k.get("hbm_bytes")
 
 
-def cpu_baseline(inp, budget_s=15.0, softmax=False):
-    """Time the fp64 oracle (forward + backward; softmax: jfa_fwd + jfa_bwd) on a prefix
-    of the batch."""
+def cpu_baseline(inp, budget_s=15.0, softmax=False, norm=""):
+    """Time the fp64 oracle (forward + backward; softmax: jfa_fwd + jfa_bwd; norm: the
+    RMSNorm-prologue forms) on a prefix of the batch."""
     import numpy as np
     import torch
     from oracle import gdpa_ref as R
@@ -121,6 +133,9 @@ def cpu_baseline(inp, budget_s=15.0, softmax=False):
             if softmax:
                 R.jfa_fwd(q, k, v, qo, ko, inp.window)
                 R.jfa_bwd(q, k, v, do, qo, ko, inp.window)
+            elif norm:
+                R.norm_gdpa_fwd(q, k, v, qo, ko, inp.act, inp.window, norm)
+                R.norm_gdpa_bwd(q, k, v, do, qo, ko, inp.act, inp.window, norm)
             else:
                 R.gdpa_fwd(q, k, v, qo, ko, inp.act, inp.window)
                 R.gdpa_bwd(q, k, v, do, qo, ko, inp.act, inp.window)
@@ -147,6 +162,8 @@ def main(argv=None):
     ap.add_argument("--act", default=None, help="override the workload's activation (e.g. gelu_poly)")
     ap.add_argument("--attn", default="gdpa", choices=["gdpa", "softmax"],
                     help="softmax: jagged softmax attention (JFA) on the same batch")
+    ap.add_argument("--norm", action="store_true",
+                    help="GDPA with the fused RMSNorm prologue on raw inputs of the same batch")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -183,16 +200,20 @@ def main(argv=None):
     if args.config == "pffn":   # one sample: every query row against the shared weight rows
         inp = make_pffn(seed=args.seed, device="cuda", act=args.act)
     else:
-        inp = make_workload(int(args.config), seed=args.seed, device="cuda", act=args.act)
+        inp = make_workload(int(args.config), seed=args.seed, device="cuda", act=args.act, raw=args.norm)
     torch.cuda.synchronize()
     qo = torch.tensor(inp.q_off, dtype=torch.int32, device="cuda")
     ko = torch.tensor(inp.kv_off, dtype=torch.int32, device="cuda")
     B, H, d, win, act = len(inp.lq), inp.H, inp.d, inp.window, inp.act
 
     sm = args.attn == "softmax"
-    if sm and args.config == "pffn":
-        print("--attn softmax runs the attention workloads", file=sys.stderr)
+    if (sm or args.norm) and args.config == "pffn":
+        print("--attn softmax and --norm run the attention workloads", file=sys.stderr)
         return 2
+    if sm and args.norm:
+        print("--norm runs GDPA, not JFA", file=sys.stderr)
+        return 2
+    norm = w["rms"] if args.norm else ""
     t0 = time.perf_counter()
     plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16")
     plan_ms = (time.perf_counter() - t0) * 1e3
@@ -236,11 +257,28 @@ def main(argv=None):
         def jdq():
             G.gdpa_jfa_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, win, stat, dq, sh)
 
-    # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels (JFA:
-    # always the pre-pass and the two kernels)
-    fused = 0 if sm else st["bwd_fused"]
+    if norm:
+        rstd = torch.empty((H * (Tq + 2 * Tk),), dtype=torch.float32, device="cuda")
+
+        def nrstd():
+            G.gdpa_norm_rstd(h, inp.q, inp.k, inp.v, H, d, norm, rstd, sh)
+
+        def nfwd():
+            G.gdpa_norm_fwd(h, inp.q, inp.k, inp.v, qo, ko, B, H, d, act, win, norm, rstd, o, sh)
+
+        def ndkdv():
+            G.gdpa_norm_bwd_dkdv(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, norm, rstd, dk, dv, sh)
+
+        def ndq():
+            G.gdpa_norm_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, norm, rstd, dq, sh)
+
+    # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels (JFA and
+    # the norm prologue: always the two kernels, after their pre-pass)
+    fused = 0 if (sm or norm) else st["bwd_fused"]
     if sm:
         calls = [("fwd", jfwd), ("stat", jstat), ("dkdv", jdkdv), ("dq", jdq)]
+    elif norm:
+        calls = [("rstd", nrstd), ("fwd", nfwd), ("dkdv", ndkdv), ("dq", ndq)]
     else:
         calls = [("fwd", fwd), ("bwd", bwd)] if fused else [("fwd", fwd), ("dkdv", dkdv), ("dq", dqk)]
     for _ in range(args.warmup):
@@ -268,10 +306,10 @@ def main(argv=None):
 
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
-    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm)
+    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm)
     kf = kernel_flops(H, d, pairs, Tq)
     dom = max(kms, key=kms.get)
-    trace_name = w["name"] + ("_jfa" if sm else "")   # the counter record of this workload's kernels
+    trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "")   # this workload's counter record
     # the roof the kernel's arithmetic intensity puts it under (ridge: peak FLOP/s / peak B/s)
     mfma_bound = kf[dom] / kb[dom] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
@@ -290,7 +328,7 @@ def main(argv=None):
     bwd_ms = kms["bwd"] if fused else kms["dkdv"] + kms["dq"] + kms.get("stat", 0.0)
 
     out = {
-        "metric": METRIC_JFA if sm else METRIC,
+        "metric": METRIC_JFA if sm else METRIC_NORM if norm else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -305,6 +343,7 @@ def main(argv=None):
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs,
                    "backward": ("row-statistics pre-pass + dK/dV + dQ kernels" if sm else
+                                "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else
                                 ["dK/dV + dQ kernels", "one KV-stationary pass", "one Q-stationary pass"][fused])},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_useful_TFLOPs": kernels["fwd"]["useful_TFLOPs"],
@@ -314,9 +353,29 @@ def main(argv=None):
         "wall_s_timed": round(wall, 3),
         "roofline": roofline,
     }
+    if norm:
+        # the plain kernels on the same batch (as gdpa_bwd runs them; timing does not
+        # depend on the values), and
+        # the HBM floor of an unfused RMSNorm of the same tensors: forward reads x and
+        # writes x^, backward reads x and dx^ and writes dx
+        pcalls = [fwd, bwd] if st["bwd_fused"] else [fwd, dkdv, dqk]
+        for c in pcalls:
+            c()
+        torch.cuda.synchronize()
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        for _ in range(K):
+            for c in pcalls:
+                c()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        rows = Tq * ("q" in norm) + Tk * ("k" in norm) + Tk * ("v" in norm)
+        out["norm"] = {"tensors": norm, "plain_kernels_ms": round(p0.elapsed_time(p1) / K, 4),
+                       "fused_ms": round(ms_step, 4),
+                       "unfused_norm_hbm_floor_ms": round(5 * 2 * H * d * rows / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, softmax=sm)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, softmax=sm, norm=norm)
     plan.close()
     print(json.dumps(out), flush=True)
     return 0

@@ -171,13 +171,14 @@ def make_from_lengths(lq, lk, H: int, d: int, *, act: str = "gelu", window: int 
 
 
 def make_workload(cfg: int, seed: int = 0, device: str = "cpu", B: Optional[int] = None,
-                  act: Optional[str] = None) -> JaggedInputs:
-    """Inputs of workload ``cfg`` (1..5); ``B`` shrinks the batch for fast tests."""
+                  act: Optional[str] = None, raw: bool = False) -> JaggedInputs:
+    """Inputs of workload ``cfg`` (1..5); ``B`` shrinks the batch for fast tests.
+    raw: no RMS normalisation, rows spread in scale (row_spread 1), for the fused-norm path."""
     w = WORKLOADS[cfg]
     lq, lk = workload_lengths(cfg, seed, B)
     return make_from_lengths(lq, lk, w["H"], w["d"], act=act or w["act"], window=w["window"],
-                             dtype=w["dtype"], seed=seed, device=device, rms=w["rms"],
-                             pma_seeds=w.get("pma_seeds", False), cfg=cfg)
+                             dtype=w["dtype"], seed=seed, device=device, rms="" if raw else w["rms"],
+                             pma_seeds=w.get("pma_seeds", False), cfg=cfg, row_spread=1.0 if raw else 0.0)
 
 
 # pFFN as GDPA (the third module of the GDPA page's unified-modules diagram; read as

@@ -258,31 +258,44 @@ gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const 
                             const float* stat, void* dq, void* stream);
 
 /*
- * gdpa_norm_fwd / gdpa_norm_bwd - GDPA with a fused RMSNorm prologue: the inputs
- * named by `norm` (a combination of 1 = Q, 2 = K, 4 = V) are taken through a
- * per-(token, head) RMSNorm over d, x^ = x / sqrt(mean(x^2) + 1e-6) with no gain,
- * before the attention (GDPA page, "Section details", chart of tanh GELU against
- * the 6th-order series: RMSNorm keeps the activation's inputs in range).  The
- * kernels read the raw tensors and scale by each row's 1/rms, so no normalised
- * copy is written; gdpa_norm_bwd returns the gradients of the RAW inputs,
- * dx = r (dx^ - x^ mean(dx^ x^)) for a normalised input (dx^ otherwise).
- * Arguments as gdpa_fwd / gdpa_bwd, plus
- *   norm : 0..7 as above;
- *   rstd : device fp32 scratch of H * (Tq + 2 Tk) floats: gdpa_norm_fwd writes the
- *          factors there ([H, Tq] for Q, then [H, Tk, 2] pairs for K and V; 1 for a
- *          tensor not normalised) and gdpa_norm_bwd reads them, so pass the
- *          forward's buffer, unchanged, with the same q, k, v and norm.
- * Enqueues a pre-pass and the forward kernel (gdpa_norm_fwd), or the dK/dV and dQ
- * kernels (gdpa_norm_bwd; never the one-pass kernels), plus chunk reductions.
- * bf16 plans only; act = GDPA_ACT_ONE is rejected (UNSUPPORTED).  Errors as
- * gdpa_fwd / gdpa_bwd.
+ * GDPA with a fused RMSNorm prologue: the inputs named by `norm` (a combination of
+ * 1 = Q, 2 = K, 4 = V) go through a per-(token, head) RMSNorm over d,
+ * x^ = x / sqrt(mean(x^2) + 1e-6) with no gain, before the attention (GDPA page,
+ * "Section details", chart of tanh GELU against the 6th-order series: RMSNorm keeps
+ * the activation's inputs in range).  The kernels read the raw tensors and scale by
+ * each row's 1/rms, so no normalised copy is written, and the backward returns the
+ * gradients of the RAW inputs, dx = r (dx^ - x^ mean(dx^ x^)) for a normalised
+ * input (dx^ otherwise).  bf16 plans only; act = GDPA_ACT_ONE is rejected
+ * (UNSUPPORTED).
+ *
+ *   gdpa_norm_rstd - the pre-pass: writes rstd, device fp32 scratch of
+ *                    H * (Tq + 2 Tk) floats: [H, Tq] (1/rms of Q's rows), then
+ *                    [H, Tk, 2] (1/rms of K's and V's rows as pairs); 1 for a
+ *                    tensor not in `norm`.  H and d must match the plan.
+ *   gdpa_norm_fwd  - O [Tq,H,d] from raw q, k, v and the rstd that gdpa_norm_rstd
+ *                    wrote for the same q, k, v and norm (read-only here);
+ *                    arguments otherwise as gdpa_fwd.
+ *   gdpa_norm_bwd  - raw-input gradients dq, dk, dv (arguments as gdpa_bwd plus
+ *                    norm and that rstd): the dK/dV kernel, then the dQ kernel
+ *                    (never the one-pass kernels), plus chunk reductions;
+ *                    == gdpa_norm_bwd_dkdv followed by gdpa_norm_bwd_dq.
+ * Errors as gdpa_fwd / gdpa_bwd; norm outside 0..7 or a NULL rstd: INVALID_ARG.
  */
+gdpa_status gdpa_norm_rstd(gdpa_plan plan, const void* q, const void* k, const void* v, int H, int d, int norm,
+                           float* rstd, void* stream);
 gdpa_status gdpa_norm_fwd(gdpa_plan plan, const void* q, const void* k, const void* v, const int32_t* q_off_dev,
                           const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act, int window, int norm,
-                          float* rstd, void* o, void* stream);
+                          const float* rstd, void* o, void* stream);
 gdpa_status gdpa_norm_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
                           const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
                           int window, int norm, const float* rstd, void* dq, void* dk, void* dv, void* stream);
+gdpa_status gdpa_norm_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                               const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                               gdpa_act act, int window, int norm, const float* rstd, void* dk, void* dv,
+                               void* stream);
+gdpa_status gdpa_norm_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                             const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
+                             int window, int norm, const float* rstd, void* dq, void* stream);
 
 /*
  * pFFN as GDPA (GDPA page, "Section details", diagram of self-attention, PMA and

@@ -83,9 +83,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_jfa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                  _vp]
+    lib.gdpa_norm_rstd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]
     lib.gdpa_norm_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_norm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                   _vp]
+    lib.gdpa_norm_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp,
+                                       _vp]
+    lib.gdpa_norm_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd_stat.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]
     lib.gdpa_jfa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
@@ -95,7 +99,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
                  "gdpa_plan_export", "gdpa_plan_stats", "gdpa_pffn_plan_create", "gdpa_pffn_fwd",
                  "gdpa_pffn_bwd", "gdpa_jfa_fwd", "gdpa_jfa_bwd", "gdpa_jfa_bwd_stat", "gdpa_jfa_bwd_dkdv",
-                 "gdpa_jfa_bwd_dq", "gdpa_norm_fwd", "gdpa_norm_bwd"):
+                 "gdpa_jfa_bwd_dq", "gdpa_norm_rstd", "gdpa_norm_fwd", "gdpa_norm_bwd", "gdpa_norm_bwd_dkdv",
+                 "gdpa_norm_bwd_dq"):
         getattr(lib, name).restype = _i
     if path == LIB_PATH:
         _lib = lib
@@ -217,8 +222,14 @@ def norm_code(norm) -> int:
     return sum(NORM_BITS[c] for c in set(norm))
 
 
+def gdpa_norm_rstd(plan, q, k, v, H, d, norm, rstd, stream=None):
+    """RMSNorm-prologue pre-pass: rstd (fp32, H (Tq + 2 Tk)) = 1/rms of the rows of the tensors in `norm`."""
+    _check(load_library().gdpa_norm_rstd(plan, _ptr(q), _ptr(k), _ptr(v), H, d, norm_code(norm), _ptr(rstd),
+                                         _stream(stream)))
+
+
 def gdpa_norm_fwd(plan, q, k, v, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, o, stream=None):
-    """GDPA with a fused RMSNorm prologue on the tensors in `norm`; rstd: fp32 H (Tq + 2 Tk) scratch."""
+    """GDPA on the RMS-normalised tensors in `norm`, from the raw tensors and gdpa_norm_rstd's factors."""
     _check(load_library().gdpa_norm_fwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(q_off_dev), _ptr(kv_off_dev), B, H,
                                         d, _enum(act, ACT), window, norm_code(norm), _ptr(rstd), _ptr(o),
                                         _stream(stream)))
@@ -226,10 +237,23 @@ def gdpa_norm_fwd(plan, q, k, v, q_off_dev, kv_off_dev, B, H, d, act, window, no
 
 def gdpa_norm_bwd(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, dq, dk, dv,
                   stream=None):
-    """Raw-input gradients of gdpa_norm_fwd, reading the forward's rstd."""
+    """Raw-input gradients of gdpa_norm_fwd."""
     _check(load_library().gdpa_norm_bwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
                                         _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, norm_code(norm),
                                         _ptr(rstd), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def gdpa_norm_bwd_dkdv(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, dk, dv,
+                       stream=None):
+    _check(load_library().gdpa_norm_bwd_dkdv(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
+                                             _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, norm_code(norm),
+                                             _ptr(rstd), _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def gdpa_norm_bwd_dq(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, dq, stream=None):
+    _check(load_library().gdpa_norm_bwd_dq(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
+                                           _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, norm_code(norm),
+                                           _ptr(rstd), _ptr(dq), _stream(stream)))
 
 
 def _opts(host_only, bins, team, blocks, deal, split, unfused):

@@ -665,22 +665,34 @@ static void norm_args(gdpa_plan plan, int norm, const float* rstd, KernelArgs& a
     a.norm = norm;
 }
 
+gdpa_status gdpa_norm_rstd(gdpa_plan plan, const void* q, const void* k, const void* v, int H, int d, int norm,
+                           float* rstd, void* stream) {
+    g_err.clear();
+    if (!plan) return fail(GDPA_ERR_INVALID_ARG, "plan is NULL");
+    if (plan->host_only) return fail(GDPA_ERR_PLAN_MISMATCH, "host-only plan cannot run kernels");
+    if (H != plan->H || d != plan->d) return fail(GDPA_ERR_PLAN_MISMATCH, "H or d differ from the plan");
+    gdpa_status st = norm_check(plan, GDPA_ACT_GELU, norm, rstd);
+    if (st != GDPA_OK) return st;
+    if ((plan->Tq > 0 && !q) || (plan->Tk > 0 && (!k || !v))) return fail(GDPA_ERR_INVALID_ARG, "q, k or v is NULL");
+    const hipError_t e = launch_norm_rstd(q, k, v, (int)plan->Tq, (int)plan->Tk, H, d, norm, kRmsEps, rstd,
+                                          rstd + (size_t)H * plan->Tq, (hipStream_t)stream);
+    if (e != hipSuccess) return fail_hip(e, "RMSNorm pre-pass launch");
+    return GDPA_OK;
+}
+
 gdpa_status gdpa_norm_fwd(gdpa_plan plan, const void* q, const void* k, const void* v, const int32_t* q_off_dev,
                           const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act, int window, int norm,
-                          float* rstd, void* o, void* stream) {
+                          const float* rstd, void* o, void* stream) {
     g_err.clear();
     gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
     if (st == GDPA_OK) st = norm_check(plan, act, norm, rstd);
     if (st != GDPA_OK) return st;
     if (plan->Tq > 0 && (!q || !o)) return fail(GDPA_ERR_INVALID_ARG, "q or o is NULL");
     if (plan->Tk > 0 && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
+    if (plan->Tq == 0) return GDPA_OK;
     hipStream_t s = (hipStream_t)stream;
     KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
     norm_args(plan, norm, rstd, a);
-    hipError_t e = launch_norm_rstd(q, k, v, (int)plan->Tq, (int)plan->Tk, H, d, norm, kRmsEps, rstd,
-                                    rstd + (size_t)H * plan->Tq, s);
-    if (e != hipSuccess) return fail_hip(e, "RMSNorm pre-pass launch");
-    if (plan->Tq == 0) return GDPA_OK;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -691,6 +703,7 @@ gdpa_status gdpa_norm_fwd(gdpa_plan plan, const void* q, const void* k, const vo
     a.P = wl.P;
     a.part = plan->d_part[LIST_FWD];
     const int code = (int)act | kActNorm;
+    hipError_t e;
     switch (d) {
         case 32: e = launch_fwd_bf16_d32(a, wl.team, wl.nb, code, s); break;
         case 64: e = launch_fwd_bf16_d64(a, wl.team, wl.nb, code, s); break;
@@ -702,16 +715,19 @@ gdpa_status gdpa_norm_fwd(gdpa_plan plan, const void* q, const void* k, const vo
     return GDPA_OK;
 }
 
-gdpa_status gdpa_norm_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
-                          const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
-                          int window, int norm, const float* rstd, void* dq, void* dk, void* dv, void* stream) {
+static gdpa_status norm_bwd_parts(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                                  const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                                  gdpa_act act, int window, int norm, const float* rstd, void* dq, void* dk, void* dv,
+                                  void* stream, bool want_dkdv, bool want_dq) {
     g_err.clear();
     gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
     if (st == GDPA_OK) st = norm_check(plan, act, norm, rstd);
     if (st != GDPA_OK) return st;
     const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
-    if (any_q && (!q || !dout || !dq)) return fail(GDPA_ERR_INVALID_ARG, "q, dout or dq is NULL");
-    if (any_k && (!k || !v || !dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "k, v, dk or dv is NULL");
+    if (any_q && (!q || !dout)) return fail(GDPA_ERR_INVALID_ARG, "q or dout is NULL");
+    if (any_k && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
+    if (want_dq && any_q && !dq) return fail(GDPA_ERR_INVALID_ARG, "dq is NULL");
+    if (want_dkdv && any_k && (!dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "dk or dv is NULL");
     hipStream_t s = (hipStream_t)stream;
     KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
     norm_args(plan, norm, rstd, a);
@@ -724,7 +740,7 @@ gdpa_status gdpa_norm_bwd(gdpa_plan plan, const void* q, const void* k, const vo
     a.dv = dv;
     const int code = (int)act | kActNorm;
     hipError_t e = hipSuccess;
-    if (any_k) {
+    if (want_dkdv && any_k) {
         const WorkList& wl = plan->lists[LIST_DKDV];
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DKDV];
@@ -739,7 +755,7 @@ gdpa_status gdpa_norm_bwd(gdpa_plan plan, const void* q, const void* k, const vo
         if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
         if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
     }
-    if (e == hipSuccess && any_q) {
+    if (e == hipSuccess && want_dq && any_q) {
         const WorkList& wl = plan->lists[LIST_DQ];
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DQ];
@@ -756,6 +772,28 @@ gdpa_status gdpa_norm_bwd(gdpa_plan plan, const void* q, const void* k, const vo
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no RMSNorm-prologue backward kernel here");
     if (e != hipSuccess) return fail_hip(e, "backward launch");
     return GDPA_OK;
+}
+
+gdpa_status gdpa_norm_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                          const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
+                          int window, int norm, const float* rstd, void* dq, void* dk, void* dv, void* stream) {
+    return norm_bwd_parts(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, dq, dk, dv,
+                          stream, true, true);
+}
+
+gdpa_status gdpa_norm_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                               const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                               gdpa_act act, int window, int norm, const float* rstd, void* dk, void* dv,
+                               void* stream) {
+    return norm_bwd_parts(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, nullptr,
+                          dk, dv, stream, true, false);
+}
+
+gdpa_status gdpa_norm_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
+                             const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
+                             int window, int norm, const float* rstd, void* dq, void* stream) {
+    return norm_bwd_parts(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, norm, rstd, dq, nullptr,
+                          nullptr, stream, false, true);
 }
 
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,

@@ -250,6 +250,7 @@ def run_norm(inp, norm, act=None, **opts):
         o = torch.empty_like(inp.q)
         dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
         args = (plan.handle, inp.q, inp.k, inp.v)
+        G.gdpa_norm_rstd(*args, inp.H, inp.d, norm, rstd)
         G.gdpa_norm_fwd(*args, qo, ko, plan.B, inp.H, inp.d, act, inp.window, norm, rstd, o)
         G.gdpa_norm_bwd(*args, inp.do, qo, ko, plan.B, inp.H, inp.d, act, inp.window, norm, rstd, dq, dk, dv)
         torch.cuda.synchronize()
@@ -299,6 +300,36 @@ def test_norm_prologue_windows(window):
     L = [1, 31, 32, 33, 127, 300, 0, 65]
     inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, rms="", row_spread=1.0, seed=63, device=DEV)
     check_norm(run_norm(inp, "qkv"), inp, "qkv", "gelu", f"window={window}")
+
+
+def test_norm_backward_parts_match_whole():
+    """gdpa_norm_bwd_dkdv then gdpa_norm_bwd_dq give gdpa_norm_bwd's outputs bit for bit."""
+    inp = make_from_lengths(JFA_LQ, JFA_LK, 2, 128, act="gelu", rms="", row_spread=1.0, seed=65, device=DEV)
+    whole = run_norm(inp, "qkv")
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, 0, "bf16") as plan:
+        rstd = torch.tensor(whole[4], device=DEV)
+        dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+        args = (plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, plan.B, inp.H, inp.d, "gelu", 0, "qkv", rstd)
+        G.gdpa_norm_bwd_dkdv(*args, dk, dv)
+        G.gdpa_norm_bwd_dq(*args, dq)
+        torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), whole[1:4]):
+        assert np.array_equal(a.float().cpu().numpy(), b), name
+
+
+def test_norm_prologue_rejects():
+    inp = make_from_lengths([40, 3], [50, 7], 2, 64, act="gelu", rms="", seed=66, device=DEV)
+    qo, ko = dev_offsets(inp)
+    rstd = torch.empty(2 * (43 + 2 * 57), device=DEV)
+    o = torch.empty_like(inp.q)
+    cases = (("f32", "gelu", 7, rstd, "GDPA_ERR_UNSUPPORTED"), ("bf16", "one", 7, rstd, "GDPA_ERR_UNSUPPORTED"),
+             ("bf16", "gelu", 8, rstd, "GDPA_ERR_INVALID_ARG"), ("bf16", "gelu", 7, None, "GDPA_ERR_INVALID_ARG"))
+    for dtype, act, norm, buf, status in cases:
+        with G.Plan(inp.q_off, inp.kv_off, 2, 64, 0, dtype) as plan:
+            with pytest.raises(G.GdpaError) as e:
+                G.gdpa_norm_fwd(plan.handle, inp.q, inp.k, inp.v, qo, ko, 2, 2, 64, act, 0, norm, buf, o)
+            assert G.STATUS[e.value.status] == status, (dtype, act, norm)
 
 
 def test_norm_prologue_cut_items():
