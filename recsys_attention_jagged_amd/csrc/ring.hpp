@@ -326,7 +326,10 @@ __device__ __forceinline__ void walk_settle(Pol& pol, Walk& w, const Rec* __rest
     // skip items without jobs
     while (w.valid && w.njobs == 0) {
         if (++w.idx < w.end) {
-            w.r = recs[w.idx];
+            // a uniform index, so that the record comes through the scalar cache: a vector
+            // load here would make the compiler wait for vmcnt(0), i.e. for every tile
+            // still in flight, each time the walk moves on to the next item
+            w.r = recs[__builtin_amdgcn_readfirstlane(w.idx)];
             w.pos = 0;
             w.njobs = w.r.s1 >= w.r.s0 ? Pol::NSTAT + Pol::NSTRM * (w.r.s1 - w.r.s0 + 1) : 0;
         } else {
