@@ -298,6 +298,23 @@ gdpa_status gdpa_norm_bwd_dq(gdpa_plan plan, const void* q, const void* k, const
                              int window, int norm, const float* rstd, void* dq, void* stream);
 
 /*
+ * gdpa_fp8_fwd - GDPA forward with 8-bit Q and K (GEM page, section on the custom
+ * kernels and precision: mixed ultra-low precision, MXFP8 among it, for attention,
+ * with the precision chosen per operation).  q8 [Tq,H,d] and
+ * k8 [Tk,H,d] are OCP FP8 E4M3 bytes (the e4m3fn encoding: bias 7, max 448, no
+ * infinities) standing for q8 * q_scale and k8 * k_scale; S = (q8 . k8) q_scale
+ * k_scale / sqrt(d) is computed by the fp8 MFMA with fp32 accumulation.  V is
+ * bf16, P is rounded to bf16 for the second product, O is bf16 (fp32 for a
+ * GDPA_BF16_F32OUT plan).  Arguments otherwise as gdpa_fwd; q_scale and k_scale
+ * finite and > 0 (INVALID_ARG otherwise).  bf16 plans only; act = GDPA_ACT_ONE is
+ * rejected (UNSUPPORTED).  Forward only: the gradients run on bf16 inputs
+ * (gdpa_bwd).
+ */
+gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const void* v, const int32_t* q_off_dev,
+                         const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act, int window, float q_scale,
+                         float k_scale, void* o, void* stream);
+
+/*
  * pFFN as GDPA (GDPA page, "Section details", diagram of self-attention, PMA and
  * pFFN unified as GDPA).  The page gives no formula; read here as: per head,
  * weight matrices W_K, W_V [M, H, d] shared by every query row of the batch,

@@ -83,6 +83,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_jfa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                  _vp]
+    lib.gdpa_fp8_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, ctypes.c_float,
+                                 _vp, _vp]
     lib.gdpa_norm_rstd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]
     lib.gdpa_norm_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_norm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
@@ -100,7 +102,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                  "gdpa_plan_export", "gdpa_plan_stats", "gdpa_pffn_plan_create", "gdpa_pffn_fwd",
                  "gdpa_pffn_bwd", "gdpa_jfa_fwd", "gdpa_jfa_bwd", "gdpa_jfa_bwd_stat", "gdpa_jfa_bwd_dkdv",
                  "gdpa_jfa_bwd_dq", "gdpa_norm_rstd", "gdpa_norm_fwd", "gdpa_norm_bwd", "gdpa_norm_bwd_dkdv",
-                 "gdpa_norm_bwd_dq"):
+                 "gdpa_norm_bwd_dq", "gdpa_fp8_fwd"):
         getattr(lib, name).restype = _i
     if path == LIB_PATH:
         _lib = lib
@@ -220,6 +222,13 @@ def norm_code(norm) -> int:
     if isinstance(norm, int):
         return norm
     return sum(NORM_BITS[c] for c in set(norm))
+
+
+def gdpa_fp8_fwd(plan, q8, k8, v, q_off_dev, kv_off_dev, B, H, d, act, window, q_scale, k_scale, o, stream=None):
+    """GDPA forward with fp8 (e4m3fn) Q and K standing for q8 * q_scale, k8 * k_scale; V and O bf16."""
+    _check(load_library().gdpa_fp8_fwd(plan, _ptr(q8), _ptr(k8), _ptr(v), _ptr(q_off_dev), _ptr(kv_off_dev), B, H, d,
+                                       _enum(act, ACT), window, float(q_scale), float(k_scale), _ptr(o),
+                                       _stream(stream)))
 
 
 def gdpa_norm_rstd(plan, q, k, v, H, d, norm, rstd, stream=None):

@@ -796,6 +796,44 @@ gdpa_status gdpa_norm_bwd_dq(gdpa_plan plan, const void* q, const void* k, const
                           nullptr, stream, false, true);
 }
 
+gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const void* v, const int32_t* q_off_dev,
+                         const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act, int window, float q_scale,
+                         float k_scale, void* o, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
+    if (st != GDPA_OK) return st;
+    if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "fp8 Q and K run on bf16 plans");
+    if (act == GDPA_ACT_ONE) return fail(GDPA_ERR_UNSUPPORTED, "GDPA_ACT_ONE has no fp8 kernels");
+    if (!(q_scale > 0.0f) || !(k_scale > 0.0f) || !std::isfinite(q_scale) || !std::isfinite(k_scale))
+        return fail(GDPA_ERR_INVALID_ARG, "q_scale and k_scale must be finite and > 0");
+    if (plan->Tq > 0 && (!q8 || !o)) return fail(GDPA_ERR_INVALID_ARG, "q8 or o is NULL");
+    if (plan->Tk > 0 && (!k8 || !v)) return fail(GDPA_ERR_INVALID_ARG, "k8 or v is NULL");
+    if (plan->Tq == 0) return GDPA_OK;
+    hipStream_t s = (hipStream_t)stream;
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    a.scale *= q_scale * k_scale;   // S = (q8 . k8) q_scale k_scale / sqrt(d)
+    a.q = q8;
+    a.k = k8;
+    a.v = v;
+    a.o = o;
+    const WorkList& wl = plan->lists[LIST_FWD];
+    a.items = plan->d_items[LIST_FWD];
+    a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+    a.P = wl.P;
+    a.part = plan->d_part[LIST_FWD];
+    const int code = (int)act | kActF8;
+    hipError_t e;
+    switch (d) {
+        case 32: e = launch_fwd_bf16_d32(a, wl.team, wl.nb, code, s); break;
+        case 64: e = launch_fwd_bf16_d64(a, wl.team, wl.nb, code, s); break;
+        default: e = launch_fwd_bf16_d128(a, wl.team, wl.nb, code, s); break;
+    }
+    if (e == hipSuccess) e = reduce_parts(plan, LIST_FWD, 1.0f, o, s);
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no fp8 forward kernel here");
+    if (e != hipSuccess) return fail_hip(e, "fp8 forward launch");
+    return GDPA_OK;
+}
+
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,
                                   gdpa_plan* out) {
     g_err.clear();

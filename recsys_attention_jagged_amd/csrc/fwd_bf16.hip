@@ -28,6 +28,11 @@
 // / sqrt(d), and P_ij r_v,j takes the place of P_ij (O = sum_j P_ij r_v,j v_j).  The
 // factors of a tile's 32 rows (a pre-pass writes them) travel with the tile in the
 // ring's side buffers: r_q with each Q tile, (r_k, r_v) pairs with each K tile.
+//
+// With fp8 Q and K (F8) the first product runs on the fp8 MFMA: Q and K arrive as
+// OCP e4m3 bytes with one dequantisation factor per tensor (folded into the score
+// scale), their tiles take half a slot, and V, P and O stay bf16 (the precision is
+// chosen per product).
 #include "kernels.hpp"
 #include "ring.hpp"
 
@@ -38,8 +43,9 @@
 namespace gdpa {
 namespace {
 
-template <int D, int T, int NB, int ACT, int NORM>
+template <int D, int T, int NB, int ACT, int MODE>   // MODE: 0 plain, 1 RMSNorm prologue, 2 fp8 Q and K
 struct FwdPol {
+    static constexpr bool NORM = MODE == 1, F8 = MODE == 2;
     static constexpr int NSTAT = T * NB, NSTRM = 2;   // stationary tiles: wave-major q blocks
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr int ROWS = 32 * T * NB;          // q rows per item
@@ -51,7 +57,8 @@ struct FwdPol {
     float scale;
     rsrc_t wq, wk, wv;    // issuing side: slices of the walk's current item
     rsrc_t wrq, wrkv, wnull;   // NORM: 1/rms of the item's q rows, (k, v) row pairs; a zero-range side
-    bf16x8 qf[NB][NKS];
+    bf16x8 qf[F8 ? 1 : NB][NKS];
+    long qf8[F8 ? NB : 1][NKS];   // F8: this lane's 8 fp8 values of each 16-wide k block
     float rqv[NB];        // NORM: 1/rms of this lane's q row
     f32x16 acc[NB][NDB];
     // softmax only: running max (log2 units) of this lane's q row and this lane's
@@ -77,7 +84,13 @@ struct FwdPol {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
         wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
         wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
-        wq = slice_rsrc((const __bf16*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs, D * 2);
+        if constexpr (F8) {   // one-byte rows, H D bytes apart
+            wk = slice_rsrc((const uint8_t*)a.k + kvb, w.lk, rs / 2, D);
+            wq = slice_rsrc((const uint8_t*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs / 2, D);
+            wnull = slice_rsrc(a.q, 0, rs / 2, D);
+        } else {
+            wq = slice_rsrc((const __bf16*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs, D * 2);
+        }
         if constexpr (NORM) {
             wrq = slice_rsrc(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
             wrkv = slice_rsrc(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
@@ -86,7 +99,25 @@ struct FwdPol {
     }
 
     template <class RingT>
+    __device__ __forceinline__ void ring_ready(RingT& g, int lane_) {
+        if constexpr (F8) g.init8(rs / 2, lane_);
+    }
+
+    template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
+        if constexpr (F8) {
+            if (i < NSTAT) {
+                g.issue8(wq, (uint32_t)(w.t * ROWS + 32 * i) * (rs / 2), wnull);
+            } else {
+                const int rel = i - NSTAT;
+                const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
+                if (rel & 1)
+                    g.issue(wv, row0 * rs);
+                else
+                    g.issue8(wk, row0 * (rs / 2), wnull);
+            }
+            return;
+        }
         if (i < NSTAT) {
             const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * i);
             if constexpr (NORM)
@@ -173,8 +204,14 @@ struct FwdPol {
         for (int u = 0; u < 2; ++u) {
             const int tile = i + u;
             if (tile < NSTAT && tile / NB == wt) {
+                if constexpr (F8) {
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) qf[tile % NB][ks] = lds_row8<D>(g.tile(job + u), r, 2 * ks + hh);
+                    for (int ks = 0; ks < NKS; ++ks)
+                        qf8[tile % NB][ks] = *(const long*)(g.tile(job + u) + tile8_off<D>(r, ks) + 8 * hh);
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) qf[tile % NB][ks] = lds_row8<D>(g.tile(job + u), r, 2 * ks + hh);
+                }
                 if constexpr (NORM) rqv[tile % NB] = *(const float*)(g.side(job + u) + 4 * r);
             }
         }
@@ -205,9 +242,15 @@ struct FwdPol {
             if constexpr (NORM) return (e & 1) ? rkv[e >> 2][(e >> 1) & 1].w : rkv[e >> 2][(e >> 1) & 1].y;
             else return 1.0f;
         };
+        long kop8[F8 ? NKS : 1];
         if constexpr (HOIST) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
+            for (int ks = 0; ks < NKS; ++ks) {
+                if constexpr (F8)
+                    kop8[ks] = *(const long*)(kt + tile8_off<D>(r, ks) + 8 * hh);
+                else
+                    kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
+            }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -218,6 +261,13 @@ struct FwdPol {
         for (int b = 0; b < NB; ++b) sc[b] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
+            if constexpr (F8) {   // S^T = K Q^T on e4m3 operands, 16 k per instruction
+                const long ko = HOIST ? kop8[ks] : *(const long*)(kt + tile8_off<D>(r, ks) + 8 * hh);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    sc[b] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(ko, qf8[b][ks], sc[b], 0, 0, 0);
+                continue;
+            }
             const bf16x8 ko = HOIST ? kop[ks] : lds_row8<D>(kt, r, 2 * ks + hh);
 #pragma unroll
             for (int b = 0; b < NB; ++b) sc[b] = mfma32(ko, qf[b][ks], sc[b]);
@@ -331,25 +381,35 @@ struct FwdPol {
     }
 };
 
-template <int D, int T, int NB, int ACT, int NORM>
+template <int D, int T, int NB, int ACT, int MODE>
 __global__ __launch_bounds__((TeamShape<D, T, 0>::THREADS), (TeamShape<D, T, 0>::WPE)) void fwd_bf16_kernel(
     const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
-    using RingT = Ring<D, T, TeamShape<D, T, 0>::LDS, NORM ? 1 : 0>;
+    using RingT = Ring<D, T, TeamShape<D, T, 0>::LDS, MODE == 1 ? 1 : 0>;
     __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
     const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
-    FwdPol<D, T, NB, ACT, NORM> pol(a, lane, wt);
-    run_team<FwdPol<D, T, NB, ACT, NORM>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt,
+    FwdPol<D, T, NB, ACT, MODE> pol(a, lane, wt);
+    run_team<FwdPol<D, T, NB, ACT, MODE>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, wt,
                                                     lane);
 }
 
-template <int T, int NB, int ACT, int NORM = 0>
+template <int T, int NB, int ACT, int MODE = 0>
 const void* kptr() {
-    return (const void*)&fwd_bf16_kernel<GDPA_D, T, NB, ACT, NORM>;
+    return (const void*)&fwd_bf16_kernel<GDPA_D, T, NB, ACT, MODE>;
 }
 
 template <int T, int NB>
 const void* kptr_act(int act) {
+    if (act & kActF8) {   // fp8 Q and K
+        switch (act & ~kActF8) {
+            case ACT_GELU: return kptr<T, NB, ACT_GELU, 2>();
+            case ACT_SILU: return kptr<T, NB, ACT_SILU, 2>();
+            case ACT_GELU_POLY: return kptr<T, NB, ACT_GELU_POLY, 2>();
+            case ACT_GELU_TAYLOR6: return kptr<T, NB, ACT_GELU_TAYLOR6, 2>();
+            case ACT_IDENTITY: return kptr<T, NB, ACT_IDENTITY, 2>();
+        }
+        return nullptr;
+    }
     if (act & kActNorm) {   // the RMSNorm-prologue variants
         switch (act & ~kActNorm) {
             case ACT_GELU: return kptr<T, NB, ACT_GELU, 1>();

@@ -55,6 +55,9 @@ constexpr int kActSoftmax = 6;
 // flag on an activation code: the RMSNorm-prologue variant of a GDPA kernel
 constexpr int kActNorm = 16;
 
+// flag on an activation code: the forward with fp8 (OCP e4m3) Q and K
+constexpr int kActF8 = 32;
+
 // bf16 MFMA kernels, one translation unit per head dimension.  A workgroup is a
 // team of `team` waves (1, or 2 for d = 128) working on one bin (P bins, P
 // workgroups); nb = 32-row stationary blocks per wave (forward and dQ: 1 or 2,

@@ -60,6 +60,27 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
     return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
 }
 
+// fp8 tiles (32 rows of D one-byte values, in the first half of a slot): the
+// 16-byte chunk c of row r sits at chunk position c ^ swz8<D>(r).  Operand reads
+// take 8 bytes of one chunk in each of 32 rows; rows share a 256-byte bank window
+// 256 / D at a time, and the swizzle spreads the rows of one window over distinct
+// chunk positions (at most two-way bank conflicts).
+template <int D>
+__device__ __forceinline__ int swz8(int row) {
+    if constexpr (D == 128) {
+        return (row >> 1) & 7;
+    } else if constexpr (D == 64) {
+        return (row >> 2) & 3;
+    } else {
+        return (row >> 3) & 1;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ int tile8_off(int row, int chunk) {
+    return row * D + ((chunk ^ swz8<D>(row)) << 4);
+}
+
 // 8 bf16 of `row`, columns [8 chunk, 8 chunk + 8)
 template <int D>
 __device__ __forceinline__ bf16x8 lds_row8(const char* tile, int row, int chunk) {
@@ -162,6 +183,7 @@ struct Ring : RingGeom<D, T, LDS_BYTES, XJ> {
     int wt;                             // this wave's index in the team (uniform)
     int issued;                         // jobs issued so far (uniform)
     uint32_t xlane;                     // this lane's byte offset in a side load
+    uint32_t off8[G::JW / 2 > 0 ? G::JW / 2 : 1];   // lane offsets of an fp8 tile's instructions
 
     __device__ __forceinline__ void init(char* slice, uint32_t row_stride_bytes, int wt_, int lane) {
         gbase = slice;
@@ -174,6 +196,17 @@ struct Ring : RingGeom<D, T, LDS_BYTES, XJ> {
             const int slot = (jj * T + wt) * 64 + lane;
             const int row = slot / CPR, pos = slot % CPR;
             off[jj] = (uint32_t)row * row_stride_bytes + (uint32_t)((pos ^ swz<D>(row)) << 4);
+        }
+    }
+
+    // fp8 tiles: lane offsets for a tensor whose rows are row_stride8 bytes apart
+    __device__ __forceinline__ void init8(uint32_t row_stride8, int lane) {
+        constexpr int CPR8 = D / 16;   // 16-byte chunks per fp8 row
+#pragma unroll
+        for (int jj = 0; jj < G::JW / 2; ++jj) {
+            const int slot = (jj * T + wt) * 64 + lane;
+            const int row = slot / CPR8, pos = slot % CPR8;
+            off8[jj] = (uint32_t)row * row_stride8 + (uint32_t)((pos ^ swz8<D>(row)) << 4);
         }
     }
 
@@ -203,6 +236,21 @@ struct Ring : RingGeom<D, T, LDS_BYTES, XJ> {
 #pragma unroll
         for (int jj = 0; jj < G::JW; ++jj) dma16(rs, off[jj] + row_off, lds + (uint32_t)(jj * T + wt) * 1024u);
         dma4(xs, x_off + xlane, base + (uint32_t)(G::R * G::TILE + slot * G::SIDE));
+        ++issued;
+    }
+
+    // an fp8 tile (32 rows, D bytes each, rows row_off8 / stride on) into the first half
+    // of the next slot; the other half of this wave's instructions load a zero-range
+    // descriptor (`none`), so an fp8 job counts as many instructions as a bf16 one
+    __device__ __forceinline__ void issue8(rsrc_t rs, uint32_t row_off8, rsrc_t none) {
+        static_assert(XJ == 0, "fp8 tiles without side buffers");
+        static_assert(G::JW % 2 == 0, "an fp8 tile takes half of a bf16 tile's instructions");
+        const uint32_t lds = base + (uint32_t)(slot_of(issued) * G::TILE);
+#pragma unroll
+        for (int jj = 0; jj < G::JW / 2; ++jj)
+            dma16(rs, off8[jj] + row_off8, lds + (uint32_t)(jj * T + wt) * 1024u);
+#pragma unroll
+        for (int jj = G::JW / 2; jj < G::JW; ++jj) dma16(none, 0u, lds + (uint32_t)(jj * T + wt) * 1024u);
         ++issued;
     }
 
@@ -351,6 +399,15 @@ __device__ __forceinline__ void pump(Pol& pol, Walk& w, RingT& ring, int consume
     }
 }
 
+// A policy may set up the ring once it is initialised (fp8 tile offsets): it does
+// so with a member ring_ready(ring, lane), which is called when present.
+template <class Pol, class RingT>
+__device__ __forceinline__ auto ring_ready(Pol& p, RingT& g, int lane, int) -> decltype(p.ring_ready(g, lane), void()) {
+    p.ring_ready(g, lane);
+}
+template <class Pol, class RingT>
+__device__ __forceinline__ void ring_ready(Pol&, RingT&, int, long) {}
+
 // This team's bin: workgroups are dispatched round-robin over the 8 XCDs, so the
 // workgroup index is remapped to make consecutive logical workgroups (whose bins
 // the planner fills with neighbouring items of equal cost, e.g. the q tiles of one
@@ -383,6 +440,7 @@ __device__ __forceinline__ void run_team(Pol& pol, int P, const Rec* __restrict_
 
     RingT ring;
     ring.init(slice, row_stride, wt, lane);
+    ring_ready(pol, ring, lane, 0);
     Walk w;
     w.idx = beg;
     w.end = end;

@@ -237,6 +237,78 @@ def test_cut_items(d, case, deal):
 
 
 # ---------------------------------------------------------------------------
+# fp8 (e4m3fn) Q and K in the forward
+# ---------------------------------------------------------------------------
+
+def quant_e4m3(t):
+    """Per-tensor scale amax / 448 and OCP e4m3fn bytes (quantised on the host by torch)."""
+    x = t.float().cpu()
+    s = float(x.abs().max()) / 448.0 if x.numel() else 1.0
+    s = s if s > 0 else 1.0
+    q8 = (x / s).to(torch.float8_e4m3fn)
+    return q8, s
+
+
+def run_fp8_fwd(inp, act=None, dtype="bf16", **opts):
+    act = act or inp.act
+    qo, ko = dev_offsets(inp)
+    q8, sq = quant_e4m3(inp.q)
+    k8, sk = quant_e4m3(inp.k)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, dtype, **opts) as plan:
+        o = torch.empty(inp.q.shape, dtype=torch.float32 if dtype == "bf16_f32out" else torch.bfloat16, device=DEV)
+        G.gdpa_fp8_fwd(plan.handle, q8.view(torch.uint8).to(DEV), k8.view(torch.uint8).to(DEV), inp.v, qo, ko,
+                       plan.B, inp.H, inp.d, act, inp.window, sq, sk, o)
+        torch.cuda.synchronize()
+        n_parts = plan.stats()["n_parts"]
+    # the oracle on the values the bytes stand for
+    ref = R.gdpa_fwd(q8.double().numpy() * sq, k8.double().numpy() * sk, inp.f64("v"), inp.q_off, inp.kv_off, act,
+                     inp.window)
+    return o.float().cpu().numpy(), ref, n_parts
+
+
+@pytest.mark.parametrize("d,team,nb", FWD_LAYOUTS)
+def test_fp8_forward_layouts(d, team, nb):
+    say(f"fp8 forward d={d} team={team} blocks={nb}")
+    inp = make_from_lengths(JFA_LQ, JFA_LK, 2, d, act="silu", seed=71, device=DEV)
+    o, ref, _ = run_fp8_fwd(inp, team=(team, 0, 0), blocks=(nb, 0, 0))
+    check_close(o, ref, f"fp8 O d={d}")
+    o32, ref, _ = run_fp8_fwd(inp, dtype="bf16_f32out", team=(team, 0, 0), blocks=(nb, 0, 0))
+    check_close(o32, ref, f"fp8 O f32out d={d}")
+
+
+@pytest.mark.parametrize("act", ["gelu", "identity"])
+@pytest.mark.parametrize("window", [0, 17])
+def test_fp8_forward_acts_windows(act, window):
+    say(f"fp8 forward act={act} window={window}")
+    L = [1, 31, 32, 33, 127, 300, 0, 65]
+    inp = make_from_lengths(L, L, 2, 128, act=act, window=window, seed=72, device=DEV)
+    o, ref, _ = run_fp8_fwd(inp)
+    check_close(o, ref, f"fp8 O act={act} window={window}")
+
+
+def test_fp8_forward_cut_items():
+    inp = make_from_lengths([32, 1], [3000, 5], 2, 64, act="gelu", seed=73, device=DEV)
+    o, ref, n_parts = run_fp8_fwd(inp, bins=(16, 16, 16))
+    assert n_parts[0] > 0
+    check_close(o, ref, "fp8 O cut")
+
+
+def test_fp8_forward_rejects():
+    inp = make_from_lengths([40, 3], [50, 7], 2, 64, act="gelu", seed=74, device=DEV)
+    qo, ko = dev_offsets(inp)
+    b8 = torch.zeros(inp.q.shape, dtype=torch.uint8, device=DEV)
+    k8 = torch.zeros(inp.k.shape, dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(inp.q)
+    for dtype, act, sq, status in (("f32", "gelu", 1.0, "GDPA_ERR_UNSUPPORTED"), ("bf16", "one", 1.0,
+                                   "GDPA_ERR_UNSUPPORTED"), ("bf16", "gelu", 0.0, "GDPA_ERR_INVALID_ARG"),
+                                   ("bf16", "gelu", float("nan"), "GDPA_ERR_INVALID_ARG")):
+        with G.Plan(inp.q_off, inp.kv_off, 2, 64, 0, dtype) as plan:
+            with pytest.raises(G.GdpaError) as e:
+                G.gdpa_fp8_fwd(plan.handle, b8, k8, inp.v, qo, ko, 2, 2, 64, act, 0, sq, 1.0, o)
+            assert G.STATUS[e.value.status] == status, (dtype, act, sq)
+
+
+# ---------------------------------------------------------------------------
 # RMSNorm prologue: GDPA on normalised Q, K, V from the raw tensors
 # ---------------------------------------------------------------------------
 
