@@ -2,7 +2,7 @@
 """Benchmark of jagged GDPA forward + backward (bf16 in, fp32 accumulate) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 2|3|4|5|pffn] [--act NAME] [--attn gdpa|softmax]
-                    [--norm]
+                    [--norm] [--fp8]
 
 A step is one forward pass plus one backward pass (dK/dV kernel, then dQ kernel)
 over the whole batch of the chosen workload, with inputs resident in HBM.  The
@@ -30,6 +30,10 @@ workload normalises: Q, K, V, or K, V for PMA): the 1/rms pre-pass, then the
 forward, dK/dV and dQ kernels that read the raw tensors.  The line also carries the
 plain kernels' time on the same batch and the HBM floor of the unfused norm the
 prologue replaces (forward: read x, write x^; backward: read x and dx^, write dx).
+
+--fp8 runs the forward with Q and K as fp8 (OCP e4m3, one scale per tensor,
+quantised on the host before the timed region) and the backward in bf16 as gdpa_bwd
+runs it; the forward's algorithmic bytes count one byte per element of Q and K.
 """
 from __future__ import annotations
 
@@ -42,6 +46,7 @@ import time
 
 METRIC = "useful TFLOP/s, jagged GDPA fwd+bwd bf16, % of MFMA peak, 1 MI355X"
 METRIC_JFA = "useful TFLOP/s, jagged softmax attention (JFA) fwd+bwd bf16, 1 MI355X"
+METRIC_FP8 = "useful TFLOP/s, jagged GDPA fwd (fp8 Q, K) + bwd (bf16), 1 MI355X"
 METRIC_NORM = "useful TFLOP/s, jagged GDPA fwd+bwd with fused RMSNorm prologue, bf16, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
@@ -58,7 +63,7 @@ def kernel_flops(H, d, pairs, Tq=0):
     return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd": 5 * u, "stat": 2.0 * H * d * Tq}
 
 
-def kernel_bytes(H, d, Tq, Tk, softmax=False, norm=""):
+def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False):
     """Algorithmic bytes per launch (bf16): every input read once, every output written
     once; softmax (JFA): plus the fp32 row LSE written by the forward, and the fp32
     (LSE, D) row pair that the pre-pass writes and the gradient kernels read; norm
@@ -67,7 +72,8 @@ def kernel_bytes(H, d, Tq, Tk, softmax=False, norm=""):
     e = 2 * H * d
     lse, st = (4 * H * Tq, 8 * H * Tq) if softmax else (0, 0)
     rs = 4 * H * (Tq + 2 * Tk) if norm else 0
-    return {"fwd": e * (2 * Tq + 2 * Tk) + lse + rs,    # Q, K, V (, rstd) -> O (, LSE)
+    qk = 0.5 if fp8 else 1.0                           # fp8 Q, K: one byte per element
+    return {"fwd": int(e * (qk * Tq + qk * Tk + Tk + Tq)) + lse + rs,   # Q, K, V (, rstd) -> O (, LSE)
             "dkdv": e * (2 * Tq + 4 * Tk) + st + rs,    # Q, dO, K, V (, stat or rstd) -> dK, dV
             "dq": e * (3 * Tq + 2 * Tk) + st + rs,      # Q, dO, K, V (, stat or rstd) -> dQ
             "bwd": e * (3 * Tq + 4 * Tk),               # one-pass backward: Q, dO, K, V -> dQ, dK, dV
@@ -164,6 +170,8 @@ def main(argv=None):
                     help="softmax: jagged softmax attention (JFA) on the same batch")
     ap.add_argument("--norm", action="store_true",
                     help="GDPA with the fused RMSNorm prologue on raw inputs of the same batch")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward with fp8 (e4m3) Q and K, backward in bf16, on the same batch")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -210,8 +218,11 @@ def main(argv=None):
     if (sm or args.norm) and args.config == "pffn":
         print("--attn softmax and --norm run the attention workloads", file=sys.stderr)
         return 2
-    if sm and args.norm:
-        print("--norm runs GDPA, not JFA", file=sys.stderr)
+    if sum([sm, args.norm, args.fp8]) > 1:
+        print("--attn softmax, --norm and --fp8 are separate modes", file=sys.stderr)
+        return 2
+    if args.fp8 and args.config == "pffn":
+        print("--fp8 runs the attention workloads", file=sys.stderr)
         return 2
     norm = w["rms"] if args.norm else ""
     t0 = time.perf_counter()
@@ -272,6 +283,17 @@ def main(argv=None):
         def ndq():
             G.gdpa_norm_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, norm, rstd, dq, sh)
 
+    if args.fp8:
+        def quant(t):   # per-tensor scale amax / 448, OCP e4m3 bytes (on the host, once)
+            x = t.float().cpu()
+            sc8 = max(float(x.abs().max()) / 448.0, 1e-30)
+            return (x / sc8).to(torch.float8_e4m3fn).view(torch.uint8).to("cuda"), sc8
+        q8, sq8 = quant(inp.q)
+        k8, sk8 = quant(inp.k)
+
+        def ffwd():
+            G.gdpa_fp8_fwd(h, q8, k8, inp.v, qo, ko, B, H, d, act, win, sq8, sk8, o, sh)
+
     # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels (JFA and
     # the norm prologue: always the two kernels, after their pre-pass)
     fused = 0 if (sm or norm) else st["bwd_fused"]
@@ -280,7 +302,8 @@ def main(argv=None):
     elif norm:
         calls = [("rstd", nrstd), ("fwd", nfwd), ("dkdv", ndkdv), ("dq", ndq)]
     else:
-        calls = [("fwd", fwd), ("bwd", bwd)] if fused else [("fwd", fwd), ("dkdv", dkdv), ("dq", dqk)]
+        f0 = ffwd if args.fp8 else fwd
+        calls = [("fwd", f0), ("bwd", bwd)] if fused else [("fwd", f0), ("dkdv", dkdv), ("dq", dqk)]
     for _ in range(args.warmup):
         for _, c in calls:
             c()
@@ -306,10 +329,10 @@ def main(argv=None):
 
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
-    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm)
+    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8)
     kf = kernel_flops(H, d, pairs, Tq)
     dom = max(kms, key=kms.get)
-    trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "")   # this workload's counter record
+    trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "_fp8" if args.fp8 else "")   # its counter record
     # the roof the kernel's arithmetic intensity puts it under (ridge: peak FLOP/s / peak B/s)
     mfma_bound = kf[dom] / kb[dom] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
@@ -328,7 +351,7 @@ def main(argv=None):
     bwd_ms = kms["bwd"] if fused else kms["dkdv"] + kms["dq"] + kms.get("stat", 0.0)
 
     out = {
-        "metric": METRIC_JFA if sm else METRIC_NORM if norm else METRIC,
+        "metric": METRIC_JFA if sm else METRIC_NORM if norm else METRIC_FP8 if args.fp8 else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -338,7 +361,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8+bf16" if args.fp8 else "bf16",
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs,
