@@ -21,9 +21,10 @@ launch stream around each launch.  `cpu_baseline` times the fp64 oracle on the
 host cores over a bounded prefix of the same batch.
 
 --attn softmax runs jagged softmax attention (JFA) through the same kernels on the
-same batch instead: the forward (also writing the row log-sum-exp), the backward's
-row-statistics pre-pass, then the dK/dV and dQ kernels; FLOPs are counted as for
-GDPA (the exponentials are not counted).
+same batch instead: the forward (also writing the row log-sum-exp), then the dQ
+kernel (which also forms each row's D = sum dO * O from a third stationary tile of
+O and writes the (LSE, D) pairs) and the dK/dV kernel that reads them; FLOPs are
+counted as for GDPA (the exponentials and D are not counted).
 
 --norm runs GDPA with the fused RMSNorm prologue on raw inputs (the tensors the
 workload normalises: Q, K, V, or K, V for PMA): the 1/rms pre-pass, then the
@@ -75,7 +76,7 @@ def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False):
     qk = 0.5 if fp8 else 1.0                           # fp8 Q, K: one byte per element
     return {"fwd": int(e * (qk * Tq + qk * Tk + Tk + Tq)) + lse + rs,   # Q, K, V (, rstd) -> O (, LSE)
             "dkdv": e * (2 * Tq + 4 * Tk) + st + rs,    # Q, dO, K, V (, stat or rstd) -> dK, dV
-            "dq": e * (3 * Tq + 2 * Tk) + st + rs,      # Q, dO, K, V (, stat or rstd) -> dQ
+            "dq": e * (3 * Tq + 2 * Tk) + (e * Tq + lse if softmax else 0) + st + rs,   # (+ O, LSE) -> dQ (, stat)
             "bwd": e * (3 * Tq + 4 * Tk),               # one-pass backward: Q, dO, K, V -> dQ, dK, dV
             "stat": 2 * e * Tq + lse + st,              # O, dO, LSE -> stat
             "rstd": e * (Tq * ("q" in norm) + Tk * ("k" in norm) + Tk * ("v" in norm)) + rs}
@@ -259,14 +260,11 @@ def main(argv=None):
         def jfwd():
             G.gdpa_jfa_fwd(h, inp.q, inp.k, inp.v, qo, ko, B, H, d, win, o, lse, sh)
 
-        def jstat():
-            G.gdpa_jfa_bwd_stat(h, o, lse, inp.do, H, d, stat, sh)
-
         def jdkdv():
             G.gdpa_jfa_bwd_dkdv(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, win, stat, dk, dv, sh)
 
         def jdq():
-            G.gdpa_jfa_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, win, stat, dq, sh)
+            G.gdpa_jfa_bwd_dq(h, inp.q, inp.k, inp.v, o, lse, inp.do, qo, ko, B, H, d, win, stat, dq, sh)
 
     if norm:
         rstd = torch.empty((H * (Tq + 2 * Tk),), dtype=torch.float32, device="cuda")
@@ -298,7 +296,7 @@ def main(argv=None):
     # the norm prologue: always the two kernels, after their pre-pass)
     fused = 0 if (sm or norm) else st["bwd_fused"]
     if sm:
-        calls = [("fwd", jfwd), ("stat", jstat), ("dkdv", jdkdv), ("dq", jdq)]
+        calls = [("fwd", jfwd), ("dq", jdq), ("dkdv", jdkdv)]
     elif norm:
         calls = [("rstd", nrstd), ("fwd", nfwd), ("dkdv", ndkdv), ("dq", ndq)]
     else:
@@ -365,7 +363,7 @@ def main(argv=None):
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs,
-                   "backward": ("row-statistics pre-pass + dK/dV + dQ kernels" if sm else
+                   "backward": ("dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
                                 "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else
                                 ["dK/dV + dQ kernels", "one KV-stationary pass", "one Q-stationary pass"][fused])},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

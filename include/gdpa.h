@@ -229,33 +229,34 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
  * dQ = dS K / sqrt(d).  Arguments as gdpa_bwd without act, plus
  *   o, lse : the forward's outputs (bf16 [Tq,H,d]; fp32 [H,Tq]), read;
  *   stat   : device fp32 [H, Tq, 2], caller-owned scratch, written: per (head, q
- *            row) the pair (LSE_i log2(e), D_i) that the gradient kernels read.
- * Enqueues a row-statistics pre-pass, the KV-stationary dK/dV kernel and the
- * Q-stationary dQ kernel (never the one-pass kernels), plus the chunk reductions
- * of cut items.  The plan must be bf16 with one-wave dQ and dK/dV teams (the
- * automatic layouts; UNSUPPORTED otherwise).  Errors as gdpa_bwd.
- * gdpa_jfa_bwd == gdpa_jfa_bwd_stat, then gdpa_jfa_bwd_dkdv, then gdpa_jfa_bwd_dq.
+ *            row) the pair (LSE_i log2(e), D_i).
+ * Enqueues the Q-stationary dQ kernel, which also forms D from O and dO and writes
+ * stat, then the KV-stationary dK/dV kernel, which reads stat (never the one-pass
+ * kernels), plus the chunk reductions of cut items.  The plan must be bf16 with
+ * one-wave dQ and dK/dV teams (the automatic layouts; UNSUPPORTED otherwise).
+ * Errors as gdpa_bwd.  gdpa_jfa_bwd == gdpa_jfa_bwd_dq, then gdpa_jfa_bwd_dkdv.
  */
 gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
                          int B, int H, int d, int window, float* stat, void* dq, void* dk, void* dv, void* stream);
 
 /*
- * The three parts of gdpa_jfa_bwd, for callers who schedule them separately:
- *   gdpa_jfa_bwd_stat - only the pre-pass: fills stat [H, Tq, 2] from o, lse and
- *                       dout (H and d must match the plan);
- *   gdpa_jfa_bwd_dkdv - only dK, dV, reading a stat filled for the same o, lse, dout;
- *   gdpa_jfa_bwd_dq   - only dQ, likewise.
- * Arguments and errors as gdpa_jfa_bwd; stat is read-only in the last two.
+ * The parts of gdpa_jfa_bwd, for callers who schedule them separately:
+ *   gdpa_jfa_bwd_dq   - dQ, and stat written from o, lse and dout;
+ *   gdpa_jfa_bwd_dkdv - dK, dV, reading a stat written for the same o, lse, dout
+ *                       (by gdpa_jfa_bwd_dq or gdpa_jfa_bwd_stat);
+ *   gdpa_jfa_bwd_stat - only stat, from o, lse and dout (one pass over O and dO;
+ *                       H and d must match the plan), so that dK/dV can run first.
+ * Arguments and errors as gdpa_jfa_bwd.
  */
-gdpa_status gdpa_jfa_bwd_stat(gdpa_plan plan, const void* o, const float* lse, const void* dout, int H, int d,
-                              float* stat, void* stream);
+gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
+                            int B, int H, int d, int window, float* stat, void* dq, void* stream);
 gdpa_status gdpa_jfa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
                               const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, int window,
                               const float* stat, void* dk, void* dv, void* stream);
-gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
-                            const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, int window,
-                            const float* stat, void* dq, void* stream);
+gdpa_status gdpa_jfa_bwd_stat(gdpa_plan plan, const void* o, const float* lse, const void* dout, int H, int d,
+                              float* stat, void* stream);
 
 /*
  * GDPA with a fused RMSNorm prologue: the inputs named by `norm` (a combination of

@@ -94,7 +94,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_norm_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd_stat.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]
     lib.gdpa_jfa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
-    lib.gdpa_jfa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
+    lib.gdpa_jfa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_pffn_plan_create.argtypes = [_i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts), ctypes.POINTER(_vp)]
     lib.gdpa_pffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
     lib.gdpa_pffn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp]
@@ -208,9 +208,10 @@ def gdpa_jfa_bwd_dkdv(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, windo
                                             _stream(stream)))
 
 
-def gdpa_jfa_bwd_dq(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, window, stat, dq, stream=None):
-    _check(load_library().gdpa_jfa_bwd_dq(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(q_off_dev),
-                                          _ptr(kv_off_dev), B, H, d, window, _ptr(stat), _ptr(dq),
+def gdpa_jfa_bwd_dq(plan, q, k, v, o, lse, dout, q_off_dev, kv_off_dev, B, H, d, window, stat, dq, stream=None):
+    """dQ of the JFA backward; also writes stat (LSE log2 e, D) for gdpa_jfa_bwd_dkdv."""
+    _check(load_library().gdpa_jfa_bwd_dq(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                          _ptr(q_off_dev), _ptr(kv_off_dev), B, H, d, window, _ptr(stat), _ptr(dq),
                                           _stream(stream)))
 
 

@@ -544,19 +544,22 @@ static gdpa_status jfa_check(gdpa_plan plan) {
     return GDPA_OK;
 }
 
-// dK/dV and/or dQ of the JFA backward from filled row statistics
-static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
-                             const int32_t* q_off_dev, const int32_t* kv_off_dev, const float* stat, void* dq,
-                             void* dk, void* dv, hipStream_t s, bool want_dkdv, bool want_dq) {
+// the JFA backward's gradient kernels: the dQ kernel (reads o and lse, writes stat),
+// then the dK/dV kernel (reads stat)
+static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
+                             float* stat, void* dq, void* dk, void* dv, hipStream_t s, bool want_dkdv, bool want_dq) {
     const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
     if (any_q && (!q || !dout || !stat)) return fail(GDPA_ERR_INVALID_ARG, "q, dout or stat is NULL");
     if (any_k && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
-    if (want_dq && any_q && !dq) return fail(GDPA_ERR_INVALID_ARG, "dq is NULL");
+    if (want_dq && any_q && (!dq || !o || !lse)) return fail(GDPA_ERR_INVALID_ARG, "dq, o or lse is NULL");
     if (want_dkdv && any_k && (!dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "dk or dv is NULL");
     KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
     a.q = q;
     a.k = k;
     a.v = v;
+    a.o = const_cast<void*>(o);   // read only: the forward's output
+    a.lse = const_cast<float*>(lse);
     a.dout = dout;
     a.dq = dq;
     a.dk = dk;
@@ -565,7 +568,21 @@ static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const
     a.Tq = (int)plan->Tq;
     const int d = plan->d;
     hipError_t e = hipSuccess;
-    if (want_dkdv && any_k) {
+    if (want_dq && any_q) {
+        const WorkList& wl = plan->lists[LIST_DQ];
+        KernelArgs b = a;
+        b.items = plan->d_items[LIST_DQ];
+        b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+        b.P = wl.P;
+        b.part = plan->d_part[LIST_DQ];
+        switch (d) {
+            case 32: e = launch_dq_bf16_d32(b, wl.team, wl.nb, kActSoftmax, s); break;
+            case 64: e = launch_dq_bf16_d64(b, wl.team, wl.nb, kActSoftmax, s); break;
+            default: e = launch_dq_bf16_d128(b, wl.team, wl.nb, kActSoftmax, s); break;
+        }
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
+    }
+    if (e == hipSuccess && want_dkdv && any_k) {
         const WorkList& wl = plan->lists[LIST_DKDV];
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DKDV];
@@ -580,20 +597,6 @@ static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const
         if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
         if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
     }
-    if (e == hipSuccess && want_dq && any_q) {
-        const WorkList& wl = plan->lists[LIST_DQ];
-        KernelArgs b = a;
-        b.items = plan->d_items[LIST_DQ];
-        b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
-        b.P = wl.P;
-        b.part = plan->d_part[LIST_DQ];
-        switch (d) {
-            case 32: e = launch_dq_bf16_d32(b, wl.team, wl.nb, kActSoftmax, s); break;
-            case 64: e = launch_dq_bf16_d64(b, wl.team, wl.nb, kActSoftmax, s); break;
-            default: e = launch_dq_bf16_d128(b, wl.team, wl.nb, kActSoftmax, s); break;
-        }
-        if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
-    }
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no JFA backward kernel for this configuration");
     if (e != hipSuccess) return fail_hip(e, "JFA backward launch");
     return GDPA_OK;
@@ -606,13 +609,8 @@ gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const voi
     gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
     if (st == GDPA_OK) st = jfa_check(plan);
     if (st != GDPA_OK) return st;
-    if (plan->Tq > 0 && !dq) return fail(GDPA_ERR_INVALID_ARG, "dq is NULL");
-    if (plan->Tk > 0 && (!k || !v || !dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "k, v, dk or dv is NULL");
-    if (plan->Tq > 0 && !q) return fail(GDPA_ERR_INVALID_ARG, "q is NULL");
-    hipStream_t s = (hipStream_t)stream;
-    st = jfa_stat(plan, o, lse, dout, stat, s);
-    if (st != GDPA_OK) return st;
-    return jfa_grads(plan, q, k, v, dout, q_off_dev, kv_off_dev, stat, dq, dk, dv, s, true, true);
+    return jfa_grads(plan, q, k, v, o, lse, dout, q_off_dev, kv_off_dev, stat, dq, dk, dv, (hipStream_t)stream, true,
+                     true);
 }
 
 gdpa_status gdpa_jfa_bwd_stat(gdpa_plan plan, const void* o, const float* lse, const void* dout, int H, int d,
@@ -633,19 +631,19 @@ gdpa_status gdpa_jfa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, cons
     gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
     if (st == GDPA_OK) st = jfa_check(plan);
     if (st != GDPA_OK) return st;
-    return jfa_grads(plan, q, k, v, dout, q_off_dev, kv_off_dev, stat, nullptr, dk, dv, (hipStream_t)stream, true,
-                     false);
+    return jfa_grads(plan, q, k, v, nullptr, nullptr, dout, q_off_dev, kv_off_dev, const_cast<float*>(stat), nullptr,
+                     dk, dv, (hipStream_t)stream, true, false);
 }
 
-gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
-                            const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, int window,
-                            const float* stat, void* dq, void* stream) {
+gdpa_status gdpa_jfa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
+                            const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
+                            int B, int H, int d, int window, float* stat, void* dq, void* stream) {
     g_err.clear();
     gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, GDPA_ACT_GELU, window);
     if (st == GDPA_OK) st = jfa_check(plan);
     if (st != GDPA_OK) return st;
-    return jfa_grads(plan, q, k, v, dout, q_off_dev, kv_off_dev, stat, dq, nullptr, nullptr, (hipStream_t)stream,
-                     false, true);
+    return jfa_grads(plan, q, k, v, o, lse, dout, q_off_dev, kv_off_dev, stat, dq, nullptr, nullptr,
+                     (hipStream_t)stream, false, true);
 }
 
 // the RMSNorm prologue's checks and its factor arrays inside `rstd`

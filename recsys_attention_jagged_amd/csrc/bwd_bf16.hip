@@ -29,7 +29,10 @@
 // 32 q rows of a tile travel with it: one more load instruction per job brings
 // them into a side buffer of the tile's ring slot (ring.hpp), and jobs without
 // statistics load a zero-range side so that every job counts the same.  Keys past
-// a sample's length are masked in dQ: exp(0 - LSE) is not 0 there.
+// a sample's length are masked in dQ: exp(0 - LSE) is not 0 there.  The dQ kernel
+// runs first: it also loads each q tile's rows of the forward's O as a third
+// stationary tile, forms D from them and the dO rows it holds, and stores the
+// (LSE log2 e, D) pairs that the dK/dV kernel's side loads then read.
 //
 // With the RMSNorm prologue (NORM) the inputs are raw and each row's 1/rms r (from a
 // pre-pass, carried in the side buffers like the JFA statistics) scales the
@@ -87,14 +90,17 @@ __device__ __forceinline__ void lds_acc_row(const char* tile, int r, int hh, bf1
 
 template <int D, int T, int NB, int ACT, int NORM>
 struct DqPol : Common {
-    // stationary tiles, wave-major: (Q, dO) of block 0, (Q, dO) of block 1, ...
-    static constexpr int NSTAT = 2 * T * NB, NSTRM = 2;
+    static constexpr bool SM = ACT == ACT_SOFTMAX;
+    // stationary tiles, wave-major: (Q, dO) of block 0, (Q, dO) of block 1, ...; softmax:
+    // (Q, dO, O) per block, O for the row's D = sum dO * O
+    static constexpr int K3 = SM ? 3 : 2;
+    static constexpr int NSTAT = K3 * T * NB, NSTRM = 2;
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr int ROWS = 32 * T * NB;   // q rows per item
     static constexpr bool HOIST = TeamShape<D, T, 2>::HOIST;
-    static constexpr bool SM = ACT == ACT_SOFTMAX;
     rsrc_t wq, wo, wk, wv;   // issuing side
-    rsrc_t wst, wnull;       // softmax: row statistics of the item's q rows; a zero-range side
+    rsrc_t wst, wnull;       // softmax: LSE of the item's q rows; a zero-range side
+    rsrc_t wfo;              // softmax: the forward's O rows
     bf16x8 qf[NB][NKS], of[NB][NKS];
     f32x16 acc[NB][NDB];
     float l2q[NB], dq_[NB];  // softmax: this lane's q row's LSE log2(e) and D
@@ -114,8 +120,9 @@ struct DqPol : Common {
         wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
         wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
         if constexpr (SM) {
-            wst = slice_rsrc(a.stat + ((size_t)w.h * a.Tq + w.qs) * 2, w.lq, 8u, 8u);
-            wnull = slice_rsrc(a.stat, 0, 8u, 8u);
+            wst = slice_rsrc(a.lse + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wnull = slice_rsrc(a.lse, 0, 4u, 4u);
+            wfo = slice_rsrc((const __bf16*)a.o + qb, w.lq, rs, D * 2);
         }
         if constexpr (NORM) {
             wrq = slice_rsrc(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
@@ -136,11 +143,22 @@ struct DqPol : Common {
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * (i >> 1));
+            // 0 Q (side: LSE or 1/rms of its rows), 1 dO, 2 O; uniform, so that the
+            // descriptor chosen by it stays in scalar registers
+            const int kind = __builtin_amdgcn_readfirstlane(i % K3);
+            const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * (i / K3));
             if constexpr (NORM)
-                put(g, (i & 1) ? wo : wq, row0 * rs, (i & 1) ? wnull : wrq, row0 * 4u);
+                put(g, kind ? wo : wq, row0 * rs, kind ? wnull : wrq, row0 * 4u);
+            else if constexpr (SM) {
+                if (kind == 0)
+                    put(g, wq, row0 * rs, wst, row0 * 4u);
+                else if (kind == 1)
+                    put(g, wo, row0 * rs, wnull, 0u);
+                else
+                    put(g, wfo, row0 * rs, wnull, 0u);
+            }
             else
-                put(g, (i & 1) ? wo : wq, row0 * rs, (i & 1) ? wnull : wst, row0 * 8u);
+                put(g, kind ? wo : wq, row0 * rs, wnull, 0u);
         } else {
             const int rel = i - NSTAT;
             const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
@@ -158,24 +176,44 @@ struct DqPol : Common {
             for (int db = 0; db < NDB; ++db) acc[b][db] = f32x16{};
     }
 
-    // stationary tiles i (Q) and i + 1 (dO) of block i / 2, owned by wave i / (2 NB)
+    // stationary tiles i, i + 1 (jobs job, job + 1): tile u is kind u % K3 (Q, dO, O)
+    // of block u / K3, owned by wave u / (K3 NB)
     template <class RingT>
-    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job, int i) {
-        const int blk = i >> 1;
-        if (blk / NB == wt) {
+    __device__ __forceinline__ void load_stat(const Rec& c, const RingT& g, int job, int i) {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                qf[blk % NB][ks] = lds_row8<D>(g.tile(job), r, 2 * ks + hh);
-                of[blk % NB][ks] = lds_row8<D>(g.tile(job + 1), r, 2 * ks + hh);
-            }
-            if constexpr (SM) {   // the Q job's side: (LSE log2 e, D) of this lane's q row
-                const float2 st = *(const float2*)(g.side(job) + 8 * r);
-                l2q[blk % NB] = st.x;
-                dq_[blk % NB] = st.y;
-            }
-            if constexpr (NORM) {   // the Q job's side: 1/rms of this lane's q row; the row for the norm's gradient
-                rqv[blk % NB] = *(const float*)(g.side(job) + 4 * r);
-                lds_acc_row<D>(g.tile(job), r, hh, qa[blk % NB]);
+        for (int u = 0; u < 2; ++u) {
+            const int tile = i + u, blk = tile / K3, kind = tile % K3;
+            if (tile >= NSTAT || blk / NB != wt) continue;
+            const int b = blk % NB;
+            const char* tl = g.tile(job + u);
+            if (kind == 0) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) qf[b][ks] = lds_row8<D>(tl, r, 2 * ks + hh);
+                if constexpr (SM) {   // the Q job's side: LSE of this lane's q row
+                    constexpr float L2E = 1.4426950408889634f;
+                    l2q[b] = *(const float*)(g.side(job + u) + 4 * r) * L2E;
+                }
+                if constexpr (NORM) {   // the Q job's side: 1/rms of this lane's q row; the row for the norm's gradient
+                    rqv[b] = *(const float*)(g.side(job + u) + 4 * r);
+                    lds_acc_row<D>(tl, r, hh, qa[b]);
+                }
+            } else if (kind == 1) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) of[b][ks] = lds_row8<D>(tl, r, 2 * ks + hh);
+            } else if constexpr (SM) {   // O: D = sum dO * O of this lane's row, both half-rows
+                float dsum = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const bf16x8 ov = lds_row8<D>(tl, r, 2 * ks + hh);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)of[b][ks][e], (float)ov[e], dsum);
+                }
+                dsum += __shfl_xor(dsum, 32);
+                dq_[b] = dsum;
+                // the pair the dK/dV kernel reads (chunks of a cut item write the same values)
+                const int row = qrow(c, b) + r;
+                if (hh == 0 && row < c.lq)
+                    *(float2*)(a.stat + ((size_t)c.h * a.Tq + c.qs + row) * 2) = make_float2(l2q[b], dsum);
             }
         }
     }
@@ -316,6 +354,15 @@ struct DqPol : Common {
         const size_t ob = ((size_t)c.qs * H + c.h) * D;
 #pragma unroll
         for (int b = 0; b < NB; ++b) zero<D>(a.dq, ob, c.lq, qrow(c, b));
+        if constexpr (SM) {   // rows without keys: LSE -inf, O = 0, so D = 0
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int row = qrow(c, b) + r;
+                if (hh == 0 && row < c.lq)
+                    *(float2*)(a.stat + ((size_t)c.h * a.Tq + c.qs + row) * 2) =
+                        make_float2(-__builtin_inff(), 0.0f);
+            }
+        }
     }
 };
 

@@ -34,10 +34,11 @@ struct KernelArgs {
     float scale;    // 1 / sqrt(d)
     int out_f32;    // outputs stored as fp32 instead of bf16
     // softmax attention (JFA) only: per-row log-sum-exp, fp32 [H, Tq] (head-major),
-    // written by the forward; the backward reads per (head, q row) the pair
-    // (LSE log2(e), D = sum of dO * O over the row), fp32 [H, Tq, 2]
+    // written by the forward (and read by the backward's dQ kernel, with the forward's
+    // O in `o`); per (head, q row) the pair (LSE log2(e), D = sum of dO * O over the
+    // row), fp32 [H, Tq, 2], written by the dQ kernel and read by the dK/dV kernel
     float* lse;
-    const float* stat;
+    float* stat;
     int Tq;
     // RMSNorm prologue only: 1/rms per (head, row) of Q, fp32 [H, Tq], and of K and V
     // as pairs, fp32 [H, Tk, 2] (1 for a tensor left raw); `norm` says which of Q (1),

@@ -576,22 +576,34 @@ def test_jfa_backward_cut_items():
 
 
 def test_jfa_backward_parts_match_whole():
-    """gdpa_jfa_bwd_stat, _dkdv and _dq in turn give gdpa_jfa_bwd's outputs bit for bit."""
-    say("JFA backward in three calls")
+    """gdpa_jfa_bwd_dq then gdpa_jfa_bwd_dkdv give gdpa_jfa_bwd's outputs bit for bit; with
+    stat from the pre-pass (gdpa_jfa_bwd_stat) dK/dV may run first, to rounding."""
+    say("JFA backward in parts")
     inp = make_from_lengths(JFA_LQ, JFA_LK, 2, 128, act="gelu", seed=58, device=DEV)
     whole = run_jfa_bwd(inp)
     qo, ko = dev_offsets(inp)
     o = torch.tensor(whole[3], dtype=torch.bfloat16, device=DEV)
     lse = torch.tensor(whole[4], device=DEV)
     with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, 0, "bf16") as plan:
+        args = (plan.handle, inp.q, inp.k, inp.v)
         stat = torch.full((inp.H, inp.q.shape[0], 2), float("nan"), device=DEV)
         dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
-        G.gdpa_jfa_bwd_stat(plan.handle, o, lse, inp.do, inp.H, inp.d, stat)
-        G.gdpa_jfa_bwd_dkdv(plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, plan.B, inp.H, inp.d, 0, stat, dk, dv)
-        G.gdpa_jfa_bwd_dq(plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, plan.B, inp.H, inp.d, 0, stat, dq)
+        G.gdpa_jfa_bwd_dq(*args, o, lse, inp.do, qo, ko, plan.B, inp.H, inp.d, 0, stat, dq)
+        G.gdpa_jfa_bwd_dkdv(*args, inp.do, qo, ko, plan.B, inp.H, inp.d, 0, stat, dk, dv)
+        # the pre-pass route: stat first, dK/dV before dQ
+        stat2 = torch.full_like(stat, float("nan"))
+        dk2, dv2 = torch.empty_like(inp.k), torch.empty_like(inp.v)
+        G.gdpa_jfa_bwd_stat(plan.handle, o, lse, inp.do, inp.H, inp.d, stat2)
+        G.gdpa_jfa_bwd_dkdv(*args, inp.do, qo, ko, plan.B, inp.H, inp.d, 0, stat2, dk2, dv2)
         torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV", "stat"), (dq, dk, dv, stat), (whole[0], whole[1], whole[2], whole[5])):
         assert np.array_equal(a.float().cpu().numpy(), b, equal_nan=True), name
+    s1, s2 = stat.cpu().numpy(), stat2.cpu().numpy()
+    assert np.array_equal(s1[..., 0], s2[..., 0])   # the same LSE log2(e) product
+    np.testing.assert_allclose(s2[..., 1], s1[..., 1], rtol=1e-5, atol=1e-5 * np.abs(s1[..., 1]).max())
+    ref = R.jfa_bwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.f64("do"), inp.q_off, inp.kv_off, 0)
+    check_close(dk2.float().cpu().numpy(), ref[1], "JFA dK after the pre-pass")
+    check_close(dv2.float().cpu().numpy(), ref[2], "JFA dV after the pre-pass")
 
 
 def test_jfa_backward_rejects():
