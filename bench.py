@@ -57,11 +57,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_flops(H, d, pairs, Tq=0):
+def kernel_flops(H, d, pairs, Tq=0, Tk=0):
     """Algorithmic FLOPs per launch: the MFMA products each kernel's algorithm performs
-    (stat: the JFA pre-pass's dot products dO . O)."""
+    (stat: the JFA pre-pass's dot products dO . O; rstd: the sums of squares of the norm)."""
     u = 2.0 * H * d * pairs          # one product over the valid pairs
-    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd": 5 * u, "stat": 2.0 * H * d * Tq}
+    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd": 5 * u, "stat": 2.0 * H * d * Tq,
+            "rstd": 2.0 * H * d * (Tq + 2 * Tk)}
 
 
 def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False):
@@ -83,7 +84,7 @@ def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False):
 
 
 KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd_common.hpp", "bwd_fused.hip",
-                  "jfa.hip", "partials.hip", "kernels.hpp", "plan.cpp", "plan.hpp", "api.cpp", "gelu_poly.h")
+                  "jfa.hip", "norm.hip", "partials.hip", "kernels.hpp", "plan.cpp", "plan.hpp", "api.cpp", "gelu_poly.h")
 
 
 def kernel_source_digest() -> str:
@@ -328,7 +329,7 @@ def main(argv=None):
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
     kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8)
-    kf = kernel_flops(H, d, pairs, Tq)
+    kf = kernel_flops(H, d, pairs, Tq, Tk)
     dom = max(kms, key=kms.get)
     trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "_fp8" if args.fp8 else "")   # its counter record
     # the roof the kernel's arithmetic intensity puts it under (ridge: peak FLOP/s / peak B/s)
