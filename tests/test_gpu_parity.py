@@ -853,3 +853,102 @@ def test_determinism():
     assert torch.equal(a, b)
     for x, y in zip(g1, g2):
         assert torch.equal(x, y)
+
+
+def _picks(inp, seed):
+    rng = np.random.default_rng(seed)
+    B = len(inp.lq)
+    return sorted(set(rng.choice(B, size=min(4, B), replace=False).tolist()
+                      + [int(np.argmax(inp.lq)), int(np.argmax(inp.lk))]))
+
+
+def _slices(inp, b):
+    return (int(inp.q_off[b]), int(inp.q_off[b + 1])), (int(inp.kv_off[b]), int(inp.kv_off[b + 1]))
+
+
+_f64 = lambda t, a, e: t[a:e].to("cpu", torch.float64).numpy()
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled_jfa(cfg):
+    """JFA forward and backward at full size in the benchmark's launch configuration;
+    sampled samples against the oracle one by one."""
+    say(f"cfg{cfg} full size JFA fwd + bwd, sampled samples")
+    inp = make_workload(cfg, device=DEV)
+    qo, ko = dev_offsets(inp)
+    Tq = inp.q.shape[0]
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16") as plan:
+        o = torch.empty_like(inp.q)
+        lse = torch.empty((inp.H, Tq), dtype=torch.float32, device=DEV)
+        stat = torch.empty((inp.H, Tq, 2), dtype=torch.float32, device=DEV)
+        dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+        G.gdpa_jfa_fwd(plan.handle, inp.q, inp.k, inp.v, qo, ko, plan.B, inp.H, inp.d, inp.window, o, lse)
+        G.gdpa_jfa_bwd(plan.handle, inp.q, inp.k, inp.v, o, lse, inp.do, qo, ko, plan.B, inp.H, inp.d, inp.window,
+                       stat, dq, dk, dv)
+        torch.cuda.synchronize()
+    for b in _picks(inp, cfg):
+        (qs, qe), (ks, ke) = _slices(inp, b)
+        one_q, one_k = np.array([0, qe - qs]), np.array([0, ke - ks])
+        args = (_f64(inp.q, qs, qe), _f64(inp.k, ks, ke), _f64(inp.v, ks, ke))
+        ro, rl = R.jfa_fwd(*args, one_q, one_k, inp.window)
+        rq, rk, rv = R.jfa_bwd(*args, _f64(inp.do, qs, qe), one_q, one_k, inp.window)
+        check_close(_f64(o, qs, qe), ro, f"cfg{cfg} JFA O sample {b}")
+        check_lse(lse[:, qs:qe].cpu().numpy(), rl, f"cfg{cfg} JFA LSE sample {b}")
+        check_close(_f64(dq, qs, qe), rq, f"cfg{cfg} JFA dQ sample {b}")
+        check_close(_f64(dk, ks, ke), rk, f"cfg{cfg} JFA dK sample {b}")
+        check_close(_f64(dv, ks, ke), rv, f"cfg{cfg} JFA dV sample {b}")
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_full_size_sampled_norm(cfg):
+    """The RMSNorm prologue at full size on raw inputs, in the benchmark's launch configuration."""
+    say(f"cfg{cfg} full size norm prologue fwd + bwd, sampled samples")
+    w = WORKLOADS[cfg]
+    inp = make_workload(cfg, device=DEV, raw=True)
+    norm = w["rms"]
+    qo, ko = dev_offsets(inp)
+    Tq, Tk = inp.q.shape[0], inp.k.shape[0]
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16") as plan:
+        rstd = torch.empty((inp.H * (Tq + 2 * Tk),), dtype=torch.float32, device=DEV)
+        o = torch.empty_like(inp.q)
+        dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+        a = (plan.handle, inp.q, inp.k, inp.v)
+        G.gdpa_norm_rstd(*a, inp.H, inp.d, norm, rstd)
+        G.gdpa_norm_fwd(*a, qo, ko, plan.B, inp.H, inp.d, inp.act, inp.window, norm, rstd, o)
+        G.gdpa_norm_bwd(*a, inp.do, qo, ko, plan.B, inp.H, inp.d, inp.act, inp.window, norm, rstd, dq, dk, dv)
+        torch.cuda.synchronize()
+    for b in _picks(inp, cfg):
+        (qs, qe), (ks, ke) = _slices(inp, b)
+        one_q, one_k = np.array([0, qe - qs]), np.array([0, ke - ks])
+        args = (_f64(inp.q, qs, qe), _f64(inp.k, ks, ke), _f64(inp.v, ks, ke))
+        ro = R.norm_gdpa_fwd(*args, one_q, one_k, inp.act, inp.window, norm)
+        rq, rk, rv = R.norm_gdpa_bwd(*args, _f64(inp.do, qs, qe), one_q, one_k, inp.act, inp.window, norm)
+        check_close(_f64(o, qs, qe), ro, f"cfg{cfg} norm O sample {b}")
+        check_close(_f64(dq, qs, qe), rq, f"cfg{cfg} norm dQ sample {b}")
+        check_close(_f64(dk, ks, ke), rk, f"cfg{cfg} norm dK sample {b}")
+        check_close(_f64(dv, ks, ke), rv, f"cfg{cfg} norm dV sample {b}")
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled_fp8(cfg):
+    """The fp8 forward at full size (one scale per tensor over the whole batch)."""
+    say(f"cfg{cfg} full size fp8 forward, sampled samples")
+    inp = make_workload(cfg, device=DEV)
+    qo, ko = dev_offsets(inp)
+    q8, sq = quant_e4m3(inp.q)
+    k8, sk = quant_e4m3(inp.k)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16") as plan:
+        o = torch.empty_like(inp.q)
+        G.gdpa_fp8_fwd(plan.handle, q8.view(torch.uint8).to(DEV), k8.view(torch.uint8).to(DEV), inp.v, qo, ko,
+                       plan.B, inp.H, inp.d, inp.act, inp.window, sq, sk, o)
+        torch.cuda.synchronize()
+    for b in _picks(inp, cfg):
+        (qs, qe), (ks, ke) = _slices(inp, b)
+        ro = R.gdpa_fwd(q8[qs:qe].double().numpy() * sq, k8[ks:ke].double().numpy() * sk, _f64(inp.v, ks, ke),
+                        np.array([0, qe - qs]), np.array([0, ke - ks]), inp.act, inp.window)
+        check_close(_f64(o, qs, qe), ro, f"cfg{cfg} fp8 O sample {b}")
+    assert torch.isfinite(o.float()).all()
