@@ -61,8 +61,9 @@ typedef enum {
 } gdpa_status;
 
 /* Activations.  GELU is the exact erf form x * Phi(x).  GELU_POLY is an
- * ALU-only clamped polynomial fit of it (FMA only; its absolute error bound is
- * gdpa_gelu_poly_bound()).  GELU_TAYLOR6 is the GDPA page's series (code figure
+ * ALU-only clamped polynomial fit of it (FMA only; absolute error bounds
+ * gdpa_gelu_poly_bound() for the value, gdpa_gelu_poly_grad_bound() for the
+ * derivative).  GELU_TAYLOR6 is the GDPA page's series (code figure
  * "ALU-only 6th-order Taylor GELU"), accurate only near 0.  IDENTITY and ONE
  * (P = 1 on valid pairs) are test probes; ONE has no backward. */
 typedef enum {
@@ -365,8 +366,14 @@ const char* gdpa_status_string(gdpa_status s);
 const char* gdpa_last_error(void);
 
 /* gdpa_gelu_poly_bound - max |GELU_POLY(x) - x Phi(x)| over all real x, as
- * derived when the polynomial was fitted (fp64 evaluation). */
+ * derived when the polynomial was fitted (the larger of the fp64 and the
+ * device-order fp32 evaluations, and the tail beyond the clamp). */
 double gdpa_gelu_poly_bound(void);
+
+/* gdpa_gelu_poly_grad_bound - the same for the derivative the backward kernels
+ * use, max |GELU_POLY'(x) - (Phi(x) + x phi(x))|; the derivative has its own
+ * polynomial, fitted to GELU' directly. */
+double gdpa_gelu_poly_grad_bound(void);
 
 #ifdef __cplusplus
 }

@@ -80,6 +80,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_last_error.restype = ctypes.c_char_p
     lib.gdpa_gelu_poly_bound.argtypes = []
     lib.gdpa_gelu_poly_bound.restype = ctypes.c_double
+    lib.gdpa_gelu_poly_grad_bound.argtypes = []
+    lib.gdpa_gelu_poly_grad_bound.restype = ctypes.c_double
     lib.gdpa_jfa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                  _vp]
@@ -326,6 +328,10 @@ def gdpa_last_error() -> str:
 
 def gdpa_gelu_poly_bound() -> float:
     return float(load_library().gdpa_gelu_poly_bound())
+
+
+def gdpa_gelu_poly_grad_bound() -> float:
+    return float(load_library().gdpa_gelu_poly_grad_bound())
 
 
 # ---------------------------------------------------------------------------

@@ -119,6 +119,7 @@ const char* gdpa_status_string(gdpa_status s) {
 const char* gdpa_last_error(void) { return g_err.c_str(); }
 
 double gdpa_gelu_poly_bound(void) { return GDPA_GELU_POLY_BOUND; }
+double gdpa_gelu_poly_grad_bound(void) { return GDPA_GELU_POLY_GRAD_BOUND; }
 
 gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_host, int B, int H,
                              int d, int window, gdpa_dtype dtype, const gdpa_plan_opts* opts,

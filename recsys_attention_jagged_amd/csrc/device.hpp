@@ -106,6 +106,16 @@ __device__ __forceinline__ void normal_cdf(float x, float& cdf, float& e) {
     cdf = x >= 0.0f ? 1.0f - c : c;
 }
 
+// Clamped polynomial GELU (value): x/2 + sum_k a_k x^(2k) on |x| <= R, else
+// max(x, 0); FMAs only.  Error bound over the real line in gelu_poly.h.
+__device__ __forceinline__ float gelu_poly_value(float x) {
+    const float u = x * x;
+    float p = kGeluPolyCoef[GDPA_GELU_POLY_DEGREE];
+#pragma unroll
+    for (int k = GDPA_GELU_POLY_DEGREE - 1; k >= 0; --k) p = __builtin_fmaf(p, u, kGeluPolyCoef[k]);
+    return __builtin_fabsf(x) <= GDPA_GELU_POLY_R ? __builtin_fmaf(0.5f, x, p) : __builtin_fmaxf(x, 0.0f);
+}
+
 template <int ACT>
 __device__ __forceinline__ float act_fwd(float x) {
     if constexpr (ACT == ACT_GELU) {
@@ -115,11 +125,7 @@ __device__ __forceinline__ float act_fwd(float x) {
     } else if constexpr (ACT == ACT_SILU) {
         return x * fast_rcp(1.0f + fast_exp2(x * -1.4426950408889634f));
     } else if constexpr (ACT == ACT_GELU_POLY) {
-        const float u = x * x;
-        float p = kGeluPolyCoef[GDPA_GELU_POLY_DEGREE];
-#pragma unroll
-        for (int k = GDPA_GELU_POLY_DEGREE - 1; k >= 0; --k) p = __builtin_fmaf(p, u, kGeluPolyCoef[k]);
-        return __builtin_fabsf(x) <= GDPA_GELU_POLY_R ? __builtin_fmaf(0.5f, x, p) : __builtin_fmaxf(x, 0.0f);
+        return gelu_poly_value(x);
     } else if constexpr (ACT == ACT_GELU_TAYLOR6) {
         // GDPA page, code figure of the ALU-only Taylor GELU: x/2 + x^2/sqrt(2 pi)
         // - x^4/(6 sqrt(2 pi)) + x^6/(40 sqrt(2 pi)).
@@ -146,17 +152,14 @@ __device__ __forceinline__ void act_fwd_grad(float x, float& f, float& g) {
         f = x * s;
         g = s * __builtin_fmaf(x, 1.0f - s, 1.0f);
     } else if constexpr (ACT == ACT_GELU_POLY) {
+        // two chains with coefficients of their own; a caller that drops f
+        // (the dQ kernel) evaluates only the derivative's
+        f = gelu_poly_value(x);
         const float u = x * x;
-        float p = kGeluPolyCoef[GDPA_GELU_POLY_DEGREE];
-        float dp = GDPA_GELU_POLY_DEGREE * kGeluPolyCoef[GDPA_GELU_POLY_DEGREE];
+        float q = kGeluPolyGradCoef[GDPA_GELU_POLY_GRAD_DEGREE];
 #pragma unroll
-        for (int k = GDPA_GELU_POLY_DEGREE - 1; k >= 0; --k) {
-            p = __builtin_fmaf(p, u, kGeluPolyCoef[k]);
-            if (k >= 1) dp = __builtin_fmaf(dp, u, (float)k * kGeluPolyCoef[k]);
-        }
-        const bool in = __builtin_fabsf(x) <= GDPA_GELU_POLY_R;
-        f = in ? __builtin_fmaf(0.5f, x, p) : __builtin_fmaxf(x, 0.0f);
-        g = in ? __builtin_fmaf(2.0f * x, dp, 0.5f) : (x > 0.0f ? 1.0f : 0.0f);
+        for (int k = GDPA_GELU_POLY_GRAD_DEGREE - 1; k >= 0; --k) q = __builtin_fmaf(q, u, kGeluPolyGradCoef[k]);
+        g = __builtin_fabsf(x) <= GDPA_GELU_POLY_R ? __builtin_fmaf(x, q, 0.5f) : (x > 0.0f ? 1.0f : 0.0f);
     } else if constexpr (ACT == ACT_GELU_TAYLOR6) {
         const float u = x * x;
         const float c2 = 0.3989422804014327f, c4 = -0.0664903800669055f, c6 = 0.0099735570100358f;

@@ -33,7 +33,45 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_poly_bound():
     for code, name in G.STATUS.items():
         assert G.gdpa_status_string(code) == name
-    assert 0 < G.gdpa_gelu_poly_bound() < 1e-4
+    assert 0 < G.gdpa_gelu_poly_bound() < 2e-4
+    assert 0 < G.gdpa_gelu_poly_grad_bound() < 2 ** -10
+
+
+def _poly_header():
+    text = open(os.path.join(ROOT, "recsys_attention_jagged_amd", "csrc", "gelu_poly.h")).read()
+    num = r"([-+0-9.eE]+)f?"
+    radius = float(re.search(r"#define GDPA_GELU_POLY_R " + num, text).group(1))
+    tables = {}
+    for name in ("kGeluPolyCoef", "kGeluPolyGradCoef"):
+        body = re.search(name + r"\[[^]]*\] = \{(.*?)\};", text, flags=re.S).group(1)
+        tables[name] = np.array([float(t.strip().rstrip("f")) for t in body.split(",") if t.strip()])
+    return radius, tables["kGeluPolyCoef"], tables["kGeluPolyGradCoef"]
+
+
+def test_gelu_poly_tables_meet_the_library_bounds():
+    """The polynomial GELU's coefficient tables, evaluated here in the device's fp32
+    Horner order, against the oracle's exact GELU and GELU' on a dense grid that runs
+    past the clamp: the errors stay within the bounds the library reports."""
+    from oracle import gdpa_ref as R
+    radius, a, b = _poly_header()
+    x = np.linspace(-2 * radius, 2 * radius, 400_001).astype(np.float32)
+    u = x * x
+    p = np.zeros_like(u)
+    for c in a[::-1]:
+        p = (p * u + np.float32(c)).astype(np.float32)
+    q = np.zeros_like(u)
+    for c in b[::-1]:
+        q = (q * u + np.float32(c)).astype(np.float32)
+    inside = np.abs(x) <= np.float32(radius)
+    f = np.where(inside, np.float32(0.5) * x + p, np.maximum(x, np.float32(0))).astype(np.float64)
+    g = np.where(inside, x * q + np.float32(0.5), (x > 0).astype(np.float32)).astype(np.float64)
+    xd = x.astype(np.float64)
+    ef = np.abs(f - R.act_fwd(xd, "gelu")).max()
+    eg = np.abs(g - R.act_grad(xd, "gelu")).max()
+    assert ef <= G.gdpa_gelu_poly_bound() * (1 + 1e-6), ef
+    assert eg <= G.gdpa_gelu_poly_grad_bound() * (1 + 1e-6), eg
+    # and the bounds are tight: the grid comes within a few percent of them
+    assert ef >= 0.9 * G.gdpa_gelu_poly_bound() and eg >= 0.9 * G.gdpa_gelu_poly_grad_bound()
 
 
 def _host_plan(lq, lk, H, d, window, P=1024, team=(0, 0, 0), blocks=(0, 0, 0), deal="greedy", split=True):

@@ -6,8 +6,9 @@ Tolerances (stated with the task's definition of the path):
   * bf16 in / fp32 accumulate: relative L2 <= 1e-2 and max |err| <= 2e-2 * max |ref|,
     for O and separately for each of dQ, dK, dV.
   * the polynomial GELU against the exact-erf oracle: the bf16 bounds plus the
-    fit's bound propagated through the second product (eps * sum_j |V_j| per
-    element for O; eps' * sum |dP| |K| style terms for the gradients).
+    fits' bounds propagated through the products (eps * sum_j |V_j| per element
+    for O and eps * sum_i |dO_i| for dV; eps' * sum_j |dO_i|.|V_j| |K_j| / sqrt d
+    for dQ and its mirror for dK).
 Offset indexing is checked bit-exactly with count probes (act = one, fp32 outputs).
 """
 import math
@@ -773,19 +774,45 @@ def test_index_probe_bit_exact(window, d, team, nb):
 # the polynomial GELU against the exact-erf oracle
 # ---------------------------------------------------------------------------
 
+def poly_bounds(inp):
+    """Per-element bounds of what the polynomial's fit errors can move O, dQ, dK, dV
+    (eps on the value, eps' on the derivative), through the products:
+      |dO_i|  <= eps  sum_j |V_j|                      (O = sum_j P_ij V_j)
+      |ddV_j| <= eps  sum_i |dO_i|                     (dV = sum_i P_ij dO_i)
+      |ddQ_i| <= eps' sum_j (|dO_i|.|V_j|) |K_j| / sqrt d   (dS = dP act', |dP_ij| <= |dO_i|.|V_j|)
+      |ddK_j| <= eps' sum_i (|dO_i|.|V_j|) |Q_i| / sqrt d
+    each sum over the valid pairs: the oracle on absolute values with act = one
+    (P = 1) or identity (dS = dP) computes exactly these sums."""
+    ef, eg = G.gdpa_gelu_poly_bound(), G.gdpa_gelu_poly_grad_bound()
+    aq, ak, av, ado = (np.abs(inp.f64(n)) for n in ("q", "k", "v", "do"))
+    bo = R.gdpa_fwd(aq, ak, av, inp.q_off, inp.kv_off, "one", inp.window) * ef
+    bdv = R.gdpa_bwd(aq, ak, av, ado, inp.q_off, inp.kv_off, "one", inp.window)[2] * ef
+    bdq, bdk, _ = R.gdpa_bwd(aq, ak, av, ado, inp.q_off, inp.kv_off, "identity", inp.window)
+    return bo, (bdq * eg, bdk * eg, bdv)
+
+
 def test_gelu_poly_within_stated_bound():
-    say("poly GELU vs exact-erf oracle, windowed shapes")
+    say("poly GELU vs exact-erf oracle, windowed shapes, fwd + two-kernel bwd")
     L = [700, 1300, 129]
     inp = make_from_lengths(L, L, 2, 128, act="gelu", window=128, seed=11, device=DEV)
-    eps = G.gdpa_gelu_poly_bound()
-    o = run_fwd(inp, act="gelu_poly")
-    ref = oracle_fwd(inp, "gelu")
-    # |sum_j (P'_ij - P_ij) V_j| <= eps sum_j |V_j| over the valid keys of row i
-    absv = np.abs(inp.f64("v"))
-    bound = R.gdpa_fwd(inp.f64("q"), inp.f64("k"), absv, inp.q_off, inp.kv_off, "one", inp.window) * eps
-    check_close(o, ref, "O poly", extra=bound)
+    bo, bgrad = poly_bounds(inp)
+    check_close(run_fwd(inp, act="gelu_poly"), oracle_fwd(inp, "gelu"), "O poly", extra=bo)
+    for name, a, b, e in zip(("dQ", "dK", "dV"), run_bwd(inp, act="gelu_poly"), oracle_bwd(inp, "gelu"), bgrad):
+        check_close(a, b, f"{name} poly", extra=e)
     # taylor6 is the pages' series; against its own definition it must meet the bf16 bound
     check_close(run_fwd(inp, act="gelu_taylor6"), oracle_fwd(inp, "gelu_taylor6"), "O taylor6")
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_gelu_poly_one_pass_and_layouts(d):
+    say(f"poly GELU vs exact-erf oracle, one-pass backward kernels and the forward, d={d}")
+    for lq, lk in (([130, 7, 64], [32, 9, 30]), ([32, 9, 30], [130, 7, 64]), ([90, 3, 250], [60, 41, 250])):
+        inp = make_from_lengths(lq, lk, 2, d, act="gelu", seed=19, device=DEV)
+        bo, bgrad = poly_bounds(inp)
+        check_close(run_fwd(inp, act="gelu_poly"), oracle_fwd(inp, "gelu"), f"O poly d={d}", extra=bo)
+        for name, a, b, e in zip(("dQ", "dK", "dV"), run_bwd(inp, act="gelu_poly"), oracle_bwd(inp, "gelu"),
+                                 bgrad):
+            check_close(a, b, f"{name} poly d={d} lq={lq}", extra=e)
 
 
 # ---------------------------------------------------------------------------
