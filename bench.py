@@ -88,12 +88,13 @@ KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the kernel and planner sources (identifies the build the counters came from)."""
+    """sha256 over the kernel and planner sources and the build script, whose code
+    generation options differ per object (identifies the build the counters came from)."""
     import hashlib
     h = hashlib.sha256()
-    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "recsys_attention_jagged_amd", "csrc")
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(root, name), "rb") as f:
+    pkg = os.path.join(os.path.dirname(os.path.abspath(__file__)), "recsys_attention_jagged_amd")
+    for name in KERNEL_SOURCES + ("../build.py",):
+        with open(os.path.normpath(os.path.join(pkg, "csrc", name)), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 

@@ -32,6 +32,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
           "-Wno-unused-command-line-argument"]
 
+# marks a unit compiled without the VGPR form of MFMA results
+AGPR_ACC = "<agpr-acc>"
+
 # (output object, source, extra flags)
 UNITS = [("plan.o", "plan.cpp", []),
          ("api.o", "api.cpp", []),
@@ -41,13 +44,25 @@ UNITS = [("plan.o", "plan.cpp", []),
          ("norm.o", "norm.hip", [])]
 for _d in (32, 64, 128):
     UNITS.append((f"fwd_d{_d}.o", "fwd_bf16.hip", [f"-DGDPA_D={_d}"]))
-    UNITS.append((f"bwd_d{_d}.o", "bwd_bf16.hip", [f"-DGDPA_D={_d}"]))
     UNITS.append((f"fused_d{_d}.o", "bwd_fused.hip", [f"-DGDPA_D={_d}"]))
+    if _d < 128:
+        UNITS.append((f"bwd_d{_d}.o", "bwd_bf16.hip", [f"-DGDPA_D={_d}"]))
+# d = 128: the dQ and dK/dV kernels in objects of their own.  The dK/dV kernel
+# (K, V, dK and dV held per wave: more than the 256 VGPRs) keeps its MFMA
+# accumulators in AGPRs; with them in VGPRs the compiler parks K and V in AGPRs
+# instead, copies them back every step and waits on each operand read.
+UNITS.append(("bwd_dq_d128.o", "bwd_bf16.hip", ["-DGDPA_D=128", "-DGDPA_BWD_PART=1"]))
+UNITS.append(("bwd_kv_d128.o", "bwd_bf16.hip", ["-DGDPA_D=128", "-DGDPA_BWD_PART=2", AGPR_ACC]))
 
 
 def _compile(unit, verbose):
     obj, src, extra = unit
-    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", os.path.join(BUILD, obj)]
+    common = list(COMMON)
+    if AGPR_ACC in extra:
+        i = common.index("-amdgpu-mfma-vgpr-form")
+        del common[i - 1:i + 1]
+        extra = [e for e in extra if e != AGPR_ACC]
+    cmd = [HIPCC, *common, *extra, "-c", os.path.join(CSRC, src), "-o", os.path.join(BUILD, obj)]
     t0 = time.time()
     p = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature; that warning is harmless

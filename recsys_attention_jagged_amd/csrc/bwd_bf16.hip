@@ -49,6 +49,13 @@
 #ifndef GDPA_D
 #error "compile with -DGDPA_D=<32|64|128>"
 #endif
+// GDPA_BWD_PART selects what one object holds: 0 both kernels, 1 the dQ kernel,
+// 2 the dK/dV kernel, so that the two can be built with different code
+// generation options (the build keeps the dK/dV kernel's MFMA accumulators in
+// AGPRs at d = 128, the dQ kernel's in VGPRs)
+#ifndef GDPA_BWD_PART
+#define GDPA_BWD_PART 0
+#endif
 
 namespace gdpa {
 namespace {
@@ -633,6 +640,7 @@ const void* dkdv_act(int act) { GDPA_ACT_SWITCH(dkdv_ptr, T, 1) }
 #define GDPA_CAT2(a, b) a##b
 #define GDPA_CAT(a, b) GDPA_CAT2(a, b)
 
+#if GDPA_BWD_PART != 2
 const void* GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
     if (act == ACT_SOFTMAX) {   // one-wave teams (the side buffers of the ring)
         if (team == 1 && nb == 1) return dq_ptr<1, 1, ACT_SOFTMAX>();
@@ -647,6 +655,9 @@ const void* GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
     return nullptr;
 }
 
+#endif
+
+#if GDPA_BWD_PART != 1
 const void* GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
     if (nb != 1) return nullptr;
     if (act == ACT_SOFTMAX) return team == 1 ? dkdv_ptr<1, 1, ACT_SOFTMAX>() : nullptr;
@@ -656,6 +667,8 @@ const void* GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) 
 #endif
     return nullptr;
 }
+
+#endif
 
 static hipError_t launch(const void* f, const KernelArgs& a, int team, hipStream_t s) {
     if (!f) return hipErrorInvalidValue;
@@ -667,12 +680,16 @@ static hipError_t launch(const void* f, const KernelArgs& a, int team, hipStream
     return hipLaunchKernel(f, dim3(a.P), dim3(64 * team), params, 0, s);
 }
 
+#if GDPA_BWD_PART != 2
 hipError_t GDPA_CAT(launch_dq_bf16_d, GDPA_D)(const KernelArgs& a, int team, int nb, int act, hipStream_t s) {
     return launch(GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(team, nb, act), a, team, s);
 }
+#endif
 
+#if GDPA_BWD_PART != 1
 hipError_t GDPA_CAT(launch_dkdv_bf16_d, GDPA_D)(const KernelArgs& a, int team, int nb, int act, hipStream_t s) {
     return launch(GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(team, nb, act), a, team, s);
 }
+#endif
 
 }  // namespace gdpa
