@@ -255,6 +255,13 @@ struct DqPol : Common {
 
     template <class RingT>
     __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
+        if (win > 0) {   // blocks with no pair in the band add nothing: a step none of whose blocks
+                         // has one is skipped (one uniform branch)
+            bool dead = true;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) dead = dead && band_none(qrow(c, b), s * 32, win);
+            if (dead) return;
+        }
         const char* kt = g.tile(job);
         const char* vt = g.tile(job + 1);
         bf16x8 kop[NKS], vop[NKS];

@@ -191,6 +191,13 @@ __device__ __forceinline__ bool in_band(int dd, int win) {
     return (uint32_t)(dd + win - 1) <= (uint32_t)(2 * win - 2);
 }
 
+// Does no pair of the 32 x 32 block (rows i0.., columns j0..) lie inside the band
+// |i - j| < win?  The block's differences j - i are the integers j0 - i0 - 31 ..
+// j0 - i0 + 31, so it misses the band iff that range lies at or beyond +-win.
+__device__ __forceinline__ bool band_none(int i0, int j0, int win) {
+    return j0 - (i0 + 31) >= win || i0 - (j0 + 31) >= win;
+}
+
 // Does every pair of the 32 x 32 block (rows i0.., columns j0..) lie inside the
 // band |i - j| < win?  (Sample lengths need no test: rows beyond a length are
 // zero-filled tiles, whose products and stores vanish.)
