@@ -79,6 +79,10 @@ struct FwdPol {
 
     // first q row of this wave's block b
     __device__ __forceinline__ int qrow(const Rec& c, int b) const { return c.t * ROWS + 32 * (wt * NB + b); }
+    __device__ __forceinline__ bool block_dead(const Rec& c, int b, int j0) const {
+        const int q0 = qrow(c, b);
+        return q0 >= c.lq || (win > 0 && band_none(q0, j0, win));
+    }
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
@@ -219,11 +223,12 @@ struct FwdPol {
 
     template <class RingT>
     __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
-        if (win > 0) {   // blocks with no pair in the band add nothing: a step none of whose blocks
-                         // has one is skipped (one uniform branch)
+        {   // a block past the sample's last query, or with no pair inside the window band,
+            // adds nothing: a step none of whose blocks adds anything is skipped (one
+            // uniform branch)
             bool dead = true;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) dead = dead && band_none(qrow(c, b), s * 32, win);
+            for (int b = 0; b < NB; ++b) dead = dead && block_dead(c, b, s * 32);
             if (dead) return;
         }
         const char* kt = g.tile(job);
@@ -352,12 +357,14 @@ struct FwdPol {
         if (a.out_f32) {
             const rsrc_t ro = slice_rsrc((const float*)a.o + ob, c.lq, rso, D * 4);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) store_block_f32<NDB>(acc[b], mul[b], ro, (uint32_t)(qrow(c, b) + r) * rso, hh);
+            for (int b = 0; b < NB; ++b)
+                if (qrow(c, b) < c.lq) store_block_f32<NDB>(acc[b], mul[b], ro, (uint32_t)(qrow(c, b) + r) * rso, hh);
             return;
         }
         const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, c.lq, rso, D * 2);
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+            if (qrow(c, b) >= c.lq) continue;   // a block past the sample's last query has no rows
             char* st = g.tile(job - 2 + (T > 1 ? wt : (b & 1)));
             stage_block<D>(acc[b], mul[b], st, r, hh);
             store_tile<D>(st, ro, (uint32_t)qrow(c, b) * rso, rso, lane);
