@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import recsys_attention_jagged_amd as G
-from gdpa_workloads import WORKLOADS, make_from_lengths, make_workload, offsets
+from gdpa_workloads import WORKLOADS, make_from_lengths, make_pffn, make_workload, offsets
 from oracle import gdpa_ref as R
 from oracle import plan_ref as PR
 
@@ -651,6 +651,26 @@ def test_pffn(Tq, M, d, bins, act):
     check_close(o, R.pffn_fwd(q, wk, wv, act), f"pFFN O d={d}")
     for name, a, b in zip(("dQ", "dW_K", "dW_V"), (dq, dwk, dwv), R.pffn_bwd(q, wk, wv, do, act)):
         check_close(a, b, f"pFFN {name} d={d}")
+
+
+def test_full_size_pffn():
+    """The benchmark's pFFN batch (the jagged self-attention batch's 79,265 query rows against
+    M = 512 shared weight rows, H = 4, d = 128, SiLU) in its launch configuration: O and dQ
+    on sampled query rows (each depends only on its own row), and the weight gradients, sums
+    over every query row, in full."""
+    say("pFFN full size: 79,265 query rows x 512 weight rows, sampled O / dQ rows, full dW_K, dW_V")
+    inp = make_pffn(device=DEV)
+    st, (o, dq, dwk, dwv) = run_pffn(inp, inp.act)
+    assert st["n_parts"][1] > 0   # the weight gradients are reduced over chunks
+    q, wk, wv, do = (inp.f64(n) for n in ("q", "k", "v", "do"))
+    idx = np.sort(np.random.default_rng(5).choice(q.shape[0], 2000, replace=False))
+    for t, name in ((o, "O"), (dq, "dQ"), (dwk, "dW_K"), (dwv, "dW_V")):
+        assert np.all(np.isfinite(t)), f"pFFN {name}: non-finite values"
+    check_close(o[idx], R.pffn_fwd(q[idx], wk, wv, inp.act), "pFFN O sampled rows")
+    check_close(dq[idx], R.pffn_bwd(q[idx], wk, wv, do[idx], inp.act)[0], "pFFN dQ sampled rows")
+    _, dwk_ref, dwv_ref = R.pffn_bwd(q, wk, wv, do, inp.act)
+    check_close(dwk, dwk_ref, "pFFN dW_K full")
+    check_close(dwv, dwv_ref, "pFFN dW_V full")
 
 
 def test_pffn_rejects_a_jagged_plan():
