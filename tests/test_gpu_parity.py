@@ -803,11 +803,15 @@ def poly_bounds(inp):
       |ddK_j| <= eps' sum_i (|dO_i|.|V_j|) |Q_i| / sqrt d
     each sum over the valid pairs: the oracle on absolute values with act = one
     (P = 1) or identity (dS = dP) computes exactly these sums."""
+    return _poly_bounds(*(inp.f64(n) for n in ("q", "k", "v", "do")), inp.q_off, inp.kv_off, inp.window)
+
+
+def _poly_bounds(q, k, v, do, q_off, kv_off, window):
     ef, eg = G.gdpa_gelu_poly_bound(), G.gdpa_gelu_poly_grad_bound()
-    aq, ak, av, ado = (np.abs(inp.f64(n)) for n in ("q", "k", "v", "do"))
-    bo = R.gdpa_fwd(aq, ak, av, inp.q_off, inp.kv_off, "one", inp.window) * ef
-    bdv = R.gdpa_bwd(aq, ak, av, ado, inp.q_off, inp.kv_off, "one", inp.window)[2] * ef
-    bdq, bdk, _ = R.gdpa_bwd(aq, ak, av, ado, inp.q_off, inp.kv_off, "identity", inp.window)
+    aq, ak, av, ado = (np.abs(t) for t in (q, k, v, do))
+    bo = R.gdpa_fwd(aq, ak, av, q_off, kv_off, "one", window) * ef
+    bdv = R.gdpa_bwd(aq, ak, av, ado, q_off, kv_off, "one", window)[2] * ef
+    bdq, bdk, _ = R.gdpa_bwd(aq, ak, av, ado, q_off, kv_off, "identity", window)
     return bo, (bdq * eg, bdk * eg, bdv)
 
 
@@ -869,6 +873,35 @@ def test_full_size_sampled(cfg):
     # properties at any size: finite everywhere, zero rows where no partner exists
     for t in (o, dq, dk, dv):
         assert torch.isfinite(t.float()).all()
+
+
+def test_full_size_poly_windowed():
+    """The windowed batch at full size with the polynomial GELU, in the benchmark's launch
+    configuration (bench.py --config 5 --act gelu_poly): sampled samples against the
+    exact-erf oracle within the bf16 bounds plus the fit's bounds carried through the
+    products."""
+    say("windowed batch full size (B=128), polynomial GELU vs exact erf, sampled samples")
+    inp = make_workload(5, device=DEV)
+    qo, ko = dev_offsets(inp)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16") as plan:
+        o = plan.fwd(inp.q, inp.k, inp.v, qo, ko, "gelu_poly")
+        dq, dk, dv = plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "gelu_poly")
+        torch.cuda.synchronize()
+    for t in (o, dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    rng = np.random.default_rng(55)
+    picks = sorted(set(rng.choice(len(inp.lq), size=3, replace=False).tolist() + [int(np.argmax(inp.lq))]))
+    f = lambda t, a, e: t[a:e].to("cpu", torch.float64).numpy()
+    for b in picks:
+        qs, qe = int(inp.q_off[b]), int(inp.q_off[b + 1])
+        one = np.array([0, qe - qs])
+        q64, k64, v64, do64 = f(inp.q, qs, qe), f(inp.k, qs, qe), f(inp.v, qs, qe), f(inp.do, qs, qe)
+        bo, bgrad = _poly_bounds(q64, k64, v64, do64, one, one, inp.window)
+        check_close(f(o, qs, qe), R.gdpa_fwd(q64, k64, v64, one, one, "gelu", inp.window), f"poly O sample {b}",
+                    extra=bo)
+        refs = R.gdpa_bwd(q64, k64, v64, do64, one, one, "gelu", inp.window)
+        for name, got, ref, e in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs, bgrad):
+            check_close(f(got, qs, qe), ref, f"poly {name} sample {b}", extra=e)
 
 
 def test_determinism_with_cut_items():
