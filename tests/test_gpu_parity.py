@@ -715,6 +715,48 @@ def test_windows(window, lay):
         check_close(a, b, f"{name} w={window}")
 
 
+def _random_case(seed):
+    """A seeded random configuration: batch size, head count, head dimension, activation,
+    window and per-sample lengths drawn from a mix that stresses tile edges (0, 1, 31, 32, 33,
+    63, 64, 65), short and long samples, and self- or cross-shaped batches."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 9))
+    H = int(rng.choice([1, 2, 3]))
+    d = int(rng.choice([32, 64, 128]))
+    act = str(rng.choice(["gelu", "silu", "gelu_taylor6", "identity"]))
+    edge = np.array([0, 1, 31, 32, 33, 63, 64, 65])
+    def draw(n):
+        pick = rng.random(n)
+        return np.where(pick < 0.4, rng.choice(edge, n), np.where(pick < 0.8, rng.integers(1, 200, n),
+                                                                  rng.integers(200, 700, n)))
+    lq = draw(B)
+    window = int(rng.choice([0, 0, 0, 0, 0, 0, 1, 7, 40, 128]))
+    shape = rng.random()
+    if window or shape < 0.3:       # self-attention
+        lk = lq.copy()
+    elif shape < 0.55:              # every key side in one tile (the KV-stationary one-pass backward)
+        lk = rng.integers(1, 33, B)
+    elif shape < 0.8:               # every query side in one tile (the Q-stationary one-pass backward)
+        lk, lq = lq, rng.integers(1, 33, B)
+    else:
+        lk = draw(B)
+    return [int(x) for x in lq], [int(x) for x in lk], H, d, act, window
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configurations(seed):
+    lq, lk, H, d, act, window = _random_case(seed)
+    say(f"random case {seed}: lq={lq} lk={lk} H={H} d={d} act={act} window={window}")
+    inp = make_from_lengths(lq, lk, H, d, act=act, window=window, seed=seed, device=DEV)
+    ro, rg = oracle_fwd(inp), oracle_bwd(inp)
+    check_close(run_fwd(inp), ro, f"O random {seed}")
+    check_close(run_fwd(inp, dtype="bf16_f32out"), ro, f"O f32out random {seed}")
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp), rg):
+        check_close(a, b, f"{name} random {seed}")
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp, unfused=True), rg):
+        check_close(a, b, f"{name} unfused random {seed}")
+
+
 def test_empty_and_degenerate():
     say("empty samples, Lk=0, Lq=0, empty batch")
     lq = [0, 5, 0, 40, 3]
