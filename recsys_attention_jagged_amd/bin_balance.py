@@ -1,0 +1,114 @@
+"""Per-bin load balance of the GDPA kernels, measured with the clock-probe library.
+
+The GDPA page (aitrends.kr/articles/26275, "Section details", the figure of tile
+scheduling) compares the per-SM load of round-robin and sorted zigzag scheduling of
+jagged tiles (max:min 12:1 against 5:4).  Here every bin is one persistent
+workgroup; the clock-probe build stamps the real-time clock (100 MHz) at the start
+and the end of each bin's walk, so the busy time of every bin is measured directly.
+
+    python -m recsys_attention_jagged_amd.build --bin-clock      # on the build host
+    python -m recsys_attention_jagged_amd.bin_balance [--config 2] [--deals greedy zigzag round_robin]
+
+Prints one JSON line per (deal, kernel): busy time per bin with items (max, mean,
+min), max:min and max:mean, the kernel's span (last end - first start), and the
+planner's own max:min bin cost for the list.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--config", default="2", choices=["2", "3", "4", "5"])
+    ap.add_argument("--deals", nargs="+", default=["greedy", "zigzag", "round_robin"])
+    ap.add_argument("--reps", type=int, default=3, help="launches per kernel; the median one is reported")
+    ap.add_argument("--dump", default=None, metavar="FILE.npz",
+                    help="also save every bin's stamps with its list's exported items")
+    args = ap.parse_args(argv)
+
+    import numpy as np
+    import torch
+
+    import recsys_attention_jagged_amd as G
+    from recsys_attention_jagged_amd.build import LIB_BIN_CLOCK
+    from gdpa_workloads import WORKLOADS, make_workload
+
+    if not os.path.exists(LIB_BIN_CLOCK):
+        print(f"{LIB_BIN_CLOCK} is not built: python -m recsys_attention_jagged_amd.build --bin-clock",
+              file=sys.stderr)
+        return 2
+    G.LIB_PATH = LIB_BIN_CLOCK          # every call below goes to the clock-probe library
+    lib = G.load_library()
+    lib.gdpa_debug_bin_clock.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdpa_debug_bin_clock.restype = ctypes.c_int
+
+    cfg = int(args.config)
+    inp = make_workload(cfg, device="cuda")
+    qo = torch.tensor(inp.q_off, dtype=torch.int32, device="cuda")
+    ko = torch.tensor(inp.kv_off, dtype=torch.int32, device="cuda")
+    B, H, d, win, act = len(inp.lq), inp.H, inp.d, inp.window, inp.act
+    o = torch.empty_like(inp.q)
+    dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
+
+    def stamps(plan):
+        n = ctypes.c_size_t(1 << 16)
+        buf = (ctypes.c_ulonglong * n.value)()
+        st = lib.gdpa_debug_bin_clock(ctypes.c_void_p(plan.handle), buf, ctypes.byref(n))
+        if st != 0:
+            raise RuntimeError(G.gdpa_last_error())
+        return np.frombuffer(buf, dtype=np.uint64)[:n.value].reshape(-1, 2).astype(np.int64)
+
+    dump = {}
+    for deal in args.deals:
+        plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", deal=deal)
+        st = plan.stats()
+        h = plan.handle
+        kernels = [("fwd", 0, lambda: G.gdpa_fwd(h, inp.q, inp.k, inp.v, qo, ko, B, H, d, act, win, o))]
+        if st["bwd_fused"]:
+            lst = 1 if st["bwd_fused"] == 1 else 2
+            kernels.append(("bwd", lst, lambda: G.gdpa_bwd(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act,
+                                                           win, dq, dk, dv)))
+        else:
+            kernels.append(("dkdv", 1, lambda: G.gdpa_bwd_dkdv(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d,
+                                                               act, win, dk, dv)))
+            kernels.append(("dq", 2, lambda: G.gdpa_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act,
+                                                           win, dq)))
+        for name, lst, call in kernels:
+            runs = []
+            for _ in range(args.reps + 1):      # the first launch warms up
+                torch.cuda.synchronize()
+                stamps(plan)                    # clear what an earlier launch left
+                call()
+                torch.cuda.synchronize()
+                s = stamps(plan)
+                stamps_last = s.copy()
+                s = s[s[:, 1] > 0]              # bins with items
+                busy = (s[:, 1] - s[:, 0]) * 10 / 1e3   # us
+                span = (s[:, 1].max() - s[:, 0].min()) * 10 / 1e3
+                runs.append((span, busy))
+            span, busy = sorted(runs[1:], key=lambda r: r[0])[len(runs[1:]) // 2]
+            if args.dump:
+                dump[f"{deal}_{name}_stamps"] = stamps_last
+                dump[f"{deal}_{name}_export"] = np.asarray(G.gdpa_plan_export(h, lst))
+            print(json.dumps({
+                "workload": WORKLOADS[cfg]["name"], "deal": deal, "kernel": name, "bins": int(busy.size),
+                "busy_us": {"max": round(float(busy.max()), 1), "mean": round(float(busy.mean()), 1),
+                            "min": round(float(busy.min()), 1)},
+                "max_over_min": round(float(busy.max() / busy.min()), 3),
+                "max_over_mean": round(float(busy.max() / busy.mean()), 3),
+                "span_us": round(float(span), 1),
+                "planned_cost_max_over_min": round(st["bin_cost_max"][lst] / max(st["bin_cost_min"][lst], 1), 3),
+            }), flush=True)
+        plan.close()
+    if args.dump:
+        np.savez(args.dump, **dump)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

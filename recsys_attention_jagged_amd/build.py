@@ -55,14 +55,19 @@ UNITS.append(("bwd_dq_d128.o", "bwd_bf16.hip", ["-DGDPA_D=128", "-DGDPA_BWD_PART
 UNITS.append(("bwd_kv_d128.o", "bwd_bf16.hip", ["-DGDPA_D=128", "-DGDPA_BWD_PART=2", AGPR_ACC]))
 
 
-def _compile(unit, verbose):
+# the clock-probe library (GDPA_BIN_CLOCK): every kernel stamps the start and the end
+# of each bin's walk; a separate file and build folder, never loaded by default
+LIB_BIN_CLOCK = os.path.join(PKG, "libgdpa_binclock.so")
+
+
+def _compile(unit, verbose, build_dir=BUILD, defines=()):
     obj, src, extra = unit
-    common = list(COMMON)
+    common = list(COMMON) + list(defines)
     if AGPR_ACC in extra:
         i = common.index("-amdgpu-mfma-vgpr-form")
         del common[i - 1:i + 1]
         extra = [e for e in extra if e != AGPR_ACC]
-    cmd = [HIPCC, *common, *extra, "-c", os.path.join(CSRC, src), "-o", os.path.join(BUILD, obj)]
+    cmd = [HIPCC, *common, *extra, "-c", os.path.join(CSRC, src), "-o", os.path.join(build_dir, obj)]
     t0 = time.time()
     p = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature; that warning is harmless
@@ -77,32 +82,37 @@ def _compile(unit, verbose):
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
-    """Compile every unit and link the library; returns its path."""
+def build(jobs: int = 0, verbose: bool = False, bin_clock: bool = False) -> str:
+    """Compile every unit and link the library (bin_clock: the clock-probe library);
+    returns its path."""
     if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    build_dir, lib, defines = (BUILD + "_binclock", LIB_BIN_CLOCK, ["-DGDPA_BIN_CLOCK"]) if bin_clock else \
+        (BUILD, LIB, [])
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(len(UNITS), os.cpu_count() or 4, 16)
     t0 = time.time()
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda u: _compile(u, verbose), UNITS))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + [os.path.join(BUILD, o) for o in objs]
+        objs = list(ex.map(lambda u: _compile(u, verbose, build_dir, defines), UNITS))
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp] + [os.path.join(build_dir, o) for o in objs]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f}s", flush=True)
-    return LIB
+        print(f"built {lib} in {time.time() - t0:.1f}s", flush=True)
+    return lib
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--bin-clock", action="store_true",
+                    help="build the clock-probe library (libgdpa_binclock.so) instead")
     args = ap.parse_args(argv)
-    build(args.jobs, args.verbose)
+    build(args.jobs, args.verbose, args.bin_clock)
 
 
 if __name__ == "__main__":

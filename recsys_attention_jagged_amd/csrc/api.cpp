@@ -88,6 +88,10 @@ struct gdpa_plan_s {
     float* d_part[3] = {nullptr, nullptr, nullptr};
     // pFFN plans: device copies of the offsets {0, Tq} and {0, M}
     int32_t* d_off = nullptr;
+#ifdef GDPA_BIN_CLOCK
+    unsigned long long* d_clock = nullptr;   // [max P][2], shared by every launch of the plan
+    size_t n_clock = 0;
+#endif
     bool pffn = false;
 
     ~gdpa_plan_s() {
@@ -98,6 +102,9 @@ struct gdpa_plan_s {
             if (d_part[l]) (void)hipFree(d_part[l]);
         }
         if (d_off) (void)hipFree(d_off);
+#ifdef GDPA_BIN_CLOCK
+        if (d_clock) (void)hipFree(d_clock);
+#endif
     }
 };
 
@@ -263,10 +270,36 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
                                                 : fail_hip(e, "work list upload");
             }
         }
+#ifdef GDPA_BIN_CLOCK
+        p->n_clock = 2 * (size_t)std::max(p->lists[0].P, std::max(p->lists[1].P, p->lists[2].P));
+        hipError_t e = hipMalloc((void**)&p->d_clock, p->n_clock * sizeof(unsigned long long));
+        if (e == hipSuccess) e = hipMemset(p->d_clock, 0, p->n_clock * sizeof(unsigned long long));
+        if (e != hipSuccess) {
+            delete p;
+            return fail_hip(e, "clock buffer");
+        }
+#endif
     }
     *out = p;
     return GDPA_OK;
 }
+
+#ifdef GDPA_BIN_CLOCK
+// Clock-probe builds only: copy the (start, end) stamps the last launch on this plan
+// wrote per bin ([P][2], 100 MHz; 0 for bins without items) to `host` (n entries at
+// most; *n is set to the buffer's size), then clear them.  The caller synchronises the
+// stream first.
+extern "C" gdpa_status gdpa_debug_bin_clock(gdpa_plan plan, unsigned long long* host, size_t* n) {
+    g_err.clear();
+    if (!plan || !host || !n) return fail(GDPA_ERR_INVALID_ARG, "plan, host or n is NULL");
+    if (!plan->d_clock) return fail(GDPA_ERR_PLAN_MISMATCH, "host-only plan");
+    const size_t m = std::min(*n, plan->n_clock);
+    hipError_t e = hipMemcpy(host, plan->d_clock, m * sizeof(unsigned long long), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemset(plan->d_clock, 0, plan->n_clock * sizeof(unsigned long long));
+    *n = plan->n_clock;
+    return e == hipSuccess ? GDPA_OK : fail_hip(e, "clock readout");
+}
+#endif
 
 void gdpa_plan_destroy(gdpa_plan plan) { delete plan; }
 
@@ -344,6 +377,9 @@ static KernelArgs base_args(gdpa_plan plan, const int32_t* q_off_dev, const int3
     a.window = plan->window;
     a.scale = 1.0f / std::sqrt((float)plan->d);
     a.out_f32 = plan->dtype != GDPA_BF16;
+#ifdef GDPA_BIN_CLOCK
+    a.bin_clock = plan->d_clock;
+#endif
     return a;
 }
 

@@ -47,6 +47,11 @@ struct KernelArgs {
     const float* rkv;
     int Tk;
     int norm;
+#ifdef GDPA_BIN_CLOCK
+    // clock-probe builds only: per bin, the real-time stamps (100 MHz) of the start and
+    // the end of its walk, [P][2]
+    unsigned long long* bin_clock;
+#endif
 };
 
 // the activation code of the softmax (JFA) variant of the bf16 kernels (device

@@ -437,6 +437,9 @@ __device__ __forceinline__ void run_team(Pol& pol, int P, const Rec* __restrict_
     if (bin >= P) return;
     const int beg = bin_ptr[bin], end = bin_ptr[bin + 1];
     if (beg >= end) return;
+#ifdef GDPA_BIN_CLOCK
+    const unsigned long long clock0 = __builtin_amdgcn_s_memrealtime();
+#endif
 
     RingT ring;
     ring.init(slice, row_stride, wt, lane);
@@ -479,6 +482,12 @@ __device__ __forceinline__ void run_team(Pol& pol, int P, const Rec* __restrict_
         team_sync<T>();   // every wave is done with the last step's slots
         pol.item_end(c, ring, job);
     }
+#ifdef GDPA_BIN_CLOCK
+    if (pol.a.bin_clock && wt == 0 && lane == 0) {
+        pol.a.bin_clock[2 * bin] = clock0;
+        pol.a.bin_clock[2 * bin + 1] = __builtin_amdgcn_s_memrealtime();
+    }
+#endif
 }
 
 }  // namespace gdpa
