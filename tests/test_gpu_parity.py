@@ -107,6 +107,21 @@ def test_fp32_backward():
         check_close(a, b, f"fp32 {name}", f32=True)
 
 
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("act,window", [("gelu", 0), ("silu", 0), ("gelu_taylor6", 0), ("identity", 0),
+                                        ("gelu", 5), ("silu", 17)])
+def test_fp32_path(d, act, window):
+    """The fp32 path at every head dimension, the activations and windows, on ragged lengths
+    with empty samples on either side, forward and backward, to the fp32 bound."""
+    say(f"fp32 path d={d} act={act} window={window}")
+    lq = [0, 1, 31, 33, 70, 5, 0]
+    lk = lq if window else [4, 0, 40, 33, 9, 64, 0]
+    inp = make_from_lengths(lq, lk, 2, d, act=act, window=window, dtype="f32", seed=61, device=DEV)
+    check_close(run_fwd(inp), oracle_fwd(inp), f"fp32 O d={d} {act} w={window}", f32=True)
+    for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp), oracle_bwd(inp)):
+        check_close(a, b, f"fp32 {name} d={d} {act} w={window}", f32=True)
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_workload_forward_small(cfg):
     say(f"cfg{cfg} forward, B={SMALL_B[cfg]}")
