@@ -772,6 +772,19 @@ def test_random_configurations(seed):
         check_close(a, b, f"{name} unfused random {seed}")
 
 
+@pytest.mark.parametrize("H,d", [(12, 64), (16, 32), (16, 128)])
+def test_many_heads(H, d):
+    """Head counts beyond the workloads' (the [T, H, d] head stride in every descriptor and
+    store): forward and backward, self and cross shapes, against the oracle."""
+    say(f"H={H} d={d}")
+    for lq, lk, window in (([70, 0, 33, 129], [70, 0, 33, 129], 0), ([70, 1, 33, 5], [9, 40, 0, 64], 0),
+                           ([70, 3, 33, 129], [70, 3, 33, 129], 17)):
+        inp = make_from_lengths(lq, lk, H, d, act="gelu", window=window, seed=H + d, device=DEV)
+        check_close(run_fwd(inp), oracle_fwd(inp), f"O H={H} d={d} lq={lq}")
+        for name, a, b in zip(("dQ", "dK", "dV"), run_bwd(inp), oracle_bwd(inp)):
+            check_close(a, b, f"{name} H={H} d={d} lq={lq}")
+
+
 def test_empty_and_degenerate():
     say("empty samples, Lk=0, Lq=0, empty batch")
     lq = [0, 5, 0, 40, 3]
