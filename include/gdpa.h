@@ -25,13 +25,17 @@
  *
  * Ownership.  The caller owns every tensor and offset buffer and keeps them
  * alive until the stream work that uses them has finished.  A plan owns its
- * host and device work lists; gdpa_plan_destroy frees them.  A plan is
- * immutable after creation and may be used from several streams at once.
+ * host and device work lists; gdpa_plan_destroy frees them.  A plan's work lists
+ * are immutable after creation and any stream may run it, but calls on one plan
+ * must not overlap in time: items cut into chunks keep their partial outputs in
+ * the plan's slot buffer (see gdpa_plan_create).
  *
  * Asynchrony.  gdpa_fwd / gdpa_bwd validate their arguments on the host, then
  * only enqueue kernels on `stream` (NULL = the null stream); they never
  * synchronise.  A fault during execution shows up at the caller's next
- * synchronisation.
+ * synchronisation.  The launch path makes no allocation, memset or copy, so the
+ * calls can be captured into a HIP graph (except with GDPA_DEBUG=1, whose offset
+ * re-check copies the device offsets to the host).
  *
  * Errors.  Every call returns a gdpa_status; no call throws.  Arguments are
  * validated before anything is enqueued.  gdpa_last_error() returns a
