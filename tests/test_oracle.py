@@ -253,6 +253,58 @@ def test_backward_matches_torch_autograd_dense(act):
         np.testing.assert_allclose(dv[ko[b]:ko[b + 1]], V.grad.numpy(), rtol=1e-11, atol=1e-12)
 
 
+# Windowed samples longer than one group of query rows (the oracle evaluates
+# them in groups of 512 queries with the keys their windows reach, and adds the
+# groups' dK and dV contributions): checked against torch fp64 autograd on the
+# whole per-sample score matrix with a banded validity mask (no groups).
+ROW_GROUP_LENGTHS = [600, 1100, 0, 513, 7]
+
+
+def _banded_autograd(q, k, v, do, qo, ko, window, f=None):
+    """Per-sample (dQ, dK, dV) of sum(O * dO) through torch autograd, fp64, on the
+    dense scores of each sample with the mask |i - j| < window; f is the
+    activation, or None for softmax attention (scaled_dot_product_attention)."""
+    d = q.shape[2]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(qo) - 1):
+        qs, qe, ks, ke = qo[b], qo[b + 1], ko[b], ko[b + 1]
+        if qe == qs or ke == ks:
+            continue
+        t = lambda x: torch.tensor(x.transpose(1, 0, 2), requires_grad=True)   # [H, L, d]
+        Q, K, V = t(q[qs:qe]), t(k[ks:ke]), t(v[ks:ke])
+        i = torch.arange(qe - qs)[:, None]
+        j = torch.arange(ke - ks)[None, :]
+        m = (i - j).abs() < window
+        if f is None:
+            O = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=m[None])
+        else:
+            S = torch.matmul(Q, K.transpose(-1, -2).contiguous()) / d ** 0.5
+            O = torch.matmul(f(S) * m.double(), V)
+        (O * torch.tensor(do[qs:qe].transpose(1, 0, 2))).sum().backward()
+        dq[qs:qe] = Q.grad.numpy().transpose(1, 0, 2)
+        dk[ks:ke] = K.grad.numpy().transpose(1, 0, 2)
+        dv[ks:ke] = V.grad.numpy().transpose(1, 0, 2)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("act", ["gelu", "silu"])
+def test_windowed_backward_crossing_row_groups_equals_torch_autograd(act):
+    q, k, v, do, qo, ko = rand_case(ROW_GROUP_LENGTHS, ROW_GROUP_LENGTHS, H=2, d=2, seed=21)
+    got = R.gdpa_bwd(q, k, v, do, qo, ko, act, 5)
+    f = {"gelu": torch.nn.functional.gelu, "silu": torch.nn.functional.silu}[act]
+    want = _banded_autograd(q, k, v, do, qo, ko, 5, f)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-11, atol=1e-12)
+
+
+def test_jfa_windowed_backward_crossing_row_groups_equals_torch_autograd():
+    q, k, v, do, qo, ko = rand_case(ROW_GROUP_LENGTHS, ROW_GROUP_LENGTHS, H=2, d=2, seed=22)
+    got = R.jfa_bwd(q, k, v, do, qo, ko, 5)
+    want = _banded_autograd(q, k, v, do, qo, ko, 5, None)
+    for g, w in zip(got, want):
+        np.testing.assert_allclose(g, w, rtol=1e-10, atol=1e-12)
+
+
 def test_useful_pairs_counts_the_valid_set():
     for lq, lk, w in (([5, 0, 7], [3, 4, 7], 0), ([9, 1, 300], [9, 1, 300], 4)):
         brute = 0
@@ -287,6 +339,32 @@ def test_pins_catch_an_inclusive_window(monkeypatch):
     monkeypatch.setattr(R, "valid_mask", bad)
     with pytest.raises(AssertionError):
         test_forward_equals_scalar_loops("gelu", 3)
+
+
+def _mutated(fn, old, new):
+    """A copy of oracle function `fn` with the source text `old` replaced by `new`,
+    compiled in a copy of the oracle module's namespace."""
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(fn))
+    assert src.count(old) == 1, old
+    ns = dict(vars(R))
+    exec(compile(src.replace(old, new), R.__file__, "exec"), ns)
+    return ns[fn.__name__]
+
+
+@pytest.mark.parametrize("target", ["dk[ks + j0:ks + j1] +=", "dv[ks + j0:ks + j1] +="])
+def test_pins_catch_row_group_gradients_overwritten(monkeypatch, target):
+    """A windowed backward that stores each group's dK or dV contribution instead of
+    adding it (key rows near a group boundary receive two groups' terms) fails the
+    row-group pin, for GDPA and for JFA.  (Query rows belong to one group each.)"""
+    bad = target.replace("+=", "=")
+    monkeypatch.setattr(R, "gdpa_bwd", _mutated(R.gdpa_bwd, target, bad))
+    with pytest.raises(AssertionError):
+        test_windowed_backward_crossing_row_groups_equals_torch_autograd("gelu")
+    monkeypatch.setattr(R, "jfa_bwd", _mutated(R.jfa_bwd, target, bad))
+    with pytest.raises(AssertionError):
+        test_jfa_windowed_backward_crossing_row_groups_equals_torch_autograd()
 
 
 def test_pins_catch_a_missing_scale(monkeypatch):

@@ -10,6 +10,7 @@ import itertools
 import numpy as np
 import pytest
 
+from gdpa_workloads import WORKLOADS, workload_lengths
 from oracle import plan_ref as PR
 from oracle.gdpa_ref import valid_mask
 
@@ -225,3 +226,74 @@ def test_few_items_are_cut_to_quarter_bins():
     whole = PR.plan_list("dkdv", lq, lk, 2, 0, 16, 1, 1, split=False)
     assert max(whole["bin_cost"]) == 2 * 2056
     assert max(pl["bin_cost"]) <= 1.1 * sum(pl["bin_cost"]) / 16
+
+
+def _tile_pairs_of_sample(kind, lq, lk, window, t_stat, t_strm):
+    """Brute force for one sample, vectorised: the (t, s) tile pairs whose block of
+    the dense validity mask holds a valid (i, j)."""
+    m = valid_mask(np.arange(lq), np.arange(lk), lq, lk, window)
+    if kind == "dkdv":
+        m = m.T
+    a, c = m.shape
+    if a == 0 or c == 0:
+        return set()
+    nt, ns = -(-a // t_stat), -(-c // t_strm)
+    pad = np.zeros((nt * t_stat, ns * t_strm), dtype=bool)
+    pad[:a, :c] = m
+    hit = pad.reshape(nt, t_stat, ns, t_strm).any(axis=(1, 3))
+    return set(zip(*(x.tolist() for x in np.nonzero(hit))))
+
+
+# the five workloads at seed 0; the windowed batch's check of the tiles runs on a
+# subset of its samples (the shortest, the longest and six more), the rest in full
+@pytest.mark.parametrize("cfg", sorted(WORKLOADS))
+@pytest.mark.parametrize("kind", PR.LISTS)
+def test_workload_plans_at_automatic_layouts_cover_each_tile_once(cfg, kind):
+    """Each workload's plan at the layout auto_layout picks for it (a tuning rule: it
+    changes tile shapes and the deal, never which pairs are computed), over 1024
+    bins with items cut into chunks: every tile pair holding a valid (i, j) is
+    visited exactly once, every stationary tile of every (sample, head) has one
+    owner (a whole item or the chunks of one cut item, with consecutive steps and
+    consecutive slots numbered in (b, h, t) order), and no bin is left idle while
+    another holds more than one item."""
+    w = WORKLOADS[cfg]
+    lq, lk = workload_lengths(cfg, 0)
+    H, window = w["H"], w["window"]
+    team, nb = PR.auto_layout(lq, lk, window, w["d"])[kind]
+    pl = PR.plan_list(kind, lq, lk, H, window, 1024, team, nb)
+    t_stat, t_strm = pl["t_stat"], pl["t_strm"]
+    ls = lk if kind == "dkdv" else lq
+    B = len(lq)
+    if cfg == 5:
+        rng = np.random.default_rng(5)
+        check = {int(np.argmin(ls)), int(np.argmax(ls))} | set(rng.choice(B, 6, replace=False).tolist())
+    else:
+        check = set(range(B))
+    seen = {b: set() for b in check}
+    whole, chunks = set(), {}
+    for b, h, t, s0, s1, part in pl["items"]:
+        if b in check:
+            for s in range(s0, s1 + 1):
+                assert (h, t, s) not in seen[b]
+                seen[b].add((h, t, s))
+        if part < 0:
+            assert (b, h, t) not in whole and (b, h, t) not in chunks
+            whole.add((b, h, t))
+        else:
+            assert (b, h, t) not in whole and s1 >= s0
+            chunks.setdefault((b, h, t), []).append((s0, s1, part))
+    for b in check:
+        pairs = _tile_pairs_of_sample(kind, int(lq[b]), int(lk[b]), window, t_stat, t_strm)
+        assert seen[b] == {(h, t, s) for h in range(H) for t, s in pairs}, b
+    slots = []
+    for key in sorted(chunks):
+        cs = sorted(chunks[key])
+        assert len(cs) >= 2
+        assert all(cs[i][1] + 1 == cs[i + 1][0] for i in range(len(cs) - 1))
+        assert [c[2] for c in cs] == list(range(cs[0][2], cs[0][2] + len(cs)))
+        slots += [c[2] for c in cs]
+    assert slots == list(range(pl["n_parts"]))
+    assert whole | set(chunks) == {(b, h, t) for b in range(B) for h in range(H)
+                                   for t in range(-(-int(ls[b]) // t_stat))}
+    counts = np.diff(pl["bin_ptr"])
+    assert not (counts.min() == 0 and counts.max() > 1)
