@@ -2,12 +2,25 @@
 """Benchmark of jagged GDPA forward + backward (bf16 in, fp32 accumulate) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 2|3|4|5|pffn] [--act NAME] [--attn gdpa|softmax]
-                    [--norm] [--fp8]
+                    [--norm] [--fp8] [--no-per-config]
 
-A step is one forward pass plus one backward pass (dK/dV kernel, then dQ kernel)
-over the whole batch of the chosen workload, with inputs resident in HBM.  The
-default workload is the jagged self-attention batch (B = 1024 samples, lognormal
-lengths with median 64 and max 512, H = 4, d = 128, SiLU, no window).
+A step is one forward pass plus one backward pass (as gdpa_bwd runs it: the dK/dV
+kernel, then the dQ kernel, or one pass) over the whole batch of the chosen
+workload, with inputs resident in HBM.  The default workload is the largest
+single-GPU configuration, the windowed long-history self-attention batch (B = 128
+samples of uniform length 512..8192, local window |i - j| < 128, H = 4, d = 128,
+exact-erf GELU): 1.02 TFLOP of useful work and 6.4 GB of algorithmic traffic per
+step, far beyond the 256 MB last-level cache, so consecutive steps do not reuse
+each other's data.  Without --steps, K is chosen after the warm-up so that the
+timed region lasts at least 1.5 s.
+
+The default run also times every workload (the four bf16 batches and the tiny fp32
+one) direction by direction under "per_config": the median of 20 launches of the
+forward and of the backward, each launch preceded by a 512 MiB device fill that
+evicts the last-level cache, with time, useful TFLOP/s and % of the bf16 MFMA peak,
+useful GB/s (forward 2 H d (2 Tq + 2 Tk) bytes, backward 2 H d (3 Tq + 4 Tk)) and %
+of the HBM peak, and % of the attainable roofline min(MFMA peak, intensity x HBM
+peak).
 
 Prints one JSON line: `value` is useful TFLOP/s over fwd + bwd, counting only
 valid (query, key) pairs: 4 H d |V| for the forward and 10 H d |V| for the
@@ -51,6 +64,7 @@ METRIC_FP8 = "useful TFLOP/s, jagged GDPA fwd (fp8 Q, K) + bwd (bf16), 1 MI355X"
 METRIC_NORM = "useful TFLOP/s, jagged GDPA fwd+bwd with fused RMSNorm prologue, bf16, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector (the fp32 path runs no MFMA)
 
 
 def log(*a):
@@ -162,12 +176,69 @@ def cpu_baseline(inp, budget_s=15.0, softmax=False, norm=""):
                       f"forward+backward, {spent:.1f} s, same seeded inputs"}
 
 
+def direction_table(cfg: int, seed: int = 0, runs: int = 20, warm: int = 3):
+    """Per-direction figures of workload `cfg` (see the module docstring)."""
+    import statistics
+    import torch
+    import recsys_attention_jagged_amd as G
+    from gdpa_workloads import WORKLOADS, make_workload
+    w = WORKLOADS[cfg]
+    inp = make_workload(cfg, seed=seed, device="cuda")
+    qo = torch.tensor(inp.q_off, dtype=torch.int32, device="cuda")
+    ko = torch.tensor(inp.kv_off, dtype=torch.int32, device="cuda")
+    B, H, d, win, act = len(inp.lq), inp.H, inp.d, inp.window, inp.act
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    out_rows = {}
+    with G.Plan(inp.q_off, inp.kv_off, H, d, win, w["dtype"]) as plan:
+        st = plan.stats()
+        Tq, Tk, pairs = st["Tq"], st["Tk"], st["valid_pairs"]
+        o, dq, dk, dv = (torch.empty_like(t) for t in (inp.q, inp.q, inp.k, inp.v))
+        calls = {"fwd": lambda: G.gdpa_fwd(plan.handle, inp.q, inp.k, inp.v, qo, ko, B, H, d, act, win, o, sh),
+                 "bwd": lambda: G.gdpa_bwd(plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win,
+                                           dq, dk, dv, sh)}
+        e = 2 * H * d if w["dtype"] == "bf16" else 4 * H * d
+        alg_bytes = {"fwd": e * (2 * Tq + 2 * Tk), "bwd": e * (3 * Tq + 4 * Tk)}
+        flops = {"fwd": 4.0 * H * d * pairs, "bwd": 10.0 * H * d * pairs}
+        for direction in w["directions"]:
+            f = calls[direction]
+            times = []
+            for r in range(warm + runs):
+                scrub.fill_(r & 0xFF)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                f()
+                b.record(stream)
+                b.synchronize()
+                if r >= warm:
+                    times.append(a.elapsed_time(b))
+            ms = statistics.median(times)
+            tf = flops[direction] / (ms * 1e-3) / 1e12
+            gbs = alg_bytes[direction] / (ms * 1e-3) / 1e9
+            peak_tf = PEAK_BF16_TFLOPS if w["dtype"] == "bf16" else PEAK_FP32_VECTOR_TFLOPS
+            ai = flops[direction] / alg_bytes[direction]
+            attain = min(peak_tf, ai * PEAK_HBM_GBS / 1e3)
+            out_rows[direction] = {"ms": round(ms, 4), "useful_TFLOPs": round(tf, 2),
+                                   "pct_peak_compute": round(100 * tf / peak_tf, 2),
+                                   "useful_GBps": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                                   "attainable_TFLOPs": round(attain, 1),
+                                   "pct_attainable": round(100 * tf / attain, 2)}
+    del scrub
+    torch.cuda.empty_cache()
+    return {"workload": w["name"], "compute_peak": "bf16 MFMA" if w["dtype"] == "bf16" else "fp32 vector",
+            **out_rows}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="2", choices=["2", "3", "4", "5", "pffn"])
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: enough for at least 1.5 s of timed work)")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="5", choices=["2", "3", "4", "5", "pffn"])
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-workload, per-direction table")
     ap.add_argument("--act", default=None, help="override the workload's activation (e.g. gelu_poly)")
     ap.add_argument("--attn", default="gdpa", choices=["gdpa", "softmax"],
                     help="softmax: jagged softmax attention (JFA) on the same batch")
@@ -310,6 +381,15 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     K = args.steps
+    if K is None:   # enough steps for 1.5 s of timed work (at least 20)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(3):
+            for _, c in calls:
+                c()
+        b.record(stream)
+        torch.cuda.synchronize()
+        K = max(20, math.ceil(1500.0 / (a.elapsed_time(b) / 3)))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -396,6 +476,12 @@ def main(argv=None):
         out["norm"] = {"tensors": norm, "plain_kernels_ms": round(p0.elapsed_time(p1) / K, 4),
                        "fused_ms": round(ms_step, 4),
                        "unfused_norm_hbm_floor_ms": round(5 * 2 * H * d * rows / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
+    default_mode = not (sm or norm or args.fp8) and args.config != "pffn" and args.act is None
+    if default_mode and not args.no_per_config:
+        out["per_config"] = {}
+        for cfg in sorted(WORKLOADS):
+            log(f"per-direction timing of workload {cfg} ...")
+            out["per_config"][str(cfg)] = direction_table(cfg, args.seed)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, softmax=sm, norm=norm)

@@ -136,6 +136,9 @@ typedef struct gdpa_plan_s* gdpa_plan;
  *                             requires Lq_b == Lk_b for every b
  *   dtype                   : storage type the plan will be used with
  *   opts                    : NULL or planning options
+ *   stream                  : a hipStream_t (NULL = the null stream) on which the
+ *                             work lists are copied to the device; ignored for a
+ *                             host_only plan
  *   out                     : receives the plan (NULL on failure)
  *
  * Items of the Q-stationary lists (forward, dQ) whose cost exceeds the mean
@@ -145,15 +148,20 @@ typedef struct gdpa_plan_s* gdpa_plan;
  * adds the chunks of each cut item in a fixed order (no atomics).  Calls that use
  * one plan therefore must not overlap in time (e.g. on two streams).
  *
- * Unless opts->host_only, uploads the work lists and allocates the slot buffers
+ * Unless opts->host_only, allocates the device work lists and the slot buffers
  * (n_parts * tile_stat * w * 4 bytes per list, w = d + 2 for the forward list,
- * 2 d for dK/dV, d for dQ) with hipMalloc / hipMemcpy on
- * the current device (synchronous).  Errors: INVALID_ARG, BAD_OFFSETS,
- * UNSUPPORTED, HIP, NOMEM.
+ * 2 d for dK/dV, d for dQ) on the current device with hipMalloc, stages the
+ * lists in a pinned host buffer that the plan owns, and enqueues their copies on
+ * `stream` without waiting for them: the call never synchronises the device.
+ * Work that uses the plan must be ordered after those copies (enqueued on the
+ * same stream, or after an event or a synchronisation of it).  Planning itself
+ * runs on the host during the call (the GDPA page, "Section details": the tiles
+ * are precomputed on the CPU).  Errors: INVALID_ARG, BAD_OFFSETS, UNSUPPORTED,
+ * HIP, NOMEM.
  */
 gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_host, int B, int H,
                              int d, int window, gdpa_dtype dtype, const gdpa_plan_opts* opts,
-                             gdpa_plan* out);
+                             void* stream, gdpa_plan* out);
 
 /*
  * gdpa_fwd - O = act(Q K^T / sqrt(d)) V over the valid pairs (see top).
@@ -237,8 +245,10 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
  *            row) the pair (LSE_i log2(e), D_i).
  * Enqueues the Q-stationary dQ kernel, which also forms D from O and dO and writes
  * stat, then the KV-stationary dK/dV kernel, which reads stat (never the one-pass
- * kernels), plus the chunk reductions of cut items.  The plan must be bf16 with
- * one-wave dQ and dK/dV teams (the automatic layouts; UNSUPPORTED otherwise).
+ * kernels), plus the chunk reductions of cut items.  The plan must be GDPA_BF16
+ * (O is read as bf16; a GDPA_BF16_F32OUT plan, whose gdpa_jfa_fwd writes fp32 O,
+ * and an F32 plan are rejected with UNSUPPORTED) with one-wave dQ and dK/dV teams
+ * (the automatic layouts; UNSUPPORTED otherwise).
  * Errors as gdpa_bwd.  gdpa_jfa_bwd == gdpa_jfa_bwd_dq, then gdpa_jfa_bwd_dkdv.
  */
 gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
@@ -330,15 +340,15 @@ gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const v
  * planner's chunks spread the weight-gradient reduction over the device.
  *
  * gdpa_pffn_plan_create - a plan for Tq >= 0 query rows and M >= 0 weight rows
- *   (H, d, dtype, opts as for gdpa_plan_create).  Also keeps device copies of the
- *   offsets, so the pFFN calls take none.  Errors as gdpa_plan_create.
+ *   (H, d, dtype, opts, stream as for gdpa_plan_create).  Also keeps device copies
+ *   of the offsets, so the pFFN calls take none.  Errors as gdpa_plan_create.
  * gdpa_pffn_fwd - O [Tq, H, d] from q [Tq, H, d], wk, wv [M, H, d]; act as gdpa_fwd.
  * gdpa_pffn_bwd - dQ [Tq, H, d], dW_K and dW_V [M, H, d] for the loss sum(O * dO).
  *   Both: device pointers in the plan's dtype; errors as gdpa_fwd / gdpa_bwd, and
  *   PLAN_MISMATCH for a plan not made by gdpa_pffn_plan_create.
  */
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,
-                                  gdpa_plan* out);
+                                  void* stream, gdpa_plan* out);
 gdpa_status gdpa_pffn_fwd(gdpa_plan plan, const void* q, const void* wk, const void* wv, gdpa_act act, void* o,
                           void* stream);
 gdpa_status gdpa_pffn_bwd(gdpa_plan plan, const void* q, const void* wk, const void* wv, const void* dout,

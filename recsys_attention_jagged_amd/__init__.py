@@ -64,7 +64,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run: python -m recsys_attention_jagged_amd.build")
     lib = ctypes.CDLL(path)
-    lib.gdpa_plan_create.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts),
+    lib.gdpa_plan_create.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts), _vp,
                                      ctypes.POINTER(_vp)]
     lib.gdpa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
     lib.gdpa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
@@ -97,7 +97,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_jfa_bwd_stat.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _vp, _vp]
     lib.gdpa_jfa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
     lib.gdpa_jfa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]
-    lib.gdpa_pffn_plan_create.argtypes = [_i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts), ctypes.POINTER(_vp)]
+    lib.gdpa_pffn_plan_create.argtypes = [_i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts), _vp,
+                                          ctypes.POINTER(_vp)]
     lib.gdpa_pffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
     lib.gdpa_pffn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp]
     for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
@@ -147,8 +148,10 @@ def _enum(v, table):
 
 def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: int, dtype,
                      host_only: bool = False, bins=(0, 0, 0), team=(0, 0, 0), blocks=(0, 0, 0),
-                     deal="greedy", split: bool = True, unfused: bool = False) -> int:
-    """Returns an opaque plan handle (int).  Offsets: host int32 [B + 1]."""
+                     deal="greedy", split: bool = True, unfused: bool = False, stream=None) -> int:
+    """Returns an opaque plan handle (int).  Offsets: host int32 [B + 1].  The work
+    lists are copied on `stream` (torch's current stream by default; none for a
+    host-only plan)."""
     qo = np.ascontiguousarray(q_off_host, dtype=np.int32)
     ko = np.ascontiguousarray(kv_off_host, dtype=np.int32)
     if qo.shape != (B + 1,) or ko.shape != (B + 1,):
@@ -156,7 +159,8 @@ def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: in
     opts = _opts(host_only, bins, team, blocks, deal, split, unfused)
     out = _vp()
     _check(load_library().gdpa_plan_create(qo.ctypes.data, ko.ctypes.data, B, H, d, window,
-                                           _enum(dtype, DTYPE), ctypes.byref(opts), ctypes.byref(out)))
+                                           _enum(dtype, DTYPE), ctypes.byref(opts),
+                                           None if host_only else _stream(stream), ctypes.byref(out)))
     return out.value
 
 
@@ -275,12 +279,12 @@ def _opts(host_only, bins, team, blocks, deal, split, unfused):
 
 def gdpa_pffn_plan_create(Tq: int, M: int, H: int, d: int, dtype, host_only: bool = False, bins=(0, 0, 0),
                           team=(0, 0, 0), blocks=(0, 0, 0), deal="greedy", split: bool = True,
-                          unfused: bool = False) -> int:
+                          unfused: bool = False, stream=None) -> int:
     """Plan of pFFN over Tq query rows and M shared weight rows (opaque handle)."""
     opts = _opts(host_only, bins, team, blocks, deal, split, unfused)
     out = _vp()
     _check(load_library().gdpa_pffn_plan_create(Tq, M, H, d, _enum(dtype, DTYPE), ctypes.byref(opts),
-                                                ctypes.byref(out)))
+                                                None if host_only else _stream(stream), ctypes.byref(out)))
     return out.value
 
 
@@ -375,20 +379,63 @@ class Plan:
         import torch
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
 
+    def _in_dtype(self):
+        import torch
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def _check_tensor(self, name, t, rows, dtype, device=None):
+        """Refuse, before any launch, a tensor the kernels would misread: not a
+        contiguous [rows, H, d] tensor of `dtype` on a GPU (or on `device`)."""
+        if t is None or not hasattr(t, "data_ptr"):
+            raise TypeError(f"{name} must be a torch tensor")
+        if tuple(t.shape) != (rows, self.H, self.d):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, the plan needs {(rows, self.H, self.d)}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} is {t.dtype}, the plan needs {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device.type != "cuda" or (device is not None and t.device != device):
+            raise ValueError(f"{name} is on {t.device}, not on the inputs' GPU")
+
+    def _check_offsets(self, q_off_dev, kv_off_dev, device):
+        import torch
+        for name, t in (("q_off_dev", q_off_dev), ("kv_off_dev", kv_off_dev)):
+            if hasattr(t, "data_ptr"):
+                if t.dtype != torch.int32 or tuple(t.shape) != (self.B + 1,) or not t.is_contiguous() \
+                        or t.device != device:
+                    raise ValueError(f"{name} must be a contiguous int32 [B + 1] tensor on {device}")
+
     def fwd(self, q, k, v, q_off_dev, kv_off_dev, act, o=None, stream=None):
         import torch
+        Tq, Tk = int(self.q_off[-1]), int(self.kv_off[-1])
+        self._check_tensor("q", q, Tq, self._in_dtype())
+        dev = q.device
+        self._check_tensor("k", k, Tk, self._in_dtype(), dev)
+        self._check_tensor("v", v, Tk, self._in_dtype(), dev)
+        self._check_offsets(q_off_dev, kv_off_dev, dev)
         if o is None:
-            o = torch.empty(q.shape, dtype=self._out_dtype(), device=q.device)
+            o = torch.empty(q.shape, dtype=self._out_dtype(), device=dev)
+        self._check_tensor("o", o, Tq, self._out_dtype(), dev)
         gdpa_fwd(self.handle, q, k, v, q_off_dev, kv_off_dev, self.B, self.H, self.d, act, self.window, o,
                  stream)
         return o
 
     def bwd(self, q, k, v, dout, q_off_dev, kv_off_dev, act, dq=None, dk=None, dv=None, stream=None):
         import torch
-        dt = self._out_dtype()
-        dq = torch.empty(q.shape, dtype=dt, device=q.device) if dq is None else dq
-        dk = torch.empty(k.shape, dtype=dt, device=k.device) if dk is None else dk
-        dv = torch.empty(v.shape, dtype=dt, device=v.device) if dv is None else dv
+        Tq, Tk = int(self.q_off[-1]), int(self.kv_off[-1])
+        dt, it = self._out_dtype(), self._in_dtype()
+        self._check_tensor("q", q, Tq, it)
+        dev = q.device
+        self._check_tensor("k", k, Tk, it, dev)
+        self._check_tensor("v", v, Tk, it, dev)
+        self._check_tensor("dout", dout, Tq, it, dev)
+        self._check_offsets(q_off_dev, kv_off_dev, dev)
+        dq = torch.empty(q.shape, dtype=dt, device=dev) if dq is None else dq
+        dk = torch.empty(k.shape, dtype=dt, device=dev) if dk is None else dk
+        dv = torch.empty(v.shape, dtype=dt, device=dev) if dv is None else dv
+        self._check_tensor("dq", dq, Tq, dt, dev)
+        self._check_tensor("dk", dk, Tk, dt, dev)
+        self._check_tensor("dv", dv, Tk, dt, dev)
         gdpa_bwd(self.handle, q, k, v, dout, q_off_dev, kv_off_dev, self.B, self.H, self.d, act,
                  self.window, dq, dk, dv, stream)
         return dq, dk, dv

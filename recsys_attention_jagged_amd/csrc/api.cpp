@@ -71,6 +71,12 @@ int64_t pairs_of(int64_t lq, int64_t lk, int64_t w) {
 
 }  // namespace
 
+struct gdpa_plan_s;
+static gdpa_status upload(gdpa_plan_s* p, hipStream_t s);
+static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_host, int B, int H, int d,
+                               int window, gdpa_dtype dtype, const gdpa_plan_opts* opts, hipStream_t stream,
+                               bool pffn, gdpa_plan_s** out);
+
 struct gdpa_plan_s {
     int B = 0, H = 0, d = 0, window = 0;
     gdpa_dtype dtype = GDPA_BF16;
@@ -88,6 +94,10 @@ struct gdpa_plan_s {
     float* d_part[3] = {nullptr, nullptr, nullptr};
     // pFFN plans: device copies of the offsets {0, Tq} and {0, M}
     int32_t* d_off = nullptr;
+    // pinned host copy of everything uploaded at creation (records, bin pointers,
+    // chunk groups, pFFN offsets): the copies are enqueued on the creation stream
+    // and read from here, so it lives as long as the plan
+    char* h_stage = nullptr;
 #ifdef GDPA_BIN_CLOCK
     unsigned long long* d_clock = nullptr;   // [max P][2], shared by every launch of the plan
     size_t n_clock = 0;
@@ -102,11 +112,63 @@ struct gdpa_plan_s {
             if (d_part[l]) (void)hipFree(d_part[l]);
         }
         if (d_off) (void)hipFree(d_off);
+        if (h_stage) (void)hipHostFree(h_stage);
 #ifdef GDPA_BIN_CLOCK
         if (d_clock) (void)hipFree(d_clock);
 #endif
     }
 };
+
+// Device work lists of a plan: allocate them (and the chunk slot buffers), stage
+// the records, bin pointers and chunk groups in one pinned host buffer owned by
+// the plan, and enqueue the copies on `s` (no synchronisation).
+static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
+    std::vector<DevRec> recs[3];
+    std::vector<DevGroup> groups[3];
+    size_t bytes = 0;
+    auto align = [](size_t n) { return (n + 255) & ~(size_t)255; };
+    for (int l = 0; l < 3; ++l) {
+        recs[l] = device_records(p->lists[l], p->q_off, p->kv_off);
+        if (p->lists[l].n_parts > 0) groups[l] = device_groups(p->lists[l], p->q_off, p->kv_off);
+        bytes += align(recs[l].size() * sizeof(DevRec)) + align(p->lists[l].bin_ptr.size() * sizeof(int32_t)) +
+                 align(groups[l].size() * sizeof(DevGroup));
+    }
+    const int32_t off[4] = {0, (int32_t)p->Tq, 0, (int32_t)p->Tk};
+    if (p->pffn) bytes += align(sizeof(off));
+    hipError_t e = hipHostMalloc((void**)&p->h_stage, std::max<size_t>(bytes, 256), hipHostMallocDefault);
+    if (e != hipSuccess) {
+        p->h_stage = nullptr;
+        return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "pinned staging buffer")
+                                        : fail_hip(e, "pinned staging buffer");
+    }
+    char* h = p->h_stage;
+    // copy n bytes of src into the staging buffer and enqueue them to *dst (allocated here)
+    auto put = [&](void** dst, const void* src, size_t n) -> hipError_t {
+        hipError_t r = hipMalloc(dst, std::max<size_t>(n, 1));
+        if (r != hipSuccess || n == 0) return r;
+        std::memcpy(h, src, n);
+        r = hipMemcpyAsync(*dst, h, n, hipMemcpyHostToDevice, s);
+        h += align(n);
+        return r;
+    };
+    for (int l = 0; l < 3 && e == hipSuccess; ++l) {
+        const WorkList& wl = p->lists[l];
+        e = put((void**)&p->d_items[l], recs[l].data(), recs[l].size() * sizeof(DevRec));
+        if (e == hipSuccess) e = put((void**)&p->d_bin_ptr[l], wl.bin_ptr.data(), wl.bin_ptr.size() * sizeof(int32_t));
+        if (e == hipSuccess && wl.n_parts > 0) {
+            p->n_groups[l] = (int)groups[l].size();
+            e = put((void**)&p->d_groups[l], groups[l].data(), groups[l].size() * sizeof(DevGroup));
+            // dK and dV blocks; the forward list also keeps two floats per slot row
+            // (softmax chunks' row max and sum) after its blocks
+            const size_t per_row = l == LIST_DKDV ? 2 * (size_t)p->d : l == LIST_FWD ? (size_t)p->d + 2 : (size_t)p->d;
+            if (e == hipSuccess) e = hipMalloc((void**)&p->d_part[l], per_row * wl.n_parts * wl.t_stat * sizeof(float));
+        }
+    }
+    if (e == hipSuccess && p->pffn) e = put((void**)&p->d_off, off, sizeof(off));
+    if (e != hipSuccess)
+        return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "work list upload") : fail_hip(e, "work list upload");
+    return GDPA_OK;
+}
 
 extern "C" {
 
@@ -129,9 +191,18 @@ double gdpa_gelu_poly_bound(void) { return GDPA_GELU_POLY_BOUND; }
 double gdpa_gelu_poly_grad_bound(void) { return GDPA_GELU_POLY_GRAD_BOUND; }
 
 gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_host, int B, int H,
-                             int d, int window, gdpa_dtype dtype, const gdpa_plan_opts* opts,
+                             int d, int window, gdpa_dtype dtype, const gdpa_plan_opts* opts, void* stream,
                              gdpa_plan* out) {
     g_err.clear();
+    return plan_create(q_off_host, kv_off_host, B, H, d, window, dtype, opts, (hipStream_t)stream, false, out);
+}
+
+}  // extern "C"
+
+// gdpa_plan_create, and for pFFN plans (pffn) also device copies {0, Tq, 0, M} of the offsets
+static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_host, int B, int H, int d,
+                               int window, gdpa_dtype dtype, const gdpa_plan_opts* opts, hipStream_t stream,
+                               bool pffn, gdpa_plan* out) {
     if (!out) return fail(GDPA_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (!q_off_host || !kv_off_host) return fail(GDPA_ERR_INVALID_ARG, "offsets are NULL");
@@ -174,6 +245,7 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
     p->window = window;
     p->dtype = dtype;
     p->host_only = o.host_only != 0;
+    p->pffn = pffn;
     p->q_off.assign(q_off_host, q_off_host + B + 1);
     p->kv_off.assign(kv_off_host, kv_off_host + B + 1);
     p->lq = lq;
@@ -241,34 +313,10 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
     }
 
     if (!p->host_only) {
-        for (int l = 0; l < 3; ++l) {
-            const WorkList& wl = p->lists[l];
-            const std::vector<DevRec> recs = device_records(wl, p->q_off, p->kv_off);
-            const size_t ni = std::max<size_t>(1, recs.size());
-            hipError_t e = hipMalloc((void**)&p->d_items[l], ni * sizeof(DevRec));
-            if (e == hipSuccess) e = hipMalloc((void**)&p->d_bin_ptr[l], wl.bin_ptr.size() * sizeof(int32_t));
-            if (e == hipSuccess && !recs.empty())
-                e = hipMemcpy(p->d_items[l], recs.data(), recs.size() * sizeof(DevRec), hipMemcpyHostToDevice);
-            if (e == hipSuccess)
-                e = hipMemcpy(p->d_bin_ptr[l], wl.bin_ptr.data(), wl.bin_ptr.size() * sizeof(int32_t),
-                              hipMemcpyHostToDevice);
-            if (e == hipSuccess && wl.n_parts > 0) {
-                const std::vector<DevGroup> g = device_groups(wl, p->q_off, p->kv_off);
-                p->n_groups[l] = (int)g.size();
-                e = hipMalloc((void**)&p->d_groups[l], g.size() * sizeof(DevGroup));
-                if (e == hipSuccess)
-                    e = hipMemcpy(p->d_groups[l], g.data(), g.size() * sizeof(DevGroup), hipMemcpyHostToDevice);
-                // dK and dV blocks; the forward list also keeps two floats per slot row
-                // (softmax chunks' row max and sum) after its blocks
-                const size_t per_row = l == LIST_DKDV ? 2 * (size_t)d : l == LIST_FWD ? (size_t)d + 2 : (size_t)d;
-                if (e == hipSuccess)
-                    e = hipMalloc((void**)&p->d_part[l], per_row * wl.n_parts * wl.t_stat * sizeof(float));
-            }
-            if (e != hipSuccess) {
-                delete p;
-                return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "work list upload")
-                                                : fail_hip(e, "work list upload");
-            }
+        const gdpa_status st = upload(p, stream);
+        if (st != GDPA_OK) {
+            delete p;
+            return st;
         }
 #ifdef GDPA_BIN_CLOCK
         p->n_clock = 2 * (size_t)std::max(p->lists[0].P, std::max(p->lists[1].P, p->lists[2].P));
@@ -283,6 +331,8 @@ gdpa_status gdpa_plan_create(const int32_t* q_off_host, const int32_t* kv_off_ho
     *out = p;
     return GDPA_OK;
 }
+
+extern "C" {
 
 #ifdef GDPA_BIN_CLOCK
 // Clock-probe builds only: copy the (start, end) stamps the last launch on this plan
@@ -575,7 +625,8 @@ static gdpa_status jfa_stat(gdpa_plan plan, const void* o, const float* lse, con
 }
 
 static gdpa_status jfa_check(gdpa_plan plan) {
-    if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "JFA runs on bf16 plans");
+    // the backward reads the forward's O as bf16: a BF16_F32OUT plan's forward writes fp32
+    if (plan->dtype != GDPA_BF16) return fail(GDPA_ERR_UNSUPPORTED, "the JFA backward runs on GDPA_BF16 plans");
     if (plan->lists[LIST_DQ].team != 1 || plan->lists[LIST_DKDV].team != 1)
         return fail(GDPA_ERR_UNSUPPORTED, "the JFA backward runs one-wave dQ and dK/dV teams");
     return GDPA_OK;
@@ -870,27 +921,13 @@ gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const v
 }
 
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,
-                                  gdpa_plan* out) {
+                                  void* stream, gdpa_plan* out) {
     g_err.clear();
     if (!out) return fail(GDPA_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (Tq < 0 || M < 0) return fail(GDPA_ERR_INVALID_ARG, "Tq and M must be >= 0");
     const int32_t q_off[2] = {0, Tq}, kv_off[2] = {0, M};
-    gdpa_plan p = nullptr;
-    gdpa_status st = gdpa_plan_create(q_off, kv_off, 1, H, d, 0, dtype, opts, &p);
-    if (st != GDPA_OK) return st;
-    p->pffn = true;
-    if (!p->host_only) {
-        const int32_t off[4] = {0, Tq, 0, M};
-        hipError_t e = hipMalloc((void**)&p->d_off, sizeof(off));
-        if (e == hipSuccess) e = hipMemcpy(p->d_off, off, sizeof(off), hipMemcpyHostToDevice);
-        if (e != hipSuccess) {
-            delete p;
-            return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "offset upload") : fail_hip(e, "offset upload");
-        }
-    }
-    *out = p;
-    return GDPA_OK;
+    return plan_create(q_off, kv_off, 1, H, d, 0, dtype, opts, (hipStream_t)stream, true, out);
 }
 
 static gdpa_status check_pffn(gdpa_plan plan) {

@@ -122,15 +122,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
-                 : "s"(lds), "v"(voff), "s"(rs));
+                 : "s"(lds), "v"(voff), "s"(rs)
+                 : "m0");
 }
 
 // One wave instruction: lane l's 4 bytes at byte offset `voff` land at LDS
-// address lds + 4 l (256 bytes per instruction).
+// address lds + 4 l (256 bytes per instruction).  Both set m0 (the LDS base of
+// the copy) and declare it clobbered.
 __device__ __forceinline__ void dma4(rsrc_t rs, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :
-                 : "s"(lds), "v"(voff), "s"(rs));
+                 : "s"(lds), "v"(voff), "s"(rs)
+                 : "m0");
 }
 
 // s_waitcnt vmcnt(J m) for a uniform m in [0, MMAX] (the count is an immediate)

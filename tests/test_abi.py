@@ -204,8 +204,8 @@ def test_create_rejects_bad_arguments():
     assert bad(ko=offsets([3, 5]), window=4) == 2               # window with Lq != Lk
     lib = G.load_library()
     out = ctypes.c_void_p()
-    assert lib.gdpa_plan_create(None, None, 1, 1, 64, 0, 1, None, ctypes.byref(out)) == 1
-    assert lib.gdpa_plan_create(qo.ctypes.data, qo.ctypes.data, 2, 1, 64, 0, 1, None, None) == 1
+    assert lib.gdpa_plan_create(None, None, 1, 1, 64, 0, 1, None, None, ctypes.byref(out)) == 1
+    assert lib.gdpa_plan_create(qo.ctypes.data, qo.ctypes.data, 2, 1, 64, 0, 1, None, None, None) == 1
     assert "NULL" in G.gdpa_last_error()
 
 

@@ -561,8 +561,6 @@ def test_jfa_backward_layouts(d, nb):
     got = run_jfa_bwd(inp, team=(0, 1, 1), blocks=(0, 1, nb))
     check_jfa_stat(got, inp, f"d={d}")
     check_jfa_grads(got, inp, f"d={d} nb={nb}")
-    got32 = run_jfa_bwd(inp, dtype="bf16_f32out", team=(0, 1, 1), blocks=(0, 1, nb))
-    check_jfa_grads(got32, inp, f"f32out d={d} nb={nb}")
 
 
 @pytest.mark.parametrize("window", [1, 2, 17, 128])
@@ -631,6 +629,38 @@ def test_jfa_backward_rejects():
             with pytest.raises(G.GdpaError) as e:
                 G.gdpa_jfa_bwd(plan.handle, inp.q, inp.k, inp.v, inp.q, z, inp.do, qo, ko, 2, 2, 128, 0, z,
                                torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v))
+            assert G.STATUS[e.value.status] == "GDPA_ERR_UNSUPPORTED"
+
+
+def test_jfa_backward_rejects_fp32_output_plans():
+    """On a GDPA_BF16_F32OUT plan the JFA forward writes fp32 O, which the backward
+    (reading O as bf16) would misread: every JFA backward entry point refuses such a
+    plan before launching anything, after the forward on the same plan ran."""
+    say("JFA backward on an fp32-output plan")
+    inp = make_from_lengths([40, 3], [50, 7], 2, 128, act="gelu", seed=59, device=DEV)
+    qo, ko = dev_offsets(inp)
+    Tq = inp.q.shape[0]
+    with G.Plan(inp.q_off, inp.kv_off, 2, 128, 0, "bf16_f32out") as plan:
+        o = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
+        lse = torch.empty((2, Tq), dtype=torch.float32, device=DEV)
+        G.gdpa_jfa_fwd(plan.handle, inp.q, inp.k, inp.v, qo, ko, plan.B, 2, 128, 0, o, lse)
+        torch.cuda.synchronize()
+        ro, _ = R.jfa_fwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_off, inp.kv_off, 0)
+        check_close(o.cpu().numpy(), ro, "JFA O on the fp32-output plan")
+        stat = torch.empty((2, Tq, 2), dtype=torch.float32, device=DEV)
+        g = [torch.empty(t.shape, dtype=torch.float32, device=DEV) for t in (inp.q, inp.k, inp.v)]
+        calls = (
+            lambda: G.gdpa_jfa_bwd(plan.handle, inp.q, inp.k, inp.v, o, lse, inp.do, qo, ko, plan.B, 2, 128, 0, stat,
+                                   *g),
+            lambda: G.gdpa_jfa_bwd_dq(plan.handle, inp.q, inp.k, inp.v, o, lse, inp.do, qo, ko, plan.B, 2, 128, 0,
+                                      stat, g[0]),
+            lambda: G.gdpa_jfa_bwd_dkdv(plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, plan.B, 2, 128, 0, stat,
+                                        g[1], g[2]),
+            lambda: G.gdpa_jfa_bwd_stat(plan.handle, o, lse, inp.do, 2, 128, stat),
+        )
+        for call in calls:
+            with pytest.raises(G.GdpaError) as e:
+                call()
             assert G.STATUS[e.value.status] == "GDPA_ERR_UNSUPPORTED"
 
 
