@@ -184,6 +184,33 @@ gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v
                      gdpa_act act, int window, void* o, void* stream);
 
 /*
+ * gdpa_fwd_noalloc - gdpa_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It makes no device or pinned allocation and calls no allocating
+ * library routine; instead of the plan's device work list and chunk slot buffer
+ * it uses the library's fixed scratch array of 32 MiB per GPU (a static device
+ * array, resident until the process ends): the call copies the plan's forward
+ * work list from the plan's host memory into it (hipMemcpyAsync on `stream`)
+ * and the kernels keep the chunk partial outputs there.
+ *
+ *   plan : any bf16 plan, in particular one made with opts->host_only = 1, which
+ *          owns no device memory at all (its bins, team and block layout are used
+ *          as planned; F32 plans: UNSUPPORTED).  It must stay alive until the
+ *          enqueued work has finished (the copy reads its host memory).
+ *   other arguments, outputs and errors as gdpa_fwd; the result is the one
+ *   gdpa_fwd computes with the same plan layout.
+ *
+ * A plan whose forward list (records, bin pointers, chunk groups and slots) needs
+ * more than the 32 MiB is rejected with INVALID_ARG before anything is enqueued.
+ * Every call on one GPU shares that GPU's array and overwrites it, so calls that
+ * overlap in time on one GPU (e.g. on two streams) race; calls on one stream are
+ * ordered.  Nothing in the array needs to start at zero.
+ */
+gdpa_status gdpa_fwd_noalloc(gdpa_plan plan, const void* q, const void* k, const void* v,
+                             const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                             gdpa_act act, int window, void* o, void* stream);
+
+/*
  * gdpa_bwd - gradients of sum(O * dO): dQ [Tq,H,d], dK and dV [Tk,H,d].
  *
  * dS = (dO V^T) * act'(S) on valid pairs; dV = P^T dO, dK = dS^T Q / sqrt(d),

@@ -67,6 +67,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.gdpa_plan_create.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(gdpa_plan_opts), _vp,
                                      ctypes.POINTER(_vp)]
     lib.gdpa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
+    lib.gdpa_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
     lib.gdpa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
     lib.gdpa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
@@ -101,7 +102,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                           ctypes.POINTER(_vp)]
     lib.gdpa_pffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _vp, _vp]
     lib.gdpa_pffn_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp]
-    for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
+    for name in ("gdpa_plan_create", "gdpa_fwd", "gdpa_fwd_noalloc", "gdpa_bwd", "gdpa_bwd_dkdv", "gdpa_bwd_dq",
                  "gdpa_plan_export", "gdpa_plan_stats", "gdpa_pffn_plan_create", "gdpa_pffn_fwd",
                  "gdpa_pffn_bwd", "gdpa_jfa_fwd", "gdpa_jfa_bwd", "gdpa_jfa_bwd_stat", "gdpa_jfa_bwd_dkdv",
                  "gdpa_jfa_bwd_dq", "gdpa_norm_rstd", "gdpa_norm_fwd", "gdpa_norm_bwd", "gdpa_norm_bwd_dkdv",
@@ -167,6 +168,12 @@ def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: in
 def gdpa_fwd(plan, q, k, v, q_off_dev, kv_off_dev, B, H, d, act, window, o, stream=None):
     _check(load_library().gdpa_fwd(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(q_off_dev), _ptr(kv_off_dev),
                                    B, H, d, _enum(act, ACT), window, _ptr(o), _stream(stream)))
+
+
+def gdpa_fwd_noalloc(plan, q, k, v, q_off_dev, kv_off_dev, B, H, d, act, window, o, stream=None):
+    """gdpa_fwd without any allocation: the work list goes into the library's fixed scratch array."""
+    _check(load_library().gdpa_fwd_noalloc(plan, _ptr(q), _ptr(k), _ptr(v), _ptr(q_off_dev), _ptr(kv_off_dev),
+                                           B, H, d, _enum(act, ACT), window, _ptr(o), _stream(stream)))
 
 
 def gdpa_bwd(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, dq, dk, dv,

@@ -41,7 +41,8 @@ UNITS = [("plan.o", "plan.cpp", []),
          ("fp32.o", "fp32.hip", []),
          ("partials.o", "partials.hip", []),
          ("jfa.o", "jfa.hip", []),
-         ("norm.o", "norm.hip", [])]
+         ("norm.o", "norm.hip", []),
+         ("noalloc.o", "noalloc.hip", [])]
 for _d in (32, 64, 128):
     UNITS.append((f"fwd_d{_d}.o", "fwd_bf16.hip", [f"-DGDPA_D={_d}"]))
     UNITS.append((f"fused_d{_d}.o", "bwd_fused.hip", [f"-DGDPA_D={_d}"]))

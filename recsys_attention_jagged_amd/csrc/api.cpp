@@ -94,6 +94,10 @@ struct gdpa_plan_s {
     float* d_part[3] = {nullptr, nullptr, nullptr};
     // pFFN plans: device copies of the offsets {0, Tq} and {0, M}
     int32_t* d_off = nullptr;
+    // the device records and chunk groups of each list, resolved on the host at
+    // creation (bf16 plans; the upload and gdpa_fwd_noalloc copy them from here)
+    std::vector<DevRec> h_recs[3];
+    std::vector<DevGroup> h_groups[3];
     // pinned host copy of everything uploaded at creation (records, bin pointers,
     // chunk groups, pFFN offsets): the copies are enqueued on the creation stream
     // and read from here, so it lives as long as the plan
@@ -123,13 +127,11 @@ struct gdpa_plan_s {
 // the records, bin pointers and chunk groups in one pinned host buffer owned by
 // the plan, and enqueue the copies on `s` (no synchronisation).
 static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
-    std::vector<DevRec> recs[3];
-    std::vector<DevGroup> groups[3];
+    const std::vector<DevRec>* recs = p->h_recs;
+    const std::vector<DevGroup>* groups = p->h_groups;
     size_t bytes = 0;
     auto align = [](size_t n) { return (n + 255) & ~(size_t)255; };
     for (int l = 0; l < 3; ++l) {
-        recs[l] = device_records(p->lists[l], p->q_off, p->kv_off);
-        if (p->lists[l].n_parts > 0) groups[l] = device_groups(p->lists[l], p->q_off, p->kv_off);
         bytes += align(recs[l].size() * sizeof(DevRec)) + align(p->lists[l].bin_ptr.size() * sizeof(int32_t)) +
                  align(groups[l].size() * sizeof(DevGroup));
     }
@@ -300,6 +302,13 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split);
     }
 
+    if (dtype != GDPA_F32) {
+        for (int l = 0; l < 3; ++l) {
+            p->h_recs[l] = device_records(p->lists[l], p->q_off, p->kv_off);
+            if (p->lists[l].n_parts > 0) p->h_groups[l] = device_groups(p->lists[l], p->q_off, p->kv_off);
+        }
+    }
+
     // one-pass backward: one side of every sample fits one 32-row tile, and no
     // sample has rows on that side only (their outputs would have no item)
     if (dtype != GDPA_F32 && o.unfused == 0) {
@@ -398,6 +407,18 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
 // RMSNorm prologue: eps under the root
 constexpr float kRmsEps = 1e-6f;
 
+// GDPA_DEBUG: the device offsets must equal the plan's (copied to the host and compared)
+static gdpa_status check_offsets(gdpa_plan plan, const int32_t* q_off_dev, const int32_t* kv_off_dev) {
+    const int B = plan->B;
+    std::vector<int32_t> hq(B + 1), hk(B + 1);
+    hipError_t e = hipMemcpy(hq.data(), q_off_dev, (B + 1) * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(hk.data(), kv_off_dev, (B + 1) * sizeof(int32_t), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail_hip(e, "GDPA_DEBUG offset check");
+    if (hq != plan->q_off || hk != plan->kv_off)
+        return fail(GDPA_ERR_PLAN_MISMATCH, "device offsets differ from the plan's");
+    return GDPA_OK;
+}
+
 static gdpa_status check_call(gdpa_plan plan, const int32_t* q_off_dev, const int32_t* kv_off_dev, int B,
                               int H, int d, gdpa_act act, int window) {
     if (!plan) return fail(GDPA_ERR_INVALID_ARG, "plan is NULL");
@@ -406,15 +427,7 @@ static gdpa_status check_call(gdpa_plan plan, const int32_t* q_off_dev, const in
         return fail(GDPA_ERR_PLAN_MISMATCH, "B, H, d or window differ from the plan");
     if ((int)act < 0 || (int)act > GDPA_ACT_ONE) return fail(GDPA_ERR_INVALID_ARG, "unknown activation");
     if (!q_off_dev || !kv_off_dev) return fail(GDPA_ERR_INVALID_ARG, "device offsets are NULL");
-    if (debug_enabled()) {
-        std::vector<int32_t> hq(B + 1), hk(B + 1);
-        hipError_t e = hipMemcpy(hq.data(), q_off_dev, (B + 1) * sizeof(int32_t), hipMemcpyDeviceToHost);
-        if (e == hipSuccess)
-            e = hipMemcpy(hk.data(), kv_off_dev, (B + 1) * sizeof(int32_t), hipMemcpyDeviceToHost);
-        if (e != hipSuccess) return fail_hip(e, "GDPA_DEBUG offset check");
-        if (hq != plan->q_off || hk != plan->kv_off)
-            return fail(GDPA_ERR_PLAN_MISMATCH, "device offsets differ from the plan's");
-    }
+    if (debug_enabled()) return check_offsets(plan, q_off_dev, kv_off_dev);
     return GDPA_OK;
 }
 
@@ -473,6 +486,70 @@ gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v
         }
         if (e == hipSuccess) e = reduce_parts(plan, LIST_FWD, 1.0f, o, s);
     }
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no forward kernel for this configuration");
+    if (e != hipSuccess) return fail_hip(e, "forward launch");
+    return GDPA_OK;
+}
+
+gdpa_status gdpa_fwd_noalloc(gdpa_plan plan, const void* q, const void* k, const void* v,
+                             const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                             gdpa_act act, int window, void* o, void* stream) {
+    g_err.clear();
+    if (!plan) return fail(GDPA_ERR_INVALID_ARG, "plan is NULL");
+    if (B != plan->B || H != plan->H || d != plan->d || window != plan->window)
+        return fail(GDPA_ERR_PLAN_MISMATCH, "B, H, d or window differ from the plan");
+    if ((int)act < 0 || (int)act > GDPA_ACT_ONE) return fail(GDPA_ERR_INVALID_ARG, "unknown activation");
+    if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "the no-allocation forward runs bf16 plans");
+    if (!q_off_dev || !kv_off_dev) return fail(GDPA_ERR_INVALID_ARG, "device offsets are NULL");
+    if (plan->Tq > 0 && (!q || !o)) return fail(GDPA_ERR_INVALID_ARG, "q or o is NULL");
+    if (plan->Tk > 0 && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
+    if (plan->Tq == 0) return GDPA_OK;
+    // the scratch layout: records, bin pointers, chunk groups, chunk slots (fp32
+    // t_stat x (d + 2) per slot, as the plan's own slot buffer), each 256-byte aligned
+    const WorkList& wl = plan->lists[LIST_FWD];
+    const std::vector<DevRec>& recs = plan->h_recs[LIST_FWD];
+    const std::vector<DevGroup>& groups = plan->h_groups[LIST_FWD];
+    auto align = [](size_t n) { return (n + 255) & ~(size_t)255; };
+    const size_t b_recs = recs.size() * sizeof(DevRec), b_ptr = wl.bin_ptr.size() * sizeof(int32_t);
+    const size_t b_groups = groups.size() * sizeof(DevGroup);
+    const size_t b_slots = (size_t)wl.n_parts * wl.t_stat * ((size_t)d + 2) * sizeof(float);
+    const size_t o_ptr = align(b_recs), o_groups = o_ptr + align(b_ptr), o_slots = o_groups + align(b_groups);
+    const size_t need = o_slots + b_slots;
+    if (need > kNoallocScratchBytes)
+        return fail(GDPA_ERR_INVALID_ARG, "the plan's forward work list needs " + std::to_string(need) +
+                                              " bytes of scratch; the no-allocation forward has " +
+                                              std::to_string(kNoallocScratchBytes));
+    if (debug_enabled()) {
+        const gdpa_status st = check_offsets(plan, q_off_dev, kv_off_dev);
+        if (st != GDPA_OK) return st;
+    }
+    void* base = nullptr;
+    hipError_t e = noalloc_scratch(&base);
+    if (e != hipSuccess) return fail_hip(e, "scratch address");
+    char* sc = (char*)base;
+    hipStream_t s = (hipStream_t)stream;
+    // the work list comes from the plan's host memory, which lives until the plan is destroyed
+    if (b_recs) e = hipMemcpyAsync(sc, recs.data(), b_recs, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(sc + o_ptr, wl.bin_ptr.data(), b_ptr, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && b_groups) e = hipMemcpyAsync(sc + o_groups, groups.data(), b_groups, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return fail_hip(e, "work list copy into scratch");
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.items = sc;
+    a.bin_ptr = (const int32_t*)(sc + o_ptr);
+    a.P = wl.P;
+    a.part = wl.n_parts > 0 ? (float*)(sc + o_slots) : nullptr;
+    switch (d) {
+        case 32: e = launch_fwd_bf16_d32(a, wl.team, wl.nb, act, s); break;
+        case 64: e = launch_fwd_bf16_d64(a, wl.team, wl.nb, act, s); break;
+        default: e = launch_fwd_bf16_d128(a, wl.team, wl.nb, act, s); break;
+    }
+    if (e == hipSuccess && !groups.empty())
+        e = launch_partial_sum((const DevGroup*)(sc + o_groups), (int)groups.size(), a.part, wl.t_stat, 1, 0, d, H,
+                               1.0f, o, plan->dtype != GDPA_BF16, s);
     if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no forward kernel for this configuration");
     if (e != hipSuccess) return fail_hip(e, "forward launch");
     return GDPA_OK;

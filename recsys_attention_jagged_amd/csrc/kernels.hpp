@@ -117,6 +117,12 @@ hipError_t launch_jfa_combine(const DevGroup* groups, int n_groups, const float*
 hipError_t launch_jfa_stat(const void* o, const void* dout, const float* lse, int Tq, int H, int d, float* stat,
                            hipStream_t s);
 
+// Bytes of the fixed device scratch array that the no-allocation entry points
+// use (per GPU, for the life of the process), and its address on the current
+// device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** out);
+
 // plain fp32 kernels (no MFMA): forward, dQ, dK/dV over the offsets directly
 hipError_t launch_fwd_f32(const KernelArgs& a, int Tq, int d, int act, hipStream_t s);
 hipError_t launch_bwd_f32(const KernelArgs& a, int Tq, int Tk, int d, int act, hipStream_t s);

@@ -259,3 +259,20 @@ def test_pffn_host_plan_is_one_sample():
     finally:
         G.gdpa_plan_destroy(h)
     assert G.STATUS[_status_of(G.gdpa_pffn_plan_create, -1, 3, 2, 64, "bf16", host_only=True)] == "GDPA_ERR_INVALID_ARG"
+
+
+def test_noalloc_forward_rejects_a_plan_beyond_its_scratch_before_any_device_call():
+    """gdpa_fwd_noalloc checks the plan's forward list against its fixed 32 MiB scratch
+    on the host: 20 samples x 60000 heads make 1.2 M forward items (57.6 MB of records),
+    refused with INVALID_ARG before anything touches a device (none is present here)."""
+    lq = [64] * 20
+    qo = offsets(lq)
+    plan = G.gdpa_plan_create(qo, qo, 20, 60000, 128, 0, "bf16", host_only=True)
+    try:
+        assert G.gdpa_plan_stats(plan)["n_items"][0] == 20 * 60000
+        fake = 1 << 20   # never dereferenced
+        st = G.load_library().gdpa_fwd_noalloc(plan, fake, fake, fake, fake, fake, 20, 60000, 128, 0, 0, fake, 0)
+        assert G.STATUS[st] == "GDPA_ERR_INVALID_ARG"
+        assert "bytes of scratch" in G.gdpa_last_error()
+    finally:
+        G.gdpa_plan_destroy(plan)
