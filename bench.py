@@ -99,7 +99,7 @@ def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False):
 
 KERNEL_SOURCES = ("device.hpp", "ring.hpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd_common.hpp", "bwd_fused.hip",
                   "jfa.hip", "norm.hip", "partials.hip", "kernels.hpp", "plan.cpp", "plan.hpp", "api.cpp", "gelu_poly.h",
-                  "noalloc.hip")
+                  "noalloc.hip", "bwd16.hip")
 
 
 def kernel_source_digest() -> str:

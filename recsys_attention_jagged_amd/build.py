@@ -54,6 +54,8 @@ for _d in (32, 64, 128):
 # instead, copies them back every step and waits on each operand read.
 UNITS.append(("bwd_dq_d128.o", "bwd_bf16.hip", ["-DGDPA_D=128", "-DGDPA_BWD_PART=1"]))
 UNITS.append(("bwd_kv_d128.o", "bwd_bf16.hip", ["-DGDPA_D=128", "-DGDPA_BWD_PART=2", AGPR_ACC]))
+# d = 128: the 16-row two-wave dK/dV kernel (MFMA results in VGPRs)
+UNITS.append(("bwd16_d128.o", "bwd16.hip", []))
 
 
 # the clock-probe library (GDPA_BIN_CLOCK): every kernel stamps the start and the end

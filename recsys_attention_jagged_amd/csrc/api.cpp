@@ -291,8 +291,10 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
                 const void* f = l == LIST_FWD ? fwd_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU)
                               : l == LIST_DQ  ? dq_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU)
                                               : dkdv_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU);
+                // the d = 128 dK/dV list's 16-row kernel runs two waves per 32 team rows
+                const bool k16 = l == LIST_DKDV && d == 128 && f && f == dkdv16_kernel_ptr(32 * L.team[l], GDPA_ACT_GELU);
                 int per_cu = 0;
-                if (f && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, 64 * L.team[l], 0) == hipSuccess &&
+                if (f && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, (k16 ? 128 : 64) * L.team[l], 0) == hipSuccess &&
                     per_cu > 0)
                     P = cus * per_cu;
             }

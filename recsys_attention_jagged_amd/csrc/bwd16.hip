@@ -1,0 +1,307 @@
+// GDPA dK / dV kernel for d = 128 on the 16 x 16 x 32 bf16 MFMA, two waves per SIMD.
+//
+// Gradients of sum(O * dO) for O = act(S) V, S = Q K^T / sqrt(d) on the valid
+// pairs (GDPA page, aitrends.kr/articles/26275, "Section details": the softmax and
+// its correction step are gone, so the backward recomputes S and needs no row
+// statistic): dP = dO V^T, dS = dP * act'(S), dV = P^T dO, dK = dS^T Q / sqrt(d).
+//
+// KV-stationary.  A workgroup is a team of two or four waves sharing one tile ring
+// (ring.hpp); an item is one (sample, head) and 32 or 64 kv rows (one or two
+// 32-row tiles), its steps the 32-row q tiles that hold valid pairs.  Each wave
+// owns 16 of the item's kv rows:
+// its K and V rows stay in registers as B operands, its dK and dV accumulate in
+// registers, and both waves read every streamed Q and dO tile from the shared
+// ring.  Per step and wave: S (32 q x 16 kv) and dP in eight 16 x 16 x 32 products
+// each, the activation and its derivative in registers, then dV^T += dO^T P and
+// dK^T += Q^T dS with P and dS taken straight from the score accumulators as B
+// operands (lane l holds kv column l % 16 and q rows 4 (l / 16) + {0..3} and
+// 16 + 4 (l / 16) + {0..3}; the A operands read the same q rows of dO and Q
+// with transposing LDS loads).  Half the register state of a 32-row wave lets two
+// waves share each SIMD, so one wave's activation overlaps the other's products.
+// No atomics: every dK, dV row has one owner.
+#include "bwd_common.hpp"
+#include "kernels.hpp"
+#include "ring.hpp"
+
+namespace gdpa {
+namespace {
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Tiles use the 16-row swizzle (ring.hpp, SW = 1).
+constexpr int SW16 = 1;
+
+// 8 bf16 of `row`, columns [8 chunk, 8 chunk + 8)
+template <int D>
+__device__ __forceinline__ bf16x8 row8_16(const char* tile, int row, int chunk) {
+    return *(const bf16x8*)(tile + tile_off_sw<D, SW16>(row, chunk));
+}
+
+// Transposed operand in the 16-column layout: lane l receives
+// tile[row0 + 4 (l / 16) + i][col0 + l % 16], i = 0..3 (row0 a multiple of 4,
+// col0 a multiple of 16).  Each 16-lane group reads one 4-row x 16-column block:
+// lanes 4k .. 4k + 3 address row k's four 8-byte pieces.
+template <int D>
+__device__ __forceinline__ bf16x4 lds_col4_16(const char* tile, int row0, int col0, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int row = row0 + 4 * g + (i >> 2);
+    const int t = i & 3;
+    const int col = col0 + 4 * t;
+    const int off = tile_off_sw<D, SW16>(row, col >> 3) + ((t & 1) << 3);
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + off));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// A operand of the 8 q rows a lane group contracts over: rows row0 + 4 (l / 16) + {0..3}
+// and row0 + 16 + 4 (l / 16) + {0..3}, column col0 + l % 16
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col8_16(const char* tile, int row0, int col0, int lane) {
+    const bf16x4 a = lds_col4_16<D>(tile, row0, col0, lane);
+    const bf16x4 b = lds_col4_16<D>(tile, row0 + 16, col0, lane);
+    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <int ACT, int T>
+struct Dkdv16Pol : Common {
+    static constexpr int D = 128;
+    static constexpr int ROWS = 16 * T;          // kv rows per item
+    static constexpr int NSTAT = ROWS / 16, NSTRM = 2;   // stationary: (K, V) of each 32-row tile
+    static constexpr int NKB = D / 32;           // 32-wide head-dimension blocks (contraction of S, dP)
+    static constexpr int NCB = D / 16;           // 16-wide head-dimension blocks (dK, dV columns)
+    Slice wk, wv, wq, wo;                       // issuing side
+    bf16x8 kf[NKB], vf[NKB];                     // this wave's 16 kv rows of K and V (B operands)
+    f32x4 accK[NCB], accV[NCB];                  // lane: kv row l % 16, columns 16 cb + 4 (l / 16) + {0..3}
+    int l16, g4;                                 // lane % 16, lane / 16
+
+    __device__ Dkdv16Pol(const KernelArgs& args, int lane_, int wt_) : Common(args, lane_, wt_, D) {
+        l16 = lane_ & 15;
+        g4 = lane_ >> 4;
+    }
+
+    // this wave's first kv row of the item, within the sample
+    __device__ __forceinline__ int krow(const Rec& c) const { return c.t * ROWS + 16 * wt; }
+
+    __device__ __forceinline__ void walk_item(const Rec& w) {
+        const size_t kvb = ((size_t)w.ks * H + w.h) * D;
+        wk = slice_of((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+        wv = slice_of((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        const size_t qb = ((size_t)w.qs * H + w.h) * D;
+        wq = slice_of((const __bf16*)a.q + qb, w.lq, rs, D * 2);
+        wo = slice_of((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
+        if (i < NSTAT) {   // tile i / 2 of the item: K (i even), V (i odd)
+            g.issue((i & 1) ? wv : wk, (uint32_t)(w.t * ROWS + 32 * (i >> 1)) * rs);
+        } else {
+            const int rel = i - NSTAT;
+            g.issue((rel & 1) ? wo : wq, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
+        }
+    }
+
+    __device__ __forceinline__ void item_begin(const Rec&) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) accK[cb] = accV[cb] = f32x4{};
+    }
+
+    // the K and V tiles i / 2 (jobs job, job + 1), read by the two waves whose rows
+    // they hold: row 16 (wt % 2) + l % 16, the 16-byte chunk 4 kb + l / 16 of each
+    // 32-wide block kb
+    template <class RingT>
+    __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job, int i) {
+        if ((wt >> 1) != (i >> 1)) return;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            kf[kb] = row8_16<D>(g.tile(job), 16 * (wt & 1) + l16, 4 * kb + g4);
+            vf[kb] = row8_16<D>(g.tile(job + 1), 16 * (wt & 1) + l16, 4 * kb + g4);
+        }
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
+        const int i0 = s * 32, j0 = krow(c);
+        // a wave whose 16 kv rows are past the sample's keys, or have no pair with this
+        // q tile in the band, skips the step
+        if (j0 >= c.lk || (win > 0 && (j0 - (i0 + 31) >= win || i0 - (j0 + 15) >= win))) return;
+        const char* qt = g.tile(job);
+        const char* ot = g.tile(job + 1);
+        // The step's LDS reads go out in batches ahead of the products that use them
+        // (the scheduling barriers keep the compiler from pairing each product with a
+        // read and a wait): the Q and dO row operands, then the products for S and dP,
+        // then the transposed operands of the second products, which land while the
+        // activation runs.
+        bf16x8 qo[2][NKB], oo[2][NKB];
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                qo[ib][kb] = row8_16<D>(qt, 16 * ib + l16, 4 * kb + g4);
+                oo[ib][kb] = row8_16<D>(ot, 16 * ib + l16, 4 * kb + g4);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        // S and dP: element v of block ib holds q row i0 + 16 ib + 4 (l / 16) + v, kv row j0 + l % 16
+        f32x4 sc[2], dp[2];
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+            sc[ib] = dp[ib] = f32x4{};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                sc[ib] = mfma16(qo[ib][kb], kf[kb], sc[ib]);
+                dp[ib] = mfma16(oo[ib][kb], vf[kb], dp[ib]);
+            }
+        }
+        constexpr int HC = NCB / 2;
+        bf16x8 tv[HC], tk[HC];
+#pragma unroll
+        for (int cb = 0; cb < HC; ++cb) {
+            tv[cb] = lds_col8_16<D>(ot, 0, 16 * cb, lane);
+            tk[cb] = lds_col8_16<D>(qt, 0, 16 * cb, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 pm, dm;
+        const bool band = win > 0 && !((i0 + 31 - j0) < win && (j0 + 15 - i0) < win);
+        if (band) {   // one uniform branch per step
+            const int base = i0 + 4 * g4 - j0 - l16;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ib = e >> 2, v = e & 3;
+                float f, gr;
+                act_fwd_grad<ACT>(sc[ib][v] * scale, f, gr);
+                const bool ok = in_band(base + 16 * ib + v, win);
+                pm[e] = (__bf16)(ok ? f : 0.0f);
+                dm[e] = (__bf16)(ok ? dp[ib][v] * gr : 0.0f);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int ib = e >> 2, v = e & 3;
+                float f, gr;
+                act_fwd_grad<ACT>(sc[ib][v] * scale, f, gr);
+                pm[e] = (__bf16)f;
+                dm[e] = (__bf16)(dp[ib][v] * gr);
+            }
+        }
+        // the second half's transposed operands go out before the first half's products
+        bf16x8 tv2[HC], tk2[HC];
+#pragma unroll
+        for (int cb = 0; cb < HC; ++cb) {
+            tv2[cb] = lds_col8_16<D>(ot, 0, 16 * (cb + HC), lane);
+            tk2[cb] = lds_col8_16<D>(qt, 0, 16 * (cb + HC), lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int cb = 0; cb < HC; ++cb) {
+            accV[cb] = mfma16(tv[cb], pm, accV[cb]);
+            accK[cb] = mfma16(tk[cb], dm, accK[cb]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < HC; ++cb) {
+            accV[cb + HC] = mfma16(tv2[cb], pm, accV[cb + HC]);
+            accK[cb + HC] = mfma16(tk2[cb], dm, accK[cb + HC]);
+        }
+    }
+
+    // this wave's 16 rows of one output (acc: kv row l % 16, columns 16 cb + 4 (l / 16) + {0..3})
+    __device__ __forceinline__ void store16(const f32x4 (&acc)[NCB], float mul, void* out, size_t base, int rows,
+                                            int row0, char* stage) const {
+        if (a.out_f32) {
+            const rsrc_t ro = slice_rsrc((const float*)out + base, rows, rso, D * 4);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                u32x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[cb][i] * mul);
+                buf_store16(ro, (uint32_t)(row0 + l16) * rso + (uint32_t)(16 * cb + 4 * g4) * 4u, v);
+            }
+            return;
+        }
+        // bf16: stage the 16 rows in a swizzled tile, then store whole rows, 16 bytes per lane
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[cb][0] * mul, acc[cb][1] * mul);
+            w[1] = pack_bf16x2(acc[cb][2] * mul, acc[cb][3] * mul);
+            *(u32x2*)(stage + tile_off_sw<D, SW16>(l16, 2 * cb + (g4 >> 1)) + 8 * (g4 & 1)) = w;
+        }
+        const rsrc_t ro = slice_rsrc((const __bf16*)out + base, rows, rso, D * 2);
+        constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16-byte chunks per row, rows per instruction
+        const int rr = lane / CPR, cc = lane % CPR;
+#pragma unroll
+        for (int k = 0; k < 16 / RPI; ++k) {
+            const int row = k * RPI + rr;
+            buf_store16(ro, (uint32_t)(row0 + row) * rso + (uint32_t)cc * 16u, *(const u32x4*)(stage + tile_off_sw<D, SW16>(row, cc)));
+        }
+    }
+
+    // a chunk's partial block: fp32 rows 16 wt + l % 16 of slot `slot` ([slots][ROWS][D])
+    __device__ __forceinline__ void partial16(const f32x4 (&acc)[NCB], int slot) const {
+        constexpr uint32_t RB = D * 4;
+        const rsrc_t ro = slice_rsrc(a.part + (size_t)slot * ROWS * D, ROWS, RB, RB);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            u32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(acc[cb][i]);
+            buf_store16(ro, (uint32_t)(16 * wt + l16) * RB + (uint32_t)(16 * cb + 4 * g4) * 4u, v);
+        }
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
+        if (c.part >= 0) {   // one chunk of a cut item: fp32 partial dK, dV (scaled by the reduction)
+            partial16(accK, 2 * c.part);
+            partial16(accV, 2 * c.part + 1);
+            return;
+        }
+        // stage through this wave's 4 KiB of the item's last two slots (free after the
+        // team barrier): dK, then dV once this wave has read dK back
+        char* stage = g.tile(job - 2 + (wt >> 1)) + (wt & 1) * (16 * D * 2);
+        const size_t ob = ((size_t)c.ks * H + c.h) * D;
+        store16(accK, scale, a.dk, ob, c.lk, krow(c), stage);
+        wait_lds();
+        store16(accV, 1.0f, a.dv, ob, c.lk, krow(c), stage);
+    }
+
+    __device__ __forceinline__ void item_zero(const Rec& c) {
+        if (wt & 1) return;   // waves 0, 2 zero the item's 32-row halves
+        const size_t ob = ((size_t)c.ks * H + c.h) * D;
+        zero<D>(a.dk, ob, c.lk, c.t * ROWS + 16 * wt);
+        zero<D>(a.dv, ob, c.lk, c.t * ROWS + 16 * wt);
+    }
+};
+
+template <int ACT, int T>
+__global__ __launch_bounds__(64 * T, 2) void dkdv16_kernel(const KernelArgs a, const Rec* __restrict__ recs,
+                                                          const int32_t* __restrict__ bin_ptr) {
+    using RingT = Ring<128, T, 40 * 512 * T, 0, SW16>;   // 40 KiB per team of two waves
+    __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
+    const int wt = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    Dkdv16Pol<ACT, T> pol(a, lane, wt);
+    run_team<Dkdv16Pol<ACT, T>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * 128 * 2, wt, lane);
+}
+
+}  // namespace
+
+template <int T>
+const void* dkdv16_ptr(int act) {
+    switch (act) {
+        case ACT_GELU: return (const void*)&dkdv16_kernel<ACT_GELU, T>;
+        case ACT_SILU: return (const void*)&dkdv16_kernel<ACT_SILU, T>;
+        case ACT_GELU_POLY: return (const void*)&dkdv16_kernel<ACT_GELU_POLY, T>;
+        case ACT_GELU_TAYLOR6: return (const void*)&dkdv16_kernel<ACT_GELU_TAYLOR6, T>;
+        case ACT_IDENTITY: return (const void*)&dkdv16_kernel<ACT_IDENTITY, T>;
+    }
+    return nullptr;
+}
+
+const void* dkdv16_kernel_ptr(int rows, int act) {
+    if (rows == 32) return dkdv16_ptr<2>(act);
+    if (rows == 64) return dkdv16_ptr<4>(act);
+    return nullptr;
+}
+
+}  // namespace gdpa

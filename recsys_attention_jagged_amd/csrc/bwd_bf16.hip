@@ -105,13 +105,13 @@ struct DqPol : Common {
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr int ROWS = 32 * T * NB;   // q rows per item
     static constexpr bool HOIST = TeamShape<D, T, 2>::HOIST;
-    rsrc_t wq, wo, wk, wv;   // issuing side
-    rsrc_t wst, wnull;       // softmax: LSE of the item's q rows; a zero-range side
-    rsrc_t wfo;              // softmax: the forward's O rows
+    Slice wq, wo, wk, wv;   // issuing side
+    Slice wst, wnull;       // softmax: LSE of the item's q rows; a zero-range side
+    Slice wfo;              // softmax: the forward's O rows
     bf16x8 qf[NB][NKS], of[NB][NKS];
     f32x16 acc[NB][NDB];
     float l2q[NB], dq_[NB];  // softmax: this lane's q row's LSE log2(e) and D
-    rsrc_t wrq, wrkv;        // NORM: 1/rms of the item's q rows, (k, v) row pairs
+    Slice wrq, wrkv;        // NORM: 1/rms of the item's q rows, (k, v) row pairs
     float rqv[NB];           // NORM: 1/rms of this lane's q row
     bf16x4 qa[NORM ? NB : 1][D / 32][4];   // NORM: this lane's q row in the accumulator's layout
 
@@ -121,26 +121,26 @@ struct DqPol : Common {
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
-        wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
-        wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        wk = slice_of((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+        wv = slice_of((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
         const size_t qb = ((size_t)w.qs * H + w.h) * D;
-        wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
-        wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        wq = slice_of((const __bf16*)a.q + qb, w.lq, rs, D * 2);
+        wo = slice_of((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
         if constexpr (SM) {
-            wst = slice_rsrc(a.lse + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
-            wnull = slice_rsrc(a.lse, 0, 4u, 4u);
-            wfo = slice_rsrc((const __bf16*)a.o + qb, w.lq, rs, D * 2);
+            wst = slice_of(a.lse + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wnull = slice_of(a.lse, 0, 4u, 4u);
+            wfo = slice_of((const __bf16*)a.o + qb, w.lq, rs, D * 2);
         }
         if constexpr (NORM) {
-            wrq = slice_rsrc(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
-            wrkv = slice_rsrc(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
-            wnull = slice_rsrc(a.rkv, 0, 8u, 8u);
+            wrq = slice_of(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wrkv = slice_of(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
+            wnull = slice_of(a.rkv, 0, 8u, 8u);
         }
     }
 
     // tile rows at byte offset `off` of `t`; softmax, NORM: and the side at x_off of `xs`
     template <class RingT>
-    __device__ __forceinline__ void put(RingT& g, rsrc_t t, uint32_t off, rsrc_t xs, uint32_t x_off) {
+    __device__ __forceinline__ void put(RingT& g, Slice t, uint32_t off, Slice xs, uint32_t x_off) {
         if constexpr (SM || NORM)
             g.issue(t, off, xs, x_off);
         else
@@ -391,9 +391,9 @@ struct DkdvPol : Common {
     static constexpr int ROWS = 32 * T;   // kv rows per item
     static constexpr bool HOIST = TeamShape<D, T, 1>::HOIST;
     static constexpr bool SM = ACT == ACT_SOFTMAX;
-    rsrc_t wk, wv, wq, wo;   // issuing side
-    rsrc_t wst, wnull;       // softmax: row statistics of the item's q rows; a zero-range side
-    rsrc_t wrq, wrkv;        // NORM: 1/rms of the item's q rows, (k, v) row pairs
+    Slice wk, wv, wq, wo;   // issuing side
+    Slice wst, wnull;       // softmax: row statistics of the item's q rows; a zero-range side
+    Slice wrq, wrkv;        // NORM: 1/rms of the item's q rows, (k, v) row pairs
     float rkl, rvl;          // NORM: 1/rms of this lane's k and v rows
     bf16x4 ka[NORM ? D / 32 : 1][4], va[NORM ? D / 32 : 1][4];   // NORM: those rows in the accumulator's layout
     bf16x8 kf[NKS], vf[NKS];
@@ -405,25 +405,25 @@ struct DkdvPol : Common {
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
-        wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
-        wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        wk = slice_of((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+        wv = slice_of((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
         const size_t qb = ((size_t)w.qs * H + w.h) * D;
-        wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
-        wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        wq = slice_of((const __bf16*)a.q + qb, w.lq, rs, D * 2);
+        wo = slice_of((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
         if constexpr (SM) {
-            wst = slice_rsrc(a.stat + ((size_t)w.h * a.Tq + w.qs) * 2, w.lq, 8u, 8u);
-            wnull = slice_rsrc(a.stat, 0, 8u, 8u);
+            wst = slice_of(a.stat + ((size_t)w.h * a.Tq + w.qs) * 2, w.lq, 8u, 8u);
+            wnull = slice_of(a.stat, 0, 8u, 8u);
         }
         if constexpr (NORM) {
-            wrq = slice_rsrc(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
-            wrkv = slice_rsrc(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
-            wnull = slice_rsrc(a.rkv, 0, 8u, 8u);
+            wrq = slice_of(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wrkv = slice_of(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
+            wnull = slice_of(a.rkv, 0, 8u, 8u);
         }
     }
 
     // tile rows at byte offset `off` of `t`; softmax, NORM: and the side at x_off of `xs`
     template <class RingT>
-    __device__ __forceinline__ void put(RingT& g, rsrc_t t, uint32_t off, rsrc_t xs, uint32_t x_off) {
+    __device__ __forceinline__ void put(RingT& g, Slice t, uint32_t off, Slice xs, uint32_t x_off) {
         if constexpr (SM || NORM)
             g.issue(t, off, xs, x_off);
         else
@@ -667,6 +667,11 @@ const void* GDPA_CAT(dq_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
 #if GDPA_BWD_PART != 1
 const void* GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) {
     if (nb != 1) return nullptr;
+#if GDPA_D == 128
+    // plain activations run on the 16-row kernel (32 team rows per item: two waves
+    // for a one-wave layout, four for a two-wave layout)
+    if (act >= ACT_GELU && act <= ACT_IDENTITY) return dkdv16_kernel_ptr(32 * team, act);
+#endif
     if (act == ACT_SOFTMAX) return team == 1 ? dkdv_ptr<1, 1, ACT_SOFTMAX>() : nullptr;
     if (team == 1) return dkdv_act<1>(act);
 #if GDPA_D == 128
@@ -695,7 +700,11 @@ hipError_t GDPA_CAT(launch_dq_bf16_d, GDPA_D)(const KernelArgs& a, int team, int
 
 #if GDPA_BWD_PART != 1
 hipError_t GDPA_CAT(launch_dkdv_bf16_d, GDPA_D)(const KernelArgs& a, int team, int nb, int act, hipStream_t s) {
-    return launch(GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(team, nb, act), a, team, s);
+    const void* f = GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(team, nb, act);
+#if GDPA_D == 128
+    if (f && f == dkdv16_kernel_ptr(32 * team, act)) return launch(f, a, 2 * team, s);   // 16 rows per wave
+#endif
+    return launch(f, a, team, s);
 }
 #endif
 

@@ -34,7 +34,7 @@ struct KvFusedPol : Common {
     static constexpr int NSTAT = 2, NSTRM = 2;   // (K, V), then (Q, dO) per step
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr bool HOIST = TeamShape<D, 1, 2>::HOIST;
-    rsrc_t wk, wv, wq, wo;   // issuing side
+    Slice wk, wv, wq, wo;   // issuing side
     bf16x8 kf[NKS], vf[NKS], kt[2][NDB];
     f32x16 accK[NDB], accV[NDB];
 
@@ -42,11 +42,11 @@ struct KvFusedPol : Common {
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
-        wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
-        wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        wk = slice_of((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+        wv = slice_of((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
         const size_t qb = ((size_t)w.qs * H + w.h) * D;
-        wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
-        wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        wq = slice_of((const __bf16*)a.q + qb, w.lq, rs, D * 2);
+        wo = slice_of((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
     }
 
     template <class RingT>
@@ -169,7 +169,7 @@ struct QFusedPol : Common {
     static constexpr int NSTAT = 2, NSTRM = 2;   // (Q, dO), then (K, V) per step
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr bool HOIST = TeamShape<D, 1, 2>::HOIST;
-    rsrc_t wq, wo, wk, wv;   // issuing side
+    Slice wq, wo, wk, wv;   // issuing side
     bf16x8 qf[NKS], of[NKS], qt[2][NDB], ot[2][NDB];
     f32x16 acc[NDB];
 
@@ -177,11 +177,11 @@ struct QFusedPol : Common {
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
-        wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
-        wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        wk = slice_of((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+        wv = slice_of((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
         const size_t qb = ((size_t)w.qs * H + w.h) * D;
-        wq = slice_rsrc((const __bf16*)a.q + qb, w.lq, rs, D * 2);
-        wo = slice_rsrc((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        wq = slice_of((const __bf16*)a.q + qb, w.lq, rs, D * 2);
+        wo = slice_of((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
     }
 
     template <class RingT>

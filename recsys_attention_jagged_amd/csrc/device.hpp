@@ -50,6 +50,29 @@ __device__ __forceinline__ rsrc_t slice_rsrc(const void* base, int rows, uint32_
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
 }
 
+// The same slice kept as (first byte, bytes in range), for the tile loads: each
+// load builds its descriptor at the tile's first row (slice_at), so the per-lane
+// offsets inside a tile never change and the range check stays exact (an offset v
+// of slice_at(s, off) is in range iff off + v is in range of s).
+struct Slice {
+    const char* base;
+    uint32_t bytes;
+};
+
+__device__ __forceinline__ Slice slice_of(const void* base, int rows, uint32_t row_stride_bytes, uint32_t row_bytes) {
+    return Slice{(const char*)base, rows > 0 ? (uint32_t)(rows - 1) * row_stride_bytes + row_bytes : 0u};
+}
+
+// (the slice and the offset are uniform; readfirstlane keeps the descriptor in
+// scalar registers, where the load instructions take it)
+__device__ __forceinline__ rsrc_t slice_at(Slice s, uint32_t off) {
+    const uint64_t a = (uint64_t)(size_t)(s.base + off);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(s.bytes > off ? s.bytes - off : 0u);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(size_t)((uint64_t)hi << 32 | lo), 0, (int)n, 0x00020000);
+}
+
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }

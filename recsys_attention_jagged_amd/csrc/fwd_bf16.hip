@@ -55,8 +55,8 @@ struct FwdPol {
     int lane, r, hh, wt, H, win;
     uint32_t rs, rso;
     float scale;
-    rsrc_t wq, wk, wv;    // issuing side: slices of the walk's current item
-    rsrc_t wrq, wrkv, wnull;   // NORM: 1/rms of the item's q rows, (k, v) row pairs; a zero-range side
+    Slice wq, wk, wv;    // issuing side: slices of the walk's current item
+    Slice wrq, wrkv, wnull;   // NORM: 1/rms of the item's q rows, (k, v) row pairs; a zero-range side
     bf16x8 qf[F8 ? 1 : NB][NKS];
     long qf8[F8 ? NB : 1][NKS];   // F8: this lane's 8 fp8 values of each 16-wide k block
     float rqv[NB];        // NORM: 1/rms of this lane's q row
@@ -86,19 +86,19 @@ struct FwdPol {
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
-        wk = slice_rsrc((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
-        wv = slice_rsrc((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        wk = slice_of((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+        wv = slice_of((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
         if constexpr (F8) {   // one-byte rows, H D bytes apart
-            wk = slice_rsrc((const uint8_t*)a.k + kvb, w.lk, rs / 2, D);
-            wq = slice_rsrc((const uint8_t*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs / 2, D);
-            wnull = slice_rsrc(a.q, 0, rs / 2, D);
+            wk = slice_of((const uint8_t*)a.k + kvb, w.lk, rs / 2, D);
+            wq = slice_of((const uint8_t*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs / 2, D);
+            wnull = slice_of(a.q, 0, rs / 2, D);
         } else {
-            wq = slice_rsrc((const __bf16*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs, D * 2);
+            wq = slice_of((const __bf16*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs, D * 2);
         }
         if constexpr (NORM) {
-            wrq = slice_rsrc(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
-            wrkv = slice_rsrc(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
-            wnull = slice_rsrc(a.rkv, 0, 8u, 8u);
+            wrq = slice_of(a.rq + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wrkv = slice_of(a.rkv + ((size_t)w.h * a.Tk + w.ks) * 2, w.lk, 8u, 8u);
+            wnull = slice_of(a.rkv, 0, 8u, 8u);
         }
     }
 

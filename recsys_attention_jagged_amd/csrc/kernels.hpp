@@ -80,6 +80,12 @@ GDPA_DECLARE_LAUNCHERS(64)
 GDPA_DECLARE_LAUNCHERS(128)
 #undef GDPA_DECLARE_LAUNCHERS
 
+// d = 128 dK/dV kernel on the 16 x 16 x 32 MFMA for kv items of `rows` = 32 or 64
+// rows (the dK/dV list's layouts team 1 and team 2, one block): a workgroup of
+// rows / 16 waves, 16 kv rows per wave, two waves per SIMD.  Plain GDPA
+// activations only (nullptr otherwise).
+const void* dkdv16_kernel_ptr(int rows, int act);
+
 // One-pass backward (one-wave teams, one block per wave): kv_stationary = 1 runs
 // over the dK/dV list when every Lk <= 32 (dQ stored per step), 0 over the dQ
 // list when every Lq <= 32 (dK, dV stored per step).

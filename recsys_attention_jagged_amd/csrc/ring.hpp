@@ -60,6 +60,27 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
     return row * (D * 2) + ((chunk ^ swz<D>(row)) << 4);
 }
 
+// A second swizzle for d = 128 (SW = 1), for kernels whose waves own 16-row
+// blocks: s(r) = ((r & 7) << 1) | ((r >> 3) & 1).  Over 16 rows it is a
+// permutation (16 rows x one chunk, the row operands, are conflict free), and
+// the chunk pairs {s(r) ^ 2m, s(r) ^ (2m + 1)} of any 8 consecutive rows 0..7 or
+// 8..15 are disjoint (8 rows x two adjacent chunks, the 16-column transposed
+// operands read by each half of a wave, are conflict free).
+template <int D, int SW>
+__device__ __forceinline__ int swz_sel(int row) {
+    if constexpr (SW == 1) {
+        static_assert(D == 128, "the 16-row swizzle is for d = 128");
+        return ((row & 7) << 1) | ((row >> 3) & 1);
+    } else {
+        return swz<D>(row);
+    }
+}
+
+template <int D, int SW>
+__device__ __forceinline__ int tile_off_sw(int row, int chunk) {
+    return row * (D * 2) + ((chunk ^ swz_sel<D, SW>(row)) << 4);
+}
+
 // fp8 tiles (32 rows of D one-byte values, in the first half of a slot): the
 // 16-byte chunk c of row r sits at chunk position c ^ swz8<D>(r).  Operand reads
 // take 8 bytes of one chunk in each of 32 rows; rows share a 256-byte bank window
@@ -119,21 +140,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // VGPR: the hardware range check covers the VGPR offset, not the scalar one.
 // No memory clobber: LDS reads of other slots may move across it; ordering
 // against the waits below is kept because volatile asm statements stay in order.
+// The copy takes its LDS base from m0, which the compiler reserves (it cannot be
+// declared clobbered), so the statement saves m0 in a scratch SGPR and restores
+// it after issuing the load: whatever the compiler keeps in m0 survives.
 __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rs)
-                 : "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "s"(lds), "v"(voff), "s"(rs));
 }
 
 // One wave instruction: lane l's 4 bytes at byte offset `voff` land at LDS
-// address lds + 4 l (256 bytes per instruction).  Both set m0 (the LDS base of
-// the copy) and declare it clobbered.
+// address lds + 4 l (256 bytes per instruction); m0 kept as in dma16.
 __device__ __forceinline__ void dma4(rsrc_t rs, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds), "v"(voff), "s"(rs)
-                 : "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_dword %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "s"(lds), "v"(voff), "s"(rs));
 }
 
 // s_waitcnt vmcnt(J m) for a uniform m in [0, MMAX] (the count is an immediate)
@@ -176,7 +201,7 @@ struct RingGeom {
     static_assert(R >= 4, "the ring needs a step plus look-ahead");
 };
 
-template <int D, int T, int LDS_BYTES, int XJ = 0>
+template <int D, int T, int LDS_BYTES, int XJ = 0, int SW = 0>
 struct Ring : RingGeom<D, T, LDS_BYTES, XJ> {
     using G = RingGeom<D, T, LDS_BYTES, XJ>;
     static constexpr int CPR = D / 8;   // 16-byte chunks per row
@@ -198,7 +223,7 @@ struct Ring : RingGeom<D, T, LDS_BYTES, XJ> {
         for (int jj = 0; jj < G::JW; ++jj) {
             const int slot = (jj * T + wt) * 64 + lane;
             const int row = slot / CPR, pos = slot % CPR;
-            off[jj] = (uint32_t)row * row_stride_bytes + (uint32_t)((pos ^ swz<D>(row)) << 4);
+            off[jj] = (uint32_t)row * row_stride_bytes + (uint32_t)((pos ^ swz_sel<D, SW>(row)) << 4);
         }
     }
 
@@ -222,38 +247,44 @@ struct Ring : RingGeom<D, T, LDS_BYTES, XJ> {
 
     // this wave's share of loading rows [row0, row0 + 32) of the slice `rs`
     // (row_off = row0 * stride) into the next slot
-    __device__ __forceinline__ void issue(rsrc_t rs, uint32_t row_off) {
+    __device__ __forceinline__ void issue(Slice rs, uint32_t row_off) {
         static_assert(XJ == 0, "jobs of a ring with side buffers carry a side load");
         const uint32_t lds = base + (uint32_t)(slot_of(issued) * G::TILE);
+        {
+            const rsrc_t rt = slice_at(rs, row_off);
 #pragma unroll
-        for (int jj = 0; jj < G::JW; ++jj) dma16(rs, off[jj] + row_off, lds + (uint32_t)(jj * T + wt) * 1024u);
+            for (int jj = 0; jj < G::JW; ++jj) dma16(rt, off[jj], lds + (uint32_t)(jj * T + wt) * 1024u);
+        }
         ++issued;
     }
 
     // issue() plus 256 bytes at byte offset x_off of `xs` into the slot's side
     // buffer (a zero-range `xs` fills it with zeros)
-    __device__ __forceinline__ void issue(rsrc_t rs, uint32_t row_off, rsrc_t xs, uint32_t x_off) {
+    __device__ __forceinline__ void issue(Slice rs, uint32_t row_off, Slice xs, uint32_t x_off) {
         static_assert(XJ == 1, "side loads need side buffers");
         const int slot = slot_of(issued);
         const uint32_t lds = base + (uint32_t)(slot * G::TILE);
+        {
+            const rsrc_t rt = slice_at(rs, row_off);
 #pragma unroll
-        for (int jj = 0; jj < G::JW; ++jj) dma16(rs, off[jj] + row_off, lds + (uint32_t)(jj * T + wt) * 1024u);
-        dma4(xs, x_off + xlane, base + (uint32_t)(G::R * G::TILE + slot * G::SIDE));
+            for (int jj = 0; jj < G::JW; ++jj) dma16(rt, off[jj], lds + (uint32_t)(jj * T + wt) * 1024u);
+        }
+        dma4(slice_at(xs, x_off), xlane, base + (uint32_t)(G::R * G::TILE + slot * G::SIDE));
         ++issued;
     }
 
     // an fp8 tile (32 rows, D bytes each, rows row_off8 / stride on) into the first half
     // of the next slot; the other half of this wave's instructions load a zero-range
     // descriptor (`none`), so an fp8 job counts as many instructions as a bf16 one
-    __device__ __forceinline__ void issue8(rsrc_t rs, uint32_t row_off8, rsrc_t none) {
+    __device__ __forceinline__ void issue8(Slice rs, uint32_t row_off8, Slice none) {
         static_assert(XJ == 0, "fp8 tiles without side buffers");
         static_assert(G::JW % 2 == 0, "an fp8 tile takes half of a bf16 tile's instructions");
         const uint32_t lds = base + (uint32_t)(slot_of(issued) * G::TILE);
+        const rsrc_t rt = slice_at(rs, row_off8), rz = slice_at(none, 0u);
 #pragma unroll
-        for (int jj = 0; jj < G::JW / 2; ++jj)
-            dma16(rs, off8[jj] + row_off8, lds + (uint32_t)(jj * T + wt) * 1024u);
+        for (int jj = 0; jj < G::JW / 2; ++jj) dma16(rt, off8[jj], lds + (uint32_t)(jj * T + wt) * 1024u);
 #pragma unroll
-        for (int jj = G::JW / 2; jj < G::JW; ++jj) dma16(none, 0u, lds + (uint32_t)(jj * T + wt) * 1024u);
+        for (int jj = G::JW / 2; jj < G::JW; ++jj) dma16(rz, 0u, lds + (uint32_t)(jj * T + wt) * 1024u);
         ++issued;
     }
 

@@ -177,6 +177,23 @@ def test_layouts_backward(d, tq, nb, tk):
         check_close(a, b, f"{name} d={d} tq={tq} nb={nb} tk={tk}")
 
 
+# The d = 128 dK/dV kernel's 16-row waves in two-wave (32-row items) and four-wave
+# (64-row items) teams: windows that cut a wave's rows out of some q tiles, items cut
+# into chunks (few bins), samples shorter than a team's rows, fp32 outputs.
+@pytest.mark.parametrize("tk", [1, 2])
+@pytest.mark.parametrize("window,bins", [(0, (0, 0, 0)), (5, (0, 0, 0)), (128, (0, 0, 0)), (0, (16, 16, 16)),
+                                         (40, (8, 8, 8))])
+def test_dkdv_16row_teams(tk, window, bins):
+    say(f"dK/dV 16-row waves: team={tk} window={window} bins={bins}")
+    L = [1, 15, 16, 17, 33, 47, 64, 65, 0, 300, 129, 700]
+    inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, seed=80 + tk + window, device=DEV)
+    r = oracle_bwd(inp)
+    for dtype in ("bf16", "bf16_f32out"):
+        g = run_bwd(inp, dtype=dtype, team=(0, tk, 0), bins=bins, unfused=True)
+        for name, a, b in zip(("dQ", "dK", "dV"), g, r):
+            check_close(a, b, f"{name} team={tk} window={window} bins={bins} {dtype}")
+
+
 @pytest.mark.parametrize("bins", [(1, 1, 1), (3, 5, 6), (13, 9, 7)])
 def test_few_bins_long_walks(bins):
     say(f"few bins {bins}: long per-wave walks across many items")
