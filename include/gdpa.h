@@ -102,6 +102,8 @@ typedef struct {
                         least cost so far), 1 zigzag (snake), 2 round robin */
     int no_split;    /* 1: never cut an item into chunks (see gdpa_plan_create) */
     int unfused;     /* 1: gdpa_bwd always runs the two backward kernels (see gdpa_bwd) */
+    int no_ds;       /* 1: gdpa_bwd recomputes dS in its dQ kernel instead of storing it
+                        (no dS buffer; see gdpa_plan_create) */
 } gdpa_plan_opts;
 
 /* Summary numbers of a plan. */
@@ -119,6 +121,7 @@ typedef struct {
                                 pass (every Lk <= 32), 2 one Q-stationary pass (every Lq <= 32) */
     int32_t n_parts[3];      /* partial-output slots per list (chunks of cut items; 0 for
                                 the dK/dV list) */
+    int64_t ds_bytes;        /* bytes of the plan's dS buffer (0: gdpa_bwd does not store dS) */
 } gdpa_plan_stats_t;
 
 typedef struct gdpa_plan_s* gdpa_plan;
@@ -140,6 +143,14 @@ typedef struct gdpa_plan_s* gdpa_plan;
  *                             work lists are copied to the device; ignored for a
  *                             host_only plan
  *   out                     : receives the plan (NULL on failure)
+ *
+ * For d = 128 bf16 plans whose gdpa_bwd runs the two backward kernels (and unless
+ * opts->no_ds, or a layout other than the automatic one-wave, one-block dK/dV and
+ * dQ lists is asked for), the plan also owns a dS buffer: one 32 x 32 bf16 block
+ * (2 KiB) per (head, 32-row q tile, 32-row kv tile) holding a valid pair
+ * (gdpa_plan_stats reports its size).  gdpa_bwd's dK/dV kernel stores dS there and
+ * its dQ kernel computes dQ = dS K / sqrt(d) from it instead of recomputing the
+ * scores and the activation's derivative.
  *
  * Items of the Q-stationary lists (forward, dQ) whose cost exceeds the mean
  * per-bin cost are cut into chunks of consecutive streaming tiles (unless
@@ -230,7 +241,9 @@ gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v
 /*
  * gdpa_bwd_dkdv - only dK and dV (one KV-stationary kernel); same arguments and
  * errors as gdpa_bwd without dq.  For callers whose queries are frozen or who
- * schedule the two halves of the backward pass separately.
+ * schedule the two halves of the backward pass separately.  On a plan with a dS
+ * buffer (gdpa_plan_stats: ds_bytes > 0) it also stores dS there, for
+ * gdpa_bwd_dq.
  */
 gdpa_status gdpa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
                           const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
@@ -239,6 +252,10 @@ gdpa_status gdpa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const vo
 /*
  * gdpa_bwd_dq - only dQ (one Q-stationary kernel); same arguments and errors as
  * gdpa_bwd without dk and dv.  gdpa_bwd == gdpa_bwd_dkdv followed by gdpa_bwd_dq.
+ * On a plan with a dS buffer it computes dQ from the dS that the last
+ * gdpa_bwd_dkdv on this plan stored, so it must follow that call, on the same
+ * inputs and ordered after it; a caller that needs dQ alone creates the plan with
+ * opts->no_ds (the kernel then recomputes dS).
  */
 gdpa_status gdpa_bwd_dq(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
                         const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,

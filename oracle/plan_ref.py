@@ -58,13 +58,12 @@ def auto_layout(lq, lk, window: int = 0, d: int = 128):
     """(team, nb) per list.  Forward: d = 128, two-wave teams with one block per
     wave when the mean non-empty query length is at least 48, else one wave and one
     block; d <= 64, one wave with nb = 2 when that mean is at least 64, else 1.
-    dQ: one wave, nb = 2 at d = 128 when that mean is at least 64, else 1.  dK/dV:
-    one wave, one block."""
+    dQ and dK/dV: one wave, one block.  (A tuning rule: it sets tile shapes, never
+    which pairs are computed.)"""
     n = sum(1 for x in lq if x > 0)
     mean_at_least = lambda m: n > 0 and sum(lq) >= m * n
     fwd = ((2 if mean_at_least(48) else 1), 1) if d == 128 else (1, 2 if mean_at_least(64) else 1)
-    dq = (1, 2 if d == 128 and mean_at_least(64) else 1)
-    return {"fwd": fwd, "dq": dq, "dkdv": (1, 1)}
+    return {"fwd": fwd, "dq": (1, 1), "dkdv": (1, 1)}
 
 
 def tile_sizes(kind: str, team: int, nb: int):

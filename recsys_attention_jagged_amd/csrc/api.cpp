@@ -94,6 +94,11 @@ struct gdpa_plan_s {
     float* d_part[3] = {nullptr, nullptr, nullptr};
     // pFFN plans: device copies of the offsets {0, Tq} and {0, M}
     int32_t* d_off = nullptr;
+    // stored dS of the d = 128 two-kernel backward (see DsLayout)
+    bool use_ds = false;
+    DsLayout ds;
+    __bf16* d_ds = nullptr;
+    int32_t* d_ds_tab = nullptr;
     // the device records and chunk groups of each list, resolved on the host at
     // creation (bf16 plans; the upload and gdpa_fwd_noalloc copy them from here)
     std::vector<DevRec> h_recs[3];
@@ -116,6 +121,8 @@ struct gdpa_plan_s {
             if (d_part[l]) (void)hipFree(d_part[l]);
         }
         if (d_off) (void)hipFree(d_off);
+        if (d_ds) (void)hipFree(d_ds);
+        if (d_ds_tab) (void)hipFree(d_ds_tab);
         if (h_stage) (void)hipHostFree(h_stage);
 #ifdef GDPA_BIN_CLOCK
         if (d_clock) (void)hipFree(d_clock);
@@ -137,6 +144,7 @@ static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
     }
     const int32_t off[4] = {0, (int32_t)p->Tq, 0, (int32_t)p->Tk};
     if (p->pffn) bytes += align(sizeof(off));
+    if (p->use_ds) bytes += align(p->ds.tab.size() * sizeof(int32_t));
     hipError_t e = hipHostMalloc((void**)&p->h_stage, std::max<size_t>(bytes, 256), hipHostMallocDefault);
     if (e != hipSuccess) {
         p->h_stage = nullptr;
@@ -167,6 +175,10 @@ static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
         }
     }
     if (e == hipSuccess && p->pffn) e = put((void**)&p->d_off, off, sizeof(off));
+    if (e == hipSuccess && p->use_ds) {
+        e = put((void**)&p->d_ds_tab, p->ds.tab.data(), p->ds.tab.size() * sizeof(int32_t));
+        if (e == hipSuccess) e = hipMalloc((void**)&p->d_ds, (size_t)p->ds.nb_total * p->H * 2048);
+    }
     if (e != hipSuccess)
         return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "work list upload") : fail_hip(e, "work list upload");
     return GDPA_OK;
@@ -304,13 +316,6 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split);
     }
 
-    if (dtype != GDPA_F32) {
-        for (int l = 0; l < 3; ++l) {
-            p->h_recs[l] = device_records(p->lists[l], p->q_off, p->kv_off);
-            if (p->lists[l].n_parts > 0) p->h_groups[l] = device_groups(p->lists[l], p->q_off, p->kv_off);
-        }
-    }
-
     // one-pass backward: one side of every sample fits one 32-row tile, and no
     // sample has rows on that side only (their outputs would have no item)
     if (dtype != GDPA_F32 && o.unfused == 0) {
@@ -321,6 +326,20 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
             q_ok = q_ok && lq[b] <= 32 && (lq[b] > 0 || lk[b] == 0);
         }
         p->fused = kv_ok ? 1 : q_ok ? 2 : 0;
+    }
+
+    // stored dS: the two-kernel backward at d = 128 with 32-row dK/dV and dQ items
+    if (dtype != GDPA_F32 && d == 128 && p->fused == 0 && o.no_ds == 0 && L.team[LIST_DKDV] == 1 &&
+        L.nb[LIST_DKDV] == 1 && L.team[LIST_DQ] == 1 && L.nb[LIST_DQ] == 1) {
+        p->ds = ds_layout(lq, lk, window);
+        p->use_ds = p->ds.nb_total > 0 && p->ds.nb_total * (int64_t)H < ((int64_t)1 << 31);
+    }
+    if (dtype != GDPA_F32) {
+        for (int l = 0; l < 3; ++l) {
+            p->h_recs[l] = p->use_ds ? device_records(p->lists[l], p->q_off, p->kv_off, p->ds)
+                                     : device_records(p->lists[l], p->q_off, p->kv_off);
+            if (p->lists[l].n_parts > 0) p->h_groups[l] = device_groups(p->lists[l], p->q_off, p->kv_off);
+        }
     }
 
     if (!p->host_only) {
@@ -402,6 +421,7 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
         }
     }
     out->bwd_fused = plan->fused;
+    out->ds_bytes = plan->use_ds ? plan->ds.nb_total * plan->H * 2048 : 0;
     for (int l = 0; l < 3; ++l) out->n_parts[l] = plan->lists[l].n_parts;
     return GDPA_OK;
 }
@@ -598,6 +618,33 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
         if (e == hipSuccess && !kv) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
         if (e == hipSuccess && kv) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
         if (e == hipSuccess && kv) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
+    } else if (plan->use_ds) {
+        // dK/dV storing dS, then dQ = dS K / sqrt(d) from the stored blocks (the two
+        // halves separately: gdpa_bwd_dq reads what gdpa_bwd_dkdv stored)
+        if (want_dkdv && any_k) {
+            const WorkList& wl = plan->lists[LIST_DKDV];
+            KernelArgs b = a;
+            b.items = plan->d_items[LIST_DKDV];
+            b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+            b.P = wl.P;
+            b.part = plan->d_part[LIST_DKDV];
+            b.ds = plan->d_ds;
+            b.ds_tab = plan->d_ds_tab;
+            e = launch_dkdv_bf16_d128(b, wl.team, wl.nb, act, s);
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
+        }
+        if (e == hipSuccess && want_dq && any_q) {
+            const WorkList& wl = plan->lists[LIST_DQ];
+            KernelArgs b = a;
+            b.items = plan->d_items[LIST_DQ];
+            b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+            b.P = wl.P;
+            b.part = plan->d_part[LIST_DQ];
+            b.ds = plan->d_ds;
+            e = launch_dq_from_ds(b, s);
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
+        }
     } else {
         if (want_dkdv && any_k) {
             const WorkList& wl = plan->lists[LIST_DKDV];

@@ -123,9 +123,26 @@ struct Dkdv16Pol : Common {
     template <class RingT>
     __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
         const int i0 = s * 32, j0 = krow(c);
+        // stored dS: this step's block (c.pad0 = the sample's first global q tile,
+        // c.pad1 = the head's first block), looked up per q tile
+        rsrc_t rds;
+        uint32_t ods = 0;
+        if (a.ds) {
+            const int gq = __builtin_amdgcn_readfirstlane(c.pad0 + s);
+            const int2 e = *(const int2*)(a.ds_tab + 2 * (size_t)gq);
+            const size_t blk = (size_t)c.pad1 + (size_t)(e.x + (c.t - e.y));
+            rds = slice_rsrc(a.ds + blk * 1024, 1, 2048u, 2048u);
+            ods = (uint32_t)(16 * wt + l16) * 64u + 8u * (uint32_t)g4;   // row j, q rows 4 (l / 16) ..
+        }
         // a wave whose 16 kv rows are past the sample's keys, or have no pair with this
-        // q tile in the band, skips the step
-        if (j0 >= c.lk || (win > 0 && (j0 - (i0 + 31) >= win || i0 - (j0 + 15) >= win))) return;
+        // q tile in the band, skips the step (its rows of a stored dS block are 0)
+        if (j0 >= c.lk || (win > 0 && (j0 - (i0 + 31) >= win || i0 - (j0 + 15) >= win))) {
+            if (a.ds) {
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rds, (int)ods, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rds, (int)(ods + 32u), 0, 0);
+            }
+            return;
+        }
         const char* qt = g.tile(job);
         const char* ot = g.tile(job + 1);
         // The step's LDS reads go out in batches ahead of the products that use them
@@ -183,6 +200,11 @@ struct Dkdv16Pol : Common {
                 pm[e] = (__bf16)f;
                 dm[e] = (__bf16)(dp[ib][v] * gr);
             }
+        }
+        if (a.ds) {   // dS of q rows 4 (l / 16) + {0..3} and 16 + 4 (l / 16) + {0..3}, kv row j0 + l % 16
+            const u32x4 w = __builtin_bit_cast(u32x4, dm);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rds, (int)ods, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[2], w[3]}, rds, (int)(ods + 32u), 0, 0);
         }
         // the second half's transposed operands go out before the first half's products
         bf16x8 tv2[HC], tk2[HC];
@@ -284,7 +306,157 @@ __global__ __launch_bounds__(64 * T, 2) void dkdv16_kernel(const KernelArgs a, c
     run_team<Dkdv16Pol<ACT, T>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * 128 * 2, wt, lane);
 }
 
+// =========================================================================
+// dQ from the stored dS blocks
+// =========================================================================
+// dQ_i = sum_j dS_ij K_j / sqrt(d): a banded product of the dS blocks the dK/dV
+// kernel stored (kv row major: block row j, 32 q columns) with K.  One wave per
+// workgroup walks its bin's 32-row q items; a step streams one 32-row K tile and
+// the item's dS block for that kv tile into one ring slot (ten 1 KiB loads), then
+// dQ^T += K^T dS^T with both operands read from LDS by transposing loads.  No
+// scores, activations or dO are touched: what the dK/dV kernel already computed
+// is reused, so this kernel moves dS and K and does a quarter of the products.
+struct DsRing {
+    static constexpr int D = 128;
+    static constexpr int KT = 32 * D * 2, DT = 32 * 32 * 2, SLOT = KT + DT;
+    static constexpr int JX = (KT + DT) / 1024;   // load instructions per job
+    static constexpr int R = 4;
+    static constexpr int BYTES = R * SLOT;
+    uint32_t offk[KT / 1024], offd[DT / 1024];
+    uint32_t base;
+    char* gbase;
+    int issued;
+
+    __device__ __forceinline__ void init(char* slice, uint32_t row_stride, int lane) {
+        gbase = slice;
+        base = lds_addr(slice);
+        issued = 0;
+#pragma unroll
+        for (int jj = 0; jj < KT / 1024; ++jj) {   // K: rows of 16 chunks, swz<128>
+            const int slot = jj * 64 + lane, row = slot / 16, pos = slot % 16;
+            offk[jj] = (uint32_t)row * row_stride + (uint32_t)((pos ^ swz<D>(row)) << 4);
+        }
+#pragma unroll
+        for (int jj = 0; jj < DT / 1024; ++jj) {   // dS block: 64-byte rows of 4 chunks, swz<32>
+            const int slot = jj * 64 + lane, row = slot / 4, pos = slot % 4;
+            offd[jj] = (uint32_t)row * 64u + (uint32_t)((pos ^ swz<32>(row)) << 4);
+        }
+    }
+    __device__ __forceinline__ char* ktile(int job) const { return gbase + (job % R) * SLOT; }
+    __device__ __forceinline__ char* dtile(int job) const { return ktile(job) + KT; }
+    // K rows [row0, row0 + 32) of the slice (k_off = row0 * stride) and the 2 KiB dS
+    // block `blk` into the next slot
+    __device__ __forceinline__ void issue(Slice k, uint32_t k_off, rsrc_t blk) {
+        const uint32_t lds = base + (uint32_t)((issued % R) * SLOT);
+        const rsrc_t rk = slice_at(k, k_off);
+#pragma unroll
+        for (int jj = 0; jj < KT / 1024; ++jj) dma16(rk, offk[jj], lds + (uint32_t)jj * 1024u);
+#pragma unroll
+        for (int jj = 0; jj < DT / 1024; ++jj) dma16(blk, offd[jj], lds + (uint32_t)(KT + jj * 1024));
+        ++issued;
+    }
+    __device__ __forceinline__ void wait(int k) const { wait_jobs<JX>(issued - 1 - k); }
+};
+
+struct DqDsPol : Common {
+    static constexpr int D = 128, NDB = D / 32;
+    f32x16 acc[NDB];
+
+    __device__ DqDsPol(const KernelArgs& args, int lane_) : Common(args, lane_, 0, D) {}
+
+    // the job of step s of item w: K tile s and dS block w.pad0 + (s - w.s0)
+    __device__ __forceinline__ void issue(DsRing& g, const Rec& w, int s) const {
+        const Slice k = slice_of((const __bf16*)a.k + ((size_t)w.ks * H + w.h) * D, w.lk, rs, D * 2);
+        const size_t blk = (size_t)w.pad0 + (size_t)(s - w.s0);
+        g.issue(k, (uint32_t)(s * 32) * rs, slice_rsrc(a.ds + blk * 1024, 1, 2048u, 2048u));
+    }
+
+    __device__ __forceinline__ void step(const DsRing& g, int job) {
+        const char* kt = g.ktile(job);
+        const char* dt = g.dtile(job);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            // dS^T operand: kv rows 16 m + {0..3, 8..11} + 4 (l / 32) of q column l % 32
+            const bf16x8 b = lds_col8<32>(dt, 16 * m, 0, lane);
+            bf16x8 kop[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) kop[db] = lds_col8<D>(kt, 16 * m, db * 32, lane);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = mfma32(kop[db], b, acc[db]);
+        }
+    }
+};
+
+__global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, const Rec* __restrict__ recs,
+                                                          const int32_t* __restrict__ bin_ptr) {
+    __shared__ __attribute__((aligned(1024))) char smem[DsRing::BYTES];
+    const int lane = threadIdx.x;
+    const int bin = team_bin();
+    if (bin >= a.P) return;
+    const int beg = bin_ptr[bin], end = bin_ptr[bin + 1];
+    if (beg >= end) return;
+    DqDsPol pol(a, lane);
+    DsRing ring;
+    ring.init(smem, (uint32_t)a.H * 128 * 2, lane);
+    // issuing side: the item and step of the next job (items without steps have none)
+    int wi = beg, ws = 0;
+    Rec wr = recs[beg];
+    while (wi < end && wr.s1 < wr.s0)
+        if (++wi < end) wr = recs[__builtin_amdgcn_readfirstlane(wi)];
+    ws = wr.s0;
+    int job = 0;
+    auto pump = [&](int consumed) {
+        while (wi < end && ring.issued < consumed + DsRing::R) {
+            pol.issue(ring, wr, ws);
+            if (++ws > wr.s1) {
+                do {
+                    if (++wi < end) wr = recs[__builtin_amdgcn_readfirstlane(wi)];
+                } while (wi < end && wr.s1 < wr.s0);
+                ws = wr.s0;
+            }
+        }
+    };
+    pump(job);
+    for (int ci = beg; ci < end; ++ci) {
+        const Rec c = recs[ci];
+        const size_t ob = ((size_t)c.qs * pol.H + c.h) * 128;
+        if (c.s1 < c.s0) {
+            pol.zero<128>(a.dq, ob, c.lq, c.t * 32);
+            continue;
+        }
+#pragma unroll
+        for (int db = 0; db < DqDsPol::NDB; ++db) pol.acc[db] = f32x16{};
+        for (int s = c.s0; s <= c.s1; ++s) {
+            ring.wait(job);
+            wait_lds();   // this wave is done reading the slot the pump re-fills next
+            pump(job);
+            pol.step(ring, job);
+            ++job;
+        }
+        wait_lds();
+        if (c.part >= 0) {
+            store_partial<DqDsPol::NDB>(pol.acc, a.part, c.part, 32, 0, pol.r, pol.hh);
+            continue;
+        }
+        // staged through the K tile of the item's last step: the pump re-fills a
+        // slot only at the next consume point, after that step's reads
+        pol.store<128>(pol.acc, pol.scale, a.dq, ob, c.lq, c.t * 32, ring.ktile(job - 1));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_dq_from_ds(const KernelArgs& a, hipStream_t s) {
+    if (a.P <= 0) return hipSuccess;
+    if (!a.ds) return hipErrorInvalidValue;
+    KernelArgs args = a;
+    const void* recs = a.items;
+    const int32_t* bin_ptr = a.bin_ptr;
+    void* params[] = {&args, &recs, &bin_ptr};
+    return hipLaunchKernel((const void*)&dq_from_ds_kernel, dim3(a.P), dim3(64), params, 0, s);
+}
+
+const void* dq_from_ds_kernel_ptr() { return (const void*)&dq_from_ds_kernel; }
 
 template <int T>
 const void* dkdv16_ptr(int act) {

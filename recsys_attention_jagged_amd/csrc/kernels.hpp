@@ -47,6 +47,11 @@ struct KernelArgs {
     const float* rkv;
     int Tk;
     int norm;
+    // stored dS (d = 128 two-kernel backward): 32 x 32 bf16 blocks (kv row major)
+    // that the dK/dV kernel writes and the dQ kernel reads, and per global 32-row
+    // q tile the pair (first block of its run, first kv tile); see DsLayout
+    __bf16* ds;
+    const int32_t* ds_tab;
 #ifdef GDPA_BIN_CLOCK
     // clock-probe builds only: per bin, the real-time stamps (100 MHz) of the start and
     // the end of its walk, [P][2]
@@ -85,6 +90,11 @@ GDPA_DECLARE_LAUNCHERS(128)
 // rows / 16 waves, 16 kv rows per wave, two waves per SIMD.  Plain GDPA
 // activations only (nullptr otherwise).
 const void* dkdv16_kernel_ptr(int rows, int act);
+
+// d = 128 dQ from the stored dS blocks: dQ = dS K / sqrt(d) over the dQ list of
+// 32-row q items (one wave per workgroup); a.ds, a.items: that list, a.part its slots
+hipError_t launch_dq_from_ds(const KernelArgs& a, hipStream_t s);
+const void* dq_from_ds_kernel_ptr();
 
 // One-pass backward (one-wave teams, one block per wave): kv_stationary = 1 runs
 // over the dK/dV list when every Lk <= 32 (dQ stored per step), 0 over the dQ

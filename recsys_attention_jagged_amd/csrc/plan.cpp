@@ -21,12 +21,11 @@ Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>&, 
     Layout L;
     if (d == 128) {
         // two-wave forward teams once the queries are long enough to fill them;
-        // two dQ blocks per wave once they fill 64 rows
+        // 32-row dQ and dK/dV items (the backward's stored-dS blocks)
         L.team[LIST_FWD] = mean_at_least(sq, nq, 48) ? 2 : 1;
         L.nb[LIST_FWD] = 1;
         L.team[LIST_DQ] = L.team[LIST_DKDV] = 1;
-        L.nb[LIST_DQ] = mean_at_least(sq, nq, 64) ? 2 : 1;
-        L.nb[LIST_DKDV] = 1;
+        L.nb[LIST_DQ] = L.nb[LIST_DKDV] = 1;
     } else {
         L.team[LIST_FWD] = L.team[LIST_DQ] = L.team[LIST_DKDV] = 1;
         L.nb[LIST_FWD] = mean_at_least(sq, nq, 64) ? 2 : 1;
@@ -199,6 +198,52 @@ std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t
         d.s1 = it.s1;
         d.part = it.part;
         d.pad0 = d.pad1 = d.pad2 = 0;
+    }
+    return out;
+}
+
+DsLayout ds_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk, int window) {
+    DsLayout L;
+    L.qt_prefix.assign(lq.size() + 1, 0);
+    for (size_t b = 0; b < lq.size(); ++b) L.qt_prefix[b + 1] = L.qt_prefix[b] + (int32_t)ceil_div(lq[b], 32);
+    L.tab.assign(2 * (size_t)L.qt_prefix.back(), 0);
+    int64_t total = 0;
+    for (size_t b = 0; b < lq.size(); ++b) {
+        for (int64_t i = 0; i < ceil_div(lq[b], 32); ++i) {
+            // the kv tiles of q tile i with a valid pair (the rule plan_list applies)
+            int64_t js0 = 0, js1 = -1;
+            if (lk[b] > 0) {
+                if (window == 0) {
+                    js1 = ceil_div(lk[b], 32) - 1;
+                } else {
+                    const int64_t a0 = 32 * i, a1 = std::min(lq[b], a0 + 32) - 1;
+                    js0 = std::max<int64_t>(0, a0 - window + 1) / 32;
+                    js1 = std::min<int64_t>(lk[b] - 1, a1 + window - 1) / 32;
+                }
+            }
+            const size_t gq = (size_t)L.qt_prefix[b] + (size_t)i;
+            L.tab[2 * gq] = (int32_t)total;
+            L.tab[2 * gq + 1] = (int32_t)js0;
+            total += js1 - js0 + 1;
+        }
+    }
+    L.nb_total = total;
+    return L;
+}
+
+std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
+                                   const std::vector<int32_t>& kv_off, const DsLayout& ds) {
+    std::vector<DevRec> out = device_records(wl, q_off, kv_off);
+    for (size_t i = 0; i < wl.items.size(); ++i) {
+        const Item& it = wl.items[i];
+        DevRec& d = out[i];
+        if (wl.kind == LIST_DKDV) {
+            d.pad0 = ds.qt_prefix[it.b];
+            d.pad1 = (int32_t)(it.h * ds.nb_total);
+        } else if (wl.kind == LIST_DQ && it.s1 >= it.s0) {
+            const size_t gq = (size_t)ds.qt_prefix[it.b] + (size_t)it.t;
+            d.pad0 = (int32_t)(it.h * ds.nb_total + ds.tab[2 * gq] + (it.s0 - ds.tab[2 * gq + 1]));
+        }
     }
     return out;
 }

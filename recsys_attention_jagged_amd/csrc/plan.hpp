@@ -80,8 +80,24 @@ void tile_sizes(int kind, int team, int nb, int* t_stat, int* t_strm);
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
                    int H, int window, int P, int team, int nb, int deal, bool split);
 std::vector<int32_t> export_list(const WorkList& wl);
+// dS blocks of the two-kernel backward with stored scores' gradients: one 32 x 32
+// bf16 block (2 KiB, kv row major) per (head, 32-row q tile, 32-row kv tile) that
+// holds a valid pair.  Per head, blocks run over the global q tiles in order
+// (sample by sample), each q tile's blocks over its kv tiles js0 .. js1 in order:
+// block(h, gq, j) = h nb_total + base(gq) + (j - js0(gq)), gq = qt_prefix[b] + i.
+struct DsLayout {
+    int64_t nb_total = 0;             // blocks per head
+    std::vector<int32_t> qt_prefix;   // B + 1: first global q tile of each sample
+    std::vector<int32_t> tab;         // per global q tile: (base, js0)
+};
+DsLayout ds_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk, int window);
+
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
                                    const std::vector<int32_t>& kv_off);
+// with a dS layout: the dK/dV list's records carry (pad0, pad1) = (qt_prefix[b], h nb_total),
+// the dQ list's (32-row q items) pad0 = the block of the item's first step
+std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
+                                   const std::vector<int32_t>& kv_off, const DsLayout& ds);
 // the cut items of a list, in slot order (output rows: queries, or keys for dK/dV)
 std::vector<DevGroup> device_groups(const WorkList& wl, const std::vector<int32_t>& q_off,
                                     const std::vector<int32_t>& kv_off);

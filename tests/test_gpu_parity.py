@@ -194,6 +194,41 @@ def test_dkdv_16row_teams(tk, window, bins):
             check_close(a, b, f"{name} team={tk} window={window} bins={bins} {dtype}")
 
 
+# d = 128 two-kernel backward with stored dS: the dK/dV kernel stores each 32 x 32 dS
+# block, the dQ kernel multiplies the stored blocks by K
+@pytest.mark.parametrize("window,bins", [(0, (0, 0, 0)), (9, (0, 0, 0)), (128, (0, 0, 0)), (0, (16, 16, 16)),
+                                         (40, (8, 8, 8))])
+@pytest.mark.parametrize("dtype", ["bf16", "bf16_f32out"])
+def test_stored_ds_backward(window, bins, dtype):
+    say(f"stored dS backward window={window} bins={bins} {dtype}")
+    L = [1, 15, 16, 17, 33, 47, 64, 65, 0, 300, 129, 700]
+    inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, seed=90 + window, device=DEV)
+    qo, ko = dev_offsets(inp)
+    r = oracle_bwd(inp)
+    with G.Plan(inp.q_off, inp.kv_off, 2, 128, window, dtype, bins=bins, unfused=True) as plan:
+        assert plan.stats()["ds_bytes"] > 0
+        whole = [t.float().cpu().numpy() for t in plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "gelu")]
+        odt = torch.float32 if dtype == "bf16_f32out" else torch.bfloat16
+        dq = torch.full(inp.q.shape, float("nan"), dtype=odt, device=DEV)
+        dk = torch.full(inp.k.shape, float("nan"), dtype=odt, device=DEV)
+        dv = torch.full(inp.v.shape, float("nan"), dtype=odt, device=DEV)
+        args = (plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, plan.B, 2, 128, "gelu", window)
+        G.gdpa_bwd_dkdv(*args, dk, dv)
+        G.gdpa_bwd_dq(*args, dq)
+        torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), whole, r):
+        check_close(a, b, f"{name} stored dS window={window} bins={bins} {dtype}")
+    for name, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), whole):
+        assert np.array_equal(a.float().cpu().numpy(), b), f"{name}: split calls differ from gdpa_bwd"
+    # without a dS buffer, dQ alone recomputes dS
+    with G.Plan(inp.q_off, inp.kv_off, 2, 128, window, dtype, bins=bins, unfused=True, store_ds=False) as plan:
+        assert plan.stats()["ds_bytes"] == 0
+        dq2 = torch.empty(inp.q.shape, dtype=torch.float32 if dtype == "bf16_f32out" else torch.bfloat16, device=DEV)
+        G.gdpa_bwd_dq(plan.handle, inp.q, inp.k, inp.v, inp.do, qo, ko, plan.B, 2, 128, "gelu", window, dq2)
+        torch.cuda.synchronize()
+    check_close(dq2.float().cpu().numpy(), r[0], f"dQ alone window={window} {dtype}")
+
+
 @pytest.mark.parametrize("bins", [(1, 1, 1), (3, 5, 6), (13, 9, 7)])
 def test_few_bins_long_walks(bins):
     say(f"few bins {bins}: long per-wave walks across many items")

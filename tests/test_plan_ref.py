@@ -103,12 +103,12 @@ def test_greedy_deal_is_least_loaded_first(P):
 def test_auto_layout_rules():
     # d = 128: two-wave forward teams from a mean query length of 48, one block per wave
     assert PR.auto_layout([32] * 8, [1000] * 8, 0, 128) == {"fwd": (1, 1), "dq": (1, 1), "dkdv": (1, 1)}
-    assert PR.auto_layout([300] * 8, [32] * 8, 0, 128) == {"fwd": (2, 1), "dq": (1, 2), "dkdv": (1, 1)}
+    assert PR.auto_layout([300] * 8, [32] * 8, 0, 128) == {"fwd": (2, 1), "dq": (1, 1), "dkdv": (1, 1)}
     assert PR.auto_layout([47, 49, 0], [5] * 3, 0, 128)["fwd"] == (2, 1)
     assert PR.auto_layout([47, 48, 0], [5] * 3, 0, 128)["fwd"] == (1, 1)
-    # d = 128: two dQ blocks per wave from a mean query length of 64
-    assert PR.auto_layout([63, 65, 0], [5] * 3, 0, 128)["dq"] == (1, 2)
-    assert PR.auto_layout([63, 64, 0], [5] * 3, 0, 128)["dq"] == (1, 1)
+    # dQ: one block per wave at every d (d = 128: the stored-dS blocks are 32 rows)
+    assert PR.auto_layout([63, 65, 0], [5] * 3, 0, 128)["dq"] == (1, 1)
+    assert PR.auto_layout([300, 900], [5] * 2, 0, 128)["dq"] == (1, 1)
     assert PR.auto_layout([63, 65, 0], [5] * 3, 0, 64)["dq"] == (1, 1)
     # d <= 64: one-wave teams, two forward blocks from a mean query length of 64
     assert PR.auto_layout([63, 65, 0], [70] * 3, 0, 64) == {"fwd": (1, 2), "dq": (1, 1), "dkdv": (1, 1)}
