@@ -98,7 +98,6 @@ struct gdpa_plan_s {
     bool use_ds = false;
     DsLayout ds;
     __bf16* d_ds = nullptr;
-    int32_t* d_ds_tab = nullptr;
     // the device records and chunk groups of each list, resolved on the host at
     // creation (bf16 plans; the upload and gdpa_fwd_noalloc copy them from here)
     std::vector<DevRec> h_recs[3];
@@ -122,7 +121,6 @@ struct gdpa_plan_s {
         }
         if (d_off) (void)hipFree(d_off);
         if (d_ds) (void)hipFree(d_ds);
-        if (d_ds_tab) (void)hipFree(d_ds_tab);
         if (h_stage) (void)hipHostFree(h_stage);
 #ifdef GDPA_BIN_CLOCK
         if (d_clock) (void)hipFree(d_clock);
@@ -144,7 +142,6 @@ static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
     }
     const int32_t off[4] = {0, (int32_t)p->Tq, 0, (int32_t)p->Tk};
     if (p->pffn) bytes += align(sizeof(off));
-    if (p->use_ds) bytes += align(p->ds.tab.size() * sizeof(int32_t));
     hipError_t e = hipHostMalloc((void**)&p->h_stage, std::max<size_t>(bytes, 256), hipHostMallocDefault);
     if (e != hipSuccess) {
         p->h_stage = nullptr;
@@ -176,8 +173,7 @@ static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
     }
     if (e == hipSuccess && p->pffn) e = put((void**)&p->d_off, off, sizeof(off));
     if (e == hipSuccess && p->use_ds) {
-        e = put((void**)&p->d_ds_tab, p->ds.tab.data(), p->ds.tab.size() * sizeof(int32_t));
-        if (e == hipSuccess) e = hipMalloc((void**)&p->d_ds, (size_t)p->ds.nb_total * p->H * 2048);
+        e = hipMalloc((void**)&p->d_ds, (size_t)p->ds.nb_total * p->H * 2048);
     }
     if (e != hipSuccess)
         return e == hipErrorOutOfMemory ? fail(GDPA_ERR_NOMEM, "work list upload") : fail_hip(e, "work list upload");
@@ -336,7 +332,7 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
     }
     if (dtype != GDPA_F32) {
         for (int l = 0; l < 3; ++l) {
-            p->h_recs[l] = p->use_ds ? device_records(p->lists[l], p->q_off, p->kv_off, p->ds)
+            p->h_recs[l] = p->use_ds ? device_records(p->lists[l], p->q_off, p->kv_off, p->ds, window)
                                      : device_records(p->lists[l], p->q_off, p->kv_off);
             if (p->lists[l].n_parts > 0) p->h_groups[l] = device_groups(p->lists[l], p->q_off, p->kv_off);
         }
@@ -629,7 +625,6 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.P = wl.P;
             b.part = plan->d_part[LIST_DKDV];
             b.ds = plan->d_ds;
-            b.ds_tab = plan->d_ds_tab;
             e = launch_dkdv_bf16_d128(b, wl.team, wl.nb, act, s);
             if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
             if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);

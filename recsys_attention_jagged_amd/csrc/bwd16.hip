@@ -123,14 +123,14 @@ struct Dkdv16Pol : Common {
     template <class RingT>
     __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
         const int i0 = s * 32, j0 = krow(c);
-        // stored dS: this step's block (c.pad0 = the sample's first global q tile,
-        // c.pad1 = the head's first block), looked up per q tile
+        // stored dS: this step's block, c.pad0 + s c.pad1 + (t - js0(s)) (c.pad0 = the
+        // sample's first block of this head, c.pad1 = blocks per q tile, js0(s) = the
+        // q tile's first kv tile in the band)
         rsrc_t rds;
         uint32_t ods = 0;
         if (a.ds) {
-            const int gq = __builtin_amdgcn_readfirstlane(c.pad0 + s);
-            const int2 e = *(const int2*)(a.ds_tab + 2 * (size_t)gq);
-            const size_t blk = (size_t)c.pad1 + (size_t)(e.x + (c.t - e.y));
+            const int js0 = win > 0 ? max(0, i0 - win + 1) >> 5 : 0;
+            const size_t blk = (size_t)c.pad0 + (size_t)s * (size_t)c.pad1 + (size_t)(c.t - js0);
             rds = slice_rsrc(a.ds + blk * 1024, 1, 2048u, 2048u);
             ods = (uint32_t)(16 * wt + l16) * 64u + 8u * (uint32_t)g4;   // row j, q rows 4 (l / 16) ..
         }

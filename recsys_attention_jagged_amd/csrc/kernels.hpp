@@ -48,10 +48,9 @@ struct KernelArgs {
     int Tk;
     int norm;
     // stored dS (d = 128 two-kernel backward): 32 x 32 bf16 blocks (kv row major)
-    // that the dK/dV kernel writes and the dQ kernel reads, and per global 32-row
-    // q tile the pair (first block of its run, first kv tile); see DsLayout
+    // that the dK/dV kernel writes and the dQ kernel reads; records locate them
+    // (see DsLayout)
     __bf16* ds;
-    const int32_t* ds_tab;
 #ifdef GDPA_BIN_CLOCK
     // clock-probe builds only: per bin, the real-time stamps (100 MHz) of the start and
     // the end of its walk, [P][2]

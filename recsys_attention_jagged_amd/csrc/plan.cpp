@@ -202,47 +202,47 @@ std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t
     return out;
 }
 
+// first kv tile with a pair for 32-row q tile i (the band rule plan_list applies)
+static int64_t ds_js0(int64_t i, int window) {
+    return window == 0 ? 0 : std::max<int64_t>(0, 32 * i - window + 1) / 32;
+}
+
 DsLayout ds_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk, int window) {
     DsLayout L;
-    L.qt_prefix.assign(lq.size() + 1, 0);
-    for (size_t b = 0; b < lq.size(); ++b) L.qt_prefix[b + 1] = L.qt_prefix[b] + (int32_t)ceil_div(lq[b], 32);
-    L.tab.assign(2 * (size_t)L.qt_prefix.back(), 0);
+    L.base.assign(lq.size(), 0);
+    L.nj.assign(lq.size(), 0);
     int64_t total = 0;
     for (size_t b = 0; b < lq.size(); ++b) {
-        for (int64_t i = 0; i < ceil_div(lq[b], 32); ++i) {
-            // the kv tiles of q tile i with a valid pair (the rule plan_list applies)
-            int64_t js0 = 0, js1 = -1;
-            if (lk[b] > 0) {
-                if (window == 0) {
-                    js1 = ceil_div(lk[b], 32) - 1;
-                } else {
-                    const int64_t a0 = 32 * i, a1 = std::min(lq[b], a0 + 32) - 1;
-                    js0 = std::max<int64_t>(0, a0 - window + 1) / 32;
-                    js1 = std::min<int64_t>(lk[b] - 1, a1 + window - 1) / 32;
-                }
+        const int64_t ntq = ceil_div(lq[b], 32);
+        int64_t nj = 0;
+        if (lk[b] > 0) {
+            for (int64_t i = 0; i < ntq; ++i) {
+                const int64_t a1 = std::min(lq[b], 32 * i + 32) - 1;
+                const int64_t js1 = window == 0 ? ceil_div(lk[b], 32) - 1
+                                                : std::min<int64_t>(lk[b] - 1, a1 + window - 1) / 32;
+                nj = std::max(nj, js1 - ds_js0(i, window) + 1);
             }
-            const size_t gq = (size_t)L.qt_prefix[b] + (size_t)i;
-            L.tab[2 * gq] = (int32_t)total;
-            L.tab[2 * gq + 1] = (int32_t)js0;
-            total += js1 - js0 + 1;
         }
+        L.base[b] = total;
+        L.nj[b] = (int32_t)nj;
+        total += ntq * nj;
     }
     L.nb_total = total;
     return L;
 }
 
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
-                                   const std::vector<int32_t>& kv_off, const DsLayout& ds) {
+                                   const std::vector<int32_t>& kv_off, const DsLayout& ds, int window) {
     std::vector<DevRec> out = device_records(wl, q_off, kv_off);
     for (size_t i = 0; i < wl.items.size(); ++i) {
         const Item& it = wl.items[i];
         DevRec& d = out[i];
+        const int64_t head = it.h * ds.nb_total + ds.base[it.b];
         if (wl.kind == LIST_DKDV) {
-            d.pad0 = ds.qt_prefix[it.b];
-            d.pad1 = (int32_t)(it.h * ds.nb_total);
+            d.pad0 = (int32_t)head;
+            d.pad1 = ds.nj[it.b];
         } else if (wl.kind == LIST_DQ && it.s1 >= it.s0) {
-            const size_t gq = (size_t)ds.qt_prefix[it.b] + (size_t)it.t;
-            d.pad0 = (int32_t)(it.h * ds.nb_total + ds.tab[2 * gq] + (it.s0 - ds.tab[2 * gq + 1]));
+            d.pad0 = (int32_t)(head + (int64_t)it.t * ds.nj[it.b] + (it.s0 - ds_js0(it.t, window)));
         }
     }
     return out;

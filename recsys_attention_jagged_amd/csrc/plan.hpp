@@ -82,22 +82,26 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
 std::vector<int32_t> export_list(const WorkList& wl);
 // dS blocks of the two-kernel backward with stored scores' gradients: one 32 x 32
 // bf16 block (2 KiB, kv row major) per (head, 32-row q tile, 32-row kv tile) that
-// holds a valid pair.  Per head, blocks run over the global q tiles in order
-// (sample by sample), each q tile's blocks over its kv tiles js0 .. js1 in order:
-// block(h, gq, j) = h nb_total + base(gq) + (j - js0(gq)), gq = qt_prefix[b] + i.
+// holds a valid pair.  Per head, samples follow each other; a sample gives each of
+// its q tiles nj[b] consecutive blocks (nj[b] = the most kv tiles any of its q tiles
+// pairs with), q tile i's blocks holding its kv tiles js0(i), js0(i) + 1, .. in order:
+//   block(h, b, i, j) = h nb_total + base[b] + i nj[b] + (j - js0(i)),
+//   js0(i) = max(0, 32 i - window + 1) / 32 for a window, else 0,
+// so both kernels find a block by arithmetic on their record (no table).
 struct DsLayout {
     int64_t nb_total = 0;             // blocks per head
-    std::vector<int32_t> qt_prefix;   // B + 1: first global q tile of each sample
-    std::vector<int32_t> tab;         // per global q tile: (base, js0)
+    std::vector<int64_t> base;        // B: first block of each sample
+    std::vector<int32_t> nj;          // B: blocks per q tile of each sample
 };
 DsLayout ds_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk, int window);
 
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
                                    const std::vector<int32_t>& kv_off);
-// with a dS layout: the dK/dV list's records carry (pad0, pad1) = (qt_prefix[b], h nb_total),
-// the dQ list's (32-row q items) pad0 = the block of the item's first step
+// with a dS layout: the dK/dV list's records carry (pad0, pad1) = (h nb_total + base[b], nj[b]),
+// the dQ list's (32-row q items) pad0 = the block of the item's first step (its steps'
+// blocks follow it)
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
-                                   const std::vector<int32_t>& kv_off, const DsLayout& ds);
+                                   const std::vector<int32_t>& kv_off, const DsLayout& ds, int window);
 // the cut items of a list, in slot order (output rows: queries, or keys for dK/dV)
 std::vector<DevGroup> device_groups(const WorkList& wl, const std::vector<int32_t>& q_off,
                                     const std::vector<int32_t>& kv_off);
