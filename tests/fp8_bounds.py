@@ -1,0 +1,51 @@
+"""Stated error bounds of the fp8 paths against the oracle run on the bf16 inputs.
+
+The fp8 paths take Q and K (and, in the backward, dO) as OCP e4m3 bytes with one
+scale per tensor (amax / 448, so the largest element maps to the format's
+largest finite value).  Rounding to e4m3 (three mantissa bits) leaves each
+element in the normal range a relative error below 2^-4, uniform within half an
+ulp: with the significand m log-uniform on [1, 2), its rms is
+2^-3 / sqrt(12) * E[m^-2]^(1/2) = 0.0266.  A score q . k / sqrt(d) of unit-rms
+rows gets an error of rms sqrt(2) * 0.0266 = 0.038 from its two operands; it
+reaches O through act'(S), and a gradient through one more quantised operand
+(dO, Q or K), about sqrt(3) * 0.0266 = 0.046 relative.  The oracle measures
+0.037 .. 0.047 relative L2 (O, dQ, dK, dV) on the four bf16 workloads, with
+largest errors up to 0.053 of max |ref|.  The bounds below add the kernels' own
+bf16 bounds against the oracle on the quantised values (1e-2 relative L2, 2e-2
+of max |ref|) to 0.06 and 0.08, which hold the quantisation's share with room
+(the error against the bf16 inputs is at most the sum of the two, by the
+triangle inequality).
+"""
+import numpy as np
+
+FP8_REL_L2 = 7e-2   # relative L2 error, per output
+FP8_MAX = 1e-1      # max abs error / max |reference|, per output
+# the kernels' own bounds against the oracle on the values the bytes stand for
+KERNEL_REL_L2, KERNEL_MAX = 1e-2, 2e-2
+E4M3_MAX = 448.0
+
+
+def quant_e4m3(x):
+    """(bytes as torch float8_e4m3fn, scale) with scale = amax / 448 (1 for an all-zero tensor)."""
+    import torch
+    x = x.float().cpu()
+    s = float(x.abs().max()) / E4M3_MAX if x.numel() else 1.0
+    s = s if s > 0 else 1.0
+    return (x / s).to(torch.float8_e4m3fn), s
+
+
+def fp8_errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    nrm = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(err)) / nrm if nrm > 0 else float(np.linalg.norm(err))
+    mx = float(np.abs(ref).max()) if ref.size else 0.0
+    return rel, (float(err.max()) / mx if mx > 0 else float(err.max(initial=0.0)))
+
+
+def check_fp8(got, ref, what):
+    assert np.all(np.isfinite(np.asarray(got, dtype=np.float64))), f"{what}: non-finite values"
+    rel, mx = fp8_errors(got, ref)
+    assert rel <= FP8_REL_L2, f"{what}: rel L2 {rel:.3e} > {FP8_REL_L2}"
+    assert mx <= FP8_MAX, f"{what}: max err {mx:.3e} of max|ref| > {FP8_MAX}"

@@ -21,6 +21,7 @@ import recsys_attention_jagged_amd as G
 from gdpa_workloads import WORKLOADS, make_from_lengths, make_pffn, make_workload, offsets
 from oracle import gdpa_ref as R
 from oracle import plan_ref as PR
+from fp8_bounds import check_fp8, quant_e4m3
 
 pytestmark = pytest.mark.gpu
 
@@ -308,15 +309,6 @@ def test_cut_items(d, case, deal):
 # fp8 (e4m3fn) Q and K in the forward
 # ---------------------------------------------------------------------------
 
-def quant_e4m3(t):
-    """Per-tensor scale amax / 448 and OCP e4m3fn bytes (quantised on the host by torch)."""
-    x = t.float().cpu()
-    s = float(x.abs().max()) / 448.0 if x.numel() else 1.0
-    s = s if s > 0 else 1.0
-    q8 = (x / s).to(torch.float8_e4m3fn)
-    return q8, s
-
-
 def run_fp8_fwd(inp, act=None, dtype="bf16", **opts):
     act = act or inp.act
     qo, ko = dev_offsets(inp)
@@ -359,6 +351,17 @@ def test_fp8_forward_cut_items():
     o, ref, n_parts = run_fp8_fwd(inp, bins=(16, 16, 16))
     assert n_parts[0] > 0
     check_close(o, ref, "fp8 O cut")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_fp8_forward_against_bf16_inputs(cfg):
+    """What quantising costs a caller: the fp8 forward on e4m3 Q, K (per-tensor
+    scales) against the oracle on the bf16 inputs, within the stated fp8 bounds."""
+    say(f"cfg{cfg} fp8 forward vs the bf16-input oracle, B={SMALL_B[cfg]}")
+    inp = make_workload(cfg, device=DEV, B=SMALL_B[cfg])
+    o, ref_q, _ = run_fp8_fwd(inp)
+    check_close(o, ref_q, f"cfg{cfg} fp8 O vs the quantised values")
+    check_fp8(o, oracle_fwd(inp), f"cfg{cfg} fp8 O vs the bf16 inputs")
 
 
 def test_fp8_forward_rejects():
