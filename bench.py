@@ -79,19 +79,23 @@ def kernel_flops(H, d, pairs, Tq=0, Tk=0):
             "rstd": 2.0 * H * d * (Tq + 2 * Tk)}
 
 
-def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False):
+def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0):
     """Algorithmic bytes per launch (bf16): every input read once, every output written
     once; softmax (JFA): plus the fp32 row LSE written by the forward, and the fp32
     (LSE, D) row pair that the pre-pass writes and the gradient kernels read; norm
     (RMSNorm prologue): plus the fp32 1/rms factors (H (Tq + 2 Tk)) that the rstd
-    pre-pass writes, after reading the tensors it normalises, and the kernels read."""
+    pre-pass writes, after reading the tensors it normalises, and the kernels read;
+    ds_bytes (a plan that stores dS): the dK/dV kernel also writes the dS blocks, and
+    the dQ kernel reads them and K instead of recomputing the scores."""
     e = 2 * H * d
     lse, st = (4 * H * Tq, 8 * H * Tq) if softmax else (0, 0)
     rs = 4 * H * (Tq + 2 * Tk) if norm else 0
     qk = 0.5 if fp8 else 1.0                           # fp8 Q, K: one byte per element
+    dq = (e * (Tq + Tk) + ds_bytes if ds_bytes else   # dS, K -> dQ
+          e * (3 * Tq + 2 * Tk) + (e * Tq + lse if softmax else 0) + st + rs)   # Q, dO, K, V (+ O, LSE) -> dQ
     return {"fwd": int(e * (qk * Tq + qk * Tk + Tk + Tq)) + lse + rs,   # Q, K, V (, rstd) -> O (, LSE)
-            "dkdv": e * (2 * Tq + 4 * Tk) + st + rs,    # Q, dO, K, V (, stat or rstd) -> dK, dV
-            "dq": e * (3 * Tq + 2 * Tk) + (e * Tq + lse if softmax else 0) + st + rs,   # (+ O, LSE) -> dQ (, stat)
+            "dkdv": e * (2 * Tq + 4 * Tk) + st + rs + ds_bytes,   # Q, dO, K, V (, stat or rstd) -> dK, dV (, dS)
+            "dq": dq,
             "bwd": e * (3 * Tq + 4 * Tk),               # one-pass backward: Q, dO, K, V -> dQ, dK, dV
             "stat": 2 * e * Tq + lse + st,              # O, dO, LSE -> stat
             "rstd": e * (Tq * ("q" in norm) + Tk * ("k" in norm) + Tk * ("v" in norm)) + rs}
@@ -410,7 +414,8 @@ def main(argv=None):
 
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
-    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8)
+    ds_bytes = 0 if (sm or norm or fused) else st["ds_bytes"]   # what gdpa_bwd_dkdv / _dq run with
+    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8, ds_bytes=ds_bytes)
     kf = kernel_flops(H, d, pairs, Tq, Tk)
     dom = max(kms, key=kms.get)
     trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "_fp8" if args.fp8 else "")   # its counter record
@@ -445,7 +450,7 @@ def main(argv=None):
         "dtype": "fp8+bf16" if args.fp8 else "bf16",
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
-                   "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs,
+                   "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs, "ds_bytes": ds_bytes,
                    "backward": ("dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
                                 "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else
                                 ["dK/dV + dQ kernels", "one KV-stationary pass", "one Q-stationary pass"][fused])},

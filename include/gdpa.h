@@ -145,10 +145,11 @@ typedef struct gdpa_plan_s* gdpa_plan;
  *   out                     : receives the plan (NULL on failure)
  *
  * For d = 128 bf16 plans whose gdpa_bwd runs the two backward kernels (and unless
- * opts->no_ds, or a layout other than the automatic one-wave, one-block dK/dV and
- * dQ lists is asked for), the plan also owns a dS buffer: one 32 x 32 bf16 block
- * (2 KiB) per (head, 32-row q tile, 32-row kv tile) holding a valid pair
- * (gdpa_plan_stats reports its size).  gdpa_bwd's dK/dV kernel stores dS there and
+ * opts->no_ds, or a layout other than one block per wave in the dK/dV list and
+ * the automatic one-wave, one-block dQ list is asked for), the plan also owns a dS
+ * buffer: each sample gives each of its 32-row q tiles as many 32 x 32 bf16 blocks
+ * (2 KiB) as the most 32-row kv tiles any of its q tiles has a valid pair with,
+ * per head (gdpa_plan_stats reports its size).  gdpa_bwd's dK/dV kernel stores dS there and
  * its dQ kernel computes dQ = dS K / sqrt(d) from it instead of recomputing the
  * scores and the activation's derivative.
  *

@@ -27,7 +27,10 @@ Readings (the page gives no cost model or tie-break):
     (chunks of earlier cut items) + j (O or dQ; dK and dV for the KV-stationary
     list), and the item's output is the sum of its slots.  The page deals tiles, not whole rows of tiles, so a long row of tiles
     need not sit in one bin; the chunks keep that freedom without atomics;
-  * stable order: cost descending, then (b, h, t, s0) ascending;
+  * stable order: cost descending, then (b, h, s0, t) ascending: among equal
+    costs, the items of one head that stream the same tiles (chunks of one step
+    range over the stationary tiles, as in a KV-stationary pass over a long Q)
+    follow each other, and the greedy deal puts them on neighbouring bins;
   * deal over P bins, by default greedy: each item, in sorted order, to the bin
     of least cost so far (lowest index on ties) -- the sorted assignment the page
     describes, taken to the least-loaded bin instead of a fixed snake; the page's
@@ -135,7 +138,7 @@ def deal(items, P: int, mode: str = "greedy"):
     """Sort and deal items to P bins.  Returns (bin_ptr, ordered items, bin_cost)."""
     if mode not in DEALS:
         raise ValueError(mode)
-    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[3], it[4]))
+    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[4], it[3]))
     bins = [[] for _ in range(P)]
     cost = [0] * P
     least = [(0, p) for p in range(P)]   # (cost so far, bin), a heap: least cost, then lowest bin

@@ -324,9 +324,10 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         p->fused = kv_ok ? 1 : q_ok ? 2 : 0;
     }
 
-    // stored dS: the two-kernel backward at d = 128 with 32-row dK/dV and dQ items
-    if (dtype != GDPA_F32 && d == 128 && p->fused == 0 && o.no_ds == 0 && L.team[LIST_DKDV] == 1 &&
-        L.nb[LIST_DKDV] == 1 && L.team[LIST_DQ] == 1 && L.nb[LIST_DQ] == 1) {
+    // stored dS: the two-kernel backward at d = 128 with 32- or 64-row dK/dV items and 32-row
+    // dQ items
+    if (dtype != GDPA_F32 && d == 128 && p->fused == 0 && o.no_ds == 0 && L.nb[LIST_DKDV] == 1 &&
+        L.team[LIST_DQ] == 1 && L.nb[LIST_DQ] == 1) {
         p->ds = ds_layout(lq, lk, window);
         p->use_ds = p->ds.nb_total > 0 && p->ds.nb_total * (int64_t)H < ((int64_t)1 << 31);
     }

@@ -123,21 +123,30 @@ struct Dkdv16Pol : Common {
     template <class RingT>
     __device__ __forceinline__ void step(const Rec& c, int s, const RingT& g, int job) {
         const int i0 = s * 32, j0 = krow(c);
-        // stored dS: this step's block, c.pad0 + s c.pad1 + (t - js0(s)) (c.pad0 = the
-        // sample's first block of this head, c.pad1 = blocks per q tile, js0(s) = the
-        // q tile's first kv tile in the band)
+        // stored dS: the block of q tile s and this wave's kv tile kt, c.pad0 + s c.pad1 +
+        // (kt - js0(s)) (c.pad0 = the sample's first block of this head, c.pad1 = blocks
+        // per q tile, js0(s) = the q tile's first kv tile in the band).  A 64-row item
+        // also steps over q tiles that pair with its other kv tile only: no block of
+        // this kv tile exists for them, and nothing is stored.
         rsrc_t rds;
         uint32_t ods = 0;
+        bool has_blk = a.ds != nullptr;
         if (a.ds) {
+            const int kt = c.t * (ROWS / 32) + (wt >> 1);
             const int js0 = win > 0 ? max(0, i0 - win + 1) >> 5 : 0;
-            const size_t blk = (size_t)c.pad0 + (size_t)s * (size_t)c.pad1 + (size_t)(c.t - js0);
+            if constexpr (ROWS > 32) {
+                const int a1 = min(c.lq - 1, i0 + 31);
+                const int js1 = win > 0 ? min(c.lk - 1, a1 + win - 1) >> 5 : (c.lk - 1) >> 5;
+                has_blk = kt >= js0 && kt <= js1;
+            }
+            const size_t blk = (size_t)c.pad0 + (size_t)s * (size_t)c.pad1 + (size_t)(kt - js0);
             rds = slice_rsrc(a.ds + blk * 1024, 1, 2048u, 2048u);
-            ods = (uint32_t)(16 * wt + l16) * 64u + 8u * (uint32_t)g4;   // row j, q rows 4 (l / 16) ..
+            ods = (uint32_t)(16 * (wt & 1) + l16) * 64u + 8u * (uint32_t)g4;   // row j, q rows 4 (l / 16) ..
         }
         // a wave whose 16 kv rows are past the sample's keys, or have no pair with this
         // q tile in the band, skips the step (its rows of a stored dS block are 0)
         if (j0 >= c.lk || (win > 0 && (j0 - (i0 + 31) >= win || i0 - (j0 + 15) >= win))) {
-            if (a.ds) {
+            if (has_blk) {
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rds, (int)ods, 0, 0);
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, rds, (int)(ods + 32u), 0, 0);
             }
@@ -201,7 +210,7 @@ struct Dkdv16Pol : Common {
                 dm[e] = (__bf16)(dp[ib][v] * gr);
             }
         }
-        if (a.ds) {   // dS of q rows 4 (l / 16) + {0..3} and 16 + 4 (l / 16) + {0..3}, kv row j0 + l % 16
+        if (has_blk) {   // dS of q rows 4 (l / 16) + {0..3} and 16 + 4 (l / 16) + {0..3}, kv row j0 + l % 16
             const u32x4 w = __builtin_bit_cast(u32x4, dm);
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, rds, (int)ods, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[2], w[3]}, rds, (int)(ods + 32u), 0, 0);

@@ -130,8 +130,8 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
         if (x.cost != y.cost) return x.cost > y.cost;
         if (x.it.b != y.it.b) return x.it.b < y.it.b;
         if (x.it.h != y.it.h) return x.it.h < y.it.h;
-        if (x.it.t != y.it.t) return x.it.t < y.it.t;
-        return x.it.s0 < y.it.s0;
+        if (x.it.s0 != y.it.s0) return x.it.s0 < y.it.s0;
+        return x.it.t < y.it.t;
     });
 
     // deal, then a bin-major CSR keeping deal order

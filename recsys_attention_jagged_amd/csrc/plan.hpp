@@ -21,7 +21,8 @@
 // s0 + floor((i + 1) n / k) - 1); each chunk writes its partial output block(s)
 // (O or dQ; dK and dV for the KV-stationary list) to its own slot (numbered in
 // (b, h, t) order) and a reduction adds the slots of one item in chunk order.  Order: cost descending,
-// then (b, h, t, s0).  Deal: greedy (default: each item, in order, to the bin of
+// then (b, h, s0, t) (equal-cost items of a head that stream the same tiles end up
+// side by side, on neighbouring bins of one XCD).  Deal: greedy (default: each item, in order, to the bin of
 // least cost so far, the lowest index on ties), zigzag (the r-th item goes to bin
 // r mod P in even rounds and P-1 - (r mod P) in odd rounds) or round robin.
 #pragma once

@@ -200,13 +200,15 @@ def test_dkdv_16row_teams(tk, window, bins):
 @pytest.mark.parametrize("window,bins", [(0, (0, 0, 0)), (9, (0, 0, 0)), (128, (0, 0, 0)), (0, (16, 16, 16)),
                                          (40, (8, 8, 8))])
 @pytest.mark.parametrize("dtype", ["bf16", "bf16_f32out"])
-def test_stored_ds_backward(window, bins, dtype):
-    say(f"stored dS backward window={window} bins={bins} {dtype}")
+@pytest.mark.parametrize("team", [1, 2])   # 32- or 64-row dK/dV items
+def test_stored_ds_backward(window, bins, dtype, team):
+    say(f"stored dS backward window={window} bins={bins} {dtype} dK/dV team={team}")
     L = [1, 15, 16, 17, 33, 47, 64, 65, 0, 300, 129, 700]
     inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, seed=90 + window, device=DEV)
     qo, ko = dev_offsets(inp)
     r = oracle_bwd(inp)
-    with G.Plan(inp.q_off, inp.kv_off, 2, 128, window, dtype, bins=bins, unfused=True) as plan:
+    with G.Plan(inp.q_off, inp.kv_off, 2, 128, window, dtype, bins=bins, unfused=True,
+                team=(0, team, 0)) as plan:
         assert plan.stats()["ds_bytes"] > 0
         whole = [t.float().cpu().numpy() for t in plan.bwd(inp.q, inp.k, inp.v, inp.do, qo, ko, "gelu")]
         odt = torch.float32 if dtype == "bf16_f32out" else torch.bfloat16
@@ -218,7 +220,7 @@ def test_stored_ds_backward(window, bins, dtype):
         G.gdpa_bwd_dq(*args, dq)
         torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), whole, r):
-        check_close(a, b, f"{name} stored dS window={window} bins={bins} {dtype}")
+        check_close(a, b, f"{name} stored dS window={window} bins={bins} {dtype} team={team}")
     for name, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), whole):
         assert np.array_equal(a.float().cpu().numpy(), b), f"{name}: split calls differ from gdpa_bwd"
     # without a dS buffer, dQ alone recomputes dS
