@@ -71,11 +71,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_flops(H, d, pairs, Tq=0, Tk=0):
+def kernel_flops(H, d, pairs, Tq=0, Tk=0, ds=False):
     """Algorithmic FLOPs per launch: the MFMA products each kernel's algorithm performs
-    (stat: the JFA pre-pass's dot products dO . O; rstd: the sums of squares of the norm)."""
+    (stat: the JFA pre-pass's dot products dO . O; rstd: the sums of squares of the norm;
+    ds: the dQ kernel multiplies the stored dS by K, one product, instead of
+    recomputing S and dP)."""
     u = 2.0 * H * d * pairs          # one product over the valid pairs
-    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": 3 * u, "bwd": 5 * u, "stat": 2.0 * H * d * Tq,
+    return {"fwd": 2 * u, "dkdv": 4 * u, "dq": (1 if ds else 3) * u, "bwd": 5 * u, "stat": 2.0 * H * d * Tq,
             "rstd": 2.0 * H * d * (Tq + 2 * Tk)}
 
 
@@ -416,7 +418,7 @@ def main(argv=None):
     value = useful / (ms_step * 1e-3) / 1e12
     ds_bytes = 0 if (sm or norm or fused) else st["ds_bytes"]   # what gdpa_bwd_dkdv / _dq run with
     kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8, ds_bytes=ds_bytes)
-    kf = kernel_flops(H, d, pairs, Tq, Tk)
+    kf = kernel_flops(H, d, pairs, Tq, Tk, ds=ds_bytes > 0)
     dom = max(kms, key=kms.get)
     trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "_fp8" if args.fp8 else "")   # its counter record
     # the roof the kernel's arithmetic intensity puts it under (ridge: peak FLOP/s / peak B/s)
