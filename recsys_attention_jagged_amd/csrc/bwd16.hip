@@ -238,6 +238,8 @@ struct Dkdv16Pol : Common {
     // this wave's 16 rows of one output (acc: kv row l % 16, columns 16 cb + 4 (l / 16) + {0..3})
     __device__ __forceinline__ void store16(const f32x4 (&acc)[NCB], float mul, void* out, size_t base, int rows,
                                             int row0, char* stage) const {
+        // lane-derived offsets computed here, once per item (see opaque)
+        const int ln = opaque(lane), l16 = ln & 15, g4 = ln >> 4;
         if (a.out_f32) {
             const rsrc_t ro = slice_rsrc((const float*)out + base, rows, rso, D * 4);
 #pragma unroll
@@ -259,7 +261,7 @@ struct Dkdv16Pol : Common {
         }
         const rsrc_t ro = slice_rsrc((const __bf16*)out + base, rows, rso, D * 2);
         constexpr int CPR = D / 8, RPI = 64 / CPR;   // 16-byte chunks per row, rows per instruction
-        const int rr = lane / CPR, cc = lane % CPR;
+        const int rr = ln / CPR, cc = ln % CPR;
 #pragma unroll
         for (int k = 0; k < 16 / RPI; ++k) {
             const int row = k * RPI + rr;
@@ -270,6 +272,7 @@ struct Dkdv16Pol : Common {
     // a chunk's partial block: fp32 rows 16 wt + l % 16 of slot `slot` ([slots][ROWS][D])
     __device__ __forceinline__ void partial16(const f32x4 (&acc)[NCB], int slot) const {
         constexpr uint32_t RB = D * 4;
+        const int ln = opaque(lane), l16 = ln & 15, g4 = ln >> 4;
         const rsrc_t ro = slice_rsrc(a.part + (size_t)slot * ROWS * D, ROWS, RB, RB);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {

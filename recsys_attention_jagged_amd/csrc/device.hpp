@@ -204,6 +204,16 @@ __device__ __forceinline__ void act_fwd_grad(float x, float& f, float& g) {
 // lk, head h, stationary tile t and streaming tiles s0..s1 (none if s1 < s0);
 // part >= 0: the item is one chunk of a longer one and stores its fp32 output
 // block into partial slot `part` instead of the output.
+// v, opaque to the compiler: values derived from it are computed where they are
+// used instead of being hoisted out of the surrounding loops, where they would be
+// kept in registers (or spilled to scratch) across every step.  A scratch reload is
+// a vector memory load and waits behind the ring's tile loads still in flight.
+__device__ __forceinline__ int opaque(int v) {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
 struct Rec {
     int32_t qs, lq, ks, lk, h, t, s0, s1, part, pad0, pad1, pad2;
 };
