@@ -362,12 +362,13 @@ struct FwdPol {
             return;
         }
         const rsrc_t ro = slice_rsrc((const __bf16*)a.o + ob, c.lq, rso, D * 2);
+        const int ln = opaque(lane);   // the staging offsets are computed here, per item
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             if (qrow(c, b) >= c.lq) continue;   // a block past the sample's last query has no rows
             char* st = g.tile(job - 2 + (T > 1 ? wt : (b & 1)));
-            stage_block<D>(acc[b], mul[b], st, r, hh);
-            store_tile<D>(st, ro, (uint32_t)qrow(c, b) * rso, rso, lane);
+            stage_block<D>(acc[b], mul[b], st, ln & 31, ln >> 5);
+            store_tile<D>(st, ro, (uint32_t)qrow(c, b) * rso, rso, ln);
         }
     }
 
