@@ -289,29 +289,6 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
             return fail_hip(e, "device query");
         }
     }
-    for (int l = 0; l < 3; ++l) {
-        // one bin per persistent workgroup (a team of waves): as many as the device
-        // holds resident (host_only: 4 per CU)
-        int P = o.bins[l];
-        if (P == 0) {
-            P = 4 * cus;
-            if (!p->host_only && dtype != GDPA_F32) {
-                const void* f = l == LIST_FWD ? fwd_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU)
-                              : l == LIST_DQ  ? dq_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU)
-                                              : dkdv_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU);
-                // the d = 128 dK/dV list's 16-row kernel runs two waves per 32 team rows
-                const bool k16 = l == LIST_DKDV && d == 128 && f && f == dkdv16_kernel_ptr(32 * L.team[l], GDPA_ACT_GELU);
-                int per_cu = 0;
-                if (f && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, (k16 ? 128 : 64) * L.team[l], 0) == hipSuccess &&
-                    per_cu > 0)
-                    P = cus * per_cu;
-            }
-        }
-        // the fp32 path runs no work lists; its plan keeps items whole
-        const bool split = o.no_split == 0 && dtype != GDPA_F32;
-        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split);
-    }
-
     // one-pass backward: one side of every sample fits one 32-row tile, and no
     // sample has rows on that side only (their outputs would have no item)
     if (dtype != GDPA_F32 && o.unfused == 0) {
@@ -331,6 +308,31 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         p->ds = ds_layout(lq, lk, window);
         p->use_ds = p->ds.nb_total > 0 && p->ds.nb_total * (int64_t)H < ((int64_t)1 << 31);
     }
+
+    for (int l = 0; l < 3; ++l) {
+        // one bin per persistent workgroup (a team of waves): as many as the device
+        // holds resident (host_only: 4 per CU)
+        int P = o.bins[l];
+        if (P == 0) {
+            P = 4 * cus;
+            if (!p->host_only && dtype != GDPA_F32) {
+                const void* f = l == LIST_FWD ? fwd_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU)
+                              : l == LIST_DQ  ? (p->use_ds ? dq_from_ds_kernel_ptr()
+                                                           : dq_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU))
+                                              : dkdv_kernel_ptr(d, L.team[l], L.nb[l], GDPA_ACT_GELU);
+                // the d = 128 dK/dV list's 16-row kernel runs two waves per 32 team rows
+                const bool k16 = l == LIST_DKDV && d == 128 && f && f == dkdv16_kernel_ptr(32 * L.team[l], GDPA_ACT_GELU);
+                int per_cu = 0;
+                if (f && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, (k16 ? 128 : 64) * L.team[l], 0) == hipSuccess &&
+                    per_cu > 0)
+                    P = cus * per_cu;
+            }
+        }
+        // the fp32 path runs no work lists; its plan keeps items whole
+        const bool split = o.no_split == 0 && dtype != GDPA_F32;
+        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split);
+    }
+
     if (dtype != GDPA_F32) {
         for (int l = 0; l < 3; ++l) {
             p->h_recs[l] = p->use_ds ? device_records(p->lists[l], p->q_off, p->kv_off, p->ds, window)

@@ -407,6 +407,9 @@ __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, c
     if (bin >= a.P) return;
     const int beg = bin_ptr[bin], end = bin_ptr[bin + 1];
     if (beg >= end) return;
+#ifdef GDPA_BIN_CLOCK
+    const unsigned long long clock0 = __builtin_amdgcn_s_memrealtime();
+#endif
     DqDsPol pol(a, lane);
     DsRing ring;
     ring.init(smem, (uint32_t)a.H * 128 * 2, lane);
@@ -454,6 +457,12 @@ __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, c
         // slot only at the next consume point, after that step's reads
         pol.store<128>(pol.acc, pol.scale, a.dq, ob, c.lq, c.t * 32, ring.ktile(job - 1));
     }
+#ifdef GDPA_BIN_CLOCK
+    if (a.bin_clock && lane == 0) {
+        a.bin_clock[2 * bin] = clock0;
+        a.bin_clock[2 * bin + 1] = __builtin_amdgcn_s_memrealtime();
+    }
+#endif
 }
 
 }  // namespace
