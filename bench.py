@@ -346,6 +346,9 @@ def main(argv=None):
         def jdq():
             G.gdpa_jfa_bwd_dq(h, inp.q, inp.k, inp.v, o, lse, inp.do, qo, ko, B, H, d, win, stat, dq, sh)
 
+        def jbwd():
+            G.gdpa_jfa_bwd(h, inp.q, inp.k, inp.v, o, lse, inp.do, qo, ko, B, H, d, win, stat, dq, dk, dv, sh)
+
     if norm:
         rstd = torch.empty((H * (Tq + 2 * Tk),), dtype=torch.float32, device="cuda")
 
@@ -372,11 +375,12 @@ def main(argv=None):
         def ffwd():
             G.gdpa_fp8_fwd(h, q8, k8, inp.v, qo, ko, B, H, d, act, win, sq8, sk8, o, sh)
 
-    # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels (JFA and
-    # the norm prologue: always the two kernels, after their pre-pass)
-    fused = 0 if (sm or norm) else st["bwd_fused"]
+    # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels (the norm
+    # prologue: always the two kernels, after its pre-pass; JFA: the two kernels, or the
+    # KV-stationary pass where every Lk <= 32)
+    fused = 0 if norm else (int(st["bwd_fused"] == 1) if sm else st["bwd_fused"])
     if sm:
-        calls = [("fwd", jfwd), ("dq", jdq), ("dkdv", jdkdv)]
+        calls = [("fwd", jfwd), ("bwd", jbwd)] if fused else [("fwd", jfwd), ("dq", jdq), ("dkdv", jdkdv)]
     elif norm:
         calls = [("rstd", nrstd), ("fwd", nfwd), ("dkdv", ndkdv), ("dq", ndq)]
     else:
@@ -453,7 +457,8 @@ def main(argv=None):
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs, "ds_bytes": ds_bytes,
-                   "backward": ("dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
+                   "backward": ("one KV-stationary pass (D formed from P and dP)" if sm and fused else
+                                "dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
                                 "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else
                                 ["dK/dV + dQ kernels", "one KV-stationary pass", "one Q-stationary pass"][fused])},
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

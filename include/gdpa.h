@@ -289,12 +289,17 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
  *   stat   : device fp32 [H, Tq, 2], caller-owned scratch, written: per (head, q
  *            row) the pair (LSE_i log2(e), D_i).
  * Enqueues the Q-stationary dQ kernel, which also forms D from O and dO and writes
- * stat, then the KV-stationary dK/dV kernel, which reads stat (never the one-pass
- * kernels), plus the chunk reductions of cut items.  The plan must be GDPA_BF16
+ * stat, then the KV-stationary dK/dV kernel, which reads stat, plus the chunk
+ * reductions of cut items.  On a plan whose every sample has Lk <= 32
+ * (gdpa_plan_stats: bwd_fused = 1) it runs one KV-stationary pass instead: all keys
+ * of a query tile are in one step there, so D_i = sum_j P_ij dP_ij (which equals
+ * sum_c dO_ic O_ic for the exact O) is formed in the pass from P and dP, O is not
+ * read and stat is not written (it may be NULL).  The plan must be GDPA_BF16
  * (O is read as bf16; a GDPA_BF16_F32OUT plan, whose gdpa_jfa_fwd writes fp32 O,
  * and an F32 plan are rejected with UNSUPPORTED) with one-wave dQ and dK/dV teams
  * (the automatic layouts; UNSUPPORTED otherwise).
- * Errors as gdpa_bwd.  gdpa_jfa_bwd == gdpa_jfa_bwd_dq, then gdpa_jfa_bwd_dkdv.
+ * Errors as gdpa_bwd.  On the other plans gdpa_jfa_bwd == gdpa_jfa_bwd_dq, then
+ * gdpa_jfa_bwd_dkdv (the parts always run the two kernels).
  */
 gdpa_status gdpa_jfa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,

@@ -757,14 +757,17 @@ static gdpa_status jfa_check(gdpa_plan plan) {
 }
 
 // the JFA backward's gradient kernels: the dQ kernel (reads o and lse, writes stat),
-// then the dK/dV kernel (reads stat)
+// then the dK/dV kernel (reads stat); or, for both on a plan whose every Lk <= 32,
+// the one KV-stationary pass (reads lse)
 static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, const int32_t* q_off_dev, const int32_t* kv_off_dev,
                              float* stat, void* dq, void* dk, void* dv, hipStream_t s, bool want_dkdv, bool want_dq) {
     const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
-    if (any_q && (!q || !dout || !stat)) return fail(GDPA_ERR_INVALID_ARG, "q, dout or stat is NULL");
+    const bool one_pass = want_dq && want_dkdv && plan->fused == 1;   // reads neither o nor stat
+    if (any_q && (!q || !dout || (!stat && !one_pass))) return fail(GDPA_ERR_INVALID_ARG, "q, dout or stat is NULL");
     if (any_k && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
-    if (want_dq && any_q && (!dq || !o || !lse)) return fail(GDPA_ERR_INVALID_ARG, "dq, o or lse is NULL");
+    if (want_dq && any_q && (!dq || !lse || (!o && !one_pass)))
+        return fail(GDPA_ERR_INVALID_ARG, "dq, o or lse is NULL");
     if (want_dkdv && any_k && (!dk || !dv)) return fail(GDPA_ERR_INVALID_ARG, "dk or dv is NULL");
     KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
     a.q = q;
@@ -780,6 +783,26 @@ static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const
     a.Tq = (int)plan->Tq;
     const int d = plan->d;
     hipError_t e = hipSuccess;
+    if (one_pass) {
+        // every Lk <= 32: one KV-stationary pass, which forms D from P and dP itself
+        // (stat is not written)
+        const WorkList& wl = plan->lists[LIST_DKDV];
+        KernelArgs b = a;
+        b.items = plan->d_items[LIST_DKDV];
+        b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+        b.P = wl.P;
+        b.part = plan->d_part[LIST_DKDV];
+        switch (d) {
+            case 32: e = launch_bwd_fused_d32(b, 1, kActSoftmax, s); break;
+            case 64: e = launch_bwd_fused_d64(b, 1, kActSoftmax, s); break;
+            default: e = launch_bwd_fused_d128(b, 1, kActSoftmax, s); break;
+        }
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
+        if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
+        if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no JFA backward kernel for this configuration");
+        if (e != hipSuccess) return fail_hip(e, "JFA backward launch");
+        return GDPA_OK;
+    }
     if (want_dq && any_q) {
         const WorkList& wl = plan->lists[LIST_DQ];
         KernelArgs b = a;

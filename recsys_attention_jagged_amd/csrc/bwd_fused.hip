@@ -9,6 +9,13 @@
 //     in one step, so dK = dS^T Q / sqrt(d) and dV = P^T dO of that tile are
 //     formed and stored per step, next to the dQ accumulation.
 //
+// JFA (softmax attention) runs the KV-stationary pass too: with the keys of a query
+// tile all in one step, D_i = sum_c dO_ic O_ic (the softmax Jacobian's row term)
+// equals sum_j P_ij dP_ij over that step's keys (O_i = sum_j P_ij V_j), so the
+// pass forms it from the P and dP it already holds, by a sum across the 32 lanes
+// of a key column, and needs from the forward only LSE, which rides with each Q
+// tile in the ring's side buffer.
+//
 // Either way the second kernel, and its full pass over the long side, goes away
 // (GDPA page, aitrends.kr/articles/26275, "Section details": backward without the
 // softmax row statistics; S is recomputed).  The products that need the other
@@ -29,12 +36,29 @@ namespace {
 // =========================================================================
 // KV-stationary: dK, dV accumulated, dQ stored per step (every Lk <= 32)
 // =========================================================================
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// sum of x over the 32 lanes of each half of the wave (every lane gets its half's sum)
+__device__ __forceinline__ float half_sum32(float x) {
+    x += dpp_f32<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_f32<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_f32<0x124>(x);   // row_ror:4
+    x += dpp_f32<0x128>(x);   // row_ror:8: the 16-lane row's sum
+    return x + __shfl_xor(x, 16);
+}
+
 template <int D, int ACT>
 struct KvFusedPol : Common {
     static constexpr int NSTAT = 2, NSTRM = 2;   // (K, V), then (Q, dO) per step
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr bool HOIST = TeamShape<D, 1, 2>::HOIST;
+    static constexpr bool SM = ACT == ACT_SOFTMAX;
+    static constexpr int XJ = SM ? 1 : 0;        // softmax: LSE of each Q tile's rows in a side buffer
     Slice wk, wv, wq, wo;   // issuing side
+    Slice wst, wnull;       // softmax: LSE of the item's q rows; a zero-range side
     bf16x8 kf[NKS], vf[NKS], kt[2][NDB];
     f32x16 accK[NDB], accV[NDB];
 
@@ -47,15 +71,29 @@ struct KvFusedPol : Common {
         const size_t qb = ((size_t)w.qs * H + w.h) * D;
         wq = slice_of((const __bf16*)a.q + qb, w.lq, rs, D * 2);
         wo = slice_of((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        if constexpr (SM) {
+            wst = slice_of(a.lse + (size_t)w.h * a.Tq + w.qs, w.lq, 4u, 4u);
+            wnull = slice_of(a.lse, 0, 4u, 4u);
+        }
+    }
+
+    // tile rows at byte offset `off` of `t`; softmax: and the side at x_off of `xs`
+    template <class RingT>
+    __device__ __forceinline__ void put(RingT& g, Slice t, uint32_t off, Slice xs, uint32_t x_off) {
+        if constexpr (SM)
+            g.issue(t, off, xs, x_off);
+        else
+            g.issue(t, off);
     }
 
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {
-            g.issue(i == 0 ? wk : wv, (uint32_t)(w.t * 32) * rs);
+            put(g, i == 0 ? wk : wv, (uint32_t)(w.t * 32) * rs, wnull, 0u);
         } else {
             const int rel = i - NSTAT;
-            g.issue((rel & 1) ? wo : wq, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
+            const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
+            put(g, (rel & 1) ? wo : wq, row0 * rs, (rel & 1) ? wnull : wst, row0 * 4u);
         }
     }
 
@@ -101,23 +139,53 @@ struct KvFusedPol : Common {
         const bool masked = win > 0 && !band_all(i0, j0, win);
         const int base = i0 + 4 * hh - j0 - r;
         bf16x8 pm[2], dm[2];
+        if constexpr (SM) {
+            // P = exp(S - LSE) (log2 units), zero for keys past the sample's length (a zero
+            // K row gives S = 0, not P = 0) and outside the band; D_i = sum_j P_ij dP_ij
+            constexpr float L2E = 1.4426950408889634f;
+            const float c2 = scale * L2E;
+            float4 ls[4];   // LSE of q rows i0 + 8 j + 4 hh + {0..3}
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+            for (int j = 0; j < 4; ++j) ls[j] = *(const float4*)(g.side(job) + 4 * (8 * j + 4 * hh));
+            const bool key_ok = r < c.lk - j0;
+            float p[16], dsum[16];
 #pragma unroll
-            for (int e8 = 0; e8 < 8; ++e8) {
-                const int e = 8 * m + e8;
-                float f, gr;
-                act_fwd_grad<ACT>(sc[e] * scale, f, gr);
-                float ds = dp[e] * gr;
-                if (masked) {
-                    const int dd = base + 8 * (e >> 2) + (e & 3);
-                    const bool ok = in_band(dd, win);
-                    f = ok ? f : 0.0f;
-                    ds = ok ? ds : 0.0f;
-                }
-                pm[m][e8] = (__bf16)f;
-                dm[m][e8] = (__bf16)ds;
+            for (int e = 0; e < 16; ++e) {
+                float pe = fast_exp2(__builtin_fmaf(sc[e], c2, -ls[e >> 2][e & 3] * L2E));
+                bool ok = key_ok;
+                if (masked) ok = ok && in_band(base + 8 * (e >> 2) + (e & 3), win);
+                p[e] = ok ? pe : 0.0f;
+                dsum[e] = p[e] * dp[e];
             }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) dsum[e] = half_sum32(dsum[e]);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int e8 = 0; e8 < 8; ++e8) {
+                    const int e = 8 * m + e8;
+                    pm[m][e8] = (__bf16)p[e];
+                    dm[m][e8] = (__bf16)(p[e] * (dp[e] - dsum[e]));
+                }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int e8 = 0; e8 < 8; ++e8) {
+                    const int e = 8 * m + e8;
+                    float f, gr;
+                    act_fwd_grad<ACT>(sc[e] * scale, f, gr);
+                    float ds = dp[e] * gr;
+                    if (masked) {
+                        const int dd = base + 8 * (e >> 2) + (e & 3);
+                        const bool ok = in_band(dd, win);
+                        f = ok ? f : 0.0f;
+                        ds = ok ? ds : 0.0f;
+                    }
+                    pm[m][e8] = (__bf16)f;
+                    dm[m][e8] = (__bf16)ds;
+                }
+        }
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -311,10 +379,10 @@ struct QFusedPol : Common {
     }
 };
 
-template <class Pol>
+template <class Pol, int XJ = 0>
 __device__ __forceinline__ void fused_body(const KernelArgs& a, const Rec* __restrict__ recs,
                                            const int32_t* __restrict__ bin_ptr, char* smem, int D) {
-    using RingT = Ring<GDPA_D, 1, TeamShape<GDPA_D, 1, 2>::LDS>;
+    using RingT = Ring<GDPA_D, 1, TeamShape<GDPA_D, 1, 2>::LDS, XJ>;
     const int lane = threadIdx.x & 63;
     Pol pol(a, lane);
     run_team<Pol, RingT, 1>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * D * 2, 0, lane);
@@ -323,8 +391,9 @@ __device__ __forceinline__ void fused_body(const KernelArgs& a, const Rec* __res
 template <int D, int ACT>
 __global__ __launch_bounds__((TeamShape<D, 1, 2>::THREADS), (TeamShape<D, 1, 2>::WPE)) void kv_fused_kernel(
     const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
-    __shared__ __attribute__((aligned(1024))) char smem[Ring<D, 1, TeamShape<D, 1, 2>::LDS>::BYTES];
-    fused_body<KvFusedPol<D, ACT>>(a, recs, bin_ptr, smem, D);
+    constexpr int XJ = KvFusedPol<D, ACT>::XJ;
+    __shared__ __attribute__((aligned(1024))) char smem[Ring<D, 1, TeamShape<D, 1, 2>::LDS, XJ>::BYTES];
+    fused_body<KvFusedPol<D, ACT>, XJ>(a, recs, bin_ptr, smem, D);
 }
 
 template <int D, int ACT>
@@ -360,6 +429,7 @@ const void* q_ptr() {
 
 const void* GDPA_CAT(bwd_fused_kernel_ptr_d, GDPA_D)(int kv_stationary, int act) {
     if (kv_stationary) {
+        if (act == ACT_SOFTMAX) return kv_ptr<ACT_SOFTMAX>();
         GDPA_FUSED_SWITCH(kv_ptr)
     }
     GDPA_FUSED_SWITCH(q_ptr)
