@@ -375,9 +375,9 @@ def main(argv=None):
         def ffwd():
             G.gdpa_fp8_fwd(h, q8, k8, inp.v, qo, ko, B, H, d, act, win, sq8, sk8, o, sh)
 
-    # the backward as gdpa_bwd runs it: one pass, or the dK/dV and dQ kernels (the norm
-    # prologue: always the two kernels, after its pre-pass; JFA: the two kernels, or the
-    # KV-stationary pass where every Lk <= 32)
+    # the backward as gdpa_bwd / gdpa_jfa_bwd run it: one pass, or the dK/dV and dQ
+    # kernels (the norm prologue: always the two kernels, after its pre-pass; JFA: one
+    # pass only where every Lk <= 32)
     fused = 0 if norm else (int(st["bwd_fused"] == 1) if sm else st["bwd_fused"])
     if sm:
         calls = [("fwd", jfwd), ("bwd", jbwd)] if fused else [("fwd", jfwd), ("dq", jdq), ("dkdv", jdkdv)]

@@ -293,8 +293,8 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
  * reductions of cut items.  On a plan whose every sample has Lk <= 32
  * (gdpa_plan_stats: bwd_fused = 1) it runs one KV-stationary pass instead: all keys
  * of a query tile are in one step there, so D_i = sum_j P_ij dP_ij (which equals
- * sum_c dO_ic O_ic for the exact O) is formed in the pass from P and dP, O is not
- * read and stat is not written (it may be NULL).  The plan must be GDPA_BF16
+ * sum_c dO_ic O_ic for the exact O) is formed in the pass from P and dP; O and stat
+ * are neither read nor written (both may be NULL).  The plan must be GDPA_BF16
  * (O is read as bf16; a GDPA_BF16_F32OUT plan, whose gdpa_jfa_fwd writes fp32 O,
  * and an F32 plan are rejected with UNSUPPORTED) with one-wave dQ and dK/dV teams
  * (the automatic layouts; UNSUPPORTED otherwise).

@@ -677,25 +677,29 @@ def test_jfa_backward_parts_match_whole():
     check_close(dv2.float().cpu().numpy(), ref[2], "JFA dV after the pre-pass")
 
 
-# every Lk <= 32 (and Lk > 0 where Lq > 0): gdpa_jfa_bwd runs one KV-stationary pass
+# every Lk <= 32 (and Lk > 0 where Lq > 0): gdpa_jfa_bwd runs one KV-stationary pass;
+# every Lq <= 32 instead: the two kernels
 JFA_ONE_PASS = [
-    ([5, 0, 70, 1, 33, 200, 31, 96, 7], [32, 3, 5, 2, 29, 31, 1, 32, 17], 0),
-    ([1, 31, 32, 17, 5, 0], [1, 31, 32, 17, 5, 0], 4),
-    ([1, 31, 32, 17, 5], [1, 31, 32, 17, 5], 17),
-    ([1, 31, 32, 17, 5], [1, 31, 32, 17, 5], 1),
+    # (lq, lk, window, bwd_fused)
+    ([5, 0, 70, 1, 33, 200, 31, 96, 7], [32, 3, 5, 2, 29, 31, 1, 32, 17], 0, 1),
+    ([1, 31, 32, 17, 5, 0], [1, 31, 32, 17, 5, 0], 4, 1),
+    ([1, 31, 32, 17, 5], [1, 31, 32, 17, 5], 17, 1),
+    ([1, 31, 32, 17, 5], [1, 31, 32, 17, 5], 1, 1),
+    ([32, 32, 7], [300, 1000, 65], 0, 2),
 ]
 
 
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("case", range(len(JFA_ONE_PASS)))
 def test_jfa_backward_one_pass(d, case):
-    """The one-pass JFA backward forms D = sum_j P dP in the pass; against the oracle, and
-    the two-kernel path on the same inputs; it reads neither O nor stat."""
-    lq, lk, window = JFA_ONE_PASS[case]
+    """The one-pass JFA backward (D = sum_j P dP in the KV-stationary pass); against the
+    oracle, and the two-kernel path on the same inputs; it reads neither O nor stat.
+    A plan whose one-pass backward would be Q-stationary runs the two kernels."""
+    lq, lk, window, fused = JFA_ONE_PASS[case]
     say(f"JFA one-pass backward d={d} case={case}")
     inp = make_from_lengths(lq, lk, 2, d, act="gelu", window=window, seed=60 + case, device=DEV)
     with G.Plan(inp.q_off, inp.kv_off, 2, d, window, "bf16") as plan:
-        assert plan.stats()["bwd_fused"] == 1
+        assert plan.stats()["bwd_fused"] == fused
     floor = (0.0, 0.0, 0.0)
     if window == 1:   # dQ = dK = 0 exactly; the fp32 rounding of dO.v - D bounds them
         mag = lambda n: float(np.max(np.abs(inp.f64(n))))
@@ -708,13 +712,15 @@ def test_jfa_backward_one_pass(d, case):
     # cut items (few bins): dK, dV from chunk partials
     cut = run_jfa_bwd(inp, bins=(2, 2, 2))
     check_jfa_grads(cut, inp, f"one pass, cut items d={d} case={case}", floor)
+    if fused != 1:
+        return
     # neither O nor stat is needed
     qo, ko = dev_offsets(inp)
-    Tq = inp.q.shape[0]
     lse = torch.tensor(one[4], device=DEV)
+    o = None
     with G.Plan(inp.q_off, inp.kv_off, 2, d, window, "bf16") as plan:
         dq, dk, dv = torch.empty_like(inp.q), torch.empty_like(inp.k), torch.empty_like(inp.v)
-        G.gdpa_jfa_bwd(plan.handle, inp.q, inp.k, inp.v, None, lse, inp.do, qo, ko, plan.B, 2, d, window, None,
+        G.gdpa_jfa_bwd(plan.handle, inp.q, inp.k, inp.v, o, lse, inp.do, qo, ko, plan.B, 2, d, window, None,
                        dq, dk, dv)
         torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), (dq, dk, dv), one[:3]):
