@@ -2,7 +2,7 @@
 """Benchmark of jagged GDPA forward + backward (bf16 in, fp32 accumulate) on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 2|3|4|5|pffn] [--act NAME] [--attn gdpa|softmax]
-                    [--norm] [--fp8] [--no-per-config]
+                    [--norm] [--fp8] [--mx] [--no-per-config]
 
 A step is one forward pass plus one backward pass (as gdpa_bwd runs it: the dK/dV
 kernel, then the dQ kernel, or one pass) over the whole batch of the chosen
@@ -48,6 +48,11 @@ prologue replaces (forward: read x, write x^; backward: read x and dx^, write dx
 --fp8 runs the forward with Q and K as fp8 (OCP e4m3, one scale per tensor,
 quantised on the host before the timed region) and the backward in bf16 as gdpa_bwd
 runs it; the forward's algorithmic bytes count one byte per element of Q and K.
+
+--mx runs the forward with Q and K block-scaled (OCP MXFP8: e4m3 elements, one E8M0
+scale per 32 head columns of a row, quantised on the host before the timed region)
+on the scaled MFMA, the backward as for --fp8; the forward's algorithmic bytes count
+one byte per element of Q and K plus their scale bytes (d / 32 per row and head).
 """
 from __future__ import annotations
 
@@ -61,6 +66,7 @@ import time
 METRIC = "useful TFLOP/s, jagged GDPA fwd+bwd bf16, % of MFMA peak, 1 MI355X"
 METRIC_JFA = "useful TFLOP/s, jagged softmax attention (JFA) fwd+bwd bf16, 1 MI355X"
 METRIC_FP8 = "useful TFLOP/s, jagged GDPA fwd (fp8 Q, K) + bwd (bf16), 1 MI355X"
+METRIC_MX = "useful TFLOP/s, jagged GDPA fwd (MXFP8 Q, K) + bwd (bf16), 1 MI355X"
 METRIC_NORM = "useful TFLOP/s, jagged GDPA fwd+bwd with fused RMSNorm prologue, bf16, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
@@ -81,21 +87,23 @@ def kernel_flops(H, d, pairs, Tq=0, Tk=0, ds=False):
             "rstd": 2.0 * H * d * (Tq + 2 * Tk)}
 
 
-def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0):
+def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0, mx=False):
     """Algorithmic bytes per launch (bf16): every input read once, every output written
     once; softmax (JFA): plus the fp32 row LSE written by the forward, and the fp32
     (LSE, D) row pair that the pre-pass writes and the gradient kernels read; norm
     (RMSNorm prologue): plus the fp32 1/rms factors (H (Tq + 2 Tk)) that the rstd
     pre-pass writes, after reading the tensors it normalises, and the kernels read;
     ds_bytes (a plan that stores dS): the dK/dV kernel also writes the dS blocks, and
-    the dQ kernel reads them and K instead of recomputing the scores."""
+    the dQ kernel reads them and K instead of recomputing the scores; mx (block-scaled
+    fp8 Q and K): their d / 32 E8M0 scale bytes per row and head as well."""
     e = 2 * H * d
     lse, st = (4 * H * Tq, 8 * H * Tq) if softmax else (0, 0)
     rs = 4 * H * (Tq + 2 * Tk) if norm else 0
     qk = 0.5 if fp8 else 1.0                           # fp8 Q, K: one byte per element
     dq = (e * (Tq + Tk) + ds_bytes if ds_bytes else   # dS, K -> dQ
           e * (3 * Tq + 2 * Tk) + (e * Tq + lse if softmax else 0) + st + rs)   # Q, dO, K, V (+ O, LSE) -> dQ
-    return {"fwd": int(e * (qk * Tq + qk * Tk + Tk + Tq)) + lse + rs,   # Q, K, V (, rstd) -> O (, LSE)
+    mxs = H * (d // 32) * (Tq + Tk) if mx else 0        # E8M0 scale bytes of Q and K
+    return {"fwd": int(e * (qk * Tq + qk * Tk + Tk + Tq)) + lse + rs + mxs,   # Q, K, V (, rstd) -> O (, LSE)
             "dkdv": e * (2 * Tq + 4 * Tk) + st + rs + ds_bytes,   # Q, dO, K, V (, stat or rstd) -> dK, dV (, dS)
             "dq": dq,
             "bwd": e * (3 * Tq + 4 * Tk),               # one-pass backward: Q, dO, K, V -> dQ, dK, dV
@@ -253,6 +261,8 @@ def main(argv=None):
                     help="GDPA with the fused RMSNorm prologue on raw inputs of the same batch")
     ap.add_argument("--fp8", action="store_true",
                     help="forward with fp8 (e4m3) Q and K, backward in bf16, on the same batch")
+    ap.add_argument("--mx", action="store_true",
+                    help="forward with block-scaled fp8 (MXFP8) Q and K, backward in bf16, on the same batch")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -299,11 +309,14 @@ def main(argv=None):
     if (sm or args.norm) and args.config == "pffn":
         print("--attn softmax and --norm run the attention workloads", file=sys.stderr)
         return 2
-    if sum([sm, args.norm, args.fp8]) > 1:
-        print("--attn softmax, --norm and --fp8 are separate modes", file=sys.stderr)
+    if sum([sm, args.norm, args.fp8, args.mx]) > 1:
+        print("--attn softmax, --norm, --fp8 and --mx are separate modes", file=sys.stderr)
         return 2
-    if args.fp8 and args.config == "pffn":
-        print("--fp8 runs the attention workloads", file=sys.stderr)
+    if (args.fp8 or args.mx) and args.config == "pffn":
+        print("--fp8 and --mx run the attention workloads", file=sys.stderr)
+        return 2
+    if args.mx and d < 64:
+        print("--mx needs d >= 64 (64-wide scaled k blocks)", file=sys.stderr)
         return 2
     norm = w["rms"] if args.norm else ""
     t0 = time.perf_counter()
@@ -375,6 +388,23 @@ def main(argv=None):
         def ffwd():
             G.gdpa_fp8_fwd(h, q8, k8, inp.v, qo, ko, B, H, d, act, win, sq8, sk8, o, sh)
 
+    if args.mx:
+        def quant_mx(t):   # e4m3 bytes [T, H, d] and E8M0 scales [H, T, d / 32] (on the host, once)
+            x = t.float().cpu()
+            T_, H_, d_ = x.shape
+            xb = x.reshape(T_, H_, d_ // 32, 32)
+            amax = xb.abs().amax(-1)
+            ex = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-38))) - 8,
+                             torch.full_like(amax, -127.0)).clamp(-127, 127)
+            q = (xb / torch.exp2(ex)[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).reshape(T_, H_, d_)
+            return (q.view(torch.uint8).to("cuda"),
+                    (ex + 127).to(torch.uint8).permute(1, 0, 2).contiguous().to("cuda"))
+        qm8, qms = quant_mx(inp.q)
+        km8, kms8 = quant_mx(inp.k)
+
+        def ffwd():
+            G.gdpa_mx_fwd(h, qm8, qms, km8, kms8, inp.v, qo, ko, B, H, d, act, win, o, sh)
+
     # the backward as gdpa_bwd / gdpa_jfa_bwd run it: one pass, or the dK/dV and dQ
     # kernels (the norm prologue: always the two kernels, after its pre-pass; JFA: one
     # pass only where every Lk <= 32)
@@ -384,7 +414,7 @@ def main(argv=None):
     elif norm:
         calls = [("rstd", nrstd), ("fwd", nfwd), ("dkdv", ndkdv), ("dq", ndq)]
     else:
-        f0 = ffwd if args.fp8 else fwd
+        f0 = ffwd if (args.fp8 or args.mx) else fwd
         calls = [("fwd", f0), ("bwd", bwd)] if fused else [("fwd", f0), ("dkdv", dkdv), ("dq", dqk)]
     for _ in range(args.warmup):
         for _, c in calls:
@@ -421,10 +451,10 @@ def main(argv=None):
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
     ds_bytes = 0 if (sm or norm or fused) else st["ds_bytes"]   # what gdpa_bwd_dkdv / _dq run with
-    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8, ds_bytes=ds_bytes)
+    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8 or args.mx, ds_bytes=ds_bytes, mx=args.mx)
     kf = kernel_flops(H, d, pairs, Tq, Tk, ds=ds_bytes > 0)
     dom = max(kms, key=kms.get)
-    trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "_fp8" if args.fp8 else "")   # its counter record
+    trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "_fp8" if args.fp8 else "_mx" if args.mx else "")   # its counter record
     # the roof the kernel's arithmetic intensity puts it under (ridge: peak FLOP/s / peak B/s)
     mfma_bound = kf[dom] / kb[dom] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if mfma_bound:
@@ -443,7 +473,8 @@ def main(argv=None):
     bwd_ms = kms["bwd"] if fused else kms["dkdv"] + kms["dq"] + kms.get("stat", 0.0)
 
     out = {
-        "metric": METRIC_JFA if sm else METRIC_NORM if norm else METRIC_FP8 if args.fp8 else METRIC,
+        "metric": (METRIC_JFA if sm else METRIC_NORM if norm else METRIC_FP8 if args.fp8 else
+                   METRIC_MX if args.mx else METRIC),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -453,7 +484,7 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8+bf16" if args.fp8 else "bf16",
+        "dtype": "fp8+bf16" if args.fp8 else "mxfp8+bf16" if args.mx else "bf16",
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs, "ds_bytes": ds_bytes,
@@ -489,7 +520,7 @@ def main(argv=None):
         out["norm"] = {"tensors": norm, "plain_kernels_ms": round(p0.elapsed_time(p1) / K, 4),
                        "fused_ms": round(ms_step, 4),
                        "unfused_norm_hbm_floor_ms": round(5 * 2 * H * d * rows / (PEAK_HBM_GBS * 1e9) * 1e3, 4)}
-    default_mode = not (sm or norm or args.fp8) and args.config != "pffn" and args.act is None
+    default_mode = not (sm or norm or args.fp8 or args.mx) and args.config != "pffn" and args.act is None
     if default_mode and not args.no_per_config:
         out["per_config"] = {}
         for cfg in sorted(WORKLOADS):

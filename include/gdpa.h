@@ -381,6 +381,24 @@ gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const v
                          float k_scale, void* o, void* stream);
 
 /*
+ * gdpa_mx_fwd - GDPA forward with block-scaled fp8 Q and K (OCP microscaling, MXFP8:
+ * the GEM page's section on custom kernels and precision names MXFP8 for attention).
+ * q8 [Tq,H,d] and k8 [Tk,H,d] are OCP FP8 E4M3 bytes (e4m3fn); q_scale [H,Tq,d/32]
+ * and k_scale [H,Tk,d/32] (head-major: the rows of one head consecutive) are E8M0
+ * bytes, one per 32 consecutive head columns of a row, each standing for 2^(byte -
+ * 127) (255 is NaN).  The element at column c of a row stands for its e4m3 value
+ * times its block's scale; S = (q . k) / sqrt(d) is computed on gfx950's scaled
+ * MFMA (32 x 32 x 64, the scales applied in hardware, fp32 accumulation).  V is
+ * bf16, P is rounded to bf16 for the second product, O is bf16 (fp32 for a
+ * GDPA_BF16_F32OUT plan).  Arguments otherwise as gdpa_fwd.  bf16 plans with
+ * d = 64 or 128 only (UNSUPPORTED otherwise, and for act = GDPA_ACT_ONE); the
+ * gradients run on bf16 inputs (gdpa_bwd).
+ */
+gdpa_status gdpa_mx_fwd(gdpa_plan plan, const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                        const void* v, const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                        gdpa_act act, int window, void* o, void* stream);
+
+/*
  * pFFN as GDPA (GDPA page, "Section details", diagram of self-attention, PMA and
  * pFFN unified as GDPA).  The page gives no formula; read here as: per head,
  * weight matrices W_K, W_V [M, H, d] shared by every query row of the batch,

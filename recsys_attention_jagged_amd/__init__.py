@@ -68,6 +68,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                      ctypes.POINTER(_vp)]
     lib.gdpa_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
     lib.gdpa_fwd_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
+    lib.gdpa_mx_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
     lib.gdpa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
     lib.gdpa_bwd_dkdv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_bwd_dq.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]
@@ -295,6 +296,13 @@ def gdpa_pffn_plan_create(Tq: int, M: int, H: int, d: int, dtype, host_only: boo
     _check(load_library().gdpa_pffn_plan_create(Tq, M, H, d, _enum(dtype, DTYPE), ctypes.byref(opts),
                                                 None if host_only else _stream(stream), ctypes.byref(out)))
     return out.value
+
+
+def gdpa_mx_fwd(plan, q8, q_scale, k8, k_scale, v, q_off_dev, kv_off_dev, B, H, d, act, window, o, stream=None):
+    """Forward with block-scaled fp8 Q, K: e4m3 bytes [T, H, d] and E8M0 scale bytes [H, T, d / 32]."""
+    _check(load_library().gdpa_mx_fwd(plan, _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v),
+                                      _ptr(q_off_dev), _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, _ptr(o),
+                                      _stream(stream)))
 
 
 def gdpa_pffn_fwd(plan, q, wk, wv, act, o, stream=None):

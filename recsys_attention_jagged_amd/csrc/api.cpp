@@ -1070,6 +1070,42 @@ gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const v
     return GDPA_OK;
 }
 
+gdpa_status gdpa_mx_fwd(gdpa_plan plan, const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                        const void* v, const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
+                        gdpa_act act, int window, void* o, void* stream) {
+    g_err.clear();
+    gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
+    if (st != GDPA_OK) return st;
+    if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "block-scaled fp8 Q and K run on bf16 plans");
+    if (d < 64) return fail(GDPA_ERR_UNSUPPORTED, "block-scaled fp8 Q and K need d = 64 or 128 (64-wide k blocks)");
+    if (act == GDPA_ACT_ONE) return fail(GDPA_ERR_UNSUPPORTED, "GDPA_ACT_ONE has no fp8 kernels");
+    if (plan->Tq > 0 && (!q8 || !q_scale || !o)) return fail(GDPA_ERR_INVALID_ARG, "q8, q_scale or o is NULL");
+    if (plan->Tk > 0 && (!k8 || !k_scale || !v)) return fail(GDPA_ERR_INVALID_ARG, "k8, k_scale or v is NULL");
+    if (plan->Tq == 0) return GDPA_OK;
+    hipStream_t s = (hipStream_t)stream;
+    KernelArgs a = base_args(plan, q_off_dev, kv_off_dev);
+    a.q = q8;
+    a.k = k8;
+    a.v = v;
+    a.o = o;
+    a.q_mx = (const uint8_t*)q_scale;
+    a.k_mx = (const uint8_t*)k_scale;
+    a.Tq = (int)plan->Tq;
+    a.Tk = (int)plan->Tk;
+    const WorkList& wl = plan->lists[LIST_FWD];
+    a.items = plan->d_items[LIST_FWD];
+    a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+    a.P = wl.P;
+    a.part = plan->d_part[LIST_FWD];
+    const int code = (int)act | kActMX;
+    hipError_t e = d == 64 ? launch_fwd_bf16_d64(a, wl.team, wl.nb, code, s)
+                           : launch_fwd_bf16_d128(a, wl.team, wl.nb, code, s);
+    if (e == hipSuccess) e = reduce_parts(plan, LIST_FWD, 1.0f, o, s);
+    if (e == hipErrorInvalidValue) return fail(GDPA_ERR_UNSUPPORTED, "no block-scaled fp8 forward kernel here");
+    if (e != hipSuccess) return fail_hip(e, "block-scaled fp8 forward launch");
+    return GDPA_OK;
+}
+
 gdpa_status gdpa_pffn_plan_create(int Tq, int M, int H, int d, gdpa_dtype dtype, const gdpa_plan_opts* opts,
                                   void* stream, gdpa_plan* out) {
     g_err.clear();

@@ -33,6 +33,16 @@
 // OCP e4m3 bytes with one dequantisation factor per tensor (folded into the score
 // scale), their tiles take half a slot, and V, P and O stay bf16 (the precision is
 // chosen per product).
+//
+// With block-scaled fp8 Q and K (MX: OCP microscaling, one E8M0 power-of-two scale
+// per 32 consecutive head columns of a row) the first product runs on gfx950's
+// scaled MFMA, 32 x 32 x 64 per instruction.  Its k order pairs the halves of the
+// two lane groups: lane l of group g = l / 32 holds columns 16 g + [0, 16) of the
+// 64-wide block in bytes 0..15 and columns 32 + 16 g + [0, 16) in bytes 16..31, so
+// the first scale block (columns 0..31) is bytes 0..15 of both groups and the second
+// bytes 16..31; the scale byte of block g of row l % 32 is passed by lane l.  The
+// hardware applies both operands' scales to the fp32 products.  The scale bytes of
+// a tile's 32 rows ride with the tile in the ring's side buffer.
 #include "kernels.hpp"
 #include "ring.hpp"
 
@@ -43,9 +53,14 @@
 namespace gdpa {
 namespace {
 
-template <int D, int T, int NB, int ACT, int MODE>   // MODE: 0 plain, 1 RMSNorm prologue, 2 fp8 Q and K
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// MODE: 0 plain, 1 RMSNorm prologue, 2 fp8 Q and K, 3 block-scaled fp8 (MX) Q and K
+template <int D, int T, int NB, int ACT, int MODE>
 struct FwdPol {
-    static constexpr bool NORM = MODE == 1, F8 = MODE == 2;
+    static constexpr bool NORM = MODE == 1, MX = MODE == 3, F8 = MODE == 2 || MX;
+    static constexpr int NMX = MX ? D / 64 : 1;       // MX: 64-wide k blocks (one scaled MFMA each)
+    static constexpr int MXW = D / 32;                // MX: scale bytes per row, one side-load unit
     static constexpr int NSTAT = T * NB, NSTRM = 2;   // stationary tiles: wave-major q blocks
     static constexpr int NDB = D / 32, NKS = D / 16;
     static constexpr int ROWS = 32 * T * NB;          // q rows per item
@@ -58,7 +73,10 @@ struct FwdPol {
     Slice wq, wk, wv;    // issuing side: slices of the walk's current item
     Slice wrq, wrkv, wnull;   // NORM: 1/rms of the item's q rows, (k, v) row pairs; a zero-range side
     bf16x8 qf[F8 ? 1 : NB][NKS];
-    long qf8[F8 ? NB : 1][NKS];   // F8: this lane's 8 fp8 values of each 16-wide k block
+    long qf8[F8 && !MX ? NB : 1][NKS];   // F8: this lane's 8 fp8 values of each 16-wide k block
+    i32x8 qx[MX ? NB : 1][NMX];   // MX: this lane's 32 fp8 values of each 64-wide k block
+    uint32_t qsa[MX ? NB : 1][NMX];   // MX: their scale (E8M0) in the low byte
+    Slice wsq, wsk;       // MX: scale bytes of the item's q rows, of its k rows
     float rqv[NB];        // NORM: 1/rms of this lane's q row
     f32x16 acc[NB][NDB];
     // softmax only: running max (log2 units) of this lane's q row and this lane's
@@ -92,6 +110,10 @@ struct FwdPol {
             wk = slice_of((const uint8_t*)a.k + kvb, w.lk, rs / 2, D);
             wq = slice_of((const uint8_t*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs / 2, D);
             wnull = slice_of(a.q, 0, rs / 2, D);
+            if constexpr (MX) {   // D / 32 scale bytes per row, the rows of a head consecutive
+                wsq = slice_of(a.q_mx + ((size_t)w.h * a.Tq + w.qs) * (D / 32), w.lq, D / 32, D / 32);
+                wsk = slice_of(a.k_mx + ((size_t)w.h * a.Tk + w.ks) * (D / 32), w.lk, D / 32, D / 32);
+            }
         } else {
             wq = slice_of((const __bf16*)a.q + ((size_t)w.qs * H + w.h) * D, w.lq, rs, D * 2);
         }
@@ -109,7 +131,19 @@ struct FwdPol {
 
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
-        if constexpr (F8) {
+        if constexpr (MX) {   // fp8 Q, K tiles with their rows' scale bytes in the side buffer
+            if (i < NSTAT) {
+                const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * i);
+                g.template issue8<MXW>(wq, row0 * (rs / 2), wnull, wsq, row0 * (D / 32));
+            } else {
+                const int rel = i - NSTAT;
+                const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
+                if (rel & 1)
+                    g.issue(wv, row0 * rs, wnull, 0u);
+                else
+                    g.template issue8<MXW>(wk, row0 * (rs / 2), wnull, wsk, row0 * (D / 32));
+            }
+        } else if constexpr (F8) {
             if (i < NSTAT) {
                 g.issue8(wq, (uint32_t)(w.t * ROWS + 32 * i) * (rs / 2), wnull);
             } else {
@@ -120,9 +154,7 @@ struct FwdPol {
                 else
                     g.issue8(wk, row0 * (rs / 2), wnull);
             }
-            return;
-        }
-        if (i < NSTAT) {
+        } else if (i < NSTAT) {
             const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * i);
             if constexpr (NORM)
                 g.issue(wq, row0 * rs, wrq, row0 * 4u);
@@ -201,6 +233,22 @@ struct FwdPol {
         }
     }
 
+    // MX: this lane's 32 bytes of row r in 64-wide k block i8: columns 64 i8 + 16 hh
+    // + [0, 16) (first scale block) and 64 i8 + 32 + 16 hh + [0, 16) (second), the
+    // 16-byte chunks 4 i8 + hh and 4 i8 + 2 + hh of the fp8 tile
+    __device__ __forceinline__ i32x8 mx_operand(const char* tile, int i8) const {
+        const int4 lo = *(const int4*)(tile + tile8_off<D>(r, 4 * i8 + hh));
+        const int4 hi = *(const int4*)(tile + tile8_off<D>(r, 4 * i8 + 2 + hh));
+        return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+    // MX: the scale byte this lane passes, that of block 2 i8 + hh of row r (the
+    // instruction takes block hh's scale from lane group hh), from the tile's side
+    // buffer, where row r's D / 32 scale bytes sit in the 4 bytes at 4 r (d = 64: two
+    // bytes, zero-extended)
+    __device__ __forceinline__ uint32_t mx_scale(const char* side, int i8) const {
+        return (*(const uint32_t*)(side + 4 * r) >> (8 * (2 * i8 + hh))) & 0xffu;
+    }
+
     // stationary tiles i, i + 1 (jobs job, job + 1): tile u belongs to wave u / NB, block u % NB
     template <class RingT>
     __device__ __forceinline__ void load_stat(const Rec&, const RingT& g, int job, int i) {
@@ -208,7 +256,13 @@ struct FwdPol {
         for (int u = 0; u < 2; ++u) {
             const int tile = i + u;
             if (tile < NSTAT && tile / NB == wt) {
-                if constexpr (F8) {
+                if constexpr (MX) {
+#pragma unroll
+                    for (int i8 = 0; i8 < NMX; ++i8) {
+                        qx[tile % NB][i8] = mx_operand(g.tile(job + u), i8);
+                        qsa[tile % NB][i8] = mx_scale(g.side(job + u), i8);
+                    }
+                } else if constexpr (F8) {
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
                         qf8[tile % NB][ks] = *(const long*)(g.tile(job + u) + tile8_off<D>(r, ks) + 8 * hh);
@@ -256,12 +310,14 @@ struct FwdPol {
         };
         long kop8[F8 ? NKS : 1];
         if constexpr (HOIST) {
+            if constexpr (!MX) {   // (MX reads its K operands next to their MFMAs)
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                if constexpr (F8)
-                    kop8[ks] = *(const long*)(kt + tile8_off<D>(r, ks) + 8 * hh);
-                else
-                    kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if constexpr (F8)
+                        kop8[ks] = *(const long*)(kt + tile8_off<D>(r, ks) + 8 * hh);
+                    else
+                        kop[ks] = lds_row8<D>(kt, r, 2 * ks + hh);
+                }
             }
 #pragma unroll
             for (int m = 0; m < 2; ++m)
@@ -271,8 +327,19 @@ struct FwdPol {
         f32x16 sc[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) sc[b] = f32x16{};
+        if constexpr (MX) {   // S^T = K Q^T on the scaled MFMA, 64 k per instruction
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+            for (int i8 = 0; i8 < NMX; ++i8) {
+                const i32x8 ko = mx_operand(kt, i8);
+                const uint32_t ksa = mx_scale(g.side(job), i8);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                    sc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ko, qx[b][i8], sc[b], 0, 0, 0, (int)ksa, 0,
+                                                                           (int)qsa[b][i8]);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < (MX ? 0 : NKS); ++ks) {
             if constexpr (F8) {   // S^T = K Q^T on e4m3 operands, 16 k per instruction
                 const long ko = HOIST ? kop8[ks] : *(const long*)(kt + tile8_off<D>(r, ks) + 8 * hh);
 #pragma unroll
@@ -399,7 +466,7 @@ struct FwdPol {
 template <int D, int T, int NB, int ACT, int MODE>
 __global__ __launch_bounds__((TeamShape<D, T, 0>::THREADS), (TeamShape<D, T, 0>::WPE)) void fwd_bf16_kernel(
     const KernelArgs a, const Rec* __restrict__ recs, const int32_t* __restrict__ bin_ptr) {
-    using RingT = Ring<D, T, TeamShape<D, T, 0>::LDS, MODE == 1 ? 1 : 0>;
+    using RingT = Ring<D, T, TeamShape<D, T, 0>::LDS, (MODE == 1 || MODE == 3) ? 1 : 0>;
     __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
     const int wt = T > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
     const int lane = threadIdx.x & 63;
@@ -415,6 +482,18 @@ const void* kptr() {
 
 template <int T, int NB>
 const void* kptr_act(int act) {
+    if (act & kActMX) {   // block-scaled fp8 Q and K (64-wide k blocks: d >= 64)
+        if constexpr (GDPA_D >= 64) {
+            switch (act & ~kActMX) {
+                case ACT_GELU: return kptr<T, NB, ACT_GELU, 3>();
+                case ACT_SILU: return kptr<T, NB, ACT_SILU, 3>();
+                case ACT_GELU_POLY: return kptr<T, NB, ACT_GELU_POLY, 3>();
+                case ACT_GELU_TAYLOR6: return kptr<T, NB, ACT_GELU_TAYLOR6, 3>();
+                case ACT_IDENTITY: return kptr<T, NB, ACT_IDENTITY, 3>();
+            }
+        }
+        return nullptr;
+    }
     if (act & kActF8) {   // fp8 Q and K
         switch (act & ~kActF8) {
             case ACT_GELU: return kptr<T, NB, ACT_GELU, 2>();

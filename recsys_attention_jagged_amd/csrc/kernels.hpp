@@ -51,6 +51,10 @@ struct KernelArgs {
     // that the dK/dV kernel writes and the dQ kernel reads; records locate them
     // (see DsLayout)
     __bf16* ds;
+    // block-scaled fp8 forward (MX): one E8M0 scale byte per 32 consecutive head
+    // columns of each Q and K row, head-major [H, Tq, d / 32] and [H, Tk, d / 32]
+    const uint8_t* q_mx;
+    const uint8_t* k_mx;
 #ifdef GDPA_BIN_CLOCK
     // clock-probe builds only: per bin, the real-time stamps (100 MHz) of the start and
     // the end of its walk, [P][2]
@@ -67,6 +71,8 @@ constexpr int kActNorm = 16;
 
 // flag on an activation code: the forward with fp8 (OCP e4m3) Q and K
 constexpr int kActF8 = 32;
+// or'ed into the act code: the forward with block-scaled fp8 (MX) Q and K
+constexpr int kActMX = 64;
 
 // bf16 MFMA kernels, one translation unit per head dimension.  A workgroup is a
 // team of `team` waves (1, or 2 for d = 128) working on one bin (P bins, P

@@ -161,6 +161,17 @@ __device__ __forceinline__ void dma4(rsrc_t rs, uint32_t voff, uint32_t lds) {
                  : "s"(lds), "v"(voff), "s"(rs));
 }
 
+// One wave instruction: lane l's 2 bytes at byte offset `voff` land, zero-extended to
+// 4 bytes, at LDS address lds + 4 l; the range check is per 2-byte unit (a unit past
+// the end of the range reads as zero).  m0 kept as in dma16.
+__device__ __forceinline__ void dma2(rsrc_t rs, uint32_t voff, uint32_t lds) {
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tbuffer_load_ushort %2, %3, 0 offen lds\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "s"(lds), "v"(voff), "s"(rs));
+}
+
 // s_waitcnt vmcnt(J m) for a uniform m in [0, MMAX] (the count is an immediate)
 template <int J>
 __device__ __forceinline__ void wait_jobs(int m) {
@@ -285,6 +296,29 @@ struct Ring : RingGeom<D, T, LDS_BYTES, XJ> {
         for (int jj = 0; jj < G::JW / 2; ++jj) dma16(rt, off8[jj], lds + (uint32_t)(jj * T + wt) * 1024u);
 #pragma unroll
         for (int jj = G::JW / 2; jj < G::JW; ++jj) dma16(rz, 0u, lds + (uint32_t)(jj * T + wt) * 1024u);
+        ++issued;
+    }
+
+    // issue8() plus a side load from byte offset x_off of `xs` into the slot's side
+    // buffer: XW = 4, 256 bytes (lane l's 4 bytes at 4 l); XW = 2, lane l's 2 bytes
+    // at 2 l, zero-extended into the 4 bytes at 4 l (units of 2 bytes range-checked
+    // one by one, for rows of 2 bytes)
+    template <int XW = 4>
+    __device__ __forceinline__ void issue8(Slice rs, uint32_t row_off8, Slice none, Slice xs, uint32_t x_off) {
+        static_assert(XJ == 1, "side loads need side buffers");
+        static_assert(G::JW % 2 == 0, "an fp8 tile takes half of a bf16 tile's instructions");
+        const int slot = slot_of(issued);
+        const uint32_t lds = base + (uint32_t)(slot * G::TILE);
+        const rsrc_t rt = slice_at(rs, row_off8), rz = slice_at(none, 0u);
+#pragma unroll
+        for (int jj = 0; jj < G::JW / 2; ++jj) dma16(rt, off8[jj], lds + (uint32_t)(jj * T + wt) * 1024u);
+#pragma unroll
+        for (int jj = G::JW / 2; jj < G::JW; ++jj) dma16(rz, 0u, lds + (uint32_t)(jj * T + wt) * 1024u);
+        static_assert(XW == 4 || XW == 2, "side loads of 4 or 2 bytes per lane");
+        if constexpr (XW == 4)
+            dma4(slice_at(xs, x_off), xlane, base + (uint32_t)(G::R * G::TILE + slot * G::SIDE));
+        else
+            dma2(slice_at(xs, x_off), xlane >> 1, base + (uint32_t)(G::R * G::TILE + slot * G::SIDE));
         ++issued;
     }
 

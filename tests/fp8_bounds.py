@@ -49,3 +49,29 @@ def check_fp8(got, ref, what):
     rel, mx = fp8_errors(got, ref)
     assert rel <= FP8_REL_L2, f"{what}: rel L2 {rel:.3e} > {FP8_REL_L2}"
     assert mx <= FP8_MAX, f"{what}: max err {mx:.3e} of max|ref| > {FP8_MAX}"
+
+
+def quant_mx(x):
+    """OCP microscaling (MXFP8, E4M3 elements): one E8M0 scale per 32 consecutive head
+    columns of each (token, head) row.  x: [T, H, d] (d a multiple of 32).  Returns
+    (e4m3 bytes [T, H, d] as torch float8_e4m3fn, E8M0 bytes [H, T, d / 32] uint8).
+    The shared exponent of a block is floor(log2(amax)) - 8 (8: the largest e4m3
+    exponent), so the block's largest element lands in [256, 512) before rounding;
+    elements beyond 448 saturate to it.  An all-zero block takes the smallest scale."""
+    import torch
+    x = x.float().cpu()
+    T, H, d = x.shape
+    xb = x.reshape(T, H, d // 32, 32)
+    amax = xb.abs().amax(-1)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp_min(1e-38))) - 8, torch.full_like(amax, -127.0))
+    e = e.clamp(-127, 127)
+    q = (xb / torch.exp2(e)[..., None]).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).reshape(T, H, d)
+    scale = (e + 127).to(torch.uint8).permute(1, 0, 2).contiguous()
+    return q, scale
+
+
+def dequant_mx(q, scale):
+    """The values that quant_mx's bytes stand for, float64 numpy [T, H, d]."""
+    T, H, d = q.shape
+    s = np.exp2(scale.numpy().astype(np.float64) - 127.0).transpose(1, 0, 2)   # [T, H, d / 32]
+    return (q.double().numpy().reshape(T, H, d // 32, 32) * s[..., None]).reshape(T, H, d)

@@ -42,3 +42,48 @@ def test_quant_e4m3_round_trip():
     got = b.float().numpy()[0]
     np.testing.assert_array_equal(got[:5], [448.0, -448.0, 1.0, 0.0, 1.0])   # 1.0625 rounds to even
     assert got[5] == 3.25
+
+
+def test_quant_mx_blocks():
+    """Per 32-column block: scale 2^(floor(log2 amax) - 8), the largest element in
+    [256, 448] after scaling; every element within half an e4m3 ulp (2^-4 relative,
+    or 2^-10 of the block scale below the normal range) of its value, except those
+    past 448 times the scale, which saturate to it."""
+    import torch
+    from fp8_bounds import dequant_mx, quant_mx
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn((7, 3, 64), generator=g) * torch.exp(torch.randn((7, 3, 1), generator=g) * 3)
+    x[2, 1, :32] = 0.0          # an all-zero block
+    x[4, 0, 5] = 1.0e4          # one large element in a block
+    q, s = quant_mx(x)
+    assert q.shape == x.shape and s.shape == (3, 7, 2) and s.dtype == torch.uint8
+    assert int(s[1, 2, 0]) == 0 and float(q[2, 1, :32].float().abs().max()) == 0.0
+    xd = dequant_mx(q, s)
+    xb = x.double().numpy().reshape(7, 3, 2, 32)
+    amax = np.abs(xb).max(-1)
+    e = s.numpy().astype(np.int64).transpose(1, 0, 2) - 127
+    nz = amax > 0
+    assert np.array_equal(e[nz], np.floor(np.log2(amax[nz])).astype(np.int64) - 8)
+    qb = np.abs(q.float().numpy().reshape(7, 3, 2, 32)).max(-1)
+    assert np.all((qb[nz] >= 256) & (qb[nz] <= 448))
+    sc = np.exp2(e.astype(np.float64))[..., None]
+    xd = xd.reshape(7, 3, 2, 32)
+    sat = np.abs(xb) > 448 * sc
+    assert np.array_equal(xd[sat], np.sign(xb[sat]) * 448 * np.broadcast_to(sc, xb.shape)[sat])
+    err = np.abs(xd - xb)[~sat]
+    tol = np.maximum(np.abs(xb) * 2.0 ** -4, sc * 2.0 ** -10)[~sat]
+    assert np.all(err <= tol)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_mx_quantisation_error_within_the_fp8_bounds(cfg):
+    """Block scales track each block's range, so the forward's error against the bf16
+    inputs stays under the per-tensor bounds (with the same room for the kernels)."""
+    from fp8_bounds import dequant_mx, quant_mx
+    inp = make_workload(cfg, B=BATCH[cfg])
+    q8, k8 = dequant_mx(*quant_mx(inp.q)), dequant_mx(*quant_mx(inp.k))
+    got = R.gdpa_fwd(q8, k8, inp.f64("v"), inp.q_off, inp.kv_off, inp.act, inp.window)
+    ref = R.gdpa_fwd(inp.f64("q"), inp.f64("k"), inp.f64("v"), inp.q_off, inp.kv_off, inp.act, inp.window)
+    rel, mx = fp8_errors(got, ref)
+    assert rel <= FP8_REL_L2 - KERNEL_REL_L2 and mx <= FP8_MAX - KERNEL_MAX, (cfg, rel, mx)
+    assert rel >= 0.005, (cfg, rel)

@@ -21,7 +21,7 @@ import recsys_attention_jagged_amd as G
 from gdpa_workloads import WORKLOADS, make_from_lengths, make_pffn, make_workload, offsets
 from oracle import gdpa_ref as R
 from oracle import plan_ref as PR
-from fp8_bounds import check_fp8, quant_e4m3
+from fp8_bounds import check_fp8, dequant_mx, quant_e4m3, quant_mx
 
 pytestmark = pytest.mark.gpu
 
@@ -364,6 +364,99 @@ def test_fp8_forward_against_bf16_inputs(cfg):
     o, ref_q, _ = run_fp8_fwd(inp)
     check_close(o, ref_q, f"cfg{cfg} fp8 O vs the quantised values")
     check_fp8(o, oracle_fwd(inp), f"cfg{cfg} fp8 O vs the bf16 inputs")
+
+
+# block-scaled fp8 (MXFP8) Q and K in the forward
+def run_mx_fwd(inp, act=None, dtype="bf16", **opts):
+    act = act or inp.act
+    qo, ko = dev_offsets(inp)
+    q8, qs = quant_mx(inp.q)
+    k8, ks = quant_mx(inp.k)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, dtype, **opts) as plan:
+        o = torch.empty(inp.q.shape, dtype=torch.float32 if dtype == "bf16_f32out" else torch.bfloat16, device=DEV)
+        G.gdpa_mx_fwd(plan.handle, q8.view(torch.uint8).to(DEV), qs.to(DEV), k8.view(torch.uint8).to(DEV),
+                      ks.to(DEV), inp.v, qo, ko, plan.B, inp.H, inp.d, act, inp.window, o)
+        torch.cuda.synchronize()
+        n_parts = plan.stats()["n_parts"]
+    # the oracle on the values the bytes and their block scales stand for
+    ref = R.gdpa_fwd(dequant_mx(q8, qs), dequant_mx(k8, ks), inp.f64("v"), inp.q_off, inp.kv_off, act, inp.window)
+    return o.float().cpu().numpy(), ref, n_parts
+
+
+@pytest.mark.parametrize("d,team,nb", [l for l in FWD_LAYOUTS if l[0] >= 64])
+def test_mx_forward_layouts(d, team, nb):
+    say(f"MX forward d={d} team={team} blocks={nb}")
+    inp = make_from_lengths(JFA_LQ, JFA_LK, 2, d, act="silu", seed=75, device=DEV)
+    o, ref, _ = run_mx_fwd(inp, team=(team, 0, 0), blocks=(nb, 0, 0))
+    check_close(o, ref, f"MX O d={d}")
+    o32, ref, _ = run_mx_fwd(inp, dtype="bf16_f32out", team=(team, 0, 0), blocks=(nb, 0, 0))
+    check_close(o32, ref, f"MX O f32out d={d}")
+
+
+@pytest.mark.parametrize("act", ["gelu", "identity"])
+@pytest.mark.parametrize("window", [0, 17])
+def test_mx_forward_acts_windows(act, window):
+    say(f"MX forward act={act} window={window}")
+    L = [1, 31, 32, 33, 127, 300, 0, 65]
+    inp = make_from_lengths(L, L, 2, 128, act=act, window=window, seed=76, device=DEV)
+    # rows of very different scales: the block scales follow them
+    g = torch.Generator(device=DEV).manual_seed(9)
+    inp.q.mul_(torch.exp(torch.randn((inp.q.shape[0], 2, 1), generator=g, device=DEV) * 2).to(inp.q.dtype))
+    o, ref, _ = run_mx_fwd(inp)
+    check_close(o, ref, f"MX O act={act} window={window}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_mx_forward_block_scales(d):
+    """Scale blocks of one row whose magnitudes differ by 2^8 or more (q: block
+    factors 2^-6, 2^4, 2^-2, 2^6; k: 2^3, 2^-5, 2^5, 2^-1): a scale applied to the
+    wrong 32 columns moves O far outside the tolerance."""
+    say(f"MX forward, block scales far apart, d={d}")
+    L = [33, 1, 70, 31, 128]
+    inp = make_from_lengths(L, L[::-1], 2, d, act="gelu", seed=79, device=DEV)
+    nb = d // 32
+    fq = torch.tensor([2.0 ** e for e in (-6, 4, -2, 6)[:nb]], device=DEV).repeat_interleave(32)
+    fk = torch.tensor([2.0 ** e for e in (3, -5, 5, -1)[:nb]], device=DEV).repeat_interleave(32)
+    inp.q.mul_(fq.to(inp.q.dtype))
+    inp.k.mul_(fk.to(inp.k.dtype))
+    _, qs = quant_mx(inp.q)
+    _, ks = quant_mx(inp.k)
+    # in every row, the two scale blocks of each 64-column MFMA block are >= 6 octaves apart
+    assert int((qs[..., 0::2].int() - qs[..., 1::2].int()).abs().min()) >= 6
+    assert int((ks[..., 0::2].int() - ks[..., 1::2].int()).abs().min()) >= 4
+    o, ref, _ = run_mx_fwd(inp)
+    check_close(o, ref, f"MX O block scales d={d}")
+
+
+def test_mx_forward_cut_items():
+    inp = make_from_lengths([32, 1], [3000, 5], 2, 64, act="gelu", seed=77, device=DEV)
+    o, ref, n_parts = run_mx_fwd(inp, bins=(16, 16, 16))
+    assert n_parts[0] > 0
+    check_close(o, ref, "MX O cut")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_mx_forward_against_bf16_inputs(cfg):
+    """The MX forward against the oracle on the quantised values (the kernel's arithmetic)
+    and on the bf16 inputs (within the stated fp8 bounds)."""
+    say(f"cfg{cfg} MX forward, B={SMALL_B[cfg]}")
+    inp = make_workload(cfg, device=DEV, B=SMALL_B[cfg])
+    o, ref_q, _ = run_mx_fwd(inp)
+    check_close(o, ref_q, f"cfg{cfg} MX O vs the quantised values")
+    check_fp8(o, oracle_fwd(inp), f"cfg{cfg} MX O vs the bf16 inputs")
+
+
+def test_mx_forward_rejects():
+    for d, dtype, act in ((32, "bf16", "gelu"), (64, "f32", "gelu"), (64, "bf16", "one")):
+        inp = make_from_lengths([40, 3], [50, 7], 2, d, act="gelu", seed=78, device=DEV)
+        qo, ko = dev_offsets(inp)
+        b8 = torch.zeros(inp.q.shape, dtype=torch.uint8, device=DEV)
+        k8 = torch.zeros(inp.k.shape, dtype=torch.uint8, device=DEV)
+        sc = torch.full((2, 60, max(d // 32, 1)), 127, dtype=torch.uint8, device=DEV)
+        with G.Plan(inp.q_off, inp.kv_off, 2, d, 0, dtype) as plan:
+            with pytest.raises(G.GdpaError) as e:
+                G.gdpa_mx_fwd(plan.handle, b8, sc, k8, sc, inp.v, qo, ko, 2, 2, d, act, 0, torch.empty_like(inp.q))
+            assert G.STATUS[e.value.status] == "GDPA_ERR_UNSUPPORTED", (d, dtype, act)
 
 
 def test_fp8_forward_rejects():
