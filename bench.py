@@ -46,8 +46,10 @@ plain kernels' time on the same batch and the HBM floor of the unfused norm the
 prologue replaces (forward: read x, write x^; backward: read x and dx^, write dx).
 
 --fp8 runs the forward with Q and K as fp8 (OCP e4m3, one scale per tensor,
-quantised on the host before the timed region) and the backward in bf16 as gdpa_bwd
-runs it; the forward's algorithmic bytes count one byte per element of Q and K.
+quantised on the host before the timed region) and, where the plan's backward is one
+pass (every Lk <= 32 or every Lq <= 32), the backward with Q, K and dO as fp8
+(gdpa_fp8_bwd); elsewhere the backward in bf16 as gdpa_bwd runs it.  Algorithmic
+bytes count one byte per element of the fp8 tensors.
 
 --mx runs the forward with Q and K block-scaled (OCP MXFP8: e4m3 elements, one E8M0
 scale per 32 head columns of a row, quantised on the host before the timed region)
@@ -65,7 +67,7 @@ import time
 
 METRIC = "useful TFLOP/s, jagged GDPA fwd+bwd bf16, % of MFMA peak, 1 MI355X"
 METRIC_JFA = "useful TFLOP/s, jagged softmax attention (JFA) fwd+bwd bf16, 1 MI355X"
-METRIC_FP8 = "useful TFLOP/s, jagged GDPA fwd (fp8 Q, K) + bwd (bf16), 1 MI355X"
+METRIC_FP8 = "useful TFLOP/s, jagged GDPA fwd (fp8 Q, K) + bwd (fp8 Q, K, dO where one pass, else bf16), 1 MI355X"
 METRIC_MX = "useful TFLOP/s, jagged GDPA fwd (MXFP8 Q, K) + bwd (bf16), 1 MI355X"
 METRIC_NORM = "useful TFLOP/s, jagged GDPA fwd+bwd with fused RMSNorm prologue, bf16, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
@@ -87,7 +89,7 @@ def kernel_flops(H, d, pairs, Tq=0, Tk=0, ds=False):
             "rstd": 2.0 * H * d * (Tq + 2 * Tk)}
 
 
-def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0, mx=False):
+def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0, mx=False, fp8_bwd=False):
     """Algorithmic bytes per launch (bf16): every input read once, every output written
     once; softmax (JFA): plus the fp32 row LSE written by the forward, and the fp32
     (LSE, D) row pair that the pre-pass writes and the gradient kernels read; norm
@@ -95,7 +97,8 @@ def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0, mx
     pre-pass writes, after reading the tensors it normalises, and the kernels read;
     ds_bytes (a plan that stores dS): the dK/dV kernel also writes the dS blocks, and
     the dQ kernel reads them and K instead of recomputing the scores; mx (block-scaled
-    fp8 Q and K): their d / 32 E8M0 scale bytes per row and head as well."""
+    fp8 Q and K): their d / 32 E8M0 scale bytes per row and head as well; fp8_bwd (the
+    one-pass backward on fp8 Q, K, dO): one byte per element of those."""
     e = 2 * H * d
     lse, st = (4 * H * Tq, 8 * H * Tq) if softmax else (0, 0)
     rs = 4 * H * (Tq + 2 * Tk) if norm else 0
@@ -106,7 +109,8 @@ def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0, mx
     return {"fwd": int(e * (qk * Tq + qk * Tk + Tk + Tq)) + lse + rs + mxs,   # Q, K, V (, rstd) -> O (, LSE)
             "dkdv": e * (2 * Tq + 4 * Tk) + st + rs + ds_bytes,   # Q, dO, K, V (, stat or rstd) -> dK, dV (, dS)
             "dq": dq,
-            "bwd": e * (3 * Tq + 4 * Tk),               # one-pass backward: Q, dO, K, V -> dQ, dK, dV
+            "bwd": (int(e * (2 * Tq + 3.5 * Tk)) if fp8_bwd  # fp8 Q, dO, K; bf16 V -> dQ, dK, dV
+                    else e * (3 * Tq + 4 * Tk)),         # one-pass backward: Q, dO, K, V -> dQ, dK, dV
             "stat": 2 * e * Tq + lse + st,              # O, dO, LSE -> stat
             "rstd": e * (Tq * ("q" in norm) + Tk * ("k" in norm) + Tk * ("v" in norm)) + rs}
 
@@ -388,6 +392,11 @@ def main(argv=None):
         def ffwd():
             G.gdpa_fp8_fwd(h, q8, k8, inp.v, qo, ko, B, H, d, act, win, sq8, sk8, o, sh)
 
+        do8, sdo8 = quant(inp.do)
+
+        def fbwd():
+            G.gdpa_fp8_bwd(h, q8, k8, inp.v, do8, qo, ko, B, H, d, act, win, sq8, sk8, sdo8, dq, dk, dv, sh)
+
     if args.mx:
         def quant_mx(t):   # e4m3 bytes [T, H, d] and E8M0 scales [H, T, d / 32] (on the host, once)
             x = t.float().cpu()
@@ -415,7 +424,8 @@ def main(argv=None):
         calls = [("rstd", nrstd), ("fwd", nfwd), ("dkdv", ndkdv), ("dq", ndq)]
     else:
         f0 = ffwd if (args.fp8 or args.mx) else fwd
-        calls = [("fwd", f0), ("bwd", bwd)] if fused else [("fwd", f0), ("dkdv", dkdv), ("dq", dqk)]
+        b0 = fbwd if args.fp8 else bwd   # (fp8 inputs: one-pass plans)
+        calls = [("fwd", f0), ("bwd", b0)] if fused else [("fwd", f0), ("dkdv", dkdv), ("dq", dqk)]
     for _ in range(args.warmup):
         for _, c in calls:
             c()
@@ -451,7 +461,8 @@ def main(argv=None):
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
     ds_bytes = 0 if (sm or norm or fused) else st["ds_bytes"]   # what gdpa_bwd_dkdv / _dq run with
-    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8 or args.mx, ds_bytes=ds_bytes, mx=args.mx)
+    kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8 or args.mx, ds_bytes=ds_bytes, mx=args.mx,
+                      fp8_bwd=args.fp8 and bool(fused))
     kf = kernel_flops(H, d, pairs, Tq, Tk, ds=ds_bytes > 0)
     dom = max(kms, key=kms.get)
     trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "_fp8" if args.fp8 else "_mx" if args.mx else "")   # its counter record
@@ -488,6 +499,7 @@ def main(argv=None):
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs, "ds_bytes": ds_bytes,
+                   "bwd_inputs": "fp8 Q, K, dO" if args.fp8 and fused else "bf16",
                    "backward": ("one KV-stationary pass (D formed from P and dP)" if sm and fused else
                                 "dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
                                 "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else

@@ -373,12 +373,34 @@ gdpa_status gdpa_norm_bwd_dq(gdpa_plan plan, const void* q, const void* k, const
  * bf16, P is rounded to bf16 for the second product, O is bf16 (fp32 for a
  * GDPA_BF16_F32OUT plan).  Arguments otherwise as gdpa_fwd; q_scale and k_scale
  * finite and > 0 (INVALID_ARG otherwise).  bf16 plans only; act = GDPA_ACT_ONE is
- * rejected (UNSUPPORTED).  Forward only: the gradients run on bf16 inputs
- * (gdpa_bwd).
+ * rejected (UNSUPPORTED).  The gradients: gdpa_bwd on bf16 inputs, or
+ * gdpa_fp8_bwd on fp8 ones.
  */
 gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const void* v, const int32_t* q_off_dev,
                          const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act, int window, float q_scale,
                          float k_scale, void* o, void* stream);
+
+/*
+ * gdpa_fp8_bwd - GDPA backward with 8-bit Q, K and dO (GEM page, section on the
+ * custom kernels and precision: mixed ultra-low precision for attention, the
+ * precision chosen per operation).  q8, dout8 [Tq,H,d] and k8 [Tk,H,d] are OCP FP8
+ * E4M3 bytes (e4m3fn) standing for q8 * q_scale, dout8 * do_scale and
+ * k8 * k_scale; v [Tk,H,d] is bf16, as in gdpa_fp8_fwd.  S = (q8 . k8) q_scale
+ * k_scale / sqrt(d) runs on the fp8 MFMA with fp32 accumulation, dP = (dout8 . v)
+ * do_scale on the bf16 MFMA with dout8 widened to bf16 (exactly: every e4m3
+ * value is a bf16 value); P = act(S) and dS = dP act'(S) in fp32, rounded to bf16
+ * as operands of dV = P^T dout, dK = dS^T q / sqrt(d) and dQ = dS k / sqrt(d),
+ * whose fp8 operand is widened the same way; each gradient takes its input's
+ * factor and is stored as bf16 (fp32 for a GDPA_BF16_F32OUT plan), as gdpa_bwd
+ * stores them.  Runs on plans whose backward is one pass (gdpa_plan_stats.bwd_fused
+ * = 1 or 2: every Lk <= 32 or every Lq <= 32; UNSUPPORTED otherwise); bf16 plans
+ * only; act = GDPA_ACT_ONE UNSUPPORTED; factors finite and > 0 (INVALID_ARG
+ * otherwise).  Arguments otherwise as gdpa_bwd.
+ */
+gdpa_status gdpa_fp8_bwd(gdpa_plan plan, const void* q8, const void* k8, const void* v, const void* dout8,
+                         const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
+                         int window, float q_scale, float k_scale, float do_scale, void* dq, void* dk, void* dv,
+                         void* stream);
 
 /*
  * gdpa_mx_fwd - GDPA forward with block-scaled fp8 Q and K (OCP microscaling, MXFP8:

@@ -89,6 +89,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                  _vp]
     lib.gdpa_fp8_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float, ctypes.c_float,
                                  _vp, _vp]
+    lib.gdpa_fp8_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.c_float,
+                                 ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, _vp]
     lib.gdpa_norm_rstd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]
     lib.gdpa_norm_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp]
     lib.gdpa_norm_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
@@ -107,7 +109,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                  "gdpa_plan_export", "gdpa_plan_stats", "gdpa_pffn_plan_create", "gdpa_pffn_fwd",
                  "gdpa_pffn_bwd", "gdpa_jfa_fwd", "gdpa_jfa_bwd", "gdpa_jfa_bwd_stat", "gdpa_jfa_bwd_dkdv",
                  "gdpa_jfa_bwd_dq", "gdpa_norm_rstd", "gdpa_norm_fwd", "gdpa_norm_bwd", "gdpa_norm_bwd_dkdv",
-                 "gdpa_norm_bwd_dq", "gdpa_fp8_fwd"):
+                 "gdpa_norm_bwd_dq", "gdpa_fp8_fwd", "gdpa_fp8_bwd", "gdpa_mx_fwd"):
         getattr(lib, name).restype = _i
     if path == LIB_PATH:
         _lib = lib
@@ -244,6 +246,15 @@ def gdpa_fp8_fwd(plan, q8, k8, v, q_off_dev, kv_off_dev, B, H, d, act, window, q
     """GDPA forward with fp8 (e4m3fn) Q and K standing for q8 * q_scale, k8 * k_scale; V and O bf16."""
     _check(load_library().gdpa_fp8_fwd(plan, _ptr(q8), _ptr(k8), _ptr(v), _ptr(q_off_dev), _ptr(kv_off_dev), B, H, d,
                                        _enum(act, ACT), window, float(q_scale), float(k_scale), _ptr(o),
+                                       _stream(stream)))
+
+
+def gdpa_fp8_bwd(plan, q8, k8, v, do8, q_off_dev, kv_off_dev, B, H, d, act, window, q_scale, k_scale, do_scale,
+                 dq, dk, dv, stream=None):
+    """GDPA backward with fp8 (e4m3fn) Q, K, dO standing for q8 * q_scale, k8 * k_scale, do8 * do_scale; V bf16."""
+    _check(load_library().gdpa_fp8_bwd(plan, _ptr(q8), _ptr(k8), _ptr(v), _ptr(do8), _ptr(q_off_dev),
+                                       _ptr(kv_off_dev), B, H, d, _enum(act, ACT), window, float(q_scale),
+                                       float(k_scale), float(do_scale), _ptr(dq), _ptr(dk), _ptr(dv),
                                        _stream(stream)))
 
 

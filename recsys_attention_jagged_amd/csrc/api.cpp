@@ -576,14 +576,29 @@ gdpa_status gdpa_fwd_noalloc(gdpa_plan plan, const void* q, const void* k, const
     return GDPA_OK;
 }
 
+// per-tensor factors of the fp8 backward's inputs (value = e4m3 byte's value * factor)
+struct F8Factors {
+    float q, k, dout;
+};
+
 static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,
                              const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d,
                              gdpa_act act, int window, void* dq, void* dk, void* dv, void* stream,
-                             bool want_dkdv, bool want_dq) {
+                             bool want_dkdv, bool want_dq, const F8Factors* f8 = nullptr) {
     g_err.clear();
     gdpa_status st = check_call(plan, q_off_dev, kv_off_dev, B, H, d, act, window);
     if (st != GDPA_OK) return st;
     if (act == GDPA_ACT_ONE) return fail(GDPA_ERR_UNSUPPORTED, "GDPA_ACT_ONE has no backward");
+    if (f8) {
+        if (plan->dtype == GDPA_F32) return fail(GDPA_ERR_UNSUPPORTED, "fp8 inputs run on bf16 plans");
+        for (float x : {f8->q, f8->k, f8->dout})
+            if (!(x > 0.0f) || !std::isfinite(x))
+                return fail(GDPA_ERR_INVALID_ARG, "q_scale, k_scale and do_scale must be finite and > 0");
+        if (!plan->fused)
+            return fail(GDPA_ERR_UNSUPPORTED,
+                        "the fp8 backward runs on plans whose backward is one pass (every Lk <= 32 or every "
+                        "Lq <= 32, see gdpa_plan_stats.bwd_fused)");
+    }
     const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
     if (any_q && (!q || !dout)) return fail(GDPA_ERR_INVALID_ARG, "q or dout is NULL");
     if (any_k && (!k || !v)) return fail(GDPA_ERR_INVALID_ARG, "k or v is NULL");
@@ -598,6 +613,20 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
+    // output factors of dQ, dK, dV (the fp8 inputs' factors folded in)
+    float mq = a.scale, mk = a.scale, mv = 1.0f;
+    int code = (int)act;
+    if (f8) {
+        mq = a.scale * f8->k;          // dQ = (dS k8) s_k / sqrt(d)
+        mk = a.scale * f8->q;          // dK = (dS^T q8) s_q / sqrt(d)
+        mv = f8->dout;                 // dV = (P^T do8) s_do
+        a.f8_dp = f8->dout;            // dP = (do8 v^T) s_do
+        a.f8_dq = mq;
+        a.f8_dk = mk;
+        a.f8_dv = mv;
+        a.scale *= f8->q * f8->k;      // S = (q8 k8^T) s_q s_k / sqrt(d)
+        code |= kActF8Bwd;
+    }
     hipError_t e = hipSuccess;
     if (plan->dtype == GDPA_F32) {
         e = launch_bwd_f32(a, want_dq ? (int)plan->Tq : 0, want_dkdv ? (int)plan->Tk : 0, d, act, s);
@@ -610,13 +639,13 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
         const int kv = plan->fused == 1;
         b.part = plan->d_part[l];
         switch (d) {
-            case 32: e = launch_bwd_fused_d32(b, kv, act, s); break;
-            case 64: e = launch_bwd_fused_d64(b, kv, act, s); break;
-            default: e = launch_bwd_fused_d128(b, kv, act, s); break;
+            case 32: e = launch_bwd_fused_d32(b, kv, code, s); break;
+            case 64: e = launch_bwd_fused_d64(b, kv, code, s); break;
+            default: e = launch_bwd_fused_d128(b, kv, code, s); break;
         }
-        if (e == hipSuccess && !kv) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
-        if (e == hipSuccess && kv) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
-        if (e == hipSuccess && kv) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
+        if (e == hipSuccess && !kv) e = reduce_parts(plan, LIST_DQ, mq, dq, s);
+        if (e == hipSuccess && kv) e = reduce_parts(plan, LIST_DKDV, mk, dk, s, 0);
+        if (e == hipSuccess && kv) e = reduce_parts(plan, LIST_DKDV, mv, dv, s, 1);
     } else if (plan->use_ds) {
         // dK/dV storing dS, then dQ = dS K / sqrt(d) from the stored blocks (the two
         // halves separately: gdpa_bwd_dq reads what gdpa_bwd_dkdv stored)
@@ -684,6 +713,15 @@ gdpa_status gdpa_bwd(gdpa_plan plan, const void* q, const void* k, const void* v
                      gdpa_act act, int window, void* dq, void* dk, void* dv, void* stream) {
     return bwd_parts(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, window, dq, dk, dv, stream,
                      true, true);
+}
+
+gdpa_status gdpa_fp8_bwd(gdpa_plan plan, const void* q8, const void* k8, const void* v, const void* do8,
+                         const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,
+                         int window, float q_scale, float k_scale, float do_scale, void* dq, void* dk, void* dv,
+                         void* stream) {
+    const F8Factors f8{q_scale, k_scale, do_scale};
+    return bwd_parts(plan, q8, k8, v, do8, q_off_dev, kv_off_dev, B, H, d, act, window, dq, dk, dv, stream, true,
+                     true, &f8);
 }
 
 gdpa_status gdpa_bwd_dkdv(gdpa_plan plan, const void* q, const void* k, const void* v, const void* dout,

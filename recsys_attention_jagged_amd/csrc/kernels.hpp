@@ -55,6 +55,11 @@ struct KernelArgs {
     // columns of each Q and K row, head-major [H, Tq, d / 32] and [H, Tk, d / 32]
     const uint8_t* q_mx;
     const uint8_t* k_mx;
+    // fp8 backward (Q, K, dO as e4m3 with one factor per tensor, V bf16): `scale` is
+    // then the score factor s_q s_k / sqrt(d); dP is the product times f8_dp = s_do;
+    // the stored dQ, dK, dV are their products times f8_dq = s_k / sqrt(d),
+    // f8_dk = s_q / sqrt(d), f8_dv = s_do
+    float f8_dp, f8_dq, f8_dk, f8_dv;
 #ifdef GDPA_BIN_CLOCK
     // clock-probe builds only: per bin, the real-time stamps (100 MHz) of the start and
     // the end of its walk, [P][2]
@@ -73,6 +78,8 @@ constexpr int kActNorm = 16;
 constexpr int kActF8 = 32;
 // or'ed into the act code: the forward with block-scaled fp8 (MX) Q and K
 constexpr int kActMX = 64;
+// or'ed into the act code of a backward kernel: Q, K and dO as fp8 (e4m3)
+constexpr int kActF8Bwd = 128;
 
 // bf16 MFMA kernels, one translation unit per head dimension.  A workgroup is a
 // team of `team` waves (1, or 2 for d = 128) working on one bin (P bins, P

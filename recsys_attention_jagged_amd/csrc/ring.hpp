@@ -102,6 +102,41 @@ __device__ __forceinline__ int tile8_off(int row, int chunk) {
     return row * D + ((chunk ^ swz8<D>(row)) << 4);
 }
 
+// fp8 tiles: the 8 e4m3 bytes of `row`, columns [16 ks + 8 half, + 8): the fp8
+// MFMA's operand for 16-wide k block ks, lane group `half` (the bf16 operand
+// lds_row8(tile, row, 2 ks + half) holds the same columns)
+template <int D>
+__device__ __forceinline__ long lds_row8_f8(const char* tile, int row, int ks, int half) {
+    return *(const long*)(tile + tile8_off<D>(row, ks) + 8 * half);
+}
+
+// 8 e4m3 values (bytes 0..3 of lo, then of hi) as bf16; exact, since every e4m3
+// value is a bf16 value
+__device__ __forceinline__ bf16x8 widen_e4m3(int lo, int hi) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const auto e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
+}
+
+// lds_col8 of an fp8 tile, widened to bf16: lane l receives rows row0 + {0..3} +
+// 4 (l/32), then row0 + 8 + {0..3} + 4 (l/32), of column col0 + l % 32 (col0 a
+// multiple of 32), in one 8-bit transposing read.  Within each 16-lane group of
+// that read, byte i of lane j is byte j % 8 of the 8 bytes addressed by lane
+// 2 i + j / 8, so lane 2 i + c addresses the group's i-th row at the columns
+// col0 + 16 (group % 2) + 8 c ..
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col8_f8(const char* tile, int row0, int col0, int lane) {
+    const int grp = lane >> 4, j = lane & 15;
+    const int i = j >> 1, c = j & 1;
+    const int row = row0 + 4 * (lane >> 5) + (i & 3) + 8 * (i >> 2);
+    const int off = tile8_off<D>(row, (col0 >> 4) + (grp & 1)) + 8 * c;
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(tile + off));
+    return widen_e4m3(v.x, v.y);
+}
+
 // 8 bf16 of `row`, columns [8 chunk, 8 chunk + 8)
 template <int D>
 __device__ __forceinline__ bf16x8 lds_row8(const char* tile, int row, int chunk) {

@@ -459,6 +459,117 @@ def test_mx_forward_rejects():
             assert G.STATUS[e.value.status] == "GDPA_ERR_UNSUPPORTED", (d, dtype, act)
 
 
+# ---------------------------------------------------------------------------
+# fp8 (e4m3fn) Q, K and dO in the backward (V bf16)
+# ---------------------------------------------------------------------------
+
+def run_fp8_bwd(inp, act=None, dtype="bf16", **opts):
+    """gdpa_fp8_bwd on per-tensor e4m3 Q, K, dO; the oracle on the values the bytes stand for."""
+    act = act or inp.act
+    qo, ko = dev_offsets(inp)
+    q8, sq = quant_e4m3(inp.q)
+    k8, sk = quant_e4m3(inp.k)
+    o8, so = quant_e4m3(inp.do)
+    odt = torch.float32 if dtype == "bf16_f32out" else torch.bfloat16
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, dtype, **opts) as plan:
+        dq = torch.empty(inp.q.shape, dtype=odt, device=DEV)
+        dk = torch.empty(inp.k.shape, dtype=odt, device=DEV)
+        dv = torch.empty(inp.v.shape, dtype=odt, device=DEV)
+        G.gdpa_fp8_bwd(plan.handle, q8.view(torch.uint8).to(DEV), k8.view(torch.uint8).to(DEV), inp.v,
+                       o8.view(torch.uint8).to(DEV), qo, ko, plan.B, inp.H, inp.d, act, inp.window, sq, sk, so,
+                       dq, dk, dv)
+        torch.cuda.synchronize()
+        st = plan.stats()
+    ref = R.gdpa_bwd(q8.double().numpy() * sq, k8.double().numpy() * sk, inp.f64("v"), o8.double().numpy() * so,
+                     inp.q_off, inp.kv_off, act, inp.window)
+    return tuple(t.float().cpu().numpy() for t in (dq, dk, dv)), ref, st
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("case", range(len(FUSED_CASES)))
+def test_fp8_backward_one_pass(d, case):
+    """Both one-pass shapes (KV- and Q-stationary), windows, empty and one-row samples,
+    bf16 and fp32 outputs."""
+    lq, lk, window = FUSED_CASES[case]
+    say(f"fp8 backward d={d} case={case}")
+    inp = make_from_lengths(lq, lk, 3, d, act="gelu", window=window, seed=81 + case, device=DEV)
+    for dtype in ("bf16", "bf16_f32out"):
+        got, ref, st = run_fp8_bwd(inp, dtype=dtype)
+        assert st["bwd_fused"] == (1 if case != 1 else 2)
+        for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+            check_close(a, b, f"fp8 {name} d={d} case={case} {dtype}")
+
+
+@pytest.mark.parametrize("act", ["silu", "identity", "gelu_taylor6"])
+def test_fp8_backward_acts(act):
+    say(f"fp8 backward act={act}")
+    for case in (0, 1):
+        lq, lk, _ = FUSED_CASES[case]
+        inp = make_from_lengths(lq, lk, 2, 64, act=act, seed=85 + case, device=DEV)
+        got, ref, _ = run_fp8_bwd(inp)
+        for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+            check_close(a, b, f"fp8 {name} act={act} case={case}")
+
+
+@pytest.mark.parametrize("case", [0, 2])
+def test_fp8_backward_cut_items(case):
+    """Items longer than a mean bin, cut into chunks whose fp32 partials the reduction
+    scales by the gradients' fp8 factors."""
+    lq, lk, bins, _, fused = CHUNK_CASES[case]
+    say(f"fp8 backward cut items case={case}")
+    inp = make_from_lengths(lq, lk, 2, 64, act="gelu", seed=87 + case, device=DEV)
+    got, ref, st = run_fp8_bwd(inp, bins=bins)
+    assert st["bwd_fused"] == fused and sum(st["n_parts"]) > 0
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        check_close(a, b, f"fp8 {name} cut case={case}")
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_fp8_backward_against_bf16_inputs(cfg):
+    """The fp8 backward against the oracle on the quantised values (the kernels'
+    arithmetic) and on the bf16 inputs (within the stated fp8 bounds), on the two
+    workloads whose backward is one pass."""
+    say(f"cfg{cfg} fp8 backward, B={SMALL_B[cfg]}")
+    inp = make_workload(cfg, device=DEV, B=SMALL_B[cfg])
+    got, ref_q, st = run_fp8_bwd(inp)
+    assert st["bwd_fused"] in (1, 2)
+    for name, a, b, c in zip(("dQ", "dK", "dV"), got, ref_q, oracle_bwd(inp)):
+        check_close(a, b, f"cfg{cfg} fp8 {name} vs the quantised values")
+        check_fp8(a, c, f"cfg{cfg} fp8 {name} vs the bf16 inputs")
+
+
+def test_fp8_backward_rejects():
+    lq, lk = [40, 3], [50, 7]   # neither side within one tile: two-kernel backward
+    inp = make_from_lengths(lq, lk, 2, 64, act="gelu", seed=89, device=DEV)
+    qo, ko = dev_offsets(inp)
+    q8 = torch.zeros(inp.q.shape, dtype=torch.uint8, device=DEV)
+    k8 = torch.zeros(inp.k.shape, dtype=torch.uint8, device=DEV)
+    o8 = torch.zeros(inp.q.shape, dtype=torch.uint8, device=DEV)
+    g = [torch.empty_like(t) for t in (inp.q, inp.k, inp.v)]
+    with G.Plan(inp.q_off, inp.kv_off, 2, 64, 0, "bf16") as plan:
+        assert plan.stats()["bwd_fused"] == 0
+        with pytest.raises(G.GdpaError) as e:
+            G.gdpa_fp8_bwd(plan.handle, q8, k8, inp.v, o8, qo, ko, 2, 2, 64, "gelu", 0, 1.0, 1.0, 1.0, *g)
+        assert G.STATUS[e.value.status] == "GDPA_ERR_UNSUPPORTED"
+    one = make_from_lengths([40, 3], [32, 7], 2, 64, act="gelu", seed=89, device=DEV)
+    qo, ko = dev_offsets(one)
+    k8 = torch.zeros(one.k.shape, dtype=torch.uint8, device=DEV)
+    g = [torch.empty_like(t) for t in (one.q, one.k, one.v)]
+    with G.Plan(one.q_off, one.kv_off, 2, 64, 0, "bf16") as plan:
+        assert plan.stats()["bwd_fused"] == 1
+        for act, scales, status in (("one", (1.0, 1.0, 1.0), "GDPA_ERR_UNSUPPORTED"),
+                                    ("gelu", (0.0, 1.0, 1.0), "GDPA_ERR_INVALID_ARG"),
+                                    ("gelu", (1.0, float("inf"), 1.0), "GDPA_ERR_INVALID_ARG"),
+                                    ("gelu", (1.0, 1.0, -1.0), "GDPA_ERR_INVALID_ARG")):
+            with pytest.raises(G.GdpaError) as e:
+                G.gdpa_fp8_bwd(plan.handle, q8, k8, one.v, o8, qo, ko, 2, 2, 64, act, 0, *scales, *g)
+            assert G.STATUS[e.value.status] == status
+    with G.Plan(one.q_off, one.kv_off, 2, 64, 0, "f32") as plan:
+        with pytest.raises(G.GdpaError) as e:
+            G.gdpa_fp8_bwd(plan.handle, q8, k8, one.v, o8, qo, ko, 2, 2, 64, "gelu", 0, 1.0, 1.0, 1.0, *g)
+        assert G.STATUS[e.value.status] == "GDPA_ERR_UNSUPPORTED"
+
+
 def test_fp8_forward_rejects():
     inp = make_from_lengths([40, 3], [50, 7], 2, 64, act="gelu", seed=74, device=DEV)
     qo, ko = dev_offsets(inp)
