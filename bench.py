@@ -46,10 +46,10 @@ plain kernels' time on the same batch and the HBM floor of the unfused norm the
 prologue replaces (forward: read x, write x^; backward: read x and dx^, write dx).
 
 --fp8 runs the forward with Q and K as fp8 (OCP e4m3, one scale per tensor,
-quantised on the host before the timed region) and, where the plan's backward is one
-pass (every Lk <= 32 or every Lq <= 32), the backward with Q, K and dO as fp8
-(gdpa_fp8_bwd); elsewhere the backward in bf16 as gdpa_bwd runs it.  Algorithmic
-bytes count one byte per element of the fp8 tensors.
+quantised on the host before the timed region) and the backward with Q, K and dO as
+fp8 (gdpa_fp8_bwd: plans whose backward is one pass, or d = 128 plans that store
+dS; timed as one call); elsewhere the backward in bf16 as gdpa_bwd runs it.
+Algorithmic bytes count one byte per element of the fp8 tensors.
 
 --mx runs the forward with Q and K block-scaled (OCP MXFP8: e4m3 elements, one E8M0
 scale per 32 head columns of a row, quantised on the host before the timed region)
@@ -98,7 +98,8 @@ def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0, mx
     ds_bytes (a plan that stores dS): the dK/dV kernel also writes the dS blocks, and
     the dQ kernel reads them and K instead of recomputing the scores; mx (block-scaled
     fp8 Q and K): their d / 32 E8M0 scale bytes per row and head as well; fp8_bwd (the
-    one-pass backward on fp8 Q, K, dO): one byte per element of those."""
+    backward on fp8 Q, K, dO, one pass or, with ds_bytes, dK/dV storing dS and dQ from
+    it, as one "bwd" entry): one byte per element of those."""
     e = 2 * H * d
     lse, st = (4 * H * Tq, 8 * H * Tq) if softmax else (0, 0)
     rs = 4 * H * (Tq + 2 * Tk) if norm else 0
@@ -109,7 +110,8 @@ def kernel_bytes(H, d, Tq, Tk, softmax=False, norm="", fp8=False, ds_bytes=0, mx
     return {"fwd": int(e * (qk * Tq + qk * Tk + Tk + Tq)) + lse + rs + mxs,   # Q, K, V (, rstd) -> O (, LSE)
             "dkdv": e * (2 * Tq + 4 * Tk) + st + rs + ds_bytes,   # Q, dO, K, V (, stat or rstd) -> dK, dV (, dS)
             "dq": dq,
-            "bwd": (int(e * (2 * Tq + 3.5 * Tk)) if fp8_bwd  # fp8 Q, dO, K; bf16 V -> dQ, dK, dV
+            "bwd": (e * (2 * Tq + 4 * Tk) + 2 * ds_bytes if fp8_bwd and ds_bytes  # + K again, dS out and in
+                    else int(e * (2 * Tq + 3.5 * Tk)) if fp8_bwd  # fp8 Q, dO, K; bf16 V -> dQ, dK, dV
                     else e * (3 * Tq + 4 * Tk)),         # one-pass backward: Q, dO, K, V -> dQ, dK, dV
             "stat": 2 * e * Tq + lse + st,              # O, dO, LSE -> stat
             "rstd": e * (Tq * ("q" in norm) + Tk * ("k" in norm) + Tk * ("v" in norm)) + rs}
@@ -418,14 +420,17 @@ def main(argv=None):
     # kernels (the norm prologue: always the two kernels, after its pre-pass; JFA: one
     # pass only where every Lk <= 32)
     fused = 0 if norm else (int(st["bwd_fused"] == 1) if sm else st["bwd_fused"])
+    fp8_bwd = args.fp8 and bool(fused or st["ds_bytes"] > 0)   # plans gdpa_fp8_bwd runs on
     if sm:
         calls = [("fwd", jfwd), ("bwd", jbwd)] if fused else [("fwd", jfwd), ("dq", jdq), ("dkdv", jdkdv)]
     elif norm:
         calls = [("rstd", nrstd), ("fwd", nfwd), ("dkdv", ndkdv), ("dq", ndq)]
     else:
         f0 = ffwd if (args.fp8 or args.mx) else fwd
-        b0 = fbwd if args.fp8 else bwd   # (fp8 inputs: one-pass plans)
-        calls = [("fwd", f0), ("bwd", b0)] if fused else [("fwd", f0), ("dkdv", dkdv), ("dq", dqk)]
+        if fp8_bwd:   # one call (one pass, or dK/dV storing dS then dQ from it)
+            calls = [("fwd", f0), ("bwd", fbwd)]
+        else:
+            calls = [("fwd", f0), ("bwd", bwd)] if fused else [("fwd", f0), ("dkdv", dkdv), ("dq", dqk)]
     for _ in range(args.warmup):
         for _, c in calls:
             c()
@@ -460,9 +465,9 @@ def main(argv=None):
 
     useful = 14.0 * H * d * pairs
     value = useful / (ms_step * 1e-3) / 1e12
-    ds_bytes = 0 if (sm or norm or fused) else st["ds_bytes"]   # what gdpa_bwd_dkdv / _dq run with
+    ds_bytes = 0 if (sm or norm or fused) else st["ds_bytes"]   # what gdpa_bwd_dkdv / _dq (or fp8) run with
     kb = kernel_bytes(H, d, Tq, Tk, softmax=sm, norm=norm, fp8=args.fp8 or args.mx, ds_bytes=ds_bytes, mx=args.mx,
-                      fp8_bwd=args.fp8 and bool(fused))
+                      fp8_bwd=fp8_bwd)
     kf = kernel_flops(H, d, pairs, Tq, Tk, ds=ds_bytes > 0)
     dom = max(kms, key=kms.get)
     trace_name = w["name"] + ("_jfa" if sm else "_norm" if norm else "_fp8" if args.fp8 else "_mx" if args.mx else "")   # its counter record
@@ -481,7 +486,7 @@ def main(argv=None):
     kernels = {n: {"ms": round(kms[n], 4), "alg_GBps": round(kb[n] / (kms[n] * 1e-3) / 1e9, 1)}
                for n in kms}
     kernels["fwd"]["useful_TFLOPs"] = round(4.0 * H * d * pairs / (kms["fwd"] * 1e-3) / 1e12, 2)
-    bwd_ms = kms["bwd"] if fused else kms["dkdv"] + kms["dq"] + kms.get("stat", 0.0)
+    bwd_ms = kms["bwd"] if "bwd" in kms else kms["dkdv"] + kms["dq"] + kms.get("stat", 0.0)
 
     out = {
         "metric": (METRIC_JFA if sm else METRIC_NORM if norm else METRIC_FP8 if args.fp8 else
@@ -499,7 +504,7 @@ def main(argv=None):
         "data": "synthetic (seeded jagged lengths and N(0,1) values; see gdpa_workloads)",
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs, "ds_bytes": ds_bytes,
-                   "bwd_inputs": "fp8 Q, K, dO" if args.fp8 and fused else "bf16",
+                   "bwd_inputs": "fp8 Q, K, dO" if fp8_bwd else "bf16",
                    "backward": ("one KV-stationary pass (D formed from P and dP)" if sm and fused else
                                 "dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
                                 "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else

@@ -393,9 +393,10 @@ gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const v
  * whose fp8 operand is widened the same way; each gradient takes its input's
  * factor and is stored as bf16 (fp32 for a GDPA_BF16_F32OUT plan), as gdpa_bwd
  * stores them.  Runs on plans whose backward is one pass (gdpa_plan_stats.bwd_fused
- * = 1 or 2: every Lk <= 32 or every Lq <= 32; UNSUPPORTED otherwise); bf16 plans
- * only; act = GDPA_ACT_ONE UNSUPPORTED; factors finite and > 0 (INVALID_ARG
- * otherwise).  Arguments otherwise as gdpa_bwd.
+ * = 1 or 2: every Lk <= 32 or every Lq <= 32) or, at d = 128, the dK/dV kernel
+ * storing dS followed by dQ from the stored blocks (gdpa_plan_stats.ds_bytes > 0);
+ * UNSUPPORTED otherwise.  bf16 plans only; act = GDPA_ACT_ONE UNSUPPORTED; factors
+ * finite and > 0 (INVALID_ARG otherwise).  Arguments otherwise as gdpa_bwd.
  */
 gdpa_status gdpa_fp8_bwd(gdpa_plan plan, const void* q8, const void* k8, const void* v, const void* dout8,
                          const int32_t* q_off_dev, const int32_t* kv_off_dev, int B, int H, int d, gdpa_act act,

@@ -594,10 +594,10 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
         for (float x : {f8->q, f8->k, f8->dout})
             if (!(x > 0.0f) || !std::isfinite(x))
                 return fail(GDPA_ERR_INVALID_ARG, "q_scale, k_scale and do_scale must be finite and > 0");
-        if (!plan->fused)
+        if (!plan->fused && !plan->use_ds)
             return fail(GDPA_ERR_UNSUPPORTED,
                         "the fp8 backward runs on plans whose backward is one pass (every Lk <= 32 or every "
-                        "Lq <= 32, see gdpa_plan_stats.bwd_fused)");
+                        "Lq <= 32) or the d = 128 stored-dS kernels (gdpa_plan_stats: bwd_fused, ds_bytes)");
     }
     const bool any_q = plan->Tq > 0, any_k = plan->Tk > 0;
     if (any_q && (!q || !dout)) return fail(GDPA_ERR_INVALID_ARG, "q or dout is NULL");
@@ -657,9 +657,9 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.P = wl.P;
             b.part = plan->d_part[LIST_DKDV];
             b.ds = plan->d_ds;
-            e = launch_dkdv_bf16_d128(b, wl.team, wl.nb, act, s);
-            if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, a.scale, dk, s, 0);
-            if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, 1.0f, dv, s, 1);
+            e = launch_dkdv_bf16_d128(b, wl.team, wl.nb, code, s);
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, mk, dk, s, 0);
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, mv, dv, s, 1);
         }
         if (e == hipSuccess && want_dq && any_q) {
             const WorkList& wl = plan->lists[LIST_DQ];
@@ -669,8 +669,8 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             b.P = wl.P;
             b.part = plan->d_part[LIST_DQ];
             b.ds = plan->d_ds;
-            e = launch_dq_from_ds(b, s);
-            if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, a.scale, dq, s);
+            e = launch_dq_from_ds(b, f8 != nullptr, s);
+            if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, mq, dq, s);
         }
     } else {
         if (want_dkdv && any_k) {

@@ -19,6 +19,12 @@
 // with transposing LDS loads).  Half the register state of a 32-row wave lets two
 // waves share each SIMD, so one wave's activation overlaps the other's products.
 // No atomics: every dK, dV row has one owner.
+//
+// With fp8 inputs (F8: Q, K and dO as e4m3 bytes, one factor per tensor; V bf16)
+// their tiles are one byte per element in the first half of a slot; S runs on the
+// 16 x 16 x 32 fp8 MFMA from row reads, dO's rows are widened exactly to bf16 for
+// dP, and the transposed Q and dO operands come from 8-bit transposing reads,
+// widened the same way.
 #include "bwd_common.hpp"
 #include "kernels.hpp"
 #include "ring.hpp"
@@ -63,7 +69,33 @@ __device__ __forceinline__ bf16x8 lds_col8_16(const char* tile, int row0, int co
     return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-template <int ACT, int T>
+// lds_col8_16 (row0 = 0) of an fp8 tile (ring.hpp's fp8 layout), widened to bf16, in
+// one 8-bit transposing read: within each 16-lane group, byte i of lane j is byte
+// j % 8 of the 8 bytes addressed by lane 2 i + j / 8, so lane 2 i + c addresses the
+// group's i-th row (4 (l / 16) + {0..3}, then 16 + 4 (l / 16) + {0..3}) at columns
+// col0 + 8 c ..  (col0 a multiple of 16)
+template <int D>
+__device__ __forceinline__ bf16x8 lds_col8_16_f8(const char* tile, int col0, int lane) {
+    const int j = lane & 15, i = j >> 1, c = j & 1;
+    const int row = 4 * (lane >> 4) + (i & 3) + 16 * (i >> 2);
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i*)(tile + tile8_off<D>(row, col0 >> 4) + 8 * c));
+    return widen_e4m3(v.x, v.y);
+}
+
+// 8 e4m3 bytes of `row`, columns [8 c8, 8 c8 + 8) of an fp8 tile (the operand that
+// row8_16(tile, row, c8) is for a bf16 one)
+template <int D>
+__device__ __forceinline__ long row8_16_f8(const char* tile, int row, int c8) {
+    return lds_row8_f8<D>(tile, row, c8 >> 1, c8 & 1);
+}
+
+__device__ __forceinline__ f32x4 mfma16_f8(long a, long b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+template <int ACT, int T, bool F8 = false>
 struct Dkdv16Pol : Common {
     static constexpr int D = 128;
     static constexpr int ROWS = 16 * T;          // kv rows per item
@@ -71,7 +103,9 @@ struct Dkdv16Pol : Common {
     static constexpr int NKB = D / 32;           // 32-wide head-dimension blocks (contraction of S, dP)
     static constexpr int NCB = D / 16;           // 16-wide head-dimension blocks (dK, dV columns)
     Slice wk, wv, wq, wo;                       // issuing side
-    bf16x8 kf[NKB], vf[NKB];                     // this wave's 16 kv rows of K and V (B operands)
+    Slice wnull;                                 // F8: a zero-range tile
+    bf16x8 kf[F8 ? 1 : NKB], vf[NKB];            // this wave's 16 kv rows of K and V (B operands)
+    long kf8[F8 ? NKB : 1];                      // F8: the K rows as fp8 operands
     f32x4 accK[NCB], accV[NCB];                  // lane: kv row l % 16, columns 16 cb + 4 (l / 16) + {0..3}
     int l16, g4;                                 // lane % 16, lane / 16
 
@@ -85,20 +119,40 @@ struct Dkdv16Pol : Common {
 
     __device__ __forceinline__ void walk_item(const Rec& w) {
         const size_t kvb = ((size_t)w.ks * H + w.h) * D;
-        wk = slice_of((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
-        wv = slice_of((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
         const size_t qb = ((size_t)w.qs * H + w.h) * D;
-        wq = slice_of((const __bf16*)a.q + qb, w.lq, rs, D * 2);
-        wo = slice_of((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        wv = slice_of((const __bf16*)a.v + kvb, w.lk, rs, D * 2);
+        if constexpr (F8) {   // one-byte rows, H D bytes apart
+            wk = slice_of((const uint8_t*)a.k + kvb, w.lk, rs / 2, D);
+            wq = slice_of((const uint8_t*)a.q + qb, w.lq, rs / 2, D);
+            wo = slice_of((const uint8_t*)a.dout + qb, w.lq, rs / 2, D);
+            wnull = slice_of(a.q, 0, rs / 2, D);
+        } else {
+            wk = slice_of((const __bf16*)a.k + kvb, w.lk, rs, D * 2);
+            wq = slice_of((const __bf16*)a.q + qb, w.lq, rs, D * 2);
+            wo = slice_of((const __bf16*)a.dout + qb, w.lq, rs, D * 2);
+        }
+    }
+
+    template <class RingT>
+    __device__ __forceinline__ void ring_ready(RingT& g, int lane_) {
+        if constexpr (F8) g.init8(rs / 2, lane_);
     }
 
     template <class RingT>
     __device__ __forceinline__ void issue_job(RingT& g, const Rec& w, int i) {
         if (i < NSTAT) {   // tile i / 2 of the item: K (i even), V (i odd)
-            g.issue((i & 1) ? wv : wk, (uint32_t)(w.t * ROWS + 32 * (i >> 1)) * rs);
+            const uint32_t row0 = (uint32_t)(w.t * ROWS + 32 * (i >> 1));
+            if (F8 && !(i & 1))
+                g.issue8(wk, row0 * (rs / 2), wnull);
+            else
+                g.issue((i & 1) ? wv : wk, row0 * rs);
         } else {
             const int rel = i - NSTAT;
-            g.issue((rel & 1) ? wo : wq, (uint32_t)((w.s0 + (rel >> 1)) * 32) * rs);
+            const uint32_t row0 = (uint32_t)((w.s0 + (rel >> 1)) * 32);
+            if constexpr (F8)
+                g.issue8((rel & 1) ? wo : wq, row0 * (rs / 2), wnull);
+            else
+                g.issue((rel & 1) ? wo : wq, row0 * rs);
         }
     }
 
@@ -115,7 +169,10 @@ struct Dkdv16Pol : Common {
         if ((wt >> 1) != (i >> 1)) return;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            kf[kb] = row8_16<D>(g.tile(job), 16 * (wt & 1) + l16, 4 * kb + g4);
+            if constexpr (F8)
+                kf8[kb] = row8_16_f8<D>(g.tile(job), 16 * (wt & 1) + l16, 4 * kb + g4);
+            else
+                kf[kb] = row8_16<D>(g.tile(job), 16 * (wt & 1) + l16, 4 * kb + g4);
             vf[kb] = row8_16<D>(g.tile(job + 1), 16 * (wt & 1) + l16, 4 * kb + g4);
         }
     }
@@ -159,32 +216,59 @@ struct Dkdv16Pol : Common {
         // read and a wait): the Q and dO row operands, then the products for S and dP,
         // then the transposed operands of the second products, which land while the
         // activation runs.
-        bf16x8 qo[2][NKB], oo[2][NKB];
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                qo[ib][kb] = row8_16<D>(qt, 16 * ib + l16, 4 * kb + g4);
-                oo[ib][kb] = row8_16<D>(ot, 16 * ib + l16, 4 * kb + g4);
-            }
-        __builtin_amdgcn_sched_barrier(0);
         // S and dP: element v of block ib holds q row i0 + 16 ib + 4 (l / 16) + v, kv row j0 + l % 16
         f32x4 sc[2], dp[2];
+        if constexpr (F8) {   // S on the fp8 MFMA; dP from dO's rows widened
+            long qo[2][NKB], oo[2][NKB];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-            sc[ib] = dp[ib] = f32x4{};
+            for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                sc[ib] = mfma16(qo[ib][kb], kf[kb], sc[ib]);
-                dp[ib] = mfma16(oo[ib][kb], vf[kb], dp[ib]);
+                for (int kb = 0; kb < NKB; ++kb) {
+                    qo[ib][kb] = row8_16_f8<D>(qt, 16 * ib + l16, 4 * kb + g4);
+                    oo[ib][kb] = row8_16_f8<D>(ot, 16 * ib + l16, 4 * kb + g4);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                sc[ib] = dp[ib] = f32x4{};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    sc[ib] = mfma16_f8(qo[ib][kb], kf8[kb], sc[ib]);
+                    dp[ib] = mfma16(widen_e4m3((int)oo[ib][kb], (int)(oo[ib][kb] >> 32)), vf[kb], dp[ib]);
+                }
             }
+        } else {
+            bf16x8 qo[2][NKB], oo[2][NKB];
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    qo[ib][kb] = row8_16<D>(qt, 16 * ib + l16, 4 * kb + g4);
+                    oo[ib][kb] = row8_16<D>(ot, 16 * ib + l16, 4 * kb + g4);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+                sc[ib] = dp[ib] = f32x4{};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    sc[ib] = mfma16(qo[ib][kb], kf[kb], sc[ib]);
+                    dp[ib] = mfma16(oo[ib][kb], vf[kb], dp[ib]);
+                }
+            }
+        }
+        if constexpr (F8) {   // dP's factor s_do
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) dp[ib][v] *= a.f8_dp;
         }
         constexpr int HC = NCB / 2;
         bf16x8 tv[HC], tk[HC];
 #pragma unroll
         for (int cb = 0; cb < HC; ++cb) {
-            tv[cb] = lds_col8_16<D>(ot, 0, 16 * cb, lane);
-            tk[cb] = lds_col8_16<D>(qt, 0, 16 * cb, lane);
+            tv[cb] = col8(ot, 16 * cb);
+            tk[cb] = col8(qt, 16 * cb);
         }
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 pm, dm;
@@ -219,8 +303,8 @@ struct Dkdv16Pol : Common {
         bf16x8 tv2[HC], tk2[HC];
 #pragma unroll
         for (int cb = 0; cb < HC; ++cb) {
-            tv2[cb] = lds_col8_16<D>(ot, 0, 16 * (cb + HC), lane);
-            tk2[cb] = lds_col8_16<D>(qt, 0, 16 * (cb + HC), lane);
+            tv2[cb] = col8(ot, 16 * (cb + HC));
+            tk2[cb] = col8(qt, 16 * (cb + HC));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -233,6 +317,14 @@ struct Dkdv16Pol : Common {
             accV[cb + HC] = mfma16(tv2[cb], pm, accV[cb + HC]);
             accK[cb + HC] = mfma16(tk2[cb], dm, accK[cb + HC]);
         }
+    }
+
+    // the transposed operand of dV^T += dO^T P and dK^T += Q^T dS (F8: widened to bf16)
+    __device__ __forceinline__ bf16x8 col8(const char* tile, int col0) const {
+        if constexpr (F8)
+            return lds_col8_16_f8<D>(tile, col0, lane);
+        else
+            return lds_col8_16<D>(tile, 0, col0, lane);
     }
 
     // this wave's 16 rows of one output (acc: kv row l % 16, columns 16 cb + 4 (l / 16) + {0..3})
@@ -294,9 +386,9 @@ struct Dkdv16Pol : Common {
         // team barrier): dK, then dV once this wave has read dK back
         char* stage = g.tile(job - 2 + (wt >> 1)) + (wt & 1) * (16 * D * 2);
         const size_t ob = ((size_t)c.ks * H + c.h) * D;
-        store16(accK, scale, a.dk, ob, c.lk, krow(c), stage);
+        store16(accK, F8 ? a.f8_dk : scale, a.dk, ob, c.lk, krow(c), stage);
         wait_lds();
-        store16(accV, 1.0f, a.dv, ob, c.lk, krow(c), stage);
+        store16(accV, F8 ? a.f8_dv : 1.0f, a.dv, ob, c.lk, krow(c), stage);
     }
 
     __device__ __forceinline__ void item_zero(const Rec& c) {
@@ -307,15 +399,15 @@ struct Dkdv16Pol : Common {
     }
 };
 
-template <int ACT, int T>
+template <int ACT, int T, bool F8>
 __global__ __launch_bounds__(64 * T, 2) void dkdv16_kernel(const KernelArgs a, const Rec* __restrict__ recs,
                                                           const int32_t* __restrict__ bin_ptr) {
     using RingT = Ring<128, T, 40 * 512 * T, 0, SW16>;   // 40 KiB per team of two waves
     __shared__ __attribute__((aligned(1024))) char smem[RingT::BYTES];
     const int wt = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    Dkdv16Pol<ACT, T> pol(a, lane, wt);
-    run_team<Dkdv16Pol<ACT, T>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * 128 * 2, wt, lane);
+    Dkdv16Pol<ACT, T, F8> pol(a, lane, wt);
+    run_team<Dkdv16Pol<ACT, T, F8>, RingT, T>(pol, a.P, recs, bin_ptr, smem, (uint32_t)a.H * 128 * 2, wt, lane);
 }
 
 // =========================================================================
@@ -328,25 +420,36 @@ __global__ __launch_bounds__(64 * T, 2) void dkdv16_kernel(const KernelArgs a, c
 // dQ^T += K^T dS^T with both operands read from LDS by transposing loads.  No
 // scores, activations or dO are touched: what the dK/dV kernel already computed
 // is reused, so this kernel moves dS and K and does a quarter of the products.
+// With fp8 K (F8) its tile is one byte per element in the first half of the K part
+// of a slot (which keeps its bf16 size: dQ is staged there), and the K^T operand
+// comes from 8-bit transposing reads widened exactly to bf16.
+template <bool F8>
 struct DsRing {
     static constexpr int D = 128;
     static constexpr int KT = 32 * D * 2, DT = 32 * 32 * 2, SLOT = KT + DT;
-    static constexpr int JX = (KT + DT) / 1024;   // load instructions per job
+    static constexpr int KL = F8 ? KT / 2 : KT;   // bytes of K loaded per job
+    static constexpr int JX = (KL + DT) / 1024;   // load instructions per job
     static constexpr int R = 4;
     static constexpr int BYTES = R * SLOT;
-    uint32_t offk[KT / 1024], offd[DT / 1024];
+    uint32_t offk[KL / 1024], offd[DT / 1024];
     uint32_t base;
     char* gbase;
     int issued;
 
+    // row_stride: bytes between K rows in memory
     __device__ __forceinline__ void init(char* slice, uint32_t row_stride, int lane) {
         gbase = slice;
         base = lds_addr(slice);
         issued = 0;
 #pragma unroll
-        for (int jj = 0; jj < KT / 1024; ++jj) {   // K: rows of 16 chunks, swz<128>
-            const int slot = jj * 64 + lane, row = slot / 16, pos = slot % 16;
-            offk[jj] = (uint32_t)row * row_stride + (uint32_t)((pos ^ swz<D>(row)) << 4);
+        for (int jj = 0; jj < KL / 1024; ++jj) {
+            if constexpr (F8) {   // fp8 K: rows of 8 chunks, swz8<128> (ring.hpp's fp8 tiles)
+                const int slot = jj * 64 + lane, row = slot / 8, pos = slot % 8;
+                offk[jj] = (uint32_t)row * row_stride + (uint32_t)((pos ^ swz8<D>(row)) << 4);
+            } else {   // K: rows of 16 chunks, swz<128>
+                const int slot = jj * 64 + lane, row = slot / 16, pos = slot % 16;
+                offk[jj] = (uint32_t)row * row_stride + (uint32_t)((pos ^ swz<D>(row)) << 4);
+            }
         }
 #pragma unroll
         for (int jj = 0; jj < DT / 1024; ++jj) {   // dS block: 64-byte rows of 4 chunks, swz<32>
@@ -362,7 +465,7 @@ struct DsRing {
         const uint32_t lds = base + (uint32_t)((issued % R) * SLOT);
         const rsrc_t rk = slice_at(k, k_off);
 #pragma unroll
-        for (int jj = 0; jj < KT / 1024; ++jj) dma16(rk, offk[jj], lds + (uint32_t)jj * 1024u);
+        for (int jj = 0; jj < KL / 1024; ++jj) dma16(rk, offk[jj], lds + (uint32_t)jj * 1024u);
 #pragma unroll
         for (int jj = 0; jj < DT / 1024; ++jj) dma16(blk, offd[jj], lds + (uint32_t)(KT + jj * 1024));
         ++issued;
@@ -370,6 +473,7 @@ struct DsRing {
     __device__ __forceinline__ void wait(int k) const { wait_jobs<JX>(issued - 1 - k); }
 };
 
+template <bool F8>
 struct DqDsPol : Common {
     static constexpr int D = 128, NDB = D / 32;
     f32x16 acc[NDB];
@@ -377,13 +481,17 @@ struct DqDsPol : Common {
     __device__ DqDsPol(const KernelArgs& args, int lane_) : Common(args, lane_, 0, D) {}
 
     // the job of step s of item w: K tile s and dS block w.pad0 + (s - w.s0)
-    __device__ __forceinline__ void issue(DsRing& g, const Rec& w, int s) const {
-        const Slice k = slice_of((const __bf16*)a.k + ((size_t)w.ks * H + w.h) * D, w.lk, rs, D * 2);
+    __device__ __forceinline__ void issue(DsRing<F8>& g, const Rec& w, int s) const {
         const size_t blk = (size_t)w.pad0 + (size_t)(s - w.s0);
-        g.issue(k, (uint32_t)(s * 32) * rs, slice_rsrc(a.ds + blk * 1024, 1, 2048u, 2048u));
+        const rsrc_t ds = slice_rsrc(a.ds + blk * 1024, 1, 2048u, 2048u);
+        const size_t kb = ((size_t)w.ks * H + w.h) * D;
+        if constexpr (F8)
+            g.issue(slice_of((const uint8_t*)a.k + kb, w.lk, rs / 2, D), (uint32_t)(s * 32) * (rs / 2), ds);
+        else
+            g.issue(slice_of((const __bf16*)a.k + kb, w.lk, rs, D * 2), (uint32_t)(s * 32) * rs, ds);
     }
 
-    __device__ __forceinline__ void step(const DsRing& g, int job) {
+    __device__ __forceinline__ void step(const DsRing<F8>& g, int job) {
         const char* kt = g.ktile(job);
         const char* dt = g.dtile(job);
 #pragma unroll
@@ -392,16 +500,18 @@ struct DqDsPol : Common {
             const bf16x8 b = lds_col8<32>(dt, 16 * m, 0, lane);
             bf16x8 kop[NDB];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) kop[db] = lds_col8<D>(kt, 16 * m, db * 32, lane);
+            for (int db = 0; db < NDB; ++db)
+                kop[db] = F8 ? lds_col8_f8<D>(kt, 16 * m, db * 32, lane) : lds_col8<D>(kt, 16 * m, db * 32, lane);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) acc[db] = mfma32(kop[db], b, acc[db]);
         }
     }
 };
 
+template <bool F8>
 __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, const Rec* __restrict__ recs,
                                                           const int32_t* __restrict__ bin_ptr) {
-    __shared__ __attribute__((aligned(1024))) char smem[DsRing::BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[DsRing<F8>::BYTES];
     const int lane = threadIdx.x;
     const int bin = team_bin();
     if (bin >= a.P) return;
@@ -410,9 +520,9 @@ __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, c
 #ifdef GDPA_BIN_CLOCK
     const unsigned long long clock0 = __builtin_amdgcn_s_memrealtime();
 #endif
-    DqDsPol pol(a, lane);
-    DsRing ring;
-    ring.init(smem, (uint32_t)a.H * 128 * 2, lane);
+    DqDsPol<F8> pol(a, lane);
+    DsRing<F8> ring;
+    ring.init(smem, (uint32_t)a.H * 128 * (F8 ? 1 : 2), lane);
     // issuing side: the item and step of the next job (items without steps have none)
     int wi = beg, ws = 0;
     Rec wr = recs[beg];
@@ -421,7 +531,7 @@ __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, c
     ws = wr.s0;
     int job = 0;
     auto pump = [&](int consumed) {
-        while (wi < end && ring.issued < consumed + DsRing::R) {
+        while (wi < end && ring.issued < consumed + DsRing<F8>::R) {
             pol.issue(ring, wr, ws);
             if (++ws > wr.s1) {
                 do {
@@ -436,11 +546,11 @@ __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, c
         const Rec c = recs[ci];
         const size_t ob = ((size_t)c.qs * pol.H + c.h) * 128;
         if (c.s1 < c.s0) {
-            pol.zero<128>(a.dq, ob, c.lq, c.t * 32);
+            pol.template zero<128>(a.dq, ob, c.lq, c.t * 32);
             continue;
         }
 #pragma unroll
-        for (int db = 0; db < DqDsPol::NDB; ++db) pol.acc[db] = f32x16{};
+        for (int db = 0; db < DqDsPol<F8>::NDB; ++db) pol.acc[db] = f32x16{};
         for (int s = c.s0; s <= c.s1; ++s) {
             ring.wait(job);
             wait_lds();   // this wave is done reading the slot the pump re-fills next
@@ -450,12 +560,12 @@ __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, c
         }
         wait_lds();
         if (c.part >= 0) {
-            store_partial<DqDsPol::NDB>(pol.acc, a.part, c.part, 32, 0, pol.r, pol.hh);
+            store_partial<DqDsPol<F8>::NDB>(pol.acc, a.part, c.part, 32, 0, pol.r, pol.hh);
             continue;
         }
         // staged through the K tile of the item's last step: the pump re-fills a
         // slot only at the next consume point, after that step's reads
-        pol.store<128>(pol.acc, pol.scale, a.dq, ob, c.lq, c.t * 32, ring.ktile(job - 1));
+        pol.template store<128>(pol.acc, F8 ? a.f8_dq : pol.scale, a.dq, ob, c.lq, c.t * 32, ring.ktile(job - 1));
     }
 #ifdef GDPA_BIN_CLOCK
     if (a.bin_clock && lane == 0) {
@@ -467,33 +577,37 @@ __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, c
 
 }  // namespace
 
-hipError_t launch_dq_from_ds(const KernelArgs& a, hipStream_t s) {
+hipError_t launch_dq_from_ds(const KernelArgs& a, int f8, hipStream_t s) {
     if (a.P <= 0) return hipSuccess;
     if (!a.ds) return hipErrorInvalidValue;
     KernelArgs args = a;
     const void* recs = a.items;
     const int32_t* bin_ptr = a.bin_ptr;
     void* params[] = {&args, &recs, &bin_ptr};
-    return hipLaunchKernel((const void*)&dq_from_ds_kernel, dim3(a.P), dim3(64), params, 0, s);
+    return hipLaunchKernel(dq_from_ds_kernel_ptr(f8), dim3(a.P), dim3(64), params, 0, s);
 }
 
-const void* dq_from_ds_kernel_ptr() { return (const void*)&dq_from_ds_kernel; }
+const void* dq_from_ds_kernel_ptr(int f8) {
+    return f8 ? (const void*)&dq_from_ds_kernel<true> : (const void*)&dq_from_ds_kernel<false>;
+}
 
-template <int T>
+template <int T, bool F8>
 const void* dkdv16_ptr(int act) {
     switch (act) {
-        case ACT_GELU: return (const void*)&dkdv16_kernel<ACT_GELU, T>;
-        case ACT_SILU: return (const void*)&dkdv16_kernel<ACT_SILU, T>;
-        case ACT_GELU_POLY: return (const void*)&dkdv16_kernel<ACT_GELU_POLY, T>;
-        case ACT_GELU_TAYLOR6: return (const void*)&dkdv16_kernel<ACT_GELU_TAYLOR6, T>;
-        case ACT_IDENTITY: return (const void*)&dkdv16_kernel<ACT_IDENTITY, T>;
+        case ACT_GELU: return (const void*)&dkdv16_kernel<ACT_GELU, T, F8>;
+        case ACT_SILU: return (const void*)&dkdv16_kernel<ACT_SILU, T, F8>;
+        case ACT_GELU_POLY: return (const void*)&dkdv16_kernel<ACT_GELU_POLY, T, F8>;
+        case ACT_GELU_TAYLOR6: return (const void*)&dkdv16_kernel<ACT_GELU_TAYLOR6, T, F8>;
+        case ACT_IDENTITY: return (const void*)&dkdv16_kernel<ACT_IDENTITY, T, F8>;
     }
     return nullptr;
 }
 
 const void* dkdv16_kernel_ptr(int rows, int act) {
-    if (rows == 32) return dkdv16_ptr<2>(act);
-    if (rows == 64) return dkdv16_ptr<4>(act);
+    const bool f8 = act & kActF8Bwd;
+    act &= ~kActF8Bwd;
+    if (rows == 32) return f8 ? dkdv16_ptr<2, true>(act) : dkdv16_ptr<2, false>(act);
+    if (rows == 64) return f8 ? dkdv16_ptr<4, true>(act) : dkdv16_ptr<4, false>(act);
     return nullptr;
 }
 

@@ -669,8 +669,10 @@ const void* GDPA_CAT(dkdv_bf16_kernel_ptr_d, GDPA_D)(int team, int nb, int act) 
     if (nb != 1) return nullptr;
 #if GDPA_D == 128
     // plain activations run on the 16-row kernel (32 team rows per item: two waves
-    // for a one-wave layout, four for a two-wave layout)
-    if (act >= ACT_GELU && act <= ACT_IDENTITY) return dkdv16_kernel_ptr(32 * team, act);
+    // for a one-wave layout, four for a two-wave layout), fp8 inputs too
+    const int plain = act & ~kActF8Bwd;
+    if (plain >= ACT_GELU && plain <= ACT_IDENTITY) return dkdv16_kernel_ptr(32 * team, act);
+    if (act & kActF8Bwd) return nullptr;
 #endif
     if (act == ACT_SOFTMAX) return team == 1 ? dkdv_ptr<1, 1, ACT_SOFTMAX>() : nullptr;
     if (team == 1) return dkdv_act<1>(act);

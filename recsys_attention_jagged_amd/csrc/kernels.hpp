@@ -100,13 +100,14 @@ GDPA_DECLARE_LAUNCHERS(128)
 // d = 128 dK/dV kernel on the 16 x 16 x 32 MFMA for kv items of `rows` = 32 or 64
 // rows (the dK/dV list's layouts team 1 and team 2, one block): a workgroup of
 // rows / 16 waves, 16 kv rows per wave, two waves per SIMD.  Plain GDPA
-// activations only (nullptr otherwise).
+// activations only, with kActF8Bwd for fp8 Q, K, dO (nullptr otherwise).
 const void* dkdv16_kernel_ptr(int rows, int act);
 
 // d = 128 dQ from the stored dS blocks: dQ = dS K / sqrt(d) over the dQ list of
-// 32-row q items (one wave per workgroup); a.ds, a.items: that list, a.part its slots
-hipError_t launch_dq_from_ds(const KernelArgs& a, hipStream_t s);
-const void* dq_from_ds_kernel_ptr();
+// 32-row q items (one wave per workgroup); a.ds, a.items: that list, a.part its
+// slots; f8: K as fp8 (e4m3)
+hipError_t launch_dq_from_ds(const KernelArgs& a, int f8, hipStream_t s);
+const void* dq_from_ds_kernel_ptr(int f8 = 0);
 
 // One-pass backward (one-wave teams, one block per wave): kv_stationary = 1 runs
 // over the dK/dV list when every Lk <= 32 (dQ stored per step), 0 over the dQ

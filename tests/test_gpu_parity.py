@@ -500,6 +500,25 @@ def test_fp8_backward_one_pass(d, case):
             check_close(a, b, f"fp8 {name} d={d} case={case} {dtype}")
 
 
+@pytest.mark.parametrize("window", [0, 17])
+@pytest.mark.parametrize("bins", [(0, 0, 0), (64, 64, 64)])   # 64: the 700-row sample's items are cut
+@pytest.mark.parametrize("dtype", ["bf16", "bf16_f32out"])
+@pytest.mark.parametrize("team", [1, 2])
+def test_fp8_backward_stored_ds(window, bins, dtype, team):
+    """d = 128 plans whose backward is the 16-row dK/dV kernel storing dS and dQ from
+    the stored blocks: ragged lengths across tile edges, windows, cut items (few
+    bins), fp32 outputs, 32- and 64-row dK/dV items."""
+    say(f"fp8 backward stored dS window={window} bins={bins} {dtype} team={team}")
+    L = [1, 15, 16, 17, 33, 47, 64, 65, 0, 300, 129, 700]
+    inp = make_from_lengths(L, L, 2, 128, act="gelu", window=window, seed=93 + window, device=DEV)
+    got, ref, st = run_fp8_bwd(inp, dtype=dtype, bins=bins, team=(0, team, 0))
+    assert st["bwd_fused"] == 0 and st["ds_bytes"] > 0
+    if bins[0]:
+        assert sum(st["n_parts"]) > 0
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        check_close(a, b, f"fp8 {name} stored dS window={window} bins={bins} {dtype} team={team}")
+
+
 @pytest.mark.parametrize("act", ["silu", "identity", "gelu_taylor6"])
 def test_fp8_backward_acts(act):
     say(f"fp8 backward act={act}")
@@ -524,15 +543,15 @@ def test_fp8_backward_cut_items(case):
         check_close(a, b, f"fp8 {name} cut case={case}")
 
 
-@pytest.mark.parametrize("cfg", [3, 4])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_fp8_backward_against_bf16_inputs(cfg):
     """The fp8 backward against the oracle on the quantised values (the kernels'
-    arithmetic) and on the bf16 inputs (within the stated fp8 bounds), on the two
-    workloads whose backward is one pass."""
+    arithmetic) and on the bf16 inputs (within the stated fp8 bounds), on the four
+    bf16 workloads (one-pass or stored-dS backward)."""
     say(f"cfg{cfg} fp8 backward, B={SMALL_B[cfg]}")
     inp = make_workload(cfg, device=DEV, B=SMALL_B[cfg])
     got, ref_q, st = run_fp8_bwd(inp)
-    assert st["bwd_fused"] in (1, 2)
+    assert st["bwd_fused"] in (1, 2) or st["ds_bytes"] > 0
     for name, a, b, c in zip(("dQ", "dK", "dV"), got, ref_q, oracle_bwd(inp)):
         check_close(a, b, f"cfg{cfg} fp8 {name} vs the quantised values")
         check_fp8(a, c, f"cfg{cfg} fp8 {name} vs the bf16 inputs")
