@@ -269,6 +269,9 @@ def main(argv=None):
                     help="forward with fp8 (e4m3) Q and K, backward in bf16, on the same batch")
     ap.add_argument("--mx", action="store_true",
                     help="forward with block-scaled fp8 (MXFP8) Q and K, backward in bf16, on the same batch")
+    ap.add_argument("--claim", default="auto", choices=["auto", "bins", "always"],
+                    help="how workgroups get items: claimed at run time where the plan decides (auto), "
+                         "the planner's bins only, or claimed wherever the kernel runs one-wave teams")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -326,7 +329,7 @@ def main(argv=None):
         return 2
     norm = w["rms"] if args.norm else ""
     t0 = time.perf_counter()
-    plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16")
+    plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", claim=args.claim)
     plan_ms = (time.perf_counter() - t0) * 1e3
     st = plan.stats()
     Tq, Tk, pairs = st["Tq"], st["Tk"], st["valid_pairs"]
@@ -505,6 +508,7 @@ def main(argv=None):
         "config": {"workload": w["name"], "B": B, "H": H, "d": d,
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs, "ds_bytes": ds_bytes,
                    "bwd_inputs": "fp8 Q, K, dO" if fp8_bwd else "bf16",
+                   "claimed_lists": st["claimed"],
                    "backward": ("one KV-stationary pass (D formed from P and dP)" if sm and fused else
                                 "dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
                                 "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else

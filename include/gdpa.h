@@ -104,6 +104,12 @@ typedef struct {
     int unfused;     /* 1: gdpa_bwd always runs the two backward kernels (see gdpa_bwd) */
     int no_ds;       /* 1: gdpa_bwd recomputes dS in its dQ kernel instead of storing it
                         (no dS buffer; see gdpa_plan_create) */
+    int claim;       /* how workgroups get items: 0 automatic (claimed at run time, in the
+                        planner's order, where the list's kernel runs one-wave teams and its
+                        items average 64 steps or more; else the planner's bins), 1 the
+                        planner's bins only, 2 claimed wherever the kernel runs one-wave
+                        teams.  A claim waits for the loads in flight (about one memory
+                        latency).  Results do not depend on it (bit for bit) */
 } gdpa_plan_opts;
 
 /* Summary numbers of a plan. */
@@ -122,6 +128,7 @@ typedef struct {
     int32_t n_parts[3];      /* partial-output slots per list (chunks of cut items; 0 for
                                 the dK/dV list) */
     int64_t ds_bytes;        /* bytes of the plan's dS buffer (0: gdpa_bwd does not store dS) */
+    int32_t claimed[3];      /* 1: the list's items are claimed at run time (see claim) */
 } gdpa_plan_stats_t;
 
 typedef struct gdpa_plan_s* gdpa_plan;

@@ -27,6 +27,8 @@ def main(argv=None):
     ap.add_argument("--config", default="2", choices=["2", "3", "4", "5"])
     ap.add_argument("--deals", nargs="+", default=["greedy", "zigzag", "round_robin"])
     ap.add_argument("--reps", type=int, default=3, help="launches per kernel; the median one is reported")
+    ap.add_argument("--claim", default="bins", choices=["bins", "auto", "always"],
+                    help="how workgroups get items (the plan option): with claims, a 'bin' is one workgroup")
     ap.add_argument("--dump", default=None, metavar="FILE.npz",
                     help="also save every bin's stamps with its list's exported items")
     args = ap.parse_args(argv)
@@ -65,7 +67,7 @@ def main(argv=None):
 
     dump = {}
     for deal in args.deals:
-        plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", deal=deal)
+        plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", deal=deal, claim=args.claim)
         st = plan.stats()
         h = plan.handle
         kernels = [("fwd", 0, lambda: G.gdpa_fwd(h, inp.q, inp.k, inp.v, qo, ko, B, H, d, act, win, o))]
@@ -96,7 +98,8 @@ def main(argv=None):
                 dump[f"{deal}_{name}_stamps"] = stamps_last
                 dump[f"{deal}_{name}_export"] = np.asarray(G.gdpa_plan_export(h, lst))
             print(json.dumps({
-                "workload": WORKLOADS[cfg]["name"], "deal": deal, "kernel": name, "bins": int(busy.size),
+                "workload": WORKLOADS[cfg]["name"], "deal": deal, "claimed": st["claimed"][lst], "kernel": name,
+                "bins": int(busy.size),
                 "busy_us": {"max": round(float(busy.max()), 1), "mean": round(float(busy.mean()), 1),
                             "min": round(float(busy.min()), 1)},
                 "max_over_min": round(float(busy.max() / busy.min()), 3),

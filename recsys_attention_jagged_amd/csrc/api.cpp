@@ -88,6 +88,11 @@ struct gdpa_plan_s {
     WorkList lists[3];
     DevRec* d_items[3] = {nullptr, nullptr, nullptr};
     int32_t* d_bin_ptr[3] = {nullptr, nullptr, nullptr};
+    // lists whose items the workgroups claim at run time: the claim order and the
+    // (claims, finished workgroups) counters
+    bool claimed[3] = {false, false, false};
+    int32_t* d_order[3] = {nullptr, nullptr, nullptr};
+    int* d_claim[3] = {nullptr, nullptr, nullptr};
     // cut items of the Q-stationary lists: groups for the reduction, fp32 slots
     int n_groups[3] = {0, 0, 0};
     DevGroup* d_groups[3] = {nullptr, nullptr, nullptr};
@@ -116,6 +121,8 @@ struct gdpa_plan_s {
         for (int l = 0; l < 3; ++l) {
             if (d_items[l]) (void)hipFree(d_items[l]);
             if (d_bin_ptr[l]) (void)hipFree(d_bin_ptr[l]);
+            if (d_order[l]) (void)hipFree(d_order[l]);
+            if (d_claim[l]) (void)hipFree(d_claim[l]);
             if (d_groups[l]) (void)hipFree(d_groups[l]);
             if (d_part[l]) (void)hipFree(d_part[l]);
         }
@@ -139,6 +146,7 @@ static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
     for (int l = 0; l < 3; ++l) {
         bytes += align(recs[l].size() * sizeof(DevRec)) + align(p->lists[l].bin_ptr.size() * sizeof(int32_t)) +
                  align(groups[l].size() * sizeof(DevGroup));
+        if (p->claimed[l]) bytes += align(p->lists[l].order.size() * sizeof(int32_t)) + align(2 * sizeof(int));
     }
     const int32_t off[4] = {0, (int32_t)p->Tq, 0, (int32_t)p->Tk};
     if (p->pffn) bytes += align(sizeof(off));
@@ -162,6 +170,11 @@ static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
         const WorkList& wl = p->lists[l];
         e = put((void**)&p->d_items[l], recs[l].data(), recs[l].size() * sizeof(DevRec));
         if (e == hipSuccess) e = put((void**)&p->d_bin_ptr[l], wl.bin_ptr.data(), wl.bin_ptr.size() * sizeof(int32_t));
+        if (e == hipSuccess && p->claimed[l]) {   // the claim order, and the counters at zero
+            const int zero[2] = {0, 0};
+            e = put((void**)&p->d_order[l], wl.order.data(), wl.order.size() * sizeof(int32_t));
+            if (e == hipSuccess) e = put((void**)&p->d_claim[l], zero, sizeof(zero));
+        }
         if (e == hipSuccess && wl.n_parts > 0) {
             p->n_groups[l] = (int)groups[l].size();
             e = put((void**)&p->d_groups[l], groups[l].data(), groups[l].size() * sizeof(DevGroup));
@@ -230,6 +243,7 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         if (o.team[l] < 0 || o.team[l] > 2) return fail(GDPA_ERR_INVALID_ARG, "team must be 0, 1 or 2");
     }
     if (o.deal < 0 || o.deal > 2) return fail(GDPA_ERR_INVALID_ARG, "deal must be 0, 1 or 2");
+    if (o.claim < 0 || o.claim > 2) return fail(GDPA_ERR_INVALID_ARG, "claim must be 0, 1 or 2");
 
     if (q_off_host[0] != 0 || kv_off_host[0] != 0)
         return fail(GDPA_ERR_BAD_OFFSETS, "offsets must start at 0");
@@ -333,6 +347,22 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split);
     }
 
+    // lists whose items are claimed at run time: those whose kernel walks them in one-wave
+    // teams (not the d = 128 16-row dK/dV kernel, nor dQ from stored dS) and, by default,
+    // whose items average 64 steps or more: a claim waits for every tile in flight, about
+    // one memory latency at full load (several microseconds), which measured more than
+    // the balance it buys on items of 10 to 30 steps
+    for (int l = 0; l < 3 && dtype != GDPA_F32; ++l) {
+        const WorkList& wl = p->lists[l];
+        bool one_wave = L.team[l] == 1;
+        if (l == LIST_DKDV && p->fused != 1 && d == 128) one_wave = false;
+        if (l == LIST_DQ && p->fused != 2 && p->use_ds) one_wave = false;
+        int64_t with_steps = 0;
+        for (const Item& it : wl.items) with_steps += it.s1 >= it.s0;
+        const bool long_items = with_steps > 0 && wl.n_steps >= 64 * with_steps;
+        p->claimed[l] = o.claim != 1 && one_wave && !wl.items.empty() && (o.claim == 2 || long_items);
+    }
+
     if (dtype != GDPA_F32) {
         for (int l = 0; l < 3; ++l) {
             p->h_recs[l] = p->use_ds ? device_records(p->lists[l], p->q_off, p->kv_off, p->ds, window)
@@ -421,7 +451,10 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
     }
     out->bwd_fused = plan->fused;
     out->ds_bytes = plan->use_ds ? plan->ds.nb_total * plan->H * 2048 : 0;
-    for (int l = 0; l < 3; ++l) out->n_parts[l] = plan->lists[l].n_parts;
+    for (int l = 0; l < 3; ++l) {
+        out->n_parts[l] = plan->lists[l].n_parts;
+        out->claimed[l] = plan->claimed[l] ? 1 : 0;
+    }
     return GDPA_OK;
 }
 
@@ -467,6 +500,15 @@ static KernelArgs base_args(gdpa_plan plan, const int32_t* q_off_dev, const int3
     return a;
 }
 
+// claims of list l for a kernel launched over it (none where the plan does not claim
+// that list's items)
+static void set_claims(KernelArgs& b, gdpa_plan plan, int l) {
+    const bool c = plan->claimed[l];
+    b.order = c ? plan->d_order[l] : nullptr;
+    b.claim = c ? plan->d_claim[l] : nullptr;
+    b.n_items = c ? (int)plan->lists[l].items.size() : 0;
+}
+
 // outputs of the cut items of list l: the sum of their chunks' slots, times mul
 // (the dK/dV list keeps two blocks per slot: block 0 dK, block 1 dV)
 static hipError_t reduce_parts(gdpa_plan plan, int l, float mul, void* out, hipStream_t s, int block = 0) {
@@ -498,6 +540,7 @@ gdpa_status gdpa_fwd(gdpa_plan plan, const void* q, const void* k, const void* v
         const WorkList& wl = plan->lists[LIST_FWD];
         a.items = plan->d_items[LIST_FWD];
         a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+        set_claims(a, plan, LIST_FWD);
         a.P = wl.P;
         a.part = plan->d_part[LIST_FWD];
         switch (d) {
@@ -635,6 +678,7 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
         KernelArgs b = a;
         b.items = plan->d_items[l];
         b.bin_ptr = plan->d_bin_ptr[l];
+        set_claims(b, plan, l);
         b.P = plan->lists[l].P;
         const int kv = plan->fused == 1;
         b.part = plan->d_part[l];
@@ -654,6 +698,7 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             KernelArgs b = a;
             b.items = plan->d_items[LIST_DKDV];
             b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+            set_claims(b, plan, LIST_DKDV);
             b.P = wl.P;
             b.part = plan->d_part[LIST_DKDV];
             b.ds = plan->d_ds;
@@ -666,6 +711,7 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             KernelArgs b = a;
             b.items = plan->d_items[LIST_DQ];
             b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+            set_claims(b, plan, LIST_DQ);
             b.P = wl.P;
             b.part = plan->d_part[LIST_DQ];
             b.ds = plan->d_ds;
@@ -678,6 +724,7 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             KernelArgs b = a;
             b.items = plan->d_items[LIST_DKDV];
             b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+            set_claims(b, plan, LIST_DKDV);
             b.P = wl.P;
             b.part = plan->d_part[LIST_DKDV];
             switch (d) {
@@ -693,6 +740,7 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             KernelArgs b = a;
             b.items = plan->d_items[LIST_DQ];
             b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+            set_claims(b, plan, LIST_DQ);
             b.P = wl.P;
             b.part = plan->d_part[LIST_DQ];
             switch (d) {
@@ -759,6 +807,7 @@ gdpa_status gdpa_jfa_fwd(gdpa_plan plan, const void* q, const void* k, const voi
     const WorkList& wl = plan->lists[LIST_FWD];
     a.items = plan->d_items[LIST_FWD];
     a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+    set_claims(a, plan, LIST_FWD);
     a.P = wl.P;
     a.part = plan->d_part[LIST_FWD];
     a.part_stat = a.part ? a.part + (size_t)wl.n_parts * wl.t_stat * d : nullptr;
@@ -831,6 +880,7 @@ static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DKDV];
         b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+        set_claims(b, plan, LIST_DKDV);
         b.P = wl.P;
         b.part = plan->d_part[LIST_DKDV];
         switch (d) {
@@ -849,6 +899,7 @@ static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DQ];
         b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+        set_claims(b, plan, LIST_DQ);
         b.P = wl.P;
         b.part = plan->d_part[LIST_DQ];
         switch (d) {
@@ -863,6 +914,7 @@ static gdpa_status jfa_grads(gdpa_plan plan, const void* q, const void* k, const
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DKDV];
         b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+        set_claims(b, plan, LIST_DKDV);
         b.P = wl.P;
         b.part = plan->d_part[LIST_DKDV];
         switch (d) {
@@ -974,6 +1026,7 @@ gdpa_status gdpa_norm_fwd(gdpa_plan plan, const void* q, const void* k, const vo
     const WorkList& wl = plan->lists[LIST_FWD];
     a.items = plan->d_items[LIST_FWD];
     a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+    set_claims(a, plan, LIST_FWD);
     a.P = wl.P;
     a.part = plan->d_part[LIST_FWD];
     const int code = (int)act | kActNorm;
@@ -1019,6 +1072,7 @@ static gdpa_status norm_bwd_parts(gdpa_plan plan, const void* q, const void* k, 
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DKDV];
         b.bin_ptr = plan->d_bin_ptr[LIST_DKDV];
+        set_claims(b, plan, LIST_DKDV);
         b.P = wl.P;
         b.part = plan->d_part[LIST_DKDV];
         switch (d) {
@@ -1034,6 +1088,7 @@ static gdpa_status norm_bwd_parts(gdpa_plan plan, const void* q, const void* k, 
         KernelArgs b = a;
         b.items = plan->d_items[LIST_DQ];
         b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
+        set_claims(b, plan, LIST_DQ);
         b.P = wl.P;
         b.part = plan->d_part[LIST_DQ];
         switch (d) {
@@ -1093,6 +1148,7 @@ gdpa_status gdpa_fp8_fwd(gdpa_plan plan, const void* q8, const void* k8, const v
     const WorkList& wl = plan->lists[LIST_FWD];
     a.items = plan->d_items[LIST_FWD];
     a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+    set_claims(a, plan, LIST_FWD);
     a.P = wl.P;
     a.part = plan->d_part[LIST_FWD];
     const int code = (int)act | kActF8;
@@ -1133,6 +1189,7 @@ gdpa_status gdpa_mx_fwd(gdpa_plan plan, const void* q8, const void* q_scale, con
     const WorkList& wl = plan->lists[LIST_FWD];
     a.items = plan->d_items[LIST_FWD];
     a.bin_ptr = plan->d_bin_ptr[LIST_FWD];
+    set_claims(a, plan, LIST_FWD);
     a.P = wl.P;
     a.part = plan->d_part[LIST_FWD];
     const int code = (int)act | kActMX;

@@ -60,6 +60,13 @@ struct KernelArgs {
     // the stored dQ, dK, dV are their products times f8_dq = s_k / sqrt(d),
     // f8_dk = s_q / sqrt(d), f8_dv = s_do
     float f8_dp, f8_dq, f8_dk, f8_dv;
+    // items claimed at run time (one-wave teams; claim == nullptr: each workgroup walks
+    // its bin): claim k takes item order[k] of `items`, k < n_items; claim[0] counts
+    // the claims of the launch, claim[1] the workgroups that have finished, and the
+    // last to finish sets both back to 0
+    const int32_t* order;
+    int* claim;
+    int n_items;
 #ifdef GDPA_BIN_CLOCK
     // clock-probe builds only: per bin, the real-time stamps (100 MHz) of the start and
     // the end of its walk, [P][2]

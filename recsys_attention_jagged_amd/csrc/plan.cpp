@@ -160,7 +160,9 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
     for (int p = 0; p < P; ++p) wl.bin_ptr[p + 1] = wl.bin_ptr[p] + count[p];
     std::vector<int32_t> fill(wl.bin_ptr.begin(), wl.bin_ptr.end() - 1);
     wl.items.resize(cands.size());
+    wl.order.resize(cands.size());
     for (size_t r = 0; r < cands.size(); ++r) {
+        wl.order[r] = fill[bin_of[r]];
         wl.items[fill[bin_of[r]]++] = cands[r].it;
         const Item& it = cands[r].it;
         if (it.s1 >= it.s0) wl.n_steps += it.s1 - it.s0 + 1;

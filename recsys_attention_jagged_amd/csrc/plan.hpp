@@ -63,6 +63,8 @@ struct WorkList {
     int kind = 0, P = 0, t_stat = 0, t_strm = 0, team = 0, nb = 0;
     std::vector<int32_t> bin_ptr;   // P + 1
     std::vector<Item> items;        // bin-major, deal order inside a bin
+    std::vector<int32_t> order;     // the items in planner order (cost descending, then the
+                                    // tie-break): order[r] = index in `items` of the r-th
     std::vector<int64_t> bin_cost;  // P
     int64_t n_steps = 0;
     int n_parts = 0;                // partial-output slots (chunks of cut items)

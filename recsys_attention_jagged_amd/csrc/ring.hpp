@@ -520,6 +520,141 @@ __device__ __forceinline__ int team_bin() {
     return (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
 }
 
+// Items claimed at run time (one-wave teams, a.claim set).  The workgroups of the
+// launch take items in the planner's order a.order: the first P (one per workgroup,
+// P = the grid) without a claim, item r by the workgroup of logical bin r, where the
+// planner's deal puts its first round (so that neighbouring items share an XCD as
+// they do there); every further item from one counter, P + (the counter's value).
+// A claim is a vector atomic from one lane whose value is used at once, so it waits
+// for the tiles still in flight (the counter orders them): the planner claims only
+// lists whose items are long against that wait.  The walk hands
+// every claimed item to the computing side through a queue held one entry per lane
+// of a register; it claims only while fewer than kClaimQueue items are unfinished
+// (entry k lives in lane k % 64 until the computing side has read it), and the
+// computing side runs the walk again whenever it has emptied the queue.  A workgroup
+// adds itself to a.claim[1] after its last claim, and the last one to do so sets
+// both counters back to 0 for the next launch.
+constexpr int kClaimQueue = 48;
+
+struct ClaimWalk {
+    Rec r;
+    int pos, njobs;   // the walk's item: jobs issued, jobs (pos == njobs: claim the next)
+    bool valid;       // false once a claim has found the list exhausted
+    bool first;       // this workgroup's first item (no claim) is still to be taken
+    int queue;        // lane (k % 64): the k-th claimed item
+    int n;            // items claimed so far (uniform)
+};
+
+template <class Pol>
+__device__ __forceinline__ void claim_one(Pol& pol, ClaimWalk& w, const Rec* __restrict__ recs, int lane) {
+    int k;
+    if (w.first) {
+        k = team_bin();
+        w.first = false;
+    } else {
+        k = 0;
+        if (lane == 0) k = __hip_atomic_fetch_add(pol.a.claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        k = (int)gridDim.x + __builtin_amdgcn_readfirstlane(k);
+    }
+    if (k >= pol.a.n_items) {
+        w.valid = false;
+        return;
+    }
+    const int idx = __builtin_amdgcn_readfirstlane(pol.a.order[k]);
+    w.queue = lane == (w.n & 63) ? idx : w.queue;
+    ++w.n;
+    w.r = recs[idx];
+    w.pos = 0;
+    w.njobs = w.r.s1 >= w.r.s0 ? Pol::NSTAT + Pol::NSTRM * (w.r.s1 - w.r.s0 + 1) : 0;
+    if (w.njobs > 0) pol.walk_item(w.r);
+}
+
+// issue jobs until the ring is full, claiming items as the walk needs them (done:
+// items the computing side has finished)
+template <class Pol, class RingT>
+__device__ __forceinline__ void claim_pump(Pol& pol, ClaimWalk& w, RingT& ring, int consumed, int done,
+                                          const Rec* __restrict__ recs, int lane) {
+    while (w.valid && ring.issued < consumed + RingT::R) {
+        if (w.pos == w.njobs) {
+            if (w.n - done >= kClaimQueue) return;
+            claim_one(pol, w, recs, lane);
+            continue;
+        }
+        pol.issue_job(ring, w.r, w.pos);
+        ++w.pos;
+    }
+}
+
+template <class Pol, class RingT>
+__device__ __forceinline__ void run_claimed(Pol& pol, const Rec* __restrict__ recs, char* slice, uint32_t row_stride,
+                                            int lane) {
+#ifdef GDPA_BIN_CLOCK
+    const unsigned long long clock0 = __builtin_amdgcn_s_memrealtime();
+#endif
+    RingT ring;
+    ring.init(slice, row_stride, 0, lane);
+    ring_ready(pol, ring, lane, 0);
+    ClaimWalk w;
+    w.queue = 0;
+    w.n = 0;
+    w.pos = w.njobs = 0;
+    w.valid = true;
+    w.first = true;
+    int job = 0, ci = 0;
+    claim_pump<Pol, RingT>(pol, w, ring, job, ci, recs, lane);
+    for (;;) {
+        if (ci == w.n) {   // every claimed item is done: claim more, or stop
+            if (!w.valid) break;
+            claim_pump<Pol, RingT>(pol, w, ring, job, ci, recs, lane);
+            continue;
+        }
+        const Rec c = recs[__builtin_amdgcn_readlane(w.queue, ci & 63)];
+        if (c.s1 < c.s0) {
+            pol.item_zero(c);
+            ++ci;
+            continue;
+        }
+        // every job before this item's first is consumed: the walk (on this item or
+        // past it) issues at least the jobs of the item's first consume point
+        claim_pump<Pol, RingT>(pol, w, ring, job, ci, recs, lane);
+        pol.item_begin(c);
+#pragma unroll
+        for (int i = 0; i < Pol::NSTAT; i += 2) {
+            const int n = (Pol::NSTAT - i) < 2 ? 1 : 2;
+            ring.wait(job + n - 1);
+            wait_lds();
+            claim_pump<Pol, RingT>(pol, w, ring, job, ci, recs, lane);
+            pol.load_stat(c, ring, job, i);
+            job += n;
+        }
+        for (int s = c.s0;; ++s) {
+            ring.wait(job + 1);
+            wait_lds();
+            claim_pump<Pol, RingT>(pol, w, ring, job, ci, recs, lane);
+            pol.step(c, s, ring, job);
+            job += 2;
+            if (s == c.s1) break;
+        }
+        wait_lds();
+        pol.item_end(c, ring, job);
+        ++ci;
+    }
+    if (lane == 0) {
+        const int fin = __hip_atomic_fetch_add(pol.a.claim + 1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (fin == (int)gridDim.x - 1) {   // every workgroup has made its last claim
+            __hip_atomic_store(pol.a.claim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pol.a.claim + 1, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+#ifdef GDPA_BIN_CLOCK
+    if (pol.a.bin_clock && lane == 0) {
+        const int bin = team_bin();
+        pol.a.bin_clock[2 * bin] = clock0;
+        pol.a.bin_clock[2 * bin + 1] = __builtin_amdgcn_s_memrealtime();
+    }
+#endif
+}
+
 // The computing side.  Pol also provides:
 //   item_begin(rec)                 zero the accumulators
 //   load_stat(rec, ring, job, i)    stationary tiles i, i + 1 (jobs job, job + 1; only
@@ -536,6 +671,12 @@ __device__ __forceinline__ void run_team(Pol& pol, int P, const Rec* __restrict_
                                          const int32_t* __restrict__ bin_ptr, char* slice, uint32_t row_stride,
                                          int wt, int lane) {
     static_assert(Pol::NSTRM == 2, "a step streams two tiles");
+    if constexpr (T == 1) {
+        if (pol.a.claim) {
+            run_claimed<Pol, RingT>(pol, recs, slice, row_stride, lane);
+            return;
+        }
+    }
     const int bin = team_bin();
     if (bin >= P) return;
     const int beg = bin_ptr[bin], end = bin_ptr[bin + 1];

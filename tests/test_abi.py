@@ -172,6 +172,36 @@ def test_plan_picks_one_pass_backward():
     assert mode(list(lq), list(lk)) == 0
 
 
+def test_plan_claims_long_item_lists():
+    """Items claimed at run time: by default, the lists whose kernel walks them in
+    one-wave teams and whose items average 64 steps or more (none of the four bf16
+    workloads; PMA-like batches of 8192 keys per sample); never the d = 128 16-row
+    dK/dV list or dQ from stored dS; every one-wave list with claim = always; none
+    with claim = bins or on an fp32 plan."""
+    def claimed(lq, lk, d=64, window=0, dtype="bf16", H=2, **kw):
+        p = G.gdpa_plan_create(offsets(lq), offsets(lk), len(lq), H, d, window, dtype, host_only=True, **kw)
+        try:
+            st = G.gdpa_plan_stats(p)
+            return st["claimed"], st["n_items"], st["n_steps"]
+        finally:
+            G.gdpa_plan_destroy(p)
+    want = {2: [0, 0, 0], 3: [0, 0, 0], 4: [0, 0, 0], 5: [0, 0, 0]}
+    for cfg in (2, 3, 4, 5):
+        w = WORKLOADS[cfg]
+        lq, lk = workload_lengths(cfg)
+        c, n_items, n_steps = claimed(list(lq), list(lk), d=w["d"], window=w["window"], H=w["H"])
+        assert c == want[cfg], (cfg, c)
+        for l in range(3):   # the rule: 64 steps or more per item (every item here has steps)
+            assert bool(c[l]) == (n_steps[l] >= 64 * n_items[l]) or (cfg in (2, 5) and l > 0), (cfg, l)
+    c, n_items, n_steps = claimed([32] * 512, [8192] * 512, d=128, H=4)
+    assert c == [1, 0, 1] and n_steps[2] >= 64 * n_items[2], (c, n_items, n_steps)
+    lq, lk = [300, 5, 0, 77], [300, 5, 0, 77]
+    assert claimed(lq, lk, claim="always")[0] == [1, 1, 1]
+    assert claimed(lq, lk, d=128, claim="always")[0][1:] == [0, 0]   # 16-row dK/dV; dQ from stored dS
+    assert claimed(lq, lk, claim="bins")[0] == [0, 0, 0]
+    assert claimed(lq, lk, dtype="f32", claim="always")[0] == [0, 0, 0]
+
+
 # ---------------------------------------------------------------------------
 # error paths (forced from the host)
 # ---------------------------------------------------------------------------
@@ -197,6 +227,8 @@ def test_create_rejects_bad_arguments():
     assert bad(blocks=(0, 0, -1)) == 1
     assert bad(team=(3, 0, 0)) == 1
     assert bad(team=(2, 0, 0)) == 1            # two-wave teams only at d = 128
+    assert bad(claim=3) == 1
+    assert bad(claim=-1) == 1
     assert bad(d=128, team=(0, 0, 2), blocks=(0, 0, 2)) == 1   # two-wave teams: one block per wave
     assert bad(d=128, team=(2, 0, 0), blocks=(2, 0, 0)) == 1
     assert bad(qo=np.array([1, 3, 7], np.int32)) == 2           # BAD_OFFSETS: not starting at 0
