@@ -1511,3 +1511,53 @@ def test_full_size_sampled_fp8(cfg):
                         np.array([0, qe - qs]), np.array([0, ke - ks]), inp.act, inp.window)
         check_close(_f64(o, qs, qe), ro, f"cfg{cfg} fp8 O sample {b}")
     assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled_fp8_backward(cfg):
+    """The fp8 backward at full size in the benchmark's launch configuration (one factor per
+    tensor over the whole batch; one pass or the stored-dS kernels): sampled samples against
+    the oracle on the values the bytes stand for."""
+    say(f"cfg{cfg} full size fp8 backward, sampled samples")
+    inp = make_workload(cfg, device=DEV)
+    qo, ko = dev_offsets(inp)
+    q8, sq = quant_e4m3(inp.q)
+    k8, sk = quant_e4m3(inp.k)
+    o8, so = quant_e4m3(inp.do)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16") as plan:
+        dq, dk, dv = (torch.empty_like(t) for t in (inp.q, inp.k, inp.v))
+        G.gdpa_fp8_bwd(plan.handle, q8.view(torch.uint8).to(DEV), k8.view(torch.uint8).to(DEV), inp.v,
+                       o8.view(torch.uint8).to(DEV), qo, ko, plan.B, inp.H, inp.d, inp.act, inp.window, sq, sk, so,
+                       dq, dk, dv)
+        torch.cuda.synchronize()
+    for b in _picks(inp, cfg):
+        (qs, qe), (ks, ke) = _slices(inp, b)
+        ref = R.gdpa_bwd(q8[qs:qe].double().numpy() * sq, k8[ks:ke].double().numpy() * sk, _f64(inp.v, ks, ke),
+                         o8[qs:qe].double().numpy() * so, np.array([0, qe - qs]), np.array([0, ke - ks]), inp.act,
+                         inp.window)
+        for name, got, r in zip(("dQ", "dK", "dV"), (_f64(dq, qs, qe), _f64(dk, ks, ke), _f64(dv, ks, ke)), ref):
+            check_close(got, r, f"cfg{cfg} fp8 {name} sample {b}")
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled_mx(cfg):
+    """The MXFP8 forward at full size: sampled samples against the oracle on the values the
+    bytes and their block scales stand for."""
+    say(f"cfg{cfg} full size MX forward, sampled samples")
+    inp = make_workload(cfg, device=DEV)
+    qo, ko = dev_offsets(inp)
+    q8, qsc = quant_mx(inp.q)
+    k8, ksc = quant_mx(inp.k)
+    with G.Plan(inp.q_off, inp.kv_off, inp.H, inp.d, inp.window, "bf16") as plan:
+        o = torch.empty_like(inp.q)
+        G.gdpa_mx_fwd(plan.handle, q8.view(torch.uint8).to(DEV), qsc.to(DEV), k8.view(torch.uint8).to(DEV),
+                      ksc.to(DEV), inp.v, qo, ko, plan.B, inp.H, inp.d, inp.act, inp.window, o)
+        torch.cuda.synchronize()
+    for b in _picks(inp, cfg):
+        (qs, qe), (ks, ke) = _slices(inp, b)
+        ro = R.gdpa_fwd(dequant_mx(q8[qs:qe], qsc[:, qs:qe]), dequant_mx(k8[ks:ke], ksc[:, ks:ke]),
+                        _f64(inp.v, ks, ke), np.array([0, qe - qs]), np.array([0, ke - ks]), inp.act, inp.window)
+        check_close(_f64(o, qs, qe), ro, f"cfg{cfg} MX O sample {b}")
+    assert torch.isfinite(o.float()).all()
