@@ -272,6 +272,9 @@ def main(argv=None):
     ap.add_argument("--claim", default="auto", choices=["auto", "bins", "always"],
                     help="how workgroups get items: claimed at run time where the plan decides (auto), "
                          "the planner's bins only, or claimed wherever the kernel runs one-wave teams")
+    ap.add_argument("--slot-time", default="auto", choices=["auto", "off"],
+                    help="deal weighted by each bin's dispatch round on its CU where the plan decides (auto), "
+                         "or every bin dealt by plain cost")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -329,7 +332,7 @@ def main(argv=None):
         return 2
     norm = w["rms"] if args.norm else ""
     t0 = time.perf_counter()
-    plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", claim=args.claim)
+    plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", claim=args.claim, slot_time=args.slot_time)
     plan_ms = (time.perf_counter() - t0) * 1e3
     st = plan.stats()
     Tq, Tk, pairs = st["Tq"], st["Tk"], st["valid_pairs"]
@@ -509,6 +512,7 @@ def main(argv=None):
                    "act": act, "window": win, "Tq": Tq, "Tk": Tk, "valid_pairs": pairs, "ds_bytes": ds_bytes,
                    "bwd_inputs": "fp8 Q, K, dO" if fp8_bwd else "bf16",
                    "claimed_lists": st["claimed"],
+                   "slot_weighted_lists": st["slot_weighted"],
                    "backward": ("one KV-stationary pass (D formed from P and dP)" if sm and fused else
                                 "dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
                                 "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else

@@ -110,6 +110,14 @@ typedef struct {
                         planner's bins only, 2 claimed wherever the kernel runs one-wave
                         teams.  A claim waits for the loads in flight (about one memory
                         latency).  Results do not depend on it (bit for bit) */
+    int slot_time;   /* 0 automatic: where a list has automatic bins and its kernel is one
+                        measured for it (the d = 128 two-wave forward and 16-row dK/dV
+                        kernels at four workgroups per CU, the d = 64 forward at eight), the
+                        greedy deal weighs each bin's cost by a time factor of its dispatch
+                        round on its CU (workgroups placed early on a CU ran up to 12 %
+                        faster than later ones), so earlier-placed bins get more work; 1 every
+                        bin is dealt by plain cost.  Results do not depend on it (bit for
+                        bit) */
 } gdpa_plan_opts;
 
 /* Summary numbers of a plan. */
@@ -129,6 +137,7 @@ typedef struct {
                                 the dK/dV list) */
     int64_t ds_bytes;        /* bytes of the plan's dS buffer (0: gdpa_bwd does not store dS) */
     int32_t claimed[3];      /* 1: the list's items are claimed at run time (see claim) */
+    int32_t slot_weighted[3];/* 1: the list's deal took the dispatch-slot time factors */
 } gdpa_plan_stats_t;
 
 typedef struct gdpa_plan_s* gdpa_plan;

@@ -38,7 +38,8 @@ class GdpaError(RuntimeError):
 class gdpa_plan_opts(ctypes.Structure):
     _fields_ = [("host_only", ctypes.c_int), ("bins", ctypes.c_int * 3), ("team", ctypes.c_int * 3),
                 ("blocks", ctypes.c_int * 3), ("deal", ctypes.c_int), ("no_split", ctypes.c_int),
-                ("unfused", ctypes.c_int), ("no_ds", ctypes.c_int), ("claim", ctypes.c_int)]
+                ("unfused", ctypes.c_int), ("no_ds", ctypes.c_int), ("claim", ctypes.c_int),
+                ("slot_time", ctypes.c_int)]
 
 
 class gdpa_plan_stats_t(ctypes.Structure):
@@ -47,7 +48,8 @@ class gdpa_plan_stats_t(ctypes.Structure):
                 ("bins", ctypes.c_int32 * 3), ("tile_stat", ctypes.c_int32 * 3),
                 ("tile_strm", ctypes.c_int32 * 3), ("bin_cost_max", ctypes.c_int64 * 3),
                 ("bin_cost_min", ctypes.c_int64 * 3), ("bwd_fused", ctypes.c_int32),
-                ("n_parts", ctypes.c_int32 * 3), ("ds_bytes", ctypes.c_int64), ("claimed", ctypes.c_int32 * 3)]
+                ("n_parts", ctypes.c_int32 * 3), ("ds_bytes", ctypes.c_int64), ("claimed", ctypes.c_int32 * 3),
+                ("slot_weighted", ctypes.c_int32 * 3)]
 
 
 _lib = None
@@ -153,7 +155,7 @@ def _enum(v, table):
 def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: int, dtype,
                      host_only: bool = False, bins=(0, 0, 0), team=(0, 0, 0), blocks=(0, 0, 0),
                      deal="greedy", split: bool = True, unfused: bool = False, stream=None,
-                     store_ds: bool = True, claim="auto") -> int:
+                     store_ds: bool = True, claim="auto", slot_time="auto") -> int:
     """Returns an opaque plan handle (int).  Offsets: host int32 [B + 1].  The work
     lists are copied on `stream` (torch's current stream by default; none for a
     host-only plan)."""
@@ -161,7 +163,7 @@ def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: in
     ko = np.ascontiguousarray(kv_off_host, dtype=np.int32)
     if qo.shape != (B + 1,) or ko.shape != (B + 1,):
         raise ValueError("offsets must have B + 1 entries")
-    opts = _opts(host_only, bins, team, blocks, deal, split, unfused, store_ds, claim)
+    opts = _opts(host_only, bins, team, blocks, deal, split, unfused, store_ds, claim, slot_time)
     out = _vp()
     _check(load_library().gdpa_plan_create(qo.ctypes.data, ko.ctypes.data, B, H, d, window,
                                            _enum(dtype, DTYPE), ctypes.byref(opts),
@@ -293,12 +295,13 @@ def gdpa_norm_bwd_dq(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, w
 
 
 CLAIM = {"auto": 0, "bins": 1, "always": 2}
+SLOT_TIME = {"auto": 0, "off": 1}
 
 
-def _opts(host_only, bins, team, blocks, deal, split, unfused, store_ds=True, claim="auto"):
+def _opts(host_only, bins, team, blocks, deal, split, unfused, store_ds=True, claim="auto", slot_time="auto"):
     return gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*team),
                           (ctypes.c_int * 3)(*blocks), _enum(deal, DEAL), int(not split), int(unfused),
-                          int(not store_ds), _enum(claim, CLAIM))
+                          int(not store_ds), _enum(claim, CLAIM), _enum(slot_time, SLOT_TIME))
 
 
 def gdpa_pffn_plan_create(Tq: int, M: int, H: int, d: int, dtype, host_only: bool = False, bins=(0, 0, 0),

@@ -10,8 +10,10 @@ and the end of each bin's walk, so the busy time of every bin is measured direct
     python -m recsys_attention_jagged_amd.bin_balance [--config 2] [--deals greedy zigzag round_robin]
 
 Prints one JSON line per (deal, kernel): busy time per bin with items (max, mean,
-min), max:min and max:mean, the kernel's span (last end - first start), and the
-planner's own max:min bin cost for the list.
+min), max:min and max:mean, the kernel's span (last end - first start), the mean
+busy time of the bins in each dispatch round on their CU (a launch of k workgroups
+per CU places them in k rounds of one per CU), and the planner's own max:min bin
+cost for the list.
 """
 from __future__ import annotations
 
@@ -29,6 +31,8 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=3, help="launches per kernel; the median one is reported")
     ap.add_argument("--claim", default="bins", choices=["bins", "auto", "always"],
                     help="how workgroups get items (the plan option): with claims, a 'bin' is one workgroup")
+    ap.add_argument("--slot-time", default="auto", choices=["auto", "off"],
+                    help="the plan's dispatch-slot time factors for the greedy deal (the plan option)")
     ap.add_argument("--dump", default=None, metavar="FILE.npz",
                     help="also save every bin's stamps with its list's exported items")
     args = ap.parse_args(argv)
@@ -65,9 +69,10 @@ def main(argv=None):
             raise RuntimeError(G.gdpa_last_error())
         return np.frombuffer(buf, dtype=np.uint64)[:n.value].reshape(-1, 2).astype(np.int64)
 
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     dump = {}
     for deal in args.deals:
-        plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", deal=deal, claim=args.claim)
+        plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", deal=deal, claim=args.claim, slot_time=args.slot_time)
         st = plan.stats()
         h = plan.handle
         kernels = [("fwd", 0, lambda: G.gdpa_fwd(h, inp.q, inp.k, inp.v, qo, ko, B, H, d, act, win, o))]
@@ -89,22 +94,32 @@ def main(argv=None):
                 torch.cuda.synchronize()
                 s = stamps(plan)
                 stamps_last = s.copy()
-                s = s[s[:, 1] > 0]              # bins with items
-                busy = (s[:, 1] - s[:, 0]) * 10 / 1e3   # us
-                span = (s[:, 1].max() - s[:, 0].min()) * 10 / 1e3
-                runs.append((span, busy))
-            span, busy = sorted(runs[1:], key=lambda r: r[0])[len(runs[1:]) // 2]
+                P = st["bins"][lst]
+                has = s[:P, 1] > 0              # bins with items
+                busy_all = (s[:P, 1] - s[:P, 0]) * 10 / 1e3   # us
+                busy = busy_all[has]
+                span = (s[:P][has, 1].max() - s[:P][has, 0].min()) * 10 / 1e3
+                # dispatch round of each bin on its CU: bin p runs on the workgroup at position
+                # p % (P / 8) of its XCD's dispatch order, and each round places one per CU
+                by_slot = []
+                if P % cus == 0 and cus % 8 == 0:
+                    slot = (np.arange(P) % (P // 8)) // (cus // 8)
+                    by_slot = [round(float(busy_all[(slot == j) & has].mean()), 1)
+                               for j in range(P // cus) if np.any((slot == j) & has)]
+                runs.append((span, busy, by_slot))
+            span, busy, by_slot = sorted(runs[1:], key=lambda r: r[0])[len(runs[1:]) // 2]
             if args.dump:
                 dump[f"{deal}_{name}_stamps"] = stamps_last
                 dump[f"{deal}_{name}_export"] = np.asarray(G.gdpa_plan_export(h, lst))
             print(json.dumps({
-                "workload": WORKLOADS[cfg]["name"], "deal": deal, "claimed": st["claimed"][lst], "kernel": name,
+                "workload": WORKLOADS[cfg]["name"], "deal": deal, "claimed": st["claimed"][lst], "slot_weighted": st["slot_weighted"][lst], "kernel": name,
                 "bins": int(busy.size),
                 "busy_us": {"max": round(float(busy.max()), 1), "mean": round(float(busy.mean()), 1),
                             "min": round(float(busy.min()), 1)},
                 "max_over_min": round(float(busy.max() / busy.min()), 3),
                 "max_over_mean": round(float(busy.max() / busy.mean()), 3),
                 "span_us": round(float(span), 1),
+                "busy_by_slot_us": by_slot,
                 "planned_cost_max_over_min": round(st["bin_cost_max"][lst] / max(st["bin_cost_min"][lst], 1), 3),
             }), flush=True)
         plan.close()

@@ -62,6 +62,29 @@ const void* dkdv_kernel_ptr(int d, int team, int nb, int act) {
     return nullptr;
 }
 
+// Time factors per dispatch round for the greedy deal.  A persistent launch of k
+// workgroups per CU reaches each CU in k rounds (an XCD's first workgroups go one per
+// CU, then the next round, ...), and on the kernels below, workgroups of the early
+// rounds finished the same planned cost measurably sooner than those placed after
+// them (busy times measured per workgroup with the clock-probe build; the cause, most
+// likely how the CU's arbitration favours older waves, is not established).  A factor
+// is a round's busy time over the mean of all rounds with every bin dealt equal cost
+// (d = 128: windowed self-attention, 567,626 rows, H = 4, window 128; d = 64: the
+// cross-attention batch, whose 8-round split was then tuned on its own timing); the
+// deal gives a bin work in inverse proportion to its factor.
+struct SlotTimes {
+    int list, d, team, nb, per_cu;   // the list and its kernel's layout, workgroups per CU
+    double f[8];                     // factor of each dispatch round (per_cu of them)
+};
+constexpr SlotTimes kSlotTimes[] = {
+    // forward, two-wave teams
+    {LIST_FWD, 128, 2, 1, 4, {0.92, 1.0, 1.01, 1.07}},
+    // dK/dV, 16-row waves, two per 32-row team
+    {LIST_DKDV, 128, 1, 1, 4, {0.88, 1.025, 1.025, 1.07}},
+    // forward, one wave of two 32-row blocks
+    {LIST_FWD, 64, 1, 2, 8, {0.93, 0.93, 0.93, 0.93, 1.07, 1.07, 1.07, 1.07}},
+};
+
 int64_t pairs_of(int64_t lq, int64_t lk, int64_t w) {
     if (w == 0) return lq * lk;
     int64_t n = 0;
@@ -244,6 +267,7 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
     }
     if (o.deal < 0 || o.deal > 2) return fail(GDPA_ERR_INVALID_ARG, "deal must be 0, 1 or 2");
     if (o.claim < 0 || o.claim > 2) return fail(GDPA_ERR_INVALID_ARG, "claim must be 0, 1 or 2");
+    if (o.slot_time < 0 || o.slot_time > 1) return fail(GDPA_ERR_INVALID_ARG, "slot_time must be 0 or 1");
 
     if (q_off_host[0] != 0 || kv_off_host[0] != 0)
         return fail(GDPA_ERR_BAD_OFFSETS, "offsets must start at 0");
@@ -327,6 +351,7 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         // one bin per persistent workgroup (a team of waves): as many as the device
         // holds resident (host_only: 4 per CU)
         int P = o.bins[l];
+        const bool auto_bins = P == 0;
         if (P == 0) {
             P = 4 * cus;
             if (!p->host_only && dtype != GDPA_F32) {
@@ -344,7 +369,22 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         }
         // the fp32 path runs no work lists; its plan keeps items whole
         const bool split = o.no_split == 0 && dtype != GDPA_F32;
-        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split);
+        // dispatch-round factors: automatic bins only (the one-pass backward's kernels are not
+        // in the table, so a fused backward's list takes none)
+        const double* slot_time = nullptr;
+        const bool list_kernel = l == LIST_FWD || p->fused == 0;
+        if (o.slot_time == 0 && auto_bins && dtype != GDPA_F32 && list_kernel && cus % 8 == 0)
+            for (const SlotTimes& t : kSlotTimes)
+                if (t.list == l && t.d == d && t.team == L.team[l] && t.nb == L.nb[l] && P == t.per_cu * cus)
+                    slot_time = t.f;
+        std::vector<double> bin_time;
+        if (slot_time) {
+            // bin q runs on the workgroup the XCD remap gives it: position q % (P / 8) in its
+            // XCD's dispatch order, so dispatch round position / (CUs per XCD)
+            bin_time.resize(P);
+            for (int q = 0; q < P; ++q) bin_time[q] = slot_time[(q % (P / 8)) / (cus / 8)];
+        }
+        p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split, bin_time);
     }
 
     // lists whose items are claimed at run time: those whose kernel walks them in one-wave
@@ -454,6 +494,7 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
     for (int l = 0; l < 3; ++l) {
         out->n_parts[l] = plan->lists[l].n_parts;
         out->claimed[l] = plan->claimed[l] ? 1 : 0;
+        out->slot_weighted[l] = plan->lists[l].weighted ? 1 : 0;
     }
     return GDPA_OK;
 }

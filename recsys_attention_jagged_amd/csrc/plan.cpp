@@ -47,7 +47,8 @@ struct Cand {
 }  // namespace
 
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
-                   int H, int window, int P, int team, int nb, int deal, bool split) {
+                   int H, int window, int P, int team, int nb, int deal, bool split,
+                   const std::vector<double>& bin_time) {
     WorkList wl;
     wl.kind = kind;
     wl.P = P;
@@ -138,16 +139,21 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
     std::vector<int32_t> bin_of(cands.size());
     std::vector<int32_t> count(P, 0);
     wl.bin_cost.assign(P, 0);
-    typedef std::pair<int64_t, int> Load;   // (cost so far, bin): least cost, then lowest bin
+    // (cost so far times the bin's time factor, bin): least, then lowest bin.  Without
+    // factors the keys are the integer costs, exact in a double
+    typedef std::pair<double, int> Load;
     std::priority_queue<Load, std::vector<Load>, std::greater<Load>> least;
+    const bool weighted = deal == DEAL_GREEDY && (int)bin_time.size() == P;
+    wl.weighted = weighted;
     if (deal == DEAL_GREEDY)
-        for (int p = 0; p < P; ++p) least.push(Load(0, p));
+        for (int p = 0; p < P; ++p) least.push(Load(0.0, p));
     for (size_t r = 0; r < cands.size(); ++r) {
         int p;
         if (deal == DEAL_GREEDY) {
             p = least.top().second;
             least.pop();
-            least.push(Load(wl.bin_cost[p] + cands[r].cost, p));
+            const int64_t c = wl.bin_cost[p] + cands[r].cost;
+            least.push(Load(weighted ? (double)c * bin_time[p] : (double)c, p));
         } else {
             const int64_t rnd = (int64_t)r / P, pos = (int64_t)r % P;
             p = (int)((deal == DEAL_ROUND_ROBIN || rnd % 2 == 0) ? pos : P - 1 - pos);

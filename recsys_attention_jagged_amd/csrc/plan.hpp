@@ -65,7 +65,8 @@ struct WorkList {
     std::vector<Item> items;        // bin-major, deal order inside a bin
     std::vector<int32_t> order;     // the items in planner order (cost descending, then the
                                     // tie-break): order[r] = index in `items` of the r-th
-    std::vector<int64_t> bin_cost;  // P
+    std::vector<int64_t> bin_cost;  // P (unweighted)
+    bool weighted = false;          // the greedy deal took per-bin time factors
     int64_t n_steps = 0;
     int n_parts = 0;                // partial-output slots (chunks of cut items)
 };
@@ -80,8 +81,11 @@ constexpr int kStepCharge = 32;
 
 Layout auto_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& lk, int d);
 void tile_sizes(int kind, int team, int nb, int* t_stat, int* t_strm);
+// bin_time: per-bin factors on the greedy deal's costs (its key is a bin's cost times
+// the factor: a bin expected to run slower gets less work); empty = all 1
 WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<int64_t>& lk,
-                   int H, int window, int P, int team, int nb, int deal, bool split);
+                   int H, int window, int P, int team, int nb, int deal, bool split,
+                   const std::vector<double>& bin_time = std::vector<double>());
 std::vector<int32_t> export_list(const WorkList& wl);
 // dS blocks of the two-kernel backward with stored scores' gradients: one 32 x 32
 // bf16 block (2 KiB, kv row major) per (head, 32-row q tile, 32-row kv tile) that

@@ -202,6 +202,47 @@ def test_plan_claims_long_item_lists():
     assert claimed(lq, lk, dtype="f32", claim="always")[0] == [0, 0, 0]
 
 
+def test_plan_slot_time_factors():
+    """The greedy deal's dispatch-round factors: taken by the d = 128 forward (two-wave
+    teams) and dK/dV lists of the jagged and windowed self-attention workloads at four
+    workgroups per CU (a host-only plan's bins), by no list of the cross-attention and
+    PMA workloads here (their d = 64 forward runs eight per CU on the device, their
+    backward is the one-pass kernel), never with explicit bins or slot_time = off.  The
+    deal follows the factors: bins of the first dispatch round get about f_last / f_first
+    times the streaming steps of those of the last."""
+    def plan(lq, lk, d, window, H, **kw):
+        return G.gdpa_plan_create(offsets(lq), offsets(lk), len(lq), H, d, window, "bf16", host_only=True, **kw)
+
+    def steps_by_round(p, lst):
+        e = np.asarray(G.gdpa_plan_export(p, lst))
+        P, n = int(e[0]), int(e[1])
+        ptr = e[6:6 + P + 1]
+        it = e[6 + P + 1:].reshape(n, 6)
+        steps = np.maximum(it[:, 4] - it[:, 3] + 1, 0)
+        per_bin = np.add.reduceat(np.append(steps, 0), ptr[:-1])[:P] * (np.diff(ptr) > 0)
+        rnd = (np.arange(P) % (P // 8)) // 32   # host-only plans: 256 CUs, 32 per XCD
+        return [float(per_bin[rnd == j].mean()) for j in range(4)]
+
+    want = {2: [1, 1, 0], 3: [0, 0, 0], 4: [0, 0, 0], 5: [1, 1, 0]}
+    for cfg in (2, 3, 4, 5):
+        w = WORKLOADS[cfg]
+        lq, lk = workload_lengths(cfg)
+        args = (list(lq), list(lk), w["d"], w["window"], w["H"])
+        for kw, exp in (({}, want[cfg]), ({"slot_time": "off"}, [0, 0, 0]), ({"bins": (1024, 1024, 1024)}, [0, 0, 0])):
+            p = plan(*args, **kw)
+            try:
+                st = G.gdpa_plan_stats(p)
+                assert st["slot_weighted"] == exp, (cfg, kw, st["slot_weighted"])
+                if cfg == 5:
+                    for lst, f_first, f_last in ((0, 0.92, 1.07), (1, 0.88, 1.07)):
+                        r = steps_by_round(p, lst)
+                        ratio = r[0] / r[3]
+                        target = f_last / f_first if exp[lst] else 1.0
+                        assert abs(ratio / target - 1) < 0.03, (kw, lst, r, target)
+            finally:
+                G.gdpa_plan_destroy(p)
+
+
 # ---------------------------------------------------------------------------
 # error paths (forced from the host)
 # ---------------------------------------------------------------------------
@@ -229,6 +270,8 @@ def test_create_rejects_bad_arguments():
     assert bad(team=(2, 0, 0)) == 1            # two-wave teams only at d = 128
     assert bad(claim=3) == 1
     assert bad(claim=-1) == 1
+    assert bad(slot_time=2) == 1
+    assert bad(slot_time=-1) == 1
     assert bad(d=128, team=(0, 0, 2), blocks=(0, 0, 2)) == 1   # two-wave teams: one block per wave
     assert bad(d=128, team=(2, 0, 0), blocks=(2, 0, 0)) == 1
     assert bad(qo=np.array([1, 3, 7], np.int32)) == 2           # BAD_OFFSETS: not starting at 0
