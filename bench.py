@@ -272,6 +272,8 @@ def main(argv=None):
     ap.add_argument("--claim", default="auto", choices=["auto", "bins", "always"],
                     help="how workgroups get items: claimed at run time where the plan decides (auto), "
                          "the planner's bins only, or claimed wherever the kernel runs one-wave teams")
+    ap.add_argument("--dq-team", default="auto", choices=["auto", "one_wave"],
+                    help="dQ from stored dS in two-wave teams over 64-row q items (auto) or one-wave workgroups")
     ap.add_argument("--slot-time", default="auto", choices=["auto", "off"],
                     help="deal weighted by each bin's dispatch round on its CU where the plan decides (auto), "
                          "or every bin dealt by plain cost")
@@ -332,7 +334,8 @@ def main(argv=None):
         return 2
     norm = w["rms"] if args.norm else ""
     t0 = time.perf_counter()
-    plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", claim=args.claim, slot_time=args.slot_time)
+    plan = G.Plan(inp.q_off, inp.kv_off, H, d, win, "bf16", claim=args.claim, slot_time=args.slot_time,
+                  dq_team=args.dq_team)
     plan_ms = (time.perf_counter() - t0) * 1e3
     st = plan.stats()
     Tq, Tk, pairs = st["Tq"], st["Tk"], st["valid_pairs"]
@@ -513,6 +516,7 @@ def main(argv=None):
                    "bwd_inputs": "fp8 Q, K, dO" if fp8_bwd else "bf16",
                    "claimed_lists": st["claimed"],
                    "slot_weighted_lists": st["slot_weighted"],
+                   "dq_team": st["dq_team"],
                    "backward": ("one KV-stationary pass (D formed from P and dP)" if sm and fused else
                                 "dQ kernel (also D and the row statistics) + dK/dV kernel" if sm else
                                 "dK/dV + dQ kernels (1/rms pre-pass before the forward)" if norm else

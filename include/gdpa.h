@@ -84,8 +84,9 @@ typedef enum {
  * out, plain fp32 arithmetic (no MFMA; a correctness path for small inputs). */
 typedef enum { GDPA_F32 = 0, GDPA_BF16 = 1, GDPA_BF16_F32OUT = 2 } gdpa_dtype;
 
-/* Work lists of a plan, for gdpa_plan_export / gdpa_plan_stats. */
-typedef enum { GDPA_LIST_FWD = 0, GDPA_LIST_DKDV = 1, GDPA_LIST_DQ = 2 } gdpa_list;
+/* Work lists of a plan, for gdpa_plan_export / gdpa_plan_stats.  DQ_TEAM: dQ from
+ * stored dS in two-wave teams (gdpa_plan_stats: dq_team 2), export only. */
+typedef enum { GDPA_LIST_FWD = 0, GDPA_LIST_DKDV = 1, GDPA_LIST_DQ = 2, GDPA_LIST_DQ_TEAM = 3 } gdpa_list;
 
 /* Planning options.  All-zero (or a NULL pointer) selects the defaults. */
 typedef struct {
@@ -118,6 +119,11 @@ typedef struct {
                         faster than later ones), so earlier-placed bins get more work; 1 every
                         bin is dealt by plain cost.  Results do not depend on it (bit for
                         bit) */
+    int dq_team;     /* dQ from stored dS (see ds_bytes): 0 automatic, two-wave teams over
+                        64-row q items (a work list of its own, list 3 of
+                        gdpa_plan_export; each K tile read once for two q tiles); 1 one-wave
+                        workgroups over the dQ list.  Results equal bit for bit unless
+                        items are cut into chunks (their chunks then differ) */
 } gdpa_plan_opts;
 
 /* Summary numbers of a plan. */
@@ -138,6 +144,11 @@ typedef struct {
     int64_t ds_bytes;        /* bytes of the plan's dS buffer (0: gdpa_bwd does not store dS) */
     int32_t claimed[3];      /* 1: the list's items are claimed at run time (see claim) */
     int32_t slot_weighted[3];/* 1: the list's deal took the dispatch-slot time factors */
+    int32_t dq_team;         /* dQ from stored dS: 0 none (ds_bytes 0), 1 one-wave workgroups
+                                over the dQ list, 2 two-wave teams over list 3 */
+    int32_t dq_team_items;   /* list 3 (dq_team 2): work items, bins, cut items' chunk slots */
+    int32_t dq_team_bins;
+    int32_t dq_team_parts;
 } gdpa_plan_stats_t;
 
 typedef struct gdpa_plan_s* gdpa_plan;
@@ -469,7 +480,7 @@ gdpa_status gdpa_pffn_bwd(gdpa_plan plan, const void* q, const void* wk, const v
  * steps, the item writes zeros) and part the chunk's partial-output slot (-1 for
  * an item that stores its outputs itself).  With buf == NULL, *n receives the length;
  * otherwise *n is the capacity of buf on entry and the length on return.
- * Errors: INVALID_ARG (bad list or capacity too small).
+ * Errors: INVALID_ARG (bad list, list 3 on a plan without it, or capacity too small).
  */
 gdpa_status gdpa_plan_export(gdpa_plan plan, int list, int32_t* buf, size_t* n);
 

@@ -24,7 +24,7 @@ STATUS = {0: "GDPA_OK", 1: "GDPA_ERR_INVALID_ARG", 2: "GDPA_ERR_BAD_OFFSETS", 3:
           4: "GDPA_ERR_PLAN_MISMATCH", 5: "GDPA_ERR_HIP", 6: "GDPA_ERR_NOMEM"}
 ACT = {"gelu": 0, "silu": 1, "gelu_poly": 2, "gelu_taylor6": 3, "identity": 4, "one": 5}
 DTYPE = {"f32": 0, "bf16": 1, "bf16_f32out": 2}
-LIST = {"fwd": 0, "dkdv": 1, "dq": 2}
+LIST = {"fwd": 0, "dkdv": 1, "dq": 2, "dq_team": 3}
 DEAL = {"greedy": 0, "zigzag": 1, "round_robin": 2}
 
 
@@ -39,7 +39,7 @@ class gdpa_plan_opts(ctypes.Structure):
     _fields_ = [("host_only", ctypes.c_int), ("bins", ctypes.c_int * 3), ("team", ctypes.c_int * 3),
                 ("blocks", ctypes.c_int * 3), ("deal", ctypes.c_int), ("no_split", ctypes.c_int),
                 ("unfused", ctypes.c_int), ("no_ds", ctypes.c_int), ("claim", ctypes.c_int),
-                ("slot_time", ctypes.c_int)]
+                ("slot_time", ctypes.c_int), ("dq_team", ctypes.c_int)]
 
 
 class gdpa_plan_stats_t(ctypes.Structure):
@@ -49,7 +49,8 @@ class gdpa_plan_stats_t(ctypes.Structure):
                 ("tile_strm", ctypes.c_int32 * 3), ("bin_cost_max", ctypes.c_int64 * 3),
                 ("bin_cost_min", ctypes.c_int64 * 3), ("bwd_fused", ctypes.c_int32),
                 ("n_parts", ctypes.c_int32 * 3), ("ds_bytes", ctypes.c_int64), ("claimed", ctypes.c_int32 * 3),
-                ("slot_weighted", ctypes.c_int32 * 3)]
+                ("slot_weighted", ctypes.c_int32 * 3), ("dq_team", ctypes.c_int32),
+                ("dq_team_items", ctypes.c_int32), ("dq_team_bins", ctypes.c_int32), ("dq_team_parts", ctypes.c_int32)]
 
 
 _lib = None
@@ -155,7 +156,7 @@ def _enum(v, table):
 def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: int, dtype,
                      host_only: bool = False, bins=(0, 0, 0), team=(0, 0, 0), blocks=(0, 0, 0),
                      deal="greedy", split: bool = True, unfused: bool = False, stream=None,
-                     store_ds: bool = True, claim="auto", slot_time="auto") -> int:
+                     store_ds: bool = True, claim="auto", slot_time="auto", dq_team="auto") -> int:
     """Returns an opaque plan handle (int).  Offsets: host int32 [B + 1].  The work
     lists are copied on `stream` (torch's current stream by default; none for a
     host-only plan)."""
@@ -163,7 +164,7 @@ def gdpa_plan_create(q_off_host, kv_off_host, B: int, H: int, d: int, window: in
     ko = np.ascontiguousarray(kv_off_host, dtype=np.int32)
     if qo.shape != (B + 1,) or ko.shape != (B + 1,):
         raise ValueError("offsets must have B + 1 entries")
-    opts = _opts(host_only, bins, team, blocks, deal, split, unfused, store_ds, claim, slot_time)
+    opts = _opts(host_only, bins, team, blocks, deal, split, unfused, store_ds, claim, slot_time, dq_team)
     out = _vp()
     _check(load_library().gdpa_plan_create(qo.ctypes.data, ko.ctypes.data, B, H, d, window,
                                            _enum(dtype, DTYPE), ctypes.byref(opts),
@@ -296,12 +297,15 @@ def gdpa_norm_bwd_dq(plan, q, k, v, dout, q_off_dev, kv_off_dev, B, H, d, act, w
 
 CLAIM = {"auto": 0, "bins": 1, "always": 2}
 SLOT_TIME = {"auto": 0, "off": 1}
+DQ_TEAM = {"auto": 0, "one_wave": 1}
 
 
-def _opts(host_only, bins, team, blocks, deal, split, unfused, store_ds=True, claim="auto", slot_time="auto"):
+def _opts(host_only, bins, team, blocks, deal, split, unfused, store_ds=True, claim="auto", slot_time="auto",
+          dq_team="auto"):
     return gdpa_plan_opts(int(host_only), (ctypes.c_int * 3)(*bins), (ctypes.c_int * 3)(*team),
                           (ctypes.c_int * 3)(*blocks), _enum(deal, DEAL), int(not split), int(unfused),
-                          int(not store_ds), _enum(claim, CLAIM), _enum(slot_time, SLOT_TIME))
+                          int(not store_ds), _enum(claim, CLAIM), _enum(slot_time, SLOT_TIME),
+                          _enum(dq_team, DQ_TEAM))
 
 
 def gdpa_pffn_plan_create(Tq: int, M: int, H: int, d: int, dtype, host_only: bool = False, bins=(0, 0, 0),

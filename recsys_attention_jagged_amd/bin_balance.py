@@ -83,8 +83,9 @@ def main(argv=None):
         else:
             kernels.append(("dkdv", 1, lambda: G.gdpa_bwd_dkdv(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d,
                                                                act, win, dk, dv)))
-            kernels.append(("dq", 2, lambda: G.gdpa_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act,
-                                                           win, dq)))
+            # dQ from stored dS in two-wave teams walks the plan's list 3
+            kernels.append(("dq", 3 if st["dq_team"] == 2 else 2,
+                            lambda: G.gdpa_bwd_dq(h, inp.q, inp.k, inp.v, inp.do, qo, ko, B, H, d, act, win, dq)))
         for name, lst, call in kernels:
             runs = []
             for _ in range(args.reps + 1):      # the first launch warms up
@@ -94,7 +95,7 @@ def main(argv=None):
                 torch.cuda.synchronize()
                 s = stamps(plan)
                 stamps_last = s.copy()
-                P = st["bins"][lst]
+                P = st["dq_team_bins"] if lst == 3 else st["bins"][lst]
                 has = s[:P, 1] > 0              # bins with items
                 busy_all = (s[:P, 1] - s[:P, 0]) * 10 / 1e3   # us
                 busy = busy_all[has]
@@ -112,7 +113,8 @@ def main(argv=None):
                 dump[f"{deal}_{name}_stamps"] = stamps_last
                 dump[f"{deal}_{name}_export"] = np.asarray(G.gdpa_plan_export(h, lst))
             print(json.dumps({
-                "workload": WORKLOADS[cfg]["name"], "deal": deal, "claimed": st["claimed"][lst], "slot_weighted": st["slot_weighted"][lst], "kernel": name,
+                "workload": WORKLOADS[cfg]["name"], "deal": deal, "claimed": st["claimed"][lst] if lst < 3 else 0,
+                "slot_weighted": st["slot_weighted"][lst] if lst < 3 else 0, "kernel": name,
                 "bins": int(busy.size),
                 "busy_us": {"max": round(float(busy.max()), 1), "mean": round(float(busy.mean()), 1),
                             "min": round(float(busy.min()), 1)},
@@ -120,7 +122,8 @@ def main(argv=None):
                 "max_over_mean": round(float(busy.max() / busy.mean()), 3),
                 "span_us": round(float(span), 1),
                 "busy_by_slot_us": by_slot,
-                "planned_cost_max_over_min": round(st["bin_cost_max"][lst] / max(st["bin_cost_min"][lst], 1), 3),
+                "planned_cost_max_over_min": (round(st["bin_cost_max"][lst] / max(st["bin_cost_min"][lst], 1), 3)
+                                              if lst < 3 else None),
             }), flush=True)
         plan.close()
     if args.dump:

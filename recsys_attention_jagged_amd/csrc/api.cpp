@@ -94,6 +94,10 @@ int64_t pairs_of(int64_t lq, int64_t lk, int64_t w) {
 
 }  // namespace
 
+// work lists of a plan: GDPA_LIST_FWD, _DKDV, _DQ and the two-wave dQ-from-dS list
+constexpr int kLists = 4;
+constexpr int LIST_DQ_TEAM = 3;
+
 struct gdpa_plan_s;
 static gdpa_status upload(gdpa_plan_s* p, hipStream_t s);
 static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_host, int B, int H, int d,
@@ -108,18 +112,22 @@ struct gdpa_plan_s {
     std::vector<int64_t> lq, lk;
     int64_t Tq = 0, Tk = 0, valid_pairs = 0;
     int fused = 0;   // gdpa_bwd: 0 two kernels, 1 one KV-stationary pass, 2 one Q-stationary pass
-    WorkList lists[3];
-    DevRec* d_items[3] = {nullptr, nullptr, nullptr};
-    int32_t* d_bin_ptr[3] = {nullptr, nullptr, nullptr};
+    // the three lists of gdpa_list, and with stored dS (dq_team) a fourth: the dQ list
+    // dealt again as 64-row items for the two-wave dQ-from-dS kernel (the dQ list
+    // itself stays, for the kernels that recompute dS: JFA, the norm prologue)
+    WorkList lists[kLists];
+    bool dq_team = false;
+    DevRec* d_items[kLists] = {};
+    int32_t* d_bin_ptr[kLists] = {};
     // lists whose items the workgroups claim at run time: the claim order and the
     // (claims, finished workgroups) counters
-    bool claimed[3] = {false, false, false};
-    int32_t* d_order[3] = {nullptr, nullptr, nullptr};
-    int* d_claim[3] = {nullptr, nullptr, nullptr};
+    bool claimed[kLists] = {};
+    int32_t* d_order[kLists] = {};
+    int* d_claim[kLists] = {};
     // cut items of the Q-stationary lists: groups for the reduction, fp32 slots
-    int n_groups[3] = {0, 0, 0};
-    DevGroup* d_groups[3] = {nullptr, nullptr, nullptr};
-    float* d_part[3] = {nullptr, nullptr, nullptr};
+    int n_groups[kLists] = {};
+    DevGroup* d_groups[kLists] = {};
+    float* d_part[kLists] = {};
     // pFFN plans: device copies of the offsets {0, Tq} and {0, M}
     int32_t* d_off = nullptr;
     // stored dS of the d = 128 two-kernel backward (see DsLayout)
@@ -128,8 +136,8 @@ struct gdpa_plan_s {
     __bf16* d_ds = nullptr;
     // the device records and chunk groups of each list, resolved on the host at
     // creation (bf16 plans; the upload and gdpa_fwd_noalloc copy them from here)
-    std::vector<DevRec> h_recs[3];
-    std::vector<DevGroup> h_groups[3];
+    std::vector<DevRec> h_recs[kLists];
+    std::vector<DevGroup> h_groups[kLists];
     // pinned host copy of everything uploaded at creation (records, bin pointers,
     // chunk groups, pFFN offsets): the copies are enqueued on the creation stream
     // and read from here, so it lives as long as the plan
@@ -141,7 +149,7 @@ struct gdpa_plan_s {
     bool pffn = false;
 
     ~gdpa_plan_s() {
-        for (int l = 0; l < 3; ++l) {
+        for (int l = 0; l < kLists; ++l) {
             if (d_items[l]) (void)hipFree(d_items[l]);
             if (d_bin_ptr[l]) (void)hipFree(d_bin_ptr[l]);
             if (d_order[l]) (void)hipFree(d_order[l]);
@@ -166,7 +174,8 @@ static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
     const std::vector<DevGroup>* groups = p->h_groups;
     size_t bytes = 0;
     auto align = [](size_t n) { return (n + 255) & ~(size_t)255; };
-    for (int l = 0; l < 3; ++l) {
+    const int n_lists = p->dq_team ? kLists : 3;
+    for (int l = 0; l < n_lists; ++l) {
         bytes += align(recs[l].size() * sizeof(DevRec)) + align(p->lists[l].bin_ptr.size() * sizeof(int32_t)) +
                  align(groups[l].size() * sizeof(DevGroup));
         if (p->claimed[l]) bytes += align(p->lists[l].order.size() * sizeof(int32_t)) + align(2 * sizeof(int));
@@ -189,7 +198,7 @@ static gdpa_status upload(gdpa_plan_s* p, hipStream_t s) {
         h += align(n);
         return r;
     };
-    for (int l = 0; l < 3 && e == hipSuccess; ++l) {
+    for (int l = 0; l < n_lists && e == hipSuccess; ++l) {
         const WorkList& wl = p->lists[l];
         e = put((void**)&p->d_items[l], recs[l].data(), recs[l].size() * sizeof(DevRec));
         if (e == hipSuccess) e = put((void**)&p->d_bin_ptr[l], wl.bin_ptr.data(), wl.bin_ptr.size() * sizeof(int32_t));
@@ -268,6 +277,7 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
     if (o.deal < 0 || o.deal > 2) return fail(GDPA_ERR_INVALID_ARG, "deal must be 0, 1 or 2");
     if (o.claim < 0 || o.claim > 2) return fail(GDPA_ERR_INVALID_ARG, "claim must be 0, 1 or 2");
     if (o.slot_time < 0 || o.slot_time > 1) return fail(GDPA_ERR_INVALID_ARG, "slot_time must be 0 or 1");
+    if (o.dq_team < 0 || o.dq_team > 1) return fail(GDPA_ERR_INVALID_ARG, "dq_team must be 0 or 1");
 
     if (q_off_host[0] != 0 || kv_off_host[0] != 0)
         return fail(GDPA_ERR_BAD_OFFSETS, "offsets must start at 0");
@@ -387,6 +397,24 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split, bin_time);
     }
 
+    // dQ from stored dS in two-wave teams (option dq_team, automatic): the dQ list dealt
+    // again as 64-row items, one 32-row q tile per wave; the dQ list's bins when given,
+    // else as many teams as the device holds resident (host_only: 4 per CU)
+    if (p->use_ds && o.dq_team == 0) {
+        int P = o.bins[LIST_DQ];
+        if (P == 0) {
+            P = 4 * cus;
+            int per_cu = 0;
+            if (!p->host_only &&
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dq_from_ds_team_kernel_ptr(), 128, 0) ==
+                    hipSuccess &&
+                per_cu > 0)
+                P = cus * per_cu;
+        }
+        p->lists[LIST_DQ_TEAM] = plan_list(LIST_DQ, lq, lk, H, window, P, 2, 1, o.deal, o.no_split == 0);
+        p->dq_team = true;
+    }
+
     // lists whose items are claimed at run time: those whose kernel walks them in one-wave
     // teams (not the d = 128 16-row dK/dV kernel, nor dQ from stored dS) and, by default,
     // whose items average 64 steps or more: a claim waits for every tile in flight, about
@@ -404,7 +432,7 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
     }
 
     if (dtype != GDPA_F32) {
-        for (int l = 0; l < 3; ++l) {
+        for (int l = 0; l < (p->dq_team ? kLists : 3); ++l) {
             p->h_recs[l] = p->use_ds ? device_records(p->lists[l], p->q_off, p->kv_off, p->ds, window)
                                      : device_records(p->lists[l], p->q_off, p->kv_off);
             if (p->lists[l].n_parts > 0) p->h_groups[l] = device_groups(p->lists[l], p->q_off, p->kv_off);
@@ -418,7 +446,7 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
             return st;
         }
 #ifdef GDPA_BIN_CLOCK
-        p->n_clock = 2 * (size_t)std::max(p->lists[0].P, std::max(p->lists[1].P, p->lists[2].P));
+        p->n_clock = 2 * (size_t)std::max(std::max(p->lists[0].P, p->lists[3].P), std::max(p->lists[1].P, p->lists[2].P));
         hipError_t e = hipMalloc((void**)&p->d_clock, p->n_clock * sizeof(unsigned long long));
         if (e == hipSuccess) e = hipMemset(p->d_clock, 0, p->n_clock * sizeof(unsigned long long));
         if (e != hipSuccess) {
@@ -455,7 +483,9 @@ void gdpa_plan_destroy(gdpa_plan plan) { delete plan; }
 gdpa_status gdpa_plan_export(gdpa_plan plan, int list, int32_t* buf, size_t* n) {
     g_err.clear();
     if (!plan || !n) return fail(GDPA_ERR_INVALID_ARG, "plan or n is NULL");
-    if (list < 0 || list > 2) return fail(GDPA_ERR_INVALID_ARG, "list must be 0, 1 or 2");
+    if (list < 0 || list > 3) return fail(GDPA_ERR_INVALID_ARG, "list must be 0, 1, 2 or 3");
+    if (list == LIST_DQ_TEAM && !plan->dq_team)
+        return fail(GDPA_ERR_INVALID_ARG, "list 3 (dQ from stored dS in two-wave teams) is not in this plan");
     const std::vector<int32_t> v = export_list(plan->lists[list]);
     if (!buf) {
         *n = v.size();
@@ -495,6 +525,13 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
         out->n_parts[l] = plan->lists[l].n_parts;
         out->claimed[l] = plan->claimed[l] ? 1 : 0;
         out->slot_weighted[l] = plan->lists[l].weighted ? 1 : 0;
+    }
+    out->dq_team = plan->use_ds ? (plan->dq_team ? 2 : 1) : 0;
+    if (plan->dq_team) {
+        const WorkList& wl = plan->lists[LIST_DQ_TEAM];
+        out->dq_team_items = (int32_t)wl.items.size();
+        out->dq_team_bins = wl.P;
+        out->dq_team_parts = wl.n_parts;
     }
     return GDPA_OK;
 }
@@ -748,16 +785,16 @@ static gdpa_status bwd_parts(gdpa_plan plan, const void* q, const void* k, const
             if (e == hipSuccess) e = reduce_parts(plan, LIST_DKDV, mv, dv, s, 1);
         }
         if (e == hipSuccess && want_dq && any_q) {
-            const WorkList& wl = plan->lists[LIST_DQ];
+            const int l = plan->dq_team ? LIST_DQ_TEAM : LIST_DQ;
             KernelArgs b = a;
-            b.items = plan->d_items[LIST_DQ];
-            b.bin_ptr = plan->d_bin_ptr[LIST_DQ];
-            set_claims(b, plan, LIST_DQ);
-            b.P = wl.P;
-            b.part = plan->d_part[LIST_DQ];
+            b.items = plan->d_items[l];
+            b.bin_ptr = plan->d_bin_ptr[l];
+            set_claims(b, plan, l);
+            b.P = plan->lists[l].P;
+            b.part = plan->d_part[l];
             b.ds = plan->d_ds;
-            e = launch_dq_from_ds(b, f8 != nullptr, s);
-            if (e == hipSuccess) e = reduce_parts(plan, LIST_DQ, mq, dq, s);
+            e = plan->dq_team ? launch_dq_from_ds_team(b, f8 != nullptr, s) : launch_dq_from_ds(b, f8 != nullptr, s);
+            if (e == hipSuccess) e = reduce_parts(plan, l, mq, dq, s);
         }
     } else {
         if (want_dkdv && any_k) {

@@ -575,6 +575,207 @@ __global__ __launch_bounds__(64, 1) void dq_from_ds_kernel(const KernelArgs a, c
 #endif
 }
 
+// -------------------------------------------------------------------------
+// dQ from the stored dS blocks, two-wave teams over 64-row q items
+// -------------------------------------------------------------------------
+// The same product with two adjacent 32-row q tiles per item, one per wave: each K
+// tile of the item's steps (the union of both tiles' bands) is loaded once into
+// the team's slot and read by both waves, and each wave loads its own tile's dS
+// block beside it.  A step costs 12 KiB of LDS for two tiles' products instead of
+// 10 KiB for one, so the same LDS holds half again as much work in flight, with
+// six waves per CU instead of four.  A wave whose tile has no block for a step (the
+// step pairs only with the other tile, or the item's second tile lies past the
+// sample's queries) loads a zero-range block (its instruction count stays the
+// team's) and skips the products.  Items of this list carry (pad0, pad1) = (the
+// sample's first block of this head, blocks per q tile), as the dK/dV list's do.
+template <bool F8>
+struct DsRing2 {
+    static constexpr int D = 128;
+    static constexpr int KT = 32 * D * 2, DT = 32 * 32 * 2, SLOT = KT + 2 * DT;
+    static constexpr int KL = F8 ? KT / 2 : KT;   // bytes of K loaded per job
+    static constexpr int JK = KL / 1024 / 2;      // K instructions per job and wave
+    static constexpr int JX = JK + DT / 1024;     // instructions per job and wave
+    static constexpr int R = 4;
+    static constexpr int BYTES = R * SLOT;
+    uint32_t offk[JK], offd[DT / 1024];
+    uint32_t base;
+    char* gbase;
+    int wt, issued;
+
+    __device__ __forceinline__ void init(char* slice, uint32_t row_stride, int wt_, int lane) {
+        gbase = slice;
+        base = lds_addr(slice);
+        wt = wt_;
+        issued = 0;
+#pragma unroll
+        for (int jj = 0; jj < JK; ++jj) {   // this wave's K instructions: 1 KiB parts 2 jj + wt
+            const int slot = (2 * jj + wt) * 64 + lane;
+            if constexpr (F8) {
+                const int row = slot / 8, pos = slot % 8;
+                offk[jj] = (uint32_t)row * row_stride + (uint32_t)((pos ^ swz8<D>(row)) << 4);
+            } else {
+                const int row = slot / 16, pos = slot % 16;
+                offk[jj] = (uint32_t)row * row_stride + (uint32_t)((pos ^ swz<D>(row)) << 4);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < DT / 1024; ++jj) {
+            const int slot = jj * 64 + lane, row = slot / 4, pos = slot % 4;
+            offd[jj] = (uint32_t)row * 64u + (uint32_t)((pos ^ swz<32>(row)) << 4);
+        }
+    }
+    __device__ __forceinline__ char* ktile(int job) const { return gbase + (job % R) * SLOT; }
+    __device__ __forceinline__ char* dtile(int job) const { return ktile(job) + KT + wt * DT; }
+    // this wave's half of K rows [row0, row0 + 32) (k_off = row0 * stride) and its own
+    // 2 KiB dS block `blk` into the next slot
+    __device__ __forceinline__ void issue(Slice k, uint32_t k_off, rsrc_t blk) {
+        const uint32_t lds = base + (uint32_t)((issued % R) * SLOT);
+        const rsrc_t rk = slice_at(k, k_off);
+#pragma unroll
+        for (int jj = 0; jj < JK; ++jj) dma16(rk, offk[jj], lds + (uint32_t)(2 * jj + wt) * 1024u);
+#pragma unroll
+        for (int jj = 0; jj < DT / 1024; ++jj) dma16(blk, offd[jj], lds + (uint32_t)(KT + wt * DT + jj * 1024));
+        ++issued;
+    }
+    __device__ __forceinline__ void wait(int k) const { wait_jobs<JX>(issued - 1 - k); }
+};
+
+template <bool F8>
+struct DqDsTeamPol : Common {
+    static constexpr int D = 128, NDB = D / 32;
+    f32x16 acc[NDB];
+
+    __device__ DqDsTeamPol(const KernelArgs& args, int lane_, int wt_) : Common(args, lane_, wt_, D) {}
+
+    // this wave's q tile of item w, and the dS block of its step s (-1: none)
+    __device__ __forceinline__ int tile(const Rec& w) const { return 2 * w.t + wt; }
+    __device__ __forceinline__ long block(const Rec& w, int s) const {
+        const int i = tile(w);
+        if (i * 32 >= w.lq) return -1;
+        const int a1 = min(w.lq - 1, i * 32 + 31);
+        const int js0 = win > 0 ? max(0, i * 32 - win + 1) >> 5 : 0;
+        const int js1 = win > 0 ? min(w.lk - 1, a1 + win - 1) >> 5 : (w.lk - 1) >> 5;
+        if (s < js0 || s > js1) return -1;
+        return (long)w.pad0 + (long)i * w.pad1 + (long)(s - js0);
+    }
+
+    __device__ __forceinline__ void issue(DsRing2<F8>& g, const Rec& w, int s) const {
+        const long blk = block(w, s);
+        const rsrc_t ds = blk >= 0 ? slice_rsrc(a.ds + (size_t)blk * 1024, 1, 2048u, 2048u)
+                                   : slice_rsrc(a.ds, 0, 2048u, 2048u);
+        const size_t kb = ((size_t)w.ks * H + w.h) * D;
+        if constexpr (F8)
+            g.issue(slice_of((const uint8_t*)a.k + kb, w.lk, rs / 2, D), (uint32_t)(s * 32) * (rs / 2), ds);
+        else
+            g.issue(slice_of((const __bf16*)a.k + kb, w.lk, rs, D * 2), (uint32_t)(s * 32) * rs, ds);
+    }
+
+    // dQ^T += K^T dS^T for this wave's tile (the operands as in the one-wave kernel)
+    __device__ __forceinline__ void step(const DsRing2<F8>& g, int job) {
+        const char* kt = g.ktile(job);
+        const char* dt = g.dtile(job);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const bf16x8 b = lds_col8<32>(dt, 16 * m, 0, lane);
+            bf16x8 kop[NDB];
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                kop[db] = F8 ? lds_col8_f8<D>(kt, 16 * m, db * 32, lane) : lds_col8<D>(kt, 16 * m, db * 32, lane);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[db] = mfma32(kop[db], b, acc[db]);
+        }
+    }
+
+    // bf16 output of this wave's 32 rows, staged 64 columns at a time through its own
+    // 4 KiB half of `tile` (the K part of the item's last slot)
+    __device__ __forceinline__ void store_halves(float mul, size_t ob, int rows, int row0, char* tile) const {
+        char* own = tile + wt * 4096;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const f32x16 part[2] = {acc[2 * hf], acc[2 * hf + 1]};
+            stage_block<64>(part, mul, own, r, hh);
+            store_tile<64>(own, slice_rsrc((const __bf16*)a.dq + ob + 64 * hf, rows, rso, 128),
+                           (uint32_t)row0 * rso, rso, lane);
+        }
+    }
+};
+
+template <bool F8>
+__global__ __launch_bounds__(128, 1) void dq_from_ds_team_kernel(const KernelArgs a, const Rec* __restrict__ recs,
+                                                                const int32_t* __restrict__ bin_ptr) {
+    __shared__ __attribute__((aligned(1024))) char smem[DsRing2<F8>::BYTES];
+    const int wt = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int bin = team_bin();
+    if (bin >= a.P) return;
+    const int beg = bin_ptr[bin], end = bin_ptr[bin + 1];
+    if (beg >= end) return;
+#ifdef GDPA_BIN_CLOCK
+    const unsigned long long clock0 = __builtin_amdgcn_s_memrealtime();
+#endif
+    DqDsTeamPol<F8> pol(a, lane, wt);
+    DsRing2<F8> ring;
+    ring.init(smem, (uint32_t)a.H * 128 * (F8 ? 1 : 2), wt, lane);
+    // issuing side: the item and step of the next job (items without steps have none);
+    // both waves walk the same jobs and issue their shares
+    int wi = beg, ws = 0;
+    Rec wr = recs[beg];
+    while (wi < end && wr.s1 < wr.s0)
+        if (++wi < end) wr = recs[__builtin_amdgcn_readfirstlane(wi)];
+    ws = wr.s0;
+    int job = 0;
+    auto pump = [&](int consumed) {
+        while (wi < end && ring.issued < consumed + DsRing2<F8>::R) {
+            pol.issue(ring, wr, ws);
+            if (++ws > wr.s1) {
+                do {
+                    if (++wi < end) wr = recs[__builtin_amdgcn_readfirstlane(wi)];
+                } while (wi < end && wr.s1 < wr.s0);
+                ws = wr.s0;
+            }
+        }
+    };
+    pump(job);
+    for (int ci = beg; ci < end; ++ci) {
+        const Rec c = recs[ci];
+        const size_t ob = ((size_t)c.qs * pol.H + c.h) * 128;
+        const int row0 = pol.tile(c) * 32;
+        const bool own = row0 < c.lq;   // this wave's tile holds queries
+        if (c.s1 < c.s0) {
+            if (own) pol.template zero<128>(a.dq, ob, c.lq, row0);
+            continue;
+        }
+#pragma unroll
+        for (int db = 0; db < DqDsTeamPol<F8>::NDB; ++db) pol.acc[db] = f32x16{};
+        for (int s = c.s0; s <= c.s1; ++s) {
+            ring.wait(job);
+            team_sync<2>();   // both waves' shares have landed and the slot the pump re-fills is read
+            pump(job);
+            if (pol.block(c, s) >= 0) pol.step(ring, job);
+            ++job;
+        }
+        if (c.part >= 0) {
+            if (own) store_partial<DqDsTeamPol<F8>::NDB>(pol.acc, a.part, c.part, 64, row0 - 64 * c.t, pol.r, pol.hh);
+            continue;
+        }
+        const float mul = F8 ? a.f8_dq : pol.scale;
+        if (a.out_f32) {
+            if (own) pol.template store<128>(pol.acc, mul, a.dq, ob, c.lq, row0, nullptr);
+            continue;
+        }
+        // the staging slot (the K part of the item's last step) is re-filled only at the
+        // next consume point, after both waves are past this barrier's reads of it
+        team_sync<2>();
+        if (own) pol.store_halves(mul, ob, c.lq, row0, ring.ktile(job - 1));
+    }
+#ifdef GDPA_BIN_CLOCK
+    if (a.bin_clock && threadIdx.x == 0) {
+        a.bin_clock[2 * bin] = clock0;
+        a.bin_clock[2 * bin + 1] = __builtin_amdgcn_s_memrealtime();
+    }
+#endif
+}
+
 }  // namespace
 
 hipError_t launch_dq_from_ds(const KernelArgs& a, int f8, hipStream_t s) {
@@ -589,6 +790,20 @@ hipError_t launch_dq_from_ds(const KernelArgs& a, int f8, hipStream_t s) {
 
 const void* dq_from_ds_kernel_ptr(int f8) {
     return f8 ? (const void*)&dq_from_ds_kernel<true> : (const void*)&dq_from_ds_kernel<false>;
+}
+
+hipError_t launch_dq_from_ds_team(const KernelArgs& a, int f8, hipStream_t s) {
+    if (a.P <= 0) return hipSuccess;
+    if (!a.ds) return hipErrorInvalidValue;
+    KernelArgs args = a;
+    const void* recs = a.items;
+    const int32_t* bin_ptr = a.bin_ptr;
+    void* params[] = {&args, &recs, &bin_ptr};
+    return hipLaunchKernel(dq_from_ds_team_kernel_ptr(f8), dim3(a.P), dim3(128), params, 0, s);
+}
+
+const void* dq_from_ds_team_kernel_ptr(int f8) {
+    return f8 ? (const void*)&dq_from_ds_team_kernel<true> : (const void*)&dq_from_ds_team_kernel<false>;
 }
 
 template <int T, bool F8>

@@ -115,6 +115,10 @@ const void* dkdv16_kernel_ptr(int rows, int act);
 // slots; f8: K as fp8 (e4m3)
 hipError_t launch_dq_from_ds(const KernelArgs& a, int f8, hipStream_t s);
 const void* dq_from_ds_kernel_ptr(int f8 = 0);
+// the same over 64-row q items in two-wave teams (items carry the dS layout's head
+// base and blocks per q tile in pad0, pad1)
+hipError_t launch_dq_from_ds_team(const KernelArgs& a, int f8, hipStream_t s);
+const void* dq_from_ds_team_kernel_ptr(int f8 = 0);
 
 // One-pass backward (one-wave teams, one block per wave): kv_stationary = 1 runs
 // over the dK/dV list when every Lk <= 32 (dQ stored per step), 0 over the dQ

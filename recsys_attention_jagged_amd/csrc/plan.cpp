@@ -249,6 +249,9 @@ std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t
         if (wl.kind == LIST_DKDV) {
             d.pad0 = (int32_t)head;
             d.pad1 = ds.nj[it.b];
+        } else if (wl.kind == LIST_DQ && wl.team == 2) {   // each wave finds its own q tile's blocks
+            d.pad0 = (int32_t)head;
+            d.pad1 = ds.nj[it.b];
         } else if (wl.kind == LIST_DQ && it.s1 >= it.s0) {
             d.pad0 = (int32_t)(head + (int64_t)it.t * ds.nj[it.b] + (it.s0 - ds_js0(it.t, window)));
         }

@@ -105,8 +105,8 @@ DsLayout ds_layout(const std::vector<int64_t>& lq, const std::vector<int64_t>& l
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
                                    const std::vector<int32_t>& kv_off);
 // with a dS layout: the dK/dV list's records carry (pad0, pad1) = (h nb_total + base[b], nj[b]),
-// the dQ list's (32-row q items) pad0 = the block of the item's first step (its steps'
-// blocks follow it)
+// and so do a dQ list's of 64-row items (two-wave teams); the dQ list's 32-row q items carry
+// pad0 = the block of the item's first step (its steps' blocks follow it)
 std::vector<DevRec> device_records(const WorkList& wl, const std::vector<int32_t>& q_off,
                                    const std::vector<int32_t>& kv_off, const DsLayout& ds, int window);
 // the cut items of a list, in slot order (output rows: queries, or keys for dK/dV)
