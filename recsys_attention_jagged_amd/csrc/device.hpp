@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include "gelu_poly.h"
+#include "gelu_tail.h"
 
 namespace gdpa {
 
@@ -139,12 +140,22 @@ __device__ __forceinline__ float gelu_poly_value(float x) {
     return __builtin_fabsf(x) <= GDPA_GELU_POLY_R ? __builtin_fmaf(0.5f, x, p) : __builtin_fmaxf(x, 0.0f);
 }
 
+// Phi(-|x|) as 2^p(|x|), p the degree-5 fit of log2 Phi(-z) in gelu_tail.h: five
+// FMAs and one exp2.  p falls without bound past its fit range, so 2^p vanishes
+// faster than |x| grows and the form needs no clamp.
+__device__ __forceinline__ float normal_tail_exp2(float x) {
+    const float z = __builtin_fabsf(x);
+    float p = kGeluTailCoef[GDPA_GELU_TAIL_DEGREE];
+#pragma unroll
+    for (int k = GDPA_GELU_TAIL_DEGREE - 1; k >= 0; --k) p = __builtin_fmaf(p, z, kGeluTailCoef[k]);
+    return fast_exp2(p);
+}
+
 template <int ACT>
 __device__ __forceinline__ float act_fwd(float x) {
     if constexpr (ACT == ACT_GELU) {
-        // x Phi(x) = max(x, 0) - |x| Phi(-|x|)
-        float e;
-        return __builtin_fmaf(-__builtin_fabsf(x), normal_tail(x, e), __builtin_fmaxf(x, 0.0f));
+        // x Phi(x) = max(x, 0) - |x| Phi(-|x|); absolute error within GDPA_GELU_TAIL_BOUND
+        return __builtin_fmaf(-__builtin_fabsf(x), normal_tail_exp2(x), __builtin_fmaxf(x, 0.0f));
     } else if constexpr (ACT == ACT_SILU) {
         return x * fast_rcp(1.0f + fast_exp2(x * -1.4426950408889634f));
     } else if constexpr (ACT == ACT_GELU_POLY) {

@@ -74,6 +74,42 @@ def test_gelu_poly_tables_meet_the_library_bounds():
     assert ef >= 0.9 * G.gdpa_gelu_poly_bound() and eg >= 0.9 * G.gdpa_gelu_poly_grad_bound()
 
 
+def _tail_header():
+    text = open(os.path.join(ROOT, "recsys_attention_jagged_amd", "csrc", "gelu_tail.h")).read()
+    bound = float(re.search(r"#define GDPA_GELU_TAIL_BOUND ([-+0-9.eE]+)", text).group(1))
+    body = re.search(r"kGeluTailCoef\[[^]]*\] = \{(.*?)\};", text, flags=re.S).group(1)
+    coef = [float(t.strip().rstrip("f")) for t in body.split(",") if t.strip()]
+    return bound, np.array(coef, dtype=np.float32)
+
+
+def test_gelu_tail_table_meets_its_bound():
+    """The forward's exact GELU, max(x, 0) - |x| 2^p(|x|) with the fitted tail p of
+    gelu_tail.h, evaluated here in the device's fp32 order (Horner by FMA, exp2 and
+    the final FMA rounded to fp32), against the oracle's x Phi(x) on a dense grid
+    and far past the fit range (no clamp): the error stays within the header's bound
+    (which also carries one ulp of the hardware exp2), and the chain falls to -inf
+    far out, where 2^p is 0."""
+    from oracle import gdpa_ref as R
+    bound, c = _tail_header()
+    assert len(c) == 6 and c[-1] < 0
+
+    def fma32(a, b, d):
+        with np.errstate(over="ignore"):
+            return (a.astype(np.float64) * b.astype(np.float64) + d.astype(np.float64)).astype(np.float32)
+
+    x = np.concatenate([np.linspace(-12, 12, 1_200_001), np.logspace(1, 30, 3001),
+                        -np.logspace(1, 30, 3001)]).astype(np.float32)
+    z = np.abs(x)
+    p = np.full_like(z, c[-1])
+    for ck in c[-2::-1]:
+        p = fma32(p, z, np.full_like(z, ck))
+    t = np.exp2(p.astype(np.float64)).astype(np.float32)
+    f = fma32(-z, t, np.maximum(x, np.float32(0)))
+    err = np.abs(f.astype(np.float64) - R.act_fwd(x.astype(np.float64), "gelu"))
+    assert err.max() <= bound, err.max()
+    assert np.all(np.isfinite(f)) and np.all(p[np.abs(x) > 1e10] == -np.inf)
+
+
 def _host_plan(lq, lk, H, d, window, P=1024, team=(0, 0, 0), blocks=(0, 0, 0), deal="greedy", split=True):
     qo, ko = offsets(lq), offsets(lk)
     return G.gdpa_plan_create(qo, ko, len(lq), H, d, window, "bf16", host_only=True,
