@@ -108,11 +108,28 @@ struct Dkdv16Pol : Common {
     long kf8[F8 ? NKB : 1];                      // F8: the K rows as fp8 operands
     f32x4 accK[NCB], accV[NCB];                  // lane: kv row l % 16, columns 16 cb + 4 (l / 16) + {0..3}
     int l16, g4;                                 // lane % 16, lane / 16
+    // exact GELU: the scale folded into the activation's constants (gelu_grad_folded), so P
+    // is formed divided by the scale and dV takes the scale at its store
+    static constexpr bool FOLD = ACT == ACT_GELU;
+    GeluFold gf;
 
     __device__ Dkdv16Pol(const KernelArgs& args, int lane_, int wt_) : Common(args, lane_, wt_, D) {
         l16 = lane_ & 15;
         g4 = lane_ >> 4;
+        if constexpr (FOLD) gf = gelu_fold(scale);
     }
+
+    // P (FOLD: P / scale) and dS of one score
+    __device__ __forceinline__ void act(float s, float dp, float& f, float& ds) const {
+        float gr;
+        if constexpr (FOLD)
+            gelu_grad_folded(s, gf, f, gr);
+        else
+            act_fwd_grad<ACT>(s * scale, f, gr);
+        ds = dp * gr;
+    }
+    // dV's factor at its store (FOLD: the scale P was formed without)
+    __device__ __forceinline__ float dv_mul() const { return (F8 ? a.f8_dv : 1.0f) * (FOLD ? scale : 1.0f); }
 
     // this wave's first kv row of the item, within the sample
     __device__ __forceinline__ int krow(const Rec& c) const { return c.t * ROWS + 16 * wt; }
@@ -278,20 +295,20 @@ struct Dkdv16Pol : Common {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int ib = e >> 2, v = e & 3;
-                float f, gr;
-                act_fwd_grad<ACT>(sc[ib][v] * scale, f, gr);
+                float f, ds;
+                act(sc[ib][v], dp[ib][v], f, ds);
                 const bool ok = in_band(base + 16 * ib + v, win);
                 pm[e] = (__bf16)(ok ? f : 0.0f);
-                dm[e] = (__bf16)(ok ? dp[ib][v] * gr : 0.0f);
+                dm[e] = (__bf16)(ok ? ds : 0.0f);
             }
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int ib = e >> 2, v = e & 3;
-                float f, gr;
-                act_fwd_grad<ACT>(sc[ib][v] * scale, f, gr);
+                float f, ds;
+                act(sc[ib][v], dp[ib][v], f, ds);
                 pm[e] = (__bf16)f;
-                dm[e] = (__bf16)(dp[ib][v] * gr);
+                dm[e] = (__bf16)ds;
             }
         }
         if (has_blk) {   // dS of q rows 4 (l / 16) + {0..3} and 16 + 4 (l / 16) + {0..3}, kv row j0 + l % 16
@@ -378,6 +395,12 @@ struct Dkdv16Pol : Common {
     template <class RingT>
     __device__ __forceinline__ void item_end(const Rec& c, const RingT& g, int job) {
         if (c.part >= 0) {   // one chunk of a cut item: fp32 partial dK, dV (scaled by the reduction)
+            if constexpr (FOLD) {   // the scale P was formed without, before the reduction's factor
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) accV[cb][i] *= scale;
+            }
             partial16(accK, 2 * c.part);
             partial16(accV, 2 * c.part + 1);
             return;
@@ -388,7 +411,7 @@ struct Dkdv16Pol : Common {
         const size_t ob = ((size_t)c.ks * H + c.h) * D;
         store16(accK, F8 ? a.f8_dk : scale, a.dk, ob, c.lk, krow(c), stage);
         wait_lds();
-        store16(accV, F8 ? a.f8_dv : 1.0f, a.dv, ob, c.lk, krow(c), stage);
+        store16(accV, dv_mul(), a.dv, ob, c.lk, krow(c), stage);
     }
 
     __device__ __forceinline__ void item_zero(const Rec& c) {

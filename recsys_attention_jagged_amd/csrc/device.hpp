@@ -124,6 +124,41 @@ __device__ __forceinline__ float normal_tail(float x, float& e) {
     return q * e;
 }
 
+// GELU and GELU' of x = scale s from the raw score s, with the scale and the density's
+// constant folded into the constants of the same erfc approximation (A&S 7.1.26):
+//   t  = 1 / (1 + (p scale / sqrt 2) |s|),
+//   e' = 2^(s^2 (-log2(e) scale^2 / 2) + log2(scale / sqrt(2 pi))) = scale phi(x),
+//   Phi(-|x|) = (sum_k a_k / (2 scale / sqrt(2 pi)) t^k) e',
+// so that GELU'(x) = Phi(x) + s e' is one FMA.  The value comes back divided by the
+// scale, GELU(x) / scale = s Phi(x): the caller applies the scale where the value's
+// products end (an output multiplier).  Two multiplies per score fewer than
+// act_fwd_grad on scale s.
+struct GeluFold {
+    float p, k, l, h1, h2, h3, h4, h5;
+};
+__device__ __forceinline__ GeluFold gelu_fold(float scale) {
+    GeluFold c;
+    const float inv = 2.5066282746310002f / scale;   // 1 / (scale / sqrt(2 pi))
+    c.p = 0.3275911f * 0.70710678118654752f * scale;
+    c.k = -0.72134752044448170f * scale * scale;
+    c.l = __builtin_amdgcn_logf(scale * 0.39894228040143268f);   // log2
+    c.h1 = 0.5f * 0.254829592f * inv;
+    c.h2 = 0.5f * -0.284496736f * inv;
+    c.h3 = 0.5f * 1.421413741f * inv;
+    c.h4 = 0.5f * -1.453152027f * inv;
+    c.h5 = 0.5f * 1.061405429f * inv;
+    return c;
+}
+__device__ __forceinline__ void gelu_grad_folded(float s, const GeluFold& c, float& f_over_scale, float& g) {
+    const float t = fast_rcp(__builtin_fmaf(c.p, __builtin_fabsf(s), 1.0f));
+    const float q = t * __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, __builtin_fmaf(t, c.h5, c.h4), c.h3), c.h2), c.h1);
+    const float e = fast_exp2(__builtin_fmaf(s * s, c.k, c.l));
+    const float tail = q * e;
+    const float cdf = s >= 0.0f ? 1.0f - tail : tail;
+    f_over_scale = s * cdf;
+    g = __builtin_fmaf(s, e, cdf);
+}
+
 // Phi(x) and exp(-x^2 / 2)
 __device__ __forceinline__ void normal_cdf(float x, float& cdf, float& e) {
     const float c = normal_tail(x, e);
