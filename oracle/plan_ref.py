@@ -15,14 +15,17 @@ Readings (the page gives no cost model or tie-break):
     [s0, s1] of streaming tiles that hold at least one valid pair; items whose
     other side is empty (Lk == 0 for Q-stationary lists, Lq == 0 for the
     KV-stationary list) have no steps (s0 = 0, s1 = -1) and only write zeros;
-  * cost = (valid stationary rows) + sum over steps of (valid streaming rows + 32),
-    i.e. rows moved through memory plus a fixed per-step charge;
+  * cost = (stationary tile rows) + sum over steps of (valid streaming rows + 32):
+    rows moved through memory plus a fixed per-step charge, the stationary side
+    charged as a whole tile even where the sample ends inside it (its products run
+    on the whole tile, and a sample's last, partial tile then costs what its
+    neighbours cost, so that it is sorted and dealt beside them);
   * chunks: with m = ceil(total cost / P), the mean bin cost, an item with n >= 2
     steps and cost > m (> ceil(m / 4) when the list has fewer than 2 P items, which
     no deal could balance) is cut into
     k = min(n, ceil(cost / ceil(m / 4))) chunks of consecutive steps (no bin could
     hold it at the mean), chunk j holding steps s0 + floor(j n / k) ..
-    s0 + floor((j + 1) n / k) - 1 and costing its stationary rows plus its steps;
+    s0 + floor((j + 1) n / k) - 1 and costing its stationary tile plus its steps;
     chunk j of the g-th cut item (in (b, h, t) order) writes partial-output slot
     (chunks of earlier cut items) + j (O or dQ; dK and dV for the KV-stationary
     list), and the item's output is the sum of its slots.  The page deals tiles, not whole rows of tiles, so a long row of tiles
@@ -88,7 +91,6 @@ def enumerate_items(kind: str, lq, lk, H: int, window: int, t_stat: int, t_strm:
             for t in range(_ceil_div(ls, t_stat)):
                 a0 = t * t_stat
                 a1 = min(ls, a0 + t_stat) - 1
-                n_stat = a1 - a0 + 1
                 if lo_other == 0:
                     s0, s1 = 0, -1
                 elif window == 0:
@@ -97,7 +99,7 @@ def enumerate_items(kind: str, lq, lk, H: int, window: int, t_stat: int, t_strm:
                     lo = max(0, a0 - window + 1)
                     hi = min(lo_other - 1, a1 + window - 1)
                     s0, s1 = lo // t_strm, hi // t_strm
-                cost = n_stat
+                cost = t_stat
                 for s in range(s0, s1 + 1):
                     cost += min(lo_other, (s + 1) * t_strm) - s * t_strm + STEP_CHARGE
                 items.append((cost, b, h, t, s0, s1))
@@ -121,11 +123,10 @@ def split_items(kind: str, items, lq, lk, P: int, t_stat: int, t_strm: int):
             out.append((cost, b, h, t, s0, s1, -1))
             continue
         k = min(n, _ceil_div(cost, piece))
-        n_stat = min(int(ls[b]), (t + 1) * t_stat) - t * t_stat
         lo_other = int(lo[b])
         for j in range(k):
             f, l = s0 + j * n // k, s0 + (j + 1) * n // k - 1
-            c = n_stat + sum(min(lo_other, (s + 1) * t_strm) - s * t_strm + STEP_CHARGE for s in range(f, l + 1))
+            c = t_stat + sum(min(lo_other, (s + 1) * t_strm) - s * t_strm + STEP_CHARGE for s in range(f, l + 1))
             out.append((c, b, h, t, f, l, slot + j))
         slot += k
     return out, slot

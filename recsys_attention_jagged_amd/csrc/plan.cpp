@@ -59,7 +59,6 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
 
     // whole items in (b, h, t) order
     std::vector<Cand> whole;
-    std::vector<int64_t> n_stat;
     for (size_t b = 0; b < lq.size(); ++b) {
         const int64_t ls = (kind == LIST_DKDV) ? lk[b] : lq[b];
         const int64_t lo = (kind == LIST_DKDV) ? lq[b] : lk[b];
@@ -81,13 +80,15 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
                     s0 = lo_row / TR;
                     s1 = hi_row / TR;
                 }
-                int64_t cost = a1 - a0 + 1;
+                // the stationary side as a whole tile: its products run on the whole tile, and a
+                // sample's last, partial tile then costs what its neighbours cost, so that it is
+                // sorted and dealt beside them (and, streaming the same tiles, meets them in L2)
+                int64_t cost = TS;
                 for (int64_t s = s0; s <= s1; ++s) cost += std::min(lo, (s + 1) * TR) - s * TR + kStepCharge;
                 Cand c;
                 c.cost = cost;
                 c.it = Item{(int32_t)b, h, (int32_t)t, (int32_t)s0, (int32_t)s1, -1, 0, 0};
                 whole.push_back(c);
-                n_stat.push_back(a1 - a0 + 1);
             }
         }
     }
@@ -114,7 +115,7 @@ WorkList plan_list(int kind, const std::vector<int64_t>& lq, const std::vector<i
             for (int64_t j = 0; j < k; ++j) {
                 const int64_t f = c.it.s0 + j * n / k, l = c.it.s0 + (j + 1) * n / k - 1;
                 Cand p = c;
-                p.cost = n_stat[i];
+                p.cost = TS;
                 for (int64_t s = f; s <= l; ++s) p.cost += std::min(lo, (s + 1) * TR) - s * TR + kStepCharge;
                 p.it.s0 = (int32_t)f;
                 p.it.s1 = (int32_t)l;

@@ -13,8 +13,8 @@
 // ("fwd", "dq"), kv tiles / q steps for the KV-stationary list ("dkdv").  Items
 // whose other side is empty get no steps and write zeros.
 //
-// Cost of an item: valid stationary rows + sum over steps of (valid streaming
-// rows + 32).  Chunks: an item with at least two steps whose cost exceeds the
+// Cost of an item: stationary tile rows (a whole tile, also where the sample ends
+// inside it) + sum over steps of (valid streaming rows + 32).  Chunks: an item with at least two steps whose cost exceeds the
 // mean bin cost m = ceil(total / P) (a quarter of it, ceil(m / 4), when the list
 // has fewer than 2 P items) is cut into k = min(steps, ceil(cost / ceil(m / 4)))
 // chunks of consecutive steps (chunk i: steps s0 + floor(i n / k) ..

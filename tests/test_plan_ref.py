@@ -175,15 +175,17 @@ def test_chunks_cover_each_tile_once(lq, lk, window, P, kind, layout):
 
 def test_chunk_rule_on_a_long_item():
     """One sample of 32 queries and 4096 keys next to 63 one-step samples, 16 bins,
-    no window: the long item (128 steps) costs 32 + 128 * 64 = 8224, the total is
-    8224 + 63 * (1 + 33) = 10366, the mean bin cost m = ceil(10366 / 16) = 648, so the
-    item is cut into k = ceil(8224 / ceil(648 / 4)) = ceil(8224 / 162) = 51 chunks of
-    2 or 3 steps; the one-step items stay whole."""
+    no window: the long item (128 steps) costs 32 + 128 * 64 = 8224, each one-step
+    item (one query row, one key row) 32 + (1 + 32) = 65 (the stationary side is
+    charged as a whole 32-row tile), the total is 8224 + 63 * 65 = 12319, the mean bin
+    cost m = ceil(12319 / 16) = 770, so the item is cut into
+    k = ceil(8224 / ceil(770 / 4)) = ceil(8224 / 193) = 43 chunks of 2 or 3 steps; the
+    one-step items stay whole."""
     lq, lk = [32] + [1] * 63, [4096] + [1] * 63
     pl = PR.plan_list("fwd", lq, lk, 1, 0, 16, 1, 1)
     parts = sorted((s0, s1, part) for b, h, t, s0, s1, part in pl["items"] if part >= 0)
-    assert pl["n_parts"] == 51 and len(parts) == 51
-    assert [s1 - s0 + 1 for s0, s1, _ in parts] == [(j + 1) * 128 // 51 - j * 128 // 51 for j in range(51)]
+    assert pl["n_parts"] == 43 and len(parts) == 43
+    assert [s1 - s0 + 1 for s0, s1, _ in parts] == [(j + 1) * 128 // 43 - j * 128 // 43 for j in range(43)]
     assert all(part == -1 for b, h, t, s0, s1, part in pl["items"] if b > 0)
     # the chunked plan balances where the whole item could not
     whole = PR.plan_list("fwd", lq, lk, 1, 0, 16, 1, 1, split=False)
@@ -191,9 +193,9 @@ def test_chunk_rule_on_a_long_item():
     for mode in PR.DEALS:
         cut = PR.plan_list("fwd", lq, lk, 1, 0, 16, 1, 1, mode=mode)
         assert max(cut["bin_cost"]) < 0.15 * max(whole["bin_cost"])
-        assert sum(cut["bin_cost"]) == sum(whole["bin_cost"]) + 50 * 32   # each extra chunk reloads 32 rows
+        assert sum(cut["bin_cost"]) == sum(whole["bin_cost"]) + 42 * 32   # each extra chunk reloads 32 rows
     g = PR.groups(pl, [0] + list(np.cumsum(lq)))
-    assert g == [(0, 32, 0, 0, 51)]
+    assert g == [(0, 32, 0, 0, 43)]
 
 
 def test_short_items_are_never_cut():
