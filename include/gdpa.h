@@ -115,7 +115,8 @@ typedef struct {
                         latency).  Results do not depend on it (bit for bit) */
     int slot_time;   /* 0 automatic: where a list has automatic bins and its kernel is one
                         measured for it (the d = 128 two-wave forward and 16-row dK/dV
-                        kernels at four workgroups per CU, the d = 64 forward at eight), the
+                        kernels at four workgroups per CU, the d = 64 forward at eight, dQ
+                        from stored dS in two-wave teams at three), the
                         greedy deal weighs each bin's cost by a time factor of its dispatch
                         round on its CU (workgroups placed early on a CU ran up to 12 %
                         faster than later ones), so earlier-placed bins get more work; 1 every
@@ -151,6 +152,7 @@ typedef struct {
     int32_t dq_team_items;   /* list 3 (dq_team 2): work items, bins, cut items' chunk slots */
     int32_t dq_team_bins;
     int32_t dq_team_parts;
+    int32_t dq_team_slot_weighted; /* 1: list 3's deal took the dispatch-slot time factors */
 } gdpa_plan_stats_t;
 
 typedef struct gdpa_plan_s* gdpa_plan;

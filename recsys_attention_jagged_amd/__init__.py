@@ -50,7 +50,8 @@ class gdpa_plan_stats_t(ctypes.Structure):
                 ("bin_cost_min", ctypes.c_int64 * 3), ("bwd_fused", ctypes.c_int32),
                 ("n_parts", ctypes.c_int32 * 3), ("ds_bytes", ctypes.c_int64), ("claimed", ctypes.c_int32 * 3),
                 ("slot_weighted", ctypes.c_int32 * 3), ("dq_team", ctypes.c_int32),
-                ("dq_team_items", ctypes.c_int32), ("dq_team_bins", ctypes.c_int32), ("dq_team_parts", ctypes.c_int32)]
+                ("dq_team_items", ctypes.c_int32), ("dq_team_bins", ctypes.c_int32), ("dq_team_parts", ctypes.c_int32),
+                ("dq_team_slot_weighted", ctypes.c_int32)]
 
 
 _lib = None

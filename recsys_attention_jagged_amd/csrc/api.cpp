@@ -62,6 +62,10 @@ const void* dkdv_kernel_ptr(int d, int team, int nb, int act) {
     return nullptr;
 }
 
+// work lists of a plan: GDPA_LIST_FWD, _DKDV, _DQ and the two-wave dQ-from-dS list
+constexpr int kLists = 4;
+constexpr int LIST_DQ_TEAM = 3;
+
 // Time factors per dispatch round for the greedy deal.  A persistent launch of k
 // workgroups per CU reaches each CU in k rounds (an XCD's first workgroups go one per
 // CU, then the next round, ...), and on the kernels below, workgroups of the early
@@ -83,7 +87,24 @@ constexpr SlotTimes kSlotTimes[] = {
     {LIST_DKDV, 128, 1, 1, 4, {0.88, 1.025, 1.025, 1.07}},
     // forward, one wave of two 32-row blocks
     {LIST_FWD, 64, 1, 2, 8, {0.93, 0.93, 0.93, 0.93, 1.07, 1.07, 1.07, 1.07}},
+    // dQ from stored dS, two-wave teams over 64-row items (three teams per CU)
+    {LIST_DQ_TEAM, 128, 2, 1, 3, {0.90, 1.045, 1.055}},
 };
+
+// Per-bin factors of list `list` (its kernel's layout d, team, nb) over P automatic bins,
+// or none where the table has no entry: bin q runs on the workgroup the XCD remap gives
+// it, position q % (P / 8) in its XCD's dispatch order, so in dispatch round
+// position / (CUs per XCD).
+std::vector<double> round_time_factors(int list, int d, int team, int nb, int P, int cus) {
+    std::vector<double> bin_time;
+    if (cus % 8 != 0) return bin_time;
+    for (const SlotTimes& t : kSlotTimes)
+        if (t.list == list && t.d == d && t.team == team && t.nb == nb && P == t.per_cu * cus) {
+            bin_time.resize(P);
+            for (int q = 0; q < P; ++q) bin_time[q] = t.f[(q % (P / 8)) / (cus / 8)];
+        }
+    return bin_time;
+}
 
 int64_t pairs_of(int64_t lq, int64_t lk, int64_t w) {
     if (w == 0) return lq * lk;
@@ -93,10 +114,6 @@ int64_t pairs_of(int64_t lq, int64_t lk, int64_t w) {
 }
 
 }  // namespace
-
-// work lists of a plan: GDPA_LIST_FWD, _DKDV, _DQ and the two-wave dQ-from-dS list
-constexpr int kLists = 4;
-constexpr int LIST_DQ_TEAM = 3;
 
 struct gdpa_plan_s;
 static gdpa_status upload(gdpa_plan_s* p, hipStream_t s);
@@ -381,19 +398,10 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
         const bool split = o.no_split == 0 && dtype != GDPA_F32;
         // dispatch-round factors: automatic bins only (the one-pass backward's kernels are not
         // in the table, so a fused backward's list takes none)
-        const double* slot_time = nullptr;
         const bool list_kernel = l == LIST_FWD || p->fused == 0;
-        if (o.slot_time == 0 && auto_bins && dtype != GDPA_F32 && list_kernel && cus % 8 == 0)
-            for (const SlotTimes& t : kSlotTimes)
-                if (t.list == l && t.d == d && t.team == L.team[l] && t.nb == L.nb[l] && P == t.per_cu * cus)
-                    slot_time = t.f;
         std::vector<double> bin_time;
-        if (slot_time) {
-            // bin q runs on the workgroup the XCD remap gives it: position q % (P / 8) in its
-            // XCD's dispatch order, so dispatch round position / (CUs per XCD)
-            bin_time.resize(P);
-            for (int q = 0; q < P; ++q) bin_time[q] = slot_time[(q % (P / 8)) / (cus / 8)];
-        }
+        if (o.slot_time == 0 && auto_bins && dtype != GDPA_F32 && list_kernel)
+            bin_time = round_time_factors(l, d, L.team[l], L.nb[l], P, cus);
         p->lists[l] = plan_list(l, lq, lk, H, window, P, L.team[l], L.nb[l], o.deal, split, bin_time);
     }
 
@@ -402,6 +410,7 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
     // else as many teams as the device holds resident (host_only: 4 per CU)
     if (p->use_ds && o.dq_team == 0) {
         int P = o.bins[LIST_DQ];
+        const bool auto_bins = P == 0;
         if (P == 0) {
             P = 4 * cus;
             int per_cu = 0;
@@ -411,7 +420,9 @@ static gdpa_status plan_create(const int32_t* q_off_host, const int32_t* kv_off_
                 per_cu > 0)
                 P = cus * per_cu;
         }
-        p->lists[LIST_DQ_TEAM] = plan_list(LIST_DQ, lq, lk, H, window, P, 2, 1, o.deal, o.no_split == 0);
+        const std::vector<double> bin_time =
+            o.slot_time == 0 && auto_bins ? round_time_factors(LIST_DQ_TEAM, d, 2, 1, P, cus) : std::vector<double>();
+        p->lists[LIST_DQ_TEAM] = plan_list(LIST_DQ, lq, lk, H, window, P, 2, 1, o.deal, o.no_split == 0, bin_time);
         p->dq_team = true;
     }
 
@@ -532,6 +543,7 @@ gdpa_status gdpa_plan_stats(gdpa_plan plan, gdpa_plan_stats_t* out) {
         out->dq_team_items = (int32_t)wl.items.size();
         out->dq_team_bins = wl.P;
         out->dq_team_parts = wl.n_parts;
+        out->dq_team_slot_weighted = wl.weighted ? 1 : 0;
     }
     return GDPA_OK;
 }

@@ -3,9 +3,10 @@
 The factors only move items between bins: each item computes the same arithmetic in
 the same order wherever it runs, and cut items' chunks are summed in their fixed slot
 order, so a plan dealt with the factors must give the outputs of one dealt by plain
-cost bit for bit.  The cases cover the three kernel layouts the factors apply to (the
-d = 128 two-wave forward and 16-row dK/dV kernels at four workgroups per CU, the d = 64
-forward with two blocks per wave at eight) and check that the deal did change."""
+cost bit for bit.  The cases cover the kernel layouts the factors apply to (the d = 128
+two-wave forward and 16-row dK/dV kernels at four workgroups per CU, the d = 64 forward
+with two blocks per wave at eight, dQ from stored dS in two-wave teams at three) and
+check that the deal did change."""
 import numpy as np
 import pytest
 import torch
@@ -69,8 +70,12 @@ def test_slot_time_bit_exact(case):
             assert sw["slot_weighted"][0] == 1, sw
         else:
             pytest.skip(f"the d = 64 forward runs {sw['bins'][0]} workgroups here, not 8 per CU")
-        for lst in range(3):
-            if sw["slot_weighted"][lst]:
+        if d == 128 and sw["dq_team"] == 2 and sw["dq_team_bins"] == 3 * cus:
+            # dQ from stored dS in two-wave teams at three per CU
+            assert sw["dq_team_slot_weighted"] == 1 and so["dq_team_slot_weighted"] == 0, sw
+        weighted = list(sw["slot_weighted"]) + [sw["dq_team_slot_weighted"]]
+        for lst in range(4):
+            if weighted[lst]:
                 assert not np.array_equal(po.export(lst), pw.export(lst)), f"list {lst}: the deal did not change"
         ref = run_all(po, inp, qo, ko)
         got = run_all(pw, inp, qo, ko)
