@@ -114,7 +114,7 @@ def main(argv=None):
                 dump[f"{deal}_{name}_export"] = np.asarray(G.gdpa_plan_export(h, lst))
             print(json.dumps({
                 "workload": WORKLOADS[cfg]["name"], "deal": deal, "claimed": st["claimed"][lst] if lst < 3 else 0,
-                "slot_weighted": st["slot_weighted"][lst] if lst < 3 else 0, "kernel": name,
+                "slot_weighted": st["slot_weighted"][lst] if lst < 3 else st["dq_team_slot_weighted"], "kernel": name,
                 "bins": int(busy.size),
                 "busy_us": {"max": round(float(busy.max()), 1), "mean": round(float(busy.mean()), 1),
                             "min": round(float(busy.min()), 1)},
