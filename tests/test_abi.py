@@ -279,6 +279,46 @@ def test_plan_slot_time_factors():
                 G.gdpa_plan_destroy(p)
 
 
+def test_plan_dq_team_list():
+    """dQ from stored dS in two-wave teams: a d = 128 two-kernel plan carries list 3, the
+    dQ list dealt again as 64-row items (team 2, one block), exported like the others and
+    equal to the planner reference's dQ list of that layout; dq_team = one_wave keeps the
+    one-wave kernel over the dQ list (no list 3); plans without stored dS (d = 64, a
+    one-pass backward) have none, and exporting list 3 from them is an error."""
+    lq = [1, 15, 16, 17, 33, 47, 64, 65, 0, 300, 129, 700, 96, 97]
+    P = 64
+
+    def plan(d, **kw):
+        return G.gdpa_plan_create(offsets(lq), offsets(lq), len(lq), 2, d, 0, "bf16", host_only=True,
+                                  bins=(P, P, P), **kw)
+
+    p = plan(128)
+    try:
+        st = G.gdpa_plan_stats(p)
+        assert st["ds_bytes"] > 0 and st["dq_team"] == 2 and st["dq_team_bins"] == P
+        ex = list(G.gdpa_plan_export(p, "dq_team"))
+        assert ex[2:6] == [64, 32, 2, 1] and ex[1] == st["dq_team_items"]
+        assert ex == PR.export(PR.plan_list("dq", lq, lq, 2, 0, P, 2, 1))
+    finally:
+        G.gdpa_plan_destroy(p)
+    p = plan(128, dq_team="one_wave")
+    try:
+        st = G.gdpa_plan_stats(p)
+        assert st["ds_bytes"] > 0 and st["dq_team"] == 1 and st["dq_team_items"] == 0
+        with pytest.raises(G.GdpaError):
+            G.gdpa_plan_export(p, 3)
+    finally:
+        G.gdpa_plan_destroy(p)
+    p = plan(64)
+    try:
+        st = G.gdpa_plan_stats(p)
+        assert st["ds_bytes"] == 0 and st["dq_team"] == 0
+        with pytest.raises(G.GdpaError):
+            G.gdpa_plan_export(p, 3)
+    finally:
+        G.gdpa_plan_destroy(p)
+
+
 # ---------------------------------------------------------------------------
 # error paths (forced from the host)
 # ---------------------------------------------------------------------------
@@ -308,6 +348,8 @@ def test_create_rejects_bad_arguments():
     assert bad(claim=-1) == 1
     assert bad(slot_time=2) == 1
     assert bad(slot_time=-1) == 1
+    assert bad(dq_team=2) == 1
+    assert bad(dq_team=-1) == 1
     assert bad(d=128, team=(0, 0, 2), blocks=(0, 0, 2)) == 1   # two-wave teams: one block per wave
     assert bad(d=128, team=(2, 0, 0), blocks=(2, 0, 0)) == 1
     assert bad(qo=np.array([1, 3, 7], np.int32)) == 2           # BAD_OFFSETS: not starting at 0
