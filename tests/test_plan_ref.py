@@ -299,3 +299,24 @@ def test_workload_plans_at_automatic_layouts_cover_each_tile_once(cfg, kind):
                                    for t in range(-(-int(ls[b]) // t_stat))}
     counts = np.diff(pl["bin_ptr"])
     assert not (counts.min() == 0 and counts.max() > 1)
+
+
+def test_partial_tiles_sort_beside_their_neighbours():
+    """The cost charges the stationary side as a whole tile, so the tiles of one (sample,
+    head) that stream the same tiles cost the same whether or not the sample ends inside
+    them: in the sorted order each (sample, head)'s items sit together, the last, partial
+    tile among them (a whole-tile charge for every stationary tile, rows or not)."""
+    lq = [100, 257, 33, 64, 1000, 95]          # every sample ends inside its last 64-row tile but one
+    lk = [32] * len(lq)                        # one streaming tile: every item costs the same
+    H = 3
+    t_stat, t_strm = PR.tile_sizes("fwd", 2, 1)
+    items = PR.enumerate_items("fwd", lq, lk, H, 0, t_stat, t_strm)
+    assert len({it[0] for it in items}) == 1   # partial tiles cost what full ones do
+    order = sorted(items, key=lambda it: (-it[0], it[1], it[2], it[4], it[3]))
+    pos = {}
+    for r, it in enumerate(order):
+        pos.setdefault((it[1], it[2]), []).append(r)
+    for key, rs in pos.items():
+        assert rs == list(range(rs[0], rs[0] + len(rs))), key   # contiguous in the sorted order
+        ts = [order[r][3] for r in rs]
+        assert ts == sorted(ts)                                  # and in tile order
